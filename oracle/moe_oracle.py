@@ -1,0 +1,425 @@
+"""Plain, slow, obviously-correct CPU oracle of one MoE FFN layer's decode step.
+
+TEST INFRASTRUCTURE ONLY.  Only `tests/`, the package smoke check and the
+bench's CPU-baseline leg import this module; the HIP product path never does,
+and this module imports nothing from it.  It shares no code, constants or
+helpers with the HIP path; the only thing both sides share is the seeded input
+generator, which holds none of the layer's arithmetic.
+
+Sources (the pages this follows; sections named, sentences restated):
+  [DeaMoE]  "DeaMoE: Efficient MoE Structure for Fast Small-Batch Decoding"
+            (arXiv 2608.14385): section 2.1 Eq. (1) expert FFN, Eq. (2) top-k
+            on router logits, Eq. (3) weighted combine; section 3.1 and
+            section 3.2 (departments, two-stage routing); section 3.3 /
+            Figure 2 (weights loaded per step); Table 1.
+  [DSMoE]   "DeepSeekMoE Guide: Fine-Grained Experts & Dynamic Routing":
+            "Shared Expert Isolation", "Mathematical Formulation of the
+            DeepSeekMoE Forward Pass", "Auxiliary-Loss-Free Dynamic Load
+            Balancing" (selection bias).
+  [MoEInf]  "MoE inference engineering, clearly explained": "How a batch
+            becomes expert-specific matrices" (the four-token worked example,
+            dispatch and combine), "Local MoE execution pipeline" (permutation
+            and its inverse mapping).
+
+Precision: inputs are fp32 (bf16 storage widens exactly).  Every dot product
+and every sum is done in float64; the only fp32 roundings are where a decision
+is taken (the logits and selection scores that top-k ranks, because the HIP
+path ranks fp32 values) and the final cast of y to the output dtype.
+
+Readings where the pages leave a step open (each is also listed with its
+justification in the design notes):
+  R1 selection ranks the router logits themselves (Eq. (2) applies TopK to
+     W_r x), softmax is applied to the selected logits afterwards;
+  R2 ties go to the lower expert index; slots are ordered by (score desc,
+     index asc);
+  R3 inside an expert group rows are ordered by assignment index t*k+j
+     (token ascending);
+  R4 route_scale multiplies the final weights (the paper's "scaling"; 1.0 in
+     every layer shape used here);
+  R5 sigmoid mode: rank s+b with s = sigmoid(l) in fp32; weights are the
+     selected *unbiased* s renormalised to sum 1;
+  R6 softmax_bias mode: rank l+b, weights = softmax of the selected unbiased
+     logits (the DeepSeekMoE guide's router);
+  R7 the layer output has no residual term;
+  R8 the shared expert is added with weight 1;
+  R9 department slice form: expert e belongs to department e // (E/m); its
+     intermediate is [department slice S ; private slice P];
+  R10 c_{t,j} = sum of the token's final weights over its selected experts
+     in department j.
+"""
+from __future__ import annotations
+
+from typing import Callable, Dict, Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "router_logits", "selection_scores", "topk_select", "routing_weights",
+    "route", "dispatch", "swiglu", "expert_outputs", "combine",
+    "layer_bruteforce", "layer_grouped", "dept_layer_expanded",
+    "dept_layer_factored", "layer_token_output", "loaded_weight_bytes",
+    "select_from_scores", "silu", "cast_output", "SOFTMAX", "SIGMOID", "SOFTMAX_BIAS",
+]
+
+SOFTMAX, SIGMOID, SOFTMAX_BIAS = "softmax", "sigmoid", "softmax_bias"
+
+
+def _f64(a) -> np.ndarray:
+    """Widen to float64 (exact for fp32 and bf16 sources)."""
+    if hasattr(a, "detach"):  # a torch tensor: widen in torch, then hand to numpy
+        a = a.detach().to("cpu")
+        import torch
+        a = a.to(torch.float64).numpy()
+    return np.asarray(a, dtype=np.float64)
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU(z) = z * sigmoid(z) = z / (1 + e^-z) [DeaMoE §2.1; §3.4 names SiLU]."""
+    return z / (1.0 + np.exp(-z))
+
+
+# ----------------------------------------------------------------------------
+# Router  [DeaMoE §2.1 Eq. (2), Eq. (3)]; [DSMoE formulation, bias routing]
+# ----------------------------------------------------------------------------
+
+def router_logits(x, w_router) -> np.ndarray:
+    """l[t, e] = sum_c x[t, c] * W_r[e, c] (Eq. (2)'s W_r x), summed in fp64
+    and rounded once to fp32 (the value the top-k ranks)."""
+    l64 = _f64(x) @ _f64(w_router).T
+    return l64.astype(np.float32)
+
+
+def selection_scores(l32: np.ndarray, score_fn: str, bias=None) -> np.ndarray:
+    """The fp32 value each expert is ranked by.
+
+    softmax:      the logit itself (R1);
+    softmax_bias: logit + b (fp32 add);
+    sigmoid:      fp32(sigmoid(l)) + b (fp32 add) (R5).
+    """
+    l32 = np.asarray(l32, dtype=np.float32)
+    if score_fn == SOFTMAX:
+        return l32.copy()
+    b = np.zeros(l32.shape[-1], np.float32) if bias is None else _f64(bias).astype(np.float32)
+    if score_fn == SOFTMAX_BIAS:
+        return (l32 + b).astype(np.float32)
+    if score_fn == SIGMOID:
+        s32 = (1.0 / (1.0 + np.exp(-l32.astype(np.float64)))).astype(np.float32)
+        return (s32 + b).astype(np.float32)
+    raise ValueError(score_fn)
+
+
+def topk_select(sel: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest scores per row, by a full stable sort on
+    (score descending, index ascending) (R2)."""
+    sel = np.asarray(sel)
+    T, E = sel.shape
+    ids = np.empty((T, k), dtype=np.int32)
+    for t in range(T):
+        order = sorted(range(E), key=lambda e: (-float(sel[t, e]), e))
+        ids[t] = order[:k]
+    return ids
+
+
+select_from_scores = topk_select
+
+
+def routing_weights(l32: np.ndarray, ids: np.ndarray, score_fn: str,
+                    renormalize: bool = True, route_scale: float = 1.0) -> np.ndarray:
+    """Per-slot weights p_i of Eq. (3), in fp64.
+
+    softmax (and softmax_bias): softmax of the selected logits when
+    renormalised, else the full softmax's probability of each selected
+    expert.  sigmoid: s_i / sum_{selected} s when renormalised, else s_i.
+    Then times route_scale (R4)."""
+    l = np.asarray(l32, dtype=np.float32).astype(np.float64)
+    T, k = ids.shape
+    w = np.empty((T, k), dtype=np.float64)
+    for t in range(T):
+        sel_l = l[t, ids[t]]
+        if score_fn in (SOFTMAX, SOFTMAX_BIAS):
+            if renormalize:
+                e = np.exp(sel_l - sel_l.max())
+                w[t] = e / e.sum()
+            else:
+                e_all = np.exp(l[t] - l[t].max())
+                w[t] = e_all[ids[t]] / e_all.sum()
+        elif score_fn == SIGMOID:
+            s = 1.0 / (1.0 + np.exp(-sel_l))
+            w[t] = s / s.sum() if renormalize else s
+        else:
+            raise ValueError(score_fn)
+    return w * route_scale
+
+
+def route(x, w_router, k: int, score_fn: str = SOFTMAX, bias=None,
+          renormalize: bool = True, route_scale: float = 1.0):
+    """Router of one decode step: (ids int32[T][k], weights f64[T][k],
+    selection scores f32[T][E], logits f32[T][E])."""
+    l32 = router_logits(x, w_router)
+    sel = selection_scores(l32, score_fn, bias)
+    ids = topk_select(sel, k)
+    w = routing_weights(l32, ids, score_fn, renormalize, route_scale)
+    return ids, w, sel, l32
+
+
+# ----------------------------------------------------------------------------
+# Dispatch / permutation  [MoEInf "How a batch becomes expert-specific
+# matrices", "Local MoE execution pipeline"]
+# ----------------------------------------------------------------------------
+
+def dispatch(ids, n_experts: int, weights=None, n_depts: int = 0) -> Dict[str, np.ndarray]:
+    """Group the T*k assignments by expert (counting sort, stable in the
+    assignment index a = t*k + j) and record the inverse mapping.
+
+    Returns counts[E], offsets[E+1], row_token/row_slot/row_expert[n_rows],
+    row_weight[n_rows] (if weights given), inv_perm[T*k] (row of assignment a,
+    -1 if its expert id is out of range), active[] (experts with rows,
+    ascending).  With n_depts > 0 also the department pairs: every (token,
+    department) with at least one selected expert in that department, grouped
+    by department and token-ascending inside it: dept_offsets[m+1],
+    dept_row_token[], dept_row_dept[], dept_row_scale[] (c_{t,j}, R10),
+    dept_inv[T*m] (pair row of (t, j), -1 if none), active_depts[].
+    """
+    ids = np.asarray(ids, dtype=np.int64)
+    T, k = ids.shape
+    A = T * k
+    flat = ids.reshape(-1)
+    wflat = None if weights is None else _f64(weights).reshape(-1)
+    rows = []  # (expert, assignment) pairs in row order
+    for e in range(n_experts):
+        for a in range(A):
+            if flat[a] == e:
+                rows.append((e, a))
+    counts = np.zeros(n_experts, np.int32)
+    for e, _ in rows:
+        counts[e] += 1
+    offsets = np.zeros(n_experts + 1, np.int32)
+    offsets[1:] = np.cumsum(counts)
+    inv_perm = np.full(A, -1, np.int32)
+    row_token = np.array([a // k for _, a in rows], np.int32)
+    row_slot = np.array([a % k for _, a in rows], np.int32)
+    row_expert = np.array([e for e, _ in rows], np.int32)
+    for r, (_, a) in enumerate(rows):
+        inv_perm[a] = r
+    plan = dict(counts=counts, offsets=offsets, row_token=row_token,
+                row_slot=row_slot, row_expert=row_expert, inv_perm=inv_perm,
+                active=np.array([e for e in range(n_experts) if counts[e] > 0], np.int32),
+                n_rows=len(rows), n_invalid=int(A - len(rows)))
+    if wflat is not None:
+        plan["row_weight"] = np.array([wflat[a] for _, a in rows], np.float64)
+    if n_depts:
+        g = n_experts // n_depts
+        pairs = []  # (dept, token, scale)
+        for j in range(n_depts):
+            for t in range(T):
+                members = [s for s in range(k) if 0 <= ids[t, s] < n_experts
+                           and ids[t, s] // g == j]
+                if members:
+                    scale = 0.0
+                    if wflat is not None:
+                        for s in members:  # slot order
+                            scale += wflat[t * k + s]
+                    pairs.append((j, t, scale))
+        dcounts = np.zeros(n_depts, np.int32)
+        for j, _, _ in pairs:
+            dcounts[j] += 1
+        doff = np.zeros(n_depts + 1, np.int32)
+        doff[1:] = np.cumsum(dcounts)
+        dinv = np.full(T * n_depts, -1, np.int32)
+        for q, (j, t, _) in enumerate(pairs):
+            dinv[t * n_depts + j] = q
+        plan.update(dept_counts=dcounts, dept_offsets=doff,
+                    dept_row_dept=np.array([j for j, _, _ in pairs], np.int32),
+                    dept_row_token=np.array([t for _, t, _ in pairs], np.int32),
+                    dept_row_scale=np.array([s for _, _, s in pairs], np.float64),
+                    dept_inv=dinv,
+                    active_depts=np.array([j for j in range(n_depts) if dcounts[j] > 0], np.int32),
+                    n_dept_rows=len(pairs))
+    return plan
+
+
+# ----------------------------------------------------------------------------
+# Expert FFN  [DeaMoE §2.1 Eq. (1)]; shared expert [DSMoE]
+# ----------------------------------------------------------------------------
+
+def _pick_rows(a, idx):
+    """Rows `idx` of a matrix (all rows if idx is None), widened to fp64."""
+    return _f64(a) if idx is None else _f64(a[list(idx)])
+
+
+def swiglu(x_t, w_gate, w_up, w_down, cols: Optional[Sequence[int]] = None) -> np.ndarray:
+    """MoE_i(x) of Eq. (1): the down projection of SiLU(W_gate x) * (W_up x).
+
+    With the nn.Linear layout used here (gate/up [I][d], down [d][I]) this is
+    down @ (silu(gate @ x) * (up @ x)).  `cols` restricts the output to the
+    listed entries of d (the intermediate h is always computed in full)."""
+    x = _f64(x_t)
+    g = _f64(w_gate) @ x
+    u = _f64(w_up) @ x
+    h = silu(g) * u
+    return _pick_rows(w_down, cols) @ h
+
+
+def _expert_mats(weights, e: int, dept_of: Optional[Callable[[int], int]] = None):
+    """(gate, up, down) of routed expert e; in the department slice form the
+    rows/columns of its department slice come first (R9)."""
+    if dept_of is None:
+        return weights["w_gate"][e], weights["w_up"][e], weights["w_down"][e]
+    j = dept_of(e)
+    g = np.concatenate([_f64(weights["wd_gate"][j]), _f64(weights["w_gate"][e])], axis=0)
+    u = np.concatenate([_f64(weights["wd_up"][j]), _f64(weights["w_up"][e])], axis=0)
+    dn = np.concatenate([_f64(weights["wd_down"][j]), _f64(weights["w_down"][e])], axis=1)
+    return g, u, dn
+
+
+def _dept_of_fn(n_experts: int, n_depts: int):
+    if not n_depts:
+        return None
+    g = n_experts // n_depts
+    return lambda e: e // g
+
+
+def _shared(weights, x_t, cols=None):
+    if weights.get("ws_gate") is None:
+        return 0.0
+    return swiglu(x_t, weights["ws_gate"], weights["ws_up"], weights["ws_down"], cols)
+
+
+def cast_output(y: np.ndarray, out_dtype: str):
+    """Round y to the output dtype: fp32, or bf16 with round-to-nearest-even
+    (done via the fp32 bit pattern: add 0x7FFF plus the lowest kept bit)."""
+    y32 = y.astype(np.float32)
+    if out_dtype == "f32":
+        return y32.astype(np.float64)
+    bits = y32.view(np.uint32).astype(np.uint64)
+    bits = (bits + 0x7FFF + ((bits >> 16) & 1)) & 0xFFFF0000
+    return bits.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def layer_token_output(x_t, ids_t, w_t, weights, n_experts: int, n_depts: int = 0,
+                       cols: Optional[Sequence[int]] = None) -> np.ndarray:
+    """y_t (fp64, no output rounding) of one token by the per-expert
+    definition: sum over its slots in slot order of p_j * MoE_{e_j}(x_t)
+    [Eq. (3)], plus the shared expert [DSMoE] (R7, R8).  Department experts use
+    the expanded per-expert form (R9)."""
+    dept_of = _dept_of_fn(n_experts, n_depts)
+    y = 0.0
+    for j in range(len(ids_t)):
+        g, u, dn = _expert_mats(weights, int(ids_t[j]), dept_of)
+        y = y + float(w_t[j]) * swiglu(x_t, g, u, dn, cols)
+    return y + _shared(weights, x_t, cols)
+
+
+def layer_bruteforce(x, weights, ids, w, n_experts: int, n_depts: int = 0,
+                     out_dtype: str = "f32", round_out: bool = False) -> np.ndarray:
+    """The whole layer by a loop over tokens and slots (no grouping)."""
+    T = ids.shape[0]
+    rows = [layer_token_output(x[t], ids[t], w[t], weights, n_experts, n_depts)
+            for t in range(T)]
+    y = np.stack(rows) if T else np.zeros((0, _f64(x).shape[1]))
+    return cast_output(y, out_dtype) if round_out else y
+
+
+def expert_outputs(x, weights, plan, n_experts: int, n_depts: int = 0,
+                   dept_split: bool = False):
+    """Unweighted per-row outputs of the grouped path.
+
+    row_out[r] = MoE_{row_expert[r]}(x[row_token[r]]) for every dispatched
+    row.  With dept_split (the department factored form) row_out uses the
+    private slice only, and dept_out[q] = SwiGLU of department slice
+    dept_row_dept[q] on token dept_row_token[q]; shared_out[t] = shared
+    expert on token t (None if the layer has none)."""
+    x = _f64(x)
+    T = x.shape[0]
+    dept_of = None if dept_split else _dept_of_fn(n_experts, n_depts)
+    row_out = []
+    for r in range(plan["n_rows"]):
+        e, t = int(plan["row_expert"][r]), int(plan["row_token"][r])
+        g, u, dn = _expert_mats(weights, e, dept_of)
+        row_out.append(swiglu(x[t], g, u, dn))
+    d = x.shape[1]
+    row_out = np.stack(row_out) if row_out else np.zeros((0, d))
+    dept_out = None
+    if dept_split and n_depts:
+        dept_out = []
+        for q in range(plan["n_dept_rows"]):
+            j, t = int(plan["dept_row_dept"][q]), int(plan["dept_row_token"][q])
+            dept_out.append(swiglu(x[t], weights["wd_gate"][j], weights["wd_up"][j],
+                                   weights["wd_down"][j]))
+        dept_out = np.stack(dept_out) if dept_out else np.zeros((0, d))
+    shared_out = None
+    if weights.get("ws_gate") is not None:
+        shared_out = np.stack([_shared(weights, x[t]) for t in range(T)]) if T else np.zeros((0, d))
+    return row_out, dept_out, shared_out
+
+
+def combine(plan, row_out, T: int, k: int, dept_out=None, shared_out=None,
+            n_depts: int = 0, d: Optional[int] = None) -> np.ndarray:
+    """Unpermute-and-combine [MoEInf]: y[t] = sum_j p_{t,j} row_out[inv(t,j)]
+    (slot order) + sum_j c_{t,j} dept_out[dept_inv(t,j)] (department order)
+    + shared_out[t]."""
+    row_out = _f64(row_out)
+    if d is None:
+        d = row_out.shape[1]
+    y = np.zeros((T, d))
+    for t in range(T):
+        for j in range(k):
+            r = int(plan["inv_perm"][t * k + j])
+            if r >= 0:
+                y[t] += plan["row_weight"][r] * row_out[r]
+        if dept_out is not None and n_depts:
+            for jd in range(n_depts):
+                q = int(plan["dept_inv"][t * n_depts + jd])
+                if q >= 0:
+                    y[t] += plan["dept_row_scale"][q] * _f64(dept_out[q])
+        if shared_out is not None:
+            y[t] += _f64(shared_out[t])
+    return y
+
+
+def layer_grouped(x, weights, ids, w, n_experts: int, n_depts: int = 0) -> np.ndarray:
+    """The layer by dispatch -> per-row expert outputs -> combine, expanded
+    department form."""
+    T, k = ids.shape
+    plan = dispatch(ids, n_experts, w, n_depts)
+    row_out, _, shared_out = expert_outputs(x, weights, plan, n_experts, n_depts)
+    return combine(plan, row_out, T, k, shared_out=shared_out, d=_f64(x).shape[1])
+
+
+def dept_layer_expanded(x, weights, ids, w, n_experts: int, n_depts: int) -> np.ndarray:
+    """Oracle-A: each selected expert run with its full intermediate
+    [department slice ; private slice] (R9)."""
+    return layer_bruteforce(x, weights, ids, w, n_experts, n_depts)
+
+
+def dept_layer_factored(x, weights, ids, w, n_experts: int, n_depts: int) -> np.ndarray:
+    """Oracle-B: the department slice once per (token, department), scaled by
+    c_{t,j}, plus each selected expert's private slice weighted by p
+    [DeaMoE §3.2's reuse of the department backbone, in slice form]."""
+    T, k = ids.shape
+    plan = dispatch(ids, n_experts, w, n_depts)
+    row_out, dept_out, shared_out = expert_outputs(x, weights, plan, n_experts,
+                                                   n_depts, dept_split=True)
+    return combine(plan, row_out, T, k, dept_out, shared_out, n_depts, d=_f64(x).shape[1])
+
+
+# ----------------------------------------------------------------------------
+# Weights streamed per step  [DeaMoE §3.3, Figure 2]
+# ----------------------------------------------------------------------------
+
+def loaded_weight_bytes(ids, n_experts: int, d: int, d_ff: int, bytes_per_w: int,
+                        n_depts: int = 0, d_ff_dept: int = 0, d_ff_shared: int = 0,
+                        include_router: bool = True) -> int:
+    """Bytes of weights one decode step must read, each matrix once:
+    router E*d, every distinct selected expert's three d x I matrices, the
+    shared expert, and (department form) every distinct selected
+    department's three d x S slices."""
+    ids = np.asarray(ids).reshape(-1)
+    experts = {int(e) for e in ids if 0 <= e < n_experts}
+    n = (n_experts * d if include_router else 0)
+    n += len(experts) * 3 * d * d_ff
+    n += 3 * d * d_ff_shared
+    if n_depts:
+        g = n_experts // n_depts
+        n += len({e // g for e in experts}) * 3 * d * d_ff_dept
+    return n * bytes_per_w

@@ -1,0 +1,411 @@
+"""Pins of the CPU oracle against facts the pages and mathematics fix.
+
+Nothing here compares the oracle with itself: each test checks it against a
+worked example printed on the pages, a closed form, a library routine, brute
+force over tiny inputs, or an invariant the method states.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _rand_layer(rng, d, E, I, Is=0, m=0, S=0):
+    w = {"w_router": rng.normal(0, 0.3, (E, d)).astype(np.float32),
+         "w_gate": rng.normal(0, 0.3, (E, I, d)).astype(np.float32),
+         "w_up": rng.normal(0, 0.3, (E, I, d)).astype(np.float32),
+         "w_down": rng.normal(0, 0.3, (E, d, I)).astype(np.float32)}
+    if Is:
+        w.update(ws_gate=rng.normal(0, 0.3, (Is, d)).astype(np.float32),
+                 ws_up=rng.normal(0, 0.3, (Is, d)).astype(np.float32),
+                 ws_down=rng.normal(0, 0.3, (d, Is)).astype(np.float32))
+    if m:
+        w.update(wd_gate=rng.normal(0, 0.3, (m, S, d)).astype(np.float32),
+                 wd_up=rng.normal(0, 0.3, (m, S, d)).astype(np.float32),
+                 wd_down=rng.normal(0, 0.3, (m, d, S)).astype(np.float32))
+    return w
+
+
+# ---------------------------------------------------------------------------
+# The worked example of "MoE inference engineering, clearly explained"
+# ---------------------------------------------------------------------------
+
+def _golden():
+    with open(os.path.join(GOLDEN, "worked_example.json")) as f:
+        return json.load(f)
+
+
+def test_worked_example_dispatch():
+    g = _golden()
+    ids = np.array(g["topk_ids"], np.int32)
+    plan = O.dispatch(ids, g["n_experts"], np.array(g["topk_w"]))
+    ex = g["expected"]
+    assert plan["n_rows"] == ex["assignments"]
+    assert plan["counts"].tolist() == ex["group_rows"]
+    assert plan["offsets"].tolist() == ex["expert_offsets"]
+    assert plan["row_token"].tolist() == ex["row_token"]
+    assert plan["inv_perm"].tolist() == ex["inv_perm"]
+    for e, toks in enumerate(ex["group_tokens"]):
+        lo, hi = plan["offsets"][e], plan["offsets"][e + 1]
+        assert plan["row_token"][lo:hi].tolist() == toks
+
+
+def test_worked_example_combine():
+    g = _golden()
+    ids = np.array(g["topk_ids"], np.int32)
+    w = np.array(g["topk_w"])
+    plan = O.dispatch(ids, g["n_experts"], w)
+    d = 5
+    row_out = np.stack([np.full(d, float(e + 1)) for e in plan["row_expert"]])
+    y = O.combine(plan, row_out, 4, 2)
+    want = g["expected"]["combine_constant_rows"]["y"]
+    np.testing.assert_allclose(y, np.repeat(np.array(want)[:, None], d, 1), rtol=0, atol=1e-12)
+    # the page's weights of each token sum to one
+    np.testing.assert_allclose(w.sum(1), 1.0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Top-k selection: brute force over all subsets, ties, and the 28 pairs
+# ---------------------------------------------------------------------------
+
+def _brute_topk(scores, k):
+    """The unique k-subset whose every member precedes every non-member in
+    the order (score desc, index asc); returned in that order."""
+    E = len(scores)
+    key = lambda e: (-scores[e], e)  # noqa: E731
+    found = []
+    for sub in itertools.combinations(range(E), k):
+        rest = [e for e in range(E) if e not in sub]
+        if all(key(a) < key(b) for a in sub for b in rest):
+            found.append(sorted(sub, key=key))
+    assert len(found) == 1
+    return found[0]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_matches_subset_bruteforce(seed):
+    rng = _rng(seed)
+    E, k = 7, 3
+    for _ in range(20):
+        s = rng.normal(size=E).astype(np.float32)
+        if seed % 2:  # force ties
+            s = np.round(s, 0).astype(np.float32)
+        assert O.topk_select(s[None], k)[0].tolist() == _brute_topk(s.tolist(), k)
+
+
+def test_topk_all_28_pairs_by_bias():
+    """Every one of the C(8,2) = 28 top-2 routes of an 8-expert layer is
+    reachable and selected exactly, by a selection bias on that pair."""
+    rng = _rng(1)
+    d, E, k = 16, 8, 2
+    x = rng.normal(0, 1, (1, d)).astype(np.float32)
+    wr = rng.normal(0, 0.1, (E, d)).astype(np.float32)
+    seen = set()
+    for a, b in itertools.combinations(range(E), 2):
+        bias = np.zeros(E, np.float32)
+        bias[a] = bias[b] = 100.0
+        ids, w, _, l32 = O.route(x, wr, k, O.SOFTMAX_BIAS, bias)
+        assert sorted(ids[0].tolist()) == [a, b]
+        seen.add((a, b))
+        # weights come from the unbiased logits
+        sel = l32[0, ids[0]].astype(np.float64)
+        np.testing.assert_allclose(w[0], scipy.special.softmax(sel), rtol=1e-12)
+    assert len(seen) == math.comb(8, 2) == 28
+
+
+def test_topk_ties_lower_index_wins():
+    s = np.zeros((1, 6), np.float32)
+    assert O.topk_select(s, 3)[0].tolist() == [0, 1, 2]
+    s = np.array([[1, 2, 2, 0, 2, 1]], np.float32)
+    assert O.topk_select(s, 4)[0].tolist() == [1, 2, 4, 0]
+
+
+# ---------------------------------------------------------------------------
+# Routing weights against library routines and closed forms
+# ---------------------------------------------------------------------------
+
+def test_softmax_k_equals_E_is_full_softmax():
+    rng = _rng(2)
+    x = rng.normal(0, 1, (3, 32)).astype(np.float32)
+    wr = rng.normal(0, 0.2, (8, 32)).astype(np.float32)
+    ids, w, _, l32 = O.route(x, wr, 8, O.SOFTMAX)
+    for t in range(3):
+        full = scipy.special.softmax(l32[t].astype(np.float64))
+        np.testing.assert_allclose(w[t], full[ids[t]], rtol=1e-12)
+        assert list(ids[t]) == list(np.argsort(-l32[t], kind="stable"))
+
+
+def test_softmax_not_renormalised_is_full_softmax_probability():
+    rng = _rng(3)
+    x = rng.normal(0, 1, (2, 32)).astype(np.float32)
+    wr = rng.normal(0, 0.2, (16, 32)).astype(np.float32)
+    ids, w, _, l32 = O.route(x, wr, 4, O.SOFTMAX, renormalize=False)
+    for t in range(2):
+        p = scipy.special.softmax(l32[t].astype(np.float64))
+        np.testing.assert_allclose(w[t], p[ids[t]], rtol=1e-12)
+        assert w[t].sum() < 1.0
+
+
+def test_sigmoid_bias_routing():
+    """Selection on sigmoid(l)+b; weights are the selected unbiased sigmoid
+    scores normalised to sum 1 (sigmoid from scipy's expit)."""
+    rng = _rng(4)
+    x = rng.normal(0, 1, (4, 64)).astype(np.float32)
+    wr = rng.normal(0, 0.05, (32, 64)).astype(np.float32)
+    b = rng.uniform(-0.1, 0.1, 32).astype(np.float32)
+    ids, w, sel, l32 = O.route(x, wr, 8, O.SIGMOID, b, route_scale=2.5)
+    for t in range(4):
+        s = scipy.special.expit(l32[t].astype(np.float64))
+        ranked = np.lexsort((np.arange(32), -(s.astype(np.float32) + b)))
+        assert ids[t].tolist() == ranked[:8].tolist()
+        np.testing.assert_allclose(w[t], 2.5 * s[ids[t]] / s[ids[t]].sum(), rtol=1e-12)
+        np.testing.assert_allclose(w[t].sum(), 2.5, rtol=1e-12)
+    # the bias changes the selection for at least one token of this seed
+    ids0 = O.topk_select(O.selection_scores(l32, O.SIGMOID, None), 8)
+    assert not np.array_equal(np.sort(ids0, 1), np.sort(ids, 1))
+
+
+def test_zero_input_gives_zero_output_and_tied_logits():
+    rng = _rng(5)
+    w = _rand_layer(rng, 16, 6, 8, Is=8)
+    x = np.zeros((3, 16), np.float32)
+    for fn, wsum in ((O.SOFTMAX, 1 / 3), (O.SIGMOID, 1 / 3)):
+        ids, rw, _, l32 = O.route(x, w["w_router"], 3, fn)
+        assert np.all(l32 == 0)
+        assert ids.tolist() == [[0, 1, 2]] * 3
+        np.testing.assert_allclose(rw, wsum, rtol=1e-12)
+        y = O.layer_bruteforce(x, w, ids, rw, 6)
+        assert np.all(y == 0)
+
+
+# ---------------------------------------------------------------------------
+# Expert FFN against a textbook SwiGLU written with torch.nn.functional
+# ---------------------------------------------------------------------------
+
+def test_single_expert_is_textbook_swiglu():
+    rng = _rng(6)
+    d, I = 24, 40
+    w = _rand_layer(rng, d, 1, I)
+    x = rng.normal(0, 1, (3, d)).astype(np.float32)
+    ids, rw, _, _ = O.route(x, w["w_router"], 1, O.SOFTMAX)
+    assert np.all(ids == 0) and np.allclose(rw, 1.0)
+    y = O.layer_bruteforce(x, w, ids, rw, 1)
+    X = torch.tensor(x, dtype=torch.float64)
+    Wg, Wu, Wd = (torch.tensor(w[n][0], dtype=torch.float64) for n in ("w_gate", "w_up", "w_down"))
+    ref = torch.nn.functional.linear(
+        torch.nn.functional.silu(torch.nn.functional.linear(X, Wg)) * torch.nn.functional.linear(X, Wu), Wd)
+    np.testing.assert_allclose(y, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_silu_matches_library():
+    z = np.linspace(-30, 30, 1001)
+    np.testing.assert_allclose(O.silu(z), z * scipy.special.expit(z), rtol=1e-14, atol=1e-300)
+
+
+def test_shared_expert_is_added_with_weight_one():
+    rng = _rng(7)
+    d, E, I, Is = 16, 4, 8, 12
+    w = _rand_layer(rng, d, E, I, Is=Is)
+    x = rng.normal(0, 1, (2, d)).astype(np.float32)
+    ids, rw, _, _ = O.route(x, w["w_router"], 2)
+    with_shared = O.layer_bruteforce(x, w, ids, rw, E)
+    w2 = {k: v for k, v in w.items() if not k.startswith("ws_")}
+    without = O.layer_bruteforce(x, w2, ids, rw, E)
+    X = torch.tensor(x, dtype=torch.float64)
+    F = torch.nn.functional
+    sh = F.linear(F.silu(F.linear(X, torch.tensor(w["ws_gate"], dtype=torch.float64)))
+                  * F.linear(X, torch.tensor(w["ws_up"], dtype=torch.float64)),
+                  torch.tensor(w["ws_down"], dtype=torch.float64))
+    np.testing.assert_allclose(with_shared - without, sh.numpy(), rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Brute force (per token, per slot) == grouped path (dispatch, experts, combine)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(8))
+def test_bruteforce_equals_grouped(seed):
+    rng = _rng(100 + seed)
+    E = int(rng.integers(1, 9))
+    k = int(rng.integers(1, E + 1))
+    T = int(rng.integers(0, 5))
+    d, I = 8 * int(rng.integers(1, 4)), 8 * int(rng.integers(1, 3))
+    Is = 8 if seed % 2 else 0
+    w = _rand_layer(rng, d, E, I, Is=Is)
+    x = rng.normal(0, 1, (T, d)).astype(np.float32)
+    fn = [O.SOFTMAX, O.SIGMOID, O.SOFTMAX_BIAS][seed % 3]
+    bias = rng.uniform(-0.1, 0.1, E).astype(np.float32)
+    ids, rw, _, _ = O.route(x, w["w_router"], k, fn, bias)
+    a = O.layer_bruteforce(x, w, ids, rw, E)
+    b = O.layer_grouped(x, w, ids, rw, E)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
+    plan = O.dispatch(ids, E, rw)
+    # grouping keeps every assignment (no token dropping) and is a bijection
+    assert plan["n_rows"] == T * k == int(plan["counts"].sum())
+    assert sorted(plan["inv_perm"].tolist()) == list(range(T * k))
+    for e in range(E):
+        toks = plan["row_token"][plan["offsets"][e]:plan["offsets"][e + 1]]
+        assert list(toks) == sorted(toks)
+
+
+# ---------------------------------------------------------------------------
+# Department variant: expanded per-expert form == factored department form
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(4))
+def test_department_expanded_equals_factored(seed):
+    rng = _rng(200 + seed)
+    d, E, m, S, P, k, T = 16, 8, 2 * (seed % 2 + 1), 24, 8, 3, 4
+    w = _rand_layer(rng, d, E, P, Is=8 if seed >= 2 else 0, m=m, S=S)
+    x = rng.normal(0, 1, (T, d)).astype(np.float32)
+    ids, rw, _, _ = O.route(x, w["w_router"], k, [O.SOFTMAX, O.SIGMOID][seed % 2],
+                            rng.uniform(-0.1, 0.1, E).astype(np.float32))
+    a = O.dept_layer_expanded(x, w, ids, rw, E, m)
+    b = O.dept_layer_factored(x, w, ids, rw, E, m)
+    np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-12)
+
+
+def test_department_one_expert_per_department_is_vanilla():
+    """m = E: every department holds one expert, so the layer is a vanilla
+    layer whose experts have intermediate [S ; P]."""
+    rng = _rng(300)
+    d, E, S, P, k, T = 16, 4, 8, 8, 2, 3
+    w = _rand_layer(rng, d, E, P, m=E, S=S)
+    van = {"w_router": w["w_router"],
+           "w_gate": np.concatenate([w["wd_gate"], w["w_gate"]], 1),
+           "w_up": np.concatenate([w["wd_up"], w["w_up"]], 1),
+           "w_down": np.concatenate([w["wd_down"], w["w_down"]], 2)}
+    x = rng.normal(0, 1, (T, d)).astype(np.float32)
+    ids, rw, _, _ = O.route(x, w["w_router"], k)
+    np.testing.assert_allclose(O.dept_layer_factored(x, w, ids, rw, E, E),
+                               O.layer_bruteforce(x, van, ids, rw, E), rtol=1e-10, atol=1e-12)
+
+
+def test_department_zero_private_is_weighted_department_sum():
+    """Private slices zero: y_t = sum_j c_{t,j} F_j(x_t), with c_{t,j} the
+    summed weights of the token's experts in department j."""
+    rng = _rng(301)
+    d, E, m, S, P, k, T = 16, 8, 4, 8, 8, 3, 3
+    w = _rand_layer(rng, d, E, P, m=m, S=S)
+    for n in ("w_gate", "w_up", "w_down"):
+        w[n] = np.zeros_like(w[n])
+    x = rng.normal(0, 1, (T, d)).astype(np.float32)
+    ids, rw, _, _ = O.route(x, w["w_router"], k)
+    y = O.dept_layer_expanded(x, w, ids, rw, E, m)
+    for t in range(T):
+        ref = np.zeros(d)
+        for j in range(m):
+            c = sum(rw[t, s] for s in range(k) if ids[t, s] // (E // m) == j)
+            if c:
+                ref += c * O.swiglu(x[t], w["wd_gate"][j], w["wd_up"][j], w["wd_down"][j])
+        np.testing.assert_allclose(y[t], ref, rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Output rounding: bf16 round-to-nearest-even against torch's conversion
+# ---------------------------------------------------------------------------
+
+def test_bf16_output_rounding_matches_torch():
+    rng = _rng(8)
+    v = np.concatenate([rng.normal(0, 1, 10000), rng.normal(0, 1e-3, 1000),
+                        [1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -8]])
+    ours = O.cast_output(v, "bf16")
+    ref = torch.tensor(v.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(ours, ref)
+
+
+# ---------------------------------------------------------------------------
+# Weights loaded per step: the paper's Table 1 and Figure 2 closed forms, and
+# the oracle's byte accounting against the expectation under uniform routing
+# ---------------------------------------------------------------------------
+
+# (model, k, h, hffn, n, n_dept, n', k_dept, k', FLOPs ratio, Params ratio)
+TABLE1 = [
+    ("DeepSeek-V3", 8, 7168, 2048, 256, 8, 864, 5, 10, 0.995, 0.996),
+    ("DeepSeek-V2", 6, 5120, 1536, 160, 8, 512, 5, 10, 1.010, 1.010),
+    ("Qwen3-235B-A22B", 8, 4096, 1536, 128, 8, 320, 5, 8, 1.005, 1.000),
+    ("Kimi-K2", 8, 7168, 2048, 384, 16, 1280, 5, 10, 1.000, 0.994),
+    ("Baseline-7B", 8, 1024, 384, 256, 8, 672, 4, 10, 1.014, 1.017),
+]
+
+
+@pytest.mark.parametrize("row", TABLE1, ids=[r[0] for r in TABLE1])
+def test_table1_budget_ratios(row):
+    """DeaMoE Table 1: params and FLOPs of the factorized department form
+    (department matrices h x hffn, private A matrices hffn x hffn, router
+    counted) over the baseline's.  The DeepSeek-V2 FLOPs cell does not follow
+    from the printed configuration and is checked as such."""
+    name, k, h, f, n, m, n2, kd, k2, flops_r, params_r = row
+    p_base = n * 3 * h * f + n * h
+    p_dea = m * 3 * h * f + n2 * 3 * f * f + n2 * h
+    f_base = k * 3 * h * f + n * h
+    f_dea = kd * 3 * h * f + k2 * 3 * f * f + n2 * h
+    assert round(p_dea / p_base, 3) == pytest.approx(params_r, abs=1.5e-3)
+    if name == "DeepSeek-V2":
+        assert abs(f_dea / f_base - flops_r) > 0.3
+    else:
+        assert round(f_dea / f_base, 3) == pytest.approx(flops_r, abs=1.5e-3)
+
+
+def _fig2_ratio(B, n=256, k=8, m=8, n2=864, k2=10, h=7168, f=2048):
+    base = n * (1 - (1 - k / n) ** B) * 3 * h * f
+    q = math.comb(n2 - n2 // m, k2) / math.comb(n2, k2)
+    dea = m * (1 - q ** B) * 3 * h * f + n2 * (1 - (1 - k2 / n2) ** B) * 3 * f * f
+    return dea / base
+
+
+def test_fig2_loading_ratio_range():
+    """DeaMoE Figure 2 / section 3.3: for the DeepSeek-V3-matched layer the
+    expected weights loaded per step stay between 49.1% and 62.8% of the
+    baseline's for 4 to 64 tokens."""
+    r = [_fig2_ratio(B) for B in range(4, 65)]
+    assert r[0] == pytest.approx(0.628, abs=1.5e-3)
+    assert min(r) == pytest.approx(0.491, abs=2.5e-3)
+    assert max(r) == pytest.approx(0.628, abs=1.5e-3)
+    assert 1 - min(r) == pytest.approx(0.509, abs=2.5e-3)  # "up to 50.9%" fewer
+
+
+@pytest.mark.parametrize("shape", ["vanilla", "dept"])
+def test_loaded_bytes_expectation_under_uniform_routing(shape):
+    """Mean of the oracle's per-step byte count over uniformly random routings
+    equals the closed-form expectation (distinct experts n(1-(1-k/n)^B),
+    distinct departments m(1-q^B))."""
+    rng = _rng(9)
+    if shape == "vanilla":
+        E, k, d, I, m, S, B = 128, 8, 2048, 768, 0, 0, 4
+    else:
+        E, k, d, I, m, S, B = 64, 8, 2048, 128, 8, 1024, 4
+    samples = []
+    for _ in range(4000):
+        ids = np.stack([rng.choice(E, k, replace=False) for _ in range(B)])
+        samples.append(O.loaded_weight_bytes(ids, E, d, I, 2, m, S, include_router=False))
+    samples = np.array(samples, np.float64)
+    exp = E * (1 - (1 - k / E) ** B) * 3 * d * I * 2
+    if m:
+        q = math.comb(E - E // m, k) / math.comb(E, k)
+        exp += m * (1 - q ** B) * 3 * d * S * 2
+    se = samples.std() / math.sqrt(len(samples))
+    assert abs(samples.mean() - exp) < 4 * se + 1e-9 * exp
+
+
+def test_resident_bytes_of_layer_shapes():
+    """DeepSeek-V3 experts are three [7168, 2048] matrices (about 44 MB at one
+    byte per weight); 256 of them at bf16 are about 22.5 GB."""
+    from moe_synth import SHAPES
+    s = SHAPES["deepseek_v3_d7168_e256_i2048_s2048_top8"]
+    per_expert = 3 * s.d * s.d_ff
+    assert per_expert / 1e6 == pytest.approx(44.04, abs=0.01)
+    assert s.n_experts * per_expert * 2 / 1e9 == pytest.approx(22.5, abs=0.1)
