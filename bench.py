@@ -1,0 +1,336 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of one MoE FFN layer on one MI355X.
+
+Default workload: the Qwen3-30B-A3B-shaped layer (d=2048, 128 experts,
+I=768, top-8 softmax, bf16 weights and activations, fp32 accumulation) at
+decode batches 1, 4 and 16; the headline value is the layer latency at
+batch 16.  Inputs are seeded synthetic tensors already resident in HBM.  The
+weights are replicated R times at distinct addresses and consecutive steps
+walk the replicas (like consecutive layers of a model), so that the weights a
+step streams (R x active bytes >= 1 GiB) cannot be served from the 256 MB
+Infinity Cache.
+
+Prints ONE JSON line (the driver contract) on stdout; --sweep also writes a
+line per (layer shape, batch) to --sweep-out.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer decode latency (us) + achieved HBM GB/s vs peak at batch 1/4/16"
+HBM_PEAK_GBS = 8000.0
+HEADLINE = "qwen3_30b_a3b_d2048_e128_i768_top8"
+HEADLINE_T = 16
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--batches", type=str, default="1,4,16")
+    p.add_argument("--shape", type=str, default=HEADLINE)
+    p.add_argument("--sweep", action="store_true", help="also time every other layer shape")
+    p.add_argument("--sweep-out", type=str, default="gpurun_out/sweep.jsonl")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--no-graph", action="store_true")
+    p.add_argument("--profile-pass", action="store_true",
+                   help="few steps + a calibration copy, for counter runs")
+    return p.parse_args()
+
+
+def desc_of(M, shape, max_tokens):
+    return M.layer_desc(shape.d, shape.n_experts, shape.top_k, shape.d_ff, n_depts=shape.n_depts,
+                        d_ff_dept=shape.d_ff_dept, d_ff_shared=shape.d_ff_shared,
+                        score=shape.score, renormalize=shape.renormalize,
+                        route_scale=shape.route_scale, dtype=shape.dtype, max_tokens=max_tokens)
+
+
+def gateup_bytes(shape, T, n_active, n_active_depts, n_rows, n_dept_rows):
+    """Algorithmic bytes of one gate/up launch: gate+up weights of every active
+    matrix once, the T activation rows, the fp32 h rows written."""
+    wb = 4 if shape.dtype == "f32" else 2
+    d = shape.d
+    b = n_active * 2 * shape.d_ff * d * wb
+    b += n_active_depts * 2 * shape.d_ff_dept * d * wb
+    b += (2 * shape.d_ff_shared * d * wb) if shape.d_ff_shared else 0
+    b += T * d * wb
+    b += 4 * (n_rows * shape.d_ff + n_dept_rows * shape.d_ff_dept + T * shape.d_ff_shared)
+    return b
+
+
+def down_bytes(shape, T, n_active, n_active_depts, n_rows, n_dept_rows):
+    wb = 4 if shape.dtype == "f32" else 2
+    d = shape.d
+    b = n_active * shape.d_ff * d * wb + n_active_depts * shape.d_ff_dept * d * wb
+    b += (shape.d_ff_shared * d * wb) if shape.d_ff_shared else 0
+    b += 4 * (n_rows * shape.d_ff + n_dept_rows * shape.d_ff_dept + T * shape.d_ff_shared)
+    b += 4 * d * (n_rows + n_dept_rows + (T if shape.d_ff_shared else 0))
+    return b
+
+
+class Runner:
+    """R replicas of one layer; step i runs replica i % R."""
+
+    def __init__(self, M, moe_synth, shape, T, dev, replicas=None, base=None):
+        import torch
+        self.M, self.shape, self.T, self.dev = M, shape, T, dev
+        self.desc = desc_of(M, shape, T)
+        self.base = base if base is not None else moe_synth.make_layer(shape, 0, dev)
+        self.x = moe_synth.make_tokens(shape, 0, T, dev)
+        self.y = torch.empty_like(self.x)
+        first = M.MoeLayer(self.desc, self.base, dev)
+        first(self.x, self.y)
+        torch.cuda.synchronize()
+        plan = first.plan(T)
+        self.plan = plan
+        self.n_active = int(plan["active"].size)
+        self.n_active_depts = int(plan.get("active_depts", []).__len__()) if shape.n_depts else 0
+        self.n_rows = int(plan["n_rows"])
+        self.n_dept_rows = int(plan.get("n_dept_rows", 0))
+        self.step_bytes = M.moe_loaded_weight_bytes(self.desc, self.n_active, self.n_active_depts)
+        self.step_bytes += 2 * T * shape.d * (4 if shape.dtype == "f32" else 2)
+        if replicas is None:
+            replicas = max(2, math.ceil((1 << 30) / max(1, self.step_bytes)))
+        self.R = replicas
+        self.layers = [first] + [M.MoeLayer(self.desc, moe_synth.clone_weights(self.base), dev)
+                                 for _ in range(replicas - 1)]
+        self.i = 0
+
+    def step(self, events=None):
+        self.layers[self.i % self.R](self.x, self.y, events)
+        self.i += 1
+
+    def time_eager(self, steps, warmup):
+        import torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            self.step()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps * 1e3  # us
+
+    def time_graph(self, steps, warmup):
+        """Capture R consecutive steps (one per replica) into one HIP graph and
+        replay it."""
+        import torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for _ in range(2):
+                for r in range(self.R):
+                    self.layers[r](self.x, self.y)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for r in range(self.R):
+                self.layers[r](self.x, self.y)
+        torch.cuda.synchronize()
+        reps = max(1, math.ceil(steps / self.R))
+        for _ in range(max(1, math.ceil(warmup / self.R))):
+            g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / (reps * self.R) * 1e3
+        # the graph must reproduce the eager result
+        y_graph = self.y.clone()
+        self.layers[0](self.x, self.y)
+        torch.cuda.synchronize()
+        same = bool(torch.equal(y_graph, self.y))
+        return us, reps * self.R, same
+
+    def stage_times(self, steps):
+        """Mean per-stage device time over `steps` eager steps (HIP events
+        recorded by the library on the launch stream)."""
+        import torch
+        M = self.M
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(M.N_STAGES + 1)]
+               for _ in range(steps)]
+        for e in evs:  # create the events before handing their handles over
+            for ev in e:
+                ev.record()
+        torch.cuda.synchronize()
+        for i in range(steps):
+            self.step(evs[i])
+        torch.cuda.synchronize()
+        tot = [0.0] * M.N_STAGES
+        for e in evs:
+            for s in range(M.N_STAGES):
+                tot[s] += e[s].elapsed_time(e[s + 1]) * 1e3
+        return {M.STAGE_NAMES[s]: tot[s] / steps for s in range(M.N_STAGES)}
+
+
+def cpu_baseline(shape, T, base, seconds):
+    """The oracle, as is, on the host: full decode steps of the same layer at
+    batch T on the same inputs, until `seconds` have elapsed."""
+    import numpy as np
+    import torch
+    import moe_synth
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    host = {k: v.detach().cpu() for k, v in base.items()}
+    x = moe_synth.make_tokens(shape, 0, T, "cpu")
+    n, t0 = 0, time.perf_counter()
+    while True:
+        ids, w, _, _ = O.route(x, host["w_router"], shape.top_k, shape.score,
+                               host.get("router_bias"), shape.renormalize, shape.route_scale)
+        for t in range(T):
+            O.layer_token_output(x[t], ids[t], w[t], host, shape.n_experts, shape.n_depts)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or n >= 50:
+            break
+    return {"value": el / n * 1e6, "unit": "us", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n} full decode steps of {shape.name} at batch {T} "
+                      f"(numpy fp64, {el:.1f} s)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this layer's hot path runs on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import moe_layer_decode_amd as M
+    import moe_synth
+
+    M.lib()
+    dev = torch.device("cuda:0")
+    shape = moe_synth.SHAPES[args.shape]
+    batches = [int(b) for b in args.batches.split(",")]
+    head_T = HEADLINE_T if HEADLINE_T in batches else batches[-1]
+    log(f"bench: {shape.name} batches {batches}, steps {args.steps}, warmup {args.warmup}")
+    base = moe_synth.make_layer(shape, 0, dev)
+
+    if args.profile_pass:
+        for T in batches:
+            r = Runner(M, moe_synth, shape, T, dev, base=base)
+            r.time_eager(max(10, args.steps), 2)
+        n = 1 << 28  # 1 GiB copy: counter calibration
+        a = torch.empty(n // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("profile pass done")
+        return
+
+    per_batch, head = {}, None
+    for T in batches:
+        r = Runner(M, moe_synth, shape, T, dev, base=base)
+        eager_us = r.time_eager(args.steps, args.warmup)
+        graph_us, graph_same = None, None
+        if not args.no_graph:
+            try:
+                graph_us, _, graph_same = r.time_graph(args.steps, args.warmup)
+            except Exception as ex:  # report, fall back to eager
+                log(f"graph capture failed: {ex!r}")
+        stages = r.stage_times(min(args.steps, 100))
+        us = graph_us if (graph_us is not None and graph_same) else eager_us
+        gu = gateup_bytes(shape, T, r.n_active, r.n_active_depts, r.n_rows, r.n_dept_rows)
+        dn = down_bytes(shape, T, r.n_active, r.n_active_depts, r.n_rows, r.n_dept_rows)
+        rec = {"us": round(us, 2), "eager_us": round(eager_us, 2),
+               "graph_us": None if graph_us is None else round(graph_us, 2),
+               "graph_matches_eager": graph_same,
+               "weight_bytes": r.step_bytes, "active_experts": r.n_active,
+               "active_depts": r.n_active_depts,
+               "GBps": round(r.step_bytes / us * 1e-3, 1),
+               "frac_peak": round(r.step_bytes / us * 1e-3 / HBM_PEAK_GBS, 4),
+               "stage_us": {k: round(v, 2) for k, v in stages.items()},
+               "gateup_GBps": round(gu / stages["gateup"] * 1e-3, 1) if stages["gateup"] > 0 else None,
+               "down_GBps": round(dn / stages["down"] * 1e-3, 1) if stages["down"] > 0 else None,
+               "replicas": r.R}
+        per_batch[str(T)] = rec
+        log(f"T={T}: {json.dumps(rec)}")
+        if T == head_T:
+            head = (r, us, gu, stages)
+        del r
+        torch.cuda.empty_cache()
+
+    r, us, gu, stages = head
+    head_R = r.R
+    del r, head
+    torch.cuda.empty_cache()
+    achieved = gu / stages["gateup"] * 1e-3  # GB/s
+    out = {
+        "metric": METRIC, "value": round(us, 2), "unit": "us", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(us / 1e3, 5),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": shape.dtype, "data": "synthetic",
+        "config": {"workload": f"{shape.name} MoE FFN layer decode step, batch {head_T}",
+                   "batch": head_T, "d": shape.d, "experts": shape.n_experts,
+                   "top_k": shape.top_k, "d_ff": shape.d_ff, "replicas": head_R,
+                   "timing": "hipgraph" if per_batch[str(head_T)]["graph_matches_eager"] else "eager"},
+        "hbm_GBps": per_batch[str(head_T)]["GBps"],
+        "batches": per_batch,
+        "roofline": {"bound": "hbm", "kernel": "gateup_kernel", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": gu,
+                     "launch_us": round(stages["gateup"], 2)},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline ...")
+        out["cpu_baseline"] = cpu_baseline(shape, head_T, base, args.cpu_seconds)
+    if args.sweep:
+        os.makedirs(os.path.dirname(args.sweep_out) or ".", exist_ok=True)
+        with open(args.sweep_out, "w") as f:
+            for name, sh in moe_synth.SHAPES.items():
+                if name == shape.name:
+                    continue
+                del base
+                torch.cuda.empty_cache()
+                base = moe_synth.make_layer(sh, 0, dev)
+                for T in sh.batches:
+                    rr = Runner(M, moe_synth, sh, T, dev, base=base)
+                    e_us = rr.time_eager(max(20, args.steps // 4), 5)
+                    g_us = None
+                    try:
+                        g_us, _, same = rr.time_graph(max(20, args.steps // 4), 5)
+                        g_us = g_us if same else None
+                    except Exception as ex:
+                        log(f"graph capture failed: {ex!r}")
+                    st = rr.stage_times(20)
+                    u = g_us or e_us
+                    line = {"shape": name, "batch": T, "us": round(u, 2), "eager_us": round(e_us, 2),
+                            "weight_bytes": rr.step_bytes, "active_experts": rr.n_active,
+                            "active_depts": rr.n_active_depts,
+                            "GBps": round(rr.step_bytes / u * 1e-3, 1),
+                            "stage_us": {k: round(v, 2) for k, v in st.items()}}
+                    f.write(json.dumps(line) + "\n")
+                    f.flush()
+                    log(json.dumps(line))
+                    del rr
+                    torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

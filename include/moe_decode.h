@@ -1,0 +1,237 @@
+/*
+ * moe_decode.h -- C ABI of the MI355X (gfx950) small-batch decode forward of
+ * one Mixture-of-Experts FFN layer.
+ *
+ * What the layer computes (the pages this follows):
+ *   - "DeaMoE: Efficient MoE Structure for Fast Small-Batch Decoding",
+ *     section 2.1: Eq. (1) SwiGLU expert, Eq. (2) top-k of the router
+ *     logits W_r x, Eq. (3) weighted sum of the selected experts' outputs;
+ *     section 3.2: the department backbone is computed once for all of a
+ *     department's tokens (here in slice form: an expert's intermediate is
+ *     [department-shared slice ; private slice]).
+ *   - "DeepSeekMoE Guide: Fine-Grained Experts & Dynamic Routing",
+ *     "Shared Expert Isolation" and "Auxiliary-Loss-Free Dynamic Load
+ *     Balancing": an always-on shared expert; selection on score + bias with
+ *     the weights taken from the unbiased scores.
+ *   - "MoE inference engineering, clearly explained", "How a batch becomes
+ *     expert-specific matrices" and "Local MoE execution pipeline": route ->
+ *     dispatch (group assignments by expert, keep each row's token id and an
+ *     inverse map) -> grouped expert compute -> combine (restore token order,
+ *     apply the routing weights, add).
+ *
+ * Conventions shared by every call
+ *   - Pointers named x, y, w_*, *_out, topk_*, workspace are DEVICE pointers
+ *     owned by the caller; `desc`, `weights` and `plan` structs are HOST
+ *     memory read during the call only.  The library never allocates or frees
+ *     memory and never synchronises the host: every call is asynchronous on
+ *     `stream` (a hipStream_t; NULL = the default stream) and may be captured
+ *     into a HIP graph.  Nothing is written with hipMemset.
+ *   - Every argument is validated on the host before anything is launched; a
+ *     call that returns an error has launched nothing and written nothing.
+ *     An asynchronous device fault surfaces as MOE_ERR_HIP from a later call.
+ *   - T = 0 is a valid no-op (returns MOE_OK, launches nothing).
+ *   - Inputs must be finite; NaN/Inf give undefined routing.
+ *   - Calls that share a workspace must be ordered on one stream; calls with
+ *     distinct workspaces are independent and reentrant.  There is no global
+ *     mutable state.
+ *
+ * Layouts (row-major, element counts; I = d_ff, S = d_ff_dept, Is = d_ff_shared)
+ *   x, y                 [T][d]        act_dtype
+ *   w_router             [E][d]        w_dtype          (router "centroids")
+ *   router_bias          [E]           float32, may be NULL (= zeros)
+ *   w_gate, w_up         [E][I][d]     w_dtype          (nn.Linear out x in)
+ *   w_down               [E][d][I]     w_dtype
+ *   wd_gate, wd_up       [m][S][d]     w_dtype          (department slices)
+ *   wd_down              [m][d][S]     w_dtype
+ *   ws_gate, ws_up       [Is][d]       w_dtype          (shared expert)
+ *   ws_down              [d][Is]       w_dtype
+ *   Every pointer must be 16-byte aligned; d, I, S, Is must be multiples of 8.
+ */
+#ifndef MOE_DECODE_H
+#define MOE_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,   /* bad descriptor field, NULL/misaligned pointer, T out of range */
+  MOE_ERR_UNSUPPORTED = 2,   /* valid request outside the limits below */
+  MOE_ERR_WORKSPACE = 3,     /* workspace NULL or smaller than moe_workspace_bytes() */
+  MOE_ERR_HIP = 4            /* the HIP runtime reported an error (launch or earlier fault) */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum {
+  /* rank the logits; weights = softmax over the selected logits
+   * (DeaMoE Eq. (2)-(3)) */
+  MOE_SCORE_SOFTMAX = 0,
+  /* rank fp32(sigmoid(l)) + bias; weights = the selected unbiased sigmoid
+   * scores, normalised to sum 1 */
+  MOE_SCORE_SIGMOID = 1,
+  /* rank l + bias; weights = softmax of the selected unbiased logits
+   * (the DeepSeekMoE guide's router) */
+  MOE_SCORE_SOFTMAX_BIAS = 2
+} moe_score_fn;
+
+/* Hard limits (MOE_ERR_UNSUPPORTED beyond them). */
+#define MOE_MAX_EXPERTS 2048
+#define MOE_MAX_TOP_K 32
+#define MOE_MAX_ASSIGNMENTS 4096      /* max_tokens * top_k */
+#define MOE_MAX_DEPT_PAIRS 4096       /* max_tokens * n_depts */
+
+typedef struct {
+  int32_t d_model;       /* d */
+  int32_t n_experts;     /* E, 1..MOE_MAX_EXPERTS */
+  int32_t top_k;         /* k, 1..min(E, MOE_MAX_TOP_K) */
+  int32_t d_ff;          /* I: routed expert intermediate (the private slice P in the department form) */
+  int32_t n_depts;       /* m: 0 = vanilla; else E % m == 0, expert e is in department e / (E/m) */
+  int32_t d_ff_dept;     /* S: department-shared slice width (n_depts > 0) */
+  int32_t d_ff_shared;   /* Is: always-on shared expert width, 0 = none */
+  int32_t score_fn;      /* moe_score_fn */
+  int32_t renormalize;   /* 1: weights sum to route_scale; 0: softmax probabilities / raw sigmoid */
+  float route_scale;     /* multiplies every routing weight */
+  int32_t w_dtype;       /* moe_dtype of all weight matrices */
+  int32_t act_dtype;     /* moe_dtype of x and y (MOE_F32 with MOE_F32 weights, else MOE_BF16) */
+  int32_t max_tokens;    /* largest T a workspace sized for this descriptor accepts */
+} moe_layer_desc;
+
+typedef struct {
+  const void* w_router;
+  const float* router_bias;   /* NULL = no bias */
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  const void* wd_gate;        /* department slices: required iff n_depts > 0 */
+  const void* wd_up;
+  const void* wd_down;
+  const void* ws_gate;        /* shared expert: required iff d_ff_shared > 0 */
+  const void* ws_up;
+  const void* ws_down;
+} moe_weights;
+
+/* Plan header entries (int32, device). */
+#define MOE_PLAN_N_ROWS 0          /* dispatched assignment rows */
+#define MOE_PLAN_N_ACTIVE 1        /* experts with >= 1 row */
+#define MOE_PLAN_N_DEPT_ROWS 2     /* (token, department) pairs */
+#define MOE_PLAN_N_ACTIVE_DEPTS 3  /* departments with >= 1 pair */
+#define MOE_PLAN_N_INVALID 4       /* caller-given expert ids outside [0, E) (dropped) */
+#define MOE_PLAN_HEADER_LEN 16
+
+/* The dispatch plan: device arrays inside the caller's workspace.
+ * Row order: experts ascending, and inside an expert the assignment index
+ * a = t*k + j ascending (so token-ascending).  A = max_tokens * top_k. */
+typedef struct {
+  int32_t* header;          /* [MOE_PLAN_HEADER_LEN] */
+  int32_t* counts;          /* [E]   rows per expert */
+  int32_t* offsets;         /* [E+1] exclusive prefix of counts */
+  int32_t* row_token;       /* [A]   token of each row */
+  int32_t* row_slot;        /* [A]   slot j of each row */
+  int32_t* row_expert;      /* [A]   expert of each row */
+  float* row_weight;        /* [A]   routing weight of each row */
+  int32_t* inv_perm;        /* [A]   row of assignment a (-1 if dropped) */
+  int32_t* active;          /* [E]   experts with rows, ascending (first header[N_ACTIVE]) */
+  int32_t* dept_counts;     /* [m]   pairs per department */
+  int32_t* dept_offsets;    /* [m+1] */
+  int32_t* dept_row_token;  /* [Pm]  token of each pair (Pm = max_tokens * min(m, k)) */
+  int32_t* dept_row_dept;   /* [Pm]  department of each pair */
+  float* dept_row_scale;    /* [Pm]  c_{t,j}: sum of the token's weights over its experts in department j */
+  int32_t* dept_inv;        /* [max_tokens*m] pair of (t, j), -1 if none */
+  int32_t* active_depts;    /* [m]   departments with pairs, ascending */
+  int32_t n_tokens;         /* T the plan was built for (host copy) */
+} moe_plan;
+
+/* Stage events for moe_layer_decode: stage_events[i] is recorded on the
+ * stream right before stage i is launched, stage_events[MOE_N_STAGES] after
+ * the last one (a stage fused into its predecessor gets an empty interval). */
+#define MOE_STAGE_ROUTE 0     /* router logits + top-k + weights */
+#define MOE_STAGE_DISPATCH 1  /* counting sort, inverse map, department pairs */
+#define MOE_STAGE_GATEUP 2    /* grouped gate/up GEMV with SiLU(g)*u */
+#define MOE_STAGE_DOWN 3      /* grouped down GEMV */
+#define MOE_STAGE_COMBINE 4   /* weighted combine to token order */
+#define MOE_N_STAGES 5
+
+/* Bytes of device workspace moe_layer_decode (and every other call) needs for
+ * `desc` (T <= desc->max_tokens).  0 if the descriptor is invalid. */
+size_t moe_workspace_bytes(const moe_layer_desc* desc);
+
+/* Host-only check of a descriptor (no HIP call). */
+moe_status moe_validate_desc(const moe_layer_desc* desc);
+
+/* Host-only: fill `plan` with the device addresses of the plan arrays inside
+ * `workspace` (the arrays moe_dispatch / moe_layer_decode write), for T tokens. */
+moe_status moe_plan_from_workspace(const moe_layer_desc* desc, void* workspace,
+                                   size_t ws_bytes, int32_t T, moe_plan* plan);
+
+/* Router: DeaMoE Eq. (2) plus the weights of Eq. (3).
+ * logits l[t][e] = sum_c x[t][c] * w_router[e][c] (fp32 accumulate); the
+ * selection score per score_fn; the k best per token, slots ordered by
+ * (score desc, expert index asc) so ties go to the lower index; weights per
+ * score_fn, times route_scale.
+ * Writes topk_ids int32[T][k], topk_w float[T][k] and, if sel_scores is not
+ * NULL, sel_scores float[T][E] = the exact fp32 values that were ranked.
+ * Uses the logits region of `workspace`. */
+moe_status moe_route(const moe_layer_desc* desc, const void* x, const void* w_router,
+                     const float* router_bias, int32_t T, int32_t* topk_ids,
+                     float* topk_w, float* sel_scores, void* workspace,
+                     size_t ws_bytes, void* stream);
+
+/* Dispatch ("How a batch becomes expert-specific matrices"): group the T*k
+ * assignments (topk_ids[t][j], topk_w[t][j]) by expert, stable in a = t*k+j,
+ * with the inverse map, the active-expert list and, for n_depts > 0, the
+ * (token, department) pairs with c_{t,j}.  Any ids are accepted; ids outside
+ * [0, E) are dropped and counted in header[MOE_PLAN_N_INVALID].  The plan is
+ * written into `workspace`; `plan` (host) receives its addresses. */
+moe_status moe_dispatch(const moe_layer_desc* desc, const int32_t* topk_ids,
+                        const float* topk_w, int32_t T, void* workspace,
+                        size_t ws_bytes, moe_plan* plan, void* stream);
+
+/* Grouped expert FFN (DeaMoE Eq. (1)), unweighted, for a plan from
+ * moe_dispatch on the same workspace:
+ *   row_out[r][:]    = expert row_expert[r] on token row_token[r]      float [n_rows][d]
+ *                      (the private slice only when n_depts > 0)
+ *   dept_out[q][:]   = department slice dept_row_dept[q] on its token  float [n_dept_rows][d]
+ *                      (required iff n_depts > 0)
+ *   shared_out[t][:] = shared expert on token t                        float [T][d]
+ *                      (required iff d_ff_shared > 0)
+ * The intermediates h = SiLU(gate x) * (up x) stay fp32 in `workspace`. */
+moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_weights* weights,
+                          const void* x, int32_t T, const moe_plan* plan,
+                          void* workspace, size_t ws_bytes, float* row_out,
+                          float* dept_out, float* shared_out, void* stream);
+
+/* Combine: y[t] = sum_j topk weight(t,j) * row_out[inv_perm[t*k+j]]  (slot order)
+ *               + sum_J c_{t,J} * dept_out[dept_inv[t*m+J]]           (J ascending)
+ *               + shared_out[t]
+ * written in act_dtype (bf16: round to nearest even). */
+moe_status moe_combine(const moe_layer_desc* desc, const moe_plan* plan,
+                       const float* row_out, const float* dept_out,
+                       const float* shared_out, int32_t T, void* y, void* stream);
+
+/* The fused decode step: route -> dispatch -> grouped gate/up -> grouped
+ * down with the combine, y[T][d] in act_dtype.  `stage_events` (NULL or an
+ * array of MOE_N_STAGES + 1 hipEvent_t created by the caller) brackets the
+ * stages for timing. */
+moe_status moe_layer_decode(const moe_layer_desc* desc, const moe_weights* weights,
+                            const void* x, int32_t T, void* y, void* workspace,
+                            size_t ws_bytes, void* const* stage_events, void* stream);
+
+/* Static text for a status code. */
+const char* moe_status_string(moe_status status);
+
+/* Bytes of weights one step streams for the given active counts: router,
+ * n_active routed experts, n_active_depts department slices, the shared
+ * expert (each matrix read once).  Host-only. */
+uint64_t moe_loaded_weight_bytes(const moe_layer_desc* desc, int32_t n_active,
+                                 int32_t n_active_depts);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_DECODE_H */

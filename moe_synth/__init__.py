@@ -178,11 +178,12 @@ def make_tokens(shape: LayerShape, seed: int, T: int, device="cpu") -> torch.Ten
     return normal(seed, _TID["x"], (T, src.d), src.x_std, shape.torch_dtype, device)
 
 
-def make_layer(shape: LayerShape, seed: int, device="cpu") -> Dict[str, torch.Tensor]:
+def make_layer(shape: LayerShape, seed: int, device="cpu",
+               router_only: bool = False) -> Dict[str, torch.Tensor]:
     """All weights of one layer, in the layout the library takes:
     router [E][d]; gate/up [E][I][d]; down [E][d][I] (nn.Linear out x in);
     department gate/up [m][S][d], down [m][d][S]; shared gate/up [Is][d],
-    down [d][Is]; bias fp32 [E]."""
+    down [d][Is]; bias fp32 [E].  router_only: just router and bias."""
     dt = shape.torch_dtype
     src = SHAPES[shape.data_seed_of] if shape.data_seed_of else shape
     E, d, I = shape.n_experts, shape.d, shape.d_ff
@@ -192,6 +193,8 @@ def make_layer(shape: LayerShape, seed: int, device="cpu") -> Dict[str, torch.Te
         w["router_bias"] = uniform(seed, _TID["router_bias"], (E,),
                                    -src.bias_range, src.bias_range,
                                    torch.float32, device)
+    if router_only:
+        return w
     # Expert tensors of a transformed layer draw from their own seed space so
     # they are not a slice of the source layer's experts.
     eseed = seed if not shape.data_seed_of else seed + 7919

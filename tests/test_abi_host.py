@@ -1,0 +1,165 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+symbol, and validates descriptors without touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_layer_decode_amd as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    with open(os.path.join(ROOT, "include", "moe_decode.h")) as f:
+        src = f.read()
+    return sorted(set(re.findall(r"^(?:const char\*|size_t|moe_status|uint64_t)\s+(moe_\w+)\(",
+                                 src, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(M.lib_path()):
+        import moe_layer_decode_amd.build as B
+        B.build()
+    return M.lib()
+
+
+def test_header_declares_the_calls():
+    decl = _declared_functions()
+    for name in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
+                 "moe_layer_decode", "moe_workspace_bytes", "moe_status_string"):
+        assert name in decl
+    assert sorted(M.EXPORTED_SYMBOLS) == decl
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert M.moe_status_string(s)
+    assert M.moe_status_string(99) == "unknown status"
+
+
+def _desc(**kw):
+    base = dict(d_model=2048, n_experts=128, top_k=8, d_ff=768)
+    base.update(kw)
+    d, E, k, I = base.pop("d_model"), base.pop("n_experts"), base.pop("top_k"), base.pop("d_ff")
+    return M.layer_desc(d, E, k, I, **base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), M.MOE_OK),
+    (dict(d_model=2047), M.MOE_ERR_INVALID_ARG),
+    (dict(d_model=0), M.MOE_ERR_INVALID_ARG),
+    (dict(top_k=0), M.MOE_ERR_INVALID_ARG),
+    (dict(top_k=129), M.MOE_ERR_INVALID_ARG),
+    (dict(d_ff=100), M.MOE_ERR_INVALID_ARG),
+    (dict(n_depts=3, d_ff_dept=64), M.MOE_ERR_INVALID_ARG),       # 128 % 3 != 0
+    (dict(n_depts=8, d_ff_dept=0), M.MOE_ERR_INVALID_ARG),
+    (dict(n_depts=8, d_ff_dept=1024), M.MOE_OK),
+    (dict(d_ff_shared=12), M.MOE_ERR_INVALID_ARG),
+    (dict(max_tokens=0), M.MOE_ERR_INVALID_ARG),
+    (dict(max_tokens=513), M.MOE_ERR_UNSUPPORTED),               # T*k > 4096
+    (dict(n_experts=4096, top_k=8), M.MOE_ERR_UNSUPPORTED),
+    (dict(top_k=33), M.MOE_ERR_UNSUPPORTED),
+    (dict(score="sigmoid", route_scale=float("inf")), M.MOE_ERR_INVALID_ARG),
+])
+def test_descriptor_validation(lib, kw, status):
+    assert M.moe_validate_desc(_desc(**kw)) == status
+    if status != M.MOE_OK:
+        assert lib.moe_workspace_bytes(ctypes.byref(_desc(**kw))) == 0
+
+
+def test_mixed_dtypes_unsupported(lib):
+    d = _desc()
+    d.w_dtype, d.act_dtype = M.MOE_BF16, M.MOE_F32
+    assert M.moe_validate_desc(d) == M.MOE_ERR_UNSUPPORTED
+
+
+def test_workspace_grows_with_tokens_and_features(lib):
+    small = M.moe_workspace_bytes(_desc(max_tokens=1))
+    big = M.moe_workspace_bytes(_desc(max_tokens=32))
+    assert 0 < small < big
+    assert M.moe_workspace_bytes(_desc(d_ff_shared=2048)) > M.moe_workspace_bytes(_desc())
+    assert M.moe_workspace_bytes(_desc(n_depts=8, d_ff_dept=1024)) > M.moe_workspace_bytes(_desc())
+    assert big % 256 == 0
+
+
+def test_calls_reject_bad_arguments_before_any_launch(lib):
+    """Errors found on the host return before any HIP call: these run on a
+    machine without a GPU."""
+    d = _desc()
+    P = M.Plan()
+    nul = None
+    # T out of range
+    assert lib.moe_dispatch(ctypes.byref(d), 256, 256, 33, 4096, 1 << 30, ctypes.byref(P), nul) \
+        == M.MOE_ERR_INVALID_ARG
+    # misaligned ids pointer
+    assert lib.moe_dispatch(ctypes.byref(d), 258, 256, 1, 4096, 1 << 30, ctypes.byref(P), nul) \
+        == M.MOE_ERR_INVALID_ARG
+    # workspace too small / misaligned
+    assert lib.moe_dispatch(ctypes.byref(d), 256, 256, 1, 4096, 16, ctypes.byref(P), nul) \
+        == M.MOE_ERR_WORKSPACE
+    assert lib.moe_dispatch(ctypes.byref(d), 256, 256, 1, 4097, 1 << 30, ctypes.byref(P), nul) \
+        == M.MOE_ERR_WORKSPACE
+    # invalid descriptor wins over everything
+    bad = _desc(d_model=7)
+    assert lib.moe_route(ctypes.byref(bad), 256, 256, None, 1, 256, 256, None, 4096, 1 << 30,
+                         nul) == M.MOE_ERR_INVALID_ARG
+    # softmax mode takes no selection bias
+    assert lib.moe_route(ctypes.byref(d), 256, 256, 512, 1, 256, 256, None, 4096, 1 << 30,
+                         nul) == M.MOE_ERR_INVALID_ARG
+    # missing expert weights
+    W = M.Weights(w_router=256)
+    assert lib.moe_layer_decode(ctypes.byref(d), ctypes.byref(W), 256, 1, 512, 4096, 1 << 30,
+                                None, nul) == M.MOE_ERR_INVALID_ARG
+    # department layer without department weights
+    dd = _desc(n_depts=8, d_ff_dept=1024)
+    W = M.Weights(w_router=256, w_gate=256, w_up=256, w_down=256)
+    assert lib.moe_layer_decode(ctypes.byref(dd), ctypes.byref(W), 256, 1, 512, 4096, 1 << 30,
+                                None, nul) == M.MOE_ERR_INVALID_ARG
+
+
+def test_zero_tokens_is_a_noop(lib):
+    d = _desc()
+    P = M.Plan()
+    ws = M.moe_workspace_bytes(d)
+    assert lib.moe_dispatch(ctypes.byref(d), 256, 256, 0, 4096, ws, ctypes.byref(P), None) == M.MOE_OK
+    assert P.n_tokens == 0
+    W = M.Weights(w_router=256, w_gate=256, w_up=256, w_down=256)
+    assert lib.moe_layer_decode(ctypes.byref(d), ctypes.byref(W), 256, 0, 512, 4096, ws,
+                                None, None) == M.MOE_OK
+
+
+def test_plan_addresses_inside_workspace(lib):
+    d = _desc(n_depts=8, d_ff_dept=1024)
+    ws = M.moe_workspace_bytes(d)
+    P = M.Plan()
+    base = 1 << 20
+    assert lib.moe_plan_from_workspace(ctypes.byref(d), base, ws, 4, ctypes.byref(P)) == M.MOE_OK
+    addrs = [getattr(P, n) for n in M._PLAN_ARRAYS]
+    assert all(base <= a < base + ws for a in addrs)
+    assert len(set(addrs)) == len(addrs)
+
+
+def test_loaded_weight_bytes(lib):
+    d = _desc()
+    per_expert = 3 * 2048 * 768 * 2
+    router = 128 * 2048 * 2
+    assert M.moe_loaded_weight_bytes(d, 8) == router + 8 * per_expert
+    dd = _desc(n_experts=64, d_ff=128, n_depts=8, d_ff_dept=1024)
+    assert M.moe_loaded_weight_bytes(dd, 10, 3) == 2 * (64 * 2048 + 10 * 3 * 2048 * 128
+                                                         + 3 * 3 * 2048 * 1024)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(M, "_LIB", None)
+    monkeypatch.setattr(M, "lib_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError, match="no CPU fallback"):
+        M.moe_validate_desc(_desc())

@@ -1,0 +1,430 @@
+"""Parity of the HIP path with the CPU oracle, through the C ABI, on seeded
+inputs of every layer shape: router and top-k, dispatch plan, expert FFN,
+combine and the fused decode step; ties, ragged shapes and edge cases."""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import moe_layer_decode_amd as M
+import moe_synth
+import oracle as O
+from _util import (TAU, assert_close, desc_of, gpu_ids_from_plan, oracle_route, reference_ids,
+                   to_np)
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+SH = moe_synth.SHAPES
+TINY = "tiny_d256_e8_i128_top2"
+QWEN = "qwen3_30b_a3b_d2048_e128_i768_top8"
+DSV3 = "deepseek_v3_d7168_e256_i2048_s2048_top8"
+DEA7 = "deamoe_7b_d2048_e64_m8_s1024_p128_top8"
+DEAV3 = "deamoe_dsv3_d7168_e256_m32_s1792_p256_top8"
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")
+
+
+def setup_module(module):
+    M.lib()  # fail loudly if the HIP library is missing
+
+
+_LAYERS = {}
+
+
+def gpu_layer(name, seed):
+    """Whole layer on the device (cached: the large shapes take seconds)."""
+    key = (name, seed)
+    if key not in _LAYERS:
+        if len(_LAYERS) >= 2:  # keep device memory bounded
+            _LAYERS.clear()
+            torch.cuda.empty_cache()
+        _LAYERS[key] = moe_synth.make_layer(SH[name], seed, DEV)
+    return _LAYERS[key]
+
+
+# ---------------------------------------------------------------------------
+# Router: top-k ids bit-exact, weights, selection scores
+# ---------------------------------------------------------------------------
+
+def run_route(desc, x, w, T, with_sel=True):
+    k, E = desc.top_k, desc.n_experts
+    ids = torch.full((T, k), -7, dtype=torch.int32, device=DEV)
+    tw = torch.full((T, k), -7.0, dtype=torch.float32, device=DEV)
+    sel = torch.full((T, E), -7.0, dtype=torch.float32, device=DEV) if with_sel else None
+    ws = M.alloc_workspace(desc, DEV)
+    M.moe_route(desc, x, w["w_router"], w.get("router_bias"), ids, tw, ws, sel)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), tw.cpu().numpy().astype(np.float64), (None if sel is None else sel.cpu().numpy())
+
+
+@pytest.mark.parametrize("name", [TINY, QWEN, DSV3, DEA7, DEAV3])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_route_parity(name, seed):
+    shape = SH[name]
+    w = moe_synth.make_layer(shape, seed, DEV, router_only=True)
+    Tmax = max(shape.batches)
+    desc = desc_of(shape)
+    xall = moe_synth.make_tokens(shape, seed, Tmax, DEV)
+    o_ids_all, o_w_all, o_sel_all, o_l32 = oracle_route(shape, xall.cpu(), {k: v.cpu() for k, v in w.items()})
+    near_total = 0
+    for T in shape.batches:
+        x = xall[:T].contiguous()
+        g_ids, g_w, g_sel = run_route(desc, x, w, T)
+        # selection on the GPU's own scores is exact: same ids, same slot order
+        assert np.array_equal(O.topk_select(g_sel, shape.top_k), g_ids)
+        # the scores agree with the oracle's to tau
+        o_sel = o_sel_all[:T]
+        tol = TAU * np.maximum(1.0, np.abs(o_sel))
+        assert np.all(np.abs(g_sel.astype(np.float64) - o_sel) <= tol)
+        ids, near = reference_ids(o_ids_all[:T], o_sel, g_ids, shape.top_k)
+        near_total += int(near.sum())
+        # weights of the selected experts, from the oracle's logits
+        o_w = O.routing_weights(o_l32[:T], g_ids, shape.score, shape.renormalize, shape.route_scale)
+        np.testing.assert_allclose(g_w, o_w, rtol=0, atol=1e-5)
+        if shape.renormalize:
+            np.testing.assert_allclose(g_w.sum(1), shape.route_scale, atol=1e-5)
+    print(f"{name} seed {seed}: near-tie tokens {near_total}")
+
+
+@pytest.mark.parametrize("score", ["softmax", "sigmoid", "softmax_bias"])
+def test_route_ties_go_to_lower_index(score):
+    """Duplicated router rows give bitwise-equal scores; the lower expert index
+    takes the earlier slot.  An all-zero router ties every expert."""
+    E, d, k, T = 96, 264, 6, 5
+    g = torch.Generator().manual_seed(3)
+    wr = (torch.randn(E, d, generator=g) * 0.05)
+    for a, b in ((3, 70), (10, 11), (40, 95)):
+        wr[b] = wr[a]
+    x = torch.randn(T, d, generator=g)
+    bias = torch.zeros(E) if score != "softmax" else None
+    desc = M.layer_desc(d, E, k, 64, score=score, dtype="f32", max_tokens=T)
+    w = {"w_router": wr.to(DEV), "router_bias": None if bias is None else bias.to(DEV)}
+    g_ids, g_w, g_sel = run_route(desc, x.to(DEV), w, T)
+    for a, b in ((3, 70), (10, 11), (40, 95)):
+        assert np.array_equal(g_sel[:, a], g_sel[:, b])
+    assert np.array_equal(O.topk_select(g_sel, k), g_ids)
+    for t in range(T):
+        ids = list(g_ids[t])
+        for a, b in ((3, 70), (10, 11), (40, 95)):
+            if b in ids:
+                assert a in ids and ids.index(a) < ids.index(b)
+    # all-zero router: experts 0..k-1, equal weights
+    w0 = {"w_router": torch.zeros(E, d, device=DEV), "router_bias": w["router_bias"]}
+    g_ids, g_w, _ = run_route(desc, x.to(DEV), w0, T)
+    assert g_ids.tolist() == [list(range(k))] * T
+    np.testing.assert_allclose(g_w, 1.0 / k, atol=1e-6)
+    if score != "softmax":
+        # zero logits: selection follows the bias alone
+        bias2 = torch.zeros(E)
+        bias2[[5, 17, 33, 60, 61, 90]] = torch.tensor([0.3, 0.9, 0.1, 0.5, 0.7, 0.2])
+        w0["router_bias"] = bias2.to(DEV)
+        g_ids, g_w, _ = run_route(desc, x.to(DEV), w0, T)
+        assert g_ids.tolist() == [[17, 61, 60, 5, 90, 33]] * T
+        np.testing.assert_allclose(g_w, 1.0 / k, atol=1e-6)
+
+
+def test_route_k_equals_E_and_not_renormalised():
+    E, d, T = 8, 256, 4
+    g = torch.Generator().manual_seed(4)
+    wr, x = torch.randn(E, d, generator=g) * 0.05, torch.randn(T, d, generator=g)
+    for k, renorm, score in ((8, True, "softmax"), (3, False, "softmax"), (3, False, "sigmoid")):
+        desc = M.layer_desc(d, E, k, 64, dtype="f32", max_tokens=T, renormalize=renorm,
+                            score=score)
+        g_ids, g_w, _ = run_route(desc, x.to(DEV), {"w_router": wr.to(DEV)}, T)
+        o_ids, o_w, _, _ = O.route(x, wr, k, score, None, renorm)
+        assert np.array_equal(g_ids, o_ids)
+        np.testing.assert_allclose(g_w, o_w, atol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# Dispatch: bit-exact plan
+# ---------------------------------------------------------------------------
+
+def run_dispatch(desc, ids, tw):
+    ws = M.alloc_workspace(desc, DEV)
+    plan = M.moe_dispatch(desc, torch.as_tensor(ids, dtype=torch.int32).to(DEV).contiguous(),
+                          torch.as_tensor(tw, dtype=torch.float32).to(DEV).contiguous(), ws)
+    return plan, ws, M.plan_to_host(desc, plan, ws)
+
+
+def assert_plan_equal(g, o, m):
+    for key in ("counts", "offsets", "row_token", "row_slot", "row_expert", "inv_perm", "active"):
+        assert np.array_equal(g[key], np.asarray(o[key])), key
+    assert g["n_rows"] == o["n_rows"] and g["n_invalid"] == o["n_invalid"]
+    np.testing.assert_array_equal(g["row_weight"], np.asarray(o["row_weight"], np.float32))
+    if m:
+        for key in ("dept_counts", "dept_offsets", "dept_row_token", "dept_row_dept", "dept_inv",
+                    "active_depts"):
+            assert np.array_equal(g[key], np.asarray(o[key])), key
+        np.testing.assert_allclose(g["dept_row_scale"], o["dept_row_scale"], rtol=1e-6, atol=1e-7)
+
+
+def test_dispatch_worked_example():
+    with open(GOLDEN) as f:
+        gd = json.load(f)
+    desc = M.layer_desc(8, gd["n_experts"], gd["top_k"], 8, dtype="f32", max_tokens=4)
+    ids, tw = np.array(gd["topk_ids"]), np.array(gd["topk_w"])
+    plan, ws, g = run_dispatch(desc, ids, tw)
+    ex = gd["expected"]
+    assert g["offsets"].tolist() == ex["expert_offsets"]
+    assert g["row_token"].tolist() == ex["row_token"]
+    assert g["inv_perm"].tolist() == ex["inv_perm"]
+    assert g["counts"].tolist() == ex["group_rows"]
+    # combine with expert n's row output = n * ones gives the page's sums
+    d = 8
+    row_out = torch.tensor(np.repeat((g["row_expert"] + 1.0)[:, None], d, 1), dtype=torch.float32, device=DEV)
+    y = torch.empty(4, d, dtype=torch.float32, device=DEV)
+    M.moe_combine(desc, plan, row_out, None, None, y)
+    want = ex["combine_constant_rows"]["y"]
+    np.testing.assert_allclose(y.cpu().numpy(), np.repeat(np.array(want)[:, None], d, 1), atol=1e-6)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_dispatch_random_plans(seed):
+    rng = np.random.default_rng(seed)
+    E, k, T, m = [(8, 2, 4, 0), (128, 8, 16, 0), (64, 8, 16, 8), (256, 8, 32, 32),
+                  (16, 4, 7, 4), (2048, 8, 32, 0)][seed]
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    tw = rng.random((T, k)).astype(np.float32)
+    desc = M.layer_desc(8, E, k, 8, n_depts=m, d_ff_dept=8 if m else 0, dtype="f32", max_tokens=T)
+    _, _, g = run_dispatch(desc, ids, tw)
+    assert_plan_equal(g, O.dispatch(ids, E, tw.astype(np.float64), m), m)
+
+
+def test_dispatch_duplicates_and_invalid_ids():
+    """Caller-given ids: a repeated expert inside a token keeps slot order;
+    ids outside [0, E) are dropped and counted."""
+    E, k, T = 6, 3, 4
+    ids = np.array([[1, 1, 4], [5, -1, 0], [2, 6, 2], [0, 1, 2]], np.int32)
+    tw = np.arange(12, dtype=np.float32).reshape(T, k) / 10
+    desc = M.layer_desc(8, E, k, 8, n_depts=3, d_ff_dept=8, dtype="f32", max_tokens=T)
+    _, _, g = run_dispatch(desc, ids, tw)
+    o = O.dispatch(ids, E, tw.astype(np.float64), 3)
+    assert o["n_invalid"] == 2
+    assert_plan_equal(g, o, 3)
+
+
+def test_dispatch_max_assignments():
+    E, k, T = 256, 8, 512  # 4096 assignments, the limit
+    rng = np.random.default_rng(9)
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    tw = rng.random((T, k)).astype(np.float32)
+    desc = M.layer_desc(8, E, k, 8, dtype="f32", max_tokens=T)
+    _, _, g = run_dispatch(desc, ids, tw)
+    assert_plan_equal(g, O.dispatch(ids, E, tw.astype(np.float64)), 0)
+
+
+# ---------------------------------------------------------------------------
+# Expert FFN and combine as separate calls
+# ---------------------------------------------------------------------------
+
+def _rand_weights(seed, d, E, I, m=0, S=0, Is=0, dtype=torch.float32, scale=0.05):
+    g = torch.Generator().manual_seed(seed)
+    r = lambda *s: (torch.randn(*s, generator=g) * scale).to(dtype).to(DEV)  # noqa: E731
+    w = {"w_router": r(E, d), "w_gate": r(E, I, d), "w_up": r(E, I, d), "w_down": r(E, d, I)}
+    if m:
+        w.update(wd_gate=r(m, S, d), wd_up=r(m, S, d), wd_down=r(m, d, S))
+    if Is:
+        w.update(ws_gate=r(Is, d), ws_up=r(Is, d), ws_down=r(d, Is))
+    return w
+
+
+@pytest.mark.parametrize("case", [
+    # (d, E, k, I, m, S, Is, T, dtype): several tiles, ragged tails, groups of >4, >8, >16 rows
+    (256, 8, 2, 128, 0, 0, 0, 4, "f32"),
+    (264, 6, 3, 40, 0, 0, 24, 5, "f32"),
+    (520, 4, 2, 136, 2, 72, 0, 20, "f32"),
+    (1024, 16, 4, 96, 4, 160, 64, 9, "bf16"),
+    (776, 3, 3, 24, 0, 0, 16, 33, "bf16"),
+])
+def test_expert_ffn_and_combine_parity(case):
+    d, E, k, I, m, S, Is, T, dt = case
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    w = _rand_weights(sum(case[:8]), d, E, I, m, S, Is, tdt)
+    g = torch.Generator().manual_seed(7)
+    x = torch.randn(T, d, generator=g).to(tdt).to(DEV)
+    desc = M.layer_desc(d, E, k, I, n_depts=m, d_ff_dept=S, d_ff_shared=Is, dtype=dt,
+                        max_tokens=T + 3)
+    rng = np.random.default_rng(case[0])
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    if T > 16:
+        ids[:, 0] = 0  # one expert with > 16 rows
+    tw = rng.random((T, k)).astype(np.float32)
+    plan, ws, gp = run_dispatch(desc, ids, tw)
+    op = O.dispatch(ids, E, tw.astype(np.float64), m)
+    assert_plan_equal(gp, op, m)
+    row_out = torch.full((T * k, d), float("nan"), device=DEV)
+    dept_out = torch.full((max(1, op.get("n_dept_rows", 0)), d), float("nan"), device=DEV) if m else None
+    shared_out = torch.full((T, d), float("nan"), device=DEV) if Is else None
+    M.moe_expert_ffn(desc, w, x, plan, ws, row_out, dept_out, shared_out)
+    wc = {kk: v.cpu() for kk, v in w.items()}
+    o_row, o_dept, o_sh = O.expert_outputs(x.cpu(), wc, op, E, m, dept_split=bool(m))
+    # row outputs are fp32 whatever the input dtype: fp32 tolerance
+    assert_close(to_np(row_out[:op["n_rows"]]), o_row, "f32", "row_out")
+    if m:
+        assert_close(to_np(dept_out[:op["n_dept_rows"]]), o_dept, "f32", "dept_out")
+    if Is:
+        assert_close(to_np(shared_out), o_sh, "f32", "shared_out")
+    y = torch.empty(T, d, dtype=tdt, device=DEV)
+    M.moe_combine(desc, plan, row_out, dept_out, shared_out, y)
+    # combine checked against the oracle combine of the GPU's own row outputs
+    y_ref = O.combine(op, to_np(row_out[:op["n_rows"]]), T, k,
+                      None if not m else to_np(dept_out[:op["n_dept_rows"]]),
+                      None if not Is else to_np(shared_out), m, d)
+    floor = 1e-6 * np.abs(y_ref).max()
+    if dt == "bf16":  # one bf16 ulp where the fp32 sum straddles a rounding boundary
+        np.testing.assert_allclose(to_np(y), O.cast_output(y_ref, "bf16"), rtol=2 ** -7, atol=floor)
+    else:
+        np.testing.assert_allclose(to_np(y), y_ref, rtol=1e-6, atol=floor)
+
+
+# ---------------------------------------------------------------------------
+# The fused decode step on every layer shape
+# ---------------------------------------------------------------------------
+
+def run_layer(desc, w, x):
+    layer = M.MoeLayer(desc, w, DEV)
+    y = torch.full_like(x, float("nan"))
+    layer(x, y)
+    torch.cuda.synchronize()
+    return y, layer
+
+
+def check_layer(name, seed, T, sample_tokens=None):
+    shape = SH[name]
+    w = gpu_layer(name, seed)
+    desc = desc_of(shape)
+    x = moe_synth.make_tokens(shape, seed, T, DEV)
+    y, layer = run_layer(desc, w, x)
+    g_plan = layer.plan(T)
+    g_ids, g_w = gpu_ids_from_plan(g_plan, T, shape.top_k)
+    xc = x.cpu()
+    o_ids, _, o_sel, o_l32 = O.route(xc, w["w_router"].cpu(), shape.top_k, shape.score,
+                                      None if w.get("router_bias") is None else w["router_bias"].cpu(),
+                                      shape.renormalize, shape.route_scale)
+    ids, near = reference_ids(o_ids, o_sel, g_ids, shape.top_k)
+    o_w = O.routing_weights(o_l32, ids, shape.score, shape.renormalize, shape.route_scale)
+    np.testing.assert_allclose(g_w, o_w, atol=1e-5)
+    # the plan is the oracle's dispatch of the selected ids
+    op = O.dispatch(g_ids, shape.n_experts, g_w.astype(np.float64), shape.n_depts)
+    assert_plan_equal(g_plan, op, shape.n_depts)
+    toks = range(T) if sample_tokens is None else sorted(set(t for t in sample_tokens if t < T))
+    yg = to_np(y)
+    assert np.isfinite(yg).all()
+    ref = np.stack([O.layer_token_output(xc[t], ids[t], o_w[t], w, shape.n_experts, shape.n_depts)
+                    for t in toks])
+    emax, rmax = assert_close(yg[list(toks)], ref, shape.dtype, f"{name} T={T}")
+    print(f"{name} seed={seed} T={T}: max|err| {emax:.3e} (max|ref| {rmax:.3e}), "
+          f"active {g_plan['active'].size}, near-ties {int(near.sum())}")
+    return y
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_layer_tiny(seed):
+    check_layer(TINY, seed, 4)
+
+
+@pytest.mark.parametrize("T", [1, 4, 16])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_layer_qwen3_shape(seed, T):
+    check_layer(QWEN, seed, T)
+
+
+@pytest.mark.parametrize("T", [1, 4, 16])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_layer_deamoe_7b(seed, T):
+    check_layer(DEA7, seed, T)
+
+
+@pytest.mark.parametrize("T", [1, 8, 32])
+def test_layer_deepseek_v3_shape(T):
+    check_layer(DSV3, 0, T, sample_tokens=[0, T // 2, T - 1])
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_layer_deamoe_dsv3(T):
+    check_layer(DEAV3, 0, T, sample_tokens=[0, T - 1])
+
+
+def test_layer_department_equals_expanded_vanilla():
+    """The department layer equals a vanilla layer whose experts carry the
+    concatenated [department ; private] matrices (computed on the GPU by the
+    vanilla path), on the same tokens."""
+    shape = SH[DEA7]
+    w = gpu_layer(DEA7, 0)
+    T = 16
+    x = moe_synth.make_tokens(shape, 0, T, DEV)
+    yd, _ = run_layer(desc_of(shape), w, x)
+    G = shape.n_experts // shape.n_depts
+    dept = torch.arange(shape.n_experts, device=DEV) // G
+    wv = {"w_router": w["w_router"],
+          "w_gate": torch.cat([w["wd_gate"][dept], w["w_gate"]], 1).contiguous(),
+          "w_up": torch.cat([w["wd_up"][dept], w["w_up"]], 1).contiguous(),
+          "w_down": torch.cat([w["wd_down"][dept], w["w_down"]], 2).contiguous()}
+    dv = M.layer_desc(shape.d, shape.n_experts, shape.top_k, shape.d_ff_dept + shape.d_ff,
+                      dtype="bf16", max_tokens=T)
+    yv, _ = run_layer(dv, wv, x)
+    assert_close(to_np(yd), to_np(yv), "bf16", "department vs expanded")
+
+
+# ---------------------------------------------------------------------------
+# Edge cases, errors, determinism
+# ---------------------------------------------------------------------------
+
+def test_layer_edge_shapes():
+    """k = 1, k = E, one expert per department, T = max_tokens, ragged d/I."""
+    cases = [dict(d=264, E=4, k=1, I=40, T=3), dict(d=256, E=8, k=8, I=128, T=4),
+             dict(d=128, E=4, k=2, I=16, m=4, S=24, T=6), dict(d=1032, E=5, k=2, I=72, Is=40, T=17)]
+    for i, c in enumerate(cases):
+        m, S, Is = c.get("m", 0), c.get("S", 0), c.get("Is", 0)
+        w = _rand_weights(50 + i, c["d"], c["E"], c["I"], m, S, Is)
+        g = torch.Generator().manual_seed(i)
+        x = torch.randn(c["T"], c["d"], generator=g).to(DEV)
+        desc = M.layer_desc(c["d"], c["E"], c["k"], c["I"], n_depts=m, d_ff_dept=S,
+                            d_ff_shared=Is, dtype="f32", max_tokens=c["T"])
+        y, layer = run_layer(desc, w, x)
+        wc = {kk: v.cpu() for kk, v in w.items()}
+        o_ids, o_w, o_sel, _ = O.route(x.cpu(), wc["w_router"], c["k"])
+        g_ids, _ = gpu_ids_from_plan(layer.plan(c["T"]), c["T"], c["k"])
+        ids, _ = reference_ids(o_ids, o_sel, g_ids, c["k"])
+        ref = O.layer_bruteforce(x.cpu(), wc, ids, o_w, c["E"], m)
+        assert_close(to_np(y), ref, "f32", f"edge case {c}")
+
+
+def test_layer_zero_tokens_and_errors():
+    shape = SH[TINY]
+    w = gpu_layer(TINY, 0)
+    desc = desc_of(shape)
+    layer = M.MoeLayer(desc, w, DEV)
+    x0 = torch.empty(0, shape.d, device=DEV)
+    assert layer(x0).shape == (0, shape.d)
+    x = moe_synth.make_tokens(shape, 0, 5, DEV)  # max_tokens is 4
+    with pytest.raises(M.MoeError) as e:
+        layer(x)
+    assert e.value.status == M.MOE_ERR_INVALID_ARG
+    small = torch.empty(64, dtype=torch.uint8, device=DEV)
+    y = torch.full((4, shape.d), 3.0, device=DEV)
+    with pytest.raises(M.MoeError) as e:
+        M.moe_layer_decode(desc, w, x[:4].contiguous(), y, small)
+    assert e.value.status == M.MOE_ERR_WORKSPACE
+    assert torch.all(y == 3.0)  # nothing written
+    # misaligned activation pointer
+    buf = torch.zeros(4 * shape.d + 1, device=DEV)
+    xm = buf[1:].view(4, shape.d)
+    with pytest.raises(M.MoeError) as e:
+        M.moe_layer_decode(desc, w, xm, y, layer.workspace)
+    assert e.value.status == M.MOE_ERR_INVALID_ARG
+
+
+def test_layer_is_deterministic():
+    shape = SH[QWEN]
+    w = gpu_layer(QWEN, 0)
+    x = moe_synth.make_tokens(shape, 0, 16, DEV)
+    layer = M.MoeLayer(desc_of(shape), w, DEV)
+    ys = [layer(x).clone() for _ in range(3)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(ys[0], y) for y in ys[1:])
