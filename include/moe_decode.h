@@ -34,6 +34,10 @@
  *   - Calls that share a workspace must be ordered on one stream; calls with
  *     distinct workspaces are independent and reentrant.  There is no global
  *     mutable state.
+ *   - The workspace (256-byte aligned, moe_workspace_bytes() long) holds a
+ *     few completion counters that must read zero before the first call:
+ *     run moe_workspace_init() once after allocating it (or zero-fill it).
+ *     Every call leaves the counters at zero again.
  *
  * Layouts (row-major, element counts; I = d_ff, S = d_ff_dept, Is = d_ff_shared)
  *   x, y                 [T][d]        act_dtype
@@ -159,6 +163,11 @@ typedef struct {
 /* Bytes of device workspace moe_layer_decode (and every other call) needs for
  * `desc` (T <= desc->max_tokens).  0 if the descriptor is invalid. */
 size_t moe_workspace_bytes(const moe_layer_desc* desc);
+
+/* Zeroes the workspace's completion counters (one small kernel on `stream`;
+ * no hipMemset).  Call once per workspace before its first use. */
+moe_status moe_workspace_init(const moe_layer_desc* desc, void* workspace, size_t ws_bytes,
+                              void* stream);
 
 /* Host-only check of a descriptor (no HIP call). */
 moe_status moe_validate_desc(const moe_layer_desc* desc);

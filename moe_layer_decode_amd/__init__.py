@@ -19,7 +19,7 @@ import torch
 
 __all__ = [
     "MoeError", "LayerDesc", "Weights", "Plan", "layer_desc", "lib", "lib_path",
-    "moe_workspace_bytes", "moe_validate_desc", "moe_route", "moe_dispatch",
+    "moe_workspace_bytes", "moe_workspace_init", "moe_validate_desc", "moe_route", "moe_dispatch",
     "moe_expert_ffn", "moe_combine", "moe_layer_decode", "moe_status_string",
     "moe_loaded_weight_bytes", "alloc_workspace", "plan_to_host", "MoeLayer",
     "MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE",
@@ -34,7 +34,7 @@ PLAN_N_ROWS, PLAN_N_ACTIVE, PLAN_N_DEPT_ROWS, PLAN_N_ACTIVE_DEPTS, PLAN_N_INVALI
 N_STAGES = 5
 STAGE_NAMES = ("route", "dispatch", "gateup", "down", "combine")
 EXPORTED_SYMBOLS = (
-    "moe_workspace_bytes", "moe_validate_desc", "moe_plan_from_workspace", "moe_route",
+    "moe_workspace_bytes", "moe_workspace_init", "moe_validate_desc", "moe_plan_from_workspace", "moe_route",
     "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_layer_decode",
     "moe_status_string", "moe_loaded_weight_bytes",
 )
@@ -94,6 +94,8 @@ def lib() -> ctypes.CDLL:
     P = ctypes.POINTER
     L.moe_workspace_bytes.argtypes = [P(LayerDesc)]
     L.moe_workspace_bytes.restype = _sz
+    L.moe_workspace_init.argtypes = [P(LayerDesc), _vp, _sz, _vp]
+    L.moe_workspace_init.restype = _i32
     L.moe_validate_desc.argtypes = [P(LayerDesc)]
     L.moe_validate_desc.restype = _i32
     L.moe_plan_from_workspace.argtypes = [P(LayerDesc), _vp, _sz, _i32, P(Plan)]
@@ -151,9 +153,18 @@ def moe_loaded_weight_bytes(desc: LayerDesc, n_active: int, n_active_depts: int 
     return int(lib().moe_loaded_weight_bytes(ctypes.byref(desc), n_active, n_active_depts))
 
 
+def moe_workspace_init(desc: LayerDesc, workspace: torch.Tensor):
+    st = lib().moe_workspace_init(ctypes.byref(desc), _ptr(workspace, "workspace", torch.uint8),
+                                  workspace.numel(), _stream(workspace.device))
+    _check(st, "moe_workspace_init")
+
+
 def alloc_workspace(desc: LayerDesc, device="cuda") -> torch.Tensor:
-    """A device workspace of moe_workspace_bytes(desc) bytes (torch-owned)."""
-    return torch.empty(moe_workspace_bytes(desc), dtype=torch.uint8, device=device)
+    """A device workspace of moe_workspace_bytes(desc) bytes (torch-owned),
+    initialised with moe_workspace_init."""
+    ws = torch.empty(moe_workspace_bytes(desc), dtype=torch.uint8, device=device)
+    moe_workspace_init(desc, ws)
+    return ws
 
 
 # ---------------------------------------------------------------------------

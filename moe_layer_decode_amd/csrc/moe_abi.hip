@@ -1,6 +1,7 @@
-// C ABI of the MoE decode layer: argument validation, workspace layout and
-// the launch sequence.  Every check runs on the host before any launch, so a
-// call that fails has launched nothing and written nothing.
+// C ABI of the MoE decode layer: argument validation, workspace layout, the
+// choice of GEMV tiling, and the launch sequence.  Every check runs on the
+// host before any launch, so a call that fails has launched nothing and
+// written nothing.
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -9,14 +10,15 @@
 
 namespace {
 
-using moe::MatSeg;
-using moe::SegSet;
+using moe::Family;
+using moe::FamilySet;
+using moe::WorkDesc;
 
 enum Region {
-  R_LOGITS, R_TOPK_IDS, R_TOPK_W, R_HEADER, R_COUNTS, R_OFFSETS, R_ROW_TOKEN, R_ROW_SLOT,
-  R_ROW_EXPERT, R_ROW_WEIGHT, R_INV_PERM, R_ACTIVE, R_DCOUNTS, R_DOFFSETS, R_DROW_TOKEN,
-  R_DROW_DEPT, R_DROW_SCALE, R_DINV, R_ACTIVE_DEPTS, R_H, R_HD, R_HS, R_ROW_OUT, R_DEPT_OUT,
-  R_SHARED_OUT, R_COUNT
+  R_COUNTERS, R_PARTIAL, R_TOPK_IDS, R_TOPK_W, R_HEADER, R_COUNTS, R_OFFSETS, R_ROW_TOKEN,
+  R_ROW_SLOT, R_ROW_EXPERT, R_ROW_WEIGHT, R_INV_PERM, R_ACTIVE, R_WORK, R_DCOUNTS, R_DOFFSETS,
+  R_DROW_TOKEN, R_DROW_DEPT, R_DROW_SCALE, R_DINV, R_ACTIVE_DEPTS, R_DWORK, R_H, R_HD, R_HS,
+  R_ROW_OUT, R_DEPT_OUT, R_SHARED_OUT, R_COUNT
 };
 
 struct Layout {
@@ -26,6 +28,13 @@ struct Layout {
 
 constexpr size_t kAlign = 256;
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Completion counters (reserved; every kernel boundary orders the steps today).
+size_t n_counters(const moe_layer_desc& d) { return 16 + (size_t)ceil_div(d.d_model, 8); }
+
+int n_route_chunks(const moe_layer_desc& d) { return ceil_div(d.d_model, moe::kRouteChunk); }
 
 // Largest number of (token, department) pairs: a token covers at most
 // min(m, k) departments.
@@ -38,19 +47,21 @@ Layout layout_of(const moe_layer_desc& d) {
   const int64_t Tm = d.max_tokens, E = d.n_experts, k = d.top_k, A = Tm * k;
   const int64_t m = d.n_depts > 0 ? d.n_depts : 0, Pm = max_dept_pairs(d);
   size_t sz[R_COUNT];
-  sz[R_LOGITS] = Tm * E * 4;
-  sz[R_TOPK_IDS] = A * 4;
-  sz[R_TOPK_W] = A * 4;
+  sz[R_COUNTERS] = n_counters(d) * 4;
+  sz[R_PARTIAL] = (size_t)n_route_chunks(d) * Tm * E * 4;
+  sz[R_TOPK_IDS] = sz[R_TOPK_W] = A * 4;
   sz[R_HEADER] = MOE_PLAN_HEADER_LEN * 4;
   sz[R_COUNTS] = E * 4;
   sz[R_OFFSETS] = (E + 1) * 4;
   sz[R_ROW_TOKEN] = sz[R_ROW_SLOT] = sz[R_ROW_EXPERT] = sz[R_ROW_WEIGHT] = sz[R_INV_PERM] = A * 4;
   sz[R_ACTIVE] = E * 4;
+  sz[R_WORK] = 2 * E * sizeof(WorkDesc);
   sz[R_DCOUNTS] = m * 4;
   sz[R_DOFFSETS] = (m + 1) * 4;
   sz[R_DROW_TOKEN] = sz[R_DROW_DEPT] = sz[R_DROW_SCALE] = Pm * 4;
   sz[R_DINV] = Tm * m * 4;
   sz[R_ACTIVE_DEPTS] = m * 4;
+  sz[R_DWORK] = 2 * m * sizeof(WorkDesc);
   sz[R_H] = A * (int64_t)d.d_ff * 4;
   sz[R_HD] = Pm * (int64_t)(m ? d.d_ff_dept : 0) * 4;
   sz[R_HS] = Tm * (int64_t)d.d_ff_shared * 4;
@@ -147,6 +158,19 @@ void fill_plan(const moe_layer_desc& d, void* ws, int32_t T, moe_plan* p) {
   p->n_tokens = T;
 }
 
+moe::PlanArgs plan_args(const moe_layer_desc& d, void* ws, int32_t T, const moe_plan& p) {
+  const Layout L = layout_of(d);
+  moe::PlanArgs pa;
+  pa.T = T;
+  pa.E = d.n_experts;
+  pa.k = d.top_k;
+  pa.m = d.n_depts;
+  pa.plan = p;
+  pa.work = at<WorkDesc>(ws, L, R_WORK);
+  pa.dwork = at<WorkDesc>(ws, L, R_DWORK);
+  return pa;
+}
+
 moe_status plan_matches(const moe_layer_desc& d, void* ws, const moe_plan* p, int32_t T) {
   if (!p || p->n_tokens != T) return MOE_ERR_INVALID_ARG;
   moe_plan q;
@@ -156,73 +180,189 @@ moe_status plan_matches(const moe_layer_desc& d, void* ws, const moe_plan* p, in
              : MOE_ERR_INVALID_ARG;
 }
 
-int ceil_div(int a, int b) { return (a + b - 1) / b; }
-
-// Matrix families of a step: routed experts (private slices in the department
-// form), department slices, the shared expert; outputs per family.
-SegSet make_segset(const moe_layer_desc& d, const moe_weights& w, const moe_plan& p, void* ws,
-                   int32_t T, float* row_out, float* dept_out, float* shared_out) {
+moe::RouteArgs route_args(const moe_layer_desc& d, void* ws, const void* x, const void* wr,
+                          const float* bias, int32_t T, int32_t* ids, float* w, float* sel) {
   const Layout L = layout_of(d);
-  SegSet set{};
+  moe::RouteArgs ra;
+  ra.x = x;
+  ra.wr = wr;
+  ra.bias = bias;
+  ra.T = T;
+  ra.d = d.d_model;
+  ra.E = d.n_experts;
+  ra.k = d.top_k;
+  ra.score_fn = d.score_fn;
+  ra.renorm = d.renormalize;
+  ra.scale = d.route_scale;
+  ra.n_chunks = n_route_chunks(d);
+  ra.partial = at<float>(ws, L, R_PARTIAL);
+  ra.ids_out = ids;
+  ra.w_out = w;
+  ra.sel_out = sel;
+  return ra;
+}
+
+// ---------------------------------------------------------------------------
+// GEMV tiling.  Measured on MI355X: the weight streams run fastest with the
+// least work per wave (one gate row + one up row per wave; two column groups
+// per wave in down), which keeps the most loads in flight per CU.  Down takes
+// as many lanes per weight row as divide every family's row length in
+// 16-byte chunks (64, 32 or 16), so no lane idles.
+// ---------------------------------------------------------------------------
+int family_rows(const moe_layer_desc& d, int f) {
+  return f == 0 ? d.d_ff : f == 1 ? d.d_ff_dept : d.d_ff_shared;
+}
+
+moe::GemvConfig choose_config(const moe_layer_desc& d, int32_t T) {
+  (void)T;
+  moe::GemvConfig c;
+#ifdef MOE_FORCE_RPW
+  c.rows_per_wave = MOE_FORCE_RPW;
+#else
+  c.rows_per_wave = 1;
+#endif
+#ifdef MOE_FORCE_RW
+  c.rows_per_pass = MOE_FORCE_RW;
+#else
+  c.rows_per_pass = 1;
+#endif
+  int lpr = 64;
+  for (int cand : {64, 32, 16}) {
+    bool ok = true;
+    for (int f = 0; f < 3; ++f) {
+      const int r = family_rows(d, f);
+      if (r > 0 && (f != 1 || d.n_depts > 0) && (r / 8) % cand) ok = false;
+    }
+    if (ok) {
+      lpr = cand;
+      break;
+    }
+  }
+  c.lpr = lpr;
+#ifdef MOE_FORCE_CG
+  c.col_groups = MOE_FORCE_CG;
+#else
+  c.col_groups = 2;
+#endif
+  return c;
+}
+
+// Matrix families of a step -- routed experts (private slices in the
+// department form), department slices, the shared expert -- each split into
+// the part for groups of at most four rows and the part for larger groups.
+// A part is left out when no group of its size can occur at this T.
+FamilySet make_families(const moe_layer_desc& d, const moe_weights& w, const moe_plan& p,
+                        void* ws, int32_t T, float* row_out, float* dept_out, float* shared_out) {
+  const Layout L = layout_of(d);
+  FamilySet set{};
   int n = 0;
-  auto add = [&](const MatSeg& s) { set.s[n++] = s; };
   const int tk = T * d.top_k;
+  const int small_max = moe::kTokInline;
+  // Small and large groups come from separate compacted work lists (the
+  // large one starts n_mats descriptors in); a large group has more than
+  // small_max rows, which bounds how many there can be.
+  auto add_parts = [&](Family f, bool can_small, bool can_large, int hdr_small, int hdr_large) {
+    if (can_small) {
+      Family g = f;
+      g.large = 0;
+      if (g.work) g.n_active = p.header + hdr_small;
+      set.f[n++] = g;
+    }
+    if (can_large) {
+      Family g = f;
+      g.large = 1;
+      if (g.work) {
+        g.work = f.work + f.n_mats;
+        g.n_active = p.header + hdr_large;
+        const int cap = f.max_rows / (small_max + 1);
+        if (cap < g.max_slots) g.max_slots = cap;
+      }
+      if (g.max_slots > 0) set.f[n++] = g;
+    }
+  };
   {
-    MatSeg s{};
-    s.gate = w.w_gate;
-    s.up = w.w_up;
-    s.down = w.w_down;
-    s.rows = d.d_ff;
-    s.active = p.active;
-    s.n_active = p.header + MOE_PLAN_N_ACTIVE;
-    s.grp_off = p.offsets;
-    s.grp_token = p.row_token;
-    s.h = at<float>(ws, L, R_H);
-    s.out = row_out;
-    s.max_slots = tk < d.n_experts ? tk : d.n_experts;
-    add(s);
+    Family f{};
+    f.gate = w.w_gate;
+    f.up = w.w_up;
+    f.down = w.w_down;
+    f.rows = d.d_ff;
+    f.work = at<WorkDesc>(ws, L, R_WORK);
+    f.n_active = p.header + MOE_PLAN_N_ACTIVE;
+    f.grp_token = p.row_token;
+    f.h = at<void>(ws, L, R_H);
+    f.out = row_out;
+    f.max_slots = tk < d.n_experts ? tk : d.n_experts;
+    f.n_mats = d.n_experts;
+    f.max_rows = tk;
+    add_parts(f, true, T > small_max, moe::kHdrSmall, moe::kHdrLarge);
   }
   if (d.n_depts > 0) {
-    MatSeg s{};
-    s.gate = w.wd_gate;
-    s.up = w.wd_up;
-    s.down = w.wd_down;
-    s.rows = d.d_ff_dept;
-    s.active = p.active_depts;
-    s.n_active = p.header + MOE_PLAN_N_ACTIVE_DEPTS;
-    s.grp_off = p.dept_offsets;
-    s.grp_token = p.dept_row_token;
-    s.h = at<float>(ws, L, R_HD);
-    s.out = dept_out;
-    s.max_slots = tk < d.n_depts ? tk : d.n_depts;
-    add(s);
+    Family f{};
+    f.gate = w.wd_gate;
+    f.up = w.wd_up;
+    f.down = w.wd_down;
+    f.rows = d.d_ff_dept;
+    f.work = at<WorkDesc>(ws, L, R_DWORK);
+    f.n_active = p.header + MOE_PLAN_N_ACTIVE_DEPTS;
+    f.grp_token = p.dept_row_token;
+    f.h = at<void>(ws, L, R_HD);
+    f.out = dept_out;
+    f.max_slots = tk < d.n_depts ? tk : d.n_depts;
+    f.n_mats = d.n_depts;
+    f.max_rows = (int)((int64_t)T * (d.n_depts < d.top_k ? d.n_depts : d.top_k));
+    add_parts(f, true, T > small_max, moe::kHdrDeptSmall, moe::kHdrDeptLarge);
   }
   if (d.d_ff_shared > 0) {
-    MatSeg s{};
-    s.gate = w.ws_gate;
-    s.up = w.ws_up;
-    s.down = w.ws_down;
-    s.rows = d.d_ff_shared;
-    s.h = at<float>(ws, L, R_HS);
-    s.out = shared_out;
-    s.max_slots = 1;
-    add(s);
+    Family f{};
+    f.gate = w.ws_gate;
+    f.up = w.ws_up;
+    f.down = w.ws_down;
+    f.rows = d.d_ff_shared;
+    f.h = at<void>(ws, L, R_HS);
+    f.out = shared_out;
+    f.max_slots = 1;
+    f.n_mats = 1;
+    f.max_rows = T;
+    add_parts(f, T <= small_max, T > small_max, 0, 0);
   }
   set.n = n;
-  set.blk_start[0] = 0;
-  for (int i = 0; i < n; ++i) {
-    set.s[i].tiles_gu = ceil_div(set.s[i].rows, moe::kGuTile);
-    set.s[i].tiles_dn = ceil_div(d.d_model, moe::kDnTile);
-  }
   return set;
 }
 
-void set_blocks(SegSet& set, bool gateup) {
+// Tiles per slot and the block prefix for one launch: small parts tile by the
+// GEMV configuration, large parts by 64 rows (gate/up) or 64 columns (down),
+// four 16-wide matrix-core tiles per block.
+void set_tiles(FamilySet& set, int d, bool gateup, const moe::GemvConfig& c) {
   set.blk_start[0] = 0;
-  for (int i = 0; i < set.n; ++i)
-    set.blk_start[i + 1] =
-        set.blk_start[i] + set.s[i].max_slots * (gateup ? set.s[i].tiles_gu : set.s[i].tiles_dn);
-  for (int i = set.n + 1; i < 4; ++i) set.blk_start[i] = set.blk_start[set.n];
+  for (int i = 0; i < set.n; ++i) {
+    Family& f = set.f[i];
+    if (f.large)
+      f.tiles = ceil_div(gateup ? f.rows : d, moe::kWaves * 16);
+    else
+      f.tiles = gateup ? ceil_div(f.rows, moe::kWaves * c.rows_per_wave)
+                       : ceil_div(d, moe::kWaves * c.col_groups * (64 / c.lpr));
+    set.blk_start[i + 1] = set.blk_start[i] + f.max_slots * f.tiles;
+  }
+  for (int i = set.n + 1; i <= moe::kMaxParts; ++i) set.blk_start[i] = set.blk_start[set.n];
+}
+
+moe::CombineArgs combine_args(const moe_layer_desc& d, const moe_plan& p, const float* row_out,
+                              const float* dept_out, const float* shared_out, int32_t T) {
+  moe::CombineArgs a;
+  a.inv_perm = p.inv_perm;
+  a.row_weight = p.row_weight;
+  a.row_out = row_out;
+  a.dept_inv = p.dept_inv;
+  a.dept_scale = p.dept_row_scale;
+  a.dept_out = dept_out;
+  a.shared_out = shared_out;
+  a.T = T;
+  a.k = d.top_k;
+  a.m = d.n_depts;
+  a.d = d.d_model;
+  a.max_rows = T * d.top_k;
+  a.max_dept_rows = (int)((int64_t)T * (d.n_depts < d.top_k ? d.n_depts : d.top_k));
+  return a;
 }
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
@@ -237,6 +377,16 @@ size_t moe_workspace_bytes(const moe_layer_desc* desc) {
 }
 
 moe_status moe_validate_desc(const moe_layer_desc* desc) { return check_desc(desc); }
+
+moe_status moe_workspace_init(const moe_layer_desc* desc, void* workspace, size_t ws_bytes,
+                              void* stream) {
+  moe_status s = check_desc(desc);
+  if (s != MOE_OK) return s;
+  if ((s = check_ws(desc, workspace, ws_bytes)) != MOE_OK) return s;
+  const Layout L = layout_of(*desc);
+  return hip_status(moe::launch_zero(at<unsigned int>(workspace, L, R_COUNTERS),
+                                     n_counters(*desc), static_cast<hipStream_t>(stream)));
+}
 
 moe_status moe_plan_from_workspace(const moe_layer_desc* desc, void* workspace, size_t ws_bytes,
                                    int32_t T, moe_plan* plan) {
@@ -261,15 +411,9 @@ moe_status moe_route(const moe_layer_desc* desc, const void* x, const void* w_ro
     return MOE_ERR_INVALID_ARG;
   if (desc->score_fn == MOE_SCORE_SOFTMAX && router_bias) return MOE_ERR_INVALID_ARG;
   if ((s = check_ws(desc, workspace, ws_bytes)) != MOE_OK) return s;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const Layout L = layout_of(*desc);
-  float* logits = at<float>(workspace, L, R_LOGITS);
-  hipError_t e = moe::launch_router_logits(desc->w_dtype, x, w_router, T, desc->d_model,
-                                           desc->n_experts, logits, st);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  moe::TopkArgs tk{logits, router_bias, T, desc->n_experts, desc->top_k, desc->score_fn,
-                   desc->renormalize, desc->route_scale, topk_ids, topk_w, sel_scores};
-  return hip_status(moe::launch_topk_dispatch(&tk, nullptr, st));
+  const moe::RouteArgs ra = route_args(*desc, workspace, x, w_router, router_bias, T, topk_ids,
+                                       topk_w, sel_scores);
+  return hip_status(moe::launch_route(desc->w_dtype, ra, nullptr, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_dispatch(const moe_layer_desc* desc, const int32_t* topk_ids, const float* topk_w,
@@ -287,8 +431,8 @@ moe_status moe_dispatch(const moe_layer_desc* desc, const int32_t* topk_ids, con
   if (!ok_ptr(topk_ids) || !ok_ptr(topk_w)) return MOE_ERR_INVALID_ARG;
   if ((s = check_ws(desc, workspace, ws_bytes)) != MOE_OK) return s;
   fill_plan(*desc, workspace, T, plan);
-  moe::DispatchArgs dp{topk_ids, topk_w, T, desc->n_experts, desc->top_k, desc->n_depts, *plan};
-  return hip_status(moe::launch_topk_dispatch(nullptr, &dp, static_cast<hipStream_t>(stream)));
+  const moe::PlanArgs pa = plan_args(*desc, workspace, T, *plan);
+  return hip_status(moe::launch_dispatch(topk_ids, topk_w, pa, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_weights* weights, const void* x,
@@ -306,12 +450,17 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_weights* weights
   if ((s = check_ws(desc, workspace, ws_bytes)) != MOE_OK) return s;
   if ((s = plan_matches(*desc, workspace, plan, T)) != MOE_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  SegSet set = make_segset(*desc, *weights, *plan, workspace, T, row_out, dept_out, shared_out);
-  set_blocks(set, true);
-  hipError_t e = moe::launch_gateup(desc->w_dtype, set, x, T, desc->d_model, st);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  set_blocks(set, false);
-  return hip_status(moe::launch_down(desc->w_dtype, set, T, desc->d_model, st));
+  const moe::GemvConfig cfg = choose_config(*desc, T);
+  FamilySet set = make_families(*desc, *weights, *plan, workspace, T, row_out, dept_out,
+                                shared_out);
+  set_tiles(set, desc->d_model, true, cfg);
+  if (moe::launch_gateup(desc->w_dtype, set, x, T, desc->d_model, cfg.rows_per_wave,
+                         cfg.rows_per_pass, st) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+  set_tiles(set, desc->d_model, false, cfg);
+  return hip_status(
+      moe::launch_down(desc->w_dtype, set, T, desc->d_model, cfg.lpr, cfg.col_groups, st));
 }
 
 moe_status moe_combine(const moe_layer_desc* desc, const moe_plan* plan, const float* row_out,
@@ -329,9 +478,7 @@ moe_status moe_combine(const moe_layer_desc* desc, const moe_plan* plan, const f
   if (desc->d_ff_shared > 0 ? !ok_ptr(shared_out) : shared_out != nullptr)
     return MOE_ERR_INVALID_ARG;
   if (desc->n_depts > 0 && (!plan->dept_inv || !plan->dept_row_scale)) return MOE_ERR_INVALID_ARG;
-  moe::CombineArgs a{plan->inv_perm, plan->row_weight, row_out, plan->dept_inv,
-                     plan->dept_row_scale, dept_out, shared_out, T, desc->top_k,
-                     desc->n_depts, desc->d_model};
+  const moe::CombineArgs a = combine_args(*desc, *plan, row_out, dept_out, shared_out, T);
   return hip_status(moe::launch_combine(desc->act_dtype, a, y, static_cast<hipStream_t>(stream)));
 }
 
@@ -351,41 +498,43 @@ moe_status moe_layer_decode(const moe_layer_desc* desc, const moe_weights* weigh
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   auto mark = [&](int i) -> bool {
-    return !stage_events || hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), st) == hipSuccess;
+    return !stage_events ||
+           hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), st) == hipSuccess;
   };
   const Layout L = layout_of(*desc);
   moe_plan plan;
   fill_plan(*desc, workspace, T, &plan);
-  float* logits = at<float>(workspace, L, R_LOGITS);
   float* row_out = at<float>(workspace, L, R_ROW_OUT);
   float* dept_out = desc->n_depts > 0 ? at<float>(workspace, L, R_DEPT_OUT) : nullptr;
   float* shared_out = desc->d_ff_shared > 0 ? at<float>(workspace, L, R_SHARED_OUT) : nullptr;
+  const moe::GemvConfig cfg = choose_config(*desc, T);
 
+  // router logits, then top-k + dispatch plan
   if (!mark(MOE_STAGE_ROUTE)) return MOE_ERR_HIP;
-  if (moe::launch_router_logits(desc->w_dtype, x, weights->w_router, T, desc->d_model,
-                                desc->n_experts, logits, st) != hipSuccess)
-    return MOE_ERR_HIP;
-  if (!mark(MOE_STAGE_DISPATCH)) return MOE_ERR_HIP;
-  moe::TopkArgs tk{logits, weights->router_bias, T, desc->n_experts, desc->top_k,
-                   desc->score_fn, desc->renormalize, desc->route_scale,
-                   at<int32_t>(workspace, L, R_TOPK_IDS), at<float>(workspace, L, R_TOPK_W),
-                   nullptr};
-  moe::DispatchArgs dp{nullptr, nullptr, T, desc->n_experts, desc->top_k, desc->n_depts, plan};
-  if (moe::launch_topk_dispatch(&tk, &dp, st) != hipSuccess) return MOE_ERR_HIP;
-  SegSet set = make_segset(*desc, *weights, plan, workspace, T, row_out, dept_out, shared_out);
-  if (!mark(MOE_STAGE_GATEUP)) return MOE_ERR_HIP;
-  set_blocks(set, true);
-  if (moe::launch_gateup(desc->w_dtype, set, x, T, desc->d_model, st) != hipSuccess)
+  const moe::RouteArgs ra =
+      route_args(*desc, workspace, x, weights->w_router, weights->router_bias, T,
+                 at<int32_t>(workspace, L, R_TOPK_IDS), at<float>(workspace, L, R_TOPK_W), nullptr);
+  const moe::PlanArgs pa = plan_args(*desc, workspace, T, plan);
+  if (moe::launch_route(desc->w_dtype, ra, &pa, st) != hipSuccess) return MOE_ERR_HIP;
+  if (!mark(MOE_STAGE_DISPATCH) || !mark(MOE_STAGE_GATEUP)) return MOE_ERR_HIP;
+
+  FamilySet set = make_families(*desc, *weights, plan, workspace, T, row_out, dept_out,
+                                shared_out);
+  set_tiles(set, desc->d_model, true, cfg);
+  if (moe::launch_gateup(desc->w_dtype, set, x, T, desc->d_model, cfg.rows_per_wave,
+                         cfg.rows_per_pass, st) !=
+      hipSuccess)
     return MOE_ERR_HIP;
   if (!mark(MOE_STAGE_DOWN)) return MOE_ERR_HIP;
-  set_blocks(set, false);
-  if (moe::launch_down(desc->w_dtype, set, T, desc->d_model, st) != hipSuccess)
+
+  // grouped down, then the combine back to token order
+  set_tiles(set, desc->d_model, false, cfg);
+  if (moe::launch_down(desc->w_dtype, set, T, desc->d_model, cfg.lpr, cfg.col_groups, st) !=
+      hipSuccess)
     return MOE_ERR_HIP;
   if (!mark(MOE_STAGE_COMBINE)) return MOE_ERR_HIP;
-  moe::CombineArgs a{plan.inv_perm, plan.row_weight, row_out, plan.dept_inv,
-                     plan.dept_row_scale, dept_out, shared_out, T, desc->top_k,
-                     desc->n_depts, desc->d_model};
-  if (moe::launch_combine(desc->act_dtype, a, y, st) != hipSuccess) return MOE_ERR_HIP;
+  const moe::CombineArgs ca = combine_args(*desc, plan, row_out, dept_out, shared_out, T);
+  if (moe::launch_combine(desc->act_dtype, ca, y, st) != hipSuccess) return MOE_ERR_HIP;
   if (!mark(MOE_N_STAGES)) return MOE_ERR_HIP;
   return MOE_OK;
 }

@@ -9,58 +9,73 @@
 
 namespace moe {
 
-// Gate/up GEMV tiling: a block is 4 waves, each wave owns kRowsPerWave rows of
-// gate and up, so a block covers kGuTile intermediate rows.
-constexpr int kGuWaves = 4;
-constexpr int kRowsPerWave = 4;
-constexpr int kGuTile = kGuWaves * kRowsPerWave;
-// Down GEMV tiling: each wave owns kColsPerWave output columns of d.
-constexpr int kDnWaves = 4;
-constexpr int kColsPerWave = 4;
-constexpr int kDnTile = kDnWaves * kColsPerWave;
-// Threads of the single-block top-k / dispatch kernel.
-constexpr int kPlanThreads = 1024;
+constexpr int kWaves = 4;            // waves per block of every kernel
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRouteChunk = 512;     // d elements one router wave covers (64 lanes x 8)
+constexpr int kTokInline = 4;        // tokens carried inline in a work descriptor
+constexpr int kPlanThreads = 1024;   // threads of the single-block top-k / plan kernel
+constexpr int kMaxParts = 6;         // 3 matrix families x (small groups, large groups)
+// Plan header entries beyond the public ones: lengths of the compacted work
+// lists of small (<= kTokInline rows) and large groups.
+constexpr int kHdrSmall = 8, kHdrLarge = 9, kHdrDeptSmall = 10, kHdrDeptLarge = 11;
 
-// One family of same-shape matrices (routed experts, department slices, or
-// the shared expert) and the row groups that use them.
-struct MatSeg {
-  const void* gate;      // [n_mats][rows][d]
-  const void* up;        // [n_mats][rows][d]
-  const void* down;      // [n_mats][d][rows]
-  int rows;              // intermediate width of this family
-  const int* active;     // active matrix ids (nullptr: the single matrix 0)
-  const int* n_active;   // device count of `active` (nullptr: 1)
-  const int* grp_off;    // [n_mats+1] row ranges (nullptr: rows 0..T-1)
-  const int* grp_token;  // token of each row (nullptr: row r is token r)
-  float* h;              // [rows_total][rows] fp32 SiLU(g)*u
-  float* out;            // [rows_total][d] fp32 unweighted down output
-  int max_slots;         // host upper bound on *n_active
-  int tiles_gu;          // ceil(rows / kGuTile)
-  int tiles_dn;          // ceil(d / kDnTile)
+// One active matrix of a family and its row group, written by the dispatch
+// phase so an expert block starts from a single 32-byte read.
+struct WorkDesc {
+  int mat;                 // expert or department index
+  int r0;                  // first row of its group in the plan's row order
+  int n;                   // rows (tokens) in the group
+  int tok[kTokInline];     // the first tokens of the group
+  int pad;
 };
 
-struct SegSet {
-  MatSeg s[3];
-  int n;
-  int blk_start[4];      // prefix sums of blocks per family
-};
-
-struct TopkArgs {
-  const float* logits;   // [T][E]
-  const float* bias;     // [E] or nullptr
-  int T, E, k;
-  int score_fn, renorm;
-  float scale;
-  int32_t* ids_out;      // [T][k] or nullptr
-  float* w_out;          // [T][k] or nullptr
-  float* sel_out;        // [T][E] or nullptr
-};
-
-struct DispatchArgs {
-  const int32_t* ids_in;  // used when the kernel does not run top-k itself
-  const float* w_in;
+// Everything the routing + dispatch phase reads and writes.
+struct PlanArgs {
   int T, E, k, m;
   moe_plan plan;
+  WorkDesc* work;          // [2E] active experts: small groups from 0, large groups from E
+  WorkDesc* dwork;         // [2m] the same for departments
+};
+
+struct RouteArgs {
+  const void* x;           // [T][d]
+  const void* wr;          // [E][d]
+  const float* bias;       // [E] or nullptr
+  int T, d, E, k;
+  int score_fn, renorm;
+  float scale;
+  int n_chunks;            // ceil(d / kRouteChunk)
+  float* partial;          // [n_chunks][T][E] partial logits
+  int32_t* ids_out;        // [T][k] or nullptr
+  float* w_out;            // [T][k] or nullptr
+  float* sel_out;          // [T][E] or nullptr
+};
+
+// One part of a family of same-shape matrices (routed experts -- private
+// slices in the department form --, department slices, or the shared
+// expert): the slots whose group has at most kTokInline rows (small part,
+// register GEMV) or more (large part, matrix-core tiles).
+struct Family {
+  const void* gate;        // [n_mats][rows][d]
+  const void* up;          // [n_mats][rows][d]
+  const void* down;        // [n_mats][d][rows]
+  int rows;
+  const WorkDesc* work;    // per active slot; nullptr: the shared expert (all T tokens)
+  const int* n_active;     // device count of active slots (nullptr: 1)
+  const int* grp_token;    // token of each row (nullptr: row r is token r)
+  void* h;                 // [rows_total][rows] SiLU(g) * u, in the layer's dtype
+  float* out;              // [rows_total][d]    unweighted down output
+  int max_slots;           // host bound on the slots this part can serve
+  int tiles;               // blocks per slot in the current launch
+  int n_mats;              // matrices in the family (bounds check of work descriptors)
+  int max_rows;            // rows h / out hold (bounds check of work descriptors)
+  int large;               // 0: groups of <= kTokInline rows; 1: larger groups
+};
+
+struct FamilySet {
+  Family f[kMaxParts];
+  int n;
+  int blk_start[kMaxParts + 1];   // prefix sums of max_slots * tiles
 };
 
 struct CombineArgs {
@@ -72,15 +87,25 @@ struct CombineArgs {
   const float* dept_out;   // nullptr when no department term
   const float* shared_out; // nullptr when no shared expert
   int T, k, m, d;
+  int max_rows;            // rows of row_out (plan entries at or past it are skipped)
+  int max_dept_rows;       // rows of dept_out
 };
 
-// Launchers (each returns the hipGetLastError() of its launch).
-hipError_t launch_router_logits(int w_dtype, const void* x, const void* w_router, int T, int d,
-                                int E, float* logits, hipStream_t st);
-hipError_t launch_topk_dispatch(const TopkArgs* topk, const DispatchArgs* disp, hipStream_t st);
-hipError_t launch_gateup(int w_dtype, const SegSet& set, const void* x, int T, int d,
-                         hipStream_t st);
-hipError_t launch_down(int w_dtype, const SegSet& set, int T, int d, hipStream_t st);
+struct GemvConfig {
+  int rows_per_wave;   // gate/up: rows of each matrix per wave (1, 2, 4, 8)
+  int rows_per_pass;   // gate/up: rows a wave streams at once (1, 2, 4)
+  int lpr;             // down: lanes per weight row (16, 32, 64)
+  int col_groups;      // down: column groups per wave (columns per wave = col_groups * 64 / lpr)
+};
+
+// Launchers: each returns hipGetLastError() after its launch.
+hipError_t launch_route(int w_dtype, const RouteArgs& ra, const PlanArgs* pa, hipStream_t st);
+hipError_t launch_dispatch(const int32_t* ids, const float* w, const PlanArgs& pa, hipStream_t st);
+hipError_t launch_gateup(int w_dtype, const FamilySet& set, const void* x, int T, int d,
+                         int rows_per_wave, int rows_per_pass, hipStream_t st);
+hipError_t launch_down(int w_dtype, const FamilySet& set, int T, int d, int lpr, int col_groups,
+                       hipStream_t st);
 hipError_t launch_combine(int act_dtype, const CombineArgs& a, void* y, hipStream_t st);
+hipError_t launch_zero(unsigned int* p, size_t n, hipStream_t st);
 
 }  // namespace moe

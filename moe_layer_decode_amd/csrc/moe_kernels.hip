@@ -1,19 +1,26 @@
 // gfx950 kernels of the MoE decode step.
 //
-//   router_logits_kernel  l[t][e] = x_t . W_r[e]   (DeaMoE section 2.1, Eq. (2))
-//   topk_dispatch_kernel  top-k + routing weights (Eq. (2)-(3); the DeepSeekMoE
-//                         guide's bias routing), then the dispatch plan: counting
-//                         sort by expert, inverse map, active lists, department
-//                         pairs ("How a batch becomes expert-specific matrices")
-//   gateup_kernel         h = SiLU(W_gate x) * (W_up x) per dispatched row (Eq. (1))
-//   down_kernel           o = W_down h per dispatched row (Eq. (1))
-//   combine_kernel        y_t = sum_j p_j o_{t,j} + department + shared terms (Eq. (3))
+//   route_kernel      partial router logits (DeaMoE section 2.1, Eq. (2)),
+//                     split over d-chunks across the whole chip
+//   topk_plan_kernel  one block: sums the partials, takes the top-k with its
+//                     weights (Eq. (3); the DeepSeekMoE guide's sigmoid/bias
+//                     routing) and builds the dispatch plan ("How a batch
+//                     becomes expert-specific matrices": group by expert, keep
+//                     token ids and the inverse map), plus one work descriptor
+//                     per active expert and department
+//   dispatch_kernel   the plan alone, for caller-given ids
+//   gateup_kernel     h = SiLU(W_gate x) * (W_up x) per dispatched row (Eq. (1))
+//   down_kernel       o = W_down h per dispatched row (Eq. (1))
+//   combine_kernel    y_t = sum_j p_j o_{t,j} + department + shared terms (Eq. (3))
 //
-// Decode streams every active expert's weights once per step at one to a few
-// rows per expert, so the expert kernels are weight-streaming GEMVs: every lane
-// reads 16 contiguous bytes per row per step (a wave covers 1 KiB of a row per
-// load instruction), accumulates in fp32 in registers, and the 64 lanes are
-// reduced once per row block with a reduce-scatter butterfly.
+// Decode reads every active expert's weights once per step at one to a few
+// rows per expert, so the expert kernels are weight-streaming GEMVs: each lane
+// reads 16 contiguous bytes of a weight row per step, the next step's weights
+// are already in flight while the current ones are used, sums are fp32 in
+// registers, and the lanes of a row are reduced once with a reduce-scatter
+// butterfly.  Blocks whose slot is beyond the device-side active count exit at
+// once, so every grid is sized on the host from T alone.
+//
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -22,72 +29,142 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Router logits: one wave per expert, lanes split d, tokens in chunks of 8.
-// The per-expert reduction order does not depend on the expert index, so
-// equal router rows give bitwise-equal logits.
+// 16-byte weight vectors kept raw (bf16 stays packed) until they are used.
 // ---------------------------------------------------------------------------
-template <typename T_>
-__global__ __launch_bounds__(256) void router_logits_kernel(const T_* __restrict__ x,
-                                                            const T_* __restrict__ wr, int T,
-                                                            int d, int E,
-                                                            float* __restrict__ logits) {
-  const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (e >= E) return;
-  const T_* wrow = wr + (size_t)e * d;
-  for (int t0 = 0; t0 < T; t0 += 8) {
-    const int nv = min(8, T - t0);
-    float acc[8];
+template <typename T_> struct Raw8;
+template <> struct Raw8<bf16_t> {
+  u32x4_t u;
+  __device__ __forceinline__ void load(const bf16_t* p) {
+    u = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  }
+  __device__ __forceinline__ void zero() { u = u32x4_t{0, 0, 0, 0}; }
+  __device__ __forceinline__ void to_f32(float (&v)[8]) const {
+    v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
+    v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z); v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
+  }
+};
+template <> struct Raw8<float> {
+  f32x4_t a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+    b = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p + 4));
+  }
+  __device__ __forceinline__ void zero() { a = b = f32x4_t{0.f, 0.f, 0.f, 0.f}; }
+  __device__ __forceinline__ void to_f32(float (&v)[8]) const {
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = 0.f;
-    for (int c = lane * 8; c < d; c += 8 * kWave) {
-      float w[8];
-      load8(wrow + c, w);
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o, kWave);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+// Reduce N per-lane values over the L lanes of an aligned lane group (lanes
+// differing only in bits below log2 L).  Upper lanes keep the upper half at
+// each halving step, so afterwards lane j of the group holds, in
+// v[0 .. max(N/L, 1)), the sums of value indices (N/L) * j + i when N >= L,
+// or of index j / (L/N) when N < L.
+template <int N, int L>
+__device__ __forceinline__ void group_reduce_scatter(float (&v)[N], int lane) {
+  int n = N;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j < nv) {
-          float xv[8];
-          load8(x + (size_t)(t0 + j) * d + c, xv);
+  for (int o = L / 2; o >= 1; o >>= 1) {
+    if (n > 1) {
+      const int half = n >> 1;
+      const bool upper = (lane & o) != 0;
 #pragma unroll
-          for (int q = 0; q < 8; ++q) acc[j] = fmaf(w[q], xv[q], acc[j]);
+      for (int i = 0; i < N / 2; ++i) {
+        if (i < half) {
+          const float send = upper ? v[i] : v[i + half];
+          const float keep = upper ? v[i + half] : v[i];
+          v[i] = keep + __shfl_xor(send, o, kWave);
         }
       }
+      n = half;
+    } else {
+      v[0] += __shfl_xor(v[0], o, kWave);
     }
-    const float r = wave_reduce_scatter<8>(acc, lane);
-    const int j = (lane >> 3) & 7;
-    if ((lane & 7) == 0 && j < nv) logits[(size_t)(t0 + j) * E + e] = r;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Top-k of one token by one wave.  Lane l holds experts l, l+64, ...; k rounds
-// of a wave-wide argmax under the order (score desc, index asc).  Lane j keeps
-// slot j, so slots come out in that order.
+// Routing + plan
 // ---------------------------------------------------------------------------
+struct PlanShared {
+  int ids[MOE_MAX_ASSIGNMENTS];
+  float w[MOE_MAX_ASSIGNMENTS];
+  int cnt[MOE_MAX_EXPERTS];
+  int off[MOE_MAX_EXPERTS + 1];
+  int slot[MOE_MAX_EXPERTS];
+  unsigned char flag[MOE_MAX_DEPT_PAIRS];
+  int invalid;
+};
+
+// Partial logits of expert e over d-chunk c for every token.  The reduction
+// order depends only on the token's position, never on e, so equal router
+// rows give bitwise-equal logits.
+template <typename T_>
+__device__ void router_partial(const RouteArgs& ra, int e, int c, int lane) {
+  const T_* x = static_cast<const T_*>(ra.x);
+  const int col = c * kRouteChunk + lane * 8;
+  const bool act = col < ra.d;
+  float w[8];
+  if (act) {
+    load8(static_cast<const T_*>(ra.wr) + (size_t)e * ra.d + col, w);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) w[q] = 0.f;
+  }
+  for (int t0 = 0; t0 < ra.T; t0 += 8) {
+    const int nv = min(8, ra.T - t0);
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      acc[j] = 0.f;
+      if (j < nv && act) {
+        float xv[8];
+        load8(x + (size_t)(t0 + j) * ra.d + col, xv);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[j] = fmaf(w[q], xv[q], acc[j]);
+      }
+    }
+    group_reduce_scatter<8, 64>(acc, lane);
+    const int j = lane >> 3;
+    if ((lane & 7) == 0 && j < nv) ra.partial[((size_t)c * ra.T + t0 + j) * ra.E + e] = acc[0];
+  }
+}
+
+// Top-k of token t by one wave: lane l holds experts l, l+64, ...; k rounds of
+// a wave-wide argmax under (score desc, index asc); lane j keeps slot j.
 template <int NPL>
-__device__ void topk_one(const TopkArgs& p, int t, int lane, int* s_ids, float* s_w) {
-  const float* lrow = p.logits + (size_t)t * p.E;
+__device__ void topk_one(const RouteArgs& p, int t, int lane, PlanShared& s) {
   float sel[NPL], aux[NPL], lg[NPL];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int e = lane + kWave * i;
-    float l = 0.f, s = 0.f, a = 0.f;
+    float l = 0.f, sc = 0.f, a = 0.f;
     if (e < p.E) {
-      l = lrow[e];
+      for (int c = 0; c < p.n_chunks; ++c) l += p.partial[((size_t)c * p.T + t) * p.E + e];
       const float b = p.bias ? p.bias[e] : 0.f;
       if (p.score_fn == MOE_SCORE_SIGMOID) {
         a = 1.0f / (1.0f + expf(-l));
-        s = a + b;
+        sc = a + b;
       } else if (p.score_fn == MOE_SCORE_SOFTMAX_BIAS) {
         a = l;
-        s = l + b;
+        sc = l + b;
       } else {
         a = l;
-        s = l;
+        sc = l;
       }
-      if (p.sel_out) p.sel_out[(size_t)t * p.E + e] = s;
+      if (p.sel_out) p.sel_out[(size_t)t * p.E + e] = sc;
     }
-    sel[i] = s;
+    sel[i] = sc;
     aux[i] = a;
     lg[i] = l;
   }
@@ -112,8 +189,7 @@ __device__ void topk_one(const TopkArgs& p, int t, int lane, int* s_ids, float* 
       const float ov = __shfl_xor(bv, o, kWave);
       const int oe = __shfl_xor(be, o, kWave);
       const float oa = __shfl_xor(ba, o, kWave);
-      const bool better = oe != INT_MAX && (be == INT_MAX || ov > bv || (ov == bv && oe < be));
-      if (better) {
+      if (oe != INT_MAX && (be == INT_MAX || ov > bv || (ov == bv && oe < be))) {
         bv = ov;
         be = oe;
         ba = oa;
@@ -133,8 +209,7 @@ __device__ void topk_one(const TopkArgs& p, int t, int lane, int* s_ids, float* 
   } else if (p.renorm) {
     const float mx = wave_max(mine ? my_aux : -INFINITY);
     const float ex = mine ? expf(my_aux - mx) : 0.f;
-    const float tot = wave_sum(ex);
-    w = ex / tot;
+    w = ex / wave_sum(ex);
   } else {
     float mx = -INFINITY;
 #pragma unroll
@@ -145,502 +220,960 @@ __device__ void topk_one(const TopkArgs& p, int t, int lane, int* s_ids, float* 
 #pragma unroll
     for (int i = 0; i < NPL; ++i)
       if (lane + kWave * i < p.E) z += expf(lg[i] - mx);
-    z = wave_sum(z);
-    w = expf(my_aux - mx) / z;
+    w = expf(my_aux - mx) / wave_sum(z);
   }
   w *= p.scale;
   if (mine) {
     const int a = t * p.k + lane;
     if (p.ids_out) p.ids_out[a] = my_id;
     if (p.w_out) p.w_out[a] = w;
-    s_ids[a] = my_id;
-    s_w[a] = w;
+    s.ids[a] = my_id;
+    s.w[a] = w;
   }
 }
 
-// Exclusive scan of in[0, n) into out[0, n], out[n] = total; LDS arrays, whole block.
-__device__ void block_exclusive_scan(const int* in, int* out, int n, int (*s_scan)[16]) {
-  const int tid = threadIdx.x, nth = blockDim.x;
-  const int lane = tid & 63, wid = tid >> 6, nw = nth >> 6;
-  const int per = (n + nth - 1) / nth;
-  const int beg = min(n, tid * per), end = min(n, beg + per);
-  int local = 0;
-  for (int i = beg; i < end; ++i) local += in[i];
-  int v = local;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(v, o, kWave);
-    if (lane >= o) v += u;
+// Wave 0 scans cnt[0, n) into off[0, n] (exclusive, off[n] = total; also
+// copied to off_copy), lists the occupied entries in `active`, and gives each
+// occupied entry its index in the compacted list of small (cnt <= kTokInline)
+// or of large groups (slot[]).  Totals go to hdr[...] from lane 63.
+__device__ void wave0_scan(PlanShared& s, int n, int32_t* active, int32_t* off_copy,
+                           int32_t* hdr, int h_rows, int h_active, int h_small, int h_large,
+                           int lane) {
+  const int per = (n + 63) / 64;
+  const int b = min(n, lane * per), en = min(n, b + per);
+  int sc = 0, sa = 0, ss = 0;
+  for (int i = b; i < en; ++i) {
+    const int c = s.cnt[i];
+    sc += c;
+    sa += c > 0 ? 1 : 0;
+    ss += (c > 0 && c <= kTokInline) ? 1 : 0;
   }
-  if (lane == 63) s_scan[0][wid] = v;
-  __syncthreads();
-  if (wid == 0) {
-    const int tot = lane < nw ? s_scan[0][lane] : 0;
-    int w = tot;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int u = __shfl_up(w, o, kWave);
-      if (lane >= o) w += u;
+  const int ic = wave_incl_scan(sc, lane), ia = wave_incl_scan(sa, lane),
+            is = wave_incl_scan(ss, lane);
+  int rc = ic - sc, ra = ia - sa, rs = is - ss, rl = (ia - sa) - (is - ss);
+  for (int i = b; i < en; ++i) {
+    const int c = s.cnt[i];
+    s.off[i] = rc;
+    off_copy[i] = rc;
+    if (c > 0) {
+      active[ra++] = i;
+      s.slot[i] = c <= kTokInline ? rs++ : rl++;
     }
-    if (lane < nw) s_scan[1][lane] = w - tot;
+    rc += c;
   }
-  __syncthreads();
-  int run = s_scan[1][wid] + v - local;
-  for (int i = beg; i < end; ++i) {
-    out[i] = run;
-    run += in[i];
+  if (lane == 63) {
+    s.off[n] = ic;
+    off_copy[n] = ic;
+    hdr[h_rows] = ic;
+    hdr[h_active] = ia;
+    hdr[h_small] = is;
+    hdr[h_large] = ia - is;
   }
-  if (tid == nth - 1) out[n] = run;
-  __syncthreads();
 }
 
-// ---------------------------------------------------------------------------
-// Top-k for all tokens, then the dispatch plan, in one block.
-// ---------------------------------------------------------------------------
-template <int NPL>
-__global__ __launch_bounds__(kPlanThreads) void topk_dispatch_kernel(TopkArgs tk, DispatchArgs dp,
-                                                                     int do_topk, int do_dispatch) {
-  __shared__ int s_ids[MOE_MAX_ASSIGNMENTS];
-  __shared__ float s_w[MOE_MAX_ASSIGNMENTS];
-  __shared__ int s_a[MOE_MAX_EXPERTS];
-  __shared__ int s_b[MOE_MAX_EXPERTS + 1];
-  __shared__ unsigned char s_flag[MOE_MAX_DEPT_PAIRS];
-  __shared__ int s_scan[2][16];
-  __shared__ int s_invalid;
+// Work descriptor of occupied entry e: compacted small list at work[slot],
+// large list at work[cap + slot].
+__device__ __forceinline__ WorkDesc* work_of(WorkDesc* work, int cap, int c, int slot) {
+  return work + (c <= kTokInline ? slot : cap + slot);
+}
 
-  const int tid = threadIdx.x, nth = blockDim.x;
-  const int lane = tid & 63, wid = tid >> 6, nw = nth >> 6;
-  const int T = dp.T, k = dp.k, A = T * k;
-
-  if (do_topk) {
-    for (int t = wid; t < tk.T; t += nw) topk_one<NPL>(tk, t, lane, s_ids, s_w);
-  } else {
-    for (int a = tid; a < A; a += nth) {
-      s_ids[a] = dp.ids_in[a];
-      s_w[a] = dp.w_in[a];
-    }
-  }
-  if (!do_dispatch) return;
-  const int E = dp.E;
-  const moe_plan& P = dp.plan;
-  for (int e = tid; e < E; e += nth) s_a[e] = 0;
-  if (tid == 0) s_invalid = 0;
+// The dispatch plan from s.ids / s.w (T*k assignments).  Whole block.
+__device__ void plan_phase(PlanShared& s, const PlanArgs& pa) {
+  const int tid = threadIdx.x, nth = blockDim.x, lane = tid & 63, wid = tid >> 6;
+  const int T = pa.T, k = pa.k, E = pa.E, A = T * k;
+  const moe_plan& P = pa.plan;
+  for (int e = tid; e < E; e += nth) s.cnt[e] = 0;
+  if (tid == 0) s.invalid = 0;
   __syncthreads();
-
-  // rows per expert
   for (int a = tid; a < A; a += nth) {
-    const int e = s_ids[a];
+    const int e = s.ids[a];
     if (e >= 0 && e < E)
-      atomicAdd(&s_a[e], 1);
+      atomicAdd(&s.cnt[e], 1);
     else
-      atomicAdd(&s_invalid, 1);
+      atomicAdd(&s.invalid, 1);
   }
   __syncthreads();
-  block_exclusive_scan(s_a, s_b, E, s_scan);
-
+  if (wid == 0)
+    wave0_scan(s, E, P.active, P.offsets, P.header, MOE_PLAN_N_ROWS, MOE_PLAN_N_ACTIVE,
+               kHdrSmall, kHdrLarge, lane);
+  __syncthreads();
   // row of assignment a = offset of its expert + earlier assignments to it
   for (int a = tid; a < A; a += nth) {
-    const int e = s_ids[a];
+    const int e = s.ids[a];
     if (e >= 0 && e < E) {
       int rank = 0;
-      for (int b = 0; b < a; ++b) rank += (s_ids[b] == e);
-      const int row = s_b[e] + rank;
-      P.row_token[row] = a / k;
-      P.row_slot[row] = a % k;
+      for (int b = 0; b < a; ++b) rank += (s.ids[b] == e) ? 1 : 0;
+      const int row = s.off[e] + rank;
+      const int t = a / k;
+      P.row_token[row] = t;
+      P.row_slot[row] = a - t * k;
       P.row_expert[row] = e;
-      P.row_weight[row] = s_w[a];
+      P.row_weight[row] = s.w[a];
       P.inv_perm[a] = row;
+      if (s.cnt[e] <= kTokInline) pa.work[s.slot[e]].tok[rank] = t;
     } else {
       P.inv_perm[a] = -1;
     }
   }
   for (int e = tid; e < E; e += nth) {
-    P.counts[e] = s_a[e];
-    P.offsets[e] = s_b[e];
+    const int c = s.cnt[e];
+    P.counts[e] = c;
+    if (c > 0) {
+      WorkDesc* wd = work_of(pa.work, E, c, s.slot[e]);
+      wd->mat = e;
+      wd->r0 = s.off[e];
+      wd->n = c;
+    }
   }
-  if (tid == 0) P.offsets[E] = s_b[E];
-  __syncthreads();
-  for (int e = tid; e < E; e += nth) s_a[e] = s_a[e] > 0 ? 1 : 0;
-  __syncthreads();
-  block_exclusive_scan(s_a, s_b, E, s_scan);
-  for (int e = tid; e < E; e += nth)
-    if (s_a[e]) P.active[s_b[e]] = e;
-  if (tid == 0) {
-    P.header[MOE_PLAN_N_ROWS] = A - s_invalid;
-    P.header[MOE_PLAN_N_ACTIVE] = s_b[E];
-    P.header[MOE_PLAN_N_INVALID] = s_invalid;
-  }
-  __syncthreads();
-
-  if (dp.m > 0) {
-    // (token, department) pairs: department j is active for token t when t
-    // selected at least one of its experts; c_{t,j} sums those weights.
-    const int m = dp.m, G = E / m, TM = T * m;
-    for (int p = tid; p < TM; p += nth) {
-      const int t = p / m, J = p - t * m;
-      int has = 0;
-      for (int j = 0; j < k; ++j) {
-        const int e = s_ids[t * k + j];
-        if (e >= 0 && e < E && e / G == J) has = 1;
-      }
-      s_flag[p] = (unsigned char)has;
-    }
-    __syncthreads();
-    for (int J = tid; J < m; J += nth) {
-      int c = 0;
-      for (int t = 0; t < T; ++t) c += s_flag[t * m + J];
-      s_a[J] = c;
-    }
-    __syncthreads();
-    block_exclusive_scan(s_a, s_b, m, s_scan);
-    for (int p = tid; p < TM; p += nth) {
-      const int t = p / m, J = p - t * m;
-      if (s_flag[p]) {
-        int rank = 0;
-        for (int u = 0; u < t; ++u) rank += s_flag[u * m + J];
-        const int q = s_b[J] + rank;
-        float sc = 0.f;
-        for (int j = 0; j < k; ++j) {
-          const int e = s_ids[t * k + j];
-          if (e >= 0 && e < E && e / G == J) sc += s_w[t * k + j];
-        }
-        P.dept_row_token[q] = t;
-        P.dept_row_dept[q] = J;
-        P.dept_row_scale[q] = sc;
-        P.dept_inv[p] = q;
-      } else {
-        P.dept_inv[p] = -1;
-      }
-    }
-    for (int J = tid; J < m; J += nth) {
-      P.dept_counts[J] = s_a[J];
-      P.dept_offsets[J] = s_b[J];
-    }
+  if (tid == 0) P.header[MOE_PLAN_N_INVALID] = s.invalid;
+  if (pa.m <= 0) {
     if (tid == 0) {
-      P.dept_offsets[m] = s_b[m];
-      P.header[MOE_PLAN_N_DEPT_ROWS] = s_b[m];
+      P.header[MOE_PLAN_N_DEPT_ROWS] = 0;
+      P.header[MOE_PLAN_N_ACTIVE_DEPTS] = 0;
+      P.header[kHdrDeptSmall] = 0;
+      P.header[kHdrDeptLarge] = 0;
     }
-    __syncthreads();
-    for (int J = tid; J < m; J += nth) s_a[J] = s_a[J] > 0 ? 1 : 0;
-    __syncthreads();
-    block_exclusive_scan(s_a, s_b, m, s_scan);
-    for (int J = tid; J < m; J += nth)
-      if (s_a[J]) P.active_depts[s_b[J]] = J;
-    if (tid == 0) P.header[MOE_PLAN_N_ACTIVE_DEPTS] = s_b[m];
-  } else if (tid == 0) {
-    P.header[MOE_PLAN_N_DEPT_ROWS] = 0;
-    P.header[MOE_PLAN_N_ACTIVE_DEPTS] = 0;
+    return;
+  }
+  // (token, department) pairs: department j is active for token t when t
+  // selected at least one of its experts; c_{t,j} sums those weights.
+  const int m = pa.m, G = E / m, TM = T * m;
+  __syncthreads();
+  for (int p = tid; p < TM; p += nth) {
+    const int t = p / m, J = p - t * m;
+    int has = 0;
+    for (int j = 0; j < k; ++j) {
+      const int e = s.ids[t * k + j];
+      if (e >= 0 && e < E && e / G == J) has = 1;
+    }
+    s.flag[p] = (unsigned char)has;
+  }
+  __syncthreads();
+  for (int J = tid; J < m; J += nth) {
+    int c = 0;
+    for (int t = 0; t < T; ++t) c += s.flag[t * m + J];
+    s.cnt[J] = c;
+  }
+  __syncthreads();
+  if (wid == 0)
+    wave0_scan(s, m, P.active_depts, P.dept_offsets, P.header, MOE_PLAN_N_DEPT_ROWS,
+               MOE_PLAN_N_ACTIVE_DEPTS, kHdrDeptSmall, kHdrDeptLarge, lane);
+  __syncthreads();
+  for (int p = tid; p < TM; p += nth) {
+    const int t = p / m, J = p - t * m;
+    if (s.flag[p]) {
+      int rank = 0;
+      for (int u = 0; u < t; ++u) rank += s.flag[u * m + J];
+      const int q = s.off[J] + rank;
+      float sc = 0.f;
+      for (int j = 0; j < k; ++j) {
+        const int e = s.ids[t * k + j];
+        if (e >= 0 && e < E && e / G == J) sc += s.w[t * k + j];
+      }
+      P.dept_row_token[q] = t;
+      P.dept_row_dept[q] = J;
+      P.dept_row_scale[q] = sc;
+      P.dept_inv[p] = q;
+      if (s.cnt[J] <= kTokInline) pa.dwork[s.slot[J]].tok[rank] = t;
+    } else {
+      P.dept_inv[p] = -1;
+    }
+  }
+  for (int J = tid; J < m; J += nth) {
+    const int c = s.cnt[J];
+    P.dept_counts[J] = c;
+    if (c > 0) {
+      WorkDesc* wd = work_of(pa.dwork, m, c, s.slot[J]);
+      wd->mat = J;
+      wd->r0 = s.off[J];
+      wd->n = c;
+    }
   }
 }
 
+// Router logits split over d-chunks: wave (e, c) of the grid.
+template <typename T_>
+__global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs ra) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int gw = blockIdx.x * kWaves + wid;
+  const int e = gw % ra.E, c = gw / ra.E;
+  if (c < ra.n_chunks) router_partial<T_>(ra, e, c, lane);
+}
+
+// One block: sum the partial logits, top-k of every token (one wave per
+// token), then (do_plan) the dispatch plan.
+template <int NPL>
+__global__ __launch_bounds__(kPlanThreads) void topk_plan_kernel(RouteArgs ra, PlanArgs pa,
+                                                                 int do_plan) {
+  __shared__ PlanShared s;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  for (int t = wid; t < ra.T; t += nw) topk_one<NPL>(ra, t, lane, s);
+  if (!do_plan) return;
+  __syncthreads();
+  plan_phase(s, pa);
+}
+
+__global__ __launch_bounds__(kPlanThreads) void dispatch_kernel(const int32_t* ids, const float* w,
+                                                                PlanArgs pa) {
+  __shared__ PlanShared s;
+  for (int a = threadIdx.x; a < pa.T * pa.k; a += blockDim.x) {
+    s.ids[a] = ids[a];
+    s.w[a] = w[a];
+  }
+  __syncthreads();
+  plan_phase(s, pa);
+}
+
 // ---------------------------------------------------------------------------
-// Grouped expert GEMVs.  A block maps to (family, active slot, tile); slots
-// beyond the device-side active count exit at once, so the grid can be sized
-// on the host from T alone.
+// Grouped expert GEMVs.  Every family of matrices is scheduled as two parts
+// of one launch: the "small" part serves groups of at most four tokens with a
+// register GEMV (most routed experts at decode batch sizes), the "large" part
+// serves bigger groups (the shared expert, department backbones, hot experts)
+// with 16x16x32 bf16 matrix-core tiles.  A block skips slots of the other part.
 // ---------------------------------------------------------------------------
-struct BlockTask {
-  const void* gate;
-  const void* up;
-  const void* down;
-  const int* grp_token;
-  float* h;
-  float* out;
-  int rows, mat, r0, n, tile;
+struct Slot {
+  int mat, r0, n;
+  int t0, t1, t2, t3;      // the first tokens of the group (inline_tok)
+  bool inline_tok;
 };
 
-// Copies the fields of this block's family into registers (a pointer into the
-// kernel-argument struct would force it into scratch memory).
-__device__ __forceinline__ bool map_block(const SegSet& set, int T, bool gateup, BlockTask& bt) {
+// Part of this block (a reference into the kernel-argument block, read with
+// scalar loads; copying the part out would force a private stack copy).
+__device__ __forceinline__ const Family& block_part(const FamilySet& set, int& tile) {
   const int b = blockIdx.x;
-  int si = 0;
-  while (si + 1 < set.n && b >= set.blk_start[si + 1]) ++si;
-  const MatSeg S = set.s[si];
-  const int tiles = gateup ? S.tiles_gu : S.tiles_dn;
-  const int lb = b - set.blk_start[si];
-  const int slot = lb / tiles;
-  const int na = S.n_active ? *S.n_active : 1;
-  if (slot >= na) return false;
-  bt.gate = S.gate;
-  bt.up = S.up;
-  bt.down = S.down;
-  bt.grp_token = S.grp_token;
-  bt.h = S.h;
-  bt.out = S.out;
-  bt.rows = S.rows;
-  bt.tile = lb - slot * tiles;
-  bt.mat = S.active ? S.active[slot] : 0;
-  bt.r0 = S.grp_off ? S.grp_off[bt.mat] : 0;
-  bt.n = S.grp_off ? S.grp_off[bt.mat + 1] - bt.r0 : T;
-  return bt.n > 0;
+  int fi = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxParts; ++i)
+    if (i < set.n && b >= set.blk_start[i]) fi = i;
+  tile = b - set.blk_start[fi];
+  return set.f[fi];
 }
 
-// RW rows of gate and up starting at i0, against the n tokens of rows
-// r0..r0+n-1 in chunks of NT.  h[row][i] = SiLU(g) * u.
-template <typename T_, int RW, int NT>
-__device__ __forceinline__ void gateup_pass(const T_* __restrict__ Wg, const T_* __restrict__ Wu,
-                                            int d, int rows, int i0, const T_* __restrict__ x,
-                                            const int* __restrict__ grp_token, int r0, int n,
-                                            float* __restrict__ h, int lane) {
+// Slot and tile of this block in part F; false when the slot is not active,
+// does not belong to this part, or its descriptor is out of range (so even a
+// plan that was never written cannot send a block outside the weights or the
+// row buffers).
+__device__ __forceinline__ bool map_slot(const Family& F, int T, Slot& sl, int& tile) {
+  const int slot = tile / F.tiles;
+  tile -= slot * F.tiles;
+  if (F.work) {
+    if (slot >= *F.n_active) return false;
+    const WorkDesc wd = F.work[slot];
+    sl.mat = wd.mat;
+    sl.r0 = wd.r0;
+    sl.n = wd.n;
+    sl.t0 = wd.tok[0];
+    sl.t1 = wd.tok[1];
+    sl.t2 = wd.tok[2];
+    sl.t3 = wd.tok[3];
+    sl.inline_tok = sl.n <= kTokInline;
+    if (sl.mat < 0 || sl.mat >= F.n_mats || sl.r0 < 0 || sl.n > F.max_rows - sl.r0) return false;
+  } else {  // shared expert: every token, in order (row r is token r)
+    sl.mat = 0;
+    sl.r0 = 0;
+    sl.n = T;
+    sl.t0 = 0;
+    sl.t1 = 1;
+    sl.t2 = 2;
+    sl.t3 = 3;
+    sl.inline_tok = false;
+  }
+  if (sl.n <= 0) return false;
+  return F.large ? sl.n > kTokInline : sl.n <= kTokInline;
+}
+
+// Token of row tc + t of the group; t is a compile-time constant at every call
+// site, so the inline case folds to one register.  Rows at or past the end of
+// the group are never dereferenced and map to token 0.
+__device__ __forceinline__ int slot_token(const Slot& sl, const int* grp_token, int tc, int t,
+                                          int nv, int T) {
+  int tok;
+  if (sl.inline_tok)
+    tok = t == 0 ? sl.t0 : t == 1 ? sl.t1 : t == 2 ? sl.t2 : sl.t3;
+  else if (t >= nv)
+    tok = 0;
+  else
+    tok = grp_token ? grp_token[sl.r0 + tc + t] : tc + t;
+  return min(max(tok, 0), T - 1);
+}
+
+// Token of row t of a large group (per lane; t < n).
+__device__ __forceinline__ int lane_token(const Slot& sl, const int* grp_token, int t, int T) {
+  const int tok = grp_token ? grp_token[sl.r0 + t] : t;
+  return min(max(tok, 0), T - 1);
+}
+
+// Activation vectors of 8 elements and the 8-term dot product with a weight
+// vector.  bf16 x bf16 uses the packed dot instruction (products are exact in
+// fp32, two per instruction); fp32 uses plain fused multiply-adds.
+template <typename T_> struct X8;
+template <> struct X8<bf16_t> {
+  u32x4_t u;
+  __device__ __forceinline__ void load(const bf16_t* p) {
+    u = *reinterpret_cast<const u32x4_t*>(p);
+  }
+  __device__ __forceinline__ void zero() { u = u32x4_t{0, 0, 0, 0}; }
+};
+template <> struct X8<float> {
+  f32x4_t a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const f32x4_t*>(p);
+    b = *reinterpret_cast<const f32x4_t*>(p + 4);
+  }
+  __device__ __forceinline__ void zero() { a = b = f32x4_t{0.f, 0.f, 0.f, 0.f}; }
+};
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+__device__ __forceinline__ float dot8(const Raw8<bf16_t>& w, const X8<bf16_t>& x, float acc) {
+  acc = dot2_bf16(w.u.x, x.u.x, acc);
+  acc = dot2_bf16(w.u.y, x.u.y, acc);
+  acc = dot2_bf16(w.u.z, x.u.z, acc);
+  return dot2_bf16(w.u.w, x.u.w, acc);
+}
+__device__ __forceinline__ float dot8(const Raw8<float>& w, const X8<float>& x, float acc) {
+  acc = fmaf(w.a.x, x.a.x, acc);
+  acc = fmaf(w.a.y, x.a.y, acc);
+  acc = fmaf(w.a.z, x.a.z, acc);
+  acc = fmaf(w.a.w, x.a.w, acc);
+  acc = fmaf(w.b.x, x.b.x, acc);
+  acc = fmaf(w.b.y, x.b.y, acc);
+  acc = fmaf(w.b.z, x.b.z, acc);
+  return fmaf(w.b.w, x.b.w, acc);
+}
+
+// ---- small groups: register GEMV -------------------------------------------
+
+// RW rows of gate and up from row i0 against the (at most four) tokens of the
+// group.  h[row][i] = SiLU(g) * u.  Every load of step c+1 (weights and
+// activations) is issued before step c is used: the vector-memory counter
+// completes loads in order, so nothing requested after the next step's loads
+// may be needed first.
+template <typename T_, int RW>
+__device__ __forceinline__ void gu_small(const T_* __restrict__ Wg, const T_* __restrict__ Wu,
+                                         int d, int rows, int i0, const T_* __restrict__ x,
+                                         int T, const Slot& sl, const int* grp_token,
+                                         T_* __restrict__ h, int lane) {
+  constexpr int NT = kTokInline;
+  const int nv = sl.n;
   const T_* gp[RW];
   const T_* up[RW];
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
-    const int i = min(i0 + r, rows - 1);
-    gp[r] = Wg + (size_t)i * d;
-    up[r] = Wu + (size_t)i * d;
+    const size_t i = (size_t)min(i0 + r, rows - 1);
+    gp[r] = Wg + i * d;
+    up[r] = Wu + i * d;
   }
-  for (int tc = 0; tc < n; tc += NT) {
-    const int nv = min(NT, n - tc);
-    const T_* xp[NT];
+  const T_* xp[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) xp[t] = x + (size_t)slot_token(sl, grp_token, 0, t, nv, T) * d;
+  float ag[RW][NT], au[RW][NT];
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) ag[r][t] = au[r][t] = 0.f;
+
+  int c = lane * 8;
+  Raw8<T_> cg[RW], cu[RW];
+  X8<T_> cx[NT];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    if (c < d) {
+      cg[r].load(gp[r] + c);
+      cu[r].load(up[r] + c);
+    } else {
+      cg[r].zero();
+      cu[r].zero();
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (t < nv && c < d)
+      cx[t].load(xp[t] + c);
+    else
+      cx[t].zero();
+  }
+  for (; c < d; c += 8 * kWave) {
+    const int cn = c + 8 * kWave;
+    Raw8<T_> ng[RW], nu[RW];
+    X8<T_> nx[NT];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      if (cn < d) {
+        ng[r].load(gp[r] + cn);
+        nu[r].load(up[r] + cn);
+      } else {
+        ng[r].zero();
+        nu[r].zero();
+      }
+    }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const int rr = r0 + tc + min(t, nv - 1);
-      const int tok = grp_token ? grp_token[rr] : rr;
-      xp[t] = x + (size_t)tok * d;
+      if (t < nv && cn < d)
+        nx[t].load(xp[t] + cn);
+      else
+        nx[t].zero();
     }
-    float ag[RW][NT], au[RW][NT];
 #pragma unroll
-    for (int r = 0; r < RW; ++r)
+    for (int t = 0; t < NT; ++t) {
+      if (t < nv) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) ag[r][t] = au[r][t] = 0.f;
-    for (int c = lane * 8; c < d; c += 8 * kWave) {
-      float wg[RW][8], wu[RW][8];
-#pragma unroll
-      for (int r = 0; r < RW; ++r) {
-        load8_stream(gp[r] + c, wg[r]);
-        load8_stream(up[r] + c, wu[r]);
-      }
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        if (t < nv) {
-          float xv[8];
-          load8(xp[t] + c, xv);
-#pragma unroll
-          for (int r = 0; r < RW; ++r)
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-              ag[r][t] = fmaf(wg[r][q], xv[q], ag[r][t]);
-              au[r][t] = fmaf(wu[r][q], xv[q], au[r][t]);
-            }
+        for (int r = 0; r < RW; ++r) {
+          ag[r][t] = dot8(cg[r], cx[t], ag[r][t]);
+          au[r][t] = dot8(cu[r], cx[t], au[r][t]);
         }
       }
     }
-    constexpr int N = 2 * RW * NT;
-    constexpr int SH = 6 - Log2<N>::value;
-    float v[N];
 #pragma unroll
-    for (int r = 0; r < RW; ++r)
+    for (int r = 0; r < RW; ++r) {
+      cg[r] = ng[r];
+      cu[r] = nu[r];
+    }
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        v[r * NT + t] = ag[r][t];
-        v[RW * NT + r * NT + t] = au[r][t];
-      }
-    const float red = wave_reduce_scatter<N>(v, lane);
-    const float upv = __shfl_xor(red, 32, kWave);  // index + N/2 lives in lane ^ 32
-    const int idx = (lane >> SH) & (N - 1);
-    if (idx < N / 2 && (lane & ((1 << SH) - 1)) == 0) {
-      const int r = idx / NT, t = idx - (idx / NT) * NT;
-      if (t < nv && i0 + r < rows) h[(size_t)(r0 + tc + t) * rows + i0 + r] = silu(red) * upv;
+    for (int t = 0; t < NT; ++t) cx[t] = nx[t];
+  }
+  constexpr int N = 2 * RW * NT;
+  float v[N];
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      v[r * NT + t] = ag[r][t];
+      v[RW * NT + r * NT + t] = au[r][t];
+    }
+  group_reduce_scatter<N, 64>(v, lane);
+  // gate index idx and up index idx + N/2 sit in lanes l and l ^ 32
+  const float upv = __shfl_xor(v[0], 32, kWave);
+  constexpr int SH = 6 - Log2<N>::value;
+  const int idx = lane >> SH;
+  if (idx < N / 2 && (lane & ((1 << SH) - 1)) == 0) {
+    const int r = idx / NT, t = idx - (idx / NT) * NT;
+    if (t < nv && i0 + r < rows) store_act(h + (size_t)(sl.r0 + t) * rows + i0 + r, silu(v[0]) * upv);
+  }
+}
+
+// CG column groups of G = 64/LPR columns each (lane group g of LPR lanes takes
+// column cb + q*G + g) against the (at most four) rows of h of the group.
+// out[row][c] = W_down[c] . h[row].  Same load order as gu_small.
+template <typename T_, int LPR, int CG>
+__device__ __forceinline__ void dn_small(const T_* __restrict__ Wd, int d, int rows, int cb,
+                                         const T_* __restrict__ h, const Slot& sl,
+                                         float* __restrict__ out, int lane) {
+  constexpr int NT = kTokInline;
+  constexpr int G = 64 / LPR;
+  const int g = lane / LPR, j = lane - g * LPR;
+  const int nv = sl.n;
+  const T_* wp[CG];
+#pragma unroll
+  for (int q = 0; q < CG; ++q) wp[q] = Wd + (size_t)min(cb + q * G + g, d - 1) * rows;
+  const T_* hp[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) hp[t] = h + (size_t)(sl.r0 + min(t, nv - 1)) * rows;
+  float acc[CG][NT];
+#pragma unroll
+  for (int q = 0; q < CG; ++q)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[q][t] = 0.f;
+  int i = j * 8;
+  Raw8<T_> cw[CG];
+  X8<T_> ch[NT];
+#pragma unroll
+  for (int q = 0; q < CG; ++q) {
+    if (i < rows)
+      cw[q].load(wp[q] + i);
+    else
+      cw[q].zero();
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (t < nv && i < rows)
+      ch[t].load(hp[t] + i);
+    else
+      ch[t].zero();
+  }
+  for (; i < rows; i += 8 * LPR) {
+    const int in = i + 8 * LPR;
+    Raw8<T_> nw[CG];
+    X8<T_> nh[NT];
+#pragma unroll
+    for (int q = 0; q < CG; ++q) {
+      if (in < rows)
+        nw[q].load(wp[q] + in);
+      else
+        nw[q].zero();
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t < nv && in < rows)
+        nh[t].load(hp[t] + in);
+      else
+        nh[t].zero();
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      if (t < nv)
+#pragma unroll
+        for (int q = 0; q < CG; ++q) acc[q][t] = dot8(cw[q], ch[t], acc[q][t]);
+#pragma unroll
+    for (int q = 0; q < CG; ++q) cw[q] = nw[q];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) ch[t] = nh[t];
+  }
+  constexpr int N = CG * NT;
+  float v[N];
+#pragma unroll
+  for (int q = 0; q < CG; ++q)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) v[q * NT + t] = acc[q][t];
+  group_reduce_scatter<N, LPR>(v, lane);
+  if constexpr (N >= LPR) {
+    constexpr int PER = N / LPR;
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int idx = j * PER + p;
+      const int q = idx / NT, t = idx - (idx / NT) * NT;
+      const int c = cb + q * G + g;
+      if (t < nv && c < d) out[(size_t)(sl.r0 + t) * d + c] = v[p];
+    }
+  } else {
+    constexpr int SPAN = LPR / N;
+    if (j % SPAN == 0) {
+      const int idx = j / SPAN;
+      const int q = idx / NT, t = idx - (idx / NT) * NT;
+      const int c = cb + q * G + g;
+      if (t < nv && c < d) out[(size_t)(sl.r0 + t) * d + c] = v[0];
     }
   }
 }
 
-template <typename T_>
-__global__ __launch_bounds__(256) void gateup_kernel(SegSet set, const T_* __restrict__ x, int T,
-                                                     int d) {
-  BlockTask bt;
-  if (!map_block(set, T, true, bt)) return;
+// ---- large groups, bf16: 16x16x32 matrix-core tiles ------------------------
+//
+// Operand layout of v_mfma_f32_16x16x32_bf16 (lane l, g = l / 16): A row l%16
+// with k = 8g..8g+7; B column l%16 with the same k; D rows 4g..4g+3 of column
+// l%16.  A dot product is indifferent to the order of k, so each lane simply
+// takes the 16-byte chunk at 8g of every 32-element step.
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& u) {
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+__device__ __forceinline__ u32x4_t ld16(const bf16_t* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+__device__ __forceinline__ u32x4_t ld16_stream(const bf16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
+// 16 rows (i0..) of gate and up against 16*NC tokens (rows tc.. of the group).
+template <int NC>
+__device__ void gu_mfma(const bf16_t* __restrict__ Wg, const bf16_t* __restrict__ Wu, int d,
+                        int rows, int i0, const bf16_t* __restrict__ x, int T, const Slot& sl,
+                        const int* grp_token, int tc, bf16_t* __restrict__ h, int lane) {
+  const int r16 = lane & 15, g = lane >> 4;
+  const size_t row = (size_t)min(i0 + r16, rows - 1);
+  const bf16_t* ap = Wg + row * d + g * 8;
+  const bf16_t* bp = Wu + row * d + g * 8;
+  const bf16_t* xp[NC];
+  bool xv[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int t = tc + c * 16 + r16;
+    xv[c] = t < sl.n;
+    xp[c] = x + (size_t)(xv[c] ? lane_token(sl, grp_token, t, T) : 0) * d + g * 8;
+  }
+  f32x4_t accg[NC], accu[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) accg[c] = accu[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const u32x4_t z = {0, 0, 0, 0};
+  const bool lane_in = g * 8 < d;
+  int k = 0;
+  u32x4_t ca = lane_in ? ld16_stream(ap) : z, cb = lane_in ? ld16_stream(bp) : z, cx[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) cx[c] = (xv[c] && lane_in) ? ld16(xp[c]) : z;
+  for (; k < d; k += 32) {
+    const int kn = k + 32;
+    const bool nin = kn + g * 8 < d;
+    const u32x4_t na = nin ? ld16_stream(ap + kn) : z, nb = nin ? ld16_stream(bp + kn) : z;
+    u32x4_t nx[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) nx[c] = (xv[c] && nin) ? ld16(xp[c] + kn) : z;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      accg[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ca), as_bf16x8(cx[c]), accg[c], 0, 0, 0);
+      accu[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cb), as_bf16x8(cx[c]), accu[c], 0, 0, 0);
+    }
+    ca = na;
+    cb = nb;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) cx[c] = nx[c];
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int t = tc + c * 16 + r16;
+    if (t < sl.n) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = i0 + 4 * g + i;
+        if (rr < rows) store_act(h + (size_t)(sl.r0 + t) * rows + rr, silu(accg[c][i]) * accu[c][i]);
+      }
+    }
+  }
+}
+
+// 16 output columns (c0..) against 16*NC rows of h (rows tc.. of the group).
+template <int NC>
+__device__ void dn_mfma(const bf16_t* __restrict__ Wd, int d, int rows, int c0,
+                        const bf16_t* __restrict__ h, const Slot& sl, int tc,
+                        float* __restrict__ out, int lane) {
+  const int r16 = lane & 15, g = lane >> 4;
+  const bf16_t* ap = Wd + (size_t)min(c0 + r16, d - 1) * rows + g * 8;
+  const bf16_t* hp[NC];
+  bool hv[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int t = tc + c * 16 + r16;
+    hv[c] = t < sl.n;
+    hp[c] = h + (size_t)(sl.r0 + (hv[c] ? t : 0)) * rows + g * 8;
+  }
+  f32x4_t acc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const u32x4_t z = {0, 0, 0, 0};
+  const bool lane_in = g * 8 < rows;
+  u32x4_t ca = lane_in ? ld16_stream(ap) : z, ch[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) ch[c] = (hv[c] && lane_in) ? ld16(hp[c]) : z;
+  for (int k = 0; k < rows; k += 32) {
+    const int kn = k + 32;
+    const bool nin = kn + g * 8 < rows;
+    const u32x4_t na = nin ? ld16_stream(ap + kn) : z;
+    u32x4_t nh[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) nh[c] = (hv[c] && nin) ? ld16(hp[c] + kn) : z;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ca), as_bf16x8(ch[c]), acc[c], 0, 0, 0);
+    ca = na;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) ch[c] = nh[c];
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int t = tc + c * 16 + r16;
+    if (t < sl.n) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int col = c0 + 4 * g + i;
+        if (col < d) out[(size_t)(sl.r0 + t) * d + col] = acc[c][i];
+      }
+    }
+  }
+}
+
+// ---- large groups, fp32 layers: plain GEMV ---------------------------------
+
+// RW rows of gate and up against NT tokens from row tc of the group, no
+// prefetch (fp32 layers are small).
+template <int RW, int NT>
+__device__ void gu_plain(const float* __restrict__ Wg, const float* __restrict__ Wu, int d,
+                         int rows, int i0, const float* __restrict__ x, int T, const Slot& sl,
+                         const int* grp_token, int tc, float* __restrict__ h, int lane) {
+  const int nv = min(NT, sl.n - tc);
+  float ag[RW][NT], au[RW][NT];
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) ag[r][t] = au[r][t] = 0.f;
+  for (int c = lane * 8; c < d; c += 8 * kWave) {
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      Raw8<float> wg, wu;
+      const size_t i = (size_t)min(i0 + r, rows - 1);
+      wg.load(Wg + i * d + c);
+      wu.load(Wu + i * d + c);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if (t < nv) {
+          X8<float> xv;
+          xv.load(x + (size_t)lane_token(sl, grp_token, tc + t, T) * d + c);
+          ag[r][t] = dot8(wg, xv, ag[r][t]);
+          au[r][t] = dot8(wu, xv, au[r][t]);
+        }
+      }
+    }
+  }
+  constexpr int N = 2 * RW * NT;
+  float v[N];
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      v[r * NT + t] = ag[r][t];
+      v[RW * NT + r * NT + t] = au[r][t];
+    }
+  group_reduce_scatter<N, 64>(v, lane);
+  const float upv = __shfl_xor(v[0], 32, kWave);
+  constexpr int SH = 6 - Log2<N>::value;
+  const int idx = lane >> SH;
+  if (idx < N / 2 && (lane & ((1 << SH) - 1)) == 0) {
+    const int r = idx / NT, t = idx - (idx / NT) * NT;
+    if (t < nv && i0 + r < rows) h[(size_t)(sl.r0 + tc + t) * rows + i0 + r] = silu(v[0]) * upv;
+  }
+}
+
+// CW columns from c0 against NT rows of h from row tc of the group.
+template <int CW, int NT>
+__device__ void dn_plain(const float* __restrict__ Wd, int d, int rows, int c0,
+                         const float* __restrict__ h, const Slot& sl, int tc,
+                         float* __restrict__ out, int lane) {
+  const int nv = min(NT, sl.n - tc);
+  float acc[CW][NT];
+#pragma unroll
+  for (int q = 0; q < CW; ++q)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[q][t] = 0.f;
+  for (int i = lane * 8; i < rows; i += 8 * kWave) {
+#pragma unroll
+    for (int q = 0; q < CW; ++q) {
+      Raw8<float> w;
+      w.load(Wd + (size_t)min(c0 + q, d - 1) * rows + i);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if (t < nv) {
+          X8<float> hv;
+          hv.load(h + (size_t)(sl.r0 + tc + t) * rows + i);
+          acc[q][t] = dot8(w, hv, acc[q][t]);
+        }
+      }
+    }
+  }
+  constexpr int N = CW * NT;
+  float v[N];
+#pragma unroll
+  for (int q = 0; q < CW; ++q)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) v[q * NT + t] = acc[q][t];
+  group_reduce_scatter<N, 64>(v, lane);
+  constexpr int SH = 6 - Log2<N>::value;
+  const int idx = lane >> SH;
+  if ((lane & ((1 << SH) - 1)) == 0) {
+    const int q = idx / NT, t = idx - (idx / NT) * NT;
+    if (t < nv && c0 + q < d) out[(size_t)(sl.r0 + tc + t) * d + c0 + q] = v[0];
+  }
+}
+
+// ---- kernels -----------------------------------------------------------------
+
+// Small groups: each wave owns RPW rows, taken RW at a time.
+template <typename T_, int RPW, int RW>
+__global__ __launch_bounds__(kThreads) void gateup_kernel(FamilySet set, const T_* __restrict__ x,
+                                                          int T, int d) {
+  int tile;
+  const Family& F = block_part(set, tile);
+  Slot sl;
+  if (!map_slot(F, T, sl, tile)) return;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int rows = bt.rows;
-  const int i0 = bt.tile * kGuTile + wid * kRowsPerWave;
-  if (i0 >= rows) return;
-  const size_t mstride = (size_t)rows * d;
-  const T_* Wg = static_cast<const T_*>(bt.gate) + (size_t)bt.mat * mstride;
-  const T_* Wu = static_cast<const T_*>(bt.up) + (size_t)bt.mat * mstride;
-  if (bt.n <= 4) {
-    gateup_pass<T_, 4, 4>(Wg, Wu, d, rows, i0, x, bt.grp_token, bt.r0, bt.n, bt.h, lane);
-  } else if (bt.n <= 8) {
-    gateup_pass<T_, 2, 8>(Wg, Wu, d, rows, i0, x, bt.grp_token, bt.r0, bt.n, bt.h, lane);
-    gateup_pass<T_, 2, 8>(Wg, Wu, d, rows, i0 + 2, x, bt.grp_token, bt.r0, bt.n, bt.h, lane);
+  const size_t ms = (size_t)F.rows * d;
+  const T_* Wg = static_cast<const T_*>(F.gate) + (size_t)sl.mat * ms;
+  const T_* Wu = static_cast<const T_*>(F.up) + (size_t)sl.mat * ms;
+  T_* h = static_cast<T_*>(F.h);
+  if (!F.large) {
+    const int i0 = tile * (kWaves * RPW) + wid * RPW;
+#pragma unroll 1
+    for (int r = 0; r < RPW && i0 + r < F.rows; r += RW)
+      gu_small<T_, RW>(Wg, Wu, d, F.rows, i0 + r, x, T, sl, F.grp_token, h, lane);
+    return;
+  }
+  const int i0 = tile * (kWaves * 16) + wid * 16;
+  if (i0 >= F.rows) return;
+  if constexpr (sizeof(T_) == 2) {
+#pragma unroll 1
+    for (int tc = 0; tc < sl.n; tc += 32) {
+      if (sl.n - tc > 16)
+        gu_mfma<2>(Wg, Wu, d, F.rows, i0, x, T, sl, F.grp_token, tc, h, lane);
+      else
+        gu_mfma<1>(Wg, Wu, d, F.rows, i0, x, T, sl, F.grp_token, tc, h, lane);
+    }
   } else {
 #pragma unroll 1
-    for (int r = 0; r < kRowsPerWave; ++r)
-      gateup_pass<T_, 1, 16>(Wg, Wu, d, rows, i0 + r, x, bt.grp_token, bt.r0, bt.n, bt.h, lane);
+    for (int r = 0; r < 16; r += 2)
+#pragma unroll 1
+      for (int tc = 0; tc < sl.n; tc += 8)
+        gu_plain<2, 8>(Wg, Wu, d, F.rows, i0 + r, x, T, sl, F.grp_token, tc, h, lane);
   }
 }
 
-// CW output columns from c0 (rows of W_down [d][rows]) against the n rows of
-// h from r0, in chunks of NT.  out[row][c] = W_down[c] . h[row].
-template <typename T_, int CW, int NT>
-__device__ __forceinline__ void down_pass(const T_* __restrict__ Wd, int d, int rows, int c0,
-                                          const float* __restrict__ h, int r0, int n,
-                                          float* __restrict__ out, int lane) {
-  const T_* wp[CW];
-#pragma unroll
-  for (int cc = 0; cc < CW; ++cc) wp[cc] = Wd + (size_t)min(c0 + cc, d - 1) * rows;
-  for (int tc = 0; tc < n; tc += NT) {
-    const int nv = min(NT, n - tc);
-    const float* hp[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) hp[t] = h + (size_t)(r0 + tc + min(t, nv - 1)) * rows;
-    float acc[CW][NT];
-#pragma unroll
-    for (int cc = 0; cc < CW; ++cc)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) acc[cc][t] = 0.f;
-    for (int i = lane * 8; i < rows; i += 8 * kWave) {
-      float wv[CW][8];
-#pragma unroll
-      for (int cc = 0; cc < CW; ++cc) load8_stream(wp[cc] + i, wv[cc]);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        if (t < nv) {
-          float hv[8];
-          load8(hp[t] + i, hv);
-#pragma unroll
-          for (int cc = 0; cc < CW; ++cc)
-#pragma unroll
-            for (int q = 0; q < 8; ++q) acc[cc][t] = fmaf(wv[cc][q], hv[q], acc[cc][t]);
-        }
-      }
-    }
-    constexpr int N = CW * NT;
-    constexpr int SH = 6 - Log2<N>::value;
-    float v[N];
-#pragma unroll
-    for (int cc = 0; cc < CW; ++cc)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) v[cc * NT + t] = acc[cc][t];
-    const float red = wave_reduce_scatter<N>(v, lane);
-    const int idx = (lane >> SH) & (N - 1);
-    if ((lane & ((1 << SH) - 1)) == 0) {
-      const int cc = idx / NT, t = idx - (idx / NT) * NT;
-      if (t < nv && c0 + cc < d) out[(size_t)(r0 + tc + t) * d + c0 + cc] = red;
-    }
-  }
-}
-
-template <typename T_>
-__global__ __launch_bounds__(256) void down_kernel(SegSet set, int T, int d) {
-  BlockTask bt;
-  if (!map_block(set, T, false, bt)) return;
+template <typename T_, int LPR, int CG>
+__global__ __launch_bounds__(kThreads) void down_kernel(FamilySet set, int T, int d) {
+  int tile;
+  const Family& F = block_part(set, tile);
+  Slot sl;
+  if (!map_slot(F, T, sl, tile)) return;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int rows = bt.rows;
-  const int c0 = bt.tile * kDnTile + wid * kColsPerWave;
+  const T_* Wd = static_cast<const T_*>(F.down) + (size_t)sl.mat * F.rows * d;
+  const T_* h = static_cast<const T_*>(F.h);
+  if (!F.large) {
+    constexpr int CPW = CG * (64 / LPR);
+    const int cb = tile * (kWaves * CPW) + wid * CPW;
+    if (cb < d) dn_small<T_, LPR, CG>(Wd, d, F.rows, cb, h, sl, F.out, lane);
+    return;
+  }
+  const int c0 = tile * (kWaves * 16) + wid * 16;
   if (c0 >= d) return;
-  const T_* Wd = static_cast<const T_*>(bt.down) + (size_t)bt.mat * rows * d;
-  if (bt.n <= 4) {
-    down_pass<T_, 4, 4>(Wd, d, rows, c0, bt.h, bt.r0, bt.n, bt.out, lane);
-  } else if (bt.n <= 8) {
-    down_pass<T_, 2, 8>(Wd, d, rows, c0, bt.h, bt.r0, bt.n, bt.out, lane);
-    down_pass<T_, 2, 8>(Wd, d, rows, c0 + 2, bt.h, bt.r0, bt.n, bt.out, lane);
+  if constexpr (sizeof(T_) == 2) {
+#pragma unroll 1
+    for (int tc = 0; tc < sl.n; tc += 32) {
+      if (sl.n - tc > 16)
+        dn_mfma<2>(Wd, d, F.rows, c0, h, sl, tc, F.out, lane);
+      else
+        dn_mfma<1>(Wd, d, F.rows, c0, h, sl, tc, F.out, lane);
+    }
   } else {
 #pragma unroll 1
-    for (int cc = 0; cc < kColsPerWave; ++cc)
-      down_pass<T_, 1, 16>(Wd, d, rows, c0 + cc, bt.h, bt.r0, bt.n, bt.out, lane);
+    for (int q = 0; q < 16; q += 2)
+#pragma unroll 1
+      for (int tc = 0; tc < sl.n; tc += 8)
+        dn_plain<2, 8>(Wd, d, F.rows, c0 + q, h, sl, tc, F.out, lane);
   }
 }
 
-// ---------------------------------------------------------------------------
-// Combine: one thread per (token, column); slot order, then departments
-// ascending, then the shared expert.
-// ---------------------------------------------------------------------------
+// One block per (256 columns, token): every thread one output element.
 template <typename AT>
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, AT* __restrict__ y) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+__global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a, AT* __restrict__ y) {
+  const int c = blockIdx.x * kThreads + threadIdx.x;
   const int t = blockIdx.y;
   if (c >= a.d) return;
   float acc = 0.f;
   for (int j = 0; j < a.k; ++j) {
     const int r = a.inv_perm[t * a.k + j];
-    if (r >= 0) acc = fmaf(a.row_weight[r], a.row_out[(size_t)r * a.d + c], acc);
+    if (r >= 0 && r < a.max_rows) acc = fmaf(a.row_weight[r], a.row_out[(size_t)r * a.d + c], acc);
   }
   if (a.dept_out) {
     for (int J = 0; J < a.m; ++J) {
       const int q = a.dept_inv[t * a.m + J];
-      if (q >= 0) acc = fmaf(a.dept_scale[q], a.dept_out[(size_t)q * a.d + c], acc);
+      if (q >= 0 && q < a.max_dept_rows)
+        acc = fmaf(a.dept_scale[q], a.dept_out[(size_t)q * a.d + c], acc);
     }
   }
   if (a.shared_out) acc += a.shared_out[(size_t)t * a.d + c];
   store_act(y + (size_t)t * a.d + c, acc);
 }
 
+__global__ void zero_kernel(unsigned int* p, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_router_logits(int w_dtype, const void* x, const void* w_router, int T, int d,
-                                int E, float* logits, hipStream_t st) {
-  const dim3 grid((E + 3) / 4), block(256);
-  if (w_dtype == MOE_BF16)
-    hipLaunchKernelGGL(router_logits_kernel<bf16_t>, grid, block, 0, st,
-                       static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(w_router), T, d,
-                       E, logits);
-  else
-    hipLaunchKernelGGL(router_logits_kernel<float>, grid, block, 0, st,
-                       static_cast<const float*>(x), static_cast<const float*>(w_router), T, d, E,
-                       logits);
-  return hipGetLastError();
-}
-
-hipError_t launch_topk_dispatch(const TopkArgs* topk, const DispatchArgs* disp, hipStream_t st) {
-  TopkArgs tk{};
-  if (topk) tk = *topk;
-  DispatchArgs dp{};
-  if (disp) dp = *disp;
-  const int do_topk = topk != nullptr, do_dispatch = disp != nullptr;
-  if (do_topk && !do_dispatch) {  // the kernel reads T and k from the dispatch arguments
-    dp.T = tk.T;
-    dp.k = tk.k;
-  }
-  const int E = do_topk ? tk.E : dp.E;
+template <typename T_>
+static hipError_t launch_route_t(const RouteArgs& ra, const PlanArgs* pa, hipStream_t st) {
+  const int waves = ra.E * ra.n_chunks;
+  hipLaunchKernelGGL((route_kernel<T_>), dim3((waves + kWaves - 1) / kWaves), dim3(kThreads), 0,
+                     st, ra);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  PlanArgs p{};
+  if (pa) p = *pa;
+  const int do_plan = pa != nullptr;
   const dim3 grid(1), block(kPlanThreads);
-#define MOE_TOPK_LAUNCH(NPL)                                                                   \
-  hipLaunchKernelGGL(topk_dispatch_kernel<NPL>, grid, block, 0, st, tk, dp, do_topk, do_dispatch)
-  if (!do_topk || E <= 64)
-    MOE_TOPK_LAUNCH(1);
-  else if (E <= 128)
-    MOE_TOPK_LAUNCH(2);
-  else if (E <= 256)
-    MOE_TOPK_LAUNCH(4);
-  else if (E <= 512)
-    MOE_TOPK_LAUNCH(8);
-  else if (E <= 1024)
-    MOE_TOPK_LAUNCH(16);
+  if (ra.E <= 64)
+    hipLaunchKernelGGL((topk_plan_kernel<1>), grid, block, 0, st, ra, p, do_plan);
+  else if (ra.E <= 128)
+    hipLaunchKernelGGL((topk_plan_kernel<2>), grid, block, 0, st, ra, p, do_plan);
+  else if (ra.E <= 256)
+    hipLaunchKernelGGL((topk_plan_kernel<4>), grid, block, 0, st, ra, p, do_plan);
+  else if (ra.E <= 512)
+    hipLaunchKernelGGL((topk_plan_kernel<8>), grid, block, 0, st, ra, p, do_plan);
+  else if (ra.E <= 1024)
+    hipLaunchKernelGGL((topk_plan_kernel<16>), grid, block, 0, st, ra, p, do_plan);
   else
-    MOE_TOPK_LAUNCH(32);
-#undef MOE_TOPK_LAUNCH
+    hipLaunchKernelGGL((topk_plan_kernel<32>), grid, block, 0, st, ra, p, do_plan);
   return hipGetLastError();
 }
 
-hipError_t launch_gateup(int w_dtype, const SegSet& set, const void* x, int T, int d,
-                         hipStream_t st) {
-  const int blocks = set.blk_start[set.n];
-  if (blocks <= 0) return hipSuccess;
-  if (w_dtype == MOE_BF16)
-    hipLaunchKernelGGL(gateup_kernel<bf16_t>, dim3(blocks), dim3(256), 0, st, set,
-                       static_cast<const bf16_t*>(x), T, d);
-  else
-    hipLaunchKernelGGL(gateup_kernel<float>, dim3(blocks), dim3(256), 0, st, set,
-                       static_cast<const float*>(x), T, d);
+hipError_t launch_route(int w_dtype, const RouteArgs& ra, const PlanArgs* pa, hipStream_t st) {
+  return w_dtype == MOE_BF16 ? launch_route_t<bf16_t>(ra, pa, st)
+                             : launch_route_t<float>(ra, pa, st);
+}
+
+hipError_t launch_dispatch(const int32_t* ids, const float* w, const PlanArgs& pa,
+                           hipStream_t st) {
+  hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kPlanThreads), 0, st, ids, w, pa);
   return hipGetLastError();
 }
 
-hipError_t launch_down(int w_dtype, const SegSet& set, int T, int d, hipStream_t st) {
-  const int blocks = set.blk_start[set.n];
-  if (blocks <= 0) return hipSuccess;
-  if (w_dtype == MOE_BF16)
-    hipLaunchKernelGGL(down_kernel<bf16_t>, dim3(blocks), dim3(256), 0, st, set, T, d);
+template <typename T_>
+static hipError_t launch_gateup_t(const FamilySet& set, const T_* x, int T, int d, int rpw,
+                                  int rw, hipStream_t st) {
+  const dim3 grid(set.blk_start[set.n]), block(kThreads);
+#define MOE_GU(P, R) hipLaunchKernelGGL((gateup_kernel<T_, P, R>), grid, block, 0, st, set, x, T, d)
+  if (rpw >= 8)
+    MOE_GU(8, 2);
+  else if (rpw == 4 && rw >= 4)
+    MOE_GU(4, 4);
+  else if (rpw == 4)
+    MOE_GU(4, 2);
+  else if (rpw == 2 && rw >= 2)
+    MOE_GU(2, 2);
+  else if (rpw == 2)
+    MOE_GU(2, 1);
   else
-    hipLaunchKernelGGL(down_kernel<float>, dim3(blocks), dim3(256), 0, st, set, T, d);
+    MOE_GU(1, 1);
+#undef MOE_GU
   return hipGetLastError();
+}
+
+hipError_t launch_gateup(int w_dtype, const FamilySet& set, const void* x, int T, int d,
+                         int rows_per_wave, int rows_per_pass, hipStream_t st) {
+  if (set.blk_start[set.n] <= 0) return hipSuccess;
+  return w_dtype == MOE_BF16 ? launch_gateup_t<bf16_t>(set, static_cast<const bf16_t*>(x), T, d,
+                                                       rows_per_wave, rows_per_pass, st)
+                             : launch_gateup_t<float>(set, static_cast<const float*>(x), T, d,
+                                                      rows_per_wave, rows_per_pass, st);
+}
+
+template <typename T_>
+static hipError_t launch_down_t(const FamilySet& set, int T, int d, int lpr, int cg,
+                                hipStream_t st) {
+  const dim3 grid(set.blk_start[set.n]), block(kThreads);
+#define MOE_DOWN(L, C) hipLaunchKernelGGL((down_kernel<T_, L, C>), grid, block, 0, st, set, T, d)
+  if (lpr == 16) {
+    if (cg >= 4) MOE_DOWN(16, 4); else MOE_DOWN(16, 2);
+  } else if (lpr == 32) {
+    if (cg >= 4) MOE_DOWN(32, 4); else MOE_DOWN(32, 2);
+  } else {
+    if (cg >= 4) MOE_DOWN(64, 4); else MOE_DOWN(64, 2);
+  }
+#undef MOE_DOWN
+  return hipGetLastError();
+}
+
+hipError_t launch_down(int w_dtype, const FamilySet& set, int T, int d, int lpr, int col_groups,
+                       hipStream_t st) {
+  if (set.blk_start[set.n] <= 0) return hipSuccess;
+  return w_dtype == MOE_BF16 ? launch_down_t<bf16_t>(set, T, d, lpr, col_groups, st)
+                             : launch_down_t<float>(set, T, d, lpr, col_groups, st);
 }
 
 hipError_t launch_combine(int act_dtype, const CombineArgs& a, void* y, hipStream_t st) {
-  const dim3 grid((a.d + 255) / 256, a.T), block(256);
+  const dim3 grid((a.d + kThreads - 1) / kThreads, a.T), block(kThreads);
   if (act_dtype == MOE_BF16)
     hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, block, 0, st, a, static_cast<bf16_t*>(y));
   else
     hipLaunchKernelGGL(combine_kernel<float>, grid, block, 0, st, a, static_cast<float*>(y));
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(unsigned int* p, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const int blocks = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
+  hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, st, p, n);
   return hipGetLastError();
 }
 

@@ -29,7 +29,8 @@ def lib():
 def test_header_declares_the_calls():
     decl = _declared_functions()
     for name in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
-                 "moe_layer_decode", "moe_workspace_bytes", "moe_status_string"):
+                 "moe_layer_decode", "moe_workspace_bytes", "moe_workspace_init",
+                 "moe_status_string"):
         assert name in decl
     assert sorted(M.EXPORTED_SYMBOLS) == decl
 

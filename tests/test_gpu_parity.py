@@ -263,12 +263,13 @@ def test_expert_ffn_and_combine_parity(case):
     M.moe_expert_ffn(desc, w, x, plan, ws, row_out, dept_out, shared_out)
     wc = {kk: v.cpu() for kk, v in w.items()}
     o_row, o_dept, o_sh = O.expert_outputs(x.cpu(), wc, op, E, m, dept_split=bool(m))
-    # row outputs are fp32 whatever the input dtype: fp32 tolerance
-    assert_close(to_np(row_out[:op["n_rows"]]), o_row, "f32", "row_out")
+    # row outputs are fp32; bf16 layers keep the intermediate h in bf16, so
+    # they get the bf16 layer tolerance
+    assert_close(to_np(row_out[:op["n_rows"]]), o_row, dt, "row_out")
     if m:
-        assert_close(to_np(dept_out[:op["n_dept_rows"]]), o_dept, "f32", "dept_out")
+        assert_close(to_np(dept_out[:op["n_dept_rows"]]), o_dept, dt, "dept_out")
     if Is:
-        assert_close(to_np(shared_out), o_sh, "f32", "shared_out")
+        assert_close(to_np(shared_out), o_sh, dt, "shared_out")
     y = torch.empty(T, d, dtype=tdt, device=DEV)
     M.moe_combine(desc, plan, row_out, dept_out, shared_out, y)
     # combine checked against the oracle combine of the GPU's own row outputs
