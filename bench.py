@@ -49,8 +49,60 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--profile-pass", action="store_true",
-                   help="few steps + a calibration copy, for counter runs")
+                   help="headline batch only, 20 eager steps + a 1 GiB calibration copy "
+                        "(for rocprofv3 --pmc runs)")
+    p.add_argument("--summarize-trace", type=str, default=None,
+                   help="print per-kernel, per-grid-size mean durations of a rocprofv3 "
+                        "kernel_trace.csv and exit")
+    p.add_argument("--summarize-pmc", type=str, default=None,
+                   help="print per-kernel, per-grid-size mean counter values of a rocprofv3 "
+                        "counter_collection.csv and exit")
+    p.add_argument("--source-hash", action="store_true",
+                   help="print the hash of the kernel sources the counter summary refers to")
     return p.parse_args()
+
+
+def _short(name):
+    import re
+    m = re.search(r"moe::(\w+)", name)
+    if m:
+        return m.group(1)
+    if "at::native" in name:
+        return "torch"
+    return name[:48]
+
+
+def summarize_trace(path):
+    """Mean kernel durations of a rocprofv3 kernel trace, per kernel and grid
+    size (the grid size tells the decode batches apart)."""
+    import csv
+    from collections import defaultdict
+    acc = defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        key = (_short(r["Kernel_Name"]), int(r["Grid_Size_X"]), int(r["Grid_Size_Y"]))
+        acc[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print("| kernel | grid x | grid y | calls | mean us | min us |")
+    print("|---|---|---|---|---|---|")
+    for (k, gx, gy), v in sorted(acc.items()):
+        if k == "torch":
+            continue
+        print(f"| {k} | {gx} | {gy} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} |")
+
+
+def summarize_pmc(path):
+    """Mean per-dispatch counter values of a rocprofv3 --pmc run, per kernel
+    and grid size."""
+    import csv
+    from collections import defaultdict
+    acc = defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        key = (_short(r["Kernel_Name"]), int(r.get("Grid_Size", r.get("Grid_Size_X", 0))),
+               r["Counter_Name"])
+        acc[key].append(float(r["Counter_Value"]))
+    print("| kernel | grid | counter | dispatches | mean value |")
+    print("|---|---|---|---|---|")
+    for (k, g, c), v in sorted(acc.items()):
+        print(f"| {k} | {g} | {c} | {len(v)} | {sum(v) / len(v):.1f} |")
 
 
 def desc_of(M, shape, max_tokens):
@@ -164,11 +216,12 @@ class Runner:
         return us, reps * self.R, same
 
     def stage_times(self, steps):
-        """Mean per-stage device time over `steps` eager steps (HIP events
-        recorded by the library on the launch stream)."""
+        """Mean kernel time per stage over `steps` eager steps: the library
+        launches each stage's kernel with start/stop events the runtime writes
+        at kernel begin/end (on the launch stream)."""
         import torch
         M = self.M
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(M.N_STAGES + 1)]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * M.N_STAGES)]
                for _ in range(steps)]
         for e in evs:  # create the events before handing their handles over
             for ev in e:
@@ -180,8 +233,43 @@ class Runner:
         tot = [0.0] * M.N_STAGES
         for e in evs:
             for s in range(M.N_STAGES):
-                tot[s] += e[s].elapsed_time(e[s + 1]) * 1e3
+                tot[s] += e[2 * s].elapsed_time(e[2 * s + 1]) * 1e3
         return {M.STAGE_NAMES[s]: tot[s] / steps for s in range(M.N_STAGES)}
+
+
+KERNEL_SOURCES = ("moe_layer_decode_amd/csrc/moe_kernels.hip",
+                  "moe_layer_decode_amd/csrc/moe_device.h",
+                  "moe_layer_decode_amd/csrc/moe_internal.h")
+PMC_SUMMARY = "profiles/pmc_gateup_qwen3_30b_a3b_batch16.md"
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per gate/up launch from the committed counter summary, only
+    if it was taken on the kernel sources as they are now (else None)."""
+    path = os.path.join(ROOT, PMC_SUMMARY)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and line.split(":", 1)[0].strip() in ("kernel_source_sha256",
+                                                            "traffic_bytes_per_launch"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(shape, T, base, seconds):
@@ -215,6 +303,15 @@ def cpu_baseline(shape, T, base, seconds):
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
+        return
+    if args.source_hash:
+        print(kernel_source_hash())
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(this layer's hot path runs on a single MI355X)", file=sys.stderr)
@@ -232,13 +329,15 @@ def main():
     base = moe_synth.make_layer(shape, 0, dev)
 
     if args.profile_pass:
-        for T in batches:
-            r = Runner(M, moe_synth, shape, T, dev, base=base)
-            r.time_eager(max(10, args.steps), 2)
-        n = 1 << 28  # 1 GiB copy: counter calibration
-        a = torch.empty(n // 4, dtype=torch.float32, device=dev).fill_(1.0)
-        b = torch.empty_like(a)
-        b.copy_(a)
+        r = Runner(M, moe_synth, shape, head_T, dev, base=base)
+        r.time_eager(20, 2)
+        # counter calibration: a plain 1 GiB read (sum) and a plain 1 GiB write (fill)
+        n = 1 << 30
+        a = torch.empty(n // 4, dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        a.fill_(1.0)
+        torch.cuda.synchronize()
+        log(f"calibration sum {float(a.sum()):.0f}")
         torch.cuda.synchronize()
         log("profile pass done")
         return
@@ -293,7 +392,8 @@ def main():
         "batches": per_batch,
         "roofline": {"bound": "hbm", "kernel": "gateup_kernel", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "algorithmic_bytes_per_launch": gu,
+                     "traffic": measured_traffic() if shape.name == HEADLINE and head_T == 16 else None,
+                     "algorithmic_bytes_per_launch": gu,
                      "launch_us": round(stages["gateup"], 2)},
     }
     if not args.no_cpu_baseline:

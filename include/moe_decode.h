@@ -150,13 +150,15 @@ typedef struct {
   int32_t n_tokens;         /* T the plan was built for (host copy) */
 } moe_plan;
 
-/* Stage events for moe_layer_decode: stage_events[i] is recorded on the
- * stream right before stage i is launched, stage_events[MOE_N_STAGES] after
- * the last one (a stage fused into its predecessor gets an empty interval). */
-#define MOE_STAGE_ROUTE 0     /* router logits + top-k + weights */
-#define MOE_STAGE_DISPATCH 1  /* counting sort, inverse map, department pairs */
-#define MOE_STAGE_GATEUP 2    /* grouped gate/up GEMV with SiLU(g)*u */
-#define MOE_STAGE_DOWN 3      /* grouped down GEMV */
+/* Kernel timing for moe_layer_decode: stage_events is NULL or an array of
+ * 2 * MOE_N_STAGES hipEvent_t created by the caller (with timing enabled);
+ * stage i's kernel is launched with hipExtLaunchKernel so that the runtime
+ * records stage_events[2i] when it starts and stage_events[2i+1] when it
+ * ends -- the interval is that kernel alone. */
+#define MOE_STAGE_ROUTE 0     /* router logits, split over d across the chip */
+#define MOE_STAGE_DISPATCH 1  /* top-k + weights + dispatch plan (one block) */
+#define MOE_STAGE_GATEUP 2    /* grouped gate/up with SiLU(g)*u */
+#define MOE_STAGE_DOWN 3      /* grouped down */
 #define MOE_STAGE_COMBINE 4   /* weighted combine to token order */
 #define MOE_N_STAGES 5
 
@@ -222,10 +224,9 @@ moe_status moe_combine(const moe_layer_desc* desc, const moe_plan* plan,
                        const float* row_out, const float* dept_out,
                        const float* shared_out, int32_t T, void* y, void* stream);
 
-/* The fused decode step: route -> dispatch -> grouped gate/up -> grouped
- * down with the combine, y[T][d] in act_dtype.  `stage_events` (NULL or an
- * array of MOE_N_STAGES + 1 hipEvent_t created by the caller) brackets the
- * stages for timing. */
+/* The whole decode step: route -> top-k + dispatch -> grouped gate/up ->
+ * grouped down -> combine, y[T][d] in act_dtype (five kernels on `stream`).
+ * `stage_events`: see MOE_N_STAGES above (NULL = no timing). */
 moe_status moe_layer_decode(const moe_layer_desc* desc, const moe_weights* weights,
                             const void* x, int32_t T, void* y, void* workspace,
                             size_t ws_bytes, void* const* stage_events, void* stream);

@@ -280,15 +280,17 @@ def moe_combine(desc: LayerDesc, plan: Plan, row_out: torch.Tensor,
 def moe_layer_decode(desc: LayerDesc, weights: Dict[str, torch.Tensor], x: torch.Tensor,
                      y: torch.Tensor, workspace: torch.Tensor, stage_events=None):
     """y[T][d] = the layer on x[T][d].  stage_events: None or a sequence of
-    N_STAGES + 1 recorded-once torch.cuda.Event(enable_timing=True)."""
+    2 * N_STAGES torch.cuda.Event(enable_timing=True), each recorded once
+    beforehand (so it exists); pairs (start, stop) bracket each stage's
+    kernel exactly."""
     T, d = x.shape[0], desc.d_model
     ws = _weights_struct(desc, weights)
     wsp, wsn = _ws(desc, workspace)
     ev = None
     if stage_events is not None:
-        if len(stage_events) != N_STAGES + 1:
-            raise ValueError(f"stage_events needs {N_STAGES + 1} events")
-        ev = (_vp * (N_STAGES + 1))(*[e.cuda_event for e in stage_events])
+        if len(stage_events) != 2 * N_STAGES:
+            raise ValueError(f"stage_events needs {2 * N_STAGES} events")
+        ev = (_vp * (2 * N_STAGES))(*[e.cuda_event for e in stage_events])
     st = lib().moe_layer_decode(
         ctypes.byref(desc), ctypes.byref(ws), _ptr(x, "x", desc.torch_dtype, (T, d)), T,
         _ptr(y, "y", desc.torch_dtype, (T, d)), wsp, wsn, ev, _stream(x.device))

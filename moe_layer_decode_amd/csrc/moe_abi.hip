@@ -15,7 +15,7 @@ using moe::FamilySet;
 using moe::WorkDesc;
 
 enum Region {
-  R_COUNTERS, R_PARTIAL, R_TOPK_IDS, R_TOPK_W, R_HEADER, R_COUNTS, R_OFFSETS, R_ROW_TOKEN,
+  R_COUNTERS, R_LOGITS, R_TOPK_IDS, R_TOPK_W, R_HEADER, R_COUNTS, R_OFFSETS, R_ROW_TOKEN,
   R_ROW_SLOT, R_ROW_EXPERT, R_ROW_WEIGHT, R_INV_PERM, R_ACTIVE, R_WORK, R_DCOUNTS, R_DOFFSETS,
   R_DROW_TOKEN, R_DROW_DEPT, R_DROW_SCALE, R_DINV, R_ACTIVE_DEPTS, R_DWORK, R_H, R_HD, R_HS,
   R_ROW_OUT, R_DEPT_OUT, R_SHARED_OUT, R_COUNT
@@ -48,7 +48,7 @@ Layout layout_of(const moe_layer_desc& d) {
   const int64_t m = d.n_depts > 0 ? d.n_depts : 0, Pm = max_dept_pairs(d);
   size_t sz[R_COUNT];
   sz[R_COUNTERS] = n_counters(d) * 4;
-  sz[R_PARTIAL] = (size_t)n_route_chunks(d) * Tm * E * 4;
+  sz[R_LOGITS] = Tm * E * 4;
   sz[R_TOPK_IDS] = sz[R_TOPK_W] = A * 4;
   sz[R_HEADER] = MOE_PLAN_HEADER_LEN * 4;
   sz[R_COUNTS] = E * 4;
@@ -195,7 +195,7 @@ moe::RouteArgs route_args(const moe_layer_desc& d, void* ws, const void* x, cons
   ra.renorm = d.renormalize;
   ra.scale = d.route_scale;
   ra.n_chunks = n_route_chunks(d);
-  ra.partial = at<float>(ws, L, R_PARTIAL);
+  ra.logits = at<float>(ws, L, R_LOGITS);
   ra.ids_out = ids;
   ra.w_out = w;
   ra.sel_out = sel;
@@ -413,7 +413,8 @@ moe_status moe_route(const moe_layer_desc* desc, const void* x, const void* w_ro
   if ((s = check_ws(desc, workspace, ws_bytes)) != MOE_OK) return s;
   const moe::RouteArgs ra = route_args(*desc, workspace, x, w_router, router_bias, T, topk_ids,
                                        topk_w, sel_scores);
-  return hip_status(moe::launch_route(desc->w_dtype, ra, nullptr, static_cast<hipStream_t>(stream)));
+  return hip_status(
+      moe::launch_route(desc->w_dtype, ra, nullptr, static_cast<hipStream_t>(stream), nullptr));
 }
 
 moe_status moe_dispatch(const moe_layer_desc* desc, const int32_t* topk_ids, const float* topk_w,
@@ -455,12 +456,11 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_weights* weights
                                 shared_out);
   set_tiles(set, desc->d_model, true, cfg);
   if (moe::launch_gateup(desc->w_dtype, set, x, T, desc->d_model, cfg.rows_per_wave,
-                         cfg.rows_per_pass, st) !=
-      hipSuccess)
+                         cfg.rows_per_pass, st, nullptr) != hipSuccess)
     return MOE_ERR_HIP;
   set_tiles(set, desc->d_model, false, cfg);
-  return hip_status(
-      moe::launch_down(desc->w_dtype, set, T, desc->d_model, cfg.lpr, cfg.col_groups, st));
+  return hip_status(moe::launch_down(desc->w_dtype, set, T, desc->d_model, cfg.lpr,
+                                     cfg.col_groups, st, nullptr));
 }
 
 moe_status moe_combine(const moe_layer_desc* desc, const moe_plan* plan, const float* row_out,
@@ -479,7 +479,8 @@ moe_status moe_combine(const moe_layer_desc* desc, const moe_plan* plan, const f
     return MOE_ERR_INVALID_ARG;
   if (desc->n_depts > 0 && (!plan->dept_inv || !plan->dept_row_scale)) return MOE_ERR_INVALID_ARG;
   const moe::CombineArgs a = combine_args(*desc, *plan, row_out, dept_out, shared_out, T);
-  return hip_status(moe::launch_combine(desc->act_dtype, a, y, static_cast<hipStream_t>(stream)));
+  return hip_status(
+      moe::launch_combine(desc->act_dtype, a, y, static_cast<hipStream_t>(stream), nullptr));
 }
 
 moe_status moe_layer_decode(const moe_layer_desc* desc, const moe_weights* weights, const void* x,
@@ -492,15 +493,17 @@ moe_status moe_layer_decode(const moe_layer_desc* desc, const moe_weights* weigh
   if ((s = check_weights(desc, weights, true, true)) != MOE_OK) return s;
   if (!ok_ptr(x) || !ok_ptr(y)) return MOE_ERR_INVALID_ARG;
   if ((s = check_ws(desc, workspace, ws_bytes)) != MOE_OK) return s;
-  if (stage_events)
-    for (int i = 0; i <= MOE_N_STAGES; ++i)
+  moe::KernelEvents ev[MOE_N_STAGES];
+  if (stage_events) {
+    for (int i = 0; i < 2 * MOE_N_STAGES; ++i)
       if (!stage_events[i]) return MOE_ERR_INVALID_ARG;
+    for (int i = 0; i < MOE_N_STAGES; ++i)
+      ev[i] = {static_cast<hipEvent_t>(stage_events[2 * i]),
+               static_cast<hipEvent_t>(stage_events[2 * i + 1])};
+  }
+  auto evp = [&](int i) -> const moe::KernelEvents* { return stage_events ? ev + i : nullptr; };
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  auto mark = [&](int i) -> bool {
-    return !stage_events ||
-           hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), st) == hipSuccess;
-  };
   const Layout L = layout_of(*desc);
   moe_plan plan;
   fill_plan(*desc, workspace, T, &plan);
@@ -510,32 +513,29 @@ moe_status moe_layer_decode(const moe_layer_desc* desc, const moe_weights* weigh
   const moe::GemvConfig cfg = choose_config(*desc, T);
 
   // router logits, then top-k + dispatch plan
-  if (!mark(MOE_STAGE_ROUTE)) return MOE_ERR_HIP;
   const moe::RouteArgs ra =
       route_args(*desc, workspace, x, weights->w_router, weights->router_bias, T,
                  at<int32_t>(workspace, L, R_TOPK_IDS), at<float>(workspace, L, R_TOPK_W), nullptr);
   const moe::PlanArgs pa = plan_args(*desc, workspace, T, plan);
-  if (moe::launch_route(desc->w_dtype, ra, &pa, st) != hipSuccess) return MOE_ERR_HIP;
-  if (!mark(MOE_STAGE_DISPATCH) || !mark(MOE_STAGE_GATEUP)) return MOE_ERR_HIP;
+  if (moe::launch_route(desc->w_dtype, ra, &pa, st, evp(MOE_STAGE_ROUTE)) != hipSuccess)
+    return MOE_ERR_HIP;
 
+  // grouped gate/up with SiLU(g) * u
   FamilySet set = make_families(*desc, *weights, plan, workspace, T, row_out, dept_out,
                                 shared_out);
   set_tiles(set, desc->d_model, true, cfg);
   if (moe::launch_gateup(desc->w_dtype, set, x, T, desc->d_model, cfg.rows_per_wave,
-                         cfg.rows_per_pass, st) !=
-      hipSuccess)
+                         cfg.rows_per_pass, st, evp(MOE_STAGE_GATEUP)) != hipSuccess)
     return MOE_ERR_HIP;
-  if (!mark(MOE_STAGE_DOWN)) return MOE_ERR_HIP;
 
   // grouped down, then the combine back to token order
   set_tiles(set, desc->d_model, false, cfg);
-  if (moe::launch_down(desc->w_dtype, set, T, desc->d_model, cfg.lpr, cfg.col_groups, st) !=
-      hipSuccess)
+  if (moe::launch_down(desc->w_dtype, set, T, desc->d_model, cfg.lpr, cfg.col_groups, st,
+                       evp(MOE_STAGE_DOWN)) != hipSuccess)
     return MOE_ERR_HIP;
-  if (!mark(MOE_STAGE_COMBINE)) return MOE_ERR_HIP;
   const moe::CombineArgs ca = combine_args(*desc, plan, row_out, dept_out, shared_out, T);
-  if (moe::launch_combine(desc->act_dtype, ca, y, st) != hipSuccess) return MOE_ERR_HIP;
-  if (!mark(MOE_N_STAGES)) return MOE_ERR_HIP;
+  if (moe::launch_combine(desc->act_dtype, ca, y, st, evp(MOE_STAGE_COMBINE)) != hipSuccess)
+    return MOE_ERR_HIP;
   return MOE_OK;
 }
 

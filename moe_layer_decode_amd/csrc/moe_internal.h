@@ -45,7 +45,7 @@ struct RouteArgs {
   int score_fn, renorm;
   float scale;
   int n_chunks;            // ceil(d / kRouteChunk)
-  float* partial;          // [n_chunks][T][E] partial logits
+  float* logits;           // [T][E]
   int32_t* ids_out;        // [T][k] or nullptr
   float* w_out;            // [T][k] or nullptr
   float* sel_out;          // [T][E] or nullptr
@@ -98,14 +98,25 @@ struct GemvConfig {
   int col_groups;      // down: column groups per wave (columns per wave = col_groups * 64 / lpr)
 };
 
-// Launchers: each returns hipGetLastError() after its launch.
-hipError_t launch_route(int w_dtype, const RouteArgs& ra, const PlanArgs* pa, hipStream_t st);
+// Optional timing of one kernel: the runtime writes `start` when the kernel
+// begins and `stop` when it ends (hipExtLaunchKernel), so the interval is the
+// kernel alone, with no event packets of its own in the stream.
+struct KernelEvents {
+  hipEvent_t start, stop;
+};
+
+// Launchers: each returns hipGetLastError() after its launch.  `ev` may be
+// null; launch_route takes two (router kernel, top-k/plan kernel).
+hipError_t launch_route(int w_dtype, const RouteArgs& ra, const PlanArgs* pa, hipStream_t st,
+                        const KernelEvents* ev);
 hipError_t launch_dispatch(const int32_t* ids, const float* w, const PlanArgs& pa, hipStream_t st);
 hipError_t launch_gateup(int w_dtype, const FamilySet& set, const void* x, int T, int d,
-                         int rows_per_wave, int rows_per_pass, hipStream_t st);
+                         int rows_per_wave, int rows_per_pass, hipStream_t st,
+                         const KernelEvents* ev);
 hipError_t launch_down(int w_dtype, const FamilySet& set, int T, int d, int lpr, int col_groups,
-                       hipStream_t st);
-hipError_t launch_combine(int act_dtype, const CombineArgs& a, void* y, hipStream_t st);
+                       hipStream_t st, const KernelEvents* ev);
+hipError_t launch_combine(int act_dtype, const CombineArgs& a, void* y, hipStream_t st,
+                          const KernelEvents* ev);
 hipError_t launch_zero(unsigned int* p, size_t n, hipStream_t st);
 
 }  // namespace moe

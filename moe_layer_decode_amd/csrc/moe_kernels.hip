@@ -24,6 +24,8 @@
 #include "moe_device.h"
 #include "moe_internal.h"
 
+#include <hip/hip_ext.h>
+
 #include <climits>
 
 namespace moe {
@@ -55,6 +57,49 @@ template <> struct Raw8<float> {
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
   }
 };
+
+// Activation vectors of 8 elements and the 8-term dot product with a weight
+// vector.  bf16 x bf16 uses the packed dot instruction (products are exact in
+// fp32, two per instruction); fp32 uses plain fused multiply-adds.
+template <typename T_> struct X8;
+template <> struct X8<bf16_t> {
+  u32x4_t u;
+  __device__ __forceinline__ void load(const bf16_t* p) {
+    u = *reinterpret_cast<const u32x4_t*>(p);
+  }
+  __device__ __forceinline__ void zero() { u = u32x4_t{0, 0, 0, 0}; }
+};
+template <> struct X8<float> {
+  f32x4_t a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const f32x4_t*>(p);
+    b = *reinterpret_cast<const f32x4_t*>(p + 4);
+  }
+  __device__ __forceinline__ void zero() { a = b = f32x4_t{0.f, 0.f, 0.f, 0.f}; }
+};
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+__device__ __forceinline__ float dot8(const Raw8<bf16_t>& w, const X8<bf16_t>& x, float acc) {
+  acc = dot2_bf16(w.u.x, x.u.x, acc);
+  acc = dot2_bf16(w.u.y, x.u.y, acc);
+  acc = dot2_bf16(w.u.z, x.u.z, acc);
+  return dot2_bf16(w.u.w, x.u.w, acc);
+}
+__device__ __forceinline__ float dot8(const Raw8<float>& w, const X8<float>& x, float acc) {
+  acc = fmaf(w.a.x, x.a.x, acc);
+  acc = fmaf(w.a.y, x.a.y, acc);
+  acc = fmaf(w.a.z, x.a.z, acc);
+  acc = fmaf(w.a.w, x.a.w, acc);
+  acc = fmaf(w.b.x, x.b.x, acc);
+  acc = fmaf(w.b.y, x.b.y, acc);
+  acc = fmaf(w.b.z, x.b.z, acc);
+  return fmaf(w.b.w, x.b.w, acc);
+}
 
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
@@ -106,40 +151,6 @@ struct PlanShared {
   int invalid;
 };
 
-// Partial logits of expert e over d-chunk c for every token.  The reduction
-// order depends only on the token's position, never on e, so equal router
-// rows give bitwise-equal logits.
-template <typename T_>
-__device__ void router_partial(const RouteArgs& ra, int e, int c, int lane) {
-  const T_* x = static_cast<const T_*>(ra.x);
-  const int col = c * kRouteChunk + lane * 8;
-  const bool act = col < ra.d;
-  float w[8];
-  if (act) {
-    load8(static_cast<const T_*>(ra.wr) + (size_t)e * ra.d + col, w);
-  } else {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) w[q] = 0.f;
-  }
-  for (int t0 = 0; t0 < ra.T; t0 += 8) {
-    const int nv = min(8, ra.T - t0);
-    float acc[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      acc[j] = 0.f;
-      if (j < nv && act) {
-        float xv[8];
-        load8(x + (size_t)(t0 + j) * ra.d + col, xv);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) acc[j] = fmaf(w[q], xv[q], acc[j]);
-      }
-    }
-    group_reduce_scatter<8, 64>(acc, lane);
-    const int j = lane >> 3;
-    if ((lane & 7) == 0 && j < nv) ra.partial[((size_t)c * ra.T + t0 + j) * ra.E + e] = acc[0];
-  }
-}
-
 // Top-k of token t by one wave: lane l holds experts l, l+64, ...; k rounds of
 // a wave-wide argmax under (score desc, index asc); lane j keeps slot j.
 template <int NPL>
@@ -150,7 +161,7 @@ __device__ void topk_one(const RouteArgs& p, int t, int lane, PlanShared& s) {
     const int e = lane + kWave * i;
     float l = 0.f, sc = 0.f, a = 0.f;
     if (e < p.E) {
-      for (int c = 0; c < p.n_chunks; ++c) l += p.partial[((size_t)c * p.T + t) * p.E + e];
+      l = p.logits[(size_t)t * p.E + e];
       const float b = p.bias ? p.bias[e] : 0.f;
       if (p.score_fn == MOE_SCORE_SIGMOID) {
         a = 1.0f / (1.0f + expf(-l));
@@ -391,17 +402,62 @@ __device__ void plan_phase(PlanShared& s, const PlanArgs& pa) {
   }
 }
 
-// Router logits split over d-chunks: wave (e, c) of the grid.
-template <typename T_>
+// Router logits l[t][e] = x_t . W_r[e].  A block owns EB experts; its four
+// waves split d (wave w takes the 512-wide chunks w, w+4, ...), each wave
+// reduces over its lanes, and the four wave sums are added in wave order.  The
+// summation order depends only on the token's position in its group of 8,
+// never on the expert, so equal router rows give bitwise-equal logits.
+template <typename T_, int EB>
 __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs ra) {
+  __shared__ float part[kWaves][EB * 8];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int gw = blockIdx.x * kWaves + wid;
-  const int e = gw % ra.E, c = gw / ra.E;
-  if (c < ra.n_chunks) router_partial<T_>(ra, e, c, lane);
+  const int e0 = blockIdx.x * EB;
+  const T_* x = static_cast<const T_*>(ra.x);
+  const T_* wr = static_cast<const T_*>(ra.wr);
+  constexpr int N = EB * 8;
+  constexpr int SH = 6 - Log2<N>::value;
+  for (int t0 = 0; t0 < ra.T; t0 += 8) {
+    const int nv = min(8, ra.T - t0);
+    float acc[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc[i] = 0.f;
+    for (int c = wid; c < ra.n_chunks; c += kWaves) {
+      const int col = c * kRouteChunk + lane * 8;
+      if (col < ra.d) {
+        Raw8<T_> w[EB];
+#pragma unroll
+        for (int eb = 0; eb < EB; ++eb) {
+          if (e0 + eb < ra.E)
+            w[eb].load(wr + (size_t)(e0 + eb) * ra.d + col);
+          else
+            w[eb].zero();
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (j < nv) {
+            X8<T_> xv;
+            xv.load(x + (size_t)(t0 + j) * ra.d + col);
+#pragma unroll
+            for (int eb = 0; eb < EB; ++eb) acc[eb * 8 + j] = dot8(w[eb], xv, acc[eb * 8 + j]);
+          }
+        }
+      }
+    }
+    group_reduce_scatter<N, 64>(acc, lane);
+    if ((lane & ((1 << SH) - 1)) == 0) part[wid][lane >> SH] = acc[0];
+    __syncthreads();
+    if (wid == 0 && lane < N) {
+      const int eb = lane >> 3, j = lane & 7;
+      if (e0 + eb < ra.E && j < nv)
+        ra.logits[(size_t)(t0 + j) * ra.E + e0 + eb] =
+            ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+    }
+    __syncthreads();
+  }
 }
 
-// One block: sum the partial logits, top-k of every token (one wave per
-// token), then (do_plan) the dispatch plan.
+// One block: top-k of every token (one wave per token), then (do_plan) the
+// dispatch plan.
 template <int NPL>
 __global__ __launch_bounds__(kPlanThreads) void topk_plan_kernel(RouteArgs ra, PlanArgs pa,
                                                                  int do_plan) {
@@ -501,49 +557,6 @@ __device__ __forceinline__ int slot_token(const Slot& sl, const int* grp_token, 
 __device__ __forceinline__ int lane_token(const Slot& sl, const int* grp_token, int t, int T) {
   const int tok = grp_token ? grp_token[sl.r0 + t] : t;
   return min(max(tok, 0), T - 1);
-}
-
-// Activation vectors of 8 elements and the 8-term dot product with a weight
-// vector.  bf16 x bf16 uses the packed dot instruction (products are exact in
-// fp32, two per instruction); fp32 uses plain fused multiply-adds.
-template <typename T_> struct X8;
-template <> struct X8<bf16_t> {
-  u32x4_t u;
-  __device__ __forceinline__ void load(const bf16_t* p) {
-    u = *reinterpret_cast<const u32x4_t*>(p);
-  }
-  __device__ __forceinline__ void zero() { u = u32x4_t{0, 0, 0, 0}; }
-};
-template <> struct X8<float> {
-  f32x4_t a, b;
-  __device__ __forceinline__ void load(const float* p) {
-    a = *reinterpret_cast<const f32x4_t*>(p);
-    b = *reinterpret_cast<const f32x4_t*>(p + 4);
-  }
-  __device__ __forceinline__ void zero() { a = b = f32x4_t{0.f, 0.f, 0.f, 0.f}; }
-};
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                         __builtin_bit_cast(bf16x2_t, b), acc, false);
-}
-__device__ __forceinline__ float dot8(const Raw8<bf16_t>& w, const X8<bf16_t>& x, float acc) {
-  acc = dot2_bf16(w.u.x, x.u.x, acc);
-  acc = dot2_bf16(w.u.y, x.u.y, acc);
-  acc = dot2_bf16(w.u.z, x.u.z, acc);
-  return dot2_bf16(w.u.w, x.u.w, acc);
-}
-__device__ __forceinline__ float dot8(const Raw8<float>& w, const X8<float>& x, float acc) {
-  acc = fmaf(w.a.x, x.a.x, acc);
-  acc = fmaf(w.a.y, x.a.y, acc);
-  acc = fmaf(w.a.z, x.a.z, acc);
-  acc = fmaf(w.a.w, x.a.w, acc);
-  acc = fmaf(w.b.x, x.b.x, acc);
-  acc = fmaf(w.b.y, x.b.y, acc);
-  acc = fmaf(w.b.z, x.b.z, acc);
-  return fmaf(w.b.w, x.b.w, acc);
 }
 
 // ---- small groups: register GEMV -------------------------------------------
@@ -1071,35 +1084,52 @@ __global__ void zero_kernel(unsigned int* p, size_t n) {
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
+template <typename K, typename... A>
+static void launch(K kernel, dim3 grid, dim3 block, hipStream_t st, const KernelEvents* ev,
+                   A... args) {
+  if (ev)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, ev->start, ev->stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+}
+
+// ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
 template <typename T_>
-static hipError_t launch_route_t(const RouteArgs& ra, const PlanArgs* pa, hipStream_t st) {
-  const int waves = ra.E * ra.n_chunks;
-  hipLaunchKernelGGL((route_kernel<T_>), dim3((waves + kWaves - 1) / kWaves), dim3(kThreads), 0,
-                     st, ra);
+static hipError_t launch_route_t(const RouteArgs& ra, const PlanArgs* pa, hipStream_t st,
+                                 const KernelEvents* ev) {
+  // two experts per block once there are enough blocks to cover the chip:
+  // each activation chunk is then read once for both
+  if (ra.E >= 256)
+    launch(route_kernel<T_, 2>, dim3((ra.E + 1) / 2), dim3(kThreads), st, ev, ra);
+  else
+    launch(route_kernel<T_, 1>, dim3(ra.E), dim3(kThreads), st, ev, ra);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   PlanArgs p{};
   if (pa) p = *pa;
   const int do_plan = pa != nullptr;
   const dim3 grid(1), block(kPlanThreads);
+  const KernelEvents* ev2 = ev ? ev + 1 : nullptr;
   if (ra.E <= 64)
-    hipLaunchKernelGGL((topk_plan_kernel<1>), grid, block, 0, st, ra, p, do_plan);
+    launch(topk_plan_kernel<1>, grid, block, st, ev2, ra, p, do_plan);
   else if (ra.E <= 128)
-    hipLaunchKernelGGL((topk_plan_kernel<2>), grid, block, 0, st, ra, p, do_plan);
+    launch(topk_plan_kernel<2>, grid, block, st, ev2, ra, p, do_plan);
   else if (ra.E <= 256)
-    hipLaunchKernelGGL((topk_plan_kernel<4>), grid, block, 0, st, ra, p, do_plan);
+    launch(topk_plan_kernel<4>, grid, block, st, ev2, ra, p, do_plan);
   else if (ra.E <= 512)
-    hipLaunchKernelGGL((topk_plan_kernel<8>), grid, block, 0, st, ra, p, do_plan);
+    launch(topk_plan_kernel<8>, grid, block, st, ev2, ra, p, do_plan);
   else if (ra.E <= 1024)
-    hipLaunchKernelGGL((topk_plan_kernel<16>), grid, block, 0, st, ra, p, do_plan);
+    launch(topk_plan_kernel<16>, grid, block, st, ev2, ra, p, do_plan);
   else
-    hipLaunchKernelGGL((topk_plan_kernel<32>), grid, block, 0, st, ra, p, do_plan);
+    launch(topk_plan_kernel<32>, grid, block, st, ev2, ra, p, do_plan);
   return hipGetLastError();
 }
 
-hipError_t launch_route(int w_dtype, const RouteArgs& ra, const PlanArgs* pa, hipStream_t st) {
-  return w_dtype == MOE_BF16 ? launch_route_t<bf16_t>(ra, pa, st)
-                             : launch_route_t<float>(ra, pa, st);
+hipError_t launch_route(int w_dtype, const RouteArgs& ra, const PlanArgs* pa, hipStream_t st,
+                        const KernelEvents* ev) {
+  return w_dtype == MOE_BF16 ? launch_route_t<bf16_t>(ra, pa, st, ev)
+                             : launch_route_t<float>(ra, pa, st, ev);
 }
 
 hipError_t launch_dispatch(const int32_t* ids, const float* w, const PlanArgs& pa,
@@ -1110,9 +1140,9 @@ hipError_t launch_dispatch(const int32_t* ids, const float* w, const PlanArgs& p
 
 template <typename T_>
 static hipError_t launch_gateup_t(const FamilySet& set, const T_* x, int T, int d, int rpw,
-                                  int rw, hipStream_t st) {
+                                  int rw, hipStream_t st, const KernelEvents* ev) {
   const dim3 grid(set.blk_start[set.n]), block(kThreads);
-#define MOE_GU(P, R) hipLaunchKernelGGL((gateup_kernel<T_, P, R>), grid, block, 0, st, set, x, T, d)
+#define MOE_GU(P, R) launch(gateup_kernel<T_, P, R>, grid, block, st, ev, set, x, T, d)
   if (rpw >= 8)
     MOE_GU(8, 2);
   else if (rpw == 4 && rw >= 4)
@@ -1130,43 +1160,45 @@ static hipError_t launch_gateup_t(const FamilySet& set, const T_* x, int T, int 
 }
 
 hipError_t launch_gateup(int w_dtype, const FamilySet& set, const void* x, int T, int d,
-                         int rows_per_wave, int rows_per_pass, hipStream_t st) {
+                         int rows_per_wave, int rows_per_pass, hipStream_t st,
+                         const KernelEvents* ev) {
   if (set.blk_start[set.n] <= 0) return hipSuccess;
   return w_dtype == MOE_BF16 ? launch_gateup_t<bf16_t>(set, static_cast<const bf16_t*>(x), T, d,
-                                                       rows_per_wave, rows_per_pass, st)
+                                                       rows_per_wave, rows_per_pass, st, ev)
                              : launch_gateup_t<float>(set, static_cast<const float*>(x), T, d,
-                                                      rows_per_wave, rows_per_pass, st);
+                                                      rows_per_wave, rows_per_pass, st, ev);
 }
 
 template <typename T_>
 static hipError_t launch_down_t(const FamilySet& set, int T, int d, int lpr, int cg,
-                                hipStream_t st) {
+                                hipStream_t st, const KernelEvents* ev) {
   const dim3 grid(set.blk_start[set.n]), block(kThreads);
-#define MOE_DOWN(L, C) hipLaunchKernelGGL((down_kernel<T_, L, C>), grid, block, 0, st, set, T, d)
+#define MOE_DOWN(L, C) launch(down_kernel<T_, L, C>, grid, block, st, ev, set, T, d)
   if (lpr == 16) {
-    if (cg >= 4) MOE_DOWN(16, 4); else MOE_DOWN(16, 2);
+    if (cg >= 4) MOE_DOWN(16, 4); else if (cg == 2) MOE_DOWN(16, 2); else MOE_DOWN(16, 1);
   } else if (lpr == 32) {
-    if (cg >= 4) MOE_DOWN(32, 4); else MOE_DOWN(32, 2);
+    if (cg >= 4) MOE_DOWN(32, 4); else if (cg == 2) MOE_DOWN(32, 2); else MOE_DOWN(32, 1);
   } else {
-    if (cg >= 4) MOE_DOWN(64, 4); else MOE_DOWN(64, 2);
+    if (cg >= 4) MOE_DOWN(64, 4); else if (cg == 2) MOE_DOWN(64, 2); else MOE_DOWN(64, 1);
   }
 #undef MOE_DOWN
   return hipGetLastError();
 }
 
 hipError_t launch_down(int w_dtype, const FamilySet& set, int T, int d, int lpr, int col_groups,
-                       hipStream_t st) {
+                       hipStream_t st, const KernelEvents* ev) {
   if (set.blk_start[set.n] <= 0) return hipSuccess;
-  return w_dtype == MOE_BF16 ? launch_down_t<bf16_t>(set, T, d, lpr, col_groups, st)
-                             : launch_down_t<float>(set, T, d, lpr, col_groups, st);
+  return w_dtype == MOE_BF16 ? launch_down_t<bf16_t>(set, T, d, lpr, col_groups, st, ev)
+                             : launch_down_t<float>(set, T, d, lpr, col_groups, st, ev);
 }
 
-hipError_t launch_combine(int act_dtype, const CombineArgs& a, void* y, hipStream_t st) {
+hipError_t launch_combine(int act_dtype, const CombineArgs& a, void* y, hipStream_t st,
+                          const KernelEvents* ev) {
   const dim3 grid((a.d + kThreads - 1) / kThreads, a.T), block(kThreads);
   if (act_dtype == MOE_BF16)
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, block, 0, st, a, static_cast<bf16_t*>(y));
+    launch(combine_kernel<bf16_t>, grid, block, st, ev, a, static_cast<bf16_t*>(y));
   else
-    hipLaunchKernelGGL(combine_kernel<float>, grid, block, 0, st, a, static_cast<float*>(y));
+    launch(combine_kernel<float>, grid, block, st, ev, a, static_cast<float*>(y));
   return hipGetLastError();
 }
 

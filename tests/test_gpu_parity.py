@@ -429,3 +429,23 @@ def test_layer_is_deterministic():
     ys = [layer(x).clone() for _ in range(3)]
     torch.cuda.synchronize()
     assert all(torch.equal(ys[0], y) for y in ys[1:])
+
+
+def test_stage_events_time_each_kernel():
+    """With stage events the step gives the same y, and every stage's
+    start/stop pair brackets a kernel of positive duration."""
+    shape = SH[QWEN]
+    w = gpu_layer(QWEN, 0)
+    x = moe_synth.make_tokens(shape, 0, 4, DEV)
+    layer = M.MoeLayer(desc_of(shape), w, DEV)
+    y0 = layer(x).clone()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * M.N_STAGES)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    y1 = layer(x, stage_events=evs)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+    for s in range(M.N_STAGES):
+        ms = evs[2 * s].elapsed_time(evs[2 * s + 1])
+        assert 0.0 < ms < 50.0, (M.STAGE_NAMES[s], ms)
