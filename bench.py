@@ -57,6 +57,15 @@ def parse():
     p.add_argument("--summarize-pmc", type=str, default=None,
                    help="print per-kernel, per-grid-size mean counter values of a rocprofv3 "
                         "counter_collection.csv and exit")
+    p.add_argument("--profile-meta", type=str, default="gpurun_out/profile_pass.json",
+                   help="--profile-pass writes the algorithmic bytes and source hash here; "
+                        "--pmc-report reads them")
+    p.add_argument("--pmc-report", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
+                   help="write the calibrated HBM traffic summary of two --pmc runs "
+                        "(FETCH_SIZE, WRITE_SIZE) of --profile-pass as markdown")
+    p.add_argument("--trace-report", nargs=2, metavar=("TRACE_CSV", "BENCH_JSON"), default=None,
+                   help="write the kernel-trace summary of a profiled default run, beside the "
+                        "JSON line of an unprofiled one, as markdown")
     p.add_argument("--source-hash", action="store_true",
                    help="print the hash of the kernel sources the counter summary refers to")
     return p.parse_args()
@@ -72,8 +81,8 @@ def _short(name):
     return name[:48]
 
 
-def summarize_trace(path):
-    """Mean kernel durations of a rocprofv3 kernel trace, per kernel and grid
+def trace_means(path):
+    """Kernel durations (us) of a rocprofv3 kernel trace, per kernel and grid
     size (the grid size tells the decode batches apart)."""
     import csv
     from collections import defaultdict
@@ -81,12 +90,53 @@ def summarize_trace(path):
     for r in csv.DictReader(open(path)):
         key = (_short(r["Kernel_Name"]), int(r["Grid_Size_X"]), int(r["Grid_Size_Y"]))
         acc[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return acc
+
+
+def summarize_trace(path):
+    acc = trace_means(path)
     print("| kernel | grid x | grid y | calls | mean us | min us |")
     print("|---|---|---|---|---|---|")
     for (k, gx, gy), v in sorted(acc.items()):
         if k == "torch":
             continue
         print(f"| {k} | {gx} | {gy} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} |")
+
+
+def trace_report(trace_csv, bench_json):
+    """Markdown summary: the kernel trace of a profiled default run, the
+    unprofiled run's per-batch stage times, and the roofline kernel's
+    event-timed launch beside its trace mean."""
+    b = json.loads(open(bench_json).read().strip().splitlines()[-1])
+    acc = trace_means(trace_csv)
+    head_T = b["config"]["batch"]
+    print(f"# Kernel trace: bench.py default run ({b['config']['workload'].split(' MoE')[0]}, "
+          f"batches {'/'.join(b['batches'])})\n")
+    print("Command (repo root, one MI355X):\n\n```")
+    print("rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_bench -o run -- python -u bench.py")
+    print("python bench.py > gpurun_out/bench.json")
+    print("python bench.py --trace-report gpurun_out/prof_bench/run_kernel_trace.csv gpurun_out/bench.json")
+    print("```\n")
+    print("Per-kernel durations, split by grid size (grid x = work-items; each decode batch gives "
+          "its own grid per expert kernel). `__amd_rocclr_copyBuffer` rows are the weight-replica "
+          "clones and torch-side copies of the harness.\n")
+    summarize_trace(trace_csv)
+    print("\nStage times of the unprofiled run (HIP events around each kernel):\n")
+    print("| batch | step us (graph) | weight GB/s | route us | top-k+plan us | gate/up us "
+          "| down us | combine us |")
+    print("|---|---|---|---|---|---|---|---|")
+    for T, r in b["batches"].items():
+        st = r["stage_us"]
+        print(f"| {T} | {r['us']} | {r['GBps']} | {st['route']} | {st['dispatch']} | {st['gateup']} "
+              f"| {st['down']} | {st['combine']} |")
+    rf = b["roofline"]
+    grids = sorted((gx, v) for (k, gx, gy), v in acc.items() if k == rf["kernel"])
+    gx, v = grids[-1] if grids else (0, [0.0])
+    mean = sum(v) / len(v)
+    print(f"\nRoofline ({rf['kernel']}, batch {head_T}): {rf['achieved']} GB/s of {rf['peak']} GB/s "
+          f"= {rf['frac']} ({rf['algorithmic_bytes_per_launch']} algorithmic bytes per launch / "
+          f"{rf['launch_us']} us event-timed launch); the trace gives the same kernel at the "
+          f"batch-{head_T} grid ({gx}) a mean of {mean:.2f} us.")
 
 
 def summarize_pmc(path):
@@ -103,6 +153,67 @@ def summarize_pmc(path):
     print("|---|---|---|---|---|")
     for (k, g, c), v in sorted(acc.items()):
         print(f"| {k} | {g} | {c} | {len(v)} | {sum(v) / len(v):.1f} |")
+
+
+def _pmc_rows(path):
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return rows
+
+
+def pmc_report(fetch_csv, write_csv, meta_path):
+    """Calibrated HBM bytes per launch of the layer kernels from a FETCH_SIZE
+    and a WRITE_SIZE run of --profile-pass.  The pass ends with a plain 1 GiB
+    write (fill) and a plain 1 GiB read (sum) after the last layer kernel:
+    the largest counter value among the dispatches after it calibrates each
+    counter to bytes."""
+    from collections import defaultdict
+    meta = json.load(open(meta_path)) if os.path.exists(meta_path) else {}
+    GiB_KiB = float(1 << 20)
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = [r for r in _pmc_rows(path) if r["Counter_Name"] == counter]
+        last = max(i for i, r in enumerate(rows) if "moe::" in r["Kernel_Name"])
+        calib = max(float(r["Counter_Value"]) for r in rows[last + 1:])
+        acc = defaultdict(list)
+        for r in rows[:last + 1]:
+            if "moe::" in r["Kernel_Name"]:
+                acc[(_short(r["Kernel_Name"]), int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
+        out[counter] = (calib, {k: sum(v) / len(v) for k, v in acc.items()},
+                        {k: len(v) for k, v in acc.items()})
+    rf, wf = GiB_KiB / out["FETCH_SIZE"][0], GiB_KiB / out["WRITE_SIZE"][0]
+    fetch, write = out["FETCH_SIZE"][1], out["WRITE_SIZE"][1]
+    shape = meta.get("shape", HEADLINE)
+    T = meta.get("batch", HEADLINE_T)
+    print(f"# HBM traffic of the layer kernels, {shape}, batch {T}\n")
+    print("Commands (repo root, one MI355X; one counter per pass):\n\n```")
+    print("rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o run -- python -u bench.py --profile-pass")
+    print("rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o run -- python -u bench.py --profile-pass")
+    print("python bench.py --pmc-report gpurun_out/pmc_fetch/run_counter_collection.csv "
+          "gpurun_out/pmc_write/run_counter_collection.csv")
+    print("```\n")
+    print(f"`--profile-pass` runs 20 eager batch-{T} steps, then a plain 1 GiB write (torch `fill_`) "
+          "and a plain 1 GiB read (torch `sum`); the largest counter value after the last layer "
+          "kernel calibrates each counter.\n")
+    print(f"Calibration: 1 GiB read -> FETCH_SIZE {out['FETCH_SIZE'][0]:.1f} KiB (factor {rf:.5f}); "
+          f"1 GiB write -> WRITE_SIZE {out['WRITE_SIZE'][0]:.1f} KiB (factor {wf:.5f}).\n")
+    alg = {"gateup_kernel": meta.get("gateup_bytes"), "down_kernel": meta.get("down_bytes")}
+    print("| kernel (grid) | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (calibrated) "
+          "| algorithmic bytes | ratio |")
+    print("|---|---|---|---|---|---|---|")
+    traffic = {}
+    for key in sorted(set(fetch) | set(write)):
+        f_kib, w_kib = fetch.get(key, 0.0), write.get(key, 0.0)
+        b = int(round((f_kib * rf + w_kib * wf) * 1024))
+        traffic[key[0]] = b
+        a = alg.get(key[0])
+        ratio = f"{b / a:.4f}" if a else ""
+        print(f"| {key[0]} ({key[1]}) | {out['FETCH_SIZE'][2].get(key, 0)} | {f_kib:.1f} | {w_kib:.1f} "
+              f"| {b} | {a or ''} | {ratio} |")
+    print()
+    print(f"kernel_source_sha256: `{meta.get('kernel_source_sha256', kernel_source_hash())}`")
+    print(f"traffic_bytes_per_launch: `{traffic.get('gateup_kernel', '')}`")
 
 
 def desc_of(M, shape, max_tokens):
@@ -240,7 +351,7 @@ class Runner:
 KERNEL_SOURCES = ("moe_layer_decode_amd/csrc/moe_kernels.hip",
                   "moe_layer_decode_amd/csrc/moe_device.h",
                   "moe_layer_decode_amd/csrc/moe_internal.h")
-PMC_SUMMARY = "profiles/pmc_gateup_qwen3_30b_a3b_batch16.md"
+PMC_SUMMARY = "profiles/pmc_layer_kernels_qwen3_30b_a3b_batch16.md"
 
 
 def kernel_source_hash():
@@ -312,6 +423,12 @@ def main():
     if args.source_hash:
         print(kernel_source_hash())
         return
+    if args.trace_report:
+        trace_report(*args.trace_report)
+        return
+    if args.pmc_report:
+        pmc_report(args.pmc_report[0], args.pmc_report[1], args.profile_meta)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(this layer's hot path runs on a single MI355X)", file=sys.stderr)
@@ -331,6 +448,14 @@ def main():
     if args.profile_pass:
         r = Runner(M, moe_synth, shape, head_T, dev, base=base)
         r.time_eager(20, 2)
+        meta = {"shape": shape.name, "batch": head_T, "kernel_source_sha256": kernel_source_hash(),
+                "gateup_bytes": gateup_bytes(shape, head_T, r.n_active, r.n_active_depts,
+                                             r.n_rows, r.n_dept_rows),
+                "down_bytes": down_bytes(shape, head_T, r.n_active, r.n_active_depts,
+                                         r.n_rows, r.n_dept_rows)}
+        os.makedirs(os.path.dirname(args.profile_meta) or ".", exist_ok=True)
+        with open(args.profile_meta, "w") as f:
+            json.dump(meta, f)
         # counter calibration: a plain 1 GiB read (sum) and a plain 1 GiB write (fill)
         n = 1 << 30
         a = torch.empty(n // 4, dtype=torch.float32, device=dev)

@@ -216,16 +216,8 @@ int family_rows(const moe_layer_desc& d, int f) {
 moe::GemvConfig choose_config(const moe_layer_desc& d, int32_t T) {
   (void)T;
   moe::GemvConfig c;
-#ifdef MOE_FORCE_RPW
-  c.rows_per_wave = MOE_FORCE_RPW;
-#else
   c.rows_per_wave = 1;
-#endif
-#ifdef MOE_FORCE_RW
-  c.rows_per_pass = MOE_FORCE_RW;
-#else
   c.rows_per_pass = 1;
-#endif
   int lpr = 64;
   for (int cand : {64, 32, 16}) {
     bool ok = true;
@@ -330,14 +322,14 @@ FamilySet make_families(const moe_layer_desc& d, const moe_weights& w, const moe
 }
 
 // Tiles per slot and the block prefix for one launch: small parts tile by the
-// GEMV configuration, large parts by 64 rows (gate/up) or 64 columns (down),
-// four 16-wide matrix-core tiles per block.
+// GEMV configuration, large parts by one 16-row (gate/up) or 16-column (down)
+// matrix-core tile per block, its K split over the block's four waves.
 void set_tiles(FamilySet& set, int d, bool gateup, const moe::GemvConfig& c) {
   set.blk_start[0] = 0;
   for (int i = 0; i < set.n; ++i) {
     Family& f = set.f[i];
     if (f.large)
-      f.tiles = ceil_div(gateup ? f.rows : d, moe::kWaves * 16);
+      f.tiles = ceil_div(gateup ? f.rows : d, 16);
     else
       f.tiles = gateup ? ceil_div(f.rows, moe::kWaves * c.rows_per_wave)
                        : ceil_div(d, moe::kWaves * c.col_groups * (64 / c.lpr));

@@ -92,10 +92,10 @@ struct CombineArgs {
 };
 
 struct GemvConfig {
-  int rows_per_wave;   // gate/up: rows of each matrix per wave (1, 2, 4, 8)
-  int rows_per_pass;   // gate/up: rows a wave streams at once (1, 2, 4)
+  int rows_per_wave;   // gate/up: rows of each matrix per wave (1)
+  int rows_per_pass;   // gate/up: rows a wave streams at once (1)
   int lpr;             // down: lanes per weight row (16, 32, 64)
-  int col_groups;      // down: column groups per wave (columns per wave = col_groups * 64 / lpr)
+  int col_groups;      // down: column groups per wave, 1 or 2 (columns per wave = col_groups * 64 / lpr)
 };
 
 // Optional timing of one kernel: the runtime writes `start` when the kernel

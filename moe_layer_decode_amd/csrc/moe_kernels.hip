@@ -780,12 +780,35 @@ __device__ __forceinline__ u32x4_t ld16_stream(const bf16_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
 }
 
+// K-split tiles: the four waves of a block share one 16-row (gate/up) or
+// 16-column (down) tile and each streams a quarter of K, two 32-wide steps
+// ahead of the matrix-core work; the four partial tiles are then added in
+// wave order through LDS, so results do not depend on timing.
+
+constexpr int kMfmaAhead = 2;  // K-steps requested ahead of the one being used
+
+// Per-wave K range [kb, ke) of a K-split tile: quarters rounded up to 32.
+__device__ __forceinline__ void k_quarter(int K, int wid, int& kb, int& ke) {
+  const int kq = ((K + 4 * 32 - 1) / (4 * 32)) * 32;
+  kb = min(K, wid * kq);
+  ke = min(K, kb + kq);
+}
+
+struct MfmaLds {
+  f32x4_t part[kWaves][2][2][kWave];  // [wave][token chunk][gate/up or down][lane]
+};
+
 // 16 rows (i0..) of gate and up against 16*NC tokens (rows tc.. of the group).
 template <int NC>
 __device__ void gu_mfma(const bf16_t* __restrict__ Wg, const bf16_t* __restrict__ Wu, int d,
                         int rows, int i0, const bf16_t* __restrict__ x, int T, const Slot& sl,
-                        const int* grp_token, int tc, bf16_t* __restrict__ h, int lane) {
+                        const int* grp_token, int tc, bf16_t* __restrict__ h, int lane, int wid,
+                        MfmaLds& lds) {
+  // two token chunks hold twice the activations: one step ahead keeps them in registers
+  constexpr int kAhead = NC > 1 ? 1 : kMfmaAhead;
   const int r16 = lane & 15, g = lane >> 4;
+  int kb, ke;
+  k_quarter(d, wid, kb, ke);
   const size_t row = (size_t)min(i0 + r16, rows - 1);
   const bf16_t* ap = Wg + row * d + g * 8;
   const bf16_t* bp = Wu + row * d + g * 8;
@@ -801,47 +824,75 @@ __device__ void gu_mfma(const bf16_t* __restrict__ Wg, const bf16_t* __restrict_
 #pragma unroll
   for (int c = 0; c < NC; ++c) accg[c] = accu[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const u32x4_t z = {0, 0, 0, 0};
-  const bool lane_in = g * 8 < d;
-  int k = 0;
-  u32x4_t ca = lane_in ? ld16_stream(ap) : z, cb = lane_in ? ld16_stream(bp) : z, cx[NC];
+  // ring of kAhead + 1 steps in registers
+  u32x4_t ra[kAhead + 1], rb[kAhead + 1], rx[kAhead + 1][NC];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) cx[c] = (xv[c] && lane_in) ? ld16(xp[c]) : z;
-  for (; k < d; k += 32) {
-    const int kn = k + 32;
-    const bool nin = kn + g * 8 < d;
-    const u32x4_t na = nin ? ld16_stream(ap + kn) : z, nb = nin ? ld16_stream(bp + kn) : z;
-    u32x4_t nx[NC];
+  for (int s = 0; s <= kAhead; ++s) {
+    const int k = kb + s * 32;
+    const bool in = k + g * 8 < ke;
+    if (s < kAhead) {
+      ra[s] = in ? ld16_stream(ap + k) : z;
+      rb[s] = in ? ld16_stream(bp + k) : z;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) nx[c] = (xv[c] && nin) ? ld16(xp[c] + kn) : z;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      accg[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ca), as_bf16x8(cx[c]), accg[c], 0, 0, 0);
-      accu[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cb), as_bf16x8(cx[c]), accu[c], 0, 0, 0);
+      for (int c = 0; c < NC; ++c) rx[s][c] = (xv[c] && in) ? ld16(xp[c] + k) : z;
     }
-    ca = na;
-    cb = nb;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) cx[c] = nx[c];
   }
+  for (int k = kb; k < ke; k += 32 * (kAhead + 1)) {
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int t = tc + c * 16 + r16;
-    if (t < sl.n) {
+    for (int s = 0; s <= kAhead; ++s) {
+      // request step s + kAhead into the slot freed last iteration
+      const int kn = k + (s + kAhead) * 32;
+      const int sn = (s + kAhead) % (kAhead + 1);
+      const bool nin = kn + g * 8 < ke;
+      ra[sn] = nin ? ld16_stream(ap + kn) : z;
+      rb[sn] = nin ? ld16_stream(bp + kn) : z;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = i0 + 4 * g + i;
-        if (rr < rows) store_act(h + (size_t)(sl.r0 + t) * rows + rr, silu(accg[c][i]) * accu[c][i]);
+      for (int c = 0; c < NC; ++c) rx[sn][c] = (xv[c] && nin) ? ld16(xp[c] + kn) : z;
+      if (k + s * 32 < ke) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          accg[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra[s]), as_bf16x8(rx[s][c]), accg[c], 0, 0, 0);
+          accu[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rb[s]), as_bf16x8(rx[s][c]), accu[c], 0, 0, 0);
+        }
       }
     }
   }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    lds.part[wid][c][0][lane] = accg[c];
+    lds.part[wid][c][1][lane] = accu[c];
+  }
+  __syncthreads();
+  if (wid == 0) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      f32x4_t sg = lds.part[0][c][0][lane], su = lds.part[0][c][1][lane];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) {
+        sg += lds.part[w][c][0][lane];
+        su += lds.part[w][c][1][lane];
+      }
+      const int t = tc + c * 16 + r16;
+      if (t < sl.n) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rr = i0 + 4 * g + i;
+          if (rr < rows) store_act(h + (size_t)(sl.r0 + t) * rows + rr, silu(sg[i]) * su[i]);
+        }
+      }
+    }
+  }
+  __syncthreads();
 }
 
 // 16 output columns (c0..) against 16*NC rows of h (rows tc.. of the group).
 template <int NC>
 __device__ void dn_mfma(const bf16_t* __restrict__ Wd, int d, int rows, int c0,
                         const bf16_t* __restrict__ h, const Slot& sl, int tc,
-                        float* __restrict__ out, int lane) {
+                        float* __restrict__ out, int lane, int wid, MfmaLds& lds) {
   const int r16 = lane & 15, g = lane >> 4;
+  int kb, ke;
+  k_quarter(rows, wid, kb, ke);
   const bf16_t* ap = Wd + (size_t)min(c0 + r16, d - 1) * rows + g * 8;
   const bf16_t* hp[NC];
   bool hv[NC];
@@ -855,35 +906,51 @@ __device__ void dn_mfma(const bf16_t* __restrict__ Wd, int d, int rows, int c0,
 #pragma unroll
   for (int c = 0; c < NC; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const u32x4_t z = {0, 0, 0, 0};
-  const bool lane_in = g * 8 < rows;
-  u32x4_t ca = lane_in ? ld16_stream(ap) : z, ch[NC];
+  u32x4_t ra[kMfmaAhead + 1], rh[kMfmaAhead + 1][NC];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) ch[c] = (hv[c] && lane_in) ? ld16(hp[c]) : z;
-  for (int k = 0; k < rows; k += 32) {
-    const int kn = k + 32;
-    const bool nin = kn + g * 8 < rows;
-    const u32x4_t na = nin ? ld16_stream(ap + kn) : z;
-    u32x4_t nh[NC];
+  for (int s = 0; s < kMfmaAhead; ++s) {
+    const int k = kb + s * 32;
+    const bool in = k + g * 8 < ke;
+    ra[s] = in ? ld16_stream(ap + k) : z;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) nh[c] = (hv[c] && nin) ? ld16(hp[c] + kn) : z;
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ca), as_bf16x8(ch[c]), acc[c], 0, 0, 0);
-    ca = na;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) ch[c] = nh[c];
+    for (int c = 0; c < NC; ++c) rh[s][c] = (hv[c] && in) ? ld16(hp[c] + k) : z;
   }
+  for (int k = kb; k < ke; k += 32 * (kMfmaAhead + 1)) {
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int t = tc + c * 16 + r16;
-    if (t < sl.n) {
+    for (int s = 0; s <= kMfmaAhead; ++s) {
+      const int kn = k + (s + kMfmaAhead) * 32;
+      const int sn = (s + kMfmaAhead) % (kMfmaAhead + 1);
+      const bool nin = kn + g * 8 < ke;
+      ra[sn] = nin ? ld16_stream(ap + kn) : z;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int col = c0 + 4 * g + i;
-        if (col < d) out[(size_t)(sl.r0 + t) * d + col] = acc[c][i];
+      for (int c = 0; c < NC; ++c) rh[sn][c] = (hv[c] && nin) ? ld16(hp[c] + kn) : z;
+      if (k + s * 32 < ke) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra[s]), as_bf16x8(rh[s][c]), acc[c], 0, 0, 0);
       }
     }
   }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) lds.part[wid][c][0][lane] = acc[c];
+  __syncthreads();
+  if (wid == 0) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      f32x4_t sum = lds.part[0][c][0][lane];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) sum += lds.part[w][c][0][lane];
+      const int t = tc + c * 16 + r16;
+      if (t < sl.n) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int col = c0 + 4 * g + i;
+          if (col < d) out[(size_t)(sl.r0 + t) * d + col] = sum[i];
+        }
+      }
+    }
+  }
+  __syncthreads();
 }
 
 // ---- large groups, fp32 layers: plain GEMV ---------------------------------
@@ -981,9 +1048,22 @@ __device__ void dn_plain(const float* __restrict__ Wd, int d, int rows, int c0,
 // ---- kernels -----------------------------------------------------------------
 
 // Small groups: each wave owns RPW rows, taken RW at a time.
-template <typename T_, int RPW, int RW>
-__global__ __launch_bounds__(kThreads) void gateup_kernel(FamilySet set, const T_* __restrict__ x,
-                                                          int T, int d) {
+// Minimum waves per SIMD the expert kernels are built for.  The bf16 small-
+// group GEMVs are latency-bound streams that want many waves in flight, so
+// the register budget is capped where the matrix-core part still fits without
+// spilling; fp32 layers keep the compiler's choice.
+template <typename T_, int NCMAX>
+constexpr int gateup_min_waves() { return sizeof(T_) == 2 ? (NCMAX > 1 ? 5 : 6) : 1; }
+template <typename T_>
+constexpr int down_min_waves() { return sizeof(T_) == 2 ? 7 : 1; }
+
+// NCMAX: 16-token chunks a large-group tile takes at once (2 only when a
+// group can exceed 16 rows, since the wider chunk costs registers).
+template <typename T_, int RPW, int RW, int NCMAX>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
+    gateup_min_waves<T_, NCMAX>(), 8))) void gateup_kernel(FamilySet set,
+                                                           const T_* __restrict__ x, int T,
+                                                           int d) {
   int tile;
   const Family& F = block_part(set, tile);
   Slot sl;
@@ -1000,19 +1080,21 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(FamilySet set, const T
       gu_small<T_, RW>(Wg, Wu, d, F.rows, i0 + r, x, T, sl, F.grp_token, h, lane);
     return;
   }
-  const int i0 = tile * (kWaves * 16) + wid * 16;
+  // large groups: the whole block on one 16-row tile
+  const int i0 = tile * 16;
   if (i0 >= F.rows) return;
   if constexpr (sizeof(T_) == 2) {
+    __shared__ MfmaLds lds;
 #pragma unroll 1
-    for (int tc = 0; tc < sl.n; tc += 32) {
-      if (sl.n - tc > 16)
-        gu_mfma<2>(Wg, Wu, d, F.rows, i0, x, T, sl, F.grp_token, tc, h, lane);
+    for (int tc = 0; tc < sl.n; tc += 16 * NCMAX) {
+      if (NCMAX > 1 && sl.n - tc > 16)
+        gu_mfma<NCMAX>(Wg, Wu, d, F.rows, i0, x, T, sl, F.grp_token, tc, h, lane, wid, lds);
       else
-        gu_mfma<1>(Wg, Wu, d, F.rows, i0, x, T, sl, F.grp_token, tc, h, lane);
+        gu_mfma<1>(Wg, Wu, d, F.rows, i0, x, T, sl, F.grp_token, tc, h, lane, wid, lds);
     }
   } else {
 #pragma unroll 1
-    for (int r = 0; r < 16; r += 2)
+    for (int r = wid * 4; r < wid * 4 + 4; r += 2)
 #pragma unroll 1
       for (int tc = 0; tc < sl.n; tc += 8)
         gu_plain<2, 8>(Wg, Wu, d, F.rows, i0 + r, x, T, sl, F.grp_token, tc, h, lane);
@@ -1020,7 +1102,8 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(FamilySet set, const T
 }
 
 template <typename T_, int LPR, int CG>
-__global__ __launch_bounds__(kThreads) void down_kernel(FamilySet set, int T, int d) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
+    down_min_waves<T_>(), 8))) void down_kernel(FamilySet set, int T, int d) {
   int tile;
   const Family& F = block_part(set, tile);
   Slot sl;
@@ -1034,19 +1117,21 @@ __global__ __launch_bounds__(kThreads) void down_kernel(FamilySet set, int T, in
     if (cb < d) dn_small<T_, LPR, CG>(Wd, d, F.rows, cb, h, sl, F.out, lane);
     return;
   }
-  const int c0 = tile * (kWaves * 16) + wid * 16;
+  // large groups: the whole block on one 16-column tile
+  const int c0 = tile * 16;
   if (c0 >= d) return;
   if constexpr (sizeof(T_) == 2) {
+    __shared__ MfmaLds lds;
 #pragma unroll 1
     for (int tc = 0; tc < sl.n; tc += 32) {
       if (sl.n - tc > 16)
-        dn_mfma<2>(Wd, d, F.rows, c0, h, sl, tc, F.out, lane);
+        dn_mfma<2>(Wd, d, F.rows, c0, h, sl, tc, F.out, lane, wid, lds);
       else
-        dn_mfma<1>(Wd, d, F.rows, c0, h, sl, tc, F.out, lane);
+        dn_mfma<1>(Wd, d, F.rows, c0, h, sl, tc, F.out, lane, wid, lds);
     }
   } else {
 #pragma unroll 1
-    for (int q = 0; q < 16; q += 2)
+    for (int q = wid * 4; q < wid * 4 + 4; q += 2)
 #pragma unroll 1
       for (int tc = 0; tc < sl.n; tc += 8)
         dn_plain<2, 8>(Wd, d, F.rows, c0 + q, h, sl, tc, F.out, lane);
@@ -1142,20 +1227,15 @@ template <typename T_>
 static hipError_t launch_gateup_t(const FamilySet& set, const T_* x, int T, int d, int rpw,
                                   int rw, hipStream_t st, const KernelEvents* ev) {
   const dim3 grid(set.blk_start[set.n]), block(kThreads);
-#define MOE_GU(P, R) launch(gateup_kernel<T_, P, R>, grid, block, st, ev, set, x, T, d)
-  if (rpw >= 8)
-    MOE_GU(8, 2);
-  else if (rpw == 4 && rw >= 4)
-    MOE_GU(4, 4);
-  else if (rpw == 4)
-    MOE_GU(4, 2);
-  else if (rpw == 2 && rw >= 2)
-    MOE_GU(2, 2);
-  else if (rpw == 2)
-    MOE_GU(2, 1);
+  // a routed group holds at most T rows, so 32-token chunks pay off only past 16
+  const bool wide = T > 16;
+  // one row per wave and pass: measured fastest, and the register budget of
+  // the capped-occupancy build leaves no room for more
+  if (rpw != 1 || rw != 1) return hipErrorInvalidValue;
+  if (wide)
+    launch(gateup_kernel<T_, 1, 1, 2>, grid, block, st, ev, set, x, T, d);
   else
-    MOE_GU(1, 1);
-#undef MOE_GU
+    launch(gateup_kernel<T_, 1, 1, 1>, grid, block, st, ev, set, x, T, d);
   return hipGetLastError();
 }
 
@@ -1175,11 +1255,11 @@ static hipError_t launch_down_t(const FamilySet& set, int T, int d, int lpr, int
   const dim3 grid(set.blk_start[set.n]), block(kThreads);
 #define MOE_DOWN(L, C) launch(down_kernel<T_, L, C>, grid, block, st, ev, set, T, d)
   if (lpr == 16) {
-    if (cg >= 4) MOE_DOWN(16, 4); else if (cg == 2) MOE_DOWN(16, 2); else MOE_DOWN(16, 1);
+    if (cg >= 2) MOE_DOWN(16, 2); else MOE_DOWN(16, 1);
   } else if (lpr == 32) {
-    if (cg >= 4) MOE_DOWN(32, 4); else if (cg == 2) MOE_DOWN(32, 2); else MOE_DOWN(32, 1);
+    if (cg >= 2) MOE_DOWN(32, 2); else MOE_DOWN(32, 1);
   } else {
-    if (cg >= 4) MOE_DOWN(64, 4); else if (cg == 2) MOE_DOWN(64, 2); else MOE_DOWN(64, 1);
+    if (cg >= 2) MOE_DOWN(64, 2); else MOE_DOWN(64, 1);
   }
 #undef MOE_DOWN
   return hipGetLastError();
