@@ -317,8 +317,16 @@ FamilySet make_families(const moe_layer_desc& d, const moe_weights& w, const moe
     f.max_rows = T;
     add_parts(f, T <= small_max, T > small_max, 0, 0);
   }
-  set.n = n;
-  return set;
+  // Large parts first: their blocks stream whole 16-row tiles and live far
+  // longer than a small-group block, so they are dispatched first and overlap
+  // the many short blocks instead of forming the launch's tail.
+  FamilySet ordered = set;
+  int o = 0;
+  for (int pass = 1; pass >= 0; --pass)
+    for (int i = 0; i < n; ++i)
+      if (set.f[i].large == pass) ordered.f[o++] = set.f[i];
+  ordered.n = n;
+  return ordered;
 }
 
 // Tiles per slot and the block prefix for one launch: small parts tile by the

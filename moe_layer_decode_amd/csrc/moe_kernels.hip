@@ -763,6 +763,196 @@ __device__ __forceinline__ void dn_small(const T_* __restrict__ Wd, int d, int r
   }
 }
 
+// ---- small groups, activations staged in LDS ------------------------------
+//
+// Every wave of a block works on the same group, so the block copies the
+// group's (at most four) activation rows into LDS once and the waves read them
+// with ds_read.  Only the weights then travel the vector-memory path: reading
+// the activations per wave costs up to four extra 16-byte loads per weight load
+// and, at four rows, makes that path (not HBM) the limit.  The copy is issued
+// after the first weight loads, so both latencies overlap.
+
+constexpr int kXLds = 2048;  // longest activation row staged (elements)
+
+template <typename T_>
+struct SmallLds {
+  T_ x[kTokInline][kXLds];
+};
+
+// Block-wide: rows t < nv of `cols` elements, row t read from src(t), into
+// lds.x[t].  cols is a multiple of 8 and at most kXLds.
+template <typename T_, typename Src>
+__device__ __forceinline__ void stage_rows(SmallLds<T_>& lds, int nv, int cols, Src src) {
+  constexpr int kChunks = kTokInline * kXLds / 8 / kThreads;
+  const int per_row = cols >> 3, total = nv * per_row;
+  X8<T_> v[kChunks];
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const int q = threadIdx.x + i * kThreads;
+    if (q < total) {
+      const int t = q / per_row, c = (q - t * per_row) * 8;
+      v[i].load(src(t) + c);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const int q = threadIdx.x + i * kThreads;
+    if (q < total) {
+      const int t = q / per_row, c = (q - t * per_row) * 8;
+      *reinterpret_cast<X8<T_>*>(&lds.x[t][c]) = v[i];
+    }
+  }
+  __syncthreads();
+}
+
+constexpr int kStageRing = 4;  // weight steps requested before the staging barrier
+
+// Gate and up row i0 (one per wave) against the group's staged activations.
+// Up to kStageRing steps of the row are requested before the staging, so they
+// are all in flight through the barrier; after it, each consumed step's slot
+// is refilled kStageRing steps ahead.  Same per-lane column order and
+// reduction as gu_small.
+template <typename T_>
+__device__ __forceinline__ void gu_small_lds(const T_* __restrict__ Wg, const T_* __restrict__ Wu,
+                                             int d, int rows, int i0, const T_* __restrict__ x,
+                                             int T, const Slot& sl, const int* grp_token,
+                                             T_* __restrict__ h, int lane, SmallLds<T_>& lds) {
+  constexpr int NT = kTokInline, R = kStageRing, STEP = 8 * kWave;
+  const int nv = sl.n;
+  const size_t i = (size_t)min(i0, rows - 1);
+  const T_* gp = Wg + i * d + lane * 8;
+  const T_* up = Wu + i * d + lane * 8;
+  const int dl = d - lane * 8;  // this lane's columns: lane*8 + k*STEP for k*STEP < dl
+  Raw8<T_> rg[R], ru[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r * STEP < dl) {
+      rg[r].load(gp + r * STEP);
+      ru[r].load(up + r * STEP);
+    } else {
+      rg[r].zero();
+      ru[r].zero();
+    }
+  }
+  stage_rows(lds, nv, d, [&](int t) {
+    return x + (size_t)slot_token(sl, grp_token, 0, t, nv, T) * d;
+  });
+  float ag[NT], au[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) ag[t] = au[t] = 0.f;
+  for (int c0 = 0; c0 < d; c0 += R * STEP) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int c = c0 + r * STEP;
+      if (c < dl) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          if (t < nv) {
+            const X8<T_> xv = *reinterpret_cast<const X8<T_>*>(&lds.x[t][lane * 8 + c]);
+            ag[t] = dot8(rg[r], xv, ag[t]);
+            au[t] = dot8(ru[r], xv, au[t]);
+          }
+        }
+        if (c + R * STEP < dl) {
+          rg[r].load(gp + c + R * STEP);
+          ru[r].load(up + c + R * STEP);
+        }
+      }
+    }
+  }
+  constexpr int N = 2 * NT;
+  float v[N];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    v[t] = ag[t];
+    v[NT + t] = au[t];
+  }
+  group_reduce_scatter<N, 64>(v, lane);
+  // gate index t and up index t + NT sit in lanes l and l ^ 32
+  const float upv = __shfl_xor(v[0], 32, kWave);
+  constexpr int SH = 6 - Log2<N>::value;
+  const int t = lane >> SH;
+  if (t < NT && (lane & ((1 << SH) - 1)) == 0 && t < nv && i0 < rows)
+    store_act(h + (size_t)(sl.r0 + t) * rows + i0, silu(v[0]) * upv);
+}
+
+// Down columns as dn_small, the group's rows of h staged in LDS; weights
+// requested kStageRing steps ahead as in gu_small_lds.
+template <typename T_, int LPR, int CG>
+__device__ __forceinline__ void dn_small_lds(const T_* __restrict__ Wd, int d, int rows, int cb,
+                                             const T_* __restrict__ h, const Slot& sl,
+                                             float* __restrict__ out, int lane,
+                                             SmallLds<T_>& lds) {
+  constexpr int NT = kTokInline, R = kStageRing, STEP = 8 * LPR;
+  constexpr int G = 64 / LPR;
+  const int g = lane / LPR, j = lane - g * LPR;
+  const int nv = sl.n;
+  const int rl = rows - j * 8;  // this lane's elements: j*8 + k*STEP for k*STEP < rl
+  const T_* wp[CG];
+#pragma unroll
+  for (int q = 0; q < CG; ++q) wp[q] = Wd + (size_t)min(cb + q * G + g, d - 1) * rows + j * 8;
+  Raw8<T_> rw[R][CG];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int q = 0; q < CG; ++q) {
+      if (r * STEP < rl)
+        rw[r][q].load(wp[q] + r * STEP);
+      else
+        rw[r][q].zero();
+    }
+  stage_rows(lds, nv, rows, [&](int t) { return h + (size_t)(sl.r0 + t) * rows; });
+  float acc[CG][NT];
+#pragma unroll
+  for (int q = 0; q < CG; ++q)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[q][t] = 0.f;
+  for (int c0 = 0; c0 < rows; c0 += R * STEP) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int c = c0 + r * STEP;
+      if (c < rl) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          if (t < nv) {
+            const X8<T_> hv = *reinterpret_cast<const X8<T_>*>(&lds.x[t][j * 8 + c]);
+#pragma unroll
+            for (int q = 0; q < CG; ++q) acc[q][t] = dot8(rw[r][q], hv, acc[q][t]);
+          }
+        if (c + R * STEP < rl) {
+#pragma unroll
+          for (int q = 0; q < CG; ++q) rw[r][q].load(wp[q] + c + R * STEP);
+        }
+      }
+    }
+  }
+  constexpr int N = CG * NT;
+  float v[N];
+#pragma unroll
+  for (int q = 0; q < CG; ++q)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) v[q * NT + t] = acc[q][t];
+  group_reduce_scatter<N, LPR>(v, lane);
+  if constexpr (N >= LPR) {
+    constexpr int PER = N / LPR;
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int idx = j * PER + p;
+      const int q = idx / NT, t = idx - (idx / NT) * NT;
+      const int c = cb + q * G + g;
+      if (t < nv && c < d) out[(size_t)(sl.r0 + t) * d + c] = v[p];
+    }
+  } else {
+    constexpr int SPAN = LPR / N;
+    if (j % SPAN == 0) {
+      const int idx = j / SPAN;
+      const int q = idx / NT, t = idx - (idx / NT) * NT;
+      const int c = cb + q * G + g;
+      if (t < nv && c < d) out[(size_t)(sl.r0 + t) * d + c] = v[0];
+    }
+  }
+}
+
 // ---- large groups, bf16: 16x16x32 matrix-core tiles ------------------------
 //
 // Operand layout of v_mfma_f32_16x16x32_bf16 (lane l, g = l / 16): A row l%16
@@ -1057,9 +1247,19 @@ constexpr int gateup_min_waves() { return sizeof(T_) == 2 ? (NCMAX > 1 ? 5 : 6) 
 template <typename T_>
 constexpr int down_min_waves() { return sizeof(T_) == 2 ? 7 : 1; }
 
+// LDS of an expert-kernel block: the matrix-core partial tiles of a large
+// group or the staged activations of a small one (a block is only ever one).
+template <typename T_, bool XL>
+constexpr size_t expert_lds_bytes() {
+  const size_t a = sizeof(T_) == 2 ? sizeof(MfmaLds) : 0;
+  const size_t b = XL ? sizeof(SmallLds<T_>) : 0;
+  return a > b ? a : (b > 0 ? b : 16);
+}
+
 // NCMAX: 16-token chunks a large-group tile takes at once (2 only when a
 // group can exceed 16 rows, since the wider chunk costs registers).
-template <typename T_, int RPW, int RW, int NCMAX>
+// XL: small groups read their activations from LDS (rows of at most kXLds).
+template <typename T_, int RPW, int RW, int NCMAX, bool XL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     gateup_min_waves<T_, NCMAX>(), 8))) void gateup_kernel(FamilySet set,
                                                            const T_* __restrict__ x, int T,
@@ -1073,7 +1273,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   const T_* Wg = static_cast<const T_*>(F.gate) + (size_t)sl.mat * ms;
   const T_* Wu = static_cast<const T_*>(F.up) + (size_t)sl.mat * ms;
   T_* h = static_cast<T_*>(F.h);
+  __shared__ __align__(16) unsigned char lds_raw[expert_lds_bytes<T_, XL>()];
   if (!F.large) {
+    if constexpr (XL) {
+      static_assert(RPW == 1 && RW == 1, "staged activations take one row per wave");
+      gu_small_lds<T_>(Wg, Wu, d, F.rows, tile * kWaves + wid, x, T, sl, F.grp_token, h, lane,
+                       *reinterpret_cast<SmallLds<T_>*>(lds_raw));
+      return;
+    }
     const int i0 = tile * (kWaves * RPW) + wid * RPW;
 #pragma unroll 1
     for (int r = 0; r < RPW && i0 + r < F.rows; r += RW)
@@ -1084,7 +1291,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   const int i0 = tile * 16;
   if (i0 >= F.rows) return;
   if constexpr (sizeof(T_) == 2) {
-    __shared__ MfmaLds lds;
+    MfmaLds& lds = *reinterpret_cast<MfmaLds*>(lds_raw);
 #pragma unroll 1
     for (int tc = 0; tc < sl.n; tc += 16 * NCMAX) {
       if (NCMAX > 1 && sl.n - tc > 16)
@@ -1101,7 +1308,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   }
 }
 
-template <typename T_, int LPR, int CG>
+template <typename T_, int LPR, int CG, bool XL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     down_min_waves<T_>(), 8))) void down_kernel(FamilySet set, int T, int d) {
   int tile;
@@ -1111,17 +1318,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const T_* Wd = static_cast<const T_*>(F.down) + (size_t)sl.mat * F.rows * d;
   const T_* h = static_cast<const T_*>(F.h);
+  __shared__ __align__(16) unsigned char lds_raw[expert_lds_bytes<T_, XL>()];
   if (!F.large) {
     constexpr int CPW = CG * (64 / LPR);
     const int cb = tile * (kWaves * CPW) + wid * CPW;
-    if (cb < d) dn_small<T_, LPR, CG>(Wd, d, F.rows, cb, h, sl, F.out, lane);
+    if constexpr (XL)  // every wave takes part in the staging
+      dn_small_lds<T_, LPR, CG>(Wd, d, F.rows, cb, h, sl, F.out, lane,
+                                *reinterpret_cast<SmallLds<T_>*>(lds_raw));
+    else if (cb < d)
+      dn_small<T_, LPR, CG>(Wd, d, F.rows, cb, h, sl, F.out, lane);
     return;
   }
   // large groups: the whole block on one 16-column tile
   const int c0 = tile * 16;
   if (c0 >= d) return;
   if constexpr (sizeof(T_) == 2) {
-    __shared__ MfmaLds lds;
+    MfmaLds& lds = *reinterpret_cast<MfmaLds*>(lds_raw);
 #pragma unroll 1
     for (int tc = 0; tc < sl.n; tc += 32) {
       if (sl.n - tc > 16)
@@ -1232,10 +1444,15 @@ static hipError_t launch_gateup_t(const FamilySet& set, const T_* x, int T, int 
   // one row per wave and pass: measured fastest, and the register budget of
   // the capped-occupancy build leaves no room for more
   if (rpw != 1 || rw != 1) return hipErrorInvalidValue;
-  if (wide)
-    launch(gateup_kernel<T_, 1, 1, 2>, grid, block, st, ev, set, x, T, d);
+  const bool xl = d <= kXLds;
+  if (wide && xl)
+    launch(gateup_kernel<T_, 1, 1, 2, true>, grid, block, st, ev, set, x, T, d);
+  else if (wide)
+    launch(gateup_kernel<T_, 1, 1, 2, false>, grid, block, st, ev, set, x, T, d);
+  else if (xl)
+    launch(gateup_kernel<T_, 1, 1, 1, true>, grid, block, st, ev, set, x, T, d);
   else
-    launch(gateup_kernel<T_, 1, 1, 1>, grid, block, st, ev, set, x, T, d);
+    launch(gateup_kernel<T_, 1, 1, 1, false>, grid, block, st, ev, set, x, T, d);
   return hipGetLastError();
 }
 
@@ -1253,7 +1470,12 @@ template <typename T_>
 static hipError_t launch_down_t(const FamilySet& set, int T, int d, int lpr, int cg,
                                 hipStream_t st, const KernelEvents* ev) {
   const dim3 grid(set.blk_start[set.n]), block(kThreads);
-#define MOE_DOWN(L, C) launch(down_kernel<T_, L, C>, grid, block, st, ev, set, T, d)
+  int max_rows = 0;
+  for (int i = 0; i < set.n; ++i) max_rows = set.f[i].rows > max_rows ? set.f[i].rows : max_rows;
+  const bool xl = max_rows <= kXLds;
+#define MOE_DOWN(L, C)                                                    \
+  (xl ? launch(down_kernel<T_, L, C, true>, grid, block, st, ev, set, T, d) \
+      : launch(down_kernel<T_, L, C, false>, grid, block, st, ev, set, T, d))
   if (lpr == 16) {
     if (cg >= 2) MOE_DOWN(16, 2); else MOE_DOWN(16, 1);
   } else if (lpr == 32) {
