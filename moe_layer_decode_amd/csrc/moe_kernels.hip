@@ -151,66 +151,103 @@ struct PlanShared {
   int invalid;
 };
 
-// Top-k of token t by one wave: lane l holds experts l, l+64, ...; k rounds of
-// a wave-wide argmax under (score desc, index asc); lane j keeps slot j.
+// Order-preserving 32-bit key of a score: a larger float gives a larger key,
+// and +0 / -0 share one key (they compare equal as floats).  Key 0 lies below
+// every float, so it marks lanes past the last expert.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  const uint32_t u = __float_as_uint(f == 0.f ? 0.f : f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int wave_count(bool b) { return __popcll(__ballot(b)); }
+
+// Top-k of token t by one wave; lane l holds experts l, l+64, ... (expert
+// e = l + 64 i in plane i).  Selection is a radix select on the score keys:
+// 32 ballot rounds find the k-th largest key; among experts tied at that key
+// the lowest indices are taken.  The chosen k are then ranked by (score desc,
+// index asc) -- each compares itself with the other k-1 -- and the expert of
+// rank j is handed to lane j through LDS.
+// Value the routing weights start from: the sigmoid affinity in sigmoid mode,
+// else the logit.
+__device__ __forceinline__ float route_aux(const RouteArgs& p, float l) {
+  return p.score_fn == MOE_SCORE_SIGMOID ? 1.0f / (1.0f + expf(-l)) : l;
+}
+
 template <int NPL>
 __device__ void topk_one(const RouteArgs& p, int t, int lane, PlanShared& s) {
-  float sel[NPL], aux[NPL], lg[NPL];
+  float lg[NPL];
+  uint32_t key[NPL];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int e = lane + kWave * i;
-    float l = 0.f, sc = 0.f, a = 0.f;
+    float l = 0.f;
+    key[i] = 0u;
     if (e < p.E) {
       l = p.logits[(size_t)t * p.E + e];
       const float b = p.bias ? p.bias[e] : 0.f;
-      if (p.score_fn == MOE_SCORE_SIGMOID) {
-        a = 1.0f / (1.0f + expf(-l));
-        sc = a + b;
-      } else if (p.score_fn == MOE_SCORE_SOFTMAX_BIAS) {
-        a = l;
-        sc = l + b;
-      } else {
-        a = l;
-        sc = l;
-      }
+      const float sc = p.score_fn == MOE_SCORE_SOFTMAX ? l : route_aux(p, l) + b;
       if (p.sel_out) p.sel_out[(size_t)t * p.E + e] = sc;
+      key[i] = score_key(sc);
     }
-    sel[i] = sc;
-    aux[i] = a;
     lg[i] = l;
   }
-  uint32_t taken = 0;
+  const int k = p.k;
+  // largest thr with #(key >= thr) >= k: the k-th largest key
+  uint32_t thr = 0u;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = thr | (1u << b);
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) n += wave_count(key[i] >= c);
+    if (n >= k) thr = c;
+  }
+  int above = 0;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) above += wave_count(key[i] > thr);
+  // ties at thr: the (k - above) lowest expert indices
+  const uint64_t below_me = (1ull << lane) - 1ull;
+  int eq_before = 0;
+  uint32_t picked = 0u;  // bit i: this lane's expert of plane i is chosen
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const uint64_t eq = __ballot(key[i] == thr);
+    const int r = eq_before + __popcll(eq & below_me);
+    const bool take = key[i] > thr || (key[i] == thr && r < k - above);
+    picked |= (take ? 1u : 0u) << i;
+    eq_before += __popcll(eq);
+  }
+  // each chosen expert's rank among the chosen; planes holding none skip
+  int* slot_id = s.ids + t * k;
+  float* slot_aux = s.w + t * k;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const bool me = (picked >> i) & 1u;
+    if (!__ballot(me)) continue;
+    const int e = lane + kWave * i;
+    int rank = 0;
+#pragma unroll
+    for (int i2 = 0; i2 < NPL; ++i2) {
+      uint64_t m = __ballot((picked >> i2) & 1u);
+      while (m) {
+        const int l2 = __builtin_ctzll(m);
+        m &= m - 1ull;
+        const uint32_t k2 = (uint32_t)__builtin_amdgcn_readlane((int)key[i2], l2);
+        const int e2 = l2 + kWave * i2;
+        rank += (k2 > key[i] || (k2 == key[i] && e2 < e)) ? 1 : 0;
+      }
+    }
+    if (me) {
+      slot_id[rank] = e;
+      slot_aux[rank] = route_aux(p, lg[i]);
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
   int my_id = -1;
   float my_aux = 0.f;
-  for (int j = 0; j < p.k; ++j) {
-    float bv = 0.f, ba = 0.f;
-    int be = INT_MAX;
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-      const int e = lane + kWave * i;
-      // indices grow with i, so a strict '>' keeps the lower index on ties
-      if (e < p.E && !((taken >> i) & 1u) && (be == INT_MAX || sel[i] > bv)) {
-        bv = sel[i];
-        be = e;
-        ba = aux[i];
-      }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oe = __shfl_xor(be, o, kWave);
-      const float oa = __shfl_xor(ba, o, kWave);
-      if (oe != INT_MAX && (be == INT_MAX || ov > bv || (ov == bv && oe < be))) {
-        bv = ov;
-        be = oe;
-        ba = oa;
-      }
-    }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    if (lane == j) {
-      my_id = be;
-      my_aux = ba;
-    }
+  if (lane < k) {
+    my_id = slot_id[lane];
+    my_aux = slot_aux[lane];
   }
   const bool mine = lane < p.k;
   float w;
