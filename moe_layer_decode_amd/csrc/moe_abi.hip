@@ -36,6 +36,19 @@ size_t n_counters(const moe_layer_desc& d) { return 16 + (size_t)ceil_div(d.d_mo
 
 int n_route_chunks(const moe_layer_desc& d) { return ceil_div(d.d_model, moe::kRouteChunk); }
 
+// K pieces of the bf16 router: enough (16-expert tile, piece) blocks to reach
+// about 128 blocks, no more partial planes than the top-k reads for this many
+// experts, and at least 64 elements of K per wave.  fp32 layers use one plane.
+int route_ksplit(const moe_layer_desc& d) {
+  if (d.w_dtype != MOE_BF16) return 1;
+  const int tiles = ceil_div(d.n_experts, 16);
+  int s = ceil_div(128, tiles);
+  if (s > moe::route_split_max(d.n_experts)) s = moe::route_split_max(d.n_experts);
+  const int kmax = d.d_model / (moe::kWaves * 64);
+  if (s > kmax) s = kmax;
+  return s < 1 ? 1 : s;
+}
+
 // Largest number of (token, department) pairs: a token covers at most
 // min(m, k) departments.
 int64_t max_dept_pairs(const moe_layer_desc& d) {
@@ -48,7 +61,7 @@ Layout layout_of(const moe_layer_desc& d) {
   const int64_t m = d.n_depts > 0 ? d.n_depts : 0, Pm = max_dept_pairs(d);
   size_t sz[R_COUNT];
   sz[R_COUNTERS] = n_counters(d) * 4;
-  sz[R_LOGITS] = Tm * E * 4;
+  sz[R_LOGITS] = (int64_t)route_ksplit(d) * Tm * E * 4;
   sz[R_TOPK_IDS] = sz[R_TOPK_W] = A * 4;
   sz[R_HEADER] = MOE_PLAN_HEADER_LEN * 4;
   sz[R_COUNTS] = E * 4;
@@ -195,6 +208,7 @@ moe::RouteArgs route_args(const moe_layer_desc& d, void* ws, const void* x, cons
   ra.renorm = d.renormalize;
   ra.scale = d.route_scale;
   ra.n_chunks = n_route_chunks(d);
+  ra.ksplit = route_ksplit(d);
   ra.logits = at<float>(ws, L, R_LOGITS);
   ra.ids_out = ids;
   ra.w_out = w;

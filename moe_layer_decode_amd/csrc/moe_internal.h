@@ -14,6 +14,12 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRouteChunk = 512;     // d elements one router wave covers (64 lanes x 8)
 constexpr int kTokInline = 4;        // tokens carried inline in a work descriptor
 constexpr int kPlanThreads = 1024;   // threads of the single-block top-k / plan kernel
+constexpr int kMaxRouteSplit = 8;   // partial-logit planes of the bf16 router at most
+// Planes the top-k reads for up to n_experts experts: fewer as each lane holds
+// more experts, so the unrolled loads stay within registers.
+constexpr int route_split_max(int n_experts) {
+  return n_experts <= 256 ? kMaxRouteSplit : n_experts <= 512 ? 4 : n_experts <= 1024 ? 2 : 1;
+}
 constexpr int kMaxParts = 6;         // 3 matrix families x (small groups, large groups)
 // Plan header entries beyond the public ones: lengths of the compacted work
 // lists of small (<= kTokInline rows) and large groups.
@@ -45,7 +51,8 @@ struct RouteArgs {
   int score_fn, renorm;
   float scale;
   int n_chunks;            // ceil(d / kRouteChunk)
-  float* logits;           // [T][E]
+  int ksplit;              // partial-logit planes: logits holds [ksplit][T][E], summed in order
+  float* logits;           // [ksplit][T][E]
   int32_t* ids_out;        // [T][k] or nullptr
   float* w_out;            // [T][k] or nullptr
   float* sel_out;          // [T][E] or nullptr

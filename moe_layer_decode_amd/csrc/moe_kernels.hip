@@ -101,6 +101,18 @@ __device__ __forceinline__ float dot8(const Raw8<float>& w, const X8<float>& x, 
   return fmaf(w.b.w, x.b.w, acc);
 }
 
+// 16-byte loads for the matrix-core paths: cached (activations) and
+// streaming (weights, read once).
+__device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& u) {
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+__device__ __forceinline__ u32x4_t ld16(const bf16_t* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+__device__ __forceinline__ u32x4_t ld16_stream(const bf16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -177,19 +189,37 @@ template <int NPL>
 __device__ void topk_one(const RouteArgs& p, int t, int lane, PlanShared& s) {
   float lg[NPL];
   uint32_t key[NPL];
+  // partial logits of the K split, added in split order; straight-line code
+  // (planes past ksplit re-read the last plane and add nothing) so every
+  // load is issued before the first add waits
+  float bias[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    lg[i] = 0.f;
+    // requested with the logits, not after them
+    bias[i] = p.bias ? p.bias[min(lane + kWave * i, p.E - 1)] : 0.f;
+  }
+#pragma unroll
+  for (int q = 0; q < route_split_max(NPL * kWave); ++q) {
+    const float* pl = p.logits + ((size_t)min(q, p.ksplit - 1) * p.T + t) * p.E;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int e = min(lane + kWave * i, p.E - 1);
+      const float v = pl[e];
+      lg[i] += q < p.ksplit ? v : 0.f;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int e = lane + kWave * i;
-    float l = 0.f;
+    const float l = e < p.E ? lg[i] : 0.f;
+    lg[i] = l;
     key[i] = 0u;
     if (e < p.E) {
-      l = p.logits[(size_t)t * p.E + e];
-      const float b = p.bias ? p.bias[e] : 0.f;
-      const float sc = p.score_fn == MOE_SCORE_SOFTMAX ? l : route_aux(p, l) + b;
+      const float sc = p.score_fn == MOE_SCORE_SOFTMAX ? l : route_aux(p, l) + bias[i];
       if (p.sel_out) p.sel_out[(size_t)t * p.E + e] = sc;
       key[i] = score_key(sc);
     }
-    lg[i] = l;
   }
   const int k = p.k;
   // largest thr with #(key >= thr) >= k: the k-th largest key
@@ -493,6 +523,88 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs ra) {
   }
 }
 
+// Router logits on the matrix cores (bf16): block (x, y) owns experts
+// 16x .. 16x+15 and K piece y of ksplit; its four waves split that piece
+// again, each accumulating 16 experts x 16 tokens per 16x16x32 step for up to
+// NCT token tiles, two K-steps of loads ahead.  The four wave tiles are added
+// in wave order through LDS and written as partial plane y; the top-k adds the
+// planes in order.  Every expert sees the same summation order, so equal
+// router rows give bitwise-equal logits.
+template <int NCT>
+__global__ __launch_bounds__(kThreads) void route_mfma_kernel(RouteArgs ra) {
+  constexpr int kAhead = 2;
+  __shared__ f32x4_t part[kWaves][NCT][kWave];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int e0 = blockIdx.x * 16, d = ra.d, T = ra.T, E = ra.E;
+  const int pieces = ra.ksplit * kWaves;
+  const int kq = ((d + pieces * 32 - 1) / (pieces * 32)) * 32;
+  const int kb = min(d, (blockIdx.y * kWaves + wid) * kq), ke = min(d, kb + kq);
+  const bf16_t* xw = static_cast<const bf16_t*>(ra.x);
+  const bf16_t* ap = static_cast<const bf16_t*>(ra.wr) + (size_t)min(e0 + r16, E - 1) * d + g * 8;
+  float* out = ra.logits + (size_t)blockIdx.y * T * E;
+  const u32x4_t z = {0, 0, 0, 0};
+  for (int t0 = 0; t0 < T; t0 += 16 * NCT) {
+    const bf16_t* bp[NCT];
+    bool bv[NCT];
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+      const int t = t0 + c * 16 + r16;
+      bv[c] = t < T;
+      bp[c] = xw + (size_t)(bv[c] ? t : 0) * d + g * 8;
+    }
+    f32x4_t acc[NCT];
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    u32x4_t ra_[kAhead + 1], rb[kAhead + 1][NCT];
+#pragma unroll
+    for (int q = 0; q < kAhead; ++q) {
+      const int k = kb + q * 32;
+      const bool in = k + g * 8 < ke;
+      ra_[q] = in ? ld16_stream(ap + k) : z;
+#pragma unroll
+      for (int c = 0; c < NCT; ++c) rb[q][c] = (bv[c] && in) ? ld16(bp[c] + k) : z;
+    }
+    for (int k = kb; k < ke; k += 32 * (kAhead + 1)) {
+#pragma unroll
+      for (int q = 0; q <= kAhead; ++q) {
+        const int kn = k + (q + kAhead) * 32;
+        const int qn = (q + kAhead) % (kAhead + 1);
+        const bool nin = kn + g * 8 < ke;
+        ra_[qn] = nin ? ld16_stream(ap + kn) : z;
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) rb[qn][c] = (bv[c] && nin) ? ld16(bp[c] + kn) : z;
+        if (k + q * 32 < ke) {
+#pragma unroll
+          for (int c = 0; c < NCT; ++c)
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra_[q]), as_bf16x8(rb[q][c]),
+                                                             acc[c], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) part[wid][c][lane] = acc[c];
+    __syncthreads();
+    if (wid == 0) {
+#pragma unroll
+      for (int c = 0; c < NCT; ++c) {
+        f32x4_t sum = part[0][c][lane];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) sum += part[w][c][lane];
+        const int t = t0 + c * 16 + r16;
+        if (t < T) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = e0 + 4 * g + i;
+            if (e < E) out[(size_t)t * E + e] = sum[i];
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // One block: top-k of every token (one wave per token), then (do_plan) the
 // dispatch plan.
 template <int NPL>
@@ -550,8 +662,27 @@ __device__ __forceinline__ bool map_slot(const Family& F, int T, Slot& sl, int& 
   const int slot = tile / F.tiles;
   tile -= slot * F.tiles;
   if (F.work) {
-    if (slot >= *F.n_active) return false;
-    const WorkDesc wd = F.work[slot];
+    // slot < max_slots keeps the descriptor read inside the work list, so it
+    // is read together with the active count (one condition, no short
+    // circuit) instead of after it
+    static_assert(sizeof(WorkDesc) == 32, "a work descriptor is two 16-byte vectors");
+    const int* na_ptr = F.n_active;
+    const u32x4_t* wd_ptr = reinterpret_cast<const u32x4_t*>(F.work + slot);
+    __asm__ volatile("" ::"s"(na_ptr), "s"(wd_ptr));  // both addresses first
+    const int n_active = *na_ptr;
+    const u32x4_t w0 = wd_ptr[0], w1 = wd_ptr[1];
+    __asm__ volatile("" ::"s"(n_active), "s"(w0), "s"(w1));  // all three loads in flight at once
+    WorkDesc wd;
+    wd.mat = (int)w0.x;
+    wd.r0 = (int)w0.y;
+    wd.n = (int)w0.z;
+    wd.tok[0] = (int)w0.w;
+    wd.tok[1] = (int)w1.x;
+    wd.tok[2] = (int)w1.y;
+    wd.tok[3] = (int)w1.z;
+    const bool ok = (slot < n_active) & (wd.mat >= 0) & (wd.mat < F.n_mats) & (wd.r0 >= 0) &
+                    (wd.n <= F.max_rows - wd.r0);
+    if (!ok) return false;
     sl.mat = wd.mat;
     sl.r0 = wd.r0;
     sl.n = wd.n;
@@ -560,7 +691,6 @@ __device__ __forceinline__ bool map_slot(const Family& F, int T, Slot& sl, int& 
     sl.t2 = wd.tok[2];
     sl.t3 = wd.tok[3];
     sl.inline_tok = sl.n <= kTokInline;
-    if (sl.mat < 0 || sl.mat >= F.n_mats || sl.r0 < 0 || sl.n > F.max_rows - sl.r0) return false;
   } else {  // shared expert: every token, in order (row r is token r)
     sl.mat = 0;
     sl.r0 = 0;
@@ -816,29 +946,27 @@ struct SmallLds {
   T_ x[kTokInline][kXLds];
 };
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
 // Block-wide: rows t < nv of `cols` elements, row t read from src(t), into
-// lds.x[t].  cols is a multiple of 8 and at most kXLds.
+// lds.x[t], by direct global-to-LDS loads (each wave instruction moves 1 KB:
+// lane l's 16 bytes land 16*l bytes past the wave-uniform destination), so
+// the copy takes no registers.  cols is a multiple of 16 bytes' worth of
+// elements and at most kXLds.  Waits for every load this wave has issued
+// (the weight prefetch included), then for the whole block.
 template <typename T_, typename Src>
-__device__ __forceinline__ void stage_rows(SmallLds<T_>& lds, int nv, int cols, Src src) {
-  constexpr int kChunks = kTokInline * kXLds / 8 / kThreads;
-  const int per_row = cols >> 3, total = nv * per_row;
-  X8<T_> v[kChunks];
-#pragma unroll
-  for (int i = 0; i < kChunks; ++i) {
-    const int q = threadIdx.x + i * kThreads;
-    if (q < total) {
-      const int t = q / per_row, c = (q - t * per_row) * 8;
-      v[i].load(src(t) + c);
-    }
+__device__ __forceinline__ void stage_rows(SmallLds<T_>& lds, int nv, int cols, Src src, int wid,
+                                           int lane) {
+  constexpr int EPL = 16 / sizeof(T_);     // elements per lane
+  constexpr int EPI = EPL * kWave;         // elements per wave instruction
+  const int per_row = (cols + EPI - 1) / EPI, total = nv * per_row;
+  for (int q = wid; q < total; q += kWaves) {
+    const int t = q / per_row, c0 = (q - t * per_row) * EPI;
+    const int c = c0 + lane * EPL;
+    if (c < cols)
+      __builtin_amdgcn_global_load_lds(src(t) + c, (lds_void_t*)&lds.x[t][c0], 16, 0, 0);
   }
-#pragma unroll
-  for (int i = 0; i < kChunks; ++i) {
-    const int q = threadIdx.x + i * kThreads;
-    if (q < total) {
-      const int t = q / per_row, c = (q - t * per_row) * 8;
-      *reinterpret_cast<X8<T_>*>(&lds.x[t][c]) = v[i];
-    }
-  }
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 }
 
@@ -853,7 +981,8 @@ template <typename T_>
 __device__ __forceinline__ void gu_small_lds(const T_* __restrict__ Wg, const T_* __restrict__ Wu,
                                              int d, int rows, int i0, const T_* __restrict__ x,
                                              int T, const Slot& sl, const int* grp_token,
-                                             T_* __restrict__ h, int lane, SmallLds<T_>& lds) {
+                                             T_* __restrict__ h, int lane, int wid,
+                                             SmallLds<T_>& lds) {
   constexpr int NT = kTokInline, R = kStageRing, STEP = 8 * kWave;
   const int nv = sl.n;
   const size_t i = (size_t)min(i0, rows - 1);
@@ -873,7 +1002,7 @@ __device__ __forceinline__ void gu_small_lds(const T_* __restrict__ Wg, const T_
   }
   stage_rows(lds, nv, d, [&](int t) {
     return x + (size_t)slot_token(sl, grp_token, 0, t, nv, T) * d;
-  });
+  }, wid, lane);
   float ag[NT], au[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) ag[t] = au[t] = 0.f;
@@ -918,7 +1047,7 @@ __device__ __forceinline__ void gu_small_lds(const T_* __restrict__ Wg, const T_
 template <typename T_, int LPR, int CG>
 __device__ __forceinline__ void dn_small_lds(const T_* __restrict__ Wd, int d, int rows, int cb,
                                              const T_* __restrict__ h, const Slot& sl,
-                                             float* __restrict__ out, int lane,
+                                             float* __restrict__ out, int lane, int wid,
                                              SmallLds<T_>& lds) {
   constexpr int NT = kTokInline, R = kStageRing, STEP = 8 * LPR;
   constexpr int G = 64 / LPR;
@@ -938,7 +1067,7 @@ __device__ __forceinline__ void dn_small_lds(const T_* __restrict__ Wd, int d, i
       else
         rw[r][q].zero();
     }
-  stage_rows(lds, nv, rows, [&](int t) { return h + (size_t)(sl.r0 + t) * rows; });
+  stage_rows(lds, nv, rows, [&](int t) { return h + (size_t)(sl.r0 + t) * rows; }, wid, lane);
   float acc[CG][NT];
 #pragma unroll
   for (int q = 0; q < CG; ++q)
@@ -997,15 +1126,6 @@ __device__ __forceinline__ void dn_small_lds(const T_* __restrict__ Wd, int d, i
 // l%16.  A dot product is indifferent to the order of k, so each lane simply
 // takes the 16-byte chunk at 8g of every 32-element step.
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& u) {
-  return __builtin_bit_cast(bf16x8_t, u);
-}
-__device__ __forceinline__ u32x4_t ld16(const bf16_t* p) {
-  return *reinterpret_cast<const u32x4_t*>(p);
-}
-__device__ __forceinline__ u32x4_t ld16_stream(const bf16_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-}
 
 // K-split tiles: the four waves of a block share one 16-row (gate/up) or
 // 16-column (down) tile and each streams a quarter of K, two 32-wide steps
@@ -1315,7 +1435,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     if constexpr (XL) {
       static_assert(RPW == 1 && RW == 1, "staged activations take one row per wave");
       gu_small_lds<T_>(Wg, Wu, d, F.rows, tile * kWaves + wid, x, T, sl, F.grp_token, h, lane,
-                       *reinterpret_cast<SmallLds<T_>*>(lds_raw));
+                       wid, *reinterpret_cast<SmallLds<T_>*>(lds_raw));
       return;
     }
     const int i0 = tile * (kWaves * RPW) + wid * RPW;
@@ -1360,7 +1480,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     constexpr int CPW = CG * (64 / LPR);
     const int cb = tile * (kWaves * CPW) + wid * CPW;
     if constexpr (XL)  // every wave takes part in the staging
-      dn_small_lds<T_, LPR, CG>(Wd, d, F.rows, cb, h, sl, F.out, lane,
+      dn_small_lds<T_, LPR, CG>(Wd, d, F.rows, cb, h, sl, F.out, lane, wid,
                                 *reinterpret_cast<SmallLds<T_>*>(lds_raw));
     else if (cb < d)
       dn_small<T_, LPR, CG>(Wd, d, F.rows, cb, h, sl, F.out, lane);
@@ -1432,12 +1552,20 @@ static void launch(K kernel, dim3 grid, dim3 block, hipStream_t st, const Kernel
 template <typename T_>
 static hipError_t launch_route_t(const RouteArgs& ra, const PlanArgs* pa, hipStream_t st,
                                  const KernelEvents* ev) {
-  // two experts per block once there are enough blocks to cover the chip:
-  // each activation chunk is then read once for both
-  if (ra.E >= 256)
+  if constexpr (sizeof(T_) == 2) {
+    // matrix cores: 16-expert tiles x ksplit K pieces
+    const dim3 grid((ra.E + 15) / 16, ra.ksplit);
+    if (ra.T > 16)
+      launch(route_mfma_kernel<2>, grid, dim3(kThreads), st, ev, ra);
+    else
+      launch(route_mfma_kernel<1>, grid, dim3(kThreads), st, ev, ra);
+  } else if (ra.E >= 256) {
+    // two experts per block once there are enough blocks to cover the chip:
+    // each activation chunk is then read once for both
     launch(route_kernel<T_, 2>, dim3((ra.E + 1) / 2), dim3(kThreads), st, ev, ra);
-  else
+  } else {
     launch(route_kernel<T_, 1>, dim3(ra.E), dim3(kThreads), st, ev, ra);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   PlanArgs p{};

@@ -90,18 +90,27 @@ def test_route_parity(name, seed):
     print(f"{name} seed {seed}: near-tie tokens {near_total}")
 
 
-@pytest.mark.parametrize("score", ["softmax", "sigmoid", "softmax_bias"])
-def test_route_ties_go_to_lower_index(score):
+@pytest.mark.parametrize("score,dtype,d,T,E", [
+    ("softmax", "f32", 264, 5, 96), ("sigmoid", "f32", 264, 5, 96),
+    ("softmax_bias", "f32", 264, 5, 96),
+    # bf16 takes the matrix-core router: a ragged K split (some K pieces
+    # empty), at T = 20 a second, partly filled token tile, and at E = 330 a
+    # ragged last expert tile with fewer partial-logit planes
+    ("softmax", "bf16", 1032, 5, 96), ("sigmoid", "bf16", 1032, 20, 96),
+    ("softmax_bias", "bf16", 264, 20, 96), ("softmax", "bf16", 2056, 20, 330)])
+def test_route_ties_go_to_lower_index(score, dtype, d, T, E):
     """Duplicated router rows give bitwise-equal scores; the lower expert index
     takes the earlier slot.  An all-zero router ties every expert."""
-    E, d, k, T = 96, 264, 6, 5
+    k = 6
     g = torch.Generator().manual_seed(3)
     wr = (torch.randn(E, d, generator=g) * 0.05)
     for a, b in ((3, 70), (10, 11), (40, 95)):
         wr[b] = wr[a]
     x = torch.randn(T, d, generator=g)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    wr, x = wr.to(tdt), x.to(tdt)
     bias = torch.zeros(E) if score != "softmax" else None
-    desc = M.layer_desc(d, E, k, 64, score=score, dtype="f32", max_tokens=T)
+    desc = M.layer_desc(d, E, k, 64, score=score, dtype=dtype, max_tokens=T)
     w = {"w_router": wr.to(DEV), "router_bias": None if bias is None else bias.to(DEV)}
     g_ids, g_w, g_sel = run_route(desc, x.to(DEV), w, T)
     for a, b in ((3, 70), (10, 11), (40, 95)):
@@ -113,7 +122,7 @@ def test_route_ties_go_to_lower_index(score):
             if b in ids:
                 assert a in ids and ids.index(a) < ids.index(b)
     # all-zero router: experts 0..k-1, equal weights
-    w0 = {"w_router": torch.zeros(E, d, device=DEV), "router_bias": w["router_bias"]}
+    w0 = {"w_router": torch.zeros(E, d, dtype=tdt, device=DEV), "router_bias": w["router_bias"]}
     g_ids, g_w, _ = run_route(desc, x.to(DEV), w0, T)
     assert g_ids.tolist() == [list(range(k))] * T
     np.testing.assert_allclose(g_w, 1.0 / k, atol=1e-6)
