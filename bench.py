@@ -66,6 +66,8 @@ def parse():
     p.add_argument("--trace-report", nargs=2, metavar=("TRACE_CSV", "BENCH_JSON"), default=None,
                    help="write the kernel-trace summary of a profiled default run, beside the "
                         "JSON line of an unprofiled one, as markdown")
+    p.add_argument("--sweep-report", type=str, default=None, metavar="SWEEP_JSONL",
+                   help="write the --sweep lines as a markdown summary")
     p.add_argument("--source-hash", action="store_true",
                    help="print the hash of the kernel sources the counter summary refers to")
     return p.parse_args()
@@ -319,6 +321,17 @@ class Runner:
         b.record()
         torch.cuda.synchronize()
         us = a.elapsed_time(b) / (reps * self.R) * 1e3
+        # spread: one event pair per replay (R steps each), in a pass of its own
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for e0, e1 in evs:
+            e0.record()
+            g.replay()
+            e1.record()
+        torch.cuda.synchronize()
+        per = sorted(e0.elapsed_time(e1) / self.R * 1e3 for e0, e1 in evs)
+        self.spread = {q: round(per[min(len(per) - 1, int(q / 100 * len(per)))], 2)
+                       for q in (10, 50, 90)}
         # the graph must reproduce the eager result
         y_graph = self.y.clone()
         self.layers[0](self.x, self.y)
@@ -346,6 +359,80 @@ class Runner:
             for s in range(M.N_STAGES):
                 tot[s] += e[2 * s].elapsed_time(e[2 * s + 1]) * 1e3
         return {M.STAGE_NAMES[s]: tot[s] / steps for s in range(M.N_STAGES)}
+
+
+def measured_peak_GBps(M, dev, gib=2, iters=10):
+    """Achievable HBM read rate of the expert kernels' load pattern: the
+    library's streaming-read helper over a `gib` GiB buffer (8x the 256 MB
+    last-level cache), best of `iters`."""
+    import torch
+    n = (gib << 30) // 2
+    a = torch.ones(n, dtype=torch.bfloat16, device=dev)
+    sink = torch.empty((gib << 30) // 16384, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        M.moe_stream_read(a, sink)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(iters):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        M.moe_stream_read(a, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3
+        best = t if best is None else min(best, t)
+    del a, sink
+    torch.cuda.empty_cache()
+    return round((gib << 30) / best * 1e-9, 1)
+
+
+def sweep_report(path):
+    """Markdown table of a --sweep run: one row per (shape, batch)."""
+    rows, dv = [], []
+    for line in open(path):
+        r = json.loads(line)
+        (dv if "dept_vs_vanilla" in r else rows).append(r.get("dept_vs_vanilla", r))
+    print("# Every layer shape at its batches: graph-replayed decode step\n")
+    print("Command (repo root, one MI355X):\n\n```")
+    print("python bench.py --sweep --sweep-out gpurun_out/sweep.jsonl")
+    print("python bench.py --sweep-report gpurun_out/sweep.jsonl")
+    print("```\n")
+    print("Weights bytes are the distinct weights one step streams (router, active experts, "
+          "active departments, shared expert) plus x in and y out; stage times come from HIP "
+          "events around each kernel in eager steps.\n")
+    print("| shape | batch | step us | weight MB | GB/s | active experts | active depts "
+          "| route | top-k+plan | gate/up | down | combine |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
+    for r in rows:
+        st = r["stage_us"]
+        print(f"| {r['shape']} | {r['batch']} | {r['us']} | {r['weight_bytes'] / 1e6:.1f} | "
+              f"{r['GBps']} | {r['active_experts']} | {r['active_depts']} | {st['route']} | "
+              f"{st['dispatch']} | {st['gateup']} | {st['down']} | {st['combine']} |")
+    if dv:
+        print("\nDepartment form against the vanilla layer it was derived from (same router, "
+              "seed and batch):\n")
+        print("| batch | vanilla us | department us | speedup | byte ratio (dept / vanilla) |")
+        print("|---|---|---|---|---|")
+        for r in dv:
+            print(f"| {r['batch']} | {r['vanilla_us']} | {r['dept_us']} | {r['speedup']} | "
+                  f"{r['byte_ratio']} |")
+
+
+def dept_vs_vanilla(lines):
+    """Department form against the vanilla layer it was derived from (same
+    router, seed and batch): speedup beside the ratio of streamed bytes."""
+    by = {(l["shape"], l["batch"]): l for l in lines}
+    out = []
+    for (dept, van) in (("deamoe_dsv3_d7168_e256_m32_s1792_p256_top8",
+                         "deepseek_v3_d7168_e256_i2048_s2048_top8"),):
+        for T in sorted({b for (s_, b) in by if s_ == dept}):
+            if (van, T) in by:
+                a, b = by[(van, T)], by[(dept, T)]
+                out.append({"batch": T, "vanilla_us": a["us"], "dept_us": b["us"],
+                            "speedup": round(a["us"] / b["us"], 3),
+                            "vanilla_bytes": a["weight_bytes"], "dept_bytes": b["weight_bytes"],
+                            "byte_ratio": round(b["weight_bytes"] / a["weight_bytes"], 3)})
+    return out
 
 
 KERNEL_SOURCES = ("moe_layer_decode_amd/csrc/moe_kernels.hip",
@@ -423,6 +510,9 @@ def main():
     if args.source_hash:
         print(kernel_source_hash())
         return
+    if args.sweep_report:
+        sweep_report(args.sweep_report)
+        return
     if args.trace_report:
         trace_report(*args.trace_report)
         return
@@ -484,6 +574,8 @@ def main():
         rec = {"us": round(us, 2), "eager_us": round(eager_us, 2),
                "graph_us": None if graph_us is None else round(graph_us, 2),
                "graph_matches_eager": graph_same,
+               "graph_replay_us_p10_p50_p90": [r.spread[q] for q in (10, 50, 90)]
+               if graph_us is not None else None,
                "weight_bytes": r.step_bytes, "active_experts": r.n_active,
                "active_depts": r.n_active_depts,
                "GBps": round(r.step_bytes / us * 1e-3, 1),
@@ -504,6 +596,7 @@ def main():
     del r, head
     torch.cuda.empty_cache()
     achieved = gu / stages["gateup"] * 1e-3  # GB/s
+    meas_peak = measured_peak_GBps(M, dev)
     out = {
         "metric": METRIC, "value": round(us, 2), "unit": "us", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(us / 1e3, 5),
@@ -519,13 +612,16 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic() if shape.name == HEADLINE and head_T == 16 else None,
                      "algorithmic_bytes_per_launch": gu,
-                     "launch_us": round(stages["gateup"], 2)},
+                     "launch_us": round(stages["gateup"], 2),
+                     "measured_peak": meas_peak,
+                     "frac_measured_peak": round(achieved / meas_peak, 4)},
     }
     if not args.no_cpu_baseline:
         log("cpu baseline ...")
         out["cpu_baseline"] = cpu_baseline(shape, head_T, base, args.cpu_seconds)
     if args.sweep:
         os.makedirs(os.path.dirname(args.sweep_out) or ".", exist_ok=True)
+        sweep_lines = []
         with open(args.sweep_out, "w") as f:
             for name, sh in moe_synth.SHAPES.items():
                 if name == shape.name:
@@ -549,11 +645,16 @@ def main():
                             "active_depts": rr.n_active_depts,
                             "GBps": round(rr.step_bytes / u * 1e-3, 1),
                             "stage_us": {k: round(v, 2) for k, v in st.items()}}
+                    sweep_lines.append(line)
                     f.write(json.dumps(line) + "\n")
                     f.flush()
                     log(json.dumps(line))
                     del rr
                     torch.cuda.empty_cache()
+            dv = dept_vs_vanilla(sweep_lines)
+            for line in dv:
+                f.write(json.dumps({"dept_vs_vanilla": line}) + "\n")
+            out["dept_vs_vanilla"] = dv
     print(json.dumps(out), flush=True)
 
 

@@ -240,6 +240,17 @@ const char* moe_status_string(moe_status status);
 uint64_t moe_loaded_weight_bytes(const moe_layer_desc* desc, int32_t n_active,
                                  int32_t n_active_depts);
 
+/* Measurement helper, not a step of the layer: reads `bytes` of device
+ * memory at `src` once with the load pattern of the expert kernels (16-byte
+ * streaming loads, one 4 KiB row per wave, four rows per 256-thread block)
+ * and writes, for every 16 KiB block of the input, the sum of its bf16
+ * values as a float into sink[block] (ceil(bytes / 16384) floats, caller
+ * owned).  Timing it gives the HBM read rate this access pattern can reach,
+ * the reference the expert kernels' roofline fraction is read against.
+ * bytes must be a positive multiple of 16384; src and sink 16-byte aligned;
+ * errors return before any launch. */
+moe_status moe_stream_read(const void* src, size_t bytes, float* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

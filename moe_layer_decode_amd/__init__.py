@@ -21,7 +21,7 @@ __all__ = [
     "MoeError", "LayerDesc", "Weights", "Plan", "layer_desc", "lib", "lib_path",
     "moe_workspace_bytes", "moe_workspace_init", "moe_validate_desc", "moe_route", "moe_dispatch",
     "moe_expert_ffn", "moe_combine", "moe_layer_decode", "moe_status_string",
-    "moe_loaded_weight_bytes", "alloc_workspace", "plan_to_host", "MoeLayer",
+    "moe_loaded_weight_bytes", "moe_stream_read", "alloc_workspace", "plan_to_host", "MoeLayer",
     "MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE",
     "MOE_ERR_HIP", "SCORE_FNS", "N_STAGES", "STAGE_NAMES", "EXPORTED_SYMBOLS",
 ]
@@ -36,7 +36,7 @@ STAGE_NAMES = ("route", "dispatch", "gateup", "down", "combine")
 EXPORTED_SYMBOLS = (
     "moe_workspace_bytes", "moe_workspace_init", "moe_validate_desc", "moe_plan_from_workspace", "moe_route",
     "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_layer_decode",
-    "moe_status_string", "moe_loaded_weight_bytes",
+    "moe_status_string", "moe_loaded_weight_bytes", "moe_stream_read",
 )
 
 _i32, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -115,8 +115,22 @@ def lib() -> ctypes.CDLL:
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_loaded_weight_bytes.argtypes = [P(LayerDesc), _i32, _i32]
     L.moe_loaded_weight_bytes.restype = ctypes.c_uint64
+    L.moe_stream_read.argtypes = [_vp, _sz, _vp, _vp]
+    L.moe_stream_read.restype = _i32
     _LIB = L
     return L
+
+
+def moe_stream_read(src: torch.Tensor, sink: torch.Tensor):
+    """Measurement helper: read `src` (bf16, a multiple of 16 KiB) once;
+    sink[b] = sum of the bf16 values of its 16 KiB block b."""
+    nbytes = src.numel() * src.element_size()
+    if src.dtype != torch.bfloat16 or not src.is_contiguous():
+        raise ValueError("src must be a contiguous bf16 tensor")
+    if sink.dtype != torch.float32 or sink.numel() < nbytes // 16384:
+        raise ValueError("sink needs one float per 16 KiB of src")
+    _check(lib().moe_stream_read(src.data_ptr(), nbytes, sink.data_ptr(), _stream(src.device)),
+           "moe_stream_read")
 
 
 def moe_status_string(status: int) -> str:

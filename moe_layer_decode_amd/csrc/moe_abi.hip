@@ -392,6 +392,14 @@ size_t moe_workspace_bytes(const moe_layer_desc* desc) {
 
 moe_status moe_validate_desc(const moe_layer_desc* desc) { return check_desc(desc); }
 
+moe_status moe_stream_read(const void* src, size_t bytes, float* sink, void* stream) {
+  constexpr size_t kBlockBytes = 16384;
+  if (!ok_ptr(src) || !ok_ptr(sink) || bytes == 0 || bytes % kBlockBytes) return MOE_ERR_INVALID_ARG;
+  const size_t blocks = bytes / kBlockBytes;
+  if (blocks > 0x7fffffffu) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_stream_read(src, blocks, sink, static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_workspace_init(const moe_layer_desc* desc, void* workspace, size_t ws_bytes,
                               void* stream) {
   moe_status s = check_desc(desc);

@@ -125,5 +125,6 @@ hipError_t launch_down(int w_dtype, const FamilySet& set, int T, int d, int lpr,
 hipError_t launch_combine(int act_dtype, const CombineArgs& a, void* y, hipStream_t st,
                           const KernelEvents* ev);
 hipError_t launch_zero(unsigned int* p, size_t n, hipStream_t st);
+hipError_t launch_stream_read(const void* src, size_t blocks, float* sink, hipStream_t st);
 
 }  // namespace moe

@@ -1669,6 +1669,38 @@ hipError_t launch_combine(int act_dtype, const CombineArgs& a, void* y, hipStrea
   return hipGetLastError();
 }
 
+// Streaming read for measurement: block b sums the 8192 bf16 values of bytes
+// [16 KiB b, 16 KiB (b+1)), one 4 KiB row per wave, each lane 16 bytes per
+// step with the next step requested before the current one is used.
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const bf16_t* __restrict__ src,
+                                                              float* __restrict__ sink) {
+  __shared__ float part[kWaves];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const bf16_t* row = src + ((size_t)blockIdx.x * kWaves + wid) * 2048 + lane * 8;
+  Raw8<bf16_t> cur, nxt;
+  cur.load(row);
+  float acc = 0.f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    if (s + 1 < 4) nxt.load(row + (s + 1) * 512);
+    float v[8];
+    cur.to_f32(v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc += v[i];
+    cur = nxt;
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) part[wid] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = ((part[0] + part[1]) + part[2]) + part[3];
+}
+
+hipError_t launch_stream_read(const void* src, size_t blocks, float* sink, hipStream_t st) {
+  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, st,
+                     static_cast<const bf16_t*>(src), sink);
+  return hipGetLastError();
+}
+
 hipError_t launch_zero(unsigned int* p, size_t n, hipStream_t st) {
   if (n == 0) return hipSuccess;
   const int blocks = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);

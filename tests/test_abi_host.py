@@ -127,6 +127,14 @@ def test_calls_reject_bad_arguments_before_any_launch(lib):
                                 None, nul) == M.MOE_ERR_INVALID_ARG
 
 
+def test_stream_read_rejects_bad_arguments(lib):
+    assert lib.moe_stream_read(256, 16384 + 16, 256, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_stream_read(256, 0, 256, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_stream_read(None, 16384, 256, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_stream_read(258, 16384, 256, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_stream_read(256, 16384, None, None) == M.MOE_ERR_INVALID_ARG
+
+
 def test_zero_tokens_is_a_noop(lib):
     d = _desc()
     P = M.Plan()

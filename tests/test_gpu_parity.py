@@ -458,3 +458,17 @@ def test_stage_events_time_each_kernel():
     for s in range(M.N_STAGES):
         ms = evs[2 * s].elapsed_time(evs[2 * s + 1])
         assert 0.0 < ms < 50.0, (M.STAGE_NAMES[s], ms)
+
+
+def test_stream_read_sums_each_16k_block():
+    """The measurement helper reads every byte once: block sums of a known
+    bf16 pattern (small integers, exact in fp32)."""
+    n_blocks = 300
+    vals = (torch.arange(n_blocks * 8192, dtype=torch.int64) % 7 - 3).to(torch.bfloat16)
+    src = vals.to(DEV)
+    sink = torch.full((n_blocks,), -1.0, dtype=torch.float32, device=DEV)
+    M.moe_stream_read(src, sink)
+    torch.cuda.synchronize()
+    ref = vals.float().view(n_blocks, 8192).sum(1)
+    assert torch.equal(sink.cpu(), ref)
+
