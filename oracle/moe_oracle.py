@@ -45,7 +45,18 @@ justification in the design notes):
   R9 department slice form: expert e belongs to department e // (E/m); its
      intermediate is [department slice S ; private slice P];
   R10 c_{t,j} = sum of the token's final weights over its selected experts
-     in department j.
+     in department j;
+  R15 factorised department experts (DeaMoE section 3.1): the interface
+     non-linearity sigma is SiLU at all three interfaces (section 3.4 adopts
+     it);
+  R16 storage of the factorised form: W_d^j is kept as its transpose
+     [d][hffn] and A_d^i as its transpose [hffn][hffn], so that each output
+     is one contiguous row; the functions below turn them back into W_d^j and
+     A_d^i and apply the transposes the pages write;
+  R17 the GPU pre-combines a token's p_i * Z^{j,i} over its experts in
+     department j before the single (W_d^j)^T product, exact by linearity;
+     the oracle keeps the pages' order (one product per expert) and a test
+     pins the two equal.
 """
 from __future__ import annotations
 
@@ -58,6 +69,8 @@ __all__ = [
     "route", "dispatch", "swiglu", "expert_outputs", "combine",
     "layer_bruteforce", "layer_grouped", "dept_layer_expanded",
     "dept_layer_factored", "layer_token_output", "loaded_weight_bytes",
+    "deamoe_expert", "deamoe_token_output", "deamoe_layer_per_expert",
+    "deamoe_layer_two_stage", "deamoe_layer_precombined",
     "select_from_scores", "silu", "cast_output", "SOFTMAX", "SIGMOID", "SOFTMAX_BIAS",
 ]
 
@@ -404,20 +417,146 @@ def dept_layer_factored(x, weights, ids, w, n_experts: int, n_depts: int) -> np.
 
 
 # ----------------------------------------------------------------------------
+# Factorised DeaMoE experts  [DeaMoE §3.1 (expert = department backbone +
+# private transforms), §3.2 (two-stage computation), §3.4 (sigma = SiLU)]
+# ----------------------------------------------------------------------------
+
+def _sigma(z):
+    """The interface non-linearity between department and expert matrices
+    (R15: SiLU)."""
+    return silu(z)
+
+
+def deamoe_expert(x_t, wd_gate_j, wd_up_j, wd_down_j, a_gate_i, a_up_i, a_down_i,
+                  cols: Optional[Sequence[int]] = None) -> np.ndarray:
+    """DeaMoE_i(x) of expert i in department j (section 3.1):
+
+        g_hat(x) = SiLU(A_g^i sigma(W_g^j x))
+        u_hat(x) = A_u^i sigma(W_u^j x)
+        d_hat(v) = (W_d^j)^T sigma((A_d^i)^T v)
+        DeaMoE_i(x) = d_hat(g_hat(x) * u_hat(x))
+
+    W_g^j, W_u^j are [hffn][d]; A_g^i, A_u^i are [hffn][hffn]; wd_down_j holds
+    (W_d^j)^T and a_down_i holds (A_d^i)^T (R16).  `cols` restricts the output
+    to the listed entries of d."""
+    x = _f64(x_t)
+    W_g, W_u = _f64(wd_gate_j), _f64(wd_up_j)
+    W_d = _f64(wd_down_j).T                 # [hffn][d]
+    A_g, A_u = _f64(a_gate_i), _f64(a_up_i)
+    A_d = _f64(a_down_i).T                  # [hffn][hffn]
+    g_hat = silu(A_g @ _sigma(W_g @ x))
+    u_hat = A_u @ _sigma(W_u @ x)
+    v = g_hat * u_hat
+    z = _sigma(A_d.T @ v)
+    W_dT = W_d.T if cols is None else W_d.T[list(cols)]
+    return W_dT @ z
+
+
+def _deamoe_mats(weights, e: int, n_experts: int, n_depts: int):
+    j = e // (n_experts // n_depts)
+    return (weights["wd_gate"][j], weights["wd_up"][j], weights["wd_down"][j],
+            weights["w_gate"][e], weights["w_up"][e], weights["w_down"][e])
+
+
+def deamoe_token_output(x_t, ids_t, w_t, weights, n_experts: int, n_depts: int,
+                        cols: Optional[Sequence[int]] = None) -> np.ndarray:
+    """y_t by Eq. (3) over factorised experts: sum over the token's slots in
+    slot order of p_j * DeaMoE_{e_j}(x_t), plus the shared expert (R8)."""
+    y = 0.0
+    for j in range(len(ids_t)):
+        y = y + float(w_t[j]) * deamoe_expert(
+            x_t, *_deamoe_mats(weights, int(ids_t[j]), n_experts, n_depts), cols=cols)
+    return y + _shared(weights, x_t, cols)
+
+
+def deamoe_layer_per_expert(x, weights, ids, w, n_experts: int, n_depts: int) -> np.ndarray:
+    """The whole factorised layer token by token, each selected expert by its
+    own DeaMoE_i (no sharing of the department work)."""
+    T = ids.shape[0]
+    rows = [deamoe_token_output(x[t], ids[t], w[t], weights, n_experts, n_depts)
+            for t in range(T)]
+    return np.stack(rows) if T else np.zeros((0, _f64(x).shape[1]))
+
+
+def deamoe_layer_two_stage(x, weights, ids, w, n_experts: int, n_depts: int) -> np.ndarray:
+    """Section 3.2's order.  For each department j, collect its tokens X^j and
+    compute X_g^j = sigma(W_g^j X^j), X_u^j = sigma(W_u^j X^j) once; hand each
+    expert i its rows: Y^{j,i} = SiLU(A_g^i X_g^{j,i}) * (A_u^i X_u^{j,i}),
+    Z^{j,i} = sigma((A_d^i)^T Y^{j,i}); collect Z^j and compute the outputs
+    O^j = (W_d^j)^T Z^j; the layer combines them by Eq. (3)."""
+    x = _f64(x)
+    T, k = ids.shape
+    d = x.shape[1]
+    plan = dispatch(ids, n_experts, w, n_depts)
+    g = n_experts // n_depts
+    X_g, X_u = {}, {}                       # (t, j) -> sigma(W x_t)
+    for q in range(plan["n_dept_rows"]):
+        j, t = int(plan["dept_row_dept"][q]), int(plan["dept_row_token"][q])
+        X_g[(t, j)] = _sigma(_f64(weights["wd_gate"][j]) @ x[t])
+        X_u[(t, j)] = _sigma(_f64(weights["wd_up"][j]) @ x[t])
+    y = np.zeros((T, d))
+    for r in range(plan["n_rows"]):         # expert by expert, row by row
+        e, t = int(plan["row_expert"][r]), int(plan["row_token"][r])
+        j = e // g
+        A_g, A_u = _f64(weights["w_gate"][e]), _f64(weights["w_up"][e])
+        A_d = _f64(weights["w_down"][e]).T
+        Y = silu(A_g @ X_g[(t, j)]) * (A_u @ X_u[(t, j)])
+        Z = _sigma(A_d.T @ Y)
+        W_d = _f64(weights["wd_down"][j]).T
+        O = W_d.T @ Z
+        y[t] += plan["row_weight"][r] * O
+    shared = weights.get("ws_gate") is not None
+    for t in range(T):
+        if shared:
+            y[t] += _shared(weights, x[t])
+    return y
+
+
+def deamoe_layer_precombined(x, weights, ids, w, n_experts: int, n_depts: int) -> np.ndarray:
+    """The same layer with a token's weighted Z^{j,i} summed over its experts
+    in department j before one (W_d^j)^T product per (token, department)
+    (R17; the order the GPU takes)."""
+    x = _f64(x)
+    T, k = ids.shape
+    d = x.shape[1]
+    plan = dispatch(ids, n_experts, w, n_depts)
+    g = n_experts // n_depts
+    y = np.zeros((T, d))
+    for q in range(plan["n_dept_rows"]):
+        j, t = int(plan["dept_row_dept"][q]), int(plan["dept_row_token"][q])
+        xg = _sigma(_f64(weights["wd_gate"][j]) @ x[t])
+        xu = _sigma(_f64(weights["wd_up"][j]) @ x[t])
+        zc = 0.0
+        for s in range(k):                  # slot order
+            e = int(ids[t, s])
+            if 0 <= e < n_experts and e // g == j:
+                A_d = _f64(weights["w_down"][e]).T
+                Y = silu(_f64(weights["w_gate"][e]) @ xg) * (_f64(weights["w_up"][e]) @ xu)
+                zc = zc + _f64(w)[t, s] * _sigma(A_d.T @ Y)
+        W_d = _f64(weights["wd_down"][j]).T
+        y[t] += W_d.T @ zc
+    if weights.get("ws_gate") is not None:
+        for t in range(T):
+            y[t] += _shared(weights, x[t])
+    return y
+
+
+# ----------------------------------------------------------------------------
 # Weights streamed per step  [DeaMoE §3.3, Figure 2]
 # ----------------------------------------------------------------------------
 
 def loaded_weight_bytes(ids, n_experts: int, d: int, d_ff: int, bytes_per_w: int,
                         n_depts: int = 0, d_ff_dept: int = 0, d_ff_shared: int = 0,
-                        include_router: bool = True) -> int:
+                        include_router: bool = True, factorised: bool = False) -> int:
     """Bytes of weights one decode step must read, each matrix once:
-    router E*d, every distinct selected expert's three d x I matrices, the
-    shared expert, and (department form) every distinct selected
-    department's three d x S slices."""
+    router E*d, every distinct selected expert's three d x I matrices (three
+    I x I private transforms in the factorised form, section 3.1), the shared
+    expert, and (department forms) every distinct selected department's
+    three d x S matrices."""
     ids = np.asarray(ids).reshape(-1)
     experts = {int(e) for e in ids if 0 <= e < n_experts}
     n = (n_experts * d if include_router else 0)
-    n += len(experts) * 3 * d * d_ff
+    n += len(experts) * 3 * (d_ff if factorised else d) * d_ff
     n += 3 * d * d_ff_shared
     if n_depts:
         g = n_experts // n_depts

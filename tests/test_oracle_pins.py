@@ -409,3 +409,110 @@ def test_resident_bytes_of_layer_shapes():
     per_expert = 3 * s.d * s.d_ff
     assert per_expert / 1e6 == pytest.approx(44.04, abs=0.01)
     assert s.n_experts * per_expert * 2 / 1e9 == pytest.approx(22.5, abs=0.1)
+
+
+# ---------------------------------------------------------------------------
+# Factorised DeaMoE experts (DeaMoE section 3.1 / 3.2): each pin below would
+# fail for a transposed A, a sigma dropped or moved, or a department mixed up
+# ---------------------------------------------------------------------------
+
+def _rand_factorised(rng, d, E, m, f, Is=0, a_std=0.3):
+    w = {"w_router": rng.normal(0, 0.3, (E, d)).astype(np.float32),
+         "wd_gate": rng.normal(0, 0.3, (m, f, d)).astype(np.float32),
+         "wd_up": rng.normal(0, 0.3, (m, f, d)).astype(np.float32),
+         "wd_down": rng.normal(0, 0.3, (m, d, f)).astype(np.float32),   # (W_d^j)^T
+         "w_gate": rng.normal(0, a_std, (E, f, f)).astype(np.float32),
+         "w_up": rng.normal(0, a_std, (E, f, f)).astype(np.float32),
+         "w_down": rng.normal(0, a_std, (E, f, f)).astype(np.float32)}  # (A_d^i)^T
+    if Is:
+        w.update(ws_gate=rng.normal(0, 0.3, (Is, d)).astype(np.float32),
+                 ws_up=rng.normal(0, 0.3, (Is, d)).astype(np.float32),
+                 ws_down=rng.normal(0, 0.3, (d, Is)).astype(np.float32))
+    return w
+
+
+def _silu_ref(z):
+    return z * scipy.special.expit(z)
+
+
+def test_factorised_expert_with_permutation_transforms():
+    """A_g, A_u, A_d permutation matrices: every matrix product with an A
+    becomes an explicit index shuffle, computed here element by element
+    without any matrix product, so the placement and orientation of each A
+    (A vs A^T) and of each sigma is checked."""
+    rng = _rng(400)
+    d, f = 6, 5
+    x = rng.normal(0, 1, d)
+    Wg, Wu = rng.normal(0, 0.5, (f, d)), rng.normal(0, 0.5, (f, d))
+    Wd = rng.normal(0, 0.5, (f, d))                 # W_d^j in the pages' [hffn][h] form
+    pg, pu, pd = rng.permutation(f), rng.permutation(f), rng.permutation(f)
+    Ag, Au, Ad = np.eye(f)[pg], np.eye(f)[pu], np.eye(f)[pd]   # (A v)[r] = v[p[r]]
+    # element by element
+    wgx = [sum(Wg[r, c] * x[c] for c in range(d)) for r in range(f)]
+    wux = [sum(Wu[r, c] * x[c] for c in range(d)) for r in range(f)]
+    g_hat = [_silu_ref(_silu_ref(wgx[pg[r]])) for r in range(f)]
+    u_hat = [_silu_ref(wux[pu[r]]) for r in range(f)]
+    v = [g_hat[r] * u_hat[r] for r in range(f)]
+    # (A_d^T v)[c] = sum_r A_d[r, c] v[r] = v[r] where pd[r] == c
+    inv = np.argsort(pd)
+    z = [_silu_ref(v[inv[c]]) for c in range(f)]
+    y = [sum(Wd[r, c] * z[r] for r in range(f)) for c in range(d)]   # (W_d^T z)[c]
+    got = O.deamoe_expert(x, Wg, Wu, Wd.T, Ag, Au, Ad.T)
+    np.testing.assert_allclose(got, y, rtol=1e-12, atol=1e-14)
+
+
+def test_factorised_identity_transforms_make_a_department_one_expert():
+    """A = I (the identity start of section 3.4): every expert of a
+    department computes the same function, W_d^T SiLU(SiLU(SiLU(W_g x)) *
+    SiLU(W_u x)), and experts of different departments differ."""
+    rng = _rng(401)
+    d, E, m, f = 12, 6, 2, 7
+    w = _rand_factorised(rng, d, E, m, f)
+    for n in ("w_gate", "w_up", "w_down"):
+        w[n] = np.broadcast_to(np.eye(f, dtype=np.float32), (E, f, f)).copy()
+    x = rng.normal(0, 1, d)
+    outs = [O.deamoe_expert(x, w["wd_gate"][e // 3], w["wd_up"][e // 3], w["wd_down"][e // 3],
+                            w["w_gate"][e], w["w_up"][e], w["w_down"][e]) for e in range(E)]
+    for j in range(m):
+        Wg, Wu, WdT = (w["wd_gate"][j].astype(np.float64), w["wd_up"][j].astype(np.float64),
+                       w["wd_down"][j].astype(np.float64))
+        ref = WdT @ _silu_ref(_silu_ref(_silu_ref(Wg @ x)) * _silu_ref(Wu @ x))
+        for e in range(3 * j, 3 * j + 3):
+            np.testing.assert_allclose(outs[e], ref, rtol=1e-12, atol=1e-14)
+    assert np.abs(outs[0] - outs[3]).max() > 1e-3
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_factorised_two_stage_equals_per_expert_and_precombined(seed):
+    """Section 3.2's two-stage computation (department work once per token,
+    then per-expert transforms) equals running every selected expert's own
+    DeaMoE_i, and the GPU's pre-combined order (R17) equals both."""
+    rng = _rng(410 + seed)
+    d, E, m, f, k, T = 10, 12, [2, 3, 4, 6][seed], 6, 4, 5
+    w = _rand_factorised(rng, d, E, m, f, Is=4 if seed % 2 else 0)
+    x = rng.normal(0, 1, (T, d)).astype(np.float32)
+    ids, rw, _, _ = O.route(x, w["w_router"], k, [O.SOFTMAX, O.SIGMOID][seed % 2],
+                            rng.uniform(-0.1, 0.1, E).astype(np.float32))
+    a = O.deamoe_layer_per_expert(x, w, ids, rw, E, m)
+    b = O.deamoe_layer_two_stage(x, w, ids, rw, E, m)
+    c = O.deamoe_layer_precombined(x, w, ids, rw, E, m)
+    np.testing.assert_allclose(b, a, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(c, a, rtol=1e-10, atol=1e-12)
+
+
+def test_factorised_loaded_bytes_reproduce_fig2():
+    """The oracle's byte count of the factorised form, averaged over uniform
+    routings at the DeepSeek-V3-matched configuration (8 departments, 864
+    experts, k = 10, hffn = 2048, h = 7168), over the vanilla layer's count
+    (256 experts, k = 8) reproduces Figure 2's ratio at 4 and 16 tokens."""
+    rng = _rng(420)
+    for B, n_samples in ((4, 3000), (16, 1500)):
+        dea, van = [], []
+        for _ in range(n_samples):
+            ids = np.stack([rng.choice(864, 10, replace=False) for _ in range(B)])
+            dea.append(O.loaded_weight_bytes(ids, 864, 7168, 2048, 1, 8, 2048,
+                                             include_router=False, factorised=True))
+            ids_v = np.stack([rng.choice(256, 8, replace=False) for _ in range(B)])
+            van.append(O.loaded_weight_bytes(ids_v, 256, 7168, 2048, 1, include_router=False))
+        ratio = np.mean(dea) / np.mean(van)
+        assert ratio == pytest.approx(_fig2_ratio(B), rel=5e-3)
