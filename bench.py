@@ -222,29 +222,35 @@ def desc_of(M, shape, max_tokens):
     return M.layer_desc(shape.d, shape.n_experts, shape.top_k, shape.d_ff, n_depts=shape.n_depts,
                         d_ff_dept=shape.d_ff_dept, d_ff_shared=shape.d_ff_shared,
                         score=shape.score, renormalize=shape.renormalize,
-                        route_scale=shape.route_scale, dtype=shape.dtype, max_tokens=max_tokens)
+                        route_scale=shape.route_scale, dtype=shape.dtype, max_tokens=max_tokens,
+                        dept_form=shape.dept_form)
 
 
 def gateup_bytes(shape, T, n_active, n_active_depts, n_rows, n_dept_rows):
-    """Algorithmic bytes of one gate/up launch: gate+up weights of every active
-    matrix once, the T activation rows, the fp32 h rows written."""
+    """Algorithmic bytes of the gate/up stage: gate+up weights of every active
+    matrix once (private transforms are S x S in the factorised form), the T
+    activation rows read, the h rows written (layer dtype)."""
     wb = 4 if shape.dtype == "f32" else 2
     d = shape.d
-    b = n_active * 2 * shape.d_ff * d * wb
+    k_priv = shape.d_ff if shape.dept_form == "factorised" else d
+    b = n_active * 2 * shape.d_ff * k_priv * wb
     b += n_active_depts * 2 * shape.d_ff_dept * d * wb
     b += (2 * shape.d_ff_shared * d * wb) if shape.d_ff_shared else 0
     b += T * d * wb
-    b += 4 * (n_rows * shape.d_ff + n_dept_rows * shape.d_ff_dept + T * shape.d_ff_shared)
+    b += wb * (n_rows * shape.d_ff + n_dept_rows * shape.d_ff_dept + T * shape.d_ff_shared)
     return b
 
 
 def down_bytes(shape, T, n_active, n_active_depts, n_rows, n_dept_rows):
+    """Algorithmic bytes of the down stage: down weights of every active matrix
+    once, the h rows read (layer dtype), the fp32 output rows written."""
     wb = 4 if shape.dtype == "f32" else 2
     d = shape.d
-    b = n_active * shape.d_ff * d * wb + n_active_depts * shape.d_ff_dept * d * wb
+    n_priv = shape.d_ff if shape.dept_form == "factorised" else d
+    b = n_active * shape.d_ff * n_priv * wb + n_active_depts * shape.d_ff_dept * d * wb
     b += (shape.d_ff_shared * d * wb) if shape.d_ff_shared else 0
-    b += 4 * (n_rows * shape.d_ff + n_dept_rows * shape.d_ff_dept + T * shape.d_ff_shared)
-    b += 4 * d * (n_rows + n_dept_rows + (T if shape.d_ff_shared else 0))
+    b += wb * (n_rows * shape.d_ff + n_dept_rows * shape.d_ff_dept + T * shape.d_ff_shared)
+    b += 4 * (n_rows * n_priv + n_dept_rows * d + (T * d if shape.d_ff_shared else 0))
     return b
 
 

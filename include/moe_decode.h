@@ -7,8 +7,11 @@
  *     section 2.1: Eq. (1) SwiGLU expert, Eq. (2) top-k of the router
  *     logits W_r x, Eq. (3) weighted sum of the selected experts' outputs;
  *     section 3.2: the department backbone is computed once for all of a
- *     department's tokens (here in slice form: an expert's intermediate is
- *     [department-shared slice ; private slice]).
+ *     department's tokens.  Two department forms: the slice form (an
+ *     expert's intermediate is [department-shared slice ; private slice])
+ *     and the factorised form of section 3.1, where expert i of department
+ *     j computes (W_d^j)^T s(A_d^i^T (SiLU(A_g^i s(W_g^j x)) * (A_u^i
+ *     s(W_u^j x)))), s = SiLU, in section 3.2's two-stage order.
  *   - "DeepSeekMoE Guide: Fine-Grained Experts & Dynamic Routing",
  *     "Shared Expert Isolation" and "Auxiliary-Loss-Free Dynamic Load
  *     Balancing": an always-on shared expert; selection on score + bias with
@@ -49,6 +52,11 @@
  *   wd_down              [m][d][S]     w_dtype
  *   ws_gate, ws_up       [Is][d]       w_dtype          (shared expert)
  *   ws_down              [d][Is]       w_dtype
+ *   Factorised department form (dept_form = MOE_DEPT_FACTORISED, I = S):
+ *   wd_gate, wd_up       [m][S][d]     W_g^j, W_u^j     (department backbones)
+ *   wd_down              [m][d][S]     (W_d^j)^T
+ *   w_gate, w_up         [E][S][S]     A_g^i, A_u^i     (private transforms)
+ *   w_down               [E][S][S]     (A_d^i)^T
  *   Every pointer must be 16-byte aligned; d, I, S, Is must be multiples of 8.
  */
 #ifndef MOE_DECODE_H
@@ -83,6 +91,14 @@ typedef enum {
   MOE_SCORE_SOFTMAX_BIAS = 2
 } moe_score_fn;
 
+typedef enum {
+  /* expert intermediate = [department slice S ; private slice I] */
+  MOE_DEPT_SLICE = 0,
+  /* DeaMoE section 3.1: department backbones W^j (S x d) and private
+   * S x S transforms A^i, computed in section 3.2's two-stage order */
+  MOE_DEPT_FACTORISED = 1
+} moe_dept_form;
+
 /* Hard limits (MOE_ERR_UNSUPPORTED beyond them). */
 #define MOE_MAX_EXPERTS 2048
 #define MOE_MAX_TOP_K 32
@@ -103,6 +119,7 @@ typedef struct {
   int32_t w_dtype;       /* moe_dtype of all weight matrices */
   int32_t act_dtype;     /* moe_dtype of x and y (MOE_F32 with MOE_F32 weights, else MOE_BF16) */
   int32_t max_tokens;    /* largest T a workspace sized for this descriptor accepts */
+  int32_t dept_form;     /* moe_dept_form (n_depts > 0); factorised requires d_ff == d_ff_dept */
 } moe_layer_desc;
 
 typedef struct {
@@ -147,6 +164,7 @@ typedef struct {
   float* dept_row_scale;    /* [Pm]  c_{t,j}: sum of the token's weights over its experts in department j */
   int32_t* dept_inv;        /* [max_tokens*m] pair of (t, j), -1 if none */
   int32_t* active_depts;    /* [m]   departments with pairs, ascending */
+  int32_t* row_pair;        /* [A]   factorised form: the (token, department) pair of each row */
   int32_t n_tokens;         /* T the plan was built for (host copy) */
 } moe_plan;
 
@@ -154,7 +172,10 @@ typedef struct {
  * 2 * MOE_N_STAGES hipEvent_t created by the caller (with timing enabled);
  * stage i's kernel is launched with hipExtLaunchKernel so that the runtime
  * records stage_events[2i] when it starts and stage_events[2i+1] when it
- * ends -- the interval is that kernel alone. */
+ * ends -- the interval is that kernel alone.  In the factorised form the
+ * GATEUP stage runs from the start of the backbone gate/up kernel to the end
+ * of the private gate/up kernel, and DOWN from the start of the private down
+ * kernel to the end of the department down kernel (pair sums in between). */
 #define MOE_STAGE_ROUTE 0     /* router logits, split over d across the chip */
 #define MOE_STAGE_DISPATCH 1  /* top-k + weights + dispatch plan (one block) */
 #define MOE_STAGE_GATEUP 2    /* grouped gate/up with SiLU(g)*u */
@@ -210,7 +231,12 @@ moe_status moe_dispatch(const moe_layer_desc* desc, const int32_t* topk_ids,
  *                      (required iff n_depts > 0)
  *   shared_out[t][:] = shared expert on token t                        float [T][d]
  *                      (required iff d_ff_shared > 0)
- * The intermediates h = SiLU(gate x) * (up x) stay fp32 in `workspace`. */
+ * The intermediates h = SiLU(gate x) * (up x) are kept in act_dtype in
+ * `workspace`.
+ * Factorised form: row_out[r][:] (float [n_rows][S], row stride S) receives
+ * Z = SiLU((A_d^i)^T Y) of row r, and dept_out[q][:] the department output
+ * (W_d^j)^T (sum over the pair's rows of weight * Z), so the routing weights
+ * are applied here and moe_combine adds dept_out unscaled. */
 moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_weights* weights,
                           const void* x, int32_t T, const moe_plan* plan,
                           void* workspace, size_t ws_bytes, float* row_out,
@@ -219,7 +245,9 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_weights* weights
 /* Combine: y[t] = sum_j topk weight(t,j) * row_out[inv_perm[t*k+j]]  (slot order)
  *               + sum_J c_{t,J} * dept_out[dept_inv[t*m+J]]           (J ascending)
  *               + shared_out[t]
- * written in act_dtype (bf16: round to nearest even). */
+ * written in act_dtype (bf16: round to nearest even).  Factorised form:
+ * y[t] = sum_J dept_out[dept_inv[t*m+J]] + shared_out[t] (row_out unused, may
+ * be NULL). */
 moe_status moe_combine(const moe_layer_desc* desc, const moe_plan* plan,
                        const float* row_out, const float* dept_out,
                        const float* shared_out, int32_t T, void* y, void* stream);

@@ -23,11 +23,14 @@ __all__ = [
     "moe_expert_ffn", "moe_combine", "moe_layer_decode", "moe_status_string",
     "moe_loaded_weight_bytes", "moe_stream_read", "alloc_workspace", "plan_to_host", "MoeLayer",
     "MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE",
-    "MOE_ERR_HIP", "SCORE_FNS", "N_STAGES", "STAGE_NAMES", "EXPORTED_SYMBOLS",
+    "MOE_ERR_HIP", "SCORE_FNS", "DEPT_FORMS", "MOE_DEPT_SLICE", "MOE_DEPT_FACTORISED",
+    "N_STAGES", "STAGE_NAMES", "EXPORTED_SYMBOLS",
 ]
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
+MOE_DEPT_SLICE, MOE_DEPT_FACTORISED = 0, 1
+DEPT_FORMS = {"slice": MOE_DEPT_SLICE, "factorised": MOE_DEPT_FACTORISED}
 SCORE_FNS = {"softmax": 0, "sigmoid": 1, "softmax_bias": 2}
 PLAN_HEADER_LEN = 16
 PLAN_N_ROWS, PLAN_N_ACTIVE, PLAN_N_DEPT_ROWS, PLAN_N_ACTIVE_DEPTS, PLAN_N_INVALID = range(5)
@@ -46,7 +49,8 @@ class LayerDesc(ctypes.Structure):
     _fields_ = [("d_model", _i32), ("n_experts", _i32), ("top_k", _i32), ("d_ff", _i32),
                 ("n_depts", _i32), ("d_ff_dept", _i32), ("d_ff_shared", _i32),
                 ("score_fn", _i32), ("renormalize", _i32), ("route_scale", _f32),
-                ("w_dtype", _i32), ("act_dtype", _i32), ("max_tokens", _i32)]
+                ("w_dtype", _i32), ("act_dtype", _i32), ("max_tokens", _i32),
+                ("dept_form", _i32)]
 
     @property
     def torch_dtype(self):
@@ -60,7 +64,8 @@ class Weights(ctypes.Structure):
 
 _PLAN_ARRAYS = ("header", "counts", "offsets", "row_token", "row_slot", "row_expert",
                 "row_weight", "inv_perm", "active", "dept_counts", "dept_offsets",
-                "dept_row_token", "dept_row_dept", "dept_row_scale", "dept_inv", "active_depts")
+                "dept_row_token", "dept_row_dept", "dept_row_scale", "dept_inv", "active_depts",
+                "row_pair")
 
 
 class Plan(ctypes.Structure):
@@ -145,11 +150,11 @@ def _check(status: int, call: str):
 def layer_desc(d_model: int, n_experts: int, top_k: int, d_ff: int, *, n_depts: int = 0,
                d_ff_dept: int = 0, d_ff_shared: int = 0, score: str = "softmax",
                renormalize: bool = True, route_scale: float = 1.0, dtype: str = "bf16",
-               max_tokens: int = 32) -> LayerDesc:
+               max_tokens: int = 32, dept_form: str = "slice") -> LayerDesc:
     dt = MOE_BF16 if dtype == "bf16" else MOE_F32
     return LayerDesc(d_model, n_experts, top_k, d_ff, n_depts, d_ff_dept, d_ff_shared,
                      SCORE_FNS[score], int(bool(renormalize)), float(route_scale), dt, dt,
-                     max_tokens)
+                     max_tokens, DEPT_FORMS[dept_form])
 
 
 def moe_validate_desc(desc: LayerDesc) -> int:
@@ -217,6 +222,9 @@ def _weights_struct(desc: LayerDesc, w: Dict[str, torch.Tensor]) -> Weights:
     wdt = _wdt(desc)
     s = Weights()
     shapes = {"w_router": (E, d), "w_gate": (E, I, d), "w_up": (E, I, d), "w_down": (E, d, I)}
+    if desc.n_depts and desc.dept_form == MOE_DEPT_FACTORISED:
+        # private transforms A_g, A_u and (A_d)^T are S x S (I == S)
+        shapes.update(w_gate=(E, I, I), w_up=(E, I, I), w_down=(E, I, I))
     if desc.n_depts:
         m, S = desc.n_depts, desc.d_ff_dept
         shapes.update(wd_gate=(m, S, d), wd_up=(m, S, d), wd_down=(m, d, S))
@@ -341,6 +349,8 @@ def plan_to_host(desc: LayerDesc, plan: Plan, workspace: torch.Tensor) -> Dict[s
                    dept_row_scale=rd("dept_row_scale", nd, "f"),
                    dept_inv=rd("dept_inv", T * m, "i"),
                    active_depts=rd("active_depts", nad, "i"))
+        if desc.dept_form == MOE_DEPT_FACTORISED:
+            out["row_pair"] = rd("row_pair", n_rows, "i")
     return out
 
 

@@ -18,8 +18,12 @@ enum Region {
   R_COUNTERS, R_LOGITS, R_TOPK_IDS, R_TOPK_W, R_HEADER, R_COUNTS, R_OFFSETS, R_ROW_TOKEN,
   R_ROW_SLOT, R_ROW_EXPERT, R_ROW_WEIGHT, R_INV_PERM, R_ACTIVE, R_WORK, R_DCOUNTS, R_DOFFSETS,
   R_DROW_TOKEN, R_DROW_DEPT, R_DROW_SCALE, R_DINV, R_ACTIVE_DEPTS, R_DWORK, R_H, R_HD, R_HS,
-  R_ROW_OUT, R_DEPT_OUT, R_SHARED_OUT, R_COUNT
+  R_ROW_OUT, R_DEPT_OUT, R_SHARED_OUT, R_XG, R_XU, R_ROW_PAIR, R_COUNT
 };
+
+bool factorised(const moe_layer_desc& d) {
+  return d.n_depts > 0 && d.dept_form == MOE_DEPT_FACTORISED;
+}
 
 struct Layout {
   size_t off[R_COUNT];
@@ -78,9 +82,14 @@ Layout layout_of(const moe_layer_desc& d) {
   sz[R_H] = A * (int64_t)d.d_ff * 4;
   sz[R_HD] = Pm * (int64_t)(m ? d.d_ff_dept : 0) * 4;
   sz[R_HS] = Tm * (int64_t)d.d_ff_shared * 4;
-  sz[R_ROW_OUT] = A * (int64_t)d.d_model * 4;
+  // factorised form: row_out holds the private outputs Z, S wide
+  const int64_t row_w = factorised(d) && d.d_ff > d.d_model ? d.d_ff : d.d_model;
+  sz[R_ROW_OUT] = A * row_w * 4;
   sz[R_DEPT_OUT] = Pm * (int64_t)d.d_model * 4;
   sz[R_SHARED_OUT] = (d.d_ff_shared > 0 ? Tm : 0) * (int64_t)d.d_model * 4;
+  // factorised form: the backbone outputs sigma(W_g^j x), sigma(W_u^j x) per pair
+  sz[R_XG] = sz[R_XU] = factorised(d) ? Pm * (int64_t)d.d_ff_dept * 4 : 0;
+  sz[R_ROW_PAIR] = A * 4;
   Layout L;
   size_t o = 0;
   for (int r = 0; r < R_COUNT; ++r) {
@@ -102,9 +111,15 @@ moe_status check_desc(const moe_layer_desc* d) {
   if (d->top_k <= 0 || d->top_k > d->n_experts) return MOE_ERR_INVALID_ARG;
   if (d->d_ff <= 0 || d->d_ff % 8) return MOE_ERR_INVALID_ARG;
   if (d->n_depts < 0 || d->d_ff_shared < 0 || d->d_ff_shared % 8) return MOE_ERR_INVALID_ARG;
+  if (d->dept_form != MOE_DEPT_SLICE && d->dept_form != MOE_DEPT_FACTORISED)
+    return MOE_ERR_INVALID_ARG;
   if (d->n_depts > 0) {
     if (d->n_experts % d->n_depts) return MOE_ERR_INVALID_ARG;
     if (d->d_ff_dept <= 0 || d->d_ff_dept % 8) return MOE_ERR_INVALID_ARG;
+    // the private transforms are S x S
+    if (d->dept_form == MOE_DEPT_FACTORISED && d->d_ff != d->d_ff_dept) return MOE_ERR_INVALID_ARG;
+  } else if (d->dept_form != MOE_DEPT_SLICE) {
+    return MOE_ERR_INVALID_ARG;
   }
   if (d->score_fn < MOE_SCORE_SOFTMAX || d->score_fn > MOE_SCORE_SOFTMAX_BIAS)
     return MOE_ERR_INVALID_ARG;
@@ -168,6 +183,7 @@ void fill_plan(const moe_layer_desc& d, void* ws, int32_t T, moe_plan* p) {
   p->dept_row_scale = at<float>(ws, L, R_DROW_SCALE);
   p->dept_inv = at<int32_t>(ws, L, R_DINV);
   p->active_depts = at<int32_t>(ws, L, R_ACTIVE_DEPTS);
+  p->row_pair = at<int32_t>(ws, L, R_ROW_PAIR);
   p->n_tokens = T;
 }
 
@@ -178,6 +194,7 @@ moe::PlanArgs plan_args(const moe_layer_desc& d, void* ws, int32_t T, const moe_
   pa.E = d.n_experts;
   pa.k = d.top_k;
   pa.m = d.n_depts;
+  pa.factorised = factorised(d) ? 1 : 0;
   pa.plan = p;
   pa.work = at<WorkDesc>(ws, L, R_WORK);
   pa.dwork = at<WorkDesc>(ws, L, R_DWORK);
@@ -253,13 +270,27 @@ moe::GemvConfig choose_config(const moe_layer_desc& d, int32_t T) {
   return c;
 }
 
+// The families one expert launch carries.
+enum class Stage {
+  kAll,              // vanilla and slice form: every family in one gate/up and one down launch
+  kFactBackbone,     // factorised: department backbones sigma(W_g x), sigma(W_u x) (+ shared gate/up)
+  kFactPrivateUp,    // factorised: SiLU(A_g x_g) * (A_u x_u) per row, inputs indexed by pair
+  kFactPrivateDown,  // factorised: SiLU((A_d)^T y) per row
+  kFactDeptDown,     // factorised: (W_d^j)^T of the pair sums (+ shared down)
+};
+
 // Matrix families of a step -- routed experts (private slices in the
 // department form), department slices, the shared expert -- each split into
 // the part for groups of at most four rows and the part for larger groups.
 // A part is left out when no group of its size can occur at this T.
 FamilySet make_families(const moe_layer_desc& d, const moe_weights& w, const moe_plan& p,
-                        void* ws, int32_t T, float* row_out, float* dept_out, float* shared_out) {
+                        void* ws, int32_t T, float* row_out, float* dept_out, float* shared_out,
+                        Stage stage = Stage::kAll) {
   const Layout L = layout_of(d);
+  const bool routed = stage == Stage::kAll || stage == Stage::kFactPrivateUp ||
+                      stage == Stage::kFactPrivateDown;
+  const bool dept_shared = stage == Stage::kAll || stage == Stage::kFactBackbone ||
+                           stage == Stage::kFactDeptDown;
   FamilySet set{};
   int n = 0;
   const int tk = T * d.top_k;
@@ -268,6 +299,7 @@ FamilySet make_families(const moe_layer_desc& d, const moe_weights& w, const moe
   // large one starts n_mats descriptors in); a large group has more than
   // small_max rows, which bounds how many there can be.
   auto add_parts = [&](Family f, bool can_small, bool can_large, int hdr_small, int hdr_large) {
+    if (f.in_rows == 0) f.in_rows = T;  // inputs are x: one row per token
     if (can_small) {
       Family g = f;
       g.large = 0;
@@ -286,7 +318,8 @@ FamilySet make_families(const moe_layer_desc& d, const moe_weights& w, const moe
       if (g.max_slots > 0) set.f[n++] = g;
     }
   };
-  {
+  const int pairs_max = (int)((int64_t)T * (d.n_depts < d.top_k ? d.n_depts : d.top_k));
+  if (routed) {
     Family f{};
     f.gate = w.w_gate;
     f.up = w.w_up;
@@ -300,9 +333,17 @@ FamilySet make_families(const moe_layer_desc& d, const moe_weights& w, const moe
     f.max_slots = tk < d.n_experts ? tk : d.n_experts;
     f.n_mats = d.n_experts;
     f.max_rows = tk;
+    if (stage == Stage::kFactPrivateUp) {
+      // inputs: the backbone outputs of the row's (token, department) pair
+      f.x_gate = at<void>(ws, L, R_XG);
+      f.x_up = at<void>(ws, L, R_XU);
+      f.grp_token = p.row_pair;
+      f.in_rows = pairs_max;
+    }
+    if (stage == Stage::kFactPrivateDown) f.epi = 1;
     add_parts(f, true, T > small_max, moe::kHdrSmall, moe::kHdrLarge);
   }
-  if (d.n_depts > 0) {
+  if (d.n_depts > 0 && dept_shared) {
     Family f{};
     f.gate = w.wd_gate;
     f.up = w.wd_up;
@@ -315,10 +356,15 @@ FamilySet make_families(const moe_layer_desc& d, const moe_weights& w, const moe
     f.out = dept_out;
     f.max_slots = tk < d.n_depts ? tk : d.n_depts;
     f.n_mats = d.n_depts;
-    f.max_rows = (int)((int64_t)T * (d.n_depts < d.top_k ? d.n_depts : d.top_k));
+    f.max_rows = pairs_max;
+    if (stage == Stage::kFactBackbone) {
+      f.h = at<void>(ws, L, R_XG);
+      f.h2 = at<void>(ws, L, R_XU);
+      f.epi = 1;
+    }
     add_parts(f, true, T > small_max, moe::kHdrDeptSmall, moe::kHdrDeptLarge);
   }
-  if (d.d_ff_shared > 0) {
+  if (d.d_ff_shared > 0 && dept_shared) {
     Family f{};
     f.gate = w.ws_gate;
     f.up = w.ws_up;
@@ -365,9 +411,10 @@ moe::CombineArgs combine_args(const moe_layer_desc& d, const moe_plan& p, const 
   moe::CombineArgs a;
   a.inv_perm = p.inv_perm;
   a.row_weight = p.row_weight;
-  a.row_out = row_out;
+  // factorised form: the weights are applied before the department down
+  a.row_out = factorised(d) ? nullptr : row_out;
   a.dept_inv = p.dept_inv;
-  a.dept_scale = p.dept_row_scale;
+  a.dept_scale = factorised(d) ? nullptr : p.dept_row_scale;
   a.dept_out = dept_out;
   a.shared_out = shared_out;
   a.T = T;
@@ -380,6 +427,78 @@ moe::CombineArgs combine_args(const moe_layer_desc& d, const moe_plan& p, const 
 }
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// The grouped expert launches of one step.  Vanilla and slice form: one
+// gate/up and one down launch over every family.  Factorised form (DeaMoE
+// section 3.2): backbone gate/up (sigma(W_g^j x), sigma(W_u^j x) once per
+// (token, department)), private gate/up on those, private down with SiLU,
+// the weighted pair sums, department down.  ev_gu / ev_dn (may be null)
+// bracket the gate/up and the down launches.
+moe_status run_experts(const moe_layer_desc& d, const moe_weights& w, const void* x, int32_t T,
+                       const moe_plan& p, void* ws, float* row_out, float* dept_out,
+                       float* shared_out, hipStream_t st, const moe::KernelEvents* ev_gu,
+                       const moe::KernelEvents* ev_dn) {
+  const moe::GemvConfig cfg = choose_config(d, T);
+  const int dm = d.d_model;
+  if (!factorised(d)) {
+    FamilySet set = make_families(d, w, p, ws, T, row_out, dept_out, shared_out);
+    set_tiles(set, dm, true, cfg);
+    if (moe::launch_gateup(d.w_dtype, set, x, T, dm, cfg.rows_per_wave, cfg.rows_per_pass, st,
+                           ev_gu) != hipSuccess)
+      return MOE_ERR_HIP;
+    set_tiles(set, dm, false, cfg);
+    return hip_status(
+        moe::launch_down(d.w_dtype, set, T, dm, cfg.lpr, cfg.col_groups, st, ev_dn));
+  }
+  const Layout L = layout_of(d);
+  const int S = d.d_ff_dept;
+  moe::KernelEvents gu0{}, gu1{}, dn0{}, dn1{};
+  if (ev_gu) {
+    gu0.start = ev_gu->start;
+    gu1.stop = ev_gu->stop;
+  }
+  if (ev_dn) {
+    dn0.start = ev_dn->start;
+    dn1.stop = ev_dn->stop;
+  }
+  FamilySet a = make_families(d, w, p, ws, T, row_out, dept_out, shared_out, Stage::kFactBackbone);
+  set_tiles(a, dm, true, cfg);
+  if (moe::launch_gateup(d.w_dtype, a, x, T, dm, cfg.rows_per_wave, cfg.rows_per_pass, st,
+                         ev_gu ? &gu0 : nullptr) != hipSuccess)
+    return MOE_ERR_HIP;
+  FamilySet b = make_families(d, w, p, ws, T, row_out, dept_out, shared_out, Stage::kFactPrivateUp);
+  set_tiles(b, S, true, cfg);
+  if (moe::launch_gateup(d.w_dtype, b, x, T, S, cfg.rows_per_wave, cfg.rows_per_pass, st,
+                         ev_gu ? &gu1 : nullptr) != hipSuccess)
+    return MOE_ERR_HIP;
+  FamilySet c =
+      make_families(d, w, p, ws, T, row_out, dept_out, shared_out, Stage::kFactPrivateDown);
+  set_tiles(c, S, false, cfg);
+  if (moe::launch_down(d.w_dtype, c, T, S, cfg.lpr, cfg.col_groups, st, ev_dn ? &dn0 : nullptr) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+  moe::PairCombineArgs pc;
+  pc.n_pairs = p.header + MOE_PLAN_N_DEPT_ROWS;
+  pc.pair_token = p.dept_row_token;
+  pc.pair_dept = p.dept_row_dept;
+  pc.inv_perm = p.inv_perm;
+  pc.row_expert = p.row_expert;
+  pc.row_weight = p.row_weight;
+  pc.z = row_out;
+  pc.T = T;
+  pc.k = d.top_k;
+  pc.group = d.n_experts / d.n_depts;
+  pc.cols = S;
+  pc.max_rows = T * d.top_k;
+  const int pairs_max = T * (d.n_depts < d.top_k ? d.n_depts : d.top_k);
+  if (moe::launch_pair_combine(d.act_dtype, pc, at<void>(ws, L, R_HD), pairs_max, st) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+  FamilySet e = make_families(d, w, p, ws, T, row_out, dept_out, shared_out, Stage::kFactDeptDown);
+  set_tiles(e, dm, false, cfg);
+  return hip_status(moe::launch_down(d.w_dtype, e, T, dm, cfg.lpr, cfg.col_groups, st,
+                                     ev_dn ? &dn1 : nullptr));
+}
 
 }  // namespace
 
@@ -472,17 +591,8 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_weights* weights
     return MOE_ERR_INVALID_ARG;
   if ((s = check_ws(desc, workspace, ws_bytes)) != MOE_OK) return s;
   if ((s = plan_matches(*desc, workspace, plan, T)) != MOE_OK) return s;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const moe::GemvConfig cfg = choose_config(*desc, T);
-  FamilySet set = make_families(*desc, *weights, *plan, workspace, T, row_out, dept_out,
-                                shared_out);
-  set_tiles(set, desc->d_model, true, cfg);
-  if (moe::launch_gateup(desc->w_dtype, set, x, T, desc->d_model, cfg.rows_per_wave,
-                         cfg.rows_per_pass, st, nullptr) != hipSuccess)
-    return MOE_ERR_HIP;
-  set_tiles(set, desc->d_model, false, cfg);
-  return hip_status(moe::launch_down(desc->w_dtype, set, T, desc->d_model, cfg.lpr,
-                                     cfg.col_groups, st, nullptr));
+  return run_experts(*desc, *weights, x, T, *plan, workspace, row_out, dept_out, shared_out,
+                     static_cast<hipStream_t>(stream), nullptr, nullptr);
 }
 
 moe_status moe_combine(const moe_layer_desc* desc, const moe_plan* plan, const float* row_out,
@@ -494,7 +604,8 @@ moe_status moe_combine(const moe_layer_desc* desc, const moe_plan* plan, const f
   if (T == 0) return MOE_OK;
   if (!plan || plan->n_tokens != T || !plan->inv_perm || !plan->row_weight)
     return MOE_ERR_INVALID_ARG;
-  if (!ok_ptr(row_out) || !ok_ptr(y) || !ok_opt(dept_out) || !ok_opt(shared_out))
+  if (!(factorised(*desc) ? ok_opt(row_out) : ok_ptr(row_out)) || !ok_ptr(y) ||
+      !ok_opt(dept_out) || !ok_opt(shared_out))
     return MOE_ERR_INVALID_ARG;
   if (desc->n_depts > 0 ? !ok_ptr(dept_out) : dept_out != nullptr) return MOE_ERR_INVALID_ARG;
   if (desc->d_ff_shared > 0 ? !ok_ptr(shared_out) : shared_out != nullptr)
@@ -532,7 +643,6 @@ moe_status moe_layer_decode(const moe_layer_desc* desc, const moe_weights* weigh
   float* row_out = at<float>(workspace, L, R_ROW_OUT);
   float* dept_out = desc->n_depts > 0 ? at<float>(workspace, L, R_DEPT_OUT) : nullptr;
   float* shared_out = desc->d_ff_shared > 0 ? at<float>(workspace, L, R_SHARED_OUT) : nullptr;
-  const moe::GemvConfig cfg = choose_config(*desc, T);
 
   // router logits, then top-k + dispatch plan
   const moe::RouteArgs ra =
@@ -542,19 +652,10 @@ moe_status moe_layer_decode(const moe_layer_desc* desc, const moe_weights* weigh
   if (moe::launch_route(desc->w_dtype, ra, &pa, st, evp(MOE_STAGE_ROUTE)) != hipSuccess)
     return MOE_ERR_HIP;
 
-  // grouped gate/up with SiLU(g) * u
-  FamilySet set = make_families(*desc, *weights, plan, workspace, T, row_out, dept_out,
-                                shared_out);
-  set_tiles(set, desc->d_model, true, cfg);
-  if (moe::launch_gateup(desc->w_dtype, set, x, T, desc->d_model, cfg.rows_per_wave,
-                         cfg.rows_per_pass, st, evp(MOE_STAGE_GATEUP)) != hipSuccess)
-    return MOE_ERR_HIP;
-
-  // grouped down, then the combine back to token order
-  set_tiles(set, desc->d_model, false, cfg);
-  if (moe::launch_down(desc->w_dtype, set, T, desc->d_model, cfg.lpr, cfg.col_groups, st,
-                       evp(MOE_STAGE_DOWN)) != hipSuccess)
-    return MOE_ERR_HIP;
+  // grouped expert FFN, then the combine back to token order
+  if ((s = run_experts(*desc, *weights, x, T, plan, workspace, row_out, dept_out, shared_out, st,
+                       evp(MOE_STAGE_GATEUP), evp(MOE_STAGE_DOWN))) != MOE_OK)
+    return s;
   const moe::CombineArgs ca = combine_args(*desc, plan, row_out, dept_out, shared_out, T);
   if (moe::launch_combine(desc->act_dtype, ca, y, st, evp(MOE_STAGE_COMBINE)) != hipSuccess)
     return MOE_ERR_HIP;
@@ -578,7 +679,11 @@ uint64_t moe_loaded_weight_bytes(const moe_layer_desc* desc, int32_t n_active,
   const uint64_t wb = desc->w_dtype == MOE_BF16 ? 2 : 4;
   const uint64_t d = desc->d_model;
   uint64_t n = (uint64_t)desc->n_experts * d;
-  n += (uint64_t)n_active * 3 * d * desc->d_ff;
+  // factorised form: each private transform is S x S (d_ff == d_ff_dept)
+  n += (uint64_t)n_active * 3 * (desc->n_depts > 0 && desc->dept_form == MOE_DEPT_FACTORISED
+                                     ? (uint64_t)desc->d_ff
+                                     : d) *
+       desc->d_ff;
   n += (uint64_t)desc->d_ff_shared * 3 * d;
   if (desc->n_depts > 0) n += (uint64_t)n_active_depts * 3 * d * desc->d_ff_dept;
   return n * wb;

@@ -38,6 +38,7 @@ struct WorkDesc {
 // Everything the routing + dispatch phase reads and writes.
 struct PlanArgs {
   int T, E, k, m;
+  int factorised;          // 1: also write plan.row_pair and pair-indexed inline rows
   moe_plan plan;
   WorkDesc* work;          // [2E] active experts: small groups from 0, large groups from E
   WorkDesc* dwork;         // [2m] the same for departments
@@ -70,8 +71,14 @@ struct Family {
   const WorkDesc* work;    // per active slot; nullptr: the shared expert (all T tokens)
   const int* n_active;     // device count of active slots (nullptr: 1)
   const int* grp_token;    // token of each row (nullptr: row r is token r)
-  void* h;                 // [rows_total][rows] SiLU(g) * u, in the layer's dtype
+  void* h;                 // [rows_total][rows] gate/up output in the layer's dtype (see epi)
+  void* h2;                // [rows_total][rows] second gate/up output (epi 1), else nullptr
   float* out;              // [rows_total][d]    unweighted down output
+  const void* x_gate;      // gate/up inputs [in_rows][d]; nullptr: the launch's x for both
+  const void* x_up;        //   (the factorised form's private transforms read two matrices)
+  int in_rows;             // rows the gate/up inputs hold (row indices are clamped to it)
+  int epi;                 // gate/up: 0 h = SiLU(g)*u, 1 h = SiLU(g) and h2 = SiLU(u);
+                           // down: 0 out = W h, 1 out = SiLU(W h)
   int max_slots;           // host bound on the slots this part can serve
   int tiles;               // blocks per slot in the current launch
   int n_mats;              // matrices in the family (bounds check of work descriptors)
@@ -88,14 +95,28 @@ struct FamilySet {
 struct CombineArgs {
   const int32_t* inv_perm;
   const float* row_weight;
-  const float* row_out;
+  const float* row_out;    // nullptr: no per-row term (factorised form)
   const int32_t* dept_inv;
-  const float* dept_scale;
+  const float* dept_scale; // nullptr: department outputs are added unscaled
   const float* dept_out;   // nullptr when no department term
   const float* shared_out; // nullptr when no shared expert
   int T, k, m, d;
   int max_rows;            // rows of row_out (plan entries at or past it are skipped)
   int max_dept_rows;       // rows of dept_out
+};
+
+// Factorised form: weighted sum of a (token, department) pair's private
+// outputs, the input of the department down projection.
+struct PairCombineArgs {
+  const int32_t* n_pairs;    // device count of pairs (plan header)
+  const int32_t* pair_token; // [pairs]
+  const int32_t* pair_dept;  // [pairs]
+  const int32_t* inv_perm;   // [T*k]
+  const int32_t* row_expert; // [rows]
+  const float* row_weight;   // [rows]
+  const float* z;            // [rows][cols] private outputs
+  int T, k, group, cols;     // group = experts per department
+  int max_rows;
 };
 
 struct GemvConfig {
@@ -126,5 +147,7 @@ hipError_t launch_combine(int act_dtype, const CombineArgs& a, void* y, hipStrea
                           const KernelEvents* ev);
 hipError_t launch_zero(unsigned int* p, size_t n, hipStream_t st);
 hipError_t launch_stream_read(const void* src, size_t blocks, float* sink, hipStream_t st);
+hipError_t launch_pair_combine(int act_dtype, const PairCombineArgs& a, void* zc, int max_pairs,
+                               hipStream_t st);
 
 }  // namespace moe

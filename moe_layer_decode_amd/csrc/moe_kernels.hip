@@ -159,6 +159,8 @@ struct PlanShared {
   int cnt[MOE_MAX_EXPERTS];
   int off[MOE_MAX_EXPERTS + 1];
   int slot[MOE_MAX_EXPERTS];
+  int eslot[MOE_MAX_EXPERTS];             // expert's slot, kept past the department pass
+  short arank[MOE_MAX_ASSIGNMENTS];       // assignment's rank inside its expert group
   unsigned char flag[MOE_MAX_DEPT_PAIRS];
   int invalid;
 };
@@ -388,6 +390,7 @@ __device__ void plan_phase(PlanShared& s, const PlanArgs& pa) {
       P.row_expert[row] = e;
       P.row_weight[row] = s.w[a];
       P.inv_perm[a] = row;
+      s.arank[a] = (short)rank;
       if (s.cnt[e] <= kTokInline) pa.work[s.slot[e]].tok[rank] = t;
     } else {
       P.inv_perm[a] = -1;
@@ -396,6 +399,7 @@ __device__ void plan_phase(PlanShared& s, const PlanArgs& pa) {
   for (int e = tid; e < E; e += nth) {
     const int c = s.cnt[e];
     P.counts[e] = c;
+    s.eslot[e] = s.slot[e];
     if (c > 0) {
       WorkDesc* wd = work_of(pa.work, E, c, s.slot[e]);
       wd->mat = e;
@@ -465,6 +469,19 @@ __device__ void plan_phase(PlanShared& s, const PlanArgs& pa) {
       wd->mat = J;
       wd->r0 = s.off[J];
       wd->n = c;
+    }
+  }
+  if (!pa.factorised) return;
+  // Factorised form: a routed row reads its (token, department) pair's
+  // backbone outputs, so the row's input index is the pair, in row_pair and
+  // in the inline entries of its small group.
+  __syncthreads();
+  for (int a = tid; a < A; a += nth) {
+    const int e = s.ids[a];
+    if (e >= 0 && e < E) {
+      const int t = a / k, q = P.dept_inv[t * m + e / G];
+      P.row_pair[P.inv_perm[a]] = q;
+      if (P.counts[e] <= kTokInline) pa.work[s.eslot[e]].tok[s.arank[a]] = q;
     }
   }
 }
@@ -705,11 +722,37 @@ __device__ __forceinline__ bool map_slot(const Family& F, int T, Slot& sl, int& 
   return F.large ? sl.n > kTokInline : sl.n <= kTokInline;
 }
 
-// Token of row tc + t of the group; t is a compile-time constant at every call
-// site, so the inline case folds to one register.  Rows at or past the end of
-// the group are never dereferenced and map to token 0.
+// Where a part's gate/up results go.  epi 0: h = SiLU(g) * u (the SwiGLU
+// intermediate).  epi 1: h = sigma(g), h2 = sigma(u) with sigma = SiLU (the
+// department backbone outputs of the factorised form, DeaMoE section 3.2).
+template <typename T_>
+struct GuOut {
+  T_* h;
+  T_* h2;
+  int epi;
+};
+template <typename T_>
+__device__ __forceinline__ void gu_store(const GuOut<T_>& o, size_t idx, float g, float u) {
+  if (o.epi) {
+    store_act(o.h + idx, silu(g));
+    store_act(o.h2 + idx, silu(u));
+  } else {
+    store_act(o.h + idx, silu(g) * u);
+  }
+}
+// Down results: epi 0 stores the product, epi 1 its SiLU (the private down
+// transform sigma((A_d)^T v) of the factorised form).
+__device__ __forceinline__ void dn_store(float* out, size_t idx, float v, int epi) {
+  out[idx] = epi ? silu(v) : v;
+}
+
+// Input row of row tc + t of the group (a token, or in the factorised form a
+// (token, department) pair); t is a compile-time constant at every call site,
+// so the inline case folds to one register.  Rows at or past the end of the
+// group are never dereferenced and map to row 0; every index is clamped to
+// the in_rows rows the input holds.
 __device__ __forceinline__ int slot_token(const Slot& sl, const int* grp_token, int tc, int t,
-                                          int nv, int T) {
+                                          int nv, int in_rows) {
   int tok;
   if (sl.inline_tok)
     tok = t == 0 ? sl.t0 : t == 1 ? sl.t1 : t == 2 ? sl.t2 : sl.t3;
@@ -717,28 +760,29 @@ __device__ __forceinline__ int slot_token(const Slot& sl, const int* grp_token, 
     tok = 0;
   else
     tok = grp_token ? grp_token[sl.r0 + tc + t] : tc + t;
-  return min(max(tok, 0), T - 1);
+  return min(max(tok, 0), in_rows - 1);
 }
 
-// Token of row t of a large group (per lane; t < n).
-__device__ __forceinline__ int lane_token(const Slot& sl, const int* grp_token, int t, int T) {
+// Input row of row t of a large group (per lane; t < n).
+__device__ __forceinline__ int lane_token(const Slot& sl, const int* grp_token, int t,
+                                          int in_rows) {
   const int tok = grp_token ? grp_token[sl.r0 + t] : t;
-  return min(max(tok, 0), T - 1);
+  return min(max(tok, 0), in_rows - 1);
 }
 
 // ---- small groups: register GEMV -------------------------------------------
 
-// RW rows of gate and up from row i0 against the (at most four) tokens of the
-// group.  h[row][i] = SiLU(g) * u.  Every load of step c+1 (weights and
-// activations) is issued before step c is used: the vector-memory counter
-// completes loads in order, so nothing requested after the next step's loads
-// may be needed first.
-template <typename T_, int RW>
+// RW rows of gate and up from row i0 against the (at most four) input rows of
+// the group (gate reads x, up reads xu: the same rows except in the two-input
+// form).  Every load of step c+1 (weights and activations) is issued before
+// step c is used: the vector-memory counter completes loads in order, so
+// nothing requested after the next step's loads may be needed first.
+template <typename T_, int RW, bool DUAL>
 __device__ __forceinline__ void gu_small(const T_* __restrict__ Wg, const T_* __restrict__ Wu,
                                          int d, int rows, int i0, const T_* __restrict__ x,
-                                         int T, const Slot& sl, const int* grp_token,
-                                         T_* __restrict__ h, int lane) {
-  constexpr int NT = kTokInline;
+                                         const T_* __restrict__ xu, int in_rows, const Slot& sl,
+                                         const int* grp_token, const GuOut<T_>& o, int lane) {
+  constexpr int NT = kTokInline, NX = DUAL ? 2 : 1;
   const int nv = sl.n;
   const T_* gp[RW];
   const T_* up[RW];
@@ -748,9 +792,13 @@ __device__ __forceinline__ void gu_small(const T_* __restrict__ Wg, const T_* __
     gp[r] = Wg + i * d;
     up[r] = Wu + i * d;
   }
-  const T_* xp[NT];
+  const T_* xp[NX][NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) xp[t] = x + (size_t)slot_token(sl, grp_token, 0, t, nv, T) * d;
+  for (int t = 0; t < NT; ++t) {
+    const size_t row = (size_t)slot_token(sl, grp_token, 0, t, nv, in_rows) * d;
+    xp[0][t] = x + row;
+    if constexpr (DUAL) xp[NX - 1][t] = xu + row;
+  }
   float ag[RW][NT], au[RW][NT];
 #pragma unroll
   for (int r = 0; r < RW; ++r)
@@ -759,7 +807,7 @@ __device__ __forceinline__ void gu_small(const T_* __restrict__ Wg, const T_* __
 
   int c = lane * 8;
   Raw8<T_> cg[RW], cu[RW];
-  X8<T_> cx[NT];
+  X8<T_> cx[NX][NT];
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     if (c < d) {
@@ -771,16 +819,18 @@ __device__ __forceinline__ void gu_small(const T_* __restrict__ Wg, const T_* __
     }
   }
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    if (t < nv && c < d)
-      cx[t].load(xp[t] + c);
-    else
-      cx[t].zero();
-  }
+  for (int v = 0; v < NX; ++v)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t < nv && c < d)
+        cx[v][t].load(xp[v][t] + c);
+      else
+        cx[v][t].zero();
+    }
   for (; c < d; c += 8 * kWave) {
     const int cn = c + 8 * kWave;
     Raw8<T_> ng[RW], nu[RW];
-    X8<T_> nx[NT];
+    X8<T_> nx[NX][NT];
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
       if (cn < d) {
@@ -792,19 +842,21 @@ __device__ __forceinline__ void gu_small(const T_* __restrict__ Wg, const T_* __
       }
     }
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if (t < nv && cn < d)
-        nx[t].load(xp[t] + cn);
-      else
-        nx[t].zero();
-    }
+    for (int v = 0; v < NX; ++v)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if (t < nv && cn < d)
+          nx[v][t].load(xp[v][t] + cn);
+        else
+          nx[v][t].zero();
+      }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       if (t < nv) {
 #pragma unroll
         for (int r = 0; r < RW; ++r) {
-          ag[r][t] = dot8(cg[r], cx[t], ag[r][t]);
-          au[r][t] = dot8(cu[r], cx[t], au[r][t]);
+          ag[r][t] = dot8(cg[r], cx[0][t], ag[r][t]);
+          au[r][t] = dot8(cu[r], cx[NX - 1][t], au[r][t]);
         }
       }
     }
@@ -814,7 +866,9 @@ __device__ __forceinline__ void gu_small(const T_* __restrict__ Wg, const T_* __
       cu[r] = nu[r];
     }
 #pragma unroll
-    for (int t = 0; t < NT; ++t) cx[t] = nx[t];
+    for (int v = 0; v < NX; ++v)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) cx[v][t] = nx[v][t];
   }
   constexpr int N = 2 * RW * NT;
   float v[N];
@@ -832,7 +886,7 @@ __device__ __forceinline__ void gu_small(const T_* __restrict__ Wg, const T_* __
   const int idx = lane >> SH;
   if (idx < N / 2 && (lane & ((1 << SH) - 1)) == 0) {
     const int r = idx / NT, t = idx - (idx / NT) * NT;
-    if (t < nv && i0 + r < rows) store_act(h + (size_t)(sl.r0 + t) * rows + i0 + r, silu(v[0]) * upv);
+    if (t < nv && i0 + r < rows) gu_store(o, (size_t)(sl.r0 + t) * rows + i0 + r, v[0], upv);
   }
 }
 
@@ -842,7 +896,7 @@ __device__ __forceinline__ void gu_small(const T_* __restrict__ Wg, const T_* __
 template <typename T_, int LPR, int CG>
 __device__ __forceinline__ void dn_small(const T_* __restrict__ Wd, int d, int rows, int cb,
                                          const T_* __restrict__ h, const Slot& sl,
-                                         float* __restrict__ out, int lane) {
+                                         float* __restrict__ out, int epi, int lane) {
   constexpr int NT = kTokInline;
   constexpr int G = 64 / LPR;
   const int g = lane / LPR, j = lane - g * LPR;
@@ -917,7 +971,7 @@ __device__ __forceinline__ void dn_small(const T_* __restrict__ Wd, int d, int r
       const int idx = j * PER + p;
       const int q = idx / NT, t = idx - (idx / NT) * NT;
       const int c = cb + q * G + g;
-      if (t < nv && c < d) out[(size_t)(sl.r0 + t) * d + c] = v[p];
+      if (t < nv && c < d) dn_store(out, (size_t)(sl.r0 + t) * d + c, v[p], epi);
     }
   } else {
     constexpr int SPAN = LPR / N;
@@ -925,7 +979,7 @@ __device__ __forceinline__ void dn_small(const T_* __restrict__ Wd, int d, int r
       const int idx = j / SPAN;
       const int q = idx / NT, t = idx - (idx / NT) * NT;
       const int c = cb + q * G + g;
-      if (t < nv && c < d) out[(size_t)(sl.r0 + t) * d + c] = v[0];
+      if (t < nv && c < d) dn_store(out, (size_t)(sl.r0 + t) * d + c, v[0], epi);
     }
   }
 }
@@ -941,22 +995,22 @@ __device__ __forceinline__ void dn_small(const T_* __restrict__ Wd, int d, int r
 
 constexpr int kXLds = 2048;  // longest activation row staged (elements)
 
-template <typename T_>
+template <typename T_, int ROWS = kTokInline>
 struct SmallLds {
-  T_ x[kTokInline][kXLds];
+  T_ x[ROWS][kXLds];
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Block-wide: rows t < nv of `cols` elements, row t read from src(t), into
-// lds.x[t], by direct global-to-LDS loads (each wave instruction moves 1 KB:
-// lane l's 16 bytes land 16*l bytes past the wave-uniform destination), so
-// the copy takes no registers.  cols is a multiple of 16 bytes' worth of
-// elements and at most kXLds.  Waits for every load this wave has issued
-// (the weight prefetch included), then for the whole block.
-template <typename T_, typename Src>
-__device__ __forceinline__ void stage_rows(SmallLds<T_>& lds, int nv, int cols, Src src, int wid,
-                                           int lane) {
+// lds.x[row0 + t], by direct global-to-LDS loads (each wave instruction moves
+// 1 KB: lane l's 16 bytes land 16*l bytes past the wave-uniform destination),
+// so the copy takes no registers.  cols is a multiple of 16 bytes' worth of
+// elements and at most kXLds.  Only issues the loads: stage_wait() completes
+// them for the whole block.
+template <typename T_, int ROWS, typename Src>
+__device__ __forceinline__ void stage_rows(SmallLds<T_, ROWS>& lds, int row0, int nv, int cols,
+                                           Src src, int wid, int lane) {
   constexpr int EPL = 16 / sizeof(T_);     // elements per lane
   constexpr int EPI = EPL * kWave;         // elements per wave instruction
   const int per_row = (cols + EPI - 1) / EPI, total = nv * per_row;
@@ -964,8 +1018,13 @@ __device__ __forceinline__ void stage_rows(SmallLds<T_>& lds, int nv, int cols, 
     const int t = q / per_row, c0 = (q - t * per_row) * EPI;
     const int c = c0 + lane * EPL;
     if (c < cols)
-      __builtin_amdgcn_global_load_lds(src(t) + c, (lds_void_t*)&lds.x[t][c0], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src(t) + c, (lds_void_t*)&lds.x[row0 + t][c0], 16, 0, 0);
   }
+}
+
+// Waits for every load this wave has issued (the weight prefetch included),
+// then for the whole block, so every staged row is in LDS.
+__device__ __forceinline__ void stage_wait() {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 }
@@ -977,13 +1036,15 @@ constexpr int kStageRing = 4;  // weight steps requested before the staging barr
 // are all in flight through the barrier; after it, each consumed step's slot
 // is refilled kStageRing steps ahead.  Same per-lane column order and
 // reduction as gu_small.
-template <typename T_>
+template <typename T_, bool DUAL>
 __device__ __forceinline__ void gu_small_lds(const T_* __restrict__ Wg, const T_* __restrict__ Wu,
                                              int d, int rows, int i0, const T_* __restrict__ x,
-                                             int T, const Slot& sl, const int* grp_token,
-                                             T_* __restrict__ h, int lane, int wid,
-                                             SmallLds<T_>& lds) {
+                                             const T_* __restrict__ xu, int in_rows,
+                                             const Slot& sl, const int* grp_token,
+                                             const GuOut<T_>& o, int lane, int wid,
+                                             SmallLds<T_, DUAL ? 2 * kTokInline : kTokInline>& lds) {
   constexpr int NT = kTokInline, R = kStageRing, STEP = 8 * kWave;
+  constexpr int UROW = DUAL ? NT : 0;  // LDS row of the up input of row t: UROW + t
   const int nv = sl.n;
   const size_t i = (size_t)min(i0, rows - 1);
   const T_* gp = Wg + i * d + lane * 8;
@@ -1000,9 +1061,14 @@ __device__ __forceinline__ void gu_small_lds(const T_* __restrict__ Wg, const T_
       ru[r].zero();
     }
   }
-  stage_rows(lds, nv, d, [&](int t) {
-    return x + (size_t)slot_token(sl, grp_token, 0, t, nv, T) * d;
+  stage_rows(lds, 0, nv, d, [&](int t) {
+    return x + (size_t)slot_token(sl, grp_token, 0, t, nv, in_rows) * d;
   }, wid, lane);
+  if constexpr (DUAL)
+    stage_rows(lds, UROW, nv, d, [&](int t) {
+      return xu + (size_t)slot_token(sl, grp_token, 0, t, nv, in_rows) * d;
+    }, wid, lane);
+  stage_wait();
   float ag[NT], au[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) ag[t] = au[t] = 0.f;
@@ -1016,7 +1082,12 @@ __device__ __forceinline__ void gu_small_lds(const T_* __restrict__ Wg, const T_
           if (t < nv) {
             const X8<T_> xv = *reinterpret_cast<const X8<T_>*>(&lds.x[t][lane * 8 + c]);
             ag[t] = dot8(rg[r], xv, ag[t]);
-            au[t] = dot8(ru[r], xv, au[t]);
+            if constexpr (DUAL) {
+              const X8<T_> xw = *reinterpret_cast<const X8<T_>*>(&lds.x[UROW + t][lane * 8 + c]);
+              au[t] = dot8(ru[r], xw, au[t]);
+            } else {
+              au[t] = dot8(ru[r], xv, au[t]);
+            }
           }
         }
         if (c + R * STEP < dl) {
@@ -1039,7 +1110,7 @@ __device__ __forceinline__ void gu_small_lds(const T_* __restrict__ Wg, const T_
   constexpr int SH = 6 - Log2<N>::value;
   const int t = lane >> SH;
   if (t < NT && (lane & ((1 << SH) - 1)) == 0 && t < nv && i0 < rows)
-    store_act(h + (size_t)(sl.r0 + t) * rows + i0, silu(v[0]) * upv);
+    gu_store(o, (size_t)(sl.r0 + t) * rows + i0, v[0], upv);
 }
 
 // Down columns as dn_small, the group's rows of h staged in LDS; weights
@@ -1047,7 +1118,7 @@ __device__ __forceinline__ void gu_small_lds(const T_* __restrict__ Wg, const T_
 template <typename T_, int LPR, int CG>
 __device__ __forceinline__ void dn_small_lds(const T_* __restrict__ Wd, int d, int rows, int cb,
                                              const T_* __restrict__ h, const Slot& sl,
-                                             float* __restrict__ out, int lane, int wid,
+                                             float* __restrict__ out, int epi, int lane, int wid,
                                              SmallLds<T_>& lds) {
   constexpr int NT = kTokInline, R = kStageRing, STEP = 8 * LPR;
   constexpr int G = 64 / LPR;
@@ -1067,7 +1138,8 @@ __device__ __forceinline__ void dn_small_lds(const T_* __restrict__ Wd, int d, i
       else
         rw[r][q].zero();
     }
-  stage_rows(lds, nv, rows, [&](int t) { return h + (size_t)(sl.r0 + t) * rows; }, wid, lane);
+  stage_rows(lds, 0, nv, rows, [&](int t) { return h + (size_t)(sl.r0 + t) * rows; }, wid, lane);
+  stage_wait();
   float acc[CG][NT];
 #pragma unroll
   for (int q = 0; q < CG; ++q)
@@ -1106,7 +1178,7 @@ __device__ __forceinline__ void dn_small_lds(const T_* __restrict__ Wd, int d, i
       const int idx = j * PER + p;
       const int q = idx / NT, t = idx - (idx / NT) * NT;
       const int c = cb + q * G + g;
-      if (t < nv && c < d) out[(size_t)(sl.r0 + t) * d + c] = v[p];
+      if (t < nv && c < d) dn_store(out, (size_t)(sl.r0 + t) * d + c, v[p], epi);
     }
   } else {
     constexpr int SPAN = LPR / N;
@@ -1114,7 +1186,7 @@ __device__ __forceinline__ void dn_small_lds(const T_* __restrict__ Wd, int d, i
       const int idx = j / SPAN;
       const int q = idx / NT, t = idx - (idx / NT) * NT;
       const int c = cb + q * G + g;
-      if (t < nv && c < d) out[(size_t)(sl.r0 + t) * d + c] = v[0];
+      if (t < nv && c < d) dn_store(out, (size_t)(sl.r0 + t) * d + c, v[0], epi);
     }
   }
 }
@@ -1146,11 +1218,13 @@ struct MfmaLds {
 };
 
 // 16 rows (i0..) of gate and up against 16*NC tokens (rows tc.. of the group).
-template <int NC>
+template <int NC, bool DUAL>
 __device__ void gu_mfma(const bf16_t* __restrict__ Wg, const bf16_t* __restrict__ Wu, int d,
-                        int rows, int i0, const bf16_t* __restrict__ x, int T, const Slot& sl,
-                        const int* grp_token, int tc, bf16_t* __restrict__ h, int lane, int wid,
+                        int rows, int i0, const bf16_t* __restrict__ x,
+                        const bf16_t* __restrict__ xu, int in_rows, const Slot& sl,
+                        const int* grp_token, int tc, const GuOut<bf16_t>& o, int lane, int wid,
                         MfmaLds& lds) {
+  constexpr int NX = DUAL ? 2 : 1;   // activation inputs: gate's, and up's when they differ
   // two token chunks hold twice the activations: one step ahead keeps them in registers
   constexpr int kAhead = NC > 1 ? 1 : kMfmaAhead;
   const int r16 = lane & 15, g = lane >> 4;
@@ -1159,20 +1233,22 @@ __device__ void gu_mfma(const bf16_t* __restrict__ Wg, const bf16_t* __restrict_
   const size_t row = (size_t)min(i0 + r16, rows - 1);
   const bf16_t* ap = Wg + row * d + g * 8;
   const bf16_t* bp = Wu + row * d + g * 8;
-  const bf16_t* xp[NC];
+  const bf16_t* xp[NX][NC];
   bool xv[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int t = tc + c * 16 + r16;
     xv[c] = t < sl.n;
-    xp[c] = x + (size_t)(xv[c] ? lane_token(sl, grp_token, t, T) : 0) * d + g * 8;
+    const size_t row = (size_t)(xv[c] ? lane_token(sl, grp_token, t, in_rows) : 0) * d + g * 8;
+    xp[0][c] = x + row;
+    if constexpr (DUAL) xp[NX - 1][c] = xu + row;
   }
   f32x4_t accg[NC], accu[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) accg[c] = accu[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const u32x4_t z = {0, 0, 0, 0};
   // ring of kAhead + 1 steps in registers
-  u32x4_t ra[kAhead + 1], rb[kAhead + 1], rx[kAhead + 1][NC];
+  u32x4_t ra[kAhead + 1], rb[kAhead + 1], rx[kAhead + 1][NX][NC];
 #pragma unroll
   for (int s = 0; s <= kAhead; ++s) {
     const int k = kb + s * 32;
@@ -1181,7 +1257,9 @@ __device__ void gu_mfma(const bf16_t* __restrict__ Wg, const bf16_t* __restrict_
       ra[s] = in ? ld16_stream(ap + k) : z;
       rb[s] = in ? ld16_stream(bp + k) : z;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) rx[s][c] = (xv[c] && in) ? ld16(xp[c] + k) : z;
+      for (int v = 0; v < NX; ++v)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) rx[s][v][c] = (xv[c] && in) ? ld16(xp[v][c] + k) : z;
     }
   }
   for (int k = kb; k < ke; k += 32 * (kAhead + 1)) {
@@ -1194,12 +1272,14 @@ __device__ void gu_mfma(const bf16_t* __restrict__ Wg, const bf16_t* __restrict_
       ra[sn] = nin ? ld16_stream(ap + kn) : z;
       rb[sn] = nin ? ld16_stream(bp + kn) : z;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) rx[sn][c] = (xv[c] && nin) ? ld16(xp[c] + kn) : z;
+      for (int v = 0; v < NX; ++v)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) rx[sn][v][c] = (xv[c] && nin) ? ld16(xp[v][c] + kn) : z;
       if (k + s * 32 < ke) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          accg[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra[s]), as_bf16x8(rx[s][c]), accg[c], 0, 0, 0);
-          accu[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rb[s]), as_bf16x8(rx[s][c]), accu[c], 0, 0, 0);
+          accg[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra[s]), as_bf16x8(rx[s][0][c]), accg[c], 0, 0, 0);
+          accu[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rb[s]), as_bf16x8(rx[s][NX - 1][c]), accu[c], 0, 0, 0);
         }
       }
     }
@@ -1224,7 +1304,7 @@ __device__ void gu_mfma(const bf16_t* __restrict__ Wg, const bf16_t* __restrict_
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int rr = i0 + 4 * g + i;
-          if (rr < rows) store_act(h + (size_t)(sl.r0 + t) * rows + rr, silu(sg[i]) * su[i]);
+          if (rr < rows) gu_store(o, (size_t)(sl.r0 + t) * rows + rr, sg[i], su[i]);
         }
       }
     }
@@ -1236,7 +1316,7 @@ __device__ void gu_mfma(const bf16_t* __restrict__ Wg, const bf16_t* __restrict_
 template <int NC>
 __device__ void dn_mfma(const bf16_t* __restrict__ Wd, int d, int rows, int c0,
                         const bf16_t* __restrict__ h, const Slot& sl, int tc,
-                        float* __restrict__ out, int lane, int wid, MfmaLds& lds) {
+                        float* __restrict__ out, int epi, int lane, int wid, MfmaLds& lds) {
   const int r16 = lane & 15, g = lane >> 4;
   int kb, ke;
   k_quarter(rows, wid, kb, ke);
@@ -1292,7 +1372,7 @@ __device__ void dn_mfma(const bf16_t* __restrict__ Wd, int d, int rows, int c0,
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int col = c0 + 4 * g + i;
-          if (col < d) out[(size_t)(sl.r0 + t) * d + col] = sum[i];
+          if (col < d) dn_store(out, (size_t)(sl.r0 + t) * d + col, sum[i], epi);
         }
       }
     }
@@ -1306,8 +1386,9 @@ __device__ void dn_mfma(const bf16_t* __restrict__ Wd, int d, int rows, int c0,
 // prefetch (fp32 layers are small).
 template <int RW, int NT>
 __device__ void gu_plain(const float* __restrict__ Wg, const float* __restrict__ Wu, int d,
-                         int rows, int i0, const float* __restrict__ x, int T, const Slot& sl,
-                         const int* grp_token, int tc, float* __restrict__ h, int lane) {
+                         int rows, int i0, const float* __restrict__ x,
+                         const float* __restrict__ xu, int in_rows, const Slot& sl,
+                         const int* grp_token, int tc, const GuOut<float>& o, int lane) {
   const int nv = min(NT, sl.n - tc);
   float ag[RW][NT], au[RW][NT];
 #pragma unroll
@@ -1324,10 +1405,12 @@ __device__ void gu_plain(const float* __restrict__ Wg, const float* __restrict__
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         if (t < nv) {
-          X8<float> xv;
-          xv.load(x + (size_t)lane_token(sl, grp_token, tc + t, T) * d + c);
+          const size_t row = (size_t)lane_token(sl, grp_token, tc + t, in_rows) * d + c;
+          X8<float> xv, xw;
+          xv.load(x + row);
+          xw.load(xu + row);
           ag[r][t] = dot8(wg, xv, ag[r][t]);
-          au[r][t] = dot8(wu, xv, au[r][t]);
+          au[r][t] = dot8(wu, xw, au[r][t]);
         }
       }
     }
@@ -1347,7 +1430,7 @@ __device__ void gu_plain(const float* __restrict__ Wg, const float* __restrict__
   const int idx = lane >> SH;
   if (idx < N / 2 && (lane & ((1 << SH) - 1)) == 0) {
     const int r = idx / NT, t = idx - (idx / NT) * NT;
-    if (t < nv && i0 + r < rows) h[(size_t)(sl.r0 + tc + t) * rows + i0 + r] = silu(v[0]) * upv;
+    if (t < nv && i0 + r < rows) gu_store(o, (size_t)(sl.r0 + tc + t) * rows + i0 + r, v[0], upv);
   }
 }
 
@@ -1355,7 +1438,7 @@ __device__ void gu_plain(const float* __restrict__ Wg, const float* __restrict__
 template <int CW, int NT>
 __device__ void dn_plain(const float* __restrict__ Wd, int d, int rows, int c0,
                          const float* __restrict__ h, const Slot& sl, int tc,
-                         float* __restrict__ out, int lane) {
+                         float* __restrict__ out, int epi, int lane) {
   const int nv = min(NT, sl.n - tc);
   float acc[CW][NT];
 #pragma unroll
@@ -1388,7 +1471,7 @@ __device__ void dn_plain(const float* __restrict__ Wd, int d, int rows, int c0,
   const int idx = lane >> SH;
   if ((lane & ((1 << SH) - 1)) == 0) {
     const int q = idx / NT, t = idx - (idx / NT) * NT;
-    if (t < nv && c0 + q < d) out[(size_t)(sl.r0 + tc + t) * d + c0 + q] = v[0];
+    if (t < nv && c0 + q < d) dn_store(out, (size_t)(sl.r0 + tc + t) * d + c0 + q, v[0], epi);
   }
 }
 
@@ -1399,26 +1482,31 @@ __device__ void dn_plain(const float* __restrict__ Wd, int d, int rows, int c0,
 // group GEMVs are latency-bound streams that want many waves in flight, so
 // the register budget is capped where the matrix-core part still fits without
 // spilling; fp32 layers keep the compiler's choice.
-template <typename T_, int NCMAX>
-constexpr int gateup_min_waves() { return sizeof(T_) == 2 ? (NCMAX > 1 ? 5 : 6) : 1; }
+template <typename T_, int NCMAX, bool DUAL>
+constexpr int gateup_min_waves() {
+  // two-input launches carry twice the activations: a register budget of 4 waves
+  return sizeof(T_) == 2 ? (DUAL ? 4 : NCMAX > 1 ? 5 : 6) : 1;
+}
 template <typename T_>
 constexpr int down_min_waves() { return sizeof(T_) == 2 ? 7 : 1; }
 
 // LDS of an expert-kernel block: the matrix-core partial tiles of a large
 // group or the staged activations of a small one (a block is only ever one).
-template <typename T_, bool XL>
+template <typename T_, bool XL, bool DUAL = false>
 constexpr size_t expert_lds_bytes() {
   const size_t a = sizeof(T_) == 2 ? sizeof(MfmaLds) : 0;
-  const size_t b = XL ? sizeof(SmallLds<T_>) : 0;
+  const size_t b = XL ? sizeof(SmallLds<T_, DUAL ? 2 * kTokInline : kTokInline>) : 0;
   return a > b ? a : (b > 0 ? b : 16);
 }
 
 // NCMAX: 16-token chunks a large-group tile takes at once (2 only when a
 // group can exceed 16 rows, since the wider chunk costs registers).
 // XL: small groups read their activations from LDS (rows of at most kXLds).
-template <typename T_, int RPW, int RW, int NCMAX, bool XL>
+// DUAL: every part of the launch reads gate and up inputs from two different
+// matrices (the private transforms of the factorised form).
+template <typename T_, int RPW, int RW, int NCMAX, bool XL, bool DUAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
-    gateup_min_waves<T_, NCMAX>(), 8))) void gateup_kernel(FamilySet set,
+    gateup_min_waves<T_, NCMAX, DUAL>(), 8))) void gateup_kernel(FamilySet set,
                                                            const T_* __restrict__ x, int T,
                                                            int d) {
   int tile;
@@ -1429,19 +1517,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   const size_t ms = (size_t)F.rows * d;
   const T_* Wg = static_cast<const T_*>(F.gate) + (size_t)sl.mat * ms;
   const T_* Wu = static_cast<const T_*>(F.up) + (size_t)sl.mat * ms;
-  T_* h = static_cast<T_*>(F.h);
-  __shared__ __align__(16) unsigned char lds_raw[expert_lds_bytes<T_, XL>()];
+  const T_* xg = F.x_gate ? static_cast<const T_*>(F.x_gate) : x;
+  const T_* xu = DUAL ? static_cast<const T_*>(F.x_up) : xg;
+  const GuOut<T_> o{static_cast<T_*>(F.h), static_cast<T_*>(F.h2), F.epi};
+  __shared__ __align__(16) unsigned char lds_raw[expert_lds_bytes<T_, XL, DUAL>()];
   if (!F.large) {
     if constexpr (XL) {
       static_assert(RPW == 1 && RW == 1, "staged activations take one row per wave");
-      gu_small_lds<T_>(Wg, Wu, d, F.rows, tile * kWaves + wid, x, T, sl, F.grp_token, h, lane,
-                       wid, *reinterpret_cast<SmallLds<T_>*>(lds_raw));
+      gu_small_lds<T_, DUAL>(
+          Wg, Wu, d, F.rows, tile * kWaves + wid, xg, xu, F.in_rows, sl, F.grp_token, o, lane, wid,
+          *reinterpret_cast<SmallLds<T_, DUAL ? 2 * kTokInline : kTokInline>*>(lds_raw));
       return;
     }
     const int i0 = tile * (kWaves * RPW) + wid * RPW;
 #pragma unroll 1
     for (int r = 0; r < RPW && i0 + r < F.rows; r += RW)
-      gu_small<T_, RW>(Wg, Wu, d, F.rows, i0 + r, x, T, sl, F.grp_token, h, lane);
+      gu_small<T_, RW, DUAL>(Wg, Wu, d, F.rows, i0 + r, xg, xu, F.in_rows, sl, F.grp_token, o,
+                             lane);
     return;
   }
   // large groups: the whole block on one 16-row tile
@@ -1452,16 +1544,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll 1
     for (int tc = 0; tc < sl.n; tc += 16 * NCMAX) {
       if (NCMAX > 1 && sl.n - tc > 16)
-        gu_mfma<NCMAX>(Wg, Wu, d, F.rows, i0, x, T, sl, F.grp_token, tc, h, lane, wid, lds);
+        gu_mfma<NCMAX, DUAL>(Wg, Wu, d, F.rows, i0, xg, xu, F.in_rows, sl, F.grp_token, tc, o,
+                             lane, wid, lds);
       else
-        gu_mfma<1>(Wg, Wu, d, F.rows, i0, x, T, sl, F.grp_token, tc, h, lane, wid, lds);
+        gu_mfma<1, DUAL>(Wg, Wu, d, F.rows, i0, xg, xu, F.in_rows, sl, F.grp_token, tc, o, lane,
+                         wid, lds);
     }
   } else {
 #pragma unroll 1
     for (int r = wid * 4; r < wid * 4 + 4; r += 2)
 #pragma unroll 1
       for (int tc = 0; tc < sl.n; tc += 8)
-        gu_plain<2, 8>(Wg, Wu, d, F.rows, i0 + r, x, T, sl, F.grp_token, tc, h, lane);
+        gu_plain<2, 8>(Wg, Wu, d, F.rows, i0 + r, xg, xu, F.in_rows, sl, F.grp_token, tc, o,
+                       lane);
   }
 }
 
@@ -1480,10 +1575,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     constexpr int CPW = CG * (64 / LPR);
     const int cb = tile * (kWaves * CPW) + wid * CPW;
     if constexpr (XL)  // every wave takes part in the staging
-      dn_small_lds<T_, LPR, CG>(Wd, d, F.rows, cb, h, sl, F.out, lane, wid,
+      dn_small_lds<T_, LPR, CG>(Wd, d, F.rows, cb, h, sl, F.out, F.epi, lane, wid,
                                 *reinterpret_cast<SmallLds<T_>*>(lds_raw));
     else if (cb < d)
-      dn_small<T_, LPR, CG>(Wd, d, F.rows, cb, h, sl, F.out, lane);
+      dn_small<T_, LPR, CG>(Wd, d, F.rows, cb, h, sl, F.out, F.epi, lane);
     return;
   }
   // large groups: the whole block on one 16-column tile
@@ -1494,17 +1589,41 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll 1
     for (int tc = 0; tc < sl.n; tc += 32) {
       if (sl.n - tc > 16)
-        dn_mfma<2>(Wd, d, F.rows, c0, h, sl, tc, F.out, lane, wid, lds);
+        dn_mfma<2>(Wd, d, F.rows, c0, h, sl, tc, F.out, F.epi, lane, wid, lds);
       else
-        dn_mfma<1>(Wd, d, F.rows, c0, h, sl, tc, F.out, lane, wid, lds);
+        dn_mfma<1>(Wd, d, F.rows, c0, h, sl, tc, F.out, F.epi, lane, wid, lds);
     }
   } else {
 #pragma unroll 1
     for (int q = wid * 4; q < wid * 4 + 4; q += 2)
 #pragma unroll 1
       for (int tc = 0; tc < sl.n; tc += 8)
-        dn_plain<2, 8>(Wd, d, F.rows, c0 + q, h, sl, tc, F.out, lane);
+        dn_plain<2, 8>(Wd, d, F.rows, c0 + q, h, sl, tc, F.out, F.epi, lane);
   }
+}
+
+// Factorised form, between the private and the department down projections
+// (DeaMoE section 3.2 collects every Z^{j,i} of department j for one W_d^j
+// product; by linearity the Eq. (3) weights are applied before it):
+//   zc[q][c] = sum over the slots s of token t (slot order) whose expert lies
+//              in department J of row_weight[r] * z[r][c],  r = inv_perm[t*k+s]
+// for pair q = (t, J).  One block per (256 columns, pair); pairs past the
+// plan's count exit at once.
+template <typename AT>
+__global__ __launch_bounds__(kThreads) void pair_combine_kernel(PairCombineArgs a,
+                                                                AT* __restrict__ zc) {
+  const int c = blockIdx.x * kThreads + threadIdx.x;
+  const int q = blockIdx.y;
+  if (q >= *a.n_pairs || c >= a.cols) return;
+  const int t = a.pair_token[q], J = a.pair_dept[q];
+  if (t < 0 || t >= a.T) return;
+  float acc = 0.f;
+  for (int s = 0; s < a.k; ++s) {
+    const int r = a.inv_perm[t * a.k + s];
+    if (r >= 0 && r < a.max_rows && a.row_expert[r] / a.group == J)
+      acc = fmaf(a.row_weight[r], a.z[(size_t)r * a.cols + c], acc);
+  }
+  store_act(zc + (size_t)q * a.cols + c, acc);
 }
 
 // One block per (256 columns, token): every thread one output element.
@@ -1514,15 +1633,19 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a, AT* __
   const int t = blockIdx.y;
   if (c >= a.d) return;
   float acc = 0.f;
-  for (int j = 0; j < a.k; ++j) {
-    const int r = a.inv_perm[t * a.k + j];
-    if (r >= 0 && r < a.max_rows) acc = fmaf(a.row_weight[r], a.row_out[(size_t)r * a.d + c], acc);
+  if (a.row_out) {
+    for (int j = 0; j < a.k; ++j) {
+      const int r = a.inv_perm[t * a.k + j];
+      if (r >= 0 && r < a.max_rows)
+        acc = fmaf(a.row_weight[r], a.row_out[(size_t)r * a.d + c], acc);
+    }
   }
   if (a.dept_out) {
     for (int J = 0; J < a.m; ++J) {
       const int q = a.dept_inv[t * a.m + J];
-      if (q >= 0 && q < a.max_dept_rows)
-        acc = fmaf(a.dept_scale[q], a.dept_out[(size_t)q * a.d + c], acc);
+      if (q >= 0 && q < a.max_dept_rows)  // no scales: the weights are already inside (factorised)
+        acc = a.dept_scale ? fmaf(a.dept_scale[q], a.dept_out[(size_t)q * a.d + c], acc)
+                           : acc + a.dept_out[(size_t)q * a.d + c];
     }
   }
   if (a.shared_out) acc += a.shared_out[(size_t)t * a.d + c];
@@ -1610,14 +1733,17 @@ static hipError_t launch_gateup_t(const FamilySet& set, const T_* x, int T, int 
   // the capped-occupancy build leaves no room for more
   if (rpw != 1 || rw != 1) return hipErrorInvalidValue;
   const bool xl = d <= kXLds;
-  if (wide && xl)
-    launch(gateup_kernel<T_, 1, 1, 2, true>, grid, block, st, ev, set, x, T, d);
-  else if (wide)
-    launch(gateup_kernel<T_, 1, 1, 2, false>, grid, block, st, ev, set, x, T, d);
-  else if (xl)
-    launch(gateup_kernel<T_, 1, 1, 1, true>, grid, block, st, ev, set, x, T, d);
-  else
-    launch(gateup_kernel<T_, 1, 1, 1, false>, grid, block, st, ev, set, x, T, d);
+  // two-input launches (factorised private transforms) have every part so
+  const bool dual = set.f[0].x_up != nullptr;
+#define MOE_GU(W, X, D) launch(gateup_kernel<T_, 1, 1, W, X, D>, grid, block, st, ev, set, x, T, d)
+  if (dual) {
+    if (wide && xl) MOE_GU(2, true, true); else if (wide) MOE_GU(2, false, true);
+    else if (xl) MOE_GU(1, true, true); else MOE_GU(1, false, true);
+  } else {
+    if (wide && xl) MOE_GU(2, true, false); else if (wide) MOE_GU(2, false, false);
+    else if (xl) MOE_GU(1, true, false); else MOE_GU(1, false, false);
+  }
+#undef MOE_GU
   return hipGetLastError();
 }
 
@@ -1693,6 +1819,17 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const bf16_t* __r
   if (lane == 0) part[wid] = acc;
   __syncthreads();
   if (threadIdx.x == 0) sink[blockIdx.x] = ((part[0] + part[1]) + part[2]) + part[3];
+}
+
+hipError_t launch_pair_combine(int act_dtype, const PairCombineArgs& a, void* zc, int max_pairs,
+                               hipStream_t st) {
+  if (max_pairs <= 0) return hipSuccess;
+  const dim3 grid((a.cols + kThreads - 1) / kThreads, max_pairs), block(kThreads);
+  if (act_dtype == MOE_BF16)
+    hipLaunchKernelGGL(pair_combine_kernel<bf16_t>, grid, block, 0, st, a, static_cast<bf16_t*>(zc));
+  else
+    hipLaunchKernelGGL(pair_combine_kernel<float>, grid, block, 0, st, a, static_cast<float*>(zc));
+  return hipGetLastError();
 }
 
 hipError_t launch_stream_read(const void* src, size_t blocks, float* sink, hipStream_t st) {

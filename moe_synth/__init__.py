@@ -14,11 +14,14 @@ bf16 is round-to-nearest-even (torch's own conversion).
 
 Layer shapes
 ------------
-The five layer shapes follow the workloads the pages name (Qwen3-30B-A3B,
-DeepSeek-V3 and the DeaMoE department layer); the value distributions follow
-the pages' own routers: router and expert weights N(0, 0.02) (the router
-initialisation in the DeepSeekMoE guide's PyTorch layer), activations N(0, 1)
-except the tiny layer (N(0, 0.02)), selection bias U(-0.1, 0.1).
+The layer shapes follow the workloads the pages name (Qwen3-30B-A3B,
+DeepSeek-V3, the DeaMoE department layer in slice form, and DeaMoE's own
+factorised experts at its DeepSeek-V3-matched configuration); the value
+distributions follow the pages' own routers: router and expert weights
+N(0, 0.02) (the router initialisation in the DeepSeekMoE guide's PyTorch
+layer), activations N(0, 1) except the tiny layer (N(0, 0.02)), selection bias
+U(-0.1, 0.1); factorised private transforms are the identity DeaMoE starts
+them from plus N(0, 0.02).
 """
 from __future__ import annotations
 
@@ -58,6 +61,8 @@ class LayerShape:
     renormalize: bool = True
     route_scale: float = 1.0
     dtype: str = "bf16"            # weights and activations
+    dept_form: str = "slice"       # "slice" | "factorised" (private S x S transforms)
+    a_std: float = 0.02            # factorised: private transforms = I + N(0, a_std)
     x_std: float = 1.0
     w_std: float = 0.02
     bias_range: float = 0.0        # U(-r, r) selection bias when > 0
@@ -97,6 +102,15 @@ SHAPES: Dict[str, LayerShape] = {
         n_experts=256, top_k=8, d_ff=256, n_depts=32, d_ff_dept=1792,
         d_ff_shared=2048, score="sigmoid", bias_range=0.1,
         batches=(1, 2, 4, 8, 16),
+        data_seed_of="deepseek_v3_d7168_e256_i2048_s2048_top8"),
+    # DeaMoE's own factorised experts at the DeepSeek-V3-matched configuration
+    # of its Table 1 (8 departments x 108 experts, h = 7168, hffn = 2048,
+    # k = 10), softmax routing (Eq. (2)-(3)); DeepSeek-V3's tokens and shared
+    # expert.
+    "deamoe_paper_dsv3_d7168_e864_m8_h2048_top10": LayerShape(
+        name="deamoe_paper_dsv3_d7168_e864_m8_h2048_top10", d=7168,
+        n_experts=864, top_k=10, d_ff=2048, n_depts=8, d_ff_dept=2048,
+        d_ff_shared=2048, dept_form="factorised", batches=(1, 2, 4, 8, 16),
         data_seed_of="deepseek_v3_d7168_e256_i2048_s2048_top8"),
 }
 
@@ -198,9 +212,18 @@ def make_layer(shape: LayerShape, seed: int, device="cpu",
     # Expert tensors of a transformed layer draw from their own seed space so
     # they are not a slice of the source layer's experts.
     eseed = seed if not shape.data_seed_of else seed + 7919
-    w["w_gate"] = normal(eseed, _TID["w_gate"], (E, I, d), shape.w_std, dt, device)
-    w["w_up"] = normal(eseed, _TID["w_up"], (E, I, d), shape.w_std, dt, device)
-    w["w_down"] = normal(eseed, _TID["w_down"], (E, d, I), shape.w_std, dt, device)
+    if shape.dept_form == "factorised":
+        # private transforms A_g, A_u and (A_d)^T, [E][S][S]: the identity the
+        # pages start them from, plus N(0, a_std); rounded once to dtype
+        for name in ("w_gate", "w_up", "w_down"):
+            a = normal(eseed, _TID[name], (E, I, I), shape.a_std, torch.float32, device)
+            a.diagonal(dim1=1, dim2=2).add_(1.0)
+            w[name] = a.to(dt)
+            del a
+    else:
+        w["w_gate"] = normal(eseed, _TID["w_gate"], (E, I, d), shape.w_std, dt, device)
+        w["w_up"] = normal(eseed, _TID["w_up"], (E, I, d), shape.w_std, dt, device)
+        w["w_down"] = normal(eseed, _TID["w_down"], (E, d, I), shape.w_std, dt, device)
     if shape.n_depts:
         m, S = shape.n_depts, shape.d_ff_dept
         w["wd_gate"] = normal(eseed, _TID["wd_gate"], (m, S, d), shape.w_std, dt, device)

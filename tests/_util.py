@@ -25,7 +25,8 @@ TOL = {"bf16": (2e-2, 4e-3), "f32": (1e-4, 1e-5)}
 def desc_of(shape: moe_synth.LayerShape, max_tokens: int = None, **over) -> M.LayerDesc:
     kw = dict(n_depts=shape.n_depts, d_ff_dept=shape.d_ff_dept, d_ff_shared=shape.d_ff_shared,
               score=shape.score, renormalize=shape.renormalize, route_scale=shape.route_scale,
-              dtype=shape.dtype, max_tokens=max_tokens or max(shape.batches))
+              dtype=shape.dtype, max_tokens=max_tokens or max(shape.batches),
+              dept_form=shape.dept_form)
     kw.update(over)
     return M.layer_desc(shape.d, shape.n_experts, shape.top_k, shape.d_ff, **kw)
 

@@ -70,6 +70,10 @@ def _desc(**kw):
     (dict(n_experts=4096, top_k=8), M.MOE_ERR_UNSUPPORTED),
     (dict(top_k=33), M.MOE_ERR_UNSUPPORTED),
     (dict(score="sigmoid", route_scale=float("inf")), M.MOE_ERR_INVALID_ARG),
+    # factorised department form: S x S private transforms need d_ff == d_ff_dept
+    (dict(n_depts=8, d_ff=1024, d_ff_dept=1024, dept_form="factorised"), M.MOE_OK),
+    (dict(n_depts=8, d_ff_dept=1024, dept_form="factorised"), M.MOE_ERR_INVALID_ARG),
+    (dict(dept_form="factorised"), M.MOE_ERR_INVALID_ARG),                # needs departments
 ])
 def test_descriptor_validation(lib, kw, status):
     assert M.moe_validate_desc(_desc(**kw)) == status
@@ -155,6 +159,21 @@ def test_plan_addresses_inside_workspace(lib):
     addrs = [getattr(P, n) for n in M._PLAN_ARRAYS]
     assert all(base <= a < base + ws for a in addrs)
     assert len(set(addrs)) == len(addrs)
+
+
+def test_dept_form_field_is_checked(lib):
+    d = _desc()
+    d.dept_form = 7
+    assert M.moe_validate_desc(d) == M.MOE_ERR_INVALID_ARG
+
+
+def test_factorised_workspace_and_bytes(lib):
+    fac = _desc(n_experts=32, top_k=6, d_ff=256, n_depts=4, d_ff_dept=256, dept_form="factorised")
+    sl = _desc(n_experts=32, top_k=6, d_ff=256, n_depts=4, d_ff_dept=256)
+    assert M.moe_workspace_bytes(fac) > M.moe_workspace_bytes(sl)  # backbone outputs per pair
+    # router + 10 private S x S triples + 3 department S x d triples, bf16
+    assert M.moe_loaded_weight_bytes(fac, 10, 3) == 2 * (32 * 2048 + 10 * 3 * 256 * 256
+                                                         + 3 * 3 * 2048 * 256)
 
 
 def test_loaded_weight_bytes(lib):
