@@ -56,7 +56,12 @@ justification in the design notes):
   R17 the GPU pre-combines a token's p_i * Z^{j,i} over its experts in
      department j before the single (W_d^j)^T product, exact by linearity;
      the oracle keeps the pages' order (one product per expert) and a test
-     pins the two equal.
+     pins the two equal;
+  R18 department-limited (group) top-k (DeaMoE section 3.4, k_dept caps the
+     departments a token activates): a department's score is the best
+     selection score among its experts; the k_dept best departments are
+     taken (ties to the lower department index), then the k best experts
+     inside them (ties to the lower expert index).
 """
 from __future__ import annotations
 
@@ -71,7 +76,8 @@ __all__ = [
     "dept_layer_factored", "layer_token_output", "loaded_weight_bytes",
     "deamoe_expert", "deamoe_token_output", "deamoe_layer_per_expert",
     "deamoe_layer_two_stage", "deamoe_layer_precombined",
-    "select_from_scores", "silu", "cast_output", "SOFTMAX", "SIGMOID", "SOFTMAX_BIAS",
+    "select_from_scores", "topk_select_grouped", "silu", "cast_output", "SOFTMAX", "SIGMOID",
+    "SOFTMAX_BIAS",
 ]
 
 SOFTMAX, SIGMOID, SOFTMAX_BIAS = "softmax", "sigmoid", "softmax_bias"
@@ -136,6 +142,25 @@ def topk_select(sel: np.ndarray, k: int) -> np.ndarray:
 select_from_scores = topk_select
 
 
+def topk_select_grouped(sel: np.ndarray, k: int, n_depts: int, k_dept: int) -> np.ndarray:
+    """Department-limited top-k (R18): per token, rank departments by their
+    best expert's score (score desc, department index asc), keep the k_dept
+    best, and take the k best experts among those departments' experts
+    (score desc, index asc)."""
+    sel = np.asarray(sel)
+    T, E = sel.shape
+    g = E // n_depts
+    ids = np.empty((T, k), dtype=np.int32)
+    for t in range(T):
+        dept_score = [max(float(sel[t, e]) for e in range(j * g, (j + 1) * g))
+                      for j in range(n_depts)]
+        depts = sorted(range(n_depts), key=lambda j: (-dept_score[j], j))[:k_dept]
+        allowed = [e for e in range(E) if e // g in depts]
+        order = sorted(allowed, key=lambda e: (-float(sel[t, e]), e))
+        ids[t] = order[:k]
+    return ids
+
+
 def routing_weights(l32: np.ndarray, ids: np.ndarray, score_fn: str,
                     renormalize: bool = True, route_scale: float = 1.0) -> np.ndarray:
     """Per-slot weights p_i of Eq. (3), in fp64.
@@ -165,12 +190,14 @@ def routing_weights(l32: np.ndarray, ids: np.ndarray, score_fn: str,
 
 
 def route(x, w_router, k: int, score_fn: str = SOFTMAX, bias=None,
-          renormalize: bool = True, route_scale: float = 1.0):
+          renormalize: bool = True, route_scale: float = 1.0, n_depts: int = 0,
+          k_dept: int = 0):
     """Router of one decode step: (ids int32[T][k], weights f64[T][k],
-    selection scores f32[T][E], logits f32[T][E])."""
+    selection scores f32[T][E], logits f32[T][E]).  k_dept > 0 limits each
+    token to k_dept departments (R18)."""
     l32 = router_logits(x, w_router)
     sel = selection_scores(l32, score_fn, bias)
-    ids = topk_select(sel, k)
+    ids = topk_select_grouped(sel, k, n_depts, k_dept) if k_dept else topk_select(sel, k)
     w = routing_weights(l32, ids, score_fn, renormalize, route_scale)
     return ids, w, sel, l32
 

@@ -516,3 +516,50 @@ def test_factorised_loaded_bytes_reproduce_fig2():
             van.append(O.loaded_weight_bytes(ids_v, 256, 7168, 2048, 1, include_router=False))
         ratio = np.mean(dea) / np.mean(van)
         assert ratio == pytest.approx(_fig2_ratio(B), rel=5e-3)
+
+
+# ---------------------------------------------------------------------------
+# Department-limited top-k (DeaMoE section 3.4: k_dept caps the departments a
+# token activates)
+# ---------------------------------------------------------------------------
+
+def test_grouped_topk_hand_example():
+    """12 experts in 3 departments of 4.  Plain top-3 takes experts 0, 5 and
+    9 (one per department); with k_dept = 2 department 2 (best score 0.6)
+    loses to departments 0 (0.9) and 1 (0.8), so the picks are 0, 5, then
+    the best remaining in departments 0-1: expert 1 (0.5) over 6 (0.4)."""
+    sel = np.array([[0.9, 0.5, 0.1, 0.0, 0.2, 0.8, 0.4, 0.3, 0.1, 0.6, 0.2, 0.05]],
+                   np.float32)
+    assert O.topk_select(sel, 3).tolist() == [[0, 5, 9]]
+    assert O.topk_select_grouped(sel, 3, 3, 2).tolist() == [[0, 5, 1]]
+    assert O.topk_select_grouped(sel, 3, 3, 1).tolist() == [[0, 1, 2]]
+    # department ties go to the lower index: departments 1 and 2 both best at 0.8
+    sel2 = sel.copy()
+    sel2[0, 9] = 0.8
+    assert O.topk_select_grouped(sel2, 2, 3, 2).tolist() == [[0, 5]]
+    sel2[0, 0] = 0.0
+    assert O.topk_select_grouped(sel2, 2, 3, 1).tolist() == [[5, 6]]
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_grouped_topk_properties(seed):
+    """Random scores: k_dept = m is the plain top-k; otherwise the picks span
+    at most k_dept departments, always include the overall best expert, and
+    equal a brute force over every set of k_dept departments (the set whose
+    best score tuple is largest)."""
+    rng = _rng(500 + seed)
+    E, m, k, T = 24, 6, 5, 8
+    g = E // m
+    sel = rng.normal(0, 1, (T, E)).astype(np.float32)
+    assert np.array_equal(O.topk_select_grouped(sel, k, m, m), O.topk_select(sel, k))
+    for kd in (2, 3):
+        ids = O.topk_select_grouped(sel, k, m, kd)
+        for t in range(T):
+            assert len({int(e) // g for e in ids[t]}) <= kd
+            assert int(np.argmax(sel[t])) in ids[t]
+            best = max(itertools.combinations(range(m), kd),
+                       key=lambda D: (sorted((sel[t, j * g:(j + 1) * g].max() for j in D),
+                                             reverse=True), [-j for j in D]))
+            pool = [e for e in range(E) if e // g in best]
+            want = sorted(pool, key=lambda e: (-sel[t, e], e))[:k]
+            assert ids[t].tolist() == want
