@@ -104,6 +104,7 @@ typedef enum {
 #define MOE_MAX_TOP_K 32
 #define MOE_MAX_ASSIGNMENTS 4096      /* max_tokens * top_k */
 #define MOE_MAX_DEPT_PAIRS 4096       /* max_tokens * n_depts */
+#define MOE_MAX_DEPTS_GROUPED 64      /* n_depts limit when k_dept > 0 */
 
 typedef struct {
   int32_t d_model;       /* d */
@@ -120,6 +121,12 @@ typedef struct {
   int32_t act_dtype;     /* moe_dtype of x and y (MOE_F32 with MOE_F32 weights, else MOE_BF16) */
   int32_t max_tokens;    /* largest T a workspace sized for this descriptor accepts */
   int32_t dept_form;     /* moe_dept_form (n_depts > 0); factorised requires d_ff == d_ff_dept */
+  int32_t k_dept;        /* 0 = no cap; else each token's experts come from at most k_dept
+                          * departments (DeaMoE section 3.4's group top-k): departments are
+                          * ranked by their best expert's selection score (ties to the lower
+                          * index), the k_dept best kept, then the top k inside them.
+                          * 1 <= k_dept <= n_depts <= MOE_MAX_DEPTS_GROUPED,
+                          * top_k <= k_dept * (E / n_depts). */
 } moe_layer_desc;
 
 typedef struct {

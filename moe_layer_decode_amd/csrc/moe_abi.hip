@@ -121,6 +121,10 @@ moe_status check_desc(const moe_layer_desc* d) {
   } else if (d->dept_form != MOE_DEPT_SLICE) {
     return MOE_ERR_INVALID_ARG;
   }
+  if (d->k_dept < 0 || d->k_dept > (d->n_depts > 0 ? d->n_depts : 0)) return MOE_ERR_INVALID_ARG;
+  if (d->k_dept > 0 && (int64_t)d->k_dept * (d->n_experts / d->n_depts) < d->top_k)
+    return MOE_ERR_INVALID_ARG;  // not enough experts in k_dept departments
+  if (d->k_dept > 0 && d->n_depts > MOE_MAX_DEPTS_GROUPED) return MOE_ERR_UNSUPPORTED;
   if (d->score_fn < MOE_SCORE_SOFTMAX || d->score_fn > MOE_SCORE_SOFTMAX_BIAS)
     return MOE_ERR_INVALID_ARG;
   if (d->renormalize != 0 && d->renormalize != 1) return MOE_ERR_INVALID_ARG;
@@ -226,6 +230,8 @@ moe::RouteArgs route_args(const moe_layer_desc& d, void* ws, const void* x, cons
   ra.scale = d.route_scale;
   ra.n_chunks = n_route_chunks(d);
   ra.ksplit = route_ksplit(d);
+  ra.m = d.n_depts;
+  ra.k_dept = d.k_dept;
   ra.logits = at<float>(ws, L, R_LOGITS);
   ra.ids_out = ids;
   ra.w_out = w;

@@ -51,6 +51,7 @@ struct RouteArgs {
   int T, d, E, k;
   int score_fn, renorm;
   float scale;
+  int m, k_dept;           // department-limited top-k when 0 < k_dept < m
   int n_chunks;            // ceil(d / kRouteChunk)
   int ksplit;              // partial-logit planes: logits holds [ksplit][T][E], summed in order
   float* logits;           // [ksplit][T][E]

@@ -162,6 +162,7 @@ struct PlanShared {
   int eslot[MOE_MAX_EXPERTS];             // expert's slot, kept past the department pass
   short arank[MOE_MAX_ASSIGNMENTS];       // assignment's rank inside its expert group
   unsigned char flag[MOE_MAX_DEPT_PAIRS];
+  unsigned dmax[kPlanThreads / kWave][MOE_MAX_DEPTS_GROUPED];  // per wave: department best keys
   int invalid;
 };
 
@@ -187,7 +188,7 @@ __device__ __forceinline__ float route_aux(const RouteArgs& p, float l) {
   return p.score_fn == MOE_SCORE_SIGMOID ? 1.0f / (1.0f + expf(-l)) : l;
 }
 
-template <int NPL>
+template <int NPL, bool GROUPED>
 __device__ void topk_one(const RouteArgs& p, int t, int lane, PlanShared& s) {
   float lg[NPL];
   uint32_t key[NPL];
@@ -224,6 +225,47 @@ __device__ void topk_one(const RouteArgs& p, int t, int lane, PlanShared& s) {
     }
   }
   const int k = p.k;
+  if (GROUPED) {
+    // Department-limited top-k: a department's key is its best expert's key
+    // (LDS max, one area per wave); the k_dept best departments are chosen
+    // like experts below (lane J holds department J; ties to the lower
+    // index) and the experts of every other department drop to key 0, below
+    // every real score.
+    const int G = p.E / p.m, wid = threadIdx.x >> 6, kd = p.k_dept;
+    // department of expert e = floor((e + 0.5) / G) in fp32: exact, since
+    // e < 2048 and the quotient is below m <= 64, so the rounding error
+    // (under 64 * 2^-23) stays inside the 0.5 / G margin to each integer
+    const float inv_g = 1.0f / (float)G;
+    auto dept_of = [&](int e) { return (unsigned)(((float)e + 0.5f) * inv_g); };
+    unsigned* dm = s.dmax[wid];
+    if (lane < p.m) dm[lane] = 0u;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int e = lane + kWave * i;
+      if (e < p.E) atomicMax(&dm[dept_of(e)], key[i]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    const uint32_t dkey = lane < p.m ? dm[lane] : 0u;
+    uint32_t dthr = 0u;
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t c = dthr | (1u << b);
+      if (wave_count(dkey >= c) >= kd) dthr = c;
+    }
+    const int dabove = wave_count(dkey > dthr);
+    const uint64_t deq = __ballot(lane < p.m && dkey == dthr);
+    const bool dtake = lane < p.m && (dkey > dthr ||
+                                      (dkey == dthr && __popcll(deq & ((1ull << lane) - 1ull)) <
+                                                           kd - dabove));
+    const uint64_t chosen_depts = __ballot(dtake);
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int e = lane + kWave * i;
+      if (e < p.E && !((chosen_depts >> dept_of(e)) & 1ull)) key[i] = 0u;
+    }
+  }
   // largest thr with #(key >= thr) >= k: the k-th largest key
   uint32_t thr = 0u;
   for (int b = 31; b >= 0; --b) {
@@ -624,12 +666,12 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(RouteArgs ra) {
 
 // One block: top-k of every token (one wave per token), then (do_plan) the
 // dispatch plan.
-template <int NPL>
+template <int NPL, bool GROUPED>
 __global__ __launch_bounds__(kPlanThreads) void topk_plan_kernel(RouteArgs ra, PlanArgs pa,
                                                                  int do_plan) {
   __shared__ PlanShared s;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  for (int t = wid; t < ra.T; t += nw) topk_one<NPL>(ra, t, lane, s);
+  for (int t = wid; t < ra.T; t += nw) topk_one<NPL, GROUPED>(ra, t, lane, s);
   if (!do_plan) return;
   __syncthreads();
   plan_phase(s, pa);
@@ -1696,18 +1738,24 @@ static hipError_t launch_route_t(const RouteArgs& ra, const PlanArgs* pa, hipStr
   const int do_plan = pa != nullptr;
   const dim3 grid(1), block(kPlanThreads);
   const KernelEvents* ev2 = ev ? ev + 1 : nullptr;
+  // department-limited top-k only where the cap binds (its own instances)
+  const bool grouped = ra.k_dept > 0 && ra.k_dept < ra.m;
+#define MOE_TOPK(N)                                                               \
+  (grouped ? launch(topk_plan_kernel<N, true>, grid, block, st, ev2, ra, p, do_plan) \
+           : launch(topk_plan_kernel<N, false>, grid, block, st, ev2, ra, p, do_plan))
   if (ra.E <= 64)
-    launch(topk_plan_kernel<1>, grid, block, st, ev2, ra, p, do_plan);
+    MOE_TOPK(1);
   else if (ra.E <= 128)
-    launch(topk_plan_kernel<2>, grid, block, st, ev2, ra, p, do_plan);
+    MOE_TOPK(2);
   else if (ra.E <= 256)
-    launch(topk_plan_kernel<4>, grid, block, st, ev2, ra, p, do_plan);
+    MOE_TOPK(4);
   else if (ra.E <= 512)
-    launch(topk_plan_kernel<8>, grid, block, st, ev2, ra, p, do_plan);
+    MOE_TOPK(8);
   else if (ra.E <= 1024)
-    launch(topk_plan_kernel<16>, grid, block, st, ev2, ra, p, do_plan);
+    MOE_TOPK(16);
   else
-    launch(topk_plan_kernel<32>, grid, block, st, ev2, ra, p, do_plan);
+    MOE_TOPK(32);
+#undef MOE_TOPK
   return hipGetLastError();
 }
 

@@ -63,6 +63,7 @@ class LayerShape:
     dtype: str = "bf16"            # weights and activations
     dept_form: str = "slice"       # "slice" | "factorised" (private S x S transforms)
     a_std: float = 0.02            # factorised: private transforms = I + N(0, a_std)
+    k_dept: int = 0                # department-limited top-k cap (0 = none)
     x_std: float = 1.0
     w_std: float = 0.02
     bias_range: float = 0.0        # U(-r, r) selection bias when > 0
@@ -105,12 +106,12 @@ SHAPES: Dict[str, LayerShape] = {
         data_seed_of="deepseek_v3_d7168_e256_i2048_s2048_top8"),
     # DeaMoE's own factorised experts at the DeepSeek-V3-matched configuration
     # of its Table 1 (8 departments x 108 experts, h = 7168, hffn = 2048,
-    # k = 10), softmax routing (Eq. (2)-(3)); DeepSeek-V3's tokens and shared
-    # expert.
+    # k = 10 within k_dept = 5 departments), softmax routing (Eq. (2)-(3));
+    # DeepSeek-V3's tokens and shared expert.
     "deamoe_paper_dsv3_d7168_e864_m8_h2048_top10": LayerShape(
         name="deamoe_paper_dsv3_d7168_e864_m8_h2048_top10", d=7168,
         n_experts=864, top_k=10, d_ff=2048, n_depts=8, d_ff_dept=2048,
-        d_ff_shared=2048, dept_form="factorised", batches=(1, 2, 4, 8, 16),
+        d_ff_shared=2048, dept_form="factorised", k_dept=5, batches=(1, 2, 4, 8, 16),
         data_seed_of="deepseek_v3_d7168_e256_i2048_s2048_top8"),
 }
 

@@ -74,6 +74,16 @@ def _desc(**kw):
     (dict(n_depts=8, d_ff=1024, d_ff_dept=1024, dept_form="factorised"), M.MOE_OK),
     (dict(n_depts=8, d_ff_dept=1024, dept_form="factorised"), M.MOE_ERR_INVALID_ARG),
     (dict(dept_form="factorised"), M.MOE_ERR_INVALID_ARG),                # needs departments
+    # department-limited top-k
+    (dict(n_depts=8, d_ff_dept=1024, k_dept=3), M.MOE_OK),
+    (dict(n_depts=8, d_ff_dept=1024, k_dept=8), M.MOE_OK),                 # no cap in effect
+    (dict(k_dept=1), M.MOE_ERR_INVALID_ARG),                               # needs departments
+    (dict(n_depts=8, d_ff_dept=1024, k_dept=9), M.MOE_ERR_INVALID_ARG),    # > n_depts
+    (dict(n_depts=8, d_ff_dept=1024, k_dept=-1), M.MOE_ERR_INVALID_ARG),
+    (dict(n_depts=64, d_ff_dept=128, top_k=2, k_dept=1), M.MOE_OK),      # k = 1 * (E / m)
+    (dict(n_depts=64, d_ff_dept=128, top_k=3, k_dept=1), M.MOE_ERR_INVALID_ARG),  # 3 > 1 * 2
+    (dict(n_experts=256, n_depts=128, d_ff_dept=128, top_k=2, k_dept=2),
+     M.MOE_ERR_UNSUPPORTED),                                               # > 64 departments
 ])
 def test_descriptor_validation(lib, kw, status):
     assert M.moe_validate_desc(_desc(**kw)) == status

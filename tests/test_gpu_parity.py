@@ -13,8 +13,8 @@ import torch
 import moe_layer_decode_amd as M
 import moe_synth
 import oracle as O
-from _util import (TAU, assert_close, desc_of, gpu_ids_from_plan, oracle_route, reference_ids,
-                   to_np)
+from _util import (TAU, TOL_FACTORISED, assert_close, desc_of, gpu_ids_from_plan, oracle_route, reference_ids,
+                   select, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -37,6 +37,10 @@ FACT = {
         name="fact_bf16_d1024_e32_m4_h256_top6", d=1024, n_experts=32, top_k=6, d_ff=256,
         n_depts=4, d_ff_dept=256, d_ff_shared=256, dept_form="factorised", score="sigmoid",
         bias_range=0.1, batches=(1, 5, 20)),
+    # department-limited routing (each token within k_dept = 2 of 4 departments)
+    "fact_bf16_d1024_e32_m4_h256_top6_kd2": moe_synth.LayerShape(
+        name="fact_bf16_d1024_e32_m4_h256_top6_kd2", d=1024, n_experts=32, top_k=6, d_ff=256,
+        n_depts=4, d_ff_dept=256, dept_form="factorised", k_dept=2, batches=(1, 5, 20)),
 }
 SH = {**moe_synth.SHAPES, **FACT}
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")
@@ -75,7 +79,7 @@ def run_route(desc, x, w, T, with_sel=True):
     return ids.cpu().numpy(), tw.cpu().numpy().astype(np.float64), (None if sel is None else sel.cpu().numpy())
 
 
-@pytest.mark.parametrize("name", [TINY, QWEN, DSV3, DEA7, DEAV3])
+@pytest.mark.parametrize("name", [TINY, QWEN, DSV3, DEA7, DEAV3, PAPER])
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_route_parity(name, seed):
     shape = SH[name]
@@ -89,12 +93,13 @@ def test_route_parity(name, seed):
         x = xall[:T].contiguous()
         g_ids, g_w, g_sel = run_route(desc, x, w, T)
         # selection on the GPU's own scores is exact: same ids, same slot order
-        assert np.array_equal(O.topk_select(g_sel, shape.top_k), g_ids)
+        assert np.array_equal(select(g_sel, shape), g_ids)
         # the scores agree with the oracle's to tau
         o_sel = o_sel_all[:T]
         tol = TAU * np.maximum(1.0, np.abs(o_sel))
         assert np.all(np.abs(g_sel.astype(np.float64) - o_sel) <= tol)
-        ids, near = reference_ids(o_ids_all[:T], o_sel, g_ids, shape.top_k)
+        ids, near = reference_ids(o_ids_all[:T], o_sel, g_ids, shape.top_k,
+                                  shape.n_depts, shape.k_dept)
         near_total += int(near.sum())
         # weights of the selected experts, from the oracle's logits
         o_w = O.routing_weights(o_l32[:T], g_ids, shape.score, shape.renormalize, shape.route_scale)
@@ -148,6 +153,75 @@ def test_route_ties_go_to_lower_index(score, dtype, d, T, E):
         g_ids, g_w, _ = run_route(desc, x.to(DEV), w0, T)
         assert g_ids.tolist() == [[17, 61, 60, 5, 90, 33]] * T
         np.testing.assert_allclose(g_w, 1.0 / k, atol=1e-6)
+
+
+@pytest.mark.parametrize("score,dtype,d,T,E,m,k,kd", [
+    ("softmax", "f32", 264, 5, 96, 8, 6, 2), ("sigmoid", "f32", 264, 7, 96, 4, 6, 1),
+    ("softmax_bias", "bf16", 1032, 20, 96, 12, 6, 3),
+    # one expert per department: department and expert ranking coincide
+    ("softmax", "bf16", 264, 5, 64, 64, 4, 5),
+    # k fills the chosen departments exactly
+    ("sigmoid", "bf16", 2056, 20, 330, 22, 30, 2),
+    ("softmax", "bf16", 7168, 16, 864, 8, 10, 5)])
+def test_route_grouped_parity(score, dtype, d, T, E, m, k, kd):
+    """Department-limited top-k: the ids are the oracle's grouped selection of
+    the GPU's own scores (bit-exact, slot order included); every token's
+    experts lie in at most k_dept departments; the weights are those of the
+    selected logits."""
+    g = torch.Generator().manual_seed(11)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    wr = (torch.randn(E, d, generator=g) * 0.05).to(tdt)
+    x = torch.randn(T, d, generator=g).to(tdt)
+    bias = (torch.rand(E, generator=g) * 0.2 - 0.1) if score != "softmax" else None
+    desc = M.layer_desc(d, E, k, 64, score=score, dtype=dtype, max_tokens=T, n_depts=m,
+                        d_ff_dept=64, k_dept=kd)
+    w = {"w_router": wr.to(DEV), "router_bias": None if bias is None else bias.to(DEV)}
+    g_ids, g_w, g_sel = run_route(desc, x.to(DEV), w, T)
+    assert np.array_equal(O.topk_select_grouped(g_sel, k, m, kd), g_ids)
+    G = E // m
+    assert all(len({int(e) // G for e in row}) <= kd for row in g_ids)
+    o_ids, _, o_sel, o_l32 = O.route(x, wr, k, score, bias, True, 1.0, m, kd)
+    tol = TAU * np.maximum(1.0, np.abs(o_sel))
+    assert np.all(np.abs(g_sel.astype(np.float64) - o_sel) <= tol)
+    ids, _ = reference_ids(o_ids, o_sel, g_ids, k, m, kd)
+    np.testing.assert_allclose(g_w, O.routing_weights(o_l32, g_ids, score), atol=1e-5)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_route_grouped_ties(dtype):
+    """Equal department scores go to the lower department; an all-zero router
+    ties everything and gives experts 0..k-1; a bias alone picks departments
+    by their best biased expert."""
+    E, m, d, T, k, kd = 96, 8, 264, 4, 5, 2
+    G = E // m
+    g = torch.Generator().manual_seed(5)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    wr = torch.randn(E, d, generator=g) * 0.05
+    x = torch.randn(T, d, generator=g)
+    # department 6's best expert copies each token's overall best expert
+    # row set: copy a whole department, so both tie on their best score
+    wr[6 * G:7 * G] = wr[1 * G:2 * G]
+    wr, x = wr.to(tdt), x.to(tdt)
+    desc = M.layer_desc(d, E, k, 64, score="softmax_bias", dtype=dtype, max_tokens=T,
+                        n_depts=m, d_ff_dept=64, k_dept=kd)
+    w = {"w_router": wr.to(DEV), "router_bias": torch.zeros(E, device=DEV)}
+    g_ids, _, g_sel = run_route(desc, x.to(DEV), w, T)
+    assert np.array_equal(g_sel[:, G:2 * G], g_sel[:, 6 * G:7 * G])
+    assert np.array_equal(O.topk_select_grouped(g_sel, k, m, kd), g_ids)
+    for row in g_ids:
+        assert not any(6 * G <= e < 7 * G for e in row) or any(G <= e < 2 * G for e in row)
+    w0 = {"w_router": torch.zeros(E, d, dtype=tdt, device=DEV),
+          "router_bias": torch.zeros(E, device=DEV)}
+    g_ids, g_w, _ = run_route(desc, x.to(DEV), w0, T)
+    assert g_ids.tolist() == [list(range(k))] * T
+    np.testing.assert_allclose(g_w, 1.0 / k, atol=1e-6)
+    # zero logits, bias on experts of departments 7 (0.9), 3 (0.8, 0.1), 5 (0.85):
+    # departments 7 and 5 win; then their experts by bias, then the lowest index
+    b = torch.zeros(E)
+    b[7 * G + 4], b[3 * G], b[3 * G + 1], b[5 * G + 2] = 0.9, 0.8, 0.1, 0.85
+    w0["router_bias"] = b.to(DEV)
+    g_ids, _, _ = run_route(desc, x.to(DEV), w0, T)
+    assert g_ids.tolist() == [[7 * G + 4, 5 * G + 2, 5 * G, 5 * G + 1, 5 * G + 3]] * T
 
 
 def test_route_k_equals_E_and_not_renormalised():
@@ -332,10 +406,8 @@ def check_layer(name, seed, T, sample_tokens=None):
     g_plan = layer.plan(T)
     g_ids, g_w = gpu_ids_from_plan(g_plan, T, shape.top_k)
     xc = x.cpu()
-    o_ids, _, o_sel, o_l32 = O.route(xc, w["w_router"].cpu(), shape.top_k, shape.score,
-                                      None if w.get("router_bias") is None else w["router_bias"].cpu(),
-                                      shape.renormalize, shape.route_scale)
-    ids, near = reference_ids(o_ids, o_sel, g_ids, shape.top_k)
+    o_ids, _, o_sel, o_l32 = oracle_route(shape, xc, {k: v.cpu() for k, v in w.items()})
+    ids, near = reference_ids(o_ids, o_sel, g_ids, shape.top_k, shape.n_depts, shape.k_dept)
     o_w = O.routing_weights(o_l32, ids, shape.score, shape.renormalize, shape.route_scale)
     np.testing.assert_allclose(g_w, o_w, atol=1e-5)
     # the plan is the oracle's dispatch of the selected ids
@@ -348,7 +420,8 @@ def check_layer(name, seed, T, sample_tokens=None):
                     else O.layer_token_output)
     ref = np.stack([token_output(xc[t], ids[t], o_w[t], w, shape.n_experts, shape.n_depts)
                     for t in toks])
-    emax, rmax = assert_close(yg[list(toks)], ref, shape.dtype, f"{name} T={T}")
+    emax, rmax = assert_close(yg[list(toks)], ref, shape.dtype, f"{name} T={T}",
+                              TOL_FACTORISED if shape.dept_form == "factorised" else None)
     print(f"{name} seed={seed} T={T}: max|err| {emax:.3e} (max|ref| {rmax:.3e}), "
           f"active {g_plan['active'].size}, near-ties {int(near.sum())}")
     return y
