@@ -62,6 +62,14 @@ justification in the design notes):
      selection score among its experts; the k_dept best departments are
      taken (ties to the lower department index), then the k best experts
      inside them (ties to the lower expert index).
+  R19 strict department coverage (DeaMoE's appendix on enforcing k_dept
+     coverage): starting from R18's selection, while it spans fewer than
+     k_dept departments, the lowest-ranked selected expert whose department
+     keeps another selected expert leaves, and the best expert (score desc,
+     index asc) of any uncovered department enters.  Removing an expert that
+     is the last of its department would not raise the coverage, so such
+     experts are skipped; k >= k_dept makes every step possible.  The final
+     slots are ordered by (score desc, index asc) like every selection.
 """
 from __future__ import annotations
 
@@ -76,7 +84,7 @@ __all__ = [
     "dept_layer_factored", "layer_token_output", "loaded_weight_bytes",
     "deamoe_expert", "deamoe_token_output", "deamoe_layer_per_expert",
     "deamoe_layer_two_stage", "deamoe_layer_precombined",
-    "select_from_scores", "topk_select_grouped", "silu", "cast_output", "SOFTMAX", "SIGMOID",
+    "select_from_scores", "topk_select_grouped", "topk_select_strict", "silu", "cast_output", "SOFTMAX", "SIGMOID",
     "SOFTMAX_BIAS",
 ]
 
@@ -161,6 +169,33 @@ def topk_select_grouped(sel: np.ndarray, k: int, n_depts: int, k_dept: int) -> n
     return ids
 
 
+def topk_select_strict(sel: np.ndarray, k: int, n_depts: int, k_dept: int) -> np.ndarray:
+    """Strict department coverage (R19): R18's selection, then swaps until
+    exactly k_dept departments are covered (needs k >= k_dept)."""
+    if k < k_dept:
+        raise ValueError("strict coverage needs k >= k_dept")
+    sel = np.asarray(sel)
+    T, E = sel.shape
+    g = E // n_depts
+    grouped = topk_select_grouped(sel, k, n_depts, k_dept)
+    ids = np.empty((T, k), dtype=np.int32)
+    for t in range(T):
+        chosen = [int(e) for e in grouped[t]]      # in rank order
+        covered = {e // g for e in chosen}
+        while len(covered) < k_dept:
+            candidates = [e for e in range(E) if e // g not in covered]
+            enter = min(candidates, key=lambda e: (-float(sel[t, e]), e))
+            for pos in range(len(chosen) - 1, -1, -1):
+                dept = chosen[pos] // g
+                if sum(1 for e in chosen if e // g == dept) >= 2:
+                    del chosen[pos]
+                    break
+            chosen.append(enter)
+            covered.add(enter // g)
+        ids[t] = sorted(chosen, key=lambda e: (-float(sel[t, e]), e))
+    return ids
+
+
 def routing_weights(l32: np.ndarray, ids: np.ndarray, score_fn: str,
                     renormalize: bool = True, route_scale: float = 1.0) -> np.ndarray:
     """Per-slot weights p_i of Eq. (3), in fp64.
@@ -191,13 +226,18 @@ def routing_weights(l32: np.ndarray, ids: np.ndarray, score_fn: str,
 
 def route(x, w_router, k: int, score_fn: str = SOFTMAX, bias=None,
           renormalize: bool = True, route_scale: float = 1.0, n_depts: int = 0,
-          k_dept: int = 0):
+          k_dept: int = 0, strict: bool = False):
     """Router of one decode step: (ids int32[T][k], weights f64[T][k],
     selection scores f32[T][E], logits f32[T][E]).  k_dept > 0 limits each
-    token to k_dept departments (R18)."""
+    token to k_dept departments (R18); strict makes it exactly k_dept (R19)."""
     l32 = router_logits(x, w_router)
     sel = selection_scores(l32, score_fn, bias)
-    ids = topk_select_grouped(sel, k, n_depts, k_dept) if k_dept else topk_select(sel, k)
+    if strict:
+        ids = topk_select_strict(sel, k, n_depts, k_dept)
+    elif k_dept:
+        ids = topk_select_grouped(sel, k, n_depts, k_dept)
+    else:
+        ids = topk_select(sel, k)
     w = routing_weights(l32, ids, score_fn, renormalize, route_scale)
     return ids, w, sel, l32
 

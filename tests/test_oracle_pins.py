@@ -563,3 +563,82 @@ def test_grouped_topk_properties(seed):
             pool = [e for e in range(E) if e // g in best]
             want = sorted(pool, key=lambda e: (-sel[t, e], e))[:k]
             assert ids[t].tolist() == want
+
+
+# ---------------------------------------------------------------------------
+# Strict department coverage (DeaMoE appendix: enforcing k_dept coverage)
+# ---------------------------------------------------------------------------
+
+def test_strict_coverage_hand_example():
+    """12 experts in 3 departments of 4, k = 4, k_dept = 3.  The top 4 are
+    experts 0, 1, 2 (department 0) and 4 (department 1), two departments.
+    Department 2's best, expert 8 (0.6), enters; the lowest-ranked expert,
+    4, is the only one of department 1 and stays, so 2 leaves."""
+    sel = np.array([[0.9, 0.85, 0.8, 0.1, 0.7, 0.2, 0.1, 0.0, 0.6, 0.5, 0.3, 0.2]],
+                   np.float32)
+    assert O.topk_select_grouped(sel, 4, 3, 3).tolist() == [[0, 1, 2, 4]]
+    assert O.topk_select_strict(sel, 4, 3, 3).tolist() == [[0, 1, 4, 8]]
+    # k_dept = 2: departments 0 and 1 are chosen and already covered
+    assert O.topk_select_strict(sel, 4, 3, 2).tolist() == [[0, 1, 2, 4]]
+    # k = 3, k_dept = 2: the top 3 lie in department 0 alone; department
+    # 1's best (4), not department 2's, enters in place of expert 2
+    assert O.topk_select_grouped(sel, 3, 3, 2).tolist() == [[0, 1, 2]]
+    assert O.topk_select_strict(sel, 3, 3, 2).tolist() == [[0, 1, 4]]
+    # k = k_dept = 3: one expert per department
+    assert O.topk_select_strict(sel, 3, 3, 3).tolist() == [[0, 4, 8]]
+    with pytest.raises(ValueError):
+        O.topk_select_strict(sel, 2, 3, 3)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_strict_coverage_properties(seed):
+    """Random scores with few departments per token: exactly k_dept departments
+    are covered, all among R18's chosen departments; the result equals R18's
+    whenever that already covers k_dept; otherwise k - (k_dept - covered) of
+    R18's experts stay, the highest ranked of each department among them, and
+    each entering expert is the best of its department; slots are in
+    (score desc, index asc) order."""
+    rng = _rng(600 + seed)
+    E, m, T = 48, 4, 40
+    g = E // m
+    sel = rng.normal(0, 1, (T, E)).astype(np.float32)
+    swaps = 0
+    for k, kd in ((6, 3), (4, 4), (5, 2), (3, 3)):
+        grouped = O.topk_select_grouped(sel, k, m, kd)
+        strict = O.topk_select_strict(sel, k, m, kd)
+        for t in range(T):
+            s_row, g_row = strict[t].tolist(), grouped[t].tolist()
+            dscore = sel[t].reshape(m, g).max(axis=1)
+            chosen = sorted(range(m), key=lambda j: (-dscore[j], j))[:kd]
+            assert {e // g for e in s_row} == set(chosen)
+            assert s_row == sorted(s_row, key=lambda e: (-sel[t, e], e))
+            cov = len({e // g for e in g_row})
+            if cov == kd:
+                assert s_row == g_row
+                continue
+            swaps += 1
+            kept = [e for e in g_row if e in s_row]
+            assert len(kept) == k - (kd - cov)
+            # removal runs from the bottom of the ranking, so the kept
+            # experts are R18's top ones once per-department leaders count
+            leaders = {min((e for e in g_row if e // g == j), key=g_row.index)
+                       for j in {e // g for e in g_row}}
+            assert leaders <= set(kept)
+            for e in set(s_row) - set(g_row):
+                assert sel[t, e] == dscore[e // g]
+                assert e == (e // g) * g + int(np.argmax(sel[t, (e // g) * g:(e // g + 1) * g]))
+    assert swaps > 0
+
+
+def test_strict_coverage_route_weights():
+    """Through route(): the weights are the renormalised softmax of the final
+    selection's logits and sum to route_scale."""
+    rng = _rng(700)
+    E, m, d, T, k, kd = 32, 4, 16, 6, 4, 3
+    x = rng.normal(0, 1, (T, d)).astype(np.float32)
+    wr = rng.normal(0, 0.5, (E, d)).astype(np.float32)
+    ids, w, sel, l32 = O.route(x, wr, k, O.SOFTMAX, None, True, 1.0, m, kd, strict=True)
+    assert np.array_equal(ids, O.topk_select_strict(sel, k, m, kd))
+    for t in range(T):
+        e = np.exp(l32[t, ids[t]].astype(np.float64) - l32[t, ids[t]].max())
+        np.testing.assert_allclose(w[t], e / e.sum(), rtol=1e-12)
