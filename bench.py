@@ -223,7 +223,8 @@ def desc_of(M, shape, max_tokens):
                         d_ff_dept=shape.d_ff_dept, d_ff_shared=shape.d_ff_shared,
                         score=shape.score, renormalize=shape.renormalize,
                         route_scale=shape.route_scale, dtype=shape.dtype, max_tokens=max_tokens,
-                        dept_form=shape.dept_form, k_dept=shape.k_dept)
+                        dept_form=shape.dept_form, k_dept=shape.k_dept,
+                        dept_strict=shape.dept_strict)
 
 
 def gateup_bytes(shape, T, n_active, n_active_depts, n_rows, n_dept_rows):
@@ -500,7 +501,7 @@ def cpu_baseline(shape, T, base, seconds):
     while True:
         ids, w, _, _ = O.route(x, host["w_router"], shape.top_k, shape.score,
                                host.get("router_bias"), shape.renormalize, shape.route_scale,
-                               shape.n_depts, shape.k_dept)
+                               shape.n_depts, shape.k_dept, shape.dept_strict)
         token_output = (O.deamoe_token_output if shape.dept_form == "factorised"
                         else O.layer_token_output)
         for t in range(T):

@@ -127,6 +127,13 @@ typedef struct {
                           * index), the k_dept best kept, then the top k inside them.
                           * 1 <= k_dept <= n_depts <= MOE_MAX_DEPTS_GROUPED,
                           * top_k <= k_dept * (E / n_depts). */
+  int32_t dept_strict;   /* 0 or 1.  1: exactly k_dept departments per token (DeaMoE's
+                          * appendix on enforcing k_dept coverage): after the top k above,
+                          * while fewer than k_dept departments are covered, the
+                          * lowest-ranked chosen expert whose department keeps another
+                          * chosen expert gives way to the best expert of the best
+                          * uncovered department; slots stay in (score desc, index asc)
+                          * order.  Requires k_dept >= 1 and top_k >= k_dept. */
 } moe_layer_desc;
 
 typedef struct {

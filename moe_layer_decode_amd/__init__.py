@@ -50,7 +50,7 @@ class LayerDesc(ctypes.Structure):
                 ("n_depts", _i32), ("d_ff_dept", _i32), ("d_ff_shared", _i32),
                 ("score_fn", _i32), ("renormalize", _i32), ("route_scale", _f32),
                 ("w_dtype", _i32), ("act_dtype", _i32), ("max_tokens", _i32),
-                ("dept_form", _i32), ("k_dept", _i32)]
+                ("dept_form", _i32), ("k_dept", _i32), ("dept_strict", _i32)]
 
     @property
     def torch_dtype(self):
@@ -150,11 +150,12 @@ def _check(status: int, call: str):
 def layer_desc(d_model: int, n_experts: int, top_k: int, d_ff: int, *, n_depts: int = 0,
                d_ff_dept: int = 0, d_ff_shared: int = 0, score: str = "softmax",
                renormalize: bool = True, route_scale: float = 1.0, dtype: str = "bf16",
-               max_tokens: int = 32, dept_form: str = "slice", k_dept: int = 0) -> LayerDesc:
+               max_tokens: int = 32, dept_form: str = "slice", k_dept: int = 0,
+               dept_strict: bool = False) -> LayerDesc:
     dt = MOE_BF16 if dtype == "bf16" else MOE_F32
     return LayerDesc(d_model, n_experts, top_k, d_ff, n_depts, d_ff_dept, d_ff_shared,
                      SCORE_FNS[score], int(bool(renormalize)), float(route_scale), dt, dt,
-                     max_tokens, DEPT_FORMS[dept_form], k_dept)
+                     max_tokens, DEPT_FORMS[dept_form], k_dept, int(dept_strict))
 
 
 def moe_validate_desc(desc: LayerDesc) -> int:

@@ -125,6 +125,9 @@ moe_status check_desc(const moe_layer_desc* d) {
   if (d->k_dept > 0 && (int64_t)d->k_dept * (d->n_experts / d->n_depts) < d->top_k)
     return MOE_ERR_INVALID_ARG;  // not enough experts in k_dept departments
   if (d->k_dept > 0 && d->n_depts > MOE_MAX_DEPTS_GROUPED) return MOE_ERR_UNSUPPORTED;
+  if (d->dept_strict != 0 && d->dept_strict != 1) return MOE_ERR_INVALID_ARG;
+  if (d->dept_strict && (d->k_dept < 1 || d->top_k < d->k_dept))
+    return MOE_ERR_INVALID_ARG;  // exact coverage needs a cap and k >= k_dept
   if (d->score_fn < MOE_SCORE_SOFTMAX || d->score_fn > MOE_SCORE_SOFTMAX_BIAS)
     return MOE_ERR_INVALID_ARG;
   if (d->renormalize != 0 && d->renormalize != 1) return MOE_ERR_INVALID_ARG;
@@ -232,6 +235,7 @@ moe::RouteArgs route_args(const moe_layer_desc& d, void* ws, const void* x, cons
   ra.ksplit = route_ksplit(d);
   ra.m = d.n_depts;
   ra.k_dept = d.k_dept;
+  ra.strict = d.dept_strict;
   ra.logits = at<float>(ws, L, R_LOGITS);
   ra.ids_out = ids;
   ra.w_out = w;

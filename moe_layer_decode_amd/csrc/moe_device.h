@@ -63,6 +63,14 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
   return v;
 }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t u = (uint32_t)__shfl_xor((int)v, o, kWave);
+    v = u > v ? u : v;
+  }
+  return v;
+}
 
 template <int N> struct Log2 { static constexpr int value = 1 + Log2<N / 2>::value; };
 template <> struct Log2<1> { static constexpr int value = 0; };

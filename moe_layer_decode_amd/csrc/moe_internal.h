@@ -51,7 +51,8 @@ struct RouteArgs {
   int T, d, E, k;
   int score_fn, renorm;
   float scale;
-  int m, k_dept;           // department-limited top-k when 0 < k_dept < m
+  int m, k_dept;           // department-limited top-k when 0 < k_dept < m (or strict)
+  int strict;              // 1: exactly k_dept departments per token
   int n_chunks;            // ceil(d / kRouteChunk)
   int ksplit;              // partial-logit planes: logits holds [ksplit][T][E], summed in order
   float* logits;           // [ksplit][T][E]

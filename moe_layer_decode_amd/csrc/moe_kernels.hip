@@ -225,19 +225,21 @@ __device__ void topk_one(const RouteArgs& p, int t, int lane, PlanShared& s) {
     }
   }
   const int k = p.k;
+  // department of expert e = floor((e + 0.5) / G) in fp32: exact, since
+  // e < 2048 and the quotient is below m <= 64, so the rounding error
+  // (under 64 * 2^-23) stays inside the 0.5 / G margin to each integer
+  const float inv_g = GROUPED ? 1.0f / (float)(p.E / p.m) : 0.f;
+  auto dept_of = [&](int e) { return (unsigned)(((float)e + 0.5f) * inv_g); };
+  unsigned* dm = s.dmax[threadIdx.x >> 6];
+  uint32_t dkey = 0u;           // lane J: department J's key
+  uint64_t chosen_depts = 0ull; // bit J: department J chosen
   if (GROUPED) {
     // Department-limited top-k: a department's key is its best expert's key
     // (LDS max, one area per wave); the k_dept best departments are chosen
     // like experts below (lane J holds department J; ties to the lower
     // index) and the experts of every other department drop to key 0, below
     // every real score.
-    const int G = p.E / p.m, wid = threadIdx.x >> 6, kd = p.k_dept;
-    // department of expert e = floor((e + 0.5) / G) in fp32: exact, since
-    // e < 2048 and the quotient is below m <= 64, so the rounding error
-    // (under 64 * 2^-23) stays inside the 0.5 / G margin to each integer
-    const float inv_g = 1.0f / (float)G;
-    auto dept_of = [&](int e) { return (unsigned)(((float)e + 0.5f) * inv_g); };
-    unsigned* dm = s.dmax[wid];
+    const int kd = p.k_dept;
     if (lane < p.m) dm[lane] = 0u;
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -248,7 +250,7 @@ __device__ void topk_one(const RouteArgs& p, int t, int lane, PlanShared& s) {
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    const uint32_t dkey = lane < p.m ? dm[lane] : 0u;
+    dkey = lane < p.m ? dm[lane] : 0u;
     uint32_t dthr = 0u;
     for (int b = 31; b >= 0; --b) {
       const uint32_t c = dthr | (1u << b);
@@ -259,7 +261,7 @@ __device__ void topk_one(const RouteArgs& p, int t, int lane, PlanShared& s) {
     const bool dtake = lane < p.m && (dkey > dthr ||
                                       (dkey == dthr && __popcll(deq & ((1ull << lane) - 1ull)) <
                                                            kd - dabove));
-    const uint64_t chosen_depts = __ballot(dtake);
+    chosen_depts = __ballot(dtake);
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
       const int e = lane + kWave * i;
@@ -322,6 +324,77 @@ __device__ void topk_one(const RouteArgs& p, int t, int lane, PlanShared& s) {
   if (lane < k) {
     my_id = slot_id[lane];
     my_aux = slot_aux[lane];
+  }
+  if (GROUPED && p.strict) {
+    // Strict department coverage: while the k chosen experts (lane j holds
+    // rank j) span fewer than k_dept departments, the lowest-ranked one
+    // whose department keeps another chosen expert leaves and the best
+    // expert of the best uncovered department enters.  Uncovered departments
+    // are all among the chosen ones, and an entering expert ranks below
+    // every kept one and below those entering before it, so the new order
+    // is the kept experts in rank order followed by the entering ones.
+    const unsigned my_dept = lane < k ? dept_of(my_id) : 0u;
+    if (lane < p.m) dm[lane] = 0u;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (lane < k) atomicAdd(&dm[my_dept], 1u);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    int cnt = lane < k ? (int)dm[my_dept] : 0;  // chosen experts in my department
+    uint64_t uncov = chosen_depts & ~__ballot(lane < p.m && dm[lane] > 0u);
+    const int n_in = __popcll(uncov);
+    if (n_in > 0) {
+      bool removed = false;
+      int in_id = -1;
+      float in_aux = 0.f;
+      for (int it = 0; it < n_in; ++it) {
+        // best uncovered department: largest key, then lowest index
+        const bool cand = (uncov >> lane) & 1ull;
+        const uint32_t best = wave_max_u32(cand ? dkey : 0u);
+        const int u = __builtin_ctzll(__ballot(cand && dkey == best));
+        // its best expert: the lowest index holding the department's key
+        int e_in = -1;
+        float l_in = 0.f;
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) {
+          const int e = lane + kWave * i;
+          const uint64_t b = __ballot(e < p.E && dept_of(e) == (unsigned)u && key[i] == best);
+          if (e_in < 0 && b) {
+            const int l = __builtin_ctzll(b);
+            e_in = l + kWave * i;
+            l_in = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lg[i]), l));
+          }
+        }
+        const uint64_t elig = __ballot(lane < k && !removed && cnt >= 2);
+        if (e_in < 0 || !elig) break;  // neither happens when k >= k_dept
+        const int r = 63 - __builtin_clzll(elig);
+        const unsigned dr = (unsigned)__builtin_amdgcn_readlane((int)my_dept, r);
+        if (lane < k && !removed && my_dept == dr) --cnt;
+        if (lane == r) removed = true;
+        if (lane == it) {
+          in_id = e_in;
+          in_aux = route_aux(p, l_in);
+        }
+        uncov &= ~(1ull << u);
+      }
+      const uint64_t rem = __ballot(lane < k && removed);
+      const int n_rem = __popcll(rem);
+      if (lane < k && !removed) {
+        const int j = lane - __popcll(rem & below_me);
+        slot_id[j] = my_id;
+        slot_aux[j] = my_aux;
+      }
+      if (lane < n_rem) {
+        slot_id[k - n_rem + lane] = in_id;
+        slot_aux[k - n_rem + lane] = in_aux;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      if (lane < k) {
+        my_id = slot_id[lane];
+        my_aux = slot_aux[lane];
+      }
+    }
   }
   const bool mine = lane < p.k;
   float w;
@@ -1738,8 +1811,9 @@ static hipError_t launch_route_t(const RouteArgs& ra, const PlanArgs* pa, hipStr
   const int do_plan = pa != nullptr;
   const dim3 grid(1), block(kPlanThreads);
   const KernelEvents* ev2 = ev ? ev + 1 : nullptr;
-  // department-limited top-k only where the cap binds (its own instances)
-  const bool grouped = ra.k_dept > 0 && ra.k_dept < ra.m;
+  // department-limited top-k only where the cap binds or coverage is
+  // enforced (its own instances)
+  const bool grouped = ra.k_dept > 0 && (ra.k_dept < ra.m || ra.strict);
 #define MOE_TOPK(N)                                                               \
   (grouped ? launch(topk_plan_kernel<N, true>, grid, block, st, ev2, ra, p, do_plan) \
            : launch(topk_plan_kernel<N, false>, grid, block, st, ev2, ra, p, do_plan))

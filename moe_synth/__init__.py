@@ -64,6 +64,7 @@ class LayerShape:
     dept_form: str = "slice"       # "slice" | "factorised" (private S x S transforms)
     a_std: float = 0.02            # factorised: private transforms = I + N(0, a_std)
     k_dept: int = 0                # department-limited top-k cap (0 = none)
+    dept_strict: bool = False      # exactly k_dept departments per token
     x_std: float = 1.0
     w_std: float = 0.02
     bias_range: float = 0.0        # U(-r, r) selection bias when > 0

@@ -26,7 +26,8 @@ def desc_of(shape: moe_synth.LayerShape, max_tokens: int = None, **over) -> M.La
     kw = dict(n_depts=shape.n_depts, d_ff_dept=shape.d_ff_dept, d_ff_shared=shape.d_ff_shared,
               score=shape.score, renormalize=shape.renormalize, route_scale=shape.route_scale,
               dtype=shape.dtype, max_tokens=max_tokens or max(shape.batches),
-              dept_form=shape.dept_form, k_dept=shape.k_dept)
+              dept_form=shape.dept_form, k_dept=shape.k_dept,
+              dept_strict=shape.dept_strict)
     kw.update(over)
     return M.layer_desc(shape.d, shape.n_experts, shape.top_k, shape.d_ff, **kw)
 
@@ -37,12 +38,15 @@ def to_np(t: torch.Tensor) -> np.ndarray:
 
 def oracle_route(shape, x, w, k=None):
     return O.route(x, w["w_router"], k or shape.top_k, shape.score, w.get("router_bias"),
-                   shape.renormalize, shape.route_scale, shape.n_depts, shape.k_dept)
+                   shape.renormalize, shape.route_scale, shape.n_depts, shape.k_dept,
+                   shape.dept_strict)
 
 
 def select(sel: np.ndarray, shape, k=None) -> np.ndarray:
     """The oracle's selection rule of this layer shape applied to given scores."""
     k = k or shape.top_k
+    if shape.dept_strict:
+        return O.topk_select_strict(sel, k, shape.n_depts, shape.k_dept)
     if shape.k_dept:
         return O.topk_select_grouped(sel, k, shape.n_depts, shape.k_dept)
     return O.topk_select(sel, k)

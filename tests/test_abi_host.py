@@ -84,6 +84,12 @@ def _desc(**kw):
     (dict(n_depts=64, d_ff_dept=128, top_k=3, k_dept=1), M.MOE_ERR_INVALID_ARG),  # 3 > 1 * 2
     (dict(n_experts=256, n_depts=128, d_ff_dept=128, top_k=2, k_dept=2),
      M.MOE_ERR_UNSUPPORTED),                                               # > 64 departments
+    # strict department coverage
+    (dict(n_depts=8, d_ff_dept=1024, k_dept=3, dept_strict=True), M.MOE_OK),
+    (dict(n_depts=8, d_ff_dept=1024, k_dept=8, dept_strict=True), M.MOE_OK),  # k = k_dept
+    (dict(n_depts=8, d_ff_dept=1024, dept_strict=True), M.MOE_ERR_INVALID_ARG),  # no cap
+    (dict(n_depts=8, d_ff_dept=1024, top_k=2, k_dept=3, dept_strict=True),
+     M.MOE_ERR_INVALID_ARG),                                               # k < k_dept
 ])
 def test_descriptor_validation(lib, kw, status):
     assert M.moe_validate_desc(_desc(**kw)) == status

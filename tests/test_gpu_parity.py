@@ -41,6 +41,11 @@ FACT = {
     "fact_bf16_d1024_e32_m4_h256_top6_kd2": moe_synth.LayerShape(
         name="fact_bf16_d1024_e32_m4_h256_top6_kd2", d=1024, n_experts=32, top_k=6, d_ff=256,
         n_depts=4, d_ff_dept=256, dept_form="factorised", k_dept=2, batches=(1, 5, 20)),
+    # ... and exactly k_dept = 3 departments per token (strict coverage)
+    "fact_bf16_d1024_e32_m4_h256_top6_kd3s": moe_synth.LayerShape(
+        name="fact_bf16_d1024_e32_m4_h256_top6_kd3s", d=1024, n_experts=32, top_k=6, d_ff=256,
+        n_depts=4, d_ff_dept=256, dept_form="factorised", k_dept=3, dept_strict=True,
+        score="softmax_bias", bias_range=0.1, batches=(1, 5, 20)),
 }
 SH = {**moe_synth.SHAPES, **FACT}
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")
@@ -185,6 +190,50 @@ def test_route_grouped_parity(score, dtype, d, T, E, m, k, kd):
     assert np.all(np.abs(g_sel.astype(np.float64) - o_sel) <= tol)
     ids, _ = reference_ids(o_ids, o_sel, g_ids, k, m, kd)
     np.testing.assert_allclose(g_w, O.routing_weights(o_l32, g_ids, score), atol=1e-5)
+
+
+@pytest.mark.parametrize("score,dtype,d,T,E,m,k,kd", [
+    ("softmax", "f32", 264, 9, 96, 4, 6, 3), ("sigmoid", "bf16", 1032, 20, 96, 4, 6, 4),
+    ("softmax_bias", "bf16", 264, 20, 128, 8, 5, 5),
+    # many departments: the paper's shape, and one expert per department
+    ("softmax", "bf16", 7168, 16, 864, 8, 10, 5), ("softmax", "bf16", 264, 5, 64, 64, 6, 6)])
+def test_route_strict_parity(score, dtype, d, T, E, m, k, kd):
+    """Strict department coverage: the ids are the oracle's strict selection
+    of the GPU's own scores (bit-exact, slot order included), every token
+    covers exactly k_dept departments, and the weights are those of the
+    final selection's logits."""
+    g = torch.Generator().manual_seed(13)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    wr = (torch.randn(E, d, generator=g) * 0.05).to(tdt)
+    x = torch.randn(T, d, generator=g).to(tdt)
+    bias = (torch.rand(E, generator=g) * 0.2 - 0.1) if score != "softmax" else None
+    desc = M.layer_desc(d, E, k, 64, score=score, dtype=dtype, max_tokens=T, n_depts=m,
+                        d_ff_dept=64, k_dept=kd, dept_strict=True)
+    w = {"w_router": wr.to(DEV), "router_bias": None if bias is None else bias.to(DEV)}
+    g_ids, g_w, g_sel = run_route(desc, x.to(DEV), w, T)
+    assert np.array_equal(O.topk_select_strict(g_sel, k, m, kd), g_ids)
+    G = E // m
+    assert all(len({int(e) // G for e in row}) == kd for row in g_ids)
+    swaps = int((O.topk_select_grouped(g_sel, k, m, kd) != g_ids).any(axis=1).sum())
+    o_ids, _, o_sel, o_l32 = O.route(x, wr, k, score, bias, True, 1.0, m, kd, strict=True)
+    tol = TAU * np.maximum(1.0, np.abs(o_sel))
+    assert np.all(np.abs(g_sel.astype(np.float64) - o_sel) <= tol)
+    np.testing.assert_allclose(g_w, O.routing_weights(o_l32, g_ids, score), atol=1e-5)
+    print(f"strict E={E} m={m} k={k} k_dept={kd}: {swaps} of {T} tokens swapped")
+
+
+def test_route_strict_all_ties():
+    """An all-zero router ties everything: departments 0..2 are chosen, the
+    top 6 are experts 0..5 of department 0 alone, and the strict swaps bring
+    in experts 24 and 48 in place of 5 and 4."""
+    E, m, d, T, k, kd = 96, 4, 264, 3, 6, 3
+    desc = M.layer_desc(d, E, k, 64, dtype="bf16", max_tokens=T, n_depts=m, d_ff_dept=64,
+                        k_dept=kd, dept_strict=True)
+    x = torch.randn(T, d, generator=torch.Generator().manual_seed(2)).to(torch.bfloat16)
+    w0 = {"w_router": torch.zeros(E, d, dtype=torch.bfloat16, device=DEV)}
+    g_ids, g_w, _ = run_route(desc, x.to(DEV), w0, T)
+    assert g_ids.tolist() == [[0, 1, 2, 3, 24, 48]] * T
+    np.testing.assert_allclose(g_w, 1.0 / k, atol=1e-6)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
