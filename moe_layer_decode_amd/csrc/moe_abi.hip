@@ -41,13 +41,13 @@ size_t n_counters(const moe_layer_desc& d) { return 16 + (size_t)ceil_div(d.d_mo
 int n_route_chunks(const moe_layer_desc& d) { return ceil_div(d.d_model, moe::kRouteChunk); }
 
 // K pieces of the bf16 router: enough (16-expert tile, piece) blocks to reach
-// about 128 blocks, no more partial planes than the top-k reads for this many
-// experts, and at least 64 elements of K per wave.  fp32 layers use one plane.
+// about 512 blocks, at most kMaxRouteSplit partial planes, and at least 64
+// elements of K per wave.  fp32 layers use one plane.
 int route_ksplit(const moe_layer_desc& d) {
   if (d.w_dtype != MOE_BF16) return 1;
   const int tiles = ceil_div(d.n_experts, 16);
-  int s = ceil_div(128, tiles);
-  if (s > moe::route_split_max(d.n_experts)) s = moe::route_split_max(d.n_experts);
+  int s = ceil_div(512, tiles);
+  if (s > moe::kMaxRouteSplit) s = moe::kMaxRouteSplit;
   const int kmax = d.d_model / (moe::kWaves * 64);
   if (s > kmax) s = kmax;
   return s < 1 ? 1 : s;

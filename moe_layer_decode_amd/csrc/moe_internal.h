@@ -15,11 +15,6 @@ constexpr int kRouteChunk = 512;     // d elements one router wave covers (64 la
 constexpr int kTokInline = 4;        // tokens carried inline in a work descriptor
 constexpr int kPlanThreads = 1024;   // threads of the single-block top-k / plan kernel
 constexpr int kMaxRouteSplit = 8;   // partial-logit planes of the bf16 router at most
-// Planes the top-k reads for up to n_experts experts: fewer as each lane holds
-// more experts, so the unrolled loads stay within registers.
-constexpr int route_split_max(int n_experts) {
-  return n_experts <= 256 ? kMaxRouteSplit : n_experts <= 512 ? 4 : n_experts <= 1024 ? 2 : 1;
-}
 constexpr int kMaxParts = 6;         // 3 matrix families x (small groups, large groups)
 // Plan header entries beyond the public ones: lengths of the compacted work
 // lists of small (<= kTokInline rows) and large groups.

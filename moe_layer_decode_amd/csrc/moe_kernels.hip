@@ -153,16 +153,37 @@ __device__ __forceinline__ void group_reduce_scatter(float (&v)[N], int lane) {
 // ---------------------------------------------------------------------------
 // Routing + plan
 // ---------------------------------------------------------------------------
+// Top-k staging: a chunk of tokens' router logits and selection keys in LDS
+// (entry j = (t - t0) * E + e), filled by the whole block, then read by the
+// token's wave.
+constexpr int kTopkBuf = 10240;   // staged (token, expert) entries per chunk
+constexpr int kCand = 128;        // compacted candidates per token
+constexpr int kPlanWaves = kPlanThreads / kWave;
+struct TopkStage {
+  float lg[kTopkBuf];
+  uint32_t key[kTopkBuf];
+  uint32_t cand_key[kPlanWaves][kCand];
+  int cand_e[kPlanWaves][kCand];
+  unsigned dmax[kPlanWaves][MOE_MAX_DEPTS_GROUPED];  // per wave: department keys / counts
+};
+// Plan-only arrays (used once every token is routed).
+struct PlanWork {
+  int off[MOE_MAX_EXPERTS + 1];           // experts: first row
+  int slot[MOE_MAX_EXPERTS];              //          index in the small / large work list
+  int doff[MOE_MAX_EXPERTS + 1];          // departments (m <= E): first pair
+  int dslot[MOE_MAX_EXPERTS];
+  int dcnt[MOE_MAX_EXPERTS];
+  int tot[kPlanWaves][4];                 // per wave: rows, active, small
+};
 struct PlanShared {
-  int ids[MOE_MAX_ASSIGNMENTS];
-  float w[MOE_MAX_ASSIGNMENTS];
-  int cnt[MOE_MAX_EXPERTS];
-  int off[MOE_MAX_EXPERTS + 1];
-  int slot[MOE_MAX_EXPERTS];
-  int eslot[MOE_MAX_EXPERTS];             // expert's slot, kept past the department pass
-  short arank[MOE_MAX_ASSIGNMENTS];       // assignment's rank inside its expert group
-  unsigned char flag[MOE_MAX_DEPT_PAIRS];
-  unsigned dmax[kPlanThreads / kWave][MOE_MAX_DEPTS_GROUPED];  // per wave: department best keys
+  int ids[MOE_MAX_ASSIGNMENTS];           // chosen experts, t*k + slot
+  float w[MOE_MAX_ASSIGNMENTS];           // their weights
+  int cnt[MOE_MAX_EXPERTS];               // assignments per expert
+  unsigned char flag[MOE_MAX_DEPT_PAIRS]; // (t, J): token t chose an expert of department J
+  union {
+    TopkStage tk;
+    PlanWork pw;
+  };
   int invalid;
 };
 
@@ -176,81 +197,159 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 
 __device__ __forceinline__ int wave_count(bool b) { return __popcll(__ballot(b)); }
 
-// Top-k of token t by one wave; lane l holds experts l, l+64, ... (expert
-// e = l + 64 i in plane i).  Selection is a radix select on the score keys:
-// 32 ballot rounds find the k-th largest key; among experts tied at that key
-// the lowest indices are taken.  The chosen k are then ranked by (score desc,
-// index asc) -- each compares itself with the other k-1 -- and the expert of
-// rank j is handed to lane j through LDS.
 // Value the routing weights start from: the sigmoid affinity in sigmoid mode,
 // else the logit.
 __device__ __forceinline__ float route_aux(const RouteArgs& p, float l) {
   return p.score_fn == MOE_SCORE_SIGMOID ? 1.0f / (1.0f + expf(-l)) : l;
 }
 
-template <int NPL, bool GROUPED>
-__device__ void topk_one(const RouteArgs& p, int t, int lane, PlanShared& s) {
-  float lg[NPL];
-  uint32_t key[NPL];
-  // partial logits of the K split, added in split order; straight-line code
-  // (planes past ksplit re-read the last plane and add nothing) so every
-  // load is issued before the first add waits
-  float bias[NPL];
+// Logits of tokens [t0, t0 + tc): the K-split partial planes added in plane
+// order (planes past ksplit add nothing), then the selection score and its
+// key, staged in LDS; the scores go to sel_out when asked for.  Each thread
+// requests NU entries' planes before the first add waits.
+template <int KS>
+__device__ void stage_scores_ks(const RouteArgs& p, int t0, int tc, PlanShared& s) {
+  constexpr int NU = KS >= 8 ? 4 : KS >= 4 ? 6 : 8;
+  const int n = tc * p.E, nth = blockDim.x, E = p.E;
+  const float* src = p.logits + (size_t)t0 * E;
+  const size_t plane = (size_t)p.T * E;
+#pragma unroll 1
+  for (int j0 = threadIdx.x; j0 < n; j0 += nth * NU) {
+    float v[NU][KS], b[NU];
 #pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    lg[i] = 0.f;
-    // requested with the logits, not after them
-    bias[i] = p.bias ? p.bias[min(lane + kWave * i, p.E - 1)] : 0.f;
-  }
+    for (int u = 0; u < NU; ++u) {
+      const int j = min(j0 + u * nth, n - 1);
 #pragma unroll
-  for (int q = 0; q < route_split_max(NPL * kWave); ++q) {
-    const float* pl = p.logits + ((size_t)min(q, p.ksplit - 1) * p.T + t) * p.E;
+      for (int q = 0; q < KS; ++q) v[u][q] = src[(size_t)min(q, p.ksplit - 1) * plane + j];
+      b[u] = p.bias ? p.bias[j % E] : 0.f;
+    }
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-      const int e = min(lane + kWave * i, p.E - 1);
-      const float v = pl[e];
-      lg[i] += q < p.ksplit ? v : 0.f;
+    for (int u = 0; u < NU; ++u) {
+      const int j = j0 + u * nth;
+      if (j < n) {
+        float l = 0.f;
+#pragma unroll
+        for (int q = 0; q < KS; ++q) l += q < p.ksplit ? v[u][q] : 0.f;
+        const float sc = p.score_fn == MOE_SCORE_SOFTMAX ? l : route_aux(p, l) + b[u];
+        if (p.sel_out) p.sel_out[(size_t)t0 * E + j] = sc;
+        s.tk.lg[j] = l;
+        s.tk.key[j] = score_key(sc);
+      }
     }
   }
+}
+
+__device__ void stage_scores(const RouteArgs& p, int t0, int tc, PlanShared& s) {
+  if (p.ksplit > 4)
+    stage_scores_ks<kMaxRouteSplit>(p, t0, tc, s);
+  else if (p.ksplit > 2)
+    stage_scores_ks<4>(p, t0, tc, s);
+  else if (p.ksplit > 1)
+    stage_scores_ks<2>(p, t0, tc, s);
+  else
+    stage_scores_ks<1>(p, t0, tc, s);
+}
+
+// Radix select of the k largest of NP planes of keys (entry i of lane l has
+// key key[i] and expert eid(i, l); planes and lanes in ascending expert
+// order): 32 ballot rounds find the k-th largest key, and among entries tied
+// at it the lowest experts are taken.  The k chosen are compacted in expert
+// order into the wave's list (ck, ce); lane j < k then ranks entry j by
+// (key desc, expert asc) against the other k - 1 and sets slot_id[rank].
+template <int NP, typename EidOf>
+__device__ __forceinline__ void select_rank(const uint32_t (&key)[NP], EidOf eid, int k, int lane,
+                                            uint32_t* ck, int* ce, int* slot_id) {
+  uint32_t thr = 0u;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = thr | (1u << b);
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) n += wave_count(key[i] >= c);
+    if (n >= k) thr = c;
+  }
+  int above = 0;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) above += wave_count(key[i] > thr);
+  const uint64_t below_me = (1ull << lane) - 1ull;
+  int eq_before = 0, base = 0;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const uint64_t eq = __ballot(key[i] == thr);
+    const int r = eq_before + __popcll(eq & below_me);
+    const bool take = key[i] > thr || (key[i] == thr && r < k - above);
+    eq_before += __popcll(eq);
+    const uint64_t tm = __ballot(take);
+    if (take) {
+      const int pos = base + __popcll(tm & below_me);
+      ck[pos] = key[i];
+      ce[pos] = eid(i, lane);
+    }
+    base += __popcll(tm);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  const uint32_t kj = lane < k ? ck[lane] : 0u;
+  const int ej = lane < k ? ce[lane] : 0;
+  int rank = 0;
+  for (int i = 0; i < k; ++i) {
+    const uint32_t k2 = (uint32_t)__builtin_amdgcn_readlane((int)kj, i);
+    const int e2 = __builtin_amdgcn_readlane(ej, i);
+    rank += (k2 > kj || (k2 == kj && e2 < ej)) ? 1 : 0;
+  }
+  if (lane < k) slot_id[rank] = ej;
+}
+
+// Top-k of token t by one wave from the staged row `row` (lane l holds experts
+// l, l+64, ...).  Every key among the k largest, ties at the k-th included,
+// is at least the k-th largest of the 64 lane maxima; those candidates (few
+// for real scores) are compacted in expert order and selected on two planes.
+// With more candidates than fit, or fewer than k, the select runs on all
+// planes.  The chosen experts are handed to lanes 0..k-1 through LDS, then the
+// weights.
+template <int NPL, bool GROUPED>
+__device__ void topk_token(const RouteArgs& p, int t, int row, int lane, PlanShared& s) {
+  const int k = p.k, E = p.E, wid = threadIdx.x >> 6;
+  const float* lgr = s.tk.lg + row;
+  uint32_t key[NPL];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int e = lane + kWave * i;
-    const float l = e < p.E ? lg[i] : 0.f;
-    lg[i] = l;
-    key[i] = 0u;
-    if (e < p.E) {
-      const float sc = p.score_fn == MOE_SCORE_SOFTMAX ? l : route_aux(p, l) + bias[i];
-      if (p.sel_out) p.sel_out[(size_t)t * p.E + e] = sc;
-      key[i] = score_key(sc);
-    }
+    key[i] = e < E ? s.tk.key[row + e] : 0u;
   }
-  const int k = p.k;
   // department of expert e = floor((e + 0.5) / G) in fp32: exact, since
   // e < 2048 and the quotient is below m <= 64, so the rounding error
   // (under 64 * 2^-23) stays inside the 0.5 / G margin to each integer
-  const float inv_g = GROUPED ? 1.0f / (float)(p.E / p.m) : 0.f;
+  const float inv_g = GROUPED ? 1.0f / (float)(E / p.m) : 0.f;
   auto dept_of = [&](int e) { return (unsigned)(((float)e + 0.5f) * inv_g); };
-  unsigned* dm = s.dmax[threadIdx.x >> 6];
+  unsigned* dm = s.tk.dmax[wid];
   uint32_t dkey = 0u;           // lane J: department J's key
   uint64_t chosen_depts = 0ull; // bit J: department J chosen
   if (GROUPED) {
     // Department-limited top-k: a department's key is its best expert's key
     // (LDS max, one area per wave); the k_dept best departments are chosen
-    // like experts below (lane J holds department J; ties to the lower
-    // index) and the experts of every other department drop to key 0, below
-    // every real score.
+    // like experts (lane J holds department J; ties to the lower index) and
+    // the experts of every other department drop to key 0, below every real
+    // score.
     const int kd = p.k_dept;
-    if (lane < p.m) dm[lane] = 0u;
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-      const int e = lane + kWave * i;
-      if (e < p.E) atomicMax(&dm[dept_of(e)], key[i]);
+    {
+      // department-major read of the staged keys: L = 64/m lanes (rounded
+      // down to a power of two) stride through each department's G keys,
+      // then a max over the L lanes; lane J takes department J's result
+      const int G = E / p.m, L = 1 << (31 - __builtin_clz(kWave / p.m));
+      const int J = lane / L, sub = lane - J * L;
+      uint32_t v = 0u;
+      if (J < p.m)
+        for (int e = J * G + sub; e < (J + 1) * G; e += L) {
+          const uint32_t u = s.tk.key[row + e];
+          v = u > v ? u : v;
+        }
+      for (int o = 1; o < L; o <<= 1) {
+        const uint32_t u = (uint32_t)__shfl_xor((int)v, o, kWave);
+        v = u > v ? u : v;
+      }
+      dkey = (uint32_t)__shfl((int)v, min(lane, p.m - 1) * L, kWave);
+      dkey = lane < p.m ? dkey : 0u;
     }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    dkey = lane < p.m ? dm[lane] : 0u;
     uint32_t dthr = 0u;
     for (int b = 31; b >= 0; --b) {
       const uint32_t c = dthr | (1u << b);
@@ -265,57 +364,59 @@ __device__ void topk_one(const RouteArgs& p, int t, int lane, PlanShared& s) {
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
       const int e = lane + kWave * i;
-      if (e < p.E && !((chosen_depts >> dept_of(e)) & 1ull)) key[i] = 0u;
+      if (e < E && !((chosen_depts >> dept_of(e)) & 1ull)) key[i] = 0u;
     }
   }
-  // largest thr with #(key >= thr) >= k: the k-th largest key
-  uint32_t thr = 0u;
+  // candidate cut: the k-th largest lane maximum (at least 1, so key-0
+  // entries never qualify)
+  uint32_t lmax = 0u;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) lmax = key[i] > lmax ? key[i] : lmax;
+  uint32_t cut = 0u;
   for (int b = 31; b >= 0; --b) {
-    const uint32_t c = thr | (1u << b);
-    int n = 0;
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) n += wave_count(key[i] >= c);
-    if (n >= k) thr = c;
+    const uint32_t c = cut | (1u << b);
+    if (wave_count(lmax >= c) >= k) cut = c;
   }
-  int above = 0;
+  cut = cut > 1u ? cut : 1u;
+  int n_cand = 0;
 #pragma unroll
-  for (int i = 0; i < NPL; ++i) above += wave_count(key[i] > thr);
-  // ties at thr: the (k - above) lowest expert indices
+  for (int i = 0; i < NPL; ++i) n_cand += wave_count(key[i] >= cut);
   const uint64_t below_me = (1ull << lane) - 1ull;
-  int eq_before = 0;
-  uint32_t picked = 0u;  // bit i: this lane's expert of plane i is chosen
-#pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    const uint64_t eq = __ballot(key[i] == thr);
-    const int r = eq_before + __popcll(eq & below_me);
-    const bool take = key[i] > thr || (key[i] == thr && r < k - above);
-    picked |= (take ? 1u : 0u) << i;
-    eq_before += __popcll(eq);
-  }
-  // each chosen expert's rank among the chosen; planes holding none skip
   int* slot_id = s.ids + t * k;
   float* slot_aux = s.w + t * k;
+  if (n_cand >= k && n_cand <= kCand) {
+    uint32_t* ck = s.tk.cand_key[wid];
+    int* ce = s.tk.cand_e[wid];
+    int base = 0;
 #pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    const bool me = (picked >> i) & 1u;
-    if (!__ballot(me)) continue;
-    const int e = lane + kWave * i;
-    int rank = 0;
-#pragma unroll
-    for (int i2 = 0; i2 < NPL; ++i2) {
-      uint64_t m = __ballot((picked >> i2) & 1u);
-      while (m) {
-        const int l2 = __builtin_ctzll(m);
-        m &= m - 1ull;
-        const uint32_t k2 = (uint32_t)__builtin_amdgcn_readlane((int)key[i2], l2);
-        const int e2 = l2 + kWave * i2;
-        rank += (k2 > key[i] || (k2 == key[i] && e2 < e)) ? 1 : 0;
+    for (int i = 0; i < NPL; ++i) {
+      const bool c = key[i] >= cut;
+      const uint64_t bm = __ballot(c);
+      if (c) {
+        const int pos = base + __popcll(bm & below_me);
+        ck[pos] = key[i];
+        ce[pos] = lane + kWave * i;
       }
+      base += __popcll(bm);
     }
-    if (me) {
-      slot_id[rank] = e;
-      slot_aux[rank] = route_aux(p, lg[i]);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    constexpr int NC = kCand / kWave;
+    uint32_t ckey[NC];
+    int cexp[NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int pos = lane + kWave * i;
+      ckey[i] = pos < n_cand ? ck[pos] : 0u;
+      cexp[i] = pos < n_cand ? ce[pos] : 0;
     }
+    // the list is rewritten with the chosen only after every lane has read it
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    select_rank<NC>(ckey, [&](int i, int) { return cexp[i]; }, k, lane, ck, ce, slot_id);
+  } else {
+    select_rank<NPL>(key, [](int i, int l) { return l + kWave * i; }, k, lane,
+                     s.tk.cand_key[wid], s.tk.cand_e[wid], slot_id);
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -323,7 +424,7 @@ __device__ void topk_one(const RouteArgs& p, int t, int lane, PlanShared& s) {
   float my_aux = 0.f;
   if (lane < k) {
     my_id = slot_id[lane];
-    my_aux = slot_aux[lane];
+    my_aux = route_aux(p, lgr[my_id]);
   }
   if (GROUPED && p.strict) {
     // Strict department coverage: while the k chosen experts (lane j holds
@@ -354,16 +455,11 @@ __device__ void topk_one(const RouteArgs& p, int t, int lane, PlanShared& s) {
         const int u = __builtin_ctzll(__ballot(cand && dkey == best));
         // its best expert: the lowest index holding the department's key
         int e_in = -1;
-        float l_in = 0.f;
 #pragma unroll
         for (int i = 0; i < NPL; ++i) {
           const int e = lane + kWave * i;
-          const uint64_t b = __ballot(e < p.E && dept_of(e) == (unsigned)u && key[i] == best);
-          if (e_in < 0 && b) {
-            const int l = __builtin_ctzll(b);
-            e_in = l + kWave * i;
-            l_in = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lg[i]), l));
-          }
+          const uint64_t b = __ballot(e < E && dept_of(e) == (unsigned)u && key[i] == best);
+          if (e_in < 0 && b) e_in = __builtin_ctzll(b) + kWave * i;
         }
         const uint64_t elig = __ballot(lane < k && !removed && cnt >= 2);
         if (e_in < 0 || !elig) break;  // neither happens when k >= k_dept
@@ -373,7 +469,7 @@ __device__ void topk_one(const RouteArgs& p, int t, int lane, PlanShared& s) {
         if (lane == r) removed = true;
         if (lane == it) {
           in_id = e_in;
-          in_aux = route_aux(p, l_in);
+          in_aux = route_aux(p, lgr[e_in]);
         }
         uncov &= ~(1ull << u);
       }
@@ -409,12 +505,12 @@ __device__ void topk_one(const RouteArgs& p, int t, int lane, PlanShared& s) {
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < NPL; ++i)
-      if (lane + kWave * i < p.E) mx = fmaxf(mx, lg[i]);
+      if (lane + kWave * i < E) mx = fmaxf(mx, lgr[lane + kWave * i]);
     mx = wave_max(mx);
     float z = 0.f;
 #pragma unroll
     for (int i = 0; i < NPL; ++i)
-      if (lane + kWave * i < p.E) z += expf(lg[i] - mx);
+      if (lane + kWave * i < E) z += expf(lgr[lane + kWave * i] - mx);
     w = expf(my_aux - mx) / wave_sum(z);
   }
   w *= p.scale;
@@ -424,45 +520,9 @@ __device__ void topk_one(const RouteArgs& p, int t, int lane, PlanShared& s) {
     if (p.w_out) p.w_out[a] = w;
     s.ids[a] = my_id;
     s.w[a] = w;
-  }
-}
-
-// Wave 0 scans cnt[0, n) into off[0, n] (exclusive, off[n] = total; also
-// copied to off_copy), lists the occupied entries in `active`, and gives each
-// occupied entry its index in the compacted list of small (cnt <= kTokInline)
-// or of large groups (slot[]).  Totals go to hdr[...] from lane 63.
-__device__ void wave0_scan(PlanShared& s, int n, int32_t* active, int32_t* off_copy,
-                           int32_t* hdr, int h_rows, int h_active, int h_small, int h_large,
-                           int lane) {
-  const int per = (n + 63) / 64;
-  const int b = min(n, lane * per), en = min(n, b + per);
-  int sc = 0, sa = 0, ss = 0;
-  for (int i = b; i < en; ++i) {
-    const int c = s.cnt[i];
-    sc += c;
-    sa += c > 0 ? 1 : 0;
-    ss += (c > 0 && c <= kTokInline) ? 1 : 0;
-  }
-  const int ic = wave_incl_scan(sc, lane), ia = wave_incl_scan(sa, lane),
-            is = wave_incl_scan(ss, lane);
-  int rc = ic - sc, ra = ia - sa, rs = is - ss, rl = (ia - sa) - (is - ss);
-  for (int i = b; i < en; ++i) {
-    const int c = s.cnt[i];
-    s.off[i] = rc;
-    off_copy[i] = rc;
-    if (c > 0) {
-      active[ra++] = i;
-      s.slot[i] = c <= kTokInline ? rs++ : rl++;
-    }
-    rc += c;
-  }
-  if (lane == 63) {
-    s.off[n] = ic;
-    off_copy[n] = ic;
-    hdr[h_rows] = ic;
-    hdr[h_active] = ia;
-    hdr[h_small] = is;
-    hdr[h_large] = ia - is;
+    // the plan's tallies (the k experts of a token are distinct)
+    atomicAdd(&s.cnt[my_id], 1);
+    if (p.m > 0) s.flag[t * p.m + my_id / (E / p.m)] = 1;
   }
 }
 
@@ -472,133 +532,192 @@ __device__ __forceinline__ WorkDesc* work_of(WorkDesc* work, int cap, int c, int
   return work + (c <= kTokInline ? slot : cap + slot);
 }
 
-// The dispatch plan from s.ids / s.w (T*k assignments).  Whole block.
+// Departments, by one wave: pairs per department (from the pair flags),
+// offsets, the ascending list of active departments, each one's index in the
+// compacted list of small (<= kTokInline pairs) or of large groups, work
+// descriptors and header totals.
+__device__ void dept_scan(PlanShared& s, const PlanArgs& pa, int lane) {
+  const int m = pa.m, T = pa.T;
+  const moe_plan& P = pa.plan;
+  const int per = (m + kWave - 1) / kWave;
+  const int b = min(m, lane * per), en = min(m, b + per);
+  int sc = 0, sa = 0, ss = 0;
+  for (int J = b; J < en; ++J) {
+    int c = 0;
+    for (int t = 0; t < T; ++t) c += s.flag[t * m + J];
+    s.pw.dcnt[J] = c;
+    sc += c;
+    sa += c > 0 ? 1 : 0;
+    ss += (c > 0 && c <= kTokInline) ? 1 : 0;
+  }
+  const int ic = wave_incl_scan(sc, lane), ia = wave_incl_scan(sa, lane),
+            is = wave_incl_scan(ss, lane);
+  int rc = ic - sc, ra = ia - sa, rs = is - ss, rl = (ia - sa) - (is - ss);
+  for (int J = b; J < en; ++J) {
+    const int c = s.pw.dcnt[J];
+    s.pw.doff[J] = rc;
+    P.dept_offsets[J] = rc;
+    P.dept_counts[J] = c;
+    if (c > 0) {
+      P.active_depts[ra++] = J;
+      const int sl = c <= kTokInline ? rs++ : rl++;
+      s.pw.dslot[J] = sl;
+      WorkDesc* wd = work_of(pa.dwork, m, c, sl);
+      wd->mat = J;
+      wd->r0 = rc;
+      wd->n = c;
+    }
+    rc += c;
+  }
+  if (lane == kWave - 1) {
+    P.dept_offsets[m] = ic;
+    P.header[MOE_PLAN_N_DEPT_ROWS] = ic;
+    P.header[MOE_PLAN_N_ACTIVE_DEPTS] = ia;
+    P.header[kHdrDeptSmall] = is;
+    P.header[kHdrDeptLarge] = ia - is;
+  }
+}
+
+// The dispatch plan from s.ids / s.w (T*k assignments), s.cnt (rows per
+// expert) and s.flag (pairs present).  Whole block, two barriers: a scan of
+// the expert counts by at most kScanWaves waves (contiguous entries per lane,
+// wave scans, wave totals through LDS) while the last wave scans the
+// departments; then every assignment and every pair writes its row.  Waves
+// with no entries stay out of the scan: cross-lane steps of idle waves would
+// only queue on the LDS crossbar.
+constexpr int kScanWaves = 4;
 __device__ void plan_phase(PlanShared& s, const PlanArgs& pa) {
   const int tid = threadIdx.x, nth = blockDim.x, lane = tid & 63, wid = tid >> 6;
-  const int T = pa.T, k = pa.k, E = pa.E, A = T * k;
+  const int nw = nth >> 6;
+  const int T = pa.T, k = pa.k, E = pa.E, A = T * k, m = pa.m;
   const moe_plan& P = pa.plan;
-  for (int e = tid; e < E; e += nth) s.cnt[e] = 0;
-  if (tid == 0) s.invalid = 0;
+  const int per = max(1, (E + kScanWaves * kWave - 1) / (kScanWaves * kWave));
+  const int nsw = (E + kWave * per - 1) / (kWave * per);  // scanning waves, <= kScanWaves
+  const int b = min(E, tid * per), en = min(E, b + per);
+  int sc = 0, sa = 0, ss = 0, ic = 0, ia = 0, is = 0;
+  if (wid < nsw) {
+    for (int e = b; e < en; ++e) {
+      const int c = s.cnt[e];
+      sc += c;
+      sa += c > 0 ? 1 : 0;
+      ss += (c > 0 && c <= kTokInline) ? 1 : 0;
+    }
+    ic = wave_incl_scan(sc, lane);
+    ia = wave_incl_scan(sa, lane);
+    is = wave_incl_scan(ss, lane);
+    if (lane == kWave - 1) {
+      s.pw.tot[wid][0] = ic;
+      s.pw.tot[wid][1] = ia;
+      s.pw.tot[wid][2] = is;
+    }
+  }
+  if (m > 0 && wid == nw - 1) dept_scan(s, pa, lane);  // nw - 1 >= kScanWaves
   __syncthreads();
-  for (int a = tid; a < A; a += nth) {
-    const int e = s.ids[a];
-    if (e >= 0 && e < E)
-      atomicAdd(&s.cnt[e], 1);
-    else
-      atomicAdd(&s.invalid, 1);
+  if (tid == 0) {
+    int gc = 0, gac = 0, gsc = 0;
+    for (int w2 = 0; w2 < nsw; ++w2) {
+      gc += s.pw.tot[w2][0];
+      gac += s.pw.tot[w2][1];
+      gsc += s.pw.tot[w2][2];
+    }
+    P.offsets[E] = gc;
+    P.header[MOE_PLAN_N_ROWS] = gc;
+    P.header[MOE_PLAN_N_ACTIVE] = gac;
+    P.header[kHdrSmall] = gsc;
+    P.header[kHdrLarge] = gac - gsc;
+    P.header[MOE_PLAN_N_INVALID] = s.invalid;
+    if (m <= 0) {
+      P.header[MOE_PLAN_N_DEPT_ROWS] = 0;
+      P.header[MOE_PLAN_N_ACTIVE_DEPTS] = 0;
+      P.header[kHdrDeptSmall] = 0;
+      P.header[kHdrDeptLarge] = 0;
+    }
+  }
+  int pc = 0, pac = 0, psc = 0;  // totals of the scanning waves before mine
+  for (int w2 = 0; w2 < wid && w2 < nsw; ++w2) {
+    pc += s.pw.tot[w2][0];
+    pac += s.pw.tot[w2][1];
+    psc += s.pw.tot[w2][2];
+  }
+  int rc = pc + ic - sc, ra = pac + ia - sa, rs = psc + is - ss;
+  int rl = ra - rs;  // large groups before mine: active minus small
+  for (int e = b; e < en && wid < nsw; ++e) {
+    const int c = s.cnt[e];
+    s.pw.off[e] = rc;
+    P.offsets[e] = rc;
+    P.counts[e] = c;
+    if (c > 0) {
+      P.active[ra++] = e;
+      const int sl = c <= kTokInline ? rs++ : rl++;
+      s.pw.slot[e] = sl;
+      WorkDesc* wd = work_of(pa.work, E, c, sl);
+      wd->mat = e;
+      wd->r0 = rc;
+      wd->n = c;
+    }
+    rc += c;
   }
   __syncthreads();
-  if (wid == 0)
-    wave0_scan(s, E, P.active, P.offsets, P.header, MOE_PLAN_N_ROWS, MOE_PLAN_N_ACTIVE,
-               kHdrSmall, kHdrLarge, lane);
-  __syncthreads();
-  // row of assignment a = offset of its expert + earlier assignments to it
+  const int G = m > 0 ? E / m : 1;
+  // row of assignment a = offset of its expert + earlier assignments to it;
+  // in the factorised form a row's inputs are its (token, department) pair's
+  // backbone outputs, so the pair index goes to row_pair and to the inline
+  // entries of small groups
   for (int a = tid; a < A; a += nth) {
     const int e = s.ids[a];
     if (e >= 0 && e < E) {
       int rank = 0;
-      for (int b = 0; b < a; ++b) rank += (s.ids[b] == e) ? 1 : 0;
-      const int row = s.off[e] + rank;
+      for (int b2 = 0; b2 < a; ++b2) rank += (s.ids[b2] == e) ? 1 : 0;
+      const int row = s.pw.off[e] + rank;
       const int t = a / k;
       P.row_token[row] = t;
       P.row_slot[row] = a - t * k;
       P.row_expert[row] = e;
       P.row_weight[row] = s.w[a];
       P.inv_perm[a] = row;
-      s.arank[a] = (short)rank;
-      if (s.cnt[e] <= kTokInline) pa.work[s.slot[e]].tok[rank] = t;
+      int in = t;
+      if (pa.factorised) {
+        const int J = e / G;
+        int rd = 0;
+        for (int u = 0; u < t; ++u) rd += s.flag[u * m + J];
+        in = s.pw.doff[J] + rd;
+        P.row_pair[row] = in;
+      }
+      if (s.cnt[e] <= kTokInline) pa.work[s.pw.slot[e]].tok[rank] = in;
     } else {
       P.inv_perm[a] = -1;
     }
   }
-  for (int e = tid; e < E; e += nth) {
-    const int c = s.cnt[e];
-    P.counts[e] = c;
-    s.eslot[e] = s.slot[e];
-    if (c > 0) {
-      WorkDesc* wd = work_of(pa.work, E, c, s.slot[e]);
-      wd->mat = e;
-      wd->r0 = s.off[e];
-      wd->n = c;
-    }
-  }
-  if (tid == 0) P.header[MOE_PLAN_N_INVALID] = s.invalid;
-  if (pa.m <= 0) {
-    if (tid == 0) {
-      P.header[MOE_PLAN_N_DEPT_ROWS] = 0;
-      P.header[MOE_PLAN_N_ACTIVE_DEPTS] = 0;
-      P.header[kHdrDeptSmall] = 0;
-      P.header[kHdrDeptLarge] = 0;
-    }
-    return;
-  }
-  // (token, department) pairs: department j is active for token t when t
-  // selected at least one of its experts; c_{t,j} sums those weights.
-  const int m = pa.m, G = E / m, TM = T * m;
-  __syncthreads();
-  for (int p = tid; p < TM; p += nth) {
-    const int t = p / m, J = p - t * m;
-    int has = 0;
-    for (int j = 0; j < k; ++j) {
-      const int e = s.ids[t * k + j];
-      if (e >= 0 && e < E && e / G == J) has = 1;
-    }
-    s.flag[p] = (unsigned char)has;
-  }
-  __syncthreads();
-  for (int J = tid; J < m; J += nth) {
-    int c = 0;
-    for (int t = 0; t < T; ++t) c += s.flag[t * m + J];
-    s.cnt[J] = c;
-  }
-  __syncthreads();
-  if (wid == 0)
-    wave0_scan(s, m, P.active_depts, P.dept_offsets, P.header, MOE_PLAN_N_DEPT_ROWS,
-               MOE_PLAN_N_ACTIVE_DEPTS, kHdrDeptSmall, kHdrDeptLarge, lane);
-  __syncthreads();
-  for (int p = tid; p < TM; p += nth) {
+  if (m <= 0) return;
+  // (token, department) pairs: department J is active for token t when t
+  // selected at least one of its experts; c_{t,J} sums those weights
+  for (int p = tid; p < T * m; p += nth) {
     const int t = p / m, J = p - t * m;
     if (s.flag[p]) {
       int rank = 0;
       for (int u = 0; u < t; ++u) rank += s.flag[u * m + J];
-      const int q = s.off[J] + rank;
-      float sc = 0.f;
+      const int q = s.pw.doff[J] + rank;
+      float sc2 = 0.f;
       for (int j = 0; j < k; ++j) {
         const int e = s.ids[t * k + j];
-        if (e >= 0 && e < E && e / G == J) sc += s.w[t * k + j];
+        if (e >= 0 && e < E && e / G == J) sc2 += s.w[t * k + j];
       }
       P.dept_row_token[q] = t;
       P.dept_row_dept[q] = J;
-      P.dept_row_scale[q] = sc;
+      P.dept_row_scale[q] = sc2;
       P.dept_inv[p] = q;
-      if (s.cnt[J] <= kTokInline) pa.dwork[s.slot[J]].tok[rank] = t;
+      if (s.pw.dcnt[J] <= kTokInline) pa.dwork[s.pw.dslot[J]].tok[rank] = t;
     } else {
       P.dept_inv[p] = -1;
     }
   }
-  for (int J = tid; J < m; J += nth) {
-    const int c = s.cnt[J];
-    P.dept_counts[J] = c;
-    if (c > 0) {
-      WorkDesc* wd = work_of(pa.dwork, m, c, s.slot[J]);
-      wd->mat = J;
-      wd->r0 = s.off[J];
-      wd->n = c;
-    }
-  }
-  if (!pa.factorised) return;
-  // Factorised form: a routed row reads its (token, department) pair's
-  // backbone outputs, so the row's input index is the pair, in row_pair and
-  // in the inline entries of its small group.
-  __syncthreads();
-  for (int a = tid; a < A; a += nth) {
-    const int e = s.ids[a];
-    if (e >= 0 && e < E) {
-      const int t = a / k, q = P.dept_inv[t * m + e / G];
-      P.row_pair[P.inv_perm[a]] = q;
-      if (P.counts[e] <= kTokInline) pa.work[s.eslot[e]].tok[s.arank[a]] = q;
-    }
-  }
+}
+
+// Per-launch clearing of the plan's LDS tallies (before any top-k or count).
+__device__ __forceinline__ void plan_clear(PlanShared& s, int T, int E, int m) {
+  for (int e = threadIdx.x; e < E; e += blockDim.x) s.cnt[e] = 0;
+  for (int p = threadIdx.x; p < T * (m > 0 ? m : 0); p += blockDim.x) s.flag[p] = 0;
+  if (threadIdx.x == 0) s.invalid = 0;
 }
 
 // Router logits l[t][e] = x_t . W_r[e].  A block owns EB experts; its four
@@ -737,14 +856,22 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(RouteArgs ra) {
   }
 }
 
-// One block: top-k of every token (one wave per token), then (do_plan) the
-// dispatch plan.
+// One block: per chunk of tokens, the whole block stages the logits and keys,
+// then one wave per token selects its top-k; then (do_plan) the dispatch plan.
 template <int NPL, bool GROUPED>
 __global__ __launch_bounds__(kPlanThreads) void topk_plan_kernel(RouteArgs ra, PlanArgs pa,
                                                                  int do_plan) {
   __shared__ PlanShared s;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  for (int t = wid; t < ra.T; t += nw) topk_one<NPL, GROUPED>(ra, t, lane, s);
+  const int tcap = kTopkBuf / ra.E;  // E <= MOE_MAX_EXPERTS < kTopkBuf
+  plan_clear(s, ra.T, ra.E, ra.m);   // ordered before the tallies by the first barrier
+  for (int t0 = 0; t0 < ra.T; t0 += tcap) {
+    const int tc = min(tcap, ra.T - t0);
+    if (t0 > 0) __syncthreads();  // the previous chunk's waves are done with the staging
+    stage_scores(ra, t0, tc, s);
+    __syncthreads();
+    for (int t = t0 + wid; t < t0 + tc; t += nw) topk_token<NPL, GROUPED>(ra, t, (t - t0) * ra.E, lane, s);
+  }
   if (!do_plan) return;
   __syncthreads();
   plan_phase(s, pa);
@@ -753,9 +880,19 @@ __global__ __launch_bounds__(kPlanThreads) void topk_plan_kernel(RouteArgs ra, P
 __global__ __launch_bounds__(kPlanThreads) void dispatch_kernel(const int32_t* ids, const float* w,
                                                                 PlanArgs pa) {
   __shared__ PlanShared s;
+  plan_clear(s, pa.T, pa.E, pa.m);
+  __syncthreads();
+  const int G = pa.m > 0 ? pa.E / pa.m : 1;
   for (int a = threadIdx.x; a < pa.T * pa.k; a += blockDim.x) {
-    s.ids[a] = ids[a];
+    const int e = ids[a];
+    s.ids[a] = e;
     s.w[a] = w[a];
+    if (e >= 0 && e < pa.E) {
+      atomicAdd(&s.cnt[e], 1);
+      if (pa.m > 0) s.flag[(a / pa.k) * pa.m + e / G] = 1;
+    } else {
+      atomicAdd(&s.invalid, 1);
+    }
   }
   __syncthreads();
   plan_phase(s, pa);
