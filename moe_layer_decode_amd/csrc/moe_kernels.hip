@@ -239,6 +239,43 @@ __device__ void stage_scores_ks(const RouteArgs& p, int t0, int tc, PlanShared& 
   }
 }
 
+// One token's row by its own wave (lane l: experts l, l+64, ...), for
+// layers with few experts per lane: the planes of all NPL entries are
+// requested before the first add waits, and no block barrier is needed.  The
+// keys stay in registers; the row in LDS gets the logits, and the keys too
+// when departments are ranked (their maxima are read department-major).
+template <int NPL, bool GROUPED>
+__device__ void stage_token(const RouteArgs& p, int t, int row, int lane, PlanShared& s,
+                            uint32_t (&key)[NPL]) {
+  const int E = p.E;
+  float v[kMaxRouteSplit][NPL], b[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = min(lane + kWave * i, E - 1);
+    b[i] = p.bias ? p.bias[e] : 0.f;
+#pragma unroll
+    for (int q = 0; q < kMaxRouteSplit; ++q)
+      v[q][i] = p.logits[((size_t)min(q, p.ksplit - 1) * p.T + t) * E + e];
+  }
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = lane + kWave * i;
+    key[i] = 0u;
+    if (e < E) {
+      float l = 0.f;
+#pragma unroll
+      for (int q = 0; q < kMaxRouteSplit; ++q) l += q < p.ksplit ? v[q][i] : 0.f;
+      const float sc = p.score_fn == MOE_SCORE_SOFTMAX ? l : route_aux(p, l) + b[i];
+      if (p.sel_out) p.sel_out[(size_t)t * E + e] = sc;
+      s.tk.lg[row + e] = l;
+      key[i] = score_key(sc);
+      if (GROUPED) s.tk.key[row + e] = key[i];
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
 __device__ void stage_scores(const RouteArgs& p, int t0, int tc, PlanShared& s) {
   if (p.ksplit > 4)
     stage_scores_ks<kMaxRouteSplit>(p, t0, tc, s);
@@ -300,22 +337,19 @@ __device__ __forceinline__ void select_rank(const uint32_t (&key)[NP], EidOf eid
 }
 
 // Top-k of token t by one wave from the staged row `row` (lane l holds experts
-// l, l+64, ...).  Every key among the k largest, ties at the k-th included,
-// is at least the k-th largest of the 64 lane maxima; those candidates (few
-// for real scores) are compacted in expert order and selected on two planes.
-// With more candidates than fit, or fewer than k, the select runs on all
-// planes.  The chosen experts are handed to lanes 0..k-1 through LDS, then the
+// l, l+64, ...).  With 8 or more planes: every key among the k largest, ties
+// at the k-th included, is at least the k-th largest of the 64 lane maxima;
+// those candidates (few for real scores) are compacted in expert order and
+// selected on two planes.  With fewer planes, more candidates than fit, or
+// fewer than k, the select runs on all planes.  The chosen experts are handed to lanes 0..k-1 through LDS, then the
 // weights.
+// `key` holds the row's keys on entry (lane l, plane i: expert l + 64 i; 0
+// past the last expert); the logits are read from the staged row.
 template <int NPL, bool GROUPED>
-__device__ void topk_token(const RouteArgs& p, int t, int row, int lane, PlanShared& s) {
+__device__ void topk_token(const RouteArgs& p, int t, int row, int lane, PlanShared& s,
+                           uint32_t (&key)[NPL]) {
   const int k = p.k, E = p.E, wid = threadIdx.x >> 6;
   const float* lgr = s.tk.lg + row;
-  uint32_t key[NPL];
-#pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    const int e = lane + kWave * i;
-    key[i] = e < E ? s.tk.key[row + e] : 0u;
-  }
   // department of expert e = floor((e + 0.5) / G) in fp32: exact, since
   // e < 2048 and the quotient is below m <= 64, so the rounding error
   // (under 64 * 2^-23) stays inside the 0.5 / G margin to each integer
@@ -367,24 +401,28 @@ __device__ void topk_token(const RouteArgs& p, int t, int row, int lane, PlanSha
       if (e < E && !((chosen_depts >> dept_of(e)) & 1ull)) key[i] = 0u;
     }
   }
-  // candidate cut: the k-th largest lane maximum (at least 1, so key-0
-  // entries never qualify)
-  uint32_t lmax = 0u;
-#pragma unroll
-  for (int i = 0; i < NPL; ++i) lmax = key[i] > lmax ? key[i] : lmax;
-  uint32_t cut = 0u;
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t c = cut | (1u << b);
-    if (wave_count(lmax >= c) >= k) cut = c;
-  }
-  cut = cut > 1u ? cut : 1u;
+  // candidate cut (8 or more planes; with fewer a direct select is
+  // cheaper): the k-th largest lane maximum, at least 1 so that key-0
+  // entries never qualify
   int n_cand = 0;
+  uint32_t cut = 1u;
+  if constexpr (NPL >= 8) {
+    uint32_t lmax = 0u;
 #pragma unroll
-  for (int i = 0; i < NPL; ++i) n_cand += wave_count(key[i] >= cut);
+    for (int i = 0; i < NPL; ++i) lmax = key[i] > lmax ? key[i] : lmax;
+    uint32_t c0 = 0u;
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t c = c0 | (1u << b);
+      if (wave_count(lmax >= c) >= k) c0 = c;
+    }
+    cut = c0 > 1u ? c0 : 1u;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) n_cand += wave_count(key[i] >= cut);
+  }
   const uint64_t below_me = (1ull << lane) - 1ull;
   int* slot_id = s.ids + t * k;
   float* slot_aux = s.w + t * k;
-  if (n_cand >= k && n_cand <= kCand) {
+  if (NPL >= 8 && n_cand >= k && n_cand <= kCand) {
     uint32_t* ck = s.tk.cand_key[wid];
     int* ce = s.tk.cand_e[wid];
     int base = 0;
@@ -863,14 +901,36 @@ __global__ __launch_bounds__(kPlanThreads) void topk_plan_kernel(RouteArgs ra, P
                                                                  int do_plan) {
   __shared__ PlanShared s;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  const int tcap = kTopkBuf / ra.E;  // E <= MOE_MAX_EXPERTS < kTopkBuf
-  plan_clear(s, ra.T, ra.E, ra.m);   // ordered before the tallies by the first barrier
-  for (int t0 = 0; t0 < ra.T; t0 += tcap) {
-    const int tc = min(tcap, ra.T - t0);
-    if (t0 > 0) __syncthreads();  // the previous chunk's waves are done with the staging
-    stage_scores(ra, t0, tc, s);
-    __syncthreads();
-    for (int t = t0 + wid; t < t0 + tc; t += nw) topk_token<NPL, GROUPED>(ra, t, (t - t0) * ra.E, lane, s);
+  plan_clear(s, ra.T, ra.E, ra.m);
+  if constexpr (NPL <= 4) {
+    // up to 256 experts: each wave stages its own token in its own row
+    static_assert(kPlanWaves * 4 * kWave <= kTopkBuf, "a row per wave");
+    __syncthreads();  // the tallies are clear
+    for (int t = wid; t < ra.T; t += nw) {
+      uint32_t key[NPL];
+      stage_token<NPL, GROUPED>(ra, t, wid * ra.E, lane, s, key);
+      topk_token<NPL, GROUPED>(ra, t, wid * ra.E, lane, s, key);
+    }
+  } else {
+    // many experts: the whole block stages chunks of tokens (the first
+    // barrier also orders the clearing before the tallies)
+    const int tcap = kTopkBuf / ra.E;  // E <= MOE_MAX_EXPERTS < kTopkBuf
+    for (int t0 = 0; t0 < ra.T; t0 += tcap) {
+      const int tc = min(tcap, ra.T - t0);
+      if (t0 > 0) __syncthreads();  // the previous chunk's waves are done with the staging
+      stage_scores(ra, t0, tc, s);
+      __syncthreads();
+      for (int t = t0 + wid; t < t0 + tc; t += nw) {
+        const int row = (t - t0) * ra.E;
+        uint32_t key[NPL];
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) {
+          const int e = lane + kWave * i;
+          key[i] = e < ra.E ? s.tk.key[row + e] : 0u;
+        }
+        topk_token<NPL, GROUPED>(ra, t, row, lane, s, key);
+      }
+    }
   }
   if (!do_plan) return;
   __syncthreads();
