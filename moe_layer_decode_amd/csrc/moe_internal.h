@@ -13,6 +13,7 @@ constexpr int kWaves = 4;            // waves per block of every kernel
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRouteChunk = 512;     // d elements one router wave covers (64 lanes x 8)
 constexpr int kTokInline = 4;        // tokens carried inline in a work descriptor
+constexpr int kWideRows = 64;        // rows / columns of a bf16 large-group tile
 constexpr int kPlanThreads = 1024;   // threads of the single-block top-k / plan kernel
 constexpr int kMaxRouteSplit = 8;   // partial-logit planes of the bf16 router at most
 constexpr int kMaxParts = 6;         // 3 matrix families x (small groups, large groups)

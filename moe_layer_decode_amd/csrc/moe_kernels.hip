@@ -27,6 +27,7 @@
 #include <hip/hip_ext.h>
 
 #include <climits>
+#include <type_traits>
 
 namespace moe {
 
@@ -1692,6 +1693,232 @@ __device__ void dn_mfma(const bf16_t* __restrict__ Wd, int d, int rows, int c0,
   __syncthreads();
 }
 
+// ---- large groups, bf16: 64-row tiles with LDS-shared inputs ---------------
+//
+// Four waves, each 16 rows (gate/up) or 16 output columns (down) over the whole
+// K.  Every 64-wide K step of the group's inputs is loaded once per block by
+// all 256 threads, written to LDS already in B-operand order, and read by each
+// wave as one contiguous 1 KiB per 16-token tile: the inputs cross the memory
+// path once per 64 rows, so at N tokens they add N/128 (gate/up, two 64-row
+// matrices) or N/64 (down) of the weight bytes.  The inputs and weights of
+// step i+1 are requested together before step i is used, so waiting for the
+// inputs (loads complete in order) never waits for a later weight request.
+// Groups of more than 16*NCMAX tokens take several passes over the weights.
+
+constexpr int kDownNC = 4;     // 16-token tiles of a down pass (one accumulator set: room for 4)
+using Slot0 = std::integral_constant<int, 0>;  // ring slots of the two-step pipeline
+using Slot1 = std::integral_constant<int, 1>;
+constexpr int kWideK = 64;     // K per step: two 32-wide matrix-core steps
+
+// Two buffers of one step's inputs: [buffer][input][token tile][half][lane],
+// lane l of (c, half) holding token 16c + l%16, k = 32 half + 8 (l/16) .. +7.
+template <int NC, int NX>
+struct WideLds {
+  u32x4_t x[2][NX * NC * 2 * kWave];
+};
+
+// Per-thread share of one step's input chunks: chunk q = tid + kThreads * r
+// of Q = NX*NC*128, with l = q % 64, half = (q/64) % 2, c = (q/128) % NC,
+// input v = q / (128 NC).
+template <int NC, int NX>
+struct WideIn {
+  static constexpr int Q = NX * NC * 2 * kWave;
+  static constexpr int R = (Q + kThreads - 1) / kThreads;
+  const bf16_t* p[R];  // input row + k offset of the chunk (nullptr: token past the group)
+  int koff[R];
+};
+
+template <int NC, int NX, typename RowOf>
+__device__ __forceinline__ void wide_inputs(WideIn<NC, NX>& in, const bf16_t* const* src, int d,
+                                            int tc, int n, RowOf row_of) {
+#pragma unroll
+  for (int r = 0; r < WideIn<NC, NX>::R; ++r) {
+    const int q = threadIdx.x + kThreads * r;
+    const int l = q & 63, half = (q >> 6) & 1, rest = q >> 7;
+    const int c = rest % NC, v = rest / NC;
+    const int t = tc + 16 * c + (l & 15);
+    in.koff[r] = 32 * half + 8 * (l >> 4);
+    in.p[r] = (q < WideIn<NC, NX>::Q && t < n) ? src[v < NX ? v : 0] + (size_t)row_of(t) * d : nullptr;
+  }
+}
+
+template <int NC, int NX>
+__device__ __forceinline__ void wide_load(u32x4_t* dst, const WideIn<NC, NX>& in, int k0,
+                                          int K) {
+  const u32x4_t z = {0, 0, 0, 0};
+#pragma unroll
+  for (int r = 0; r < WideIn<NC, NX>::R; ++r) {
+    const int k = k0 + in.koff[r];
+    dst[r] = (in.p[r] && k < K) ? ld16(in.p[r] + k) : z;
+  }
+}
+
+template <int NC, int NX>
+__device__ __forceinline__ void wide_stage(WideLds<NC, NX>& lds, int buf, const u32x4_t* v) {
+#pragma unroll
+  for (int r = 0; r < WideIn<NC, NX>::R; ++r) {
+    const int q = threadIdx.x + kThreads * r;
+    if (q < WideIn<NC, NX>::Q) lds.x[buf][q] = v[r];
+  }
+}
+
+// 64 rows (i0..) of gate and up against 16*NC tokens (rows tc.. of the group
+// [r0, r0 + n) of the plan).
+template <int NC, bool DUAL>
+__device__ __forceinline__ void gu_wide(const bf16_t* __restrict__ Wg,
+                                                  const bf16_t* __restrict__ Wu, int d, int rows,
+                                                  int i0, const bf16_t* __restrict__ x,
+                                                  const bf16_t* __restrict__ xu, int in_rows,
+                                                  int r0, int n, const int* grp_token, int tc,
+                                                  GuOut<bf16_t> o, int lane, int wid,
+                                                  WideLds<NC, DUAL ? 2 : 1>& lds) {
+  constexpr int NX = DUAL ? 2 : 1;
+  constexpr int R = WideIn<NC, NX>::R;
+  const int r16 = lane & 15, g = lane >> 4;
+  const size_t wrow = (size_t)min(i0 + 16 * wid + r16, rows - 1) * d + 8 * g;
+  const bf16_t* ap = Wg + wrow;
+  const bf16_t* bp = Wu + wrow;
+  WideIn<NC, NX> in;
+  const bf16_t* src[NX];
+  src[0] = x;
+  if constexpr (DUAL) src[NX - 1] = xu;
+  wide_inputs<NC, NX>(in, src, d, tc, n, [&](int t) {
+    const int tok = grp_token ? grp_token[r0 + t] : t;
+    return min(max(tok, 0), in_rows - 1);
+  });
+  f32x4_t accg[NC], accu[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) accg[c] = accu[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const u32x4_t z = {0, 0, 0, 0};
+  u32x4_t rx[2][R], ra[2][2], rb[2][2];
+  auto request = [&](auto S, int k0) {
+    constexpr int s = decltype(S)::value;
+    wide_load<NC, NX>(rx[s], in, k0, d);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = k0 + 32 * h;
+      ra[s][h] = k + 8 * g < d ? ld16_stream(ap + k) : z;
+      rb[s][h] = k + 8 * g < d ? ld16_stream(bp + k) : z;
+    }
+  };
+  auto use = [&](auto S) {
+    constexpr int s = decltype(S)::value;
+    wide_stage<NC, NX>(lds, s, rx[s]);
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const u32x4_t bg = lds.x[s][(c * 2 + h) * kWave + lane];
+        const u32x4_t bu = lds.x[s][((NX - 1) * NC * 2 + c * 2 + h) * kWave + lane];
+        accg[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra[s][h]), as_bf16x8(bg), accg[c], 0, 0, 0);
+        accu[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rb[s][h]), as_bf16x8(bu), accu[c], 0, 0, 0);
+      }
+  };
+  const int nk = (d + kWideK - 1) / kWideK;
+  const Slot0 s0;
+  const Slot1 s1;
+  request(s0, 0);
+  for (int it = 0; it < nk; it += 2) {
+    if (it + 1 < nk) request(s1, (it + 1) * kWideK);
+    use(s0);
+    if (it + 1 < nk) {
+      if (it + 2 < nk) request(s0, (it + 2) * kWideK);
+      use(s1);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int t = tc + c * 16 + r16;
+    if (t < n) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = i0 + 16 * wid + 4 * g + i;
+        if (rr < rows) gu_store(o, (size_t)(r0 + t) * rows + rr, accg[c][i], accu[c][i]);
+      }
+    }
+  }
+  __syncthreads();  // the buffers are free for the next pass
+}
+
+// The same, out of line, for launches where large groups are rare (T <= 16):
+// its registers then never raise the pressure, or cause spills, in the
+// small-group path that shares the kernel.  Plain-value arguments, so the
+// call makes the caller materialise nothing.
+template <int NC, bool DUAL>
+__device__ __attribute__((noinline)) void gu_wide_call(
+    const bf16_t* __restrict__ Wg, const bf16_t* __restrict__ Wu, int d, int rows, int i0,
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ xu, int in_rows, int r0, int n,
+    const int* grp_token, int tc, GuOut<bf16_t> o, int lane, int wid,
+    WideLds<NC, DUAL ? 2 : 1>& lds) {
+  gu_wide<NC, DUAL>(Wg, Wu, d, rows, i0, x, xu, in_rows, r0, n, grp_token, tc, o, lane, wid, lds);
+}
+
+// 64 output columns (c0..) against 16*NC rows of h (rows tc.. of the group).
+// Out of line, like gu_wide.
+template <int NC>
+__device__ __attribute__((noinline)) void dn_wide(const bf16_t* __restrict__ Wd, int d, int rows,
+                                                  int c0, const bf16_t* __restrict__ h, int r0,
+                                                  int n, int tc, float* __restrict__ out, int epi,
+                                                  int lane, int wid, WideLds<NC, 1>& lds) {
+  constexpr int R = WideIn<NC, 1>::R;
+  const int r16 = lane & 15, g = lane >> 4;
+  const bf16_t* ap = Wd + (size_t)min(c0 + 16 * wid + r16, d - 1) * rows + 8 * g;
+  WideIn<NC, 1> in;
+  const bf16_t* const src[1] = {h};
+  wide_inputs<NC, 1>(in, src, rows, tc, n, [&](int t) { return r0 + t; });
+  f32x4_t acc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const u32x4_t z = {0, 0, 0, 0};
+  u32x4_t rx[2][R], ra[2][2];
+  auto request = [&](auto S, int k0) {
+    constexpr int s = decltype(S)::value;
+    wide_load<NC, 1>(rx[s], in, k0, rows);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int k = k0 + 32 * hh;
+      ra[s][hh] = k + 8 * g < rows ? ld16_stream(ap + k) : z;
+    }
+  };
+  auto use = [&](auto S) {
+    constexpr int s = decltype(S)::value;
+    wide_stage<NC, 1>(lds, s, rx[s]);
+    __syncthreads();
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const u32x4_t b = lds.x[s][(c * 2 + hh) * kWave + lane];
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra[s][hh]), as_bf16x8(b), acc[c], 0, 0, 0);
+      }
+  };
+  const int nk = (rows + kWideK - 1) / kWideK;
+  const Slot0 s0;
+  const Slot1 s1;
+  request(s0, 0);
+  for (int it = 0; it < nk; it += 2) {
+    if (it + 1 < nk) request(s1, (it + 1) * kWideK);
+    use(s0);
+    if (it + 1 < nk) {
+      if (it + 2 < nk) request(s0, (it + 2) * kWideK);
+      use(s1);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int t = tc + c * 16 + r16;
+    if (t < n) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int col = c0 + 16 * wid + 4 * g + i;
+        if (col < d) dn_store(out, (size_t)(r0 + t) * d + col, acc[c][i], epi);
+      }
+    }
+  }
+  __syncthreads();
+}
+
 // ---- large groups, fp32 layers: plain GEMV ---------------------------------
 
 // RW rows of gate and up against NT tokens from row tc of the group, no
@@ -1796,17 +2023,18 @@ __device__ void dn_plain(const float* __restrict__ Wd, int d, int rows, int c0,
 // spilling; fp32 layers keep the compiler's choice.
 template <typename T_, int NCMAX, bool DUAL>
 constexpr int gateup_min_waves() {
-  // two-input launches carry twice the activations: a register budget of 4 waves
-  return sizeof(T_) == 2 ? (DUAL ? 4 : NCMAX > 1 ? 5 : 6) : 1;
+  // two-input launches carry twice the activations, and 64-token tiles four
+  // accumulator pairs: a register budget of 4 waves
+  return sizeof(T_) == 2 ? (DUAL || NCMAX >= 4 ? 4 : NCMAX > 1 ? 5 : 6) : 1;
 }
 template <typename T_>
 constexpr int down_min_waves() { return sizeof(T_) == 2 ? 7 : 1; }
 
 // LDS of an expert-kernel block: the matrix-core partial tiles of a large
 // group or the staged activations of a small one (a block is only ever one).
-template <typename T_, bool XL, bool DUAL = false>
+template <typename T_, bool XL, bool DUAL = false, int NC = kDownNC>
 constexpr size_t expert_lds_bytes() {
-  const size_t a = sizeof(T_) == 2 ? sizeof(MfmaLds) : 0;
+  const size_t a = sizeof(T_) == 2 ? sizeof(WideLds<NC, DUAL ? 2 : 1>) : 0;
   const size_t b = XL ? sizeof(SmallLds<T_, DUAL ? 2 * kTokInline : kTokInline>) : 0;
   return a > b ? a : (b > 0 ? b : 16);
 }
@@ -1832,7 +2060,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   const T_* xg = F.x_gate ? static_cast<const T_*>(F.x_gate) : x;
   const T_* xu = DUAL ? static_cast<const T_*>(F.x_up) : xg;
   const GuOut<T_> o{static_cast<T_*>(F.h), static_cast<T_*>(F.h2), F.epi};
-  __shared__ __align__(16) unsigned char lds_raw[expert_lds_bytes<T_, XL, DUAL>()];
+  __shared__ __align__(16) unsigned char lds_raw[expert_lds_bytes<T_, XL, DUAL, NCMAX>()];
   if (!F.large) {
     if constexpr (XL) {
       static_assert(RPW == 1 && RW == 1, "staged activations take one row per wave");
@@ -1848,21 +2076,39 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
                              lane);
     return;
   }
-  // large groups: the whole block on one 16-row tile
-  const int i0 = tile * 16;
-  if (i0 >= F.rows) return;
   if constexpr (sizeof(T_) == 2) {
-    MfmaLds& lds = *reinterpret_cast<MfmaLds*>(lds_raw);
+    // large groups: the whole block on one 64-row tile, 16*NC tokens a pass
+    const int i0 = tile * kWideRows;
+    if (i0 >= F.rows) return;
+    constexpr int NX = DUAL ? 2 : 1;
+    // out of line where large groups are rare (T <= 16, or the two-input
+    // private transforms, whose groups seldom pass four rows)
+    constexpr bool kCall = NCMAX == 1 || DUAL;
+#define MOE_GU_WIDE(NC_)                                                                      \
+  do {                                                                                       \
+    auto& lw = *reinterpret_cast<WideLds<NC_, NX>*>(lds_raw);                                \
+    if (kCall)                                                                               \
+      gu_wide_call<NC_, DUAL>(Wg, Wu, d, F.rows, i0, xg, xu, F.in_rows, sl.r0, sl.n,         \
+                              F.grp_token, tc, o, lane, wid, lw);                            \
+    else                                                                                     \
+      gu_wide<NC_, DUAL>(Wg, Wu, d, F.rows, i0, xg, xu, F.in_rows, sl.r0, sl.n, F.grp_token, \
+                         tc, o, lane, wid, lw);                                              \
+  } while (0)
 #pragma unroll 1
     for (int tc = 0; tc < sl.n; tc += 16 * NCMAX) {
-      if (NCMAX > 1 && sl.n - tc > 16)
-        gu_mfma<NCMAX, DUAL>(Wg, Wu, d, F.rows, i0, xg, xu, F.in_rows, sl, F.grp_token, tc, o,
-                             lane, wid, lds);
+      const int rem = sl.n - tc;
+      if (NCMAX >= 4 && rem > 32)
+        MOE_GU_WIDE((NCMAX >= 4 ? 4 : 1));
+      else if (NCMAX >= 2 && rem > 16)
+        MOE_GU_WIDE((NCMAX >= 2 ? 2 : 1));
       else
-        gu_mfma<1, DUAL>(Wg, Wu, d, F.rows, i0, xg, xu, F.in_rows, sl, F.grp_token, tc, o, lane,
-                         wid, lds);
+        MOE_GU_WIDE(1);
     }
+#undef MOE_GU_WIDE
   } else {
+    // large groups, fp32 layers: the whole block on one 16-row tile
+    const int i0 = tile * 16;
+    if (i0 >= F.rows) return;
 #pragma unroll 1
     for (int r = wid * 4; r < wid * 4 + 4; r += 2)
 #pragma unroll 1
@@ -1893,19 +2139,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       dn_small<T_, LPR, CG>(Wd, d, F.rows, cb, h, sl, F.out, F.epi, lane);
     return;
   }
-  // large groups: the whole block on one 16-column tile
-  const int c0 = tile * 16;
-  if (c0 >= d) return;
   if constexpr (sizeof(T_) == 2) {
-    MfmaLds& lds = *reinterpret_cast<MfmaLds*>(lds_raw);
+    // large groups: the whole block on one 64-column tile, 16*NC rows of h a pass
+    const int c0 = tile * kWideRows;
+    if (c0 >= d) return;
 #pragma unroll 1
-    for (int tc = 0; tc < sl.n; tc += 32) {
-      if (sl.n - tc > 16)
-        dn_mfma<2>(Wd, d, F.rows, c0, h, sl, tc, F.out, F.epi, lane, wid, lds);
+    for (int tc = 0; tc < sl.n; tc += 16 * kDownNC) {
+      const int rem = sl.n - tc;
+      if (rem > 32)
+        dn_wide<kDownNC>(Wd, d, F.rows, c0, h, sl.r0, sl.n, tc, F.out, F.epi, lane, wid,
+                         *reinterpret_cast<WideLds<kDownNC, 1>*>(lds_raw));
+      else if (rem > 16)
+        dn_wide<2>(Wd, d, F.rows, c0, h, sl.r0, sl.n, tc, F.out, F.epi, lane, wid,
+                   *reinterpret_cast<WideLds<2, 1>*>(lds_raw));
       else
-        dn_mfma<1>(Wd, d, F.rows, c0, h, sl, tc, F.out, F.epi, lane, wid, lds);
+        dn_wide<1>(Wd, d, F.rows, c0, h, sl.r0, sl.n, tc, F.out, F.epi, lane, wid,
+                   *reinterpret_cast<WideLds<1, 1>*>(lds_raw));
     }
   } else {
+    // large groups, fp32 layers: the whole block on one 16-column tile
+    const int c0 = tile * 16;
+    if (c0 >= d) return;
 #pragma unroll 1
     for (int q = wid * 4; q < wid * 4 + 4; q += 2)
 #pragma unroll 1
@@ -2046,8 +2300,9 @@ template <typename T_>
 static hipError_t launch_gateup_t(const FamilySet& set, const T_* x, int T, int d, int rpw,
                                   int rw, hipStream_t st, const KernelEvents* ev) {
   const dim3 grid(set.blk_start[set.n]), block(kThreads);
-  // a routed group holds at most T rows, so 32-token chunks pay off only past 16
-  const bool wide = T > 16;
+  // a group holds at most T rows: wider token passes (more accumulators) only
+  // where a group can use them
+  const int ncmax = T > 32 ? 4 : T > 16 ? 2 : 1;
   // one row per wave and pass: measured fastest, and the register budget of
   // the capped-occupancy build leaves no room for more
   if (rpw != 1 || rw != 1) return hipErrorInvalidValue;
@@ -2056,10 +2311,11 @@ static hipError_t launch_gateup_t(const FamilySet& set, const T_* x, int T, int 
   const bool dual = set.f[0].x_up != nullptr;
 #define MOE_GU(W, X, D) launch(gateup_kernel<T_, 1, 1, W, X, D>, grid, block, st, ev, set, x, T, d)
   if (dual) {
-    if (wide && xl) MOE_GU(2, true, true); else if (wide) MOE_GU(2, false, true);
-    else if (xl) MOE_GU(1, true, true); else MOE_GU(1, false, true);
+    // the private transforms' groups seldom pass four rows: 16-token passes
+    if (xl) MOE_GU(1, true, true); else MOE_GU(1, false, true);
   } else {
-    if (wide && xl) MOE_GU(2, true, false); else if (wide) MOE_GU(2, false, false);
+    if (ncmax == 4) { if (xl) MOE_GU(4, true, false); else MOE_GU(4, false, false); }
+    else if (ncmax == 2) { if (xl) MOE_GU(2, true, false); else MOE_GU(2, false, false); }
     else if (xl) MOE_GU(1, true, false); else MOE_GU(1, false, false);
   }
 #undef MOE_GU
