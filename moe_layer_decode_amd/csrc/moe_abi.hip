@@ -449,7 +449,7 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 moe_status run_experts(const moe_layer_desc& d, const moe_weights& w, const void* x, int32_t T,
                        const moe_plan& p, void* ws, float* row_out, float* dept_out,
                        float* shared_out, hipStream_t st, const moe::KernelEvents* ev_gu,
-                       const moe::KernelEvents* ev_dn) {
+                       const moe::KernelEvents* ev_dn, bool gateup_only = false) {
   const moe::GemvConfig cfg = choose_config(d, T);
   const int dm = d.d_model;
   if (!factorised(d)) {
@@ -458,6 +458,7 @@ moe_status run_experts(const moe_layer_desc& d, const moe_weights& w, const void
     if (moe::launch_gateup(d.w_dtype, set, x, T, dm, cfg.rows_per_wave, cfg.rows_per_pass, st,
                            ev_gu) != hipSuccess)
       return MOE_ERR_HIP;
+    if (gateup_only) return MOE_OK;
     set_tiles(set, dm, false, d.w_dtype, cfg);
     return hip_status(
         moe::launch_down(d.w_dtype, set, T, dm, cfg.lpr, cfg.col_groups, st, ev_dn));
@@ -510,6 +511,77 @@ moe_status run_experts(const moe_layer_desc& d, const moe_weights& w, const void
   set_tiles(e, dm, false, d.w_dtype, cfg);
   return hip_status(moe::launch_down(d.w_dtype, e, T, dm, cfg.lpr, cfg.col_groups, st,
                                      ev_dn ? &dn1 : nullptr));
+}
+
+// The down projection with the combine as its epilogue (one launch writing y)
+// serves bf16 layers in the plain and slice forms at batches of at most
+// kTokInline tokens, where every group is small, when the rows of h it stages
+// fit kDcMaxLds and no intermediate row is longer than kDcMaxRows.  Returns false (and fills nothing) otherwise; the step then
+// takes the separate down and combine launches.
+constexpr size_t kDcMaxLds = 64 * 1024;
+bool down_combine_args(const moe_layer_desc& d, const moe_weights& w, const moe_plan& p,
+                       void* ws, int32_t T, moe::DownCombineArgs* out) {
+  if (d.w_dtype != MOE_BF16 || d.act_dtype != MOE_BF16 || factorised(d)) return false;
+  if (T < 1 || T > moe::kTokInline) return false;
+  const Layout L = layout_of(d);
+  moe::DownCombineArgs a{};
+  const int tk = T * d.top_k;
+  const int pairs = (int)((int64_t)T * (d.n_depts < d.top_k ? d.n_depts : d.top_k));
+  int64_t off = 0, items = 0;
+  bool fits = true;
+  auto add = [&](moe::DcFamily f) {
+    if (f.rows > moe::kDcMaxRows) fits = false;
+    f.lds_off = (int)off;
+    off += (int64_t)f.max_hrows * f.rows;
+    items += f.max_items;
+    a.f[a.nf++] = f;
+  };
+  {
+    moe::DcFamily f{};
+    f.down = w.w_down;
+    f.work = at<WorkDesc>(ws, L, R_WORK);  // the small list: every group at T <= kTokInline
+    f.n_items = p.header + moe::kHdrSmall;
+    f.wrow = p.row_weight;
+    f.h = at<void>(ws, L, R_H);
+    f.n_hrows = p.header + MOE_PLAN_N_ROWS;
+    f.rows = d.d_ff;
+    f.max_items = tk < d.n_experts ? tk : d.n_experts;
+    f.max_hrows = tk;
+    f.n_mats = d.n_experts;
+    add(f);
+  }
+  if (d.n_depts > 0) {
+    moe::DcFamily f{};
+    f.down = w.wd_down;
+    f.work = at<WorkDesc>(ws, L, R_DWORK);
+    f.n_items = p.header + moe::kHdrDeptSmall;
+    f.wrow = p.dept_row_scale;
+    f.h = at<void>(ws, L, R_HD);
+    f.n_hrows = p.header + MOE_PLAN_N_DEPT_ROWS;
+    f.rows = d.d_ff_dept;
+    f.max_items = pairs < d.n_depts ? pairs : d.n_depts;
+    f.max_hrows = pairs;
+    f.n_mats = d.n_depts;
+    add(f);
+  }
+  if (d.d_ff_shared > 0) {
+    moe::DcFamily f{};
+    f.down = w.ws_down;
+    f.h = at<void>(ws, L, R_HS);
+    f.rows = d.d_ff_shared;
+    f.max_items = 1;
+    f.max_hrows = T;
+    f.n_mats = 1;
+    add(f);
+  }
+  a.T = T;
+  a.d = d.d_model;
+  a.h_elems = (int)off;
+  a.max_items = (int)items;
+  if (!fits || off > (int64_t)kDcMaxLds || moe::down_combine_lds_bytes(a) > kDcMaxLds)
+    return false;
+  *out = a;
+  return true;
 }
 
 }  // namespace
@@ -664,7 +736,22 @@ moe_status moe_layer_decode(const moe_layer_desc* desc, const moe_weights* weigh
   if (moe::launch_route(desc->w_dtype, ra, &pa, st, evp(MOE_STAGE_ROUTE)) != hipSuccess)
     return MOE_ERR_HIP;
 
-  // grouped expert FFN, then the combine back to token order
+  // grouped expert FFN, then the combine back to token order: at decode
+  // batches of a few tokens, one down launch that writes y itself (the
+  // combine stage is then an empty interval)
+  moe::DownCombineArgs dca;
+  if (down_combine_args(*desc, *weights, plan, workspace, T, &dca)) {
+    if ((s = run_experts(*desc, *weights, x, T, plan, workspace, row_out, dept_out, shared_out,
+                         st, evp(MOE_STAGE_GATEUP), nullptr, true)) != MOE_OK)
+      return s;
+    if (moe::launch_down_combine(dca, y, st, evp(MOE_STAGE_DOWN)) != hipSuccess)
+      return MOE_ERR_HIP;
+    if (stage_events &&
+        (hipEventRecord(ev[MOE_STAGE_COMBINE].start, st) != hipSuccess ||
+         hipEventRecord(ev[MOE_STAGE_COMBINE].stop, st) != hipSuccess))
+      return MOE_ERR_HIP;
+    return MOE_OK;
+  }
   if ((s = run_experts(*desc, *weights, x, T, plan, workspace, row_out, dept_out, shared_out, st,
                        evp(MOE_STAGE_GATEUP), evp(MOE_STAGE_DOWN))) != MOE_OK)
     return s;

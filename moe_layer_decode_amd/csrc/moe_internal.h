@@ -103,6 +103,36 @@ struct CombineArgs {
   int max_dept_rows;       // rows of dept_out
 };
 
+// Down projection with the combine as its epilogue, for decode batches of at
+// most kTokInline tokens (every group is then a small one): each wave owns one
+// output column and streams that column's weight row of every active matrix
+// of every family, so y is written once, with no per-row outputs, atomics or
+// second launch.
+constexpr int kDcWaves = 4;          // waves (output columns) per block
+constexpr int kDcFamilies = 3;       // routed experts, department slices, shared expert
+constexpr int kDcMaxRows = 2048;     // longest intermediate row it streams (4 steps of 512)
+struct DcFamily {
+  const void* down;        // [n_mats][d][rows]
+  const WorkDesc* work;    // small-group descriptors; nullptr: the shared expert (one group, all T tokens)
+  const int* n_items;      // device count of descriptors (unused when work is nullptr)
+  const float* wrow;       // weight of h row r (routing weight or c_{t,J}); nullptr: 1
+  const void* h;           // gate/up outputs, row r at h + r * rows (layer dtype)
+  const int* n_hrows;      // device count of rows of h in use; nullptr: T
+  int rows;                // row length (intermediate size)
+  int max_items;           // host bound on descriptors
+  int max_hrows;           // host bound on the rows of h staged
+  int lds_off;             // element offset of the family's rows of h in LDS
+  int n_mats;              // matrices in the family (bounds check of descriptors)
+};
+struct DownCombineArgs {
+  DcFamily f[kDcFamilies];
+  int nf;                  // families in use (the first nf)
+  int T, d;
+  int h_elems;             // staged elements of h over all families (multiple of 8)
+  int max_items;           // sum of the families' max_items
+};
+size_t down_combine_lds_bytes(const DownCombineArgs& a);
+
 // Factorised form: weighted sum of a (token, department) pair's private
 // outputs, the input of the department down projection.
 struct PairCombineArgs {
@@ -143,6 +173,9 @@ hipError_t launch_down(int w_dtype, const FamilySet& set, int T, int d, int lpr,
                        hipStream_t st, const KernelEvents* ev);
 hipError_t launch_combine(int act_dtype, const CombineArgs& a, void* y, hipStream_t st,
                           const KernelEvents* ev);
+// bf16 layers only; the caller checks T <= kTokInline and the LDS size.
+hipError_t launch_down_combine(const DownCombineArgs& a, void* y, hipStream_t st,
+                               const KernelEvents* ev);
 hipError_t launch_zero(unsigned int* p, size_t n, hipStream_t st);
 hipError_t launch_stream_read(const void* src, size_t blocks, float* sink, hipStream_t st);
 hipError_t launch_pair_combine(int act_dtype, const PairCombineArgs& a, void* zc, int max_pairs,

@@ -2218,6 +2218,227 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a, AT* __
   store_act(y + (size_t)t * a.d + c, acc);
 }
 
+// ---------------------------------------------------------------------------
+// Down projection with the combine as its epilogue, for batches of at most
+// kTokInline tokens.  DeaMoE Eq. (3) sums each token's routing-weighted expert
+// outputs, and W_down is linear, so output column c of token t is
+//   y[t][c] = sum over groups g and rows j of g with token t of
+//             w_{g,j} * (W_down[mat(g)][c] . h[row r_g + j])
+// over the routed experts (w = routing weight), the department slices
+// (w = c_{t,J}) and the shared expert (w = 1).  Wave c streams the weight rows
+// W[mat][c] of every group of every family once, 16 bytes a lane per step,
+// kDcRing steps ahead; each lane keeps one partial dot product per row of the
+// current group and, when the group ends, adds it with the row's weight into
+// its token's accumulator.  The accumulators are reduced over the wave once,
+// at the end, and y is written in the layer dtype.  The groups' rows of h are
+// staged in LDS for the whole block.  Summation order is fixed by the group
+// order of the plan, so results do not depend on timing.
+// ---------------------------------------------------------------------------
+struct DcItem {
+  const bf16_t* w;          // the group's matrix [d][rows]
+  int rows;                 // row length (elements)
+  int nsteps;               // steps of 64 lanes x 8 elements per weight row
+  int n;                    // rows of the group (0: invalid descriptor, streamed and unused)
+  int hoff[kTokInline];     // LDS element offset of the group's row j of h
+  int tok[kTokInline];      // token of row j
+  float wt[kTokInline];     // weight of row j (0 past n)
+};
+
+size_t down_combine_lds_bytes(const DownCombineArgs& a) {
+  return (((size_t)a.h_elems * 2 + 15) & ~(size_t)15) + (size_t)a.max_items * sizeof(DcItem);
+}
+
+constexpr int kDcLoads = 12;  // 16-byte weight loads in flight per lane
+constexpr int kDcMaxSteps = kDcMaxRows / (8 * kWave);  // steps of the longest row
+
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ float uni(float v) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+__device__ __forceinline__ const bf16_t* uni(const bf16_t* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+  return reinterpret_cast<const bf16_t*>(lo | (hi << 32));
+}
+
+// Weight row of column c of group i < ie: NS steps of 64 lanes x 8 elements,
+// through a buffer resource that spans exactly that row, so lanes past the
+// row's end read zeros without a memory access; for i >= ie the resource is
+// empty and every lane reads zeros.  The loads are thereby unconditional:
+// a branch around them would make the compiler wait for all loads in flight
+// before each use instead of only the oldest.
+constexpr int kGfx9BufferDword3 = 0x00020000;  // raw (untyped) 32-bit buffer access
+constexpr int kCpolNt = 2;                     // non-temporal: weights are read once
+
+template <int NS>
+__device__ __forceinline__ void dc_load(const DcItem* items, int i, int ie, int c, int lane,
+                                        u32x4_t (&dst)[NS]) {
+  const DcItem& it = items[min(i, ie - 1)];
+  const int rows = uni(it.rows);
+  const bf16_t* w = uni(it.w) + (size_t)c * rows;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(w), (short)0, i < ie ? rows * 2 : 0, kGfx9BufferDword3);
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+    dst[s] = __builtin_bit_cast(
+        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (lane * 8 + s * 8 * kWave) * 2, 0,
+                                                       kCpolNt));
+}
+
+// Dot products of group i's weight row with its rows of h (LDS), folded into
+// the token accumulators with the rows' weights; nothing outside [ib, ie).
+template <int NS>
+__device__ __forceinline__ void dc_consume(const DcItem* items, int i, int ib, int ie,
+                                           const bf16_t* hl,
+                                           int lane, const u32x4_t (&wv)[NS],
+                                           float (&acc)[kTokInline]) {
+  const DcItem& it = items[min(max(i, ib), ie - 1)];
+  const int rows = uni(it.rows), n = (i >= ib && i < ie) ? uni(it.n) : 0;
+#pragma unroll
+  for (int j = 0; j < kTokInline; ++j) {
+    if (j < n) {
+      const int ho = uni(it.hoff[j]);
+      float part = 0.f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        // past the row's end the weights are zero and h is read at the row's
+        // last 16 bytes (finite values)
+        const int e = min(lane * 8 + s * 8 * kWave, rows - 8);
+        Raw8<bf16_t> w8;
+        w8.u = wv[s];
+        part = dot8(w8, *reinterpret_cast<const X8<bf16_t>*>(hl + ho + e), part);
+      }
+      // a weight of 0 for the other tokens rather than a branch per token
+      // keeps acc in registers
+      const int tk = uni(it.tok[j]);
+      const float wt = uni(it.wt[j]);
+#pragma unroll
+      for (int t = 0; t < kTokInline; ++t) acc[t] = fmaf(tk == t ? wt : 0.f, part, acc[t]);
+    }
+  }
+}
+
+// Groups [ib, ie) of one family (rows of at most NS steps), D groups of loads
+// ahead of the one being used.
+template <int NS>
+__device__ __forceinline__ void dc_family(const DcItem* items, int ib, int ie, int c,
+                                          const bf16_t* hl, int lane, float (&acc)[kTokInline]) {
+  constexpr int D = kDcLoads / NS > 0 ? kDcLoads / NS : 1;
+  // The first pass only loads (groups before ib are not consumed): with no
+  // loads ahead of the loop, the buffers need no copies on entry, and each
+  // use waits only for its own group's loads.
+  u32x4_t buf[D][NS];
+  for (int i0 = ib - D; i0 < ie; i0 += D) {
+#pragma unroll
+    for (int q = 0; q < D; ++q) {
+      dc_consume<NS>(items, i0 + q, ib, ie, hl, lane, buf[q], acc);
+      dc_load<NS>(items, i0 + q + D, ie, c, lane, buf[q]);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kDcWaves * kWave) void down_combine_kernel(DownCombineArgs a,
+                                                                     bf16_t* __restrict__ y) {
+  extern __shared__ __align__(16) unsigned char dc_lds[];
+  bf16_t* hl = reinterpret_cast<bf16_t*>(dc_lds);
+  DcItem* items =
+      reinterpret_cast<DcItem*>(dc_lds + (((size_t)a.h_elems * 2 + 15) & ~(size_t)15));
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int T = a.T, d = a.d;
+  constexpr int STEP = 8 * kWave;  // elements of a weight row per step
+  // The group table (descriptors checked against the family's bounds and the
+  // rows of h in use), and the staging of those rows: family f's rows
+  // [0, nh) are contiguous in global memory and go to hl + lds_off.
+  int fb[kDcFamilies + 1];
+  fb[0] = 0;
+#pragma unroll
+  for (int fi = 0; fi < kDcFamilies; ++fi) {
+    fb[fi + 1] = fb[fi];
+    if (fi < a.nf) {
+      const DcFamily& F = a.f[fi];
+      // (counts read back as wave-uniform values: the group loop bounds and
+      // the weight-row resources built from them stay scalar)
+      const int nf = uni(F.work ? min(max(*F.n_items, 0), F.max_items) : 1);
+      const int nh = uni(F.n_hrows ? min(max(*F.n_hrows, 0), F.max_hrows) : min(T, F.max_hrows));
+      const size_t ms = (size_t)d * F.rows;
+      for (int i = tid; i < nf; i += kDcWaves * kWave) {
+        int mat = 0, r0 = 0, n = 0;
+        int tk[kTokInline] = {0, 1, 2, 3};
+        if (F.work) {
+          // the descriptor as two 16-byte vectors (a struct copy would go
+          // through the private stack)
+          const u32x4_t* wv = reinterpret_cast<const u32x4_t*>(F.work + i);
+          const u32x4_t w0 = wv[0], w1 = wv[1];
+          const int dm = (int)w0.x, dr = (int)w0.y, dn = (int)w0.z;
+          if (dm >= 0 && dm < F.n_mats && dr >= 0 && dn >= 1 && dn <= kTokInline &&
+              dn <= nh - dr) {
+            mat = dm;
+            r0 = dr;
+            n = dn;
+            tk[0] = (int)w0.w;
+            tk[1] = (int)w1.x;
+            tk[2] = (int)w1.y;
+            tk[3] = (int)w1.z;
+          }
+        } else {
+          n = min(min(T, kTokInline), nh);  // the shared expert: row t is token t
+        }
+        DcItem it;
+        it.w = static_cast<const bf16_t*>(F.down) + (size_t)mat * ms;
+        it.rows = F.rows;
+        it.nsteps = (F.rows + STEP - 1) / STEP;
+        it.n = n;
+#pragma unroll
+        for (int j = 0; j < kTokInline; ++j) {
+          it.hoff[j] = F.lds_off + (r0 + min(j, max(n - 1, 0))) * F.rows;
+          it.tok[j] = min(max(tk[j], 0), T - 1);
+          it.wt[j] = j < n ? (F.wrow ? F.wrow[r0 + j] : 1.f) : 0.f;
+        }
+        items[fb[fi] + i] = it;
+      }
+      const int nch = nh * (F.rows / 8);  // 16-byte chunks of the rows in use
+      const bf16_t* src = static_cast<const bf16_t*>(F.h);
+      for (int q = wid; q * kWave < nch; q += kDcWaves) {
+        const int ch = q * kWave + lane;
+        if (ch < nch)
+          __builtin_amdgcn_global_load_lds(src + (size_t)ch * 8,
+                                           (lds_void_t*)(hl + F.lds_off + q * STEP), 16, 0, 0);
+      }
+      fb[fi + 1] += nf;
+    }
+  }
+  // every wave's staged rows have landed, and the table is complete, for the block
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const int c = uni((int)(blockIdx.x * kDcWaves) + wid);  // wave-uniform: scalar resource base
+  if (c >= d) return;
+  float acc[kTokInline];
+#pragma unroll
+  for (int t = 0; t < kTokInline; ++t) acc[t] = 0.f;
+#pragma unroll
+  for (int fi = 0; fi < kDcFamilies; ++fi) {
+    if (fi < a.nf && fb[fi] < fb[fi + 1]) {
+      const int ns = (a.f[fi].rows + STEP - 1) / STEP;
+      if (ns <= 1)
+        dc_family<1>(items, fb[fi], fb[fi + 1], c, hl, lane, acc);
+      else if (ns == 2)
+        dc_family<2>(items, fb[fi], fb[fi + 1], c, hl, lane, acc);
+      else if (ns == 3)
+        dc_family<3>(items, fb[fi], fb[fi + 1], c, hl, lane, acc);
+      else
+        dc_family<kDcMaxSteps>(items, fb[fi], fb[fi + 1], c, hl, lane, acc);
+    }
+  }
+  // lane 16 t holds token t's sum
+  float v[kTokInline];
+#pragma unroll
+  for (int j = 0; j < kTokInline; ++j) v[j] = acc[j];
+  wave_reduce_scatter<kTokInline>(v, lane);
+  const int t = lane >> 4;
+  if ((lane & 15) == 0 && t < T) y[(size_t)t * d + c] = f32_to_bf16(v[0]);
+}
+
 __global__ void zero_kernel(unsigned int* p, size_t n) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x)
@@ -2367,6 +2588,19 @@ hipError_t launch_combine(int act_dtype, const CombineArgs& a, void* y, hipStrea
     launch(combine_kernel<bf16_t>, grid, block, st, ev, a, static_cast<bf16_t*>(y));
   else
     launch(combine_kernel<float>, grid, block, st, ev, a, static_cast<float*>(y));
+  return hipGetLastError();
+}
+
+hipError_t launch_down_combine(const DownCombineArgs& a, void* y, hipStream_t st,
+                               const KernelEvents* ev) {
+  const dim3 grid((a.d + kDcWaves - 1) / kDcWaves), block(kDcWaves * kWave);
+  const size_t lds = down_combine_lds_bytes(a);
+  auto k = down_combine_kernel;
+  bf16_t* yo = static_cast<bf16_t*>(y);
+  if (ev)
+    hipExtLaunchKernelGGL(k, grid, block, lds, st, ev->start, ev->stop, 0, a, yo);
+  else
+    hipLaunchKernelGGL(k, grid, block, lds, st, a, yo);
   return hipGetLastError();
 }
 

@@ -608,6 +608,53 @@ def test_layer_edge_shapes():
         assert_close(to_np(y), ref, "f32", f"edge case {c}")
 
 
+@pytest.mark.parametrize("case", [
+    # (d, E, k, I, m, S, Is): rows of one step with idle lanes (I = 40, Is = 24),
+    # rows of several steps with a ragged last one (I = 1096: 137 chunks of 16
+    # bytes over 64 lanes), department slices with the shared expert, a d that
+    # leaves the last block with one live wave (d = 776 = 4 * 194)
+    (776, 6, 3, 40, 0, 0, 24),
+    (264, 8, 2, 1096, 0, 0, 0),
+    (1024, 16, 4, 96, 4, 160, 64),
+    (520, 12, 6, 56, 3, 200, 0),
+])
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
+def test_layer_down_with_combine_epilogue(case, T):
+    """bf16 layers at batches of at most four tokens take the down projection
+    that writes y itself (each wave one output column over every group of
+    every family); against the oracle's per-token evaluation of the GPU's
+    selection, every token."""
+    d, E, k, I, m, S, Is = case
+    w = _rand_weights(sum(case) + T, d, E, I, m, S, Is, torch.bfloat16)
+    g = torch.Generator().manual_seed(T)
+    x = torch.randn(T, d, generator=g).to(torch.bfloat16).to(DEV)
+    desc = M.layer_desc(d, E, k, I, n_depts=m, d_ff_dept=S, d_ff_shared=Is, dtype="bf16",
+                        max_tokens=4)
+    y, layer = run_layer(desc, w, x)
+    wc = {kk: v.cpu() for kk, v in w.items()}
+    o_ids, o_w, o_sel, _ = O.route(x.cpu(), wc["w_router"], k)
+    g_ids, _ = gpu_ids_from_plan(layer.plan(T), T, k)
+    ids, _ = reference_ids(o_ids, o_sel, g_ids, k)
+    ref = O.layer_bruteforce(x.cpu(), wc, ids, o_w, E, m)
+    assert_close(to_np(y), ref, "bf16", f"fused down+combine {case} T={T}")
+    # the same step without the fused epilogue: per-row outputs, then the
+    # combine (summation orders differ, so bf16-rounding agreement)
+    ws = M.alloc_workspace(desc, DEV)
+    g_ids_t = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    g_w_t = torch.empty(T, k, dtype=torch.float32, device=DEV)
+    M.moe_route(desc, x, w["w_router"], None, g_ids_t, g_w_t, ws)
+    plan = M.moe_dispatch(desc, g_ids_t, g_w_t, ws)
+    row_out = torch.empty(T * k, d, device=DEV)
+    dept_out = torch.empty(T * min(m, k), d, device=DEV) if m else None
+    shared_out = torch.empty(T, d, device=DEV) if Is else None
+    M.moe_expert_ffn(desc, w, x, plan, ws, row_out, dept_out, shared_out)
+    y2 = torch.empty_like(y)
+    M.moe_combine(desc, plan, row_out, dept_out, shared_out, y2)
+    torch.cuda.synchronize()
+    a, b = to_np(y), to_np(y2)
+    np.testing.assert_allclose(a, b, rtol=2 ** -7, atol=1e-6 * np.abs(b).max())
+
+
 def test_layer_zero_tokens_and_errors():
     shape = SH[TINY]
     w = gpu_layer(TINY, 0)
@@ -660,7 +707,10 @@ def test_stage_events_time_each_kernel():
     assert torch.equal(y0, y1)
     for s in range(M.N_STAGES):
         ms = evs[2 * s].elapsed_time(evs[2 * s + 1])
-        assert 0.0 < ms < 50.0, (M.STAGE_NAMES[s], ms)
+        # at four tokens the down launch writes y itself: the combine stage is
+        # an empty interval
+        lo = 0.0 if M.STAGE_NAMES[s] == "combine" else 1e-6
+        assert lo <= ms < 50.0, (M.STAGE_NAMES[s], ms)
 
 
 def test_stream_read_sums_each_16k_block():
