@@ -516,9 +516,10 @@ moe_status run_experts(const moe_layer_desc& d, const moe_weights& w, const void
 // The down projection with the combine as its epilogue (one launch writing y)
 // serves bf16 layers in the plain and slice forms at batches of at most
 // kTokInline tokens, where every group is small, when the rows of h it stages
-// fit kDcMaxLds and no intermediate row is longer than kDcMaxRows.  Returns false (and fills nothing) otherwise; the step then
+// fit kDcMaxLds (two blocks per CU) and no intermediate row is longer than
+// kDcMaxRows.  Returns false (and fills nothing) otherwise; the step then
 // takes the separate down and combine launches.
-constexpr size_t kDcMaxLds = 64 * 1024;
+constexpr size_t kDcMaxLds = 80 * 1024;
 bool down_combine_args(const moe_layer_desc& d, const moe_weights& w, const moe_plan& p,
                        void* ws, int32_t T, moe::DownCombineArgs* out) {
   if (d.w_dtype != MOE_BF16 || d.act_dtype != MOE_BF16 || factorised(d)) return false;

@@ -108,7 +108,7 @@ struct CombineArgs {
 // output column and streams that column's weight row of every active matrix
 // of every family, so y is written once, with no per-row outputs, atomics or
 // second launch.
-constexpr int kDcWaves = 4;          // waves (output columns) per block
+constexpr int kDcWaves = 8;          // waves (output columns) per block
 constexpr int kDcFamilies = 3;       // routed experts, department slices, shared expert
 constexpr int kDcMaxRows = 2048;     // longest intermediate row it streams (4 steps of 512)
 struct DcFamily {

@@ -2248,7 +2248,7 @@ size_t down_combine_lds_bytes(const DownCombineArgs& a) {
   return (((size_t)a.h_elems * 2 + 15) & ~(size_t)15) + (size_t)a.max_items * sizeof(DcItem);
 }
 
-constexpr int kDcLoads = 12;  // 16-byte weight loads in flight per lane
+constexpr int kDcLoads = 4;   // 16-byte weight loads in flight per lane
 constexpr int kDcMaxSteps = kDcMaxRows / (8 * kWave);  // steps of the longest row
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }

@@ -611,8 +611,8 @@ def test_layer_edge_shapes():
 @pytest.mark.parametrize("case", [
     # (d, E, k, I, m, S, Is): rows of one step with idle lanes (I = 40, Is = 24),
     # rows of several steps with a ragged last one (I = 1096: 137 chunks of 16
-    # bytes over 64 lanes), department slices with the shared expert, a d that
-    # leaves the last block with one live wave (d = 776 = 4 * 194)
+    # bytes over 64 lanes), department slices with and without the shared
+    # expert
     (776, 6, 3, 40, 0, 0, 24),
     (264, 8, 2, 1096, 0, 0, 0),
     (1024, 16, 4, 96, 4, 160, 64),
