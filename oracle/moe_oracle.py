@@ -70,6 +70,13 @@ justification in the design notes):
      is the last of its department would not raise the coverage, so such
      experts are skipped; k >= k_dept makes every step possible.  The final
      slots are ordered by (score desc, index asc) like every selection.
+  R20 FP8 expert weights ([DeaMoE] section 2.2 sizes a DeepSeek-V3 expert
+     stored in FP8; the pages fix neither the format nor a scaling scheme):
+     codes are OCP E4M3 (the OCP 8-bit floating point specification), and
+     each output row of each expert matrix carries one fp32 scale, so the
+     weight is scale[row] * value(code).  The router stays in the activation
+     dtype.  The oracle computes the layer on these dequantized weights
+     exactly; the quantization error belongs to the inputs.
 """
 from __future__ import annotations
 
@@ -85,7 +92,8 @@ __all__ = [
     "deamoe_expert", "deamoe_token_output", "deamoe_layer_per_expert",
     "deamoe_layer_two_stage", "deamoe_layer_precombined",
     "select_from_scores", "topk_select_grouped", "topk_select_strict", "silu", "cast_output", "SOFTMAX", "SIGMOID",
-    "SOFTMAX_BIAS",
+    "SOFTMAX_BIAS", "fp8_e4m3_decode", "fp8_dequantize", "dequantize_layer",
+    "loaded_weight_bytes_fp8",
 ]
 
 SOFTMAX, SIGMOID, SOFTMAX_BIAS = "softmax", "sigmoid", "softmax_bias"
@@ -629,3 +637,74 @@ def loaded_weight_bytes(ids, n_experts: int, d: int, d_ff: int, bytes_per_w: int
         g = n_experts // n_depts
         n += len({e // g for e in experts}) * 3 * d * d_ff_dept
     return n * bytes_per_w
+
+
+# ----------------------------------------------------------------------------
+# FP8 expert weights  (reading R20: OCP E4M3 codes, one fp32 scale per
+# output row)
+# ----------------------------------------------------------------------------
+
+def fp8_e4m3_decode(codes) -> np.ndarray:
+    """Values of OCP E4M3 codes in float64, from the format's definition:
+    bit 7 is the sign, bits 6..3 the exponent field E (bias 7), bits 2..0
+    the mantissa field M.  E = 0 holds zero and the subnormals M/8 * 2^-6;
+    otherwise the value is (1 + M/8) * 2^(E-7).  The two codes with E = 15
+    and M = 7 are NaN; the format has no infinities, so E = 15 with M < 7 is
+    finite (up to 448)."""
+    c = np.asarray(codes).astype(np.int64) & 0xFF
+    sign = np.where(c >= 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m, -9), np.ldexp(8.0 + m, e - 10))
+    return np.where((c & 0x7F) == 0x7F, np.nan, sign * mag)
+
+
+def fp8_dequantize(codes, scales) -> np.ndarray:
+    """Weight matrix from its codes [..., rows, cols] and per-row scales
+    [..., rows]: W[..., r, c] = scales[..., r] * value(codes[..., r, c])."""
+    v = fp8_e4m3_decode(codes)
+    s = _f64(scales)
+    assert s.shape == v.shape[:-1], (s.shape, v.shape)
+    return v * s[..., None]
+
+
+_FP8_MATS = ("w_gate", "w_up", "w_down", "wd_gate", "wd_up", "wd_down",
+             "ws_gate", "ws_up", "ws_down")
+
+
+def dequantize_layer(weights) -> Dict[str, np.ndarray]:
+    """The layer's weights with every FP8 expert matrix (codes under its own
+    name, per-row scales under name + "_scale") replaced by its float64
+    dequantized values; the router and bias are passed through."""
+    out = {}
+    for k, v in weights.items():
+        if k.endswith("_scale"):
+            continue
+        if k in _FP8_MATS and (k + "_scale") in weights:
+            codes = v.detach().cpu().numpy() if hasattr(v, "detach") else np.asarray(v)
+            out[k] = fp8_dequantize(codes, weights[k + "_scale"])
+        else:
+            out[k] = v
+    return out
+
+
+def loaded_weight_bytes_fp8(ids, n_experts: int, d: int, d_ff: int, router_bytes: int,
+                            n_depts: int = 0, d_ff_dept: int = 0,
+                            d_ff_shared: int = 0) -> int:
+    """Bytes one decode step reads with FP8 expert matrices: the router
+    (E*d at router_bytes each), one byte per expert weight and a 4-byte
+    scale per output row of every matrix read (gate and up rows are I long,
+    down rows d)."""
+    ids = np.asarray(ids).reshape(-1)
+    experts = {int(e) for e in ids if 0 <= e < n_experts}
+
+    def mat3(rows_i):  # gate, up (rows_i rows of d) and down (d rows of rows_i)
+        return 3 * d * rows_i + 4 * (2 * rows_i + d)
+    n = n_experts * d * router_bytes
+    n += len(experts) * mat3(d_ff)
+    if d_ff_shared:
+        n += mat3(d_ff_shared)
+    if n_depts:
+        g = n_experts // n_depts
+        n += len({e // g for e in experts}) * mat3(d_ff_dept)
+    return n

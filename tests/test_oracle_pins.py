@@ -642,3 +642,123 @@ def test_strict_coverage_route_weights():
     for t in range(T):
         e = np.exp(l32[t, ids[t]].astype(np.float64) - l32[t, ids[t]].max())
         np.testing.assert_allclose(w[t], e / e.sum(), rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# FP8 expert weights: OCP E4M3 codes with one fp32 scale per output row.
+# The decoder is pinned to the format's definition (named values, structure)
+# and to torch's float8_e4m3fn conversion; the dequantized layer to a closed
+# form.
+# ---------------------------------------------------------------------------
+
+def test_fp8_decode_named_values():
+    """Values the E4M3 definition fixes: zero and negative zero, the smallest
+    subnormal 2^-9 and the largest 7 * 2^-9, the smallest normal 2^-6, 1.0,
+    1.5, 2.0, the exponent-15 codes that are finite (256 .. 448, no
+    infinities), and the two NaN codes."""
+    v = O.fp8_e4m3_decode(np.arange(256))
+    named = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6,
+             0x38: 1.0, 0x3C: 1.5, 0x40: 2.0, 0x77: 240.0, 0x78: 256.0,
+             0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0, 0x81: -(2.0 ** -9)}
+    for c, want in named.items():
+        assert v[c] == want, hex(c)
+    assert v[0x80] == 0.0 and np.signbit(v[0x80])
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF])
+    assert np.isfinite(v).sum() == 254
+
+
+def test_fp8_decode_structure():
+    """Positive codes 0x00..0x7E increase strictly, negative codes mirror
+    them, every finite value is an integer multiple of 2^-9, and inside each
+    binade (exponent field E >= 1) the spacing is 2^(E-10)."""
+    v = O.fp8_e4m3_decode(np.arange(256))
+    pos = v[:0x7F]
+    assert np.all(np.diff(pos) > 0)
+    assert np.array_equal(v[0x80:0xFF], -pos)
+    fin = v[np.isfinite(v)]
+    assert np.array_equal(fin * 512.0, np.round(fin * 512.0))
+    for e in range(1, 16):
+        codes = [(e << 3) | m for m in range(8) if ((e << 3) | m) < 0x7F]
+        steps = np.diff(v[codes])
+        assert np.all(steps == 2.0 ** (e - 10)), e
+
+
+def test_fp8_decode_matches_torch_float8_e4m3fn():
+    """Every code against torch's float8_e4m3fn -> float32 conversion."""
+    if not hasattr(torch, "float8_e4m3fn"):
+        pytest.skip("torch has no float8_e4m3fn")
+    t = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float32)
+    ref = t.double().numpy()
+    v = O.fp8_e4m3_decode(np.arange(256))
+    assert np.array_equal(np.isnan(v), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(v[ok], ref[ok])
+    assert np.array_equal(np.signbit(v[ok]), np.signbit(ref[ok]))
+
+
+def test_fp8_dequantize_scales_rows():
+    """Each output row takes its own scale: on a non-square [2][3][5] code
+    array with a distinct scale per (matrix, row), W[e][r][c] = s[e][r] *
+    value(code[e][r][c]) element by element (a column-wise or transposed
+    scale fails the shape check or the values)."""
+    rng = _rng(3)
+    codes = rng.integers(0, 0x7F, (2, 3, 5)).astype(np.uint8)
+    codes[1] |= 0x80  # negative half
+    s = np.array([[0.5, 2.0, 3.0], [0.25, 8.0, 1.5]])
+    W = O.fp8_dequantize(codes, s)
+    for e in range(2):
+        for r in range(3):
+            for c in range(5):
+                assert W[e, r, c] == s[e, r] * O.fp8_e4m3_decode(codes[e, r, c])
+    with pytest.raises(AssertionError):
+        O.fp8_dequantize(codes, s.T)
+
+
+def test_fp8_layer_with_unit_codes_is_closed_form():
+    """Every expert code 0x38 (1.0): gate row i is g_i * (1, ..., 1) with g_i
+    its scale, so expert e gives o_c = sd_c * sum_i SiLU(sg_i S) su_i S with
+    S = sum(x); the layer output is the routing-weighted sum of those, plus
+    the shared expert's own closed form."""
+    rng = _rng(5)
+    d, E, I, Is, k, T = 24, 5, 16, 8, 2, 3
+    x = rng.normal(0, 0.3, (T, d))
+    codes = lambda *sh: np.full(sh, 0x38, np.uint8)  # noqa: E731
+    w = {"w_router": rng.normal(0, 0.3, (E, d)),
+         "w_gate": codes(E, I, d), "w_up": codes(E, I, d), "w_down": codes(E, d, I),
+         "ws_gate": codes(Is, d), "ws_up": codes(Is, d), "ws_down": codes(d, Is),
+         "w_gate_scale": rng.uniform(0.01, 0.1, (E, I)), "w_up_scale": rng.uniform(0.01, 0.1, (E, I)),
+         "w_down_scale": rng.uniform(0.01, 0.1, (E, d)),
+         "ws_gate_scale": rng.uniform(0.01, 0.1, Is), "ws_up_scale": rng.uniform(0.01, 0.1, Is),
+         "ws_down_scale": rng.uniform(0.01, 0.1, d)}
+    wd = O.dequantize_layer(w)
+    ids, tw, _, _ = O.route(x, w["w_router"], k)
+    y = O.layer_bruteforce(x, wd, ids, tw, E)
+    for t in range(T):
+        S = x[t].sum()
+        want = np.zeros(d)
+        for j in range(k):
+            e = ids[t, j]
+            h = _silu_ref(w["w_gate_scale"][e] * S) * (w["w_up_scale"][e] * S)
+            want += tw[t, j] * w["w_down_scale"][e] * h.sum()
+        hs = _silu_ref(w["ws_gate_scale"] * S) * (w["ws_up_scale"] * S)
+        want += w["ws_down_scale"] * hs.sum()
+        np.testing.assert_allclose(y[t], want, rtol=1e-12, atol=1e-15)
+
+
+def test_fp8_loaded_bytes_of_a_deepseek_v3_expert():
+    """[DeaMoE] section 2.2: a DeepSeek-V3 expert in FP8 is about 44 MB.
+    One byte per weight of its three [7168, 2048] matrices plus a 4-byte
+    scale per output row (2048 + 2048 + 7168 rows) gives 44.09 MB; a step that
+    selects one expert reads that plus the router."""
+    from moe_synth import SHAPES
+    s = SHAPES["deepseek_v3_d7168_e256_i2048_s2048_top8"]
+    one = O.loaded_weight_bytes_fp8([[3]], s.n_experts, s.d, s.d_ff, router_bytes=2)
+    router = s.n_experts * s.d * 2
+    assert (one - router) == 3 * 7168 * 2048 + 4 * (2 * 2048 + 7168)
+    assert (one - router) / 1e6 == pytest.approx(44.09, abs=0.01)
+    # two distinct experts, the shared expert and a department slice each once
+    # (12 experts in 2 departments of 6: experts 3 and 9 sit in different ones)
+    two = O.loaded_weight_bytes_fp8([[3, 9], [9, 3]], 12, 16, 4, router_bytes=2,
+                                    n_depts=2, d_ff_dept=8, d_ff_shared=8)
+    mat3 = lambda r: 3 * 16 * r + 4 * (2 * r + 16)  # noqa: E731
+    assert two == 12 * 16 * 2 + 2 * mat3(4) + mat3(8) + 2 * mat3(8)
