@@ -224,33 +224,41 @@ def desc_of(M, shape, max_tokens):
                         score=shape.score, renormalize=shape.renormalize,
                         route_scale=shape.route_scale, dtype=shape.dtype, max_tokens=max_tokens,
                         dept_form=shape.dept_form, k_dept=shape.k_dept,
-                        dept_strict=shape.dept_strict)
+                        dept_strict=shape.dept_strict, expert_dtype=shape.expert_dtype)
 
 
 def gateup_bytes(shape, T, n_active, n_active_depts, n_rows, n_dept_rows):
     """Algorithmic bytes of the gate/up stage: gate+up weights of every active
-    matrix once (private transforms are S x S in the factorised form), the T
-    activation rows read, the h rows written (layer dtype)."""
-    wb = 4 if shape.dtype == "f32" else 2
+    matrix once (private transforms are S x S in the factorised form; FP8:
+    one byte per weight plus a 4-byte scale per row), the T activation rows
+    read, the h rows written (activation dtype)."""
+    ab = 4 if shape.dtype == "f32" else 2
+    fp8 = shape.expert_dtype == "fp8"
+    wb = 1 if fp8 else ab
     d = shape.d
     k_priv = shape.d_ff if shape.dept_form == "factorised" else d
-    b = n_active * 2 * shape.d_ff * k_priv * wb
-    b += n_active_depts * 2 * shape.d_ff_dept * d * wb
-    b += (2 * shape.d_ff_shared * d * wb) if shape.d_ff_shared else 0
-    b += T * d * wb
-    b += wb * (n_rows * shape.d_ff + n_dept_rows * shape.d_ff_dept + T * shape.d_ff_shared)
+    b = n_active * 2 * shape.d_ff * (k_priv * wb + (4 if fp8 else 0))
+    b += n_active_depts * 2 * shape.d_ff_dept * (d * wb + (4 if fp8 else 0))
+    b += (2 * shape.d_ff_shared * (d * wb + (4 if fp8 else 0))) if shape.d_ff_shared else 0
+    b += T * d * ab
+    b += ab * (n_rows * shape.d_ff + n_dept_rows * shape.d_ff_dept + T * shape.d_ff_shared)
     return b
 
 
 def down_bytes(shape, T, n_active, n_active_depts, n_rows, n_dept_rows):
     """Algorithmic bytes of the down stage: down weights of every active matrix
-    once, the h rows read (layer dtype), the fp32 output rows written."""
-    wb = 4 if shape.dtype == "f32" else 2
+    once (FP8: one byte per weight plus a 4-byte scale per output row), the h
+    rows read (activation dtype), the fp32 output rows written."""
+    ab = 4 if shape.dtype == "f32" else 2
+    fp8 = shape.expert_dtype == "fp8"
+    wb = 1 if fp8 else ab
     d = shape.d
     n_priv = shape.d_ff if shape.dept_form == "factorised" else d
-    b = n_active * shape.d_ff * n_priv * wb + n_active_depts * shape.d_ff_dept * d * wb
-    b += (shape.d_ff_shared * d * wb) if shape.d_ff_shared else 0
-    b += wb * (n_rows * shape.d_ff + n_dept_rows * shape.d_ff_dept + T * shape.d_ff_shared)
+    sc = 4 if fp8 else 0
+    b = n_active * n_priv * (shape.d_ff * wb + sc)
+    b += n_active_depts * d * (shape.d_ff_dept * wb + sc)
+    b += (d * (shape.d_ff_shared * wb + sc)) if shape.d_ff_shared else 0
+    b += ab * (n_rows * shape.d_ff + n_dept_rows * shape.d_ff_dept + T * shape.d_ff_shared)
     b += 4 * (n_rows * n_priv + n_dept_rows * d + (T * d if shape.d_ff_shared else 0))
     return b
 
@@ -496,6 +504,8 @@ def cpu_baseline(shape, T, base, seconds):
     except Exception:
         cores = 1
     host = {k: v.detach().cpu() for k, v in base.items()}
+    if shape.expert_dtype == "fp8":  # the layer on its dequantized weights
+        host = O.dequantize_layer(host)
     x = moe_synth.make_tokens(shape, 0, T, "cpu")
     n, t0 = 0, time.perf_counter()
     while True:
@@ -624,7 +634,9 @@ def main():
                    "timing": "hipgraph" if per_batch[str(head_T)]["graph_matches_eager"] else "eager"},
         "hbm_GBps": per_batch[str(head_T)]["GBps"],
         "batches": per_batch,
-        "roofline": {"bound": "hbm", "kernel": "gateup_kernel", "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm",
+                     "kernel": "gateup_fp8_kernel" if shape.expert_dtype == "fp8" else "gateup_kernel",
+                     "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic() if shape.name == HEADLINE and head_T == 16 else None,
                      "algorithmic_bytes_per_launch": gu,

@@ -58,6 +58,16 @@
  *   w_gate, w_up         [E][S][S]     A_g^i, A_u^i     (private transforms)
  *   w_down               [E][S][S]     (A_d^i)^T
  *   Every pointer must be 16-byte aligned; d, I, S, Is must be multiples of 8.
+ *
+ * FP8 expert weights (w_dtype = MOE_FP8_E4M3; plain and slice forms)
+ *   The DeaMoE page sizes a DeepSeek-V3 expert stored in FP8 (section 2.2)
+ *   without fixing a format: here every expert matrix above (routed,
+ *   department, shared) holds OCP E4M3 codes, one byte per weight, in the
+ *   same layout, and each of its output rows carries one float32 scale:
+ *     *_gate_scale, *_up_scale   [.][I] / [m][S] / [Is]  (one per gate/up row)
+ *     *_down_scale               [.][d] / [m][d] / [d]   (one per output column)
+ *   weight = scale[row] * value(code).  The router stays in act_dtype (BF16).
+ *   d, I, S, Is must be multiples of 16 and at most MOE_FP8_MAX_WIDTH.
  */
 #ifndef MOE_DECODE_H
 #define MOE_DECODE_H
@@ -77,7 +87,13 @@ typedef enum {
   MOE_ERR_HIP = 4            /* the HIP runtime reported an error (launch or earlier fault) */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+typedef enum {
+  MOE_F32 = 0,
+  MOE_BF16 = 1,
+  /* OCP 8-bit floating point E4M3 (bias 7, no infinities, S.1111.111 = NaN)
+   * expert codes with per-row float32 scales; w_dtype only */
+  MOE_FP8_E4M3 = 2
+} moe_dtype;
 
 typedef enum {
   /* rank the logits; weights = softmax over the selected logits
@@ -105,6 +121,7 @@ typedef enum {
 #define MOE_MAX_ASSIGNMENTS 4096      /* max_tokens * top_k */
 #define MOE_MAX_DEPT_PAIRS 4096       /* max_tokens * n_depts */
 #define MOE_MAX_DEPTS_GROUPED 64      /* n_depts limit when k_dept > 0 */
+#define MOE_FP8_MAX_WIDTH 8192        /* FP8 layers: largest d, I, S, Is */
 
 typedef struct {
   int32_t d_model;       /* d */
@@ -117,7 +134,9 @@ typedef struct {
   int32_t score_fn;      /* moe_score_fn */
   int32_t renormalize;   /* 1: weights sum to route_scale; 0: softmax probabilities / raw sigmoid */
   float route_scale;     /* multiplies every routing weight */
-  int32_t w_dtype;       /* moe_dtype of all weight matrices */
+  int32_t w_dtype;       /* moe_dtype of all weight matrices; MOE_FP8_E4M3: the expert
+                          * matrices (codes + per-row scales, see above), the router in
+                          * act_dtype, which must be MOE_BF16 (factorised form: unsupported) */
   int32_t act_dtype;     /* moe_dtype of x and y (MOE_F32 with MOE_F32 weights, else MOE_BF16) */
   int32_t max_tokens;    /* largest T a workspace sized for this descriptor accepts */
   int32_t dept_form;     /* moe_dept_form (n_depts > 0); factorised requires d_ff == d_ff_dept */
@@ -148,6 +167,17 @@ typedef struct {
   const void* ws_gate;        /* shared expert: required iff d_ff_shared > 0 */
   const void* ws_up;
   const void* ws_down;
+  /* per-row float32 scales of FP8 expert matrices (w_dtype = MOE_FP8_E4M3):
+   * required for each matrix present, ignored otherwise */
+  const float* w_gate_scale;  /* [E][I] */
+  const float* w_up_scale;    /* [E][I] */
+  const float* w_down_scale;  /* [E][d] */
+  const float* wd_gate_scale; /* [m][S] */
+  const float* wd_up_scale;   /* [m][S] */
+  const float* wd_down_scale; /* [m][d] */
+  const float* ws_gate_scale; /* [Is] */
+  const float* ws_up_scale;   /* [Is] */
+  const float* ws_down_scale; /* [d] */
 } moe_weights;
 
 /* Plan header entries (int32, device). */
@@ -278,7 +308,8 @@ const char* moe_status_string(moe_status status);
 
 /* Bytes of weights one step streams for the given active counts: router,
  * n_active routed experts, n_active_depts department slices, the shared
- * expert (each matrix read once).  Host-only. */
+ * expert (each matrix read once; FP8 layers: one byte per expert weight plus
+ * the 4-byte row scales, the router in act_dtype).  Host-only. */
 uint64_t moe_loaded_weight_bytes(const moe_layer_desc* desc, int32_t n_active,
                                  int32_t n_active_depts);
 

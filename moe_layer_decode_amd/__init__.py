@@ -24,11 +24,12 @@ __all__ = [
     "moe_loaded_weight_bytes", "moe_stream_read", "alloc_workspace", "plan_to_host", "MoeLayer",
     "MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE",
     "MOE_ERR_HIP", "SCORE_FNS", "DEPT_FORMS", "MOE_DEPT_SLICE", "MOE_DEPT_FACTORISED",
+    "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3",
     "N_STAGES", "STAGE_NAMES", "EXPORTED_SYMBOLS",
 ]
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-MOE_F32, MOE_BF16 = 0, 1
+MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_DEPT_SLICE, MOE_DEPT_FACTORISED = 0, 1
 DEPT_FORMS = {"slice": MOE_DEPT_SLICE, "factorised": MOE_DEPT_FACTORISED}
 SCORE_FNS = {"softmax": 0, "sigmoid": 1, "softmax_bias": 2}
@@ -57,9 +58,13 @@ class LayerDesc(ctypes.Structure):
         return torch.bfloat16 if self.act_dtype == MOE_BF16 else torch.float32
 
 
+_MATS = ("w_gate", "w_up", "w_down", "wd_gate", "wd_up", "wd_down", "ws_gate", "ws_up",
+         "ws_down")
+
+
 class Weights(ctypes.Structure):
-    _fields_ = [(n, _vp) for n in ("w_router", "router_bias", "w_gate", "w_up", "w_down",
-                                   "wd_gate", "wd_up", "wd_down", "ws_gate", "ws_up", "ws_down")]
+    _fields_ = [(n, _vp) for n in ("w_router", "router_bias", *_MATS,
+                                   *(m + "_scale" for m in _MATS))]
 
 
 _PLAN_ARRAYS = ("header", "counts", "offsets", "row_token", "row_slot", "row_expert",
@@ -151,10 +156,13 @@ def layer_desc(d_model: int, n_experts: int, top_k: int, d_ff: int, *, n_depts: 
                d_ff_dept: int = 0, d_ff_shared: int = 0, score: str = "softmax",
                renormalize: bool = True, route_scale: float = 1.0, dtype: str = "bf16",
                max_tokens: int = 32, dept_form: str = "slice", k_dept: int = 0,
-               dept_strict: bool = False) -> LayerDesc:
+               dept_strict: bool = False, expert_dtype: str = "") -> LayerDesc:
+    """dtype: weights and activations ("bf16" | "f32"); expert_dtype "fp8":
+    the expert matrices are E4M3 codes with per-row scales (bf16 only)."""
     dt = MOE_BF16 if dtype == "bf16" else MOE_F32
+    wdt = MOE_FP8_E4M3 if expert_dtype == "fp8" else dt
     return LayerDesc(d_model, n_experts, top_k, d_ff, n_depts, d_ff_dept, d_ff_shared,
-                     SCORE_FNS[score], int(bool(renormalize)), float(route_scale), dt, dt,
+                     SCORE_FNS[score], int(bool(renormalize)), float(route_scale), wdt, dt,
                      max_tokens, DEPT_FORMS[dept_form], k_dept, int(dept_strict))
 
 
@@ -215,14 +223,24 @@ def _stream(device) -> int:
 
 
 def _wdt(desc):
+    """torch dtype of the expert matrices (FP8: their raw E4M3 codes)."""
+    if desc.w_dtype == MOE_FP8_E4M3:
+        return torch.uint8
     return torch.bfloat16 if desc.w_dtype == MOE_BF16 else torch.float32
+
+
+def _rdt(desc):
+    """torch dtype of the router (the activation dtype next to FP8 experts)."""
+    return desc.torch_dtype if desc.w_dtype == MOE_FP8_E4M3 else _wdt(desc)
 
 
 def _weights_struct(desc: LayerDesc, w: Dict[str, torch.Tensor]) -> Weights:
     E, d, I = desc.n_experts, desc.d_model, desc.d_ff
     wdt = _wdt(desc)
     s = Weights()
-    shapes = {"w_router": (E, d), "w_gate": (E, I, d), "w_up": (E, I, d), "w_down": (E, d, I)}
+    shapes = {"w_gate": (E, I, d), "w_up": (E, I, d), "w_down": (E, d, I)}
+    if w.get("w_router") is not None:
+        s.w_router = _ptr(w["w_router"], "w_router", _rdt(desc), (E, d))
     if desc.n_depts and desc.dept_form == MOE_DEPT_FACTORISED:
         # private transforms A_g, A_u and (A_d)^T are S x S (I == S)
         shapes.update(w_gate=(E, I, I), w_up=(E, I, I), w_down=(E, I, I))
@@ -235,6 +253,11 @@ def _weights_struct(desc: LayerDesc, w: Dict[str, torch.Tensor]) -> Weights:
     for name, shp in shapes.items():
         if name in w and w[name] is not None:
             setattr(s, name, _ptr(w[name], name, wdt, shp))
+            if desc.w_dtype == MOE_FP8_E4M3:  # one fp32 scale per output row
+                sc = w.get(name + "_scale")
+                setattr(s, name + "_scale",
+                        _ptr(sc, name + "_scale", torch.float32, shp[:-1]) if sc is not None
+                        else None)
     if w.get("router_bias") is not None:
         s.router_bias = _ptr(w["router_bias"], "router_bias", torch.float32, (E,))
     return s
@@ -252,7 +275,7 @@ def moe_route(desc: LayerDesc, x: torch.Tensor, w_router: torch.Tensor,
     wsp, wsn = _ws(desc, workspace)
     st = lib().moe_route(
         ctypes.byref(desc), _ptr(x, "x", desc.torch_dtype, (T, d)),
-        _ptr(w_router, "w_router", _wdt(desc), (E, d)),
+        _ptr(w_router, "w_router", _rdt(desc), (E, d)),
         _ptr(router_bias, "router_bias", torch.float32, (E,)), T,
         _ptr(topk_ids, "topk_ids", torch.int32, (T, k)),
         _ptr(topk_w, "topk_w", torch.float32, (T, k)),

@@ -40,11 +40,16 @@ size_t n_counters(const moe_layer_desc& d) { return 16 + (size_t)ceil_div(d.d_mo
 
 int n_route_chunks(const moe_layer_desc& d) { return ceil_div(d.d_model, moe::kRouteChunk); }
 
+bool fp8(const moe_layer_desc& d) { return d.w_dtype == MOE_FP8_E4M3; }
+
+// Element type of the router: the activation dtype when the experts are FP8.
+int router_dtype(const moe_layer_desc& d) { return fp8(d) ? d.act_dtype : d.w_dtype; }
+
 // K pieces of the bf16 router: enough (16-expert tile, piece) blocks to reach
 // about 512 blocks, at most kMaxRouteSplit partial planes, and at least 64
 // elements of K per wave.  fp32 layers use one plane.
 int route_ksplit(const moe_layer_desc& d) {
-  if (d.w_dtype != MOE_BF16) return 1;
+  if (router_dtype(d) != MOE_BF16) return 1;
   const int tiles = ceil_div(d.n_experts, 16);
   int s = ceil_div(512, tiles);
   if (s > moe::kMaxRouteSplit) s = moe::kMaxRouteSplit;
@@ -133,9 +138,23 @@ moe_status check_desc(const moe_layer_desc* d) {
   if (d->renormalize != 0 && d->renormalize != 1) return MOE_ERR_INVALID_ARG;
   if (!isfinite(d->route_scale)) return MOE_ERR_INVALID_ARG;
   if (d->max_tokens <= 0) return MOE_ERR_INVALID_ARG;
-  if (d->w_dtype != MOE_F32 && d->w_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (d->w_dtype != MOE_F32 && d->w_dtype != MOE_BF16 && d->w_dtype != MOE_FP8_E4M3)
+    return MOE_ERR_INVALID_ARG;
   if (d->act_dtype != MOE_F32 && d->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
-  if (d->w_dtype != d->act_dtype) return MOE_ERR_UNSUPPORTED;
+  if (d->w_dtype == MOE_FP8_E4M3) {
+    // E4M3 codes with bf16 activations, plain and slice forms; 16 codes per
+    // 16-byte load; rows staged in LDS (four of them) bound the widths
+    if (d->act_dtype != MOE_BF16 || d->dept_form == MOE_DEPT_FACTORISED)
+      return MOE_ERR_UNSUPPORTED;
+    const int32_t widths[4] = {d->d_model, d->d_ff, d->n_depts > 0 ? d->d_ff_dept : 0,
+                               d->d_ff_shared};
+    for (int32_t wdt : widths) {
+      if (wdt % 16) return MOE_ERR_INVALID_ARG;
+      if (wdt > MOE_FP8_MAX_WIDTH) return MOE_ERR_UNSUPPORTED;
+    }
+  } else if (d->w_dtype != d->act_dtype) {
+    return MOE_ERR_UNSUPPORTED;
+  }
   if (d->n_experts > MOE_MAX_EXPERTS || d->top_k > MOE_MAX_TOP_K) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)d->max_tokens * d->top_k > MOE_MAX_ASSIGNMENTS) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)d->max_tokens * d->n_depts > MOE_MAX_DEPT_PAIRS) return MOE_ERR_UNSUPPORTED;
@@ -164,6 +183,16 @@ moe_status check_weights(const moe_layer_desc* d, const moe_weights* w, bool nee
     return MOE_ERR_INVALID_ARG;
   if (d->d_ff_shared > 0 && (!ok_ptr(w->ws_gate) || !ok_ptr(w->ws_up) || !ok_ptr(w->ws_down)))
     return MOE_ERR_INVALID_ARG;
+  if (d->w_dtype == MOE_FP8_E4M3) {  // every matrix present needs its per-row scales
+    if (!ok_ptr(w->w_gate_scale) || !ok_ptr(w->w_up_scale) || !ok_ptr(w->w_down_scale))
+      return MOE_ERR_INVALID_ARG;
+    if (d->n_depts > 0 &&
+        (!ok_ptr(w->wd_gate_scale) || !ok_ptr(w->wd_up_scale) || !ok_ptr(w->wd_down_scale)))
+      return MOE_ERR_INVALID_ARG;
+    if (d->d_ff_shared > 0 &&
+        (!ok_ptr(w->ws_gate_scale) || !ok_ptr(w->ws_up_scale) || !ok_ptr(w->ws_down_scale)))
+      return MOE_ERR_INVALID_ARG;
+  }
   return MOE_OK;
 }
 
@@ -280,6 +309,21 @@ moe::GemvConfig choose_config(const moe_layer_desc& d, int32_t T) {
   return c;
 }
 
+// FP8 down: lanes per weight row, so that every family's row length in
+// 16-byte chunks (16 codes) divides evenly where possible (64, 32 or 16; rows
+// that none divides take 16 lanes and leave some idle in their last step).
+int fp8_lanes_per_row(const moe_layer_desc& d) {
+  for (int cand : {64, 32, 16}) {
+    bool ok = true;
+    for (int f = 0; f < 3; ++f) {
+      const int r = family_rows(d, f);
+      if (r > 0 && (f != 1 || d.n_depts > 0) && (r / 16) % cand) ok = false;
+    }
+    if (ok) return cand;
+  }
+  return 16;
+}
+
 // The families one expert launch carries.
 enum class Stage {
   kAll,              // vanilla and slice form: every family in one gate/up and one down launch
@@ -343,6 +387,9 @@ FamilySet make_families(const moe_layer_desc& d, const moe_weights& w, const moe
     f.max_slots = tk < d.n_experts ? tk : d.n_experts;
     f.n_mats = d.n_experts;
     f.max_rows = tk;
+    f.gate_scale = w.w_gate_scale;
+    f.up_scale = w.w_up_scale;
+    f.down_scale = w.w_down_scale;
     if (stage == Stage::kFactPrivateUp) {
       // inputs: the backbone outputs of the row's (token, department) pair
       f.x_gate = at<void>(ws, L, R_XG);
@@ -367,6 +414,9 @@ FamilySet make_families(const moe_layer_desc& d, const moe_weights& w, const moe
     f.max_slots = tk < d.n_depts ? tk : d.n_depts;
     f.n_mats = d.n_depts;
     f.max_rows = pairs_max;
+    f.gate_scale = w.wd_gate_scale;
+    f.up_scale = w.wd_up_scale;
+    f.down_scale = w.wd_down_scale;
     if (stage == Stage::kFactBackbone) {
       f.h = at<void>(ws, L, R_XG);
       f.h2 = at<void>(ws, L, R_XU);
@@ -385,6 +435,9 @@ FamilySet make_families(const moe_layer_desc& d, const moe_weights& w, const moe
     f.max_slots = 1;
     f.n_mats = 1;
     f.max_rows = T;
+    f.gate_scale = w.ws_gate_scale;
+    f.up_scale = w.ws_up_scale;
+    f.down_scale = w.ws_down_scale;
     add_parts(f, T <= small_max, T > small_max, 0, 0);
   }
   // Large parts first: their blocks stream whole 16-row tiles and live far
@@ -452,6 +505,27 @@ moe_status run_experts(const moe_layer_desc& d, const moe_weights& w, const void
                        const moe::KernelEvents* ev_dn, bool gateup_only = false) {
   const moe::GemvConfig cfg = choose_config(d, T);
   const int dm = d.d_model;
+  if (fp8(d)) {
+    // FP8 experts: every part tiled like a small one (one gate/up row per
+    // wave; down: 64 / lpr columns per wave), any group size
+    FamilySet set = make_families(d, w, p, ws, T, row_out, dept_out, shared_out);
+    const int lpr = fp8_lanes_per_row(d);
+    set.blk_start[0] = 0;
+    for (int i = 0; i < set.n; ++i) {
+      set.f[i].tiles = ceil_div(set.f[i].rows, moe::kWaves);
+      set.blk_start[i + 1] = set.blk_start[i] + set.f[i].max_slots * set.f[i].tiles;
+    }
+    for (int i = set.n + 1; i <= moe::kMaxParts; ++i) set.blk_start[i] = set.blk_start[set.n];
+    if (moe::launch_gateup_fp8(set, x, T, dm, st, ev_gu) != hipSuccess) return MOE_ERR_HIP;
+    if (gateup_only) return MOE_OK;
+    set.blk_start[0] = 0;
+    for (int i = 0; i < set.n; ++i) {
+      set.f[i].tiles = ceil_div(dm, moe::kWaves * (64 / lpr));
+      set.blk_start[i + 1] = set.blk_start[i] + set.f[i].max_slots * set.f[i].tiles;
+    }
+    for (int i = set.n + 1; i <= moe::kMaxParts; ++i) set.blk_start[i] = set.blk_start[set.n];
+    return hip_status(moe::launch_down_fp8(set, T, dm, lpr, st, ev_dn));
+  }
   if (!factorised(d)) {
     FamilySet set = make_families(d, w, p, ws, T, row_out, dept_out, shared_out);
     set_tiles(set, dm, true, d.w_dtype, cfg);
@@ -640,7 +714,8 @@ moe_status moe_route(const moe_layer_desc* desc, const void* x, const void* w_ro
   const moe::RouteArgs ra = route_args(*desc, workspace, x, w_router, router_bias, T, topk_ids,
                                        topk_w, sel_scores);
   return hip_status(
-      moe::launch_route(desc->w_dtype, ra, nullptr, static_cast<hipStream_t>(stream), nullptr));
+      moe::launch_route(router_dtype(*desc), ra, nullptr, static_cast<hipStream_t>(stream),
+                        nullptr));
 }
 
 moe_status moe_dispatch(const moe_layer_desc* desc, const int32_t* topk_ids, const float* topk_w,
@@ -734,7 +809,7 @@ moe_status moe_layer_decode(const moe_layer_desc* desc, const moe_weights* weigh
       route_args(*desc, workspace, x, weights->w_router, weights->router_bias, T,
                  at<int32_t>(workspace, L, R_TOPK_IDS), at<float>(workspace, L, R_TOPK_W), nullptr);
   const moe::PlanArgs pa = plan_args(*desc, workspace, T, plan);
-  if (moe::launch_route(desc->w_dtype, ra, &pa, st, evp(MOE_STAGE_ROUTE)) != hipSuccess)
+  if (moe::launch_route(router_dtype(*desc), ra, &pa, st, evp(MOE_STAGE_ROUTE)) != hipSuccess)
     return MOE_ERR_HIP;
 
   // grouped expert FFN, then the combine back to token order: at decode
@@ -776,8 +851,18 @@ const char* moe_status_string(moe_status status) {
 uint64_t moe_loaded_weight_bytes(const moe_layer_desc* desc, int32_t n_active,
                                  int32_t n_active_depts) {
   if (check_desc(desc) != MOE_OK) return 0;
-  const uint64_t wb = desc->w_dtype == MOE_BF16 ? 2 : 4;
   const uint64_t d = desc->d_model;
+  if (fp8(*desc)) {
+    // router in the activation dtype; one byte per expert weight and a
+    // 4-byte scale per output row (gate/up rows are I long, down rows d)
+    const uint64_t rb = desc->act_dtype == MOE_BF16 ? 2 : 4;
+    auto mat3 = [&](uint64_t r) { return 3 * d * r + 4 * (2 * r + d); };
+    uint64_t n = (uint64_t)desc->n_experts * d * rb + (uint64_t)n_active * mat3(desc->d_ff);
+    if (desc->d_ff_shared > 0) n += mat3(desc->d_ff_shared);
+    if (desc->n_depts > 0) n += (uint64_t)n_active_depts * mat3(desc->d_ff_dept);
+    return n;
+  }
+  const uint64_t wb = desc->w_dtype == MOE_BF16 ? 2 : 4;
   uint64_t n = (uint64_t)desc->n_experts * d;
   // factorised form: each private transform is S x S (d_ff == d_ff_dept)
   n += (uint64_t)n_active * 3 * (desc->n_depts > 0 && desc->dept_form == MOE_DEPT_FACTORISED

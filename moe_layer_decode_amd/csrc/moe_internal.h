@@ -82,6 +82,9 @@ struct Family {
   int n_mats;              // matrices in the family (bounds check of work descriptors)
   int max_rows;            // rows h / out hold (bounds check of work descriptors)
   int large;               // 0: groups of <= kTokInline rows; 1: larger groups
+  const float* gate_scale; // FP8 weights: per-row scales [n_mats][rows] (gate, up)
+  const float* up_scale;   //   and [n_mats][d] (down); unused otherwise
+  const float* down_scale;
 };
 
 struct FamilySet {
@@ -176,6 +179,15 @@ hipError_t launch_combine(int act_dtype, const CombineArgs& a, void* y, hipStrea
 // bf16 layers only; the caller checks T <= kTokInline and the LDS size.
 hipError_t launch_down_combine(const DownCombineArgs& a, void* y, hipStream_t st,
                                const KernelEvents* ev);
+// FP8 expert weights (E4M3 codes + per-row scales, bf16 activations): every
+// part of the set is tiled like a small part (one gate/up row per wave; down:
+// 64 / lpr columns per wave), groups of any size taken kTokInline tokens at a
+// time.  d and every row length are multiples of 16 and at most
+// MOE_FP8_MAX_WIDTH.
+hipError_t launch_gateup_fp8(const FamilySet& set, const void* x, int T, int d, hipStream_t st,
+                             const KernelEvents* ev);
+hipError_t launch_down_fp8(const FamilySet& set, int T, int d, int lpr, hipStream_t st,
+                           const KernelEvents* ev);
 hipError_t launch_zero(unsigned int* p, size_t n, hipStream_t st);
 hipError_t launch_stream_read(const void* src, size_t blocks, float* sink, hipStream_t st);
 hipError_t launch_pair_combine(int act_dtype, const PairCombineArgs& a, void* zc, int max_pairs,

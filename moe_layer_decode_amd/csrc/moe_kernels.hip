@@ -2439,6 +2439,227 @@ __global__ __launch_bounds__(kDcWaves * kWave) void down_combine_kernel(DownComb
   if ((lane & 15) == 0 && t < T) y[(size_t)t * d + c] = f32_to_bf16(v[0]);
 }
 
+// ---------------------------------------------------------------------------
+// FP8 expert weights: OCP E4M3 codes with one fp32 scale per output row.
+// A lane reads 16 codes (16 bytes) of a weight row per step.  Every E4M3
+// value is exactly a bf16 value, so v_cvt_scalef32_pk_bf16_fp8 with scale 1
+// widens each pair of codes to a bf16 pair and the packed bf16 dot
+// instruction multiplies them with the bf16 activations, summing in fp32; the
+// row's scale multiplies the finished sum.  Groups of any size are taken
+// kTokInline tokens at a time, their activation rows (gate/up) or rows of h
+// (down) staged in LDS once per chunk; no matrix-core path (decode groups are
+// small, and the weights of a group of more than kTokInline rows are re-read
+// from the cache for each further chunk).
+// ---------------------------------------------------------------------------
+constexpr int kFp8Ahead = 4;  // weight steps requested ahead per row
+
+// Codes 4q .. 4q+3 of dword q as two bf16 pairs (byte 0 in the low half).
+__device__ __forceinline__ void fp8x16_to_bf16(const u32x4_t& w, uint32_t (&o)[8]) {
+  const uint32_t d4[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    o[2 * q] = __builtin_bit_cast(uint32_t,
+                                  __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d4[q], 1.0f, false));
+    o[2 * q + 1] = __builtin_bit_cast(uint32_t,
+                                      __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d4[q], 1.0f, true));
+  }
+}
+
+// sum over 16 consecutive k of weight (widened codes) * activation, where
+// the activations are 16 bf16 at p (16-byte aligned, LDS)
+__device__ __forceinline__ float dot16(const uint32_t (&wb)[8], const bf16_t* p, float acc) {
+  const u32x4_t a = *reinterpret_cast<const u32x4_t*>(p);
+  const u32x4_t b = *reinterpret_cast<const u32x4_t*>(p + 8);
+  acc = dot2_bf16(wb[0], a.x, acc);
+  acc = dot2_bf16(wb[1], a.y, acc);
+  acc = dot2_bf16(wb[2], a.z, acc);
+  acc = dot2_bf16(wb[3], a.w, acc);
+  acc = dot2_bf16(wb[4], b.x, acc);
+  acc = dot2_bf16(wb[5], b.y, acc);
+  acc = dot2_bf16(wb[6], b.z, acc);
+  return dot2_bf16(wb[7], b.w, acc);
+}
+
+__device__ __forceinline__ u32x4_t ld16_fp8(const uint8_t* p, bool stream) {
+  return stream ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p))
+                : *reinterpret_cast<const u32x4_t*>(p);
+}
+
+// Gate and up row i (one per wave) of matrix `mat` for every row of the
+// group, kTokInline tokens a chunk: h[r0 + t][i] = SiLU(sg * g_t) * (su * u_t).
+__device__ __forceinline__ void gu_fp8(const Family& F, const Slot& sl, const bf16_t* __restrict__ x,
+                                       int T, int d, int i0, bf16_t* __restrict__ xl, int lane,
+                                       int wid) {
+  constexpr int NT = kTokInline, R = kFp8Ahead, STEP = 16 * kWave;
+  const int rows = F.rows, n = sl.n;
+  const int i = min(i0, rows - 1);
+  const size_t ms = (size_t)rows * d;
+  const uint8_t* gp = static_cast<const uint8_t*>(F.gate) + (size_t)sl.mat * ms + (size_t)i * d + lane * 16;
+  const uint8_t* up = static_cast<const uint8_t*>(F.up) + (size_t)sl.mat * ms + (size_t)i * d + lane * 16;
+  const float sg = F.gate_scale[(size_t)sl.mat * rows + i];
+  const float su = F.up_scale[(size_t)sl.mat * rows + i];
+  const int dl = d - lane * 16;     // this lane's codes: lane*16 + k*STEP for k*STEP < dl
+  const bool stream = n <= NT;      // read once: streaming hint; else re-read per chunk
+  const bf16_t* xg = F.x_gate ? static_cast<const bf16_t*>(F.x_gate) : x;
+  bf16_t* h = static_cast<bf16_t*>(F.h);
+#pragma unroll 1
+  for (int tc = 0; tc < n; tc += NT) {
+    const int nv = min(NT, n - tc);
+    u32x4_t rg[R], ru[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (r * STEP < dl) {
+        rg[r] = ld16_fp8(gp + r * STEP, stream);
+        ru[r] = ld16_fp8(up + r * STEP, stream);
+      } else {
+        rg[r] = ru[r] = u32x4_t{0, 0, 0, 0};
+      }
+    }
+    // the chunk's activation rows, one 1 KB wave instruction at a time
+    {
+      constexpr int EPI = 8 * kWave;  // bf16 elements per wave instruction
+      const int per_row = (d + EPI - 1) / EPI, total = nv * per_row;
+      for (int q = wid; q < total; q += kWaves) {
+        const int t = q / per_row, c0 = (q - t * per_row) * EPI;
+        const int c = c0 + lane * 8;
+        const int tok = slot_token(sl, F.grp_token, tc, t, n, F.in_rows);
+        if (c < d)
+          __builtin_amdgcn_global_load_lds(xg + (size_t)tok * d + c,
+                                           (lds_void_t*)(xl + (size_t)t * d + c0), 16, 0, 0);
+      }
+    }
+    stage_wait();
+    float ag[NT], au[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) ag[t] = au[t] = 0.f;
+    for (int c0 = 0; c0 < d; c0 += R * STEP) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int c = c0 + r * STEP;
+        if (c < dl) {
+          uint32_t wg[8], wu[8];
+          fp8x16_to_bf16(rg[r], wg);
+          fp8x16_to_bf16(ru[r], wu);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            if (t < nv) {
+              const bf16_t* xp = xl + (size_t)t * d + lane * 16 + c;
+              ag[t] = dot16(wg, xp, ag[t]);
+              au[t] = dot16(wu, xp, au[t]);
+            }
+          }
+          if (c + R * STEP < dl) {
+            rg[r] = ld16_fp8(gp + c + R * STEP, stream);
+            ru[r] = ld16_fp8(up + c + R * STEP, stream);
+          }
+        }
+      }
+    }
+    constexpr int N = 2 * NT;
+    float v[N];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      v[t] = ag[t];
+      v[NT + t] = au[t];
+    }
+    group_reduce_scatter<N, 64>(v, lane);
+    // gate index t and up index t + NT sit in lanes l and l ^ 32
+    const float upv = __shfl_xor(v[0], 32, kWave);
+    constexpr int SH = 6 - Log2<N>::value;
+    const int t = lane >> SH;
+    if (t < NT && (lane & ((1 << SH) - 1)) == 0 && t < nv && i0 < rows)
+      store_act(h + (size_t)(sl.r0 + tc + t) * rows + i0, silu(sg * v[0]) * (su * upv));
+    __syncthreads();  // every wave is done with the staged rows before the next chunk
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void gateup_fp8_kernel(FamilySet set,
+                                                             const bf16_t* __restrict__ x, int T,
+                                                             int d) {
+  extern __shared__ __align__(16) unsigned char fp8_lds[];
+  int tile;
+  const Family& F = block_part(set, tile);
+  Slot sl;
+  if (!map_slot(F, T, sl, tile)) return;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  gu_fp8(F, sl, x, T, d, tile * kWaves + wid, reinterpret_cast<bf16_t*>(fp8_lds), lane, wid);
+}
+
+// Down columns cb + g (lane group g of LPR lanes) of matrix `mat` for every
+// row of the group, kTokInline rows of h a chunk: out[r0 + t][c] = sd[c] *
+// (W_down[c] . h[r0 + t]).
+template <int LPR>
+__device__ __forceinline__ void dn_fp8(const Family& F, const Slot& sl, int d, int cb,
+                                       bf16_t* __restrict__ hl, int lane, int wid) {
+  constexpr int NT = kTokInline, R = kFp8Ahead, STEP = 16 * LPR;
+  const int rows = F.rows, n = sl.n;
+  const int g = lane / LPR, j = lane - g * LPR;
+  const int c = min(cb + g, d - 1);
+  const uint8_t* wp = static_cast<const uint8_t*>(F.down) + (size_t)sl.mat * rows * d +
+                      (size_t)c * rows + j * 16;
+  const float sd = F.down_scale[(size_t)sl.mat * d + c];
+  const int rl = rows - j * 16;  // this lane's codes: j*16 + k*STEP for k*STEP < rl
+  const bool stream = n <= NT;
+  const bf16_t* h = static_cast<const bf16_t*>(F.h);
+#pragma unroll 1
+  for (int tc = 0; tc < n; tc += NT) {
+    const int nv = min(NT, n - tc);
+    u32x4_t rw[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      rw[r] = r * STEP < rl ? ld16_fp8(wp + r * STEP, stream) : u32x4_t{0, 0, 0, 0};
+    {
+      constexpr int EPI = 8 * kWave;
+      const int per_row = (rows + EPI - 1) / EPI, total = nv * per_row;
+      for (int q = wid; q < total; q += kWaves) {
+        const int t = q / per_row, c0 = (q - t * per_row) * EPI;
+        const int e = c0 + lane * 8;
+        if (e < rows)
+          __builtin_amdgcn_global_load_lds(h + (size_t)(sl.r0 + tc + t) * rows + e,
+                                           (lds_void_t*)(hl + (size_t)t * rows + c0), 16, 0, 0);
+      }
+    }
+    stage_wait();
+    float acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = 0.f;
+    for (int k0 = 0; k0 < rows; k0 += R * STEP) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int k = k0 + r * STEP;
+        if (k < rl) {
+          uint32_t wb[8];
+          fp8x16_to_bf16(rw[r], wb);
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            if (t < nv) acc[t] = dot16(wb, hl + (size_t)t * rows + j * 16 + k, acc[t]);
+          if (k + R * STEP < rl) rw[r] = ld16_fp8(wp + k + R * STEP, stream);
+        }
+      }
+    }
+    group_reduce_scatter<NT, LPR>(acc, lane);
+    // lane j of the group holds token j / (LPR / NT)
+    constexpr int SPAN = LPR / NT;
+    const int t = j / SPAN;
+    if (j % SPAN == 0 && t < nv && cb + g < d)
+      F.out[(size_t)(sl.r0 + tc + t) * d + cb + g] = sd * acc[0];
+    __syncthreads();
+  }
+}
+
+template <int LPR>
+__global__ __launch_bounds__(kThreads) void down_fp8_kernel(FamilySet set, int T, int d) {
+  extern __shared__ __align__(16) unsigned char fp8_lds[];
+  int tile;
+  const Family& F = block_part(set, tile);
+  Slot sl;
+  if (!map_slot(F, T, sl, tile)) return;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  constexpr int G = 64 / LPR;
+  dn_fp8<LPR>(F, sl, d, tile * (kWaves * G) + wid * G, reinterpret_cast<bf16_t*>(fp8_lds), lane,
+              wid);
+}
+
 __global__ void zero_kernel(unsigned int* p, size_t n) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x)
@@ -2601,6 +2822,42 @@ hipError_t launch_down_combine(const DownCombineArgs& a, void* y, hipStream_t st
     hipExtLaunchKernelGGL(k, grid, block, lds, st, ev->start, ev->stop, 0, a, yo);
   else
     hipLaunchKernelGGL(k, grid, block, lds, st, a, yo);
+  return hipGetLastError();
+}
+
+hipError_t launch_gateup_fp8(const FamilySet& set, const void* x, int T, int d, hipStream_t st,
+                             const KernelEvents* ev) {
+  if (set.blk_start[set.n] <= 0) return hipSuccess;
+  const dim3 grid(set.blk_start[set.n]), block(kThreads);
+  const size_t lds = (size_t)kTokInline * d * sizeof(bf16_t);
+  const bf16_t* xb = static_cast<const bf16_t*>(x);
+  if (ev)
+    hipExtLaunchKernelGGL(gateup_fp8_kernel, grid, block, lds, st, ev->start, ev->stop, 0, set, xb,
+                          T, d);
+  else
+    hipLaunchKernelGGL(gateup_fp8_kernel, grid, block, lds, st, set, xb, T, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_fp8(const FamilySet& set, int T, int d, int lpr, hipStream_t st,
+                           const KernelEvents* ev) {
+  if (set.blk_start[set.n] <= 0) return hipSuccess;
+  const dim3 grid(set.blk_start[set.n]), block(kThreads);
+  int max_rows = 0;
+  for (int i = 0; i < set.n; ++i) max_rows = set.f[i].rows > max_rows ? set.f[i].rows : max_rows;
+  const size_t lds = (size_t)kTokInline * max_rows * sizeof(bf16_t);
+  auto go = [&](auto kernel) {
+    if (ev)
+      hipExtLaunchKernelGGL(kernel, grid, block, lds, st, ev->start, ev->stop, 0, set, T, d);
+    else
+      hipLaunchKernelGGL(kernel, grid, block, lds, st, set, T, d);
+  };
+  if (lpr == 16)
+    go(down_fp8_kernel<16>);
+  else if (lpr == 32)
+    go(down_fp8_kernel<32>);
+  else
+    go(down_fp8_kernel<64>);
   return hipGetLastError();
 }
 

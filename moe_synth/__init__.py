@@ -22,6 +22,12 @@ N(0, 0.02) (the router initialisation in the DeepSeekMoE guide's PyTorch
 layer), activations N(0, 1) except the tiny layer (N(0, 0.02)), selection bias
 U(-0.1, 0.1); factorised private transforms are the identity DeaMoE starts
 them from plus N(0, 0.02).
+
+FP8 expert weights (shapes with expert_dtype "fp8") are the same fp32 draws
+stored as OCP E4M3 codes with one fp32 scale per output row: the scale is the
+row's largest magnitude over 448 (the largest E4M3 value), and the codes are
+torch's float8_e4m3fn rounding of the row divided by its scale.  This is
+input preparation (an offline weight format), not the layer's arithmetic.
 """
 from __future__ import annotations
 
@@ -33,7 +39,7 @@ import torch
 
 __all__ = [
     "LayerShape", "SHAPES", "normal", "uniform", "make_layer", "make_tokens",
-    "clone_weights",
+    "clone_weights", "E4M3_MAX",
 ]
 
 _MASK32 = 0xFFFFFFFF
@@ -70,6 +76,7 @@ class LayerShape:
     bias_range: float = 0.0        # U(-r, r) selection bias when > 0
     batches: tuple = (1, 4, 16)
     data_seed_of: Optional[str] = None  # reuse x / router / bias of this shape
+    expert_dtype: str = ""         # "" = dtype; "fp8": E4M3 codes + per-row fp32 scales
 
     @property
     def torch_dtype(self):
@@ -114,6 +121,15 @@ SHAPES: Dict[str, LayerShape] = {
         n_experts=864, top_k=10, d_ff=2048, n_depts=8, d_ff_dept=2048,
         d_ff_shared=2048, dept_form="factorised", k_dept=5, batches=(1, 2, 4, 8, 16),
         data_seed_of="deepseek_v3_d7168_e256_i2048_s2048_top8"),
+    # The Qwen3-30B-A3B- and DeepSeek-V3-shaped layers with FP8 expert weights
+    # (same draws, quantized per output row; router and activations bf16).
+    "qwen3_30b_a3b_d2048_e128_i768_top8_fp8": LayerShape(
+        name="qwen3_30b_a3b_d2048_e128_i768_top8_fp8", d=2048, n_experts=128,
+        top_k=8, d_ff=768, batches=(1, 4, 16), expert_dtype="fp8"),
+    "deepseek_v3_d7168_e256_i2048_s2048_top8_fp8": LayerShape(
+        name="deepseek_v3_d7168_e256_i2048_s2048_top8_fp8", d=7168,
+        n_experts=256, top_k=8, d_ff=2048, d_ff_shared=2048, score="sigmoid",
+        bias_range=0.1, batches=(1, 2, 4, 8, 16, 32), expert_dtype="fp8"),
 }
 
 # Tensor ids: part of the counter, so every tensor of a layer draws its own
@@ -156,14 +172,16 @@ def _chunk_elems(device) -> int:
     return (1 << 26) if torch.device(device).type == "cuda" else (1 << 22)
 
 
-def _fill(out: torch.Tensor, seed: int, tid: int, fn) -> torch.Tensor:
+def _fill(out: torch.Tensor, seed: int, tid: int, fn, offset: int = 0) -> torch.Tensor:
+    """Fill `out` with elements [offset, offset + out.numel()) of the
+    tensor's stream."""
     flat = out.view(-1)
     n = flat.numel()
     step = _chunk_elems(out.device)
     ka, kb = _key(seed, tid, 1), _key(seed, tid, 2)
     for s in range(0, n, step):
         e = min(n, s + step)
-        idx = torch.arange(s, e, dtype=torch.int64, device=out.device)
+        idx = torch.arange(s + offset, e + offset, dtype=torch.int64, device=out.device)
         ua = (_words(idx, ka).to(torch.float64) + 0.5) * (1.0 / 4294967296.0)
         ub = (_words(idx, kb).to(torch.float64) + 0.5) * (1.0 / 4294967296.0)
         flat[s:e] = fn(ua, ub).to(out.dtype)
@@ -171,13 +189,38 @@ def _fill(out: torch.Tensor, seed: int, tid: int, fn) -> torch.Tensor:
 
 
 def normal(seed: int, tid: int, shape, std: float, dtype=torch.float32,
-           device="cpu", mean: float = 0.0) -> torch.Tensor:
-    """N(mean, std^2) samples, rounded once to `dtype`."""
+           device="cpu", mean: float = 0.0, offset: int = 0) -> torch.Tensor:
+    """N(mean, std^2) samples, rounded once to `dtype`; `offset` starts at
+    that flat element of the stream (a slice of a larger tensor)."""
     out = torch.empty(shape, dtype=dtype, device=device)
 
     def bm(ua, ub):
         return torch.sqrt(-2.0 * torch.log(ua)) * torch.cos(2.0 * math.pi * ub) * std + mean
-    return _fill(out, seed, tid, bm)
+    return _fill(out, seed, tid, bm, offset)
+
+
+E4M3_MAX = 448.0  # largest finite OCP E4M3 value
+
+
+def _normal_fp8(seed: int, tid: int, shape, std: float, device):
+    """The fp32 N(0, std^2) draws of `shape` as E4M3 codes (uint8) and one
+    fp32 scale per row of the last dimension, generated one leading slice at
+    a time so no full fp32 copy is held."""
+    shape = tuple(shape)
+    codes = torch.empty(shape, dtype=torch.uint8, device=device)
+    scales = torch.empty(shape[:-1], dtype=torch.float32, device=device)
+    lead = shape[0] if len(shape) == 3 else 1
+    per = int(math.prod(shape[1:])) if len(shape) == 3 else int(math.prod(shape))
+    cv = codes.view(lead, *shape[-2:])
+    sv = scales.view(lead, shape[-2])
+    for i in range(lead):
+        w = normal(seed, tid, shape[-2:], std, torch.float32, device, offset=i * per)
+        amax = w.abs().amax(dim=-1)
+        sc = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+        q = (w / sc[:, None]).clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+        cv[i] = q.view(torch.uint8)
+        sv[i] = sc
+    return codes, scales
 
 
 def uniform(seed: int, tid: int, shape, lo: float, hi: float,
@@ -223,22 +266,32 @@ def make_layer(shape: LayerShape, seed: int, device="cpu",
             w[name] = a.to(dt)
             del a
     else:
-        w["w_gate"] = normal(eseed, _TID["w_gate"], (E, I, d), shape.w_std, dt, device)
-        w["w_up"] = normal(eseed, _TID["w_up"], (E, I, d), shape.w_std, dt, device)
-        w["w_down"] = normal(eseed, _TID["w_down"], (E, d, I), shape.w_std, dt, device)
+        mat(w, "w_gate", eseed, (E, I, d), shape, dt, device)
+        mat(w, "w_up", eseed, (E, I, d), shape, dt, device)
+        mat(w, "w_down", eseed, (E, d, I), shape, dt, device)
     if shape.n_depts:
         m, S = shape.n_depts, shape.d_ff_dept
-        w["wd_gate"] = normal(eseed, _TID["wd_gate"], (m, S, d), shape.w_std, dt, device)
-        w["wd_up"] = normal(eseed, _TID["wd_up"], (m, S, d), shape.w_std, dt, device)
-        w["wd_down"] = normal(eseed, _TID["wd_down"], (m, d, S), shape.w_std, dt, device)
+        mat(w, "wd_gate", eseed, (m, S, d), shape, dt, device)
+        mat(w, "wd_up", eseed, (m, S, d), shape, dt, device)
+        mat(w, "wd_down", eseed, (m, d, S), shape, dt, device)
     if shape.d_ff_shared:
         Is = shape.d_ff_shared
         # The shared expert is the source layer's own (same seed space), so a
         # transformed layer keeps its shared expert.
-        w["ws_gate"] = normal(seed, _TID["ws_gate"], (Is, d), shape.w_std, dt, device)
-        w["ws_up"] = normal(seed, _TID["ws_up"], (Is, d), shape.w_std, dt, device)
-        w["ws_down"] = normal(seed, _TID["ws_down"], (d, Is), shape.w_std, dt, device)
+        mat(w, "ws_gate", seed, (Is, d), shape, dt, device)
+        mat(w, "ws_up", seed, (Is, d), shape, dt, device)
+        mat(w, "ws_down", seed, (d, Is), shape, dt, device)
     return w
+
+
+def mat(w: Dict[str, torch.Tensor], name: str, seed: int, shape, layer: LayerShape, dt,
+        device) -> None:
+    """One expert matrix into w: in the layer dtype, or (FP8 layers) as E4M3
+    codes under `name` and per-row fp32 scales under name + "_scale"."""
+    if layer.expert_dtype == "fp8":
+        w[name], w[name + "_scale"] = _normal_fp8(seed, _TID[name], shape, layer.w_std, device)
+    else:
+        w[name] = normal(seed, _TID[name], shape, layer.w_std, dt, device)
 
 
 def clone_weights(w: Dict[str, torch.Tensor]) -> Dict[str, torch.Tensor]:

@@ -672,17 +672,35 @@ _FP8_MATS = ("w_gate", "w_up", "w_down", "wd_gate", "wd_up", "wd_down",
              "ws_gate", "ws_up", "ws_down")
 
 
-def dequantize_layer(weights) -> Dict[str, np.ndarray]:
+class _Fp8Stack:
+    """A stack of FP8 matrices [n][rows][cols] read one matrix at a time:
+    indexing by a matrix number dequantizes that matrix alone (a whole
+    DeepSeek-V3-sized layer in float64 would not fit in host memory)."""
+
+    def __init__(self, codes, scales):
+        self.codes, self.scales = codes, scales
+        self.shape = tuple(codes.shape)
+
+    def __len__(self):
+        return self.shape[0]
+
+    def __getitem__(self, i):
+        return fp8_dequantize(self.codes[i], self.scales[i])
+
+
+def dequantize_layer(weights) -> Dict[str, object]:
     """The layer's weights with every FP8 expert matrix (codes under its own
     name, per-row scales under name + "_scale") replaced by its float64
-    dequantized values; the router and bias are passed through."""
+    dequantized values -- stacked matrices lazily, one matrix per index --
+    and the router and bias passed through."""
     out = {}
     for k, v in weights.items():
         if k.endswith("_scale"):
             continue
         if k in _FP8_MATS and (k + "_scale") in weights:
             codes = v.detach().cpu().numpy() if hasattr(v, "detach") else np.asarray(v)
-            out[k] = fp8_dequantize(codes, weights[k + "_scale"])
+            sc = _f64(weights[k + "_scale"])
+            out[k] = _Fp8Stack(codes, sc) if codes.ndim == 3 else fp8_dequantize(codes, sc)
         else:
             out[k] = v
     return out

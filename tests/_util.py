@@ -27,7 +27,7 @@ def desc_of(shape: moe_synth.LayerShape, max_tokens: int = None, **over) -> M.La
               score=shape.score, renormalize=shape.renormalize, route_scale=shape.route_scale,
               dtype=shape.dtype, max_tokens=max_tokens or max(shape.batches),
               dept_form=shape.dept_form, k_dept=shape.k_dept,
-              dept_strict=shape.dept_strict)
+              dept_strict=shape.dept_strict, expert_dtype=shape.expert_dtype)
     kw.update(over)
     return M.layer_desc(shape.d, shape.n_experts, shape.top_k, shape.d_ff, **kw)
 

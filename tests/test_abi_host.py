@@ -207,3 +207,55 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(M, "lib_path", lambda: str(tmp_path / "missing.so"))
     with pytest.raises(ImportError, match="no CPU fallback"):
         M.moe_validate_desc(_desc())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(expert_dtype="fp8"), M.MOE_OK),
+    (dict(expert_dtype="fp8", d_ff=776), M.MOE_ERR_INVALID_ARG),           # 776 % 16 != 0
+    (dict(expert_dtype="fp8", d_model=2056), M.MOE_ERR_INVALID_ARG),
+    (dict(expert_dtype="fp8", d_ff_shared=24), M.MOE_ERR_INVALID_ARG),
+    (dict(expert_dtype="fp8", n_depts=8, d_ff_dept=1032), M.MOE_ERR_INVALID_ARG),
+    (dict(expert_dtype="fp8", n_depts=8, d_ff_dept=1024, d_ff_shared=2048), M.MOE_OK),
+    (dict(expert_dtype="fp8", d_model=8192 + 16), M.MOE_ERR_UNSUPPORTED),  # > MOE_FP8_MAX_WIDTH
+    (dict(expert_dtype="fp8", d_ff=8192), M.MOE_OK),
+    (dict(expert_dtype="fp8", dtype="f32"), M.MOE_ERR_UNSUPPORTED),       # bf16 activations only
+    (dict(expert_dtype="fp8", n_depts=8, d_ff=1024, d_ff_dept=1024, dept_form="factorised"),
+     M.MOE_ERR_UNSUPPORTED),
+])
+def test_fp8_descriptor_validation(lib, kw, status):
+    assert M.moe_validate_desc(_desc(**kw)) == status
+
+
+def test_fp8_calls_need_row_scales(lib):
+    """An FP8 layer without the per-row scales of a matrix it has is refused
+    on the host (no GPU needed)."""
+    d = _desc(expert_dtype="fp8", d_ff_shared=2048)
+    full = dict(w_router=256, w_gate=256, w_up=256, w_down=256, ws_gate=256, ws_up=256,
+                ws_down=256, w_gate_scale=512, w_up_scale=512, w_down_scale=512,
+                ws_gate_scale=512, ws_up_scale=512, ws_down_scale=512)
+    ws = M.moe_workspace_bytes(d)
+    assert lib.moe_layer_decode(ctypes.byref(d), ctypes.byref(M.Weights(**full)), 256, 0, 512,
+                                4096, ws, None, None) == M.MOE_OK  # T = 0: valid no-op
+    for missing in ("w_down_scale", "ws_gate_scale"):
+        W = M.Weights(**{k: v for k, v in full.items() if k != missing})
+        assert lib.moe_layer_decode(ctypes.byref(d), ctypes.byref(W), 256, 1, 512, 4096, ws,
+                                    None, None) == M.MOE_ERR_INVALID_ARG, missing
+
+
+def test_fp8_loaded_weight_bytes_match_the_oracle(lib):
+    """The library's FP8 byte count equals the oracle's (one byte per expert
+    weight, 4 per row scale, the router in bf16) for the plain layer, the
+    shared expert and department slices."""
+    import numpy as np
+    import oracle as O
+    for kw, n_act, n_dep in ((dict(), 8, 0), (dict(d_ff_shared=2048), 5, 0),
+                             (dict(n_experts=64, d_ff=128, n_depts=8, d_ff_dept=1024), 10, 3)):
+        d = _desc(expert_dtype="fp8", **kw)
+        E = d.n_experts
+        G = E // d.n_depts if d.n_depts else E
+        # n_act distinct experts spread over exactly n_dep departments (or any)
+        ids = [(i % max(n_dep, 1)) * G + i // max(n_dep, 1) for i in range(n_act)]
+        want = O.loaded_weight_bytes_fp8(np.array(ids), E, d.d_model, d.d_ff, router_bytes=2,
+                                         n_depts=d.n_depts, d_ff_dept=d.d_ff_dept,
+                                         d_ff_shared=d.d_ff_shared)
+        assert M.moe_loaded_weight_bytes(d, n_act, n_dep) == want

@@ -47,7 +47,19 @@ FACT = {
         n_depts=4, d_ff_dept=256, dept_form="factorised", k_dept=3, dept_strict=True,
         score="softmax_bias", bias_range=0.1, batches=(1, 5, 20)),
 }
-SH = {**moe_synth.SHAPES, **FACT}
+# Small FP8 layers (E4M3 expert codes, per-row scales) the oracle runs in
+# full: department slices with a shared expert, rows of one to several
+# 16-code steps, and batches whose groups exceed four rows (T = 9).
+FP8 = {
+    "fp8_d1040_e12_m3_s208_i48_sh32_top4": moe_synth.LayerShape(
+        name="fp8_d1040_e12_m3_s208_i48_sh32_top4", d=1040, n_experts=12, top_k=4, d_ff=48,
+        n_depts=3, d_ff_dept=208, d_ff_shared=32, score="sigmoid", bias_range=0.1,
+        expert_dtype="fp8", batches=(1, 4, 9)),
+    "fp8_d512_e6_i1040_top3": moe_synth.LayerShape(
+        name="fp8_d512_e6_i1040_top3", d=512, n_experts=6, top_k=3, d_ff=1040,
+        expert_dtype="fp8", batches=(1, 3, 9)),
+}
+SH = {**moe_synth.SHAPES, **FACT, **FP8}
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")
 
 
@@ -467,7 +479,9 @@ def check_layer(name, seed, T, sample_tokens=None):
     assert np.isfinite(yg).all()
     token_output = (O.deamoe_token_output if shape.dept_form == "factorised"
                     else O.layer_token_output)
-    ref = np.stack([token_output(xc[t], ids[t], o_w[t], w, shape.n_experts, shape.n_depts)
+    wref = O.dequantize_layer({k: v.cpu() for k, v in w.items()}) \
+        if shape.expert_dtype == "fp8" else w
+    ref = np.stack([token_output(xc[t], ids[t], o_w[t], wref, shape.n_experts, shape.n_depts)
                     for t in toks])
     emax, rmax = assert_close(yg[list(toks)], ref, shape.dtype, f"{name} T={T}",
                               TOL_FACTORISED if shape.dept_form == "factorised" else None)
@@ -515,6 +529,62 @@ def test_layer_factorised_paper_shape(T):
     """DeaMoE's DeepSeek-V3-matched layer (864 experts in 8 departments,
     hffn = 2048, k = 10), sampled tokens against the oracle."""
     check_layer(PAPER, 0, T, sample_tokens=[0, T - 1])
+
+
+@pytest.mark.parametrize("name,T", [(n, T) for n in FP8 for T in FP8[n].batches])
+def test_layer_fp8_small(name, T):
+    """FP8 expert layers end to end against the oracle on the dequantized
+    weights, every token."""
+    check_layer(name, 0, T)
+
+
+@pytest.mark.parametrize("T", [1, 4, 16])
+def test_layer_fp8_qwen3_shape(T):
+    check_layer("qwen3_30b_a3b_d2048_e128_i768_top8_fp8", 0, T)
+
+
+@pytest.mark.parametrize("T", [1, 8, 32])
+def test_layer_fp8_deepseek_v3_shape(T):
+    check_layer("deepseek_v3_d7168_e256_i2048_s2048_top8_fp8", 0, T,
+                sample_tokens=[0, T // 2, T - 1])
+
+
+def test_fp8_every_code():
+    """Codes drawn over every E4M3 value (subnormals, both zeros, +-448; no
+    NaN) with per-row scales over six binades: moe_expert_ffn's per-row
+    outputs and the combined y against the oracle's dequantized weights, so
+    that each code's widening on the GPU is checked against the format's
+    definition."""
+    d, E, k, I, m, S, Is, T = 528, 5, 2, 64, 0, 0, 48, 6
+    g = torch.Generator().manual_seed(11)
+    finite = torch.tensor([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=torch.uint8)
+
+    def codes(*shape):
+        return finite[torch.randint(0, finite.numel(), shape, generator=g)].to(DEV)
+
+    def scales(*shape):
+        return (2.0 ** torch.randint(-14, -8, shape, generator=g).float()).to(DEV)
+    w = {"w_router": (torch.randn(E, d, generator=g) * 0.05).to(torch.bfloat16).to(DEV),
+         "w_gate": codes(E, I, d), "w_up": codes(E, I, d), "w_down": codes(E, d, I),
+         "w_gate_scale": scales(E, I), "w_up_scale": scales(E, I), "w_down_scale": scales(E, d),
+         "ws_gate": codes(Is, d), "ws_up": codes(Is, d), "ws_down": codes(d, Is),
+         "ws_gate_scale": scales(Is), "ws_up_scale": scales(Is), "ws_down_scale": scales(d)}
+    x = torch.randn(T, d, generator=g).to(torch.bfloat16).to(DEV)
+    desc = M.layer_desc(d, E, k, I, d_ff_shared=Is, dtype="bf16", expert_dtype="fp8",
+                        max_tokens=T)
+    rng = np.random.default_rng(2)
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    ids[:, 0] = 1  # one group of six rows: two token chunks
+    tw = rng.random((T, k)).astype(np.float32)
+    plan, ws, gp = run_dispatch(desc, ids, tw)
+    op = O.dispatch(ids, E, tw.astype(np.float64), 0)
+    row_out = torch.full((T * k, d), float("nan"), device=DEV)
+    shared_out = torch.full((T, d), float("nan"), device=DEV)
+    M.moe_expert_ffn(desc, w, x, plan, ws, row_out, None, shared_out)
+    wref = O.dequantize_layer({kk: v.cpu() for kk, v in w.items()})
+    o_row, _, o_sh = O.expert_outputs(x.cpu(), wref, op, E, 0)
+    assert_close(to_np(row_out[:op["n_rows"]]), o_row, "bf16", "fp8 row_out")
+    assert_close(to_np(shared_out), o_sh, "bf16", "fp8 shared_out")
 
 
 def test_factorised_expert_ffn_and_combine_match_the_fused_step():
