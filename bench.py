@@ -403,10 +403,15 @@ def measured_peak_GBps(M, dev, gib=2, iters=10):
 
 def sweep_report(path):
     """Markdown table of a --sweep run: one row per (shape, batch)."""
-    rows, dv = [], []
+    rows, dv, fv = [], [], []
     for line in open(path):
         r = json.loads(line)
-        (dv if "dept_vs_vanilla" in r else rows).append(r.get("dept_vs_vanilla", r))
+        if "dept_vs_vanilla" in r:
+            dv.append(r["dept_vs_vanilla"])
+        elif "fp8_vs_bf16" in r:
+            fv.append(r["fp8_vs_bf16"])
+        else:
+            rows.append(r)
     print("# Every layer shape at its batches: graph-replayed decode step\n")
     print("Command (repo root, one MI355X):\n\n```")
     print("python bench.py --sweep --sweep-out gpurun_out/sweep.jsonl")
@@ -433,6 +438,14 @@ def sweep_report(path):
         for r in dv:
             print(f"| {r.get('dept_shape', '')} | {r['batch']} | {r['vanilla_us']} | {r['dept_us']} "
                   f"| {r['speedup']} | {r['byte_ratio']} |")
+    if fv:
+        print("\nFP8 expert weights (E4M3 codes, per-row fp32 scales) against the bf16 layer of "
+              "the same shape and draws at the same batch:\n")
+        print("| FP8 shape | batch | bf16 us | FP8 us | speedup | byte ratio (FP8 / bf16) |")
+        print("|---|---|---|---|---|---|")
+        for r in fv:
+            print(f"| {r['fp8_shape']} | {r['batch']} | {r['bf16_us']} | {r['fp8_us']} "
+                  f"| {r['speedup']} | {r['byte_ratio']} |")
 
 
 def dept_vs_vanilla(lines):
@@ -453,6 +466,21 @@ def dept_vs_vanilla(lines):
                             "speedup": round(a["us"] / b["us"], 3),
                             "vanilla_bytes": a["weight_bytes"], "dept_bytes": b["weight_bytes"],
                             "byte_ratio": round(b["weight_bytes"] / a["weight_bytes"], 3)})
+    return out
+
+
+def fp8_vs_bf16(lines):
+    """Each FP8-expert layer against the bf16 layer of the same shape and
+    draws at the same batch: speedup beside the ratio of streamed bytes."""
+    by = {(l["shape"], l["batch"]): l for l in lines}
+    out = []
+    for (name, T), b in sorted(by.items()):
+        if not name.endswith("_fp8") or (name[:-4], T) not in by:
+            continue
+        a = by[(name[:-4], T)]
+        out.append({"fp8_shape": name, "batch": T, "bf16_us": a["us"], "fp8_us": b["us"],
+                    "speedup": round(a["us"] / b["us"], 3),
+                    "byte_ratio": round(b["weight_bytes"] / a["weight_bytes"], 3)})
     return out
 
 
@@ -683,6 +711,15 @@ def main():
             for line in dv:
                 f.write(json.dumps({"dept_vs_vanilla": line}) + "\n")
             out["dept_vs_vanilla"] = dv
+            # the headline shape's own line joins the FP8 comparison
+            head_line = {"shape": shape.name, "batch": head_T, "us": round(us, 2),
+                         "weight_bytes": per_batch[str(head_T)]["weight_bytes"]}
+            extra = [dict(head_line, batch=int(b), us=r["us"], weight_bytes=r["weight_bytes"])
+                     for b, r in per_batch.items()]
+            fv = fp8_vs_bf16(sweep_lines + extra)
+            for line in fv:
+                f.write(json.dumps({"fp8_vs_bf16": line}) + "\n")
+            out["fp8_vs_bf16"] = fv
     print(json.dumps(out), flush=True)
 
 

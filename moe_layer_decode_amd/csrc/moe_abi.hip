@@ -506,13 +506,14 @@ moe_status run_experts(const moe_layer_desc& d, const moe_weights& w, const void
   const moe::GemvConfig cfg = choose_config(d, T);
   const int dm = d.d_model;
   if (fp8(d)) {
-    // FP8 experts: every part tiled like a small one (one gate/up row per
-    // wave; down: 64 / lpr columns per wave), any group size
+    // FP8 experts: every part tiled like a small one (kFp8RowsPerWave
+    // gate/up rows per wave; down: kFp8DownColGroups * 64 / lpr columns per
+    // wave), any group size
     FamilySet set = make_families(d, w, p, ws, T, row_out, dept_out, shared_out);
     const int lpr = fp8_lanes_per_row(d);
     set.blk_start[0] = 0;
     for (int i = 0; i < set.n; ++i) {
-      set.f[i].tiles = ceil_div(set.f[i].rows, moe::kWaves);
+      set.f[i].tiles = ceil_div(set.f[i].rows, moe::kWaves * moe::kFp8RowsPerWave);
       set.blk_start[i + 1] = set.blk_start[i] + set.f[i].max_slots * set.f[i].tiles;
     }
     for (int i = set.n + 1; i <= moe::kMaxParts; ++i) set.blk_start[i] = set.blk_start[set.n];
@@ -520,7 +521,7 @@ moe_status run_experts(const moe_layer_desc& d, const moe_weights& w, const void
     if (gateup_only) return MOE_OK;
     set.blk_start[0] = 0;
     for (int i = 0; i < set.n; ++i) {
-      set.f[i].tiles = ceil_div(dm, moe::kWaves * (64 / lpr));
+      set.f[i].tiles = ceil_div(dm, moe::kWaves * moe::kFp8DownColGroups * (64 / lpr));
       set.blk_start[i + 1] = set.blk_start[i] + set.f[i].max_slots * set.f[i].tiles;
     }
     for (int i = set.n + 1; i <= moe::kMaxParts; ++i) set.blk_start[i] = set.blk_start[set.n];

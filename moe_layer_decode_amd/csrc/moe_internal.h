@@ -184,6 +184,9 @@ hipError_t launch_down_combine(const DownCombineArgs& a, void* y, hipStream_t st
 // 64 / lpr columns per wave), groups of any size taken kTokInline tokens at a
 // time.  d and every row length are multiples of 16 and at most
 // MOE_FP8_MAX_WIDTH.
+constexpr int kFp8RowsPerWave = 2;   // gate/up rows per wave (tiles of 4 * 2 rows)
+constexpr int kFp8DownColGroups = 2; // down: columns per wave = 2 * 64 / lpr
+constexpr int kFp8DnAhead = 2;       // down: 16-code steps requested ahead per column
 hipError_t launch_gateup_fp8(const FamilySet& set, const void* x, int T, int d, hipStream_t st,
                              const KernelEvents* ev);
 hipError_t launch_down_fp8(const FamilySet& set, int T, int d, int lpr, hipStream_t st,

@@ -2451,7 +2451,6 @@ __global__ __launch_bounds__(kDcWaves * kWave) void down_combine_kernel(DownComb
 // small, and the weights of a group of more than kTokInline rows are re-read
 // from the cache for each further chunk).
 // ---------------------------------------------------------------------------
-constexpr int kFp8Ahead = 4;  // weight steps requested ahead per row
 
 // Codes 4q .. 4q+3 of dword q as two bf16 pairs (byte 0 in the low half).
 __device__ __forceinline__ void fp8x16_to_bf16(const u32x4_t& w, uint32_t (&o)[8]) {
@@ -2480,26 +2479,46 @@ __device__ __forceinline__ float dot16(const uint32_t (&wb)[8], const bf16_t* p,
   return dot2_bf16(wb[7], b.w, acc);
 }
 
-__device__ __forceinline__ u32x4_t ld16_fp8(const uint8_t* p, bool stream) {
-  return stream ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p))
-                : *reinterpret_cast<const u32x4_t*>(p);
+// A buffer resource spanning one FP8 matrix: a load at a byte offset at or
+// past `bytes` returns zeros without a memory access, so a lane past its
+// row's end (or a row past the matrix end) takes an out-of-range offset
+// instead of a branch, and every load is unconditional -- the compiler then
+// waits for each step's own loads only, not for all loads in flight.
+constexpr uint32_t kFp8Oob = 0x80000000u;  // beyond every FP8 matrix (< 2^31 bytes)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t fp8_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kGfx9BufferDword3);
+}
+__device__ __forceinline__ u32x4_t fp8_ld(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
 }
 
-// Gate and up row i (one per wave) of matrix `mat` for every row of the
-// group, kTokInline tokens a chunk: h[r0 + t][i] = SiLU(sg * g_t) * (su * u_t).
+// Gate and up rows i0 .. i0 + RPW - 1 (one wave) of matrix `mat` for every
+// row of the group, kTokInline tokens a chunk: h[r0 + t][i] =
+// SiLU(sg_i * g_t) * (su_i * u_t).  A wave takes RPW consecutive rows so that
+// it streams as many bytes as a bf16 wave of one row; its loads run R steps
+// ahead across the row boundaries (the steps after the last row are out of
+// range).  Rows past the matrix end store nothing.
+template <int RPW, int R>
 __device__ __forceinline__ void gu_fp8(const Family& F, const Slot& sl, const bf16_t* __restrict__ x,
-                                       int T, int d, int i0, bf16_t* __restrict__ xl, int lane,
-                                       int wid) {
-  constexpr int NT = kTokInline, R = kFp8Ahead, STEP = 16 * kWave;
+                                       int d, int i0, bf16_t* __restrict__ xl, int lane, int wid) {
+  constexpr int NT = kTokInline, STEP = 16 * kWave;
   const int rows = F.rows, n = sl.n;
-  const int i = min(i0, rows - 1);
   const size_t ms = (size_t)rows * d;
-  const uint8_t* gp = static_cast<const uint8_t*>(F.gate) + (size_t)sl.mat * ms + (size_t)i * d + lane * 16;
-  const uint8_t* up = static_cast<const uint8_t*>(F.up) + (size_t)sl.mat * ms + (size_t)i * d + lane * 16;
-  const float sg = F.gate_scale[(size_t)sl.mat * rows + i];
-  const float su = F.up_scale[(size_t)sl.mat * rows + i];
-  const int dl = d - lane * 16;     // this lane's codes: lane*16 + k*STEP for k*STEP < dl
-  const bool stream = n <= NT;      // read once: streaming hint; else re-read per chunk
+  const __amdgpu_buffer_rsrc_t rsg =
+      fp8_rsrc(static_cast<const uint8_t*>(F.gate) + (size_t)sl.mat * ms, (uint32_t)ms);
+  const __amdgpu_buffer_rsrc_t rsu =
+      fp8_rsrc(static_cast<const uint8_t*>(F.up) + (size_t)sl.mat * ms, (uint32_t)ms);
+  const float* gsc = F.gate_scale + (size_t)sl.mat * rows;
+  const float* usc = F.up_scale + (size_t)sl.mat * rows;
+  const int nsteps = (d + STEP - 1) / STEP;
+  const int nouter = (nsteps + R - 1) / R;
+  const int spr = nouter * R;  // steps per row, padded to the ring
+  // byte offset of flat step f = k * spr + s (row i0 + k) for this lane
+  auto off = [&](int f) -> uint32_t {
+    const int k = f / spr, e = lane * 16 + (f - k * spr) * STEP;
+    return (k < RPW && i0 + k < rows && e < d) ? (uint32_t)((i0 + k) * d + e) : kFp8Oob;
+  };
   const bf16_t* xg = F.x_gate ? static_cast<const bf16_t*>(F.x_gate) : x;
   bf16_t* h = static_cast<bf16_t*>(F.h);
 #pragma unroll 1
@@ -2508,12 +2527,8 @@ __device__ __forceinline__ void gu_fp8(const Family& F, const Slot& sl, const bf
     u32x4_t rg[R], ru[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      if (r * STEP < dl) {
-        rg[r] = ld16_fp8(gp + r * STEP, stream);
-        ru[r] = ld16_fp8(up + r * STEP, stream);
-      } else {
-        rg[r] = ru[r] = u32x4_t{0, 0, 0, 0};
-      }
+      rg[r] = fp8_ld(rsg, off(r));
+      ru[r] = fp8_ld(rsu, off(r));
     }
     // the chunk's activation rows, one 1 KB wave instruction at a time
     {
@@ -2529,50 +2544,64 @@ __device__ __forceinline__ void gu_fp8(const Family& F, const Slot& sl, const bf
       }
     }
     stage_wait();
-    float ag[NT], au[NT];
+    float res[RPW], resu[RPW];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) ag[t] = au[t] = 0.f;
-    for (int c0 = 0; c0 < d; c0 += R * STEP) {
+    for (int k = 0; k < RPW; ++k) {
+      float ag[NT], au[NT];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int c = c0 + r * STEP;
-        if (c < dl) {
+      for (int t = 0; t < NT; ++t) ag[t] = au[t] = 0.f;
+      for (int o = 0; o < nouter; ++o) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int sidx = o * R + r;
+          // past the row's end the weights are zero and x is read at the
+          // row's last 16 elements (finite values)
+          const int xo = min(lane * 16 + sidx * STEP, d - 16);
           uint32_t wg[8], wu[8];
           fp8x16_to_bf16(rg[r], wg);
           fp8x16_to_bf16(ru[r], wu);
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
             if (t < nv) {
-              const bf16_t* xp = xl + (size_t)t * d + lane * 16 + c;
+              const bf16_t* xp = xl + (size_t)t * d + xo;
               ag[t] = dot16(wg, xp, ag[t]);
               au[t] = dot16(wu, xp, au[t]);
             }
           }
-          if (c + R * STEP < dl) {
-            rg[r] = ld16_fp8(gp + c + R * STEP, stream);
-            ru[r] = ld16_fp8(up + c + R * STEP, stream);
-          }
+          const int f = k * spr + sidx + R;
+          rg[r] = fp8_ld(rsg, off(f));
+          ru[r] = fp8_ld(rsu, off(f));
         }
       }
-    }
-    constexpr int N = 2 * NT;
-    float v[N];
+      constexpr int N = 2 * NT;
+      float v[N];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      v[t] = ag[t];
-      v[NT + t] = au[t];
+      for (int t = 0; t < NT; ++t) {
+        v[t] = ag[t];
+        v[NT + t] = au[t];
+      }
+      group_reduce_scatter<N, 64>(v, lane);
+      res[k] = v[0];
+      resu[k] = __shfl_xor(v[0], 32, kWave);  // gate index t and up index t + NT: lanes l, l ^ 32
     }
-    group_reduce_scatter<N, 64>(v, lane);
-    // gate index t and up index t + NT sit in lanes l and l ^ 32
-    const float upv = __shfl_xor(v[0], 32, kWave);
-    constexpr int SH = 6 - Log2<N>::value;
+    constexpr int SH = 6 - Log2<2 * NT>::value;
     const int t = lane >> SH;
-    if (t < NT && (lane & ((1 << SH) - 1)) == 0 && t < nv && i0 < rows)
-      store_act(h + (size_t)(sl.r0 + tc + t) * rows + i0, silu(sg * v[0]) * (su * upv));
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) {
+      const int i = i0 + k;
+      if (t < NT && (lane & ((1 << SH) - 1)) == 0 && t < nv && i < rows)
+        store_act(h + (size_t)(sl.r0 + tc + t) * rows + i,
+                  silu(gsc[i] * res[k]) * (usc[i] * resu[k]));
+    }
     __syncthreads();  // every wave is done with the staged rows before the next chunk
   }
 }
 
+constexpr int kFp8Rows = kFp8RowsPerWave;
+
+// R: 16-code steps requested ahead per row (more for long rows, whose
+// staged activations leave room for fewer waves per CU)
+template <int R>
 __global__ __launch_bounds__(kThreads) void gateup_fp8_kernel(FamilySet set,
                                                              const bf16_t* __restrict__ x, int T,
                                                              int d) {
@@ -2582,32 +2611,47 @@ __global__ __launch_bounds__(kThreads) void gateup_fp8_kernel(FamilySet set,
   Slot sl;
   if (!map_slot(F, T, sl, tile)) return;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  gu_fp8(F, sl, x, T, d, tile * kWaves + wid, reinterpret_cast<bf16_t*>(fp8_lds), lane, wid);
+  // the wave's first row, wave-uniform (the weight resources are scalar)
+  const int i0 = __builtin_amdgcn_readfirstlane((tile * kWaves + wid) * kFp8Rows);
+  gu_fp8<kFp8Rows, R>(F, sl, x, d, i0, reinterpret_cast<bf16_t*>(fp8_lds), lane, wid);
 }
 
-// Down columns cb + g (lane group g of LPR lanes) of matrix `mat` for every
-// row of the group, kTokInline rows of h a chunk: out[r0 + t][c] = sd[c] *
-// (W_down[c] . h[r0 + t]).
-template <int LPR>
+// Down columns cb + q*G + g (lane group g of LPR lanes, column group q < CG,
+// G = 64 / LPR) of matrix `mat` for every row of the group, kTokInline rows
+// of h a chunk: out[r0 + t][c] = sd[c] * (W_down[c] . h[r0 + t]).  CG column
+// groups per wave give it as many bytes as a bf16 wave.  Loads are
+// unconditional (out-of-range offsets past a row's end), R steps ahead.
+template <int LPR, int CG, int R>
 __device__ __forceinline__ void dn_fp8(const Family& F, const Slot& sl, int d, int cb,
                                        bf16_t* __restrict__ hl, int lane, int wid) {
-  constexpr int NT = kTokInline, R = kFp8Ahead, STEP = 16 * LPR;
+  constexpr int NT = kTokInline, STEP = 16 * LPR, G = 64 / LPR;
   const int rows = F.rows, n = sl.n;
   const int g = lane / LPR, j = lane - g * LPR;
-  const int c = min(cb + g, d - 1);
-  const uint8_t* wp = static_cast<const uint8_t*>(F.down) + (size_t)sl.mat * rows * d +
-                      (size_t)c * rows + j * 16;
-  const float sd = F.down_scale[(size_t)sl.mat * d + c];
+  const size_t ms = (size_t)rows * d;
+  const __amdgpu_buffer_rsrc_t rs =
+      fp8_rsrc(static_cast<const uint8_t*>(F.down) + (size_t)sl.mat * ms, (uint32_t)ms);
+  uint32_t cbase[CG];
+  float sd[CG];
+#pragma unroll
+  for (int q = 0; q < CG; ++q) {
+    const int c = cb + q * G + g;
+    cbase[q] = c < d ? (uint32_t)(c * rows + j * 16) : kFp8Oob;
+    sd[q] = F.down_scale[(size_t)sl.mat * d + min(c, d - 1)];
+  }
   const int rl = rows - j * 16;  // this lane's codes: j*16 + k*STEP for k*STEP < rl
-  const bool stream = n <= NT;
+  const int nouter = ((rows + STEP - 1) / STEP + R - 1) / R;
+  auto off = [&](int q, int sidx) -> uint32_t {
+    return (sidx * STEP < rl && cbase[q] != kFp8Oob) ? cbase[q] + sidx * STEP : kFp8Oob;
+  };
   const bf16_t* h = static_cast<const bf16_t*>(F.h);
 #pragma unroll 1
   for (int tc = 0; tc < n; tc += NT) {
     const int nv = min(NT, n - tc);
-    u32x4_t rw[R];
+    u32x4_t rw[R][CG];
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      rw[r] = r * STEP < rl ? ld16_fp8(wp + r * STEP, stream) : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int q = 0; q < CG; ++q) rw[r][q] = fp8_ld(rs, off(q, r));
     {
       constexpr int EPI = 8 * kWave;
       const int per_row = (rows + EPI - 1) / EPI, total = nv * per_row;
@@ -2620,32 +2664,57 @@ __device__ __forceinline__ void dn_fp8(const Family& F, const Slot& sl, int d, i
       }
     }
     stage_wait();
-    float acc[NT];
+    float acc[CG][NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = 0.f;
-    for (int k0 = 0; k0 < rows; k0 += R * STEP) {
+    for (int q = 0; q < CG; ++q)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[q][t] = 0.f;
+    for (int o = 0; o < nouter; ++o) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const int k = k0 + r * STEP;
-        if (k < rl) {
+        const int sidx = o * R + r;
+        const int ho = min(j * 16 + sidx * STEP, rows - 16);
+#pragma unroll
+        for (int q = 0; q < CG; ++q) {
           uint32_t wb[8];
-          fp8x16_to_bf16(rw[r], wb);
+          fp8x16_to_bf16(rw[r][q], wb);
 #pragma unroll
           for (int t = 0; t < NT; ++t)
-            if (t < nv) acc[t] = dot16(wb, hl + (size_t)t * rows + j * 16 + k, acc[t]);
-          if (k + R * STEP < rl) rw[r] = ld16_fp8(wp + k + R * STEP, stream);
+            if (t < nv) acc[q][t] = dot16(wb, hl + (size_t)t * rows + ho, acc[q][t]);
+          rw[r][q] = fp8_ld(rs, off(q, sidx + R));
         }
       }
     }
-    group_reduce_scatter<NT, LPR>(acc, lane);
-    // lane j of the group holds token j / (LPR / NT)
-    constexpr int SPAN = LPR / NT;
-    const int t = j / SPAN;
-    if (j % SPAN == 0 && t < nv && cb + g < d)
-      F.out[(size_t)(sl.r0 + tc + t) * d + cb + g] = sd * acc[0];
+    constexpr int N = CG * NT;
+    float v[N];
+#pragma unroll
+    for (int q = 0; q < CG; ++q)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) v[q * NT + t] = acc[q][t];
+    group_reduce_scatter<N, LPR>(v, lane);
+    if constexpr (N >= LPR) {
+      constexpr int PER = N / LPR;
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const int idx = j * PER + p, q = idx / NT, t = idx - (idx / NT) * NT;
+        const int c = cb + q * G + g;
+        if (t < nv && c < d) F.out[(size_t)(sl.r0 + tc + t) * d + c] = sd[q] * v[p];
+      }
+    } else {
+      // lane j of the group holds value index j / (LPR / N)
+      constexpr int SPAN = LPR / N;
+      const int idx = j / SPAN, q = idx / NT, t = idx - (idx / NT) * NT;
+      const int c = cb + q * G + g;
+      float sc = sd[0];
+#pragma unroll
+      for (int qq = 1; qq < CG; ++qq) sc = q == qq ? sd[qq] : sc;
+      if (j % SPAN == 0 && t < nv && c < d) F.out[(size_t)(sl.r0 + tc + t) * d + c] = sc * v[0];
+    }
     __syncthreads();
   }
 }
+
+constexpr int kFp8ColGroups = kFp8DownColGroups;
 
 template <int LPR>
 __global__ __launch_bounds__(kThreads) void down_fp8_kernel(FamilySet set, int T, int d) {
@@ -2655,9 +2724,10 @@ __global__ __launch_bounds__(kThreads) void down_fp8_kernel(FamilySet set, int T
   Slot sl;
   if (!map_slot(F, T, sl, tile)) return;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  constexpr int G = 64 / LPR;
-  dn_fp8<LPR>(F, sl, d, tile * (kWaves * G) + wid * G, reinterpret_cast<bf16_t*>(fp8_lds), lane,
-              wid);
+  constexpr int CPW = kFp8ColGroups * (64 / LPR);  // columns per wave
+  const int cb = __builtin_amdgcn_readfirstlane(tile * (kWaves * CPW) + wid * CPW);
+  dn_fp8<LPR, kFp8ColGroups, kFp8DnAhead>(F, sl, d, cb, reinterpret_cast<bf16_t*>(fp8_lds), lane,
+                                          wid);
 }
 
 __global__ void zero_kernel(unsigned int* p, size_t n) {
@@ -2829,13 +2899,20 @@ hipError_t launch_gateup_fp8(const FamilySet& set, const void* x, int T, int d, 
                              const KernelEvents* ev) {
   if (set.blk_start[set.n] <= 0) return hipSuccess;
   const dim3 grid(set.blk_start[set.n]), block(kThreads);
-  const size_t lds = (size_t)kTokInline * d * sizeof(bf16_t);
+  // a chunk stages at most min(T, kTokInline) activation rows
+  const size_t lds = (size_t)(T < kTokInline ? T : kTokInline) * d * sizeof(bf16_t);
   const bf16_t* xb = static_cast<const bf16_t*>(x);
-  if (ev)
-    hipExtLaunchKernelGGL(gateup_fp8_kernel, grid, block, lds, st, ev->start, ev->stop, 0, set, xb,
-                          T, d);
+  auto go = [&](auto kernel) {
+    if (ev)
+      hipExtLaunchKernelGGL(kernel, grid, block, lds, st, ev->start, ev->stop, 0, set, xb, T, d);
+    else
+      hipLaunchKernelGGL(kernel, grid, block, lds, st, set, xb, T, d);
+  };
+  // measured: two steps ahead for rows of up to 2048 codes, four beyond
+  if (d <= 2048)
+    go(gateup_fp8_kernel<2>);
   else
-    hipLaunchKernelGGL(gateup_fp8_kernel, grid, block, lds, st, set, xb, T, d);
+    go(gateup_fp8_kernel<4>);
   return hipGetLastError();
 }
 
@@ -2845,7 +2922,8 @@ hipError_t launch_down_fp8(const FamilySet& set, int T, int d, int lpr, hipStrea
   const dim3 grid(set.blk_start[set.n]), block(kThreads);
   int max_rows = 0;
   for (int i = 0; i < set.n; ++i) max_rows = set.f[i].rows > max_rows ? set.f[i].rows : max_rows;
-  const size_t lds = (size_t)kTokInline * max_rows * sizeof(bf16_t);
+  // a group has at most T rows: a chunk stages at most min(T, kTokInline) rows of h
+  const size_t lds = (size_t)(T < kTokInline ? T : kTokInline) * max_rows * sizeof(bf16_t);
   auto go = [&](auto kernel) {
     if (ev)
       hipExtLaunchKernelGGL(kernel, grid, block, lds, st, ev->start, ev->stop, 0, set, T, d);
