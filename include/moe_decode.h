@@ -306,6 +306,15 @@ moe_status moe_layer_decode(const moe_layer_desc* desc, const moe_weights* weigh
 /* Static text for a status code. */
 const char* moe_status_string(moe_status status);
 
+/* Host-only: the number of kernels moe_layer_decode launches for T tokens
+ * (0 for T = 0, -1 for an invalid descriptor or T): 5 (route, top-k + plan,
+ * gate/up, down, combine); 4 where the down projection writes y itself (bf16
+ * plain and slice forms at T <= 4 whose rows of h fit its LDS budget -- the
+ * combine stage is then an empty interval); 8 in the factorised form
+ * (backbone gate/up, private gate/up, private down, pair sums, department
+ * down). */
+int32_t moe_layer_kernel_count(const moe_layer_desc* desc, int32_t T);
+
 /* Bytes of weights one step streams for the given active counts: router,
  * n_active routed experts, n_active_depts department slices, the shared
  * expert (each matrix read once; FP8 layers: one byte per expert weight plus

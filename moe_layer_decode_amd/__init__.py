@@ -21,7 +21,8 @@ __all__ = [
     "MoeError", "LayerDesc", "Weights", "Plan", "layer_desc", "lib", "lib_path",
     "moe_workspace_bytes", "moe_workspace_init", "moe_validate_desc", "moe_route", "moe_dispatch",
     "moe_expert_ffn", "moe_combine", "moe_layer_decode", "moe_status_string",
-    "moe_loaded_weight_bytes", "moe_stream_read", "alloc_workspace", "plan_to_host", "MoeLayer",
+    "moe_loaded_weight_bytes", "moe_stream_read", "moe_layer_kernel_count", "alloc_workspace",
+    "plan_to_host", "MoeLayer",
     "MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE",
     "MOE_ERR_HIP", "SCORE_FNS", "DEPT_FORMS", "MOE_DEPT_SLICE", "MOE_DEPT_FACTORISED",
     "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3",
@@ -40,7 +41,7 @@ STAGE_NAMES = ("route", "dispatch", "gateup", "down", "combine")
 EXPORTED_SYMBOLS = (
     "moe_workspace_bytes", "moe_workspace_init", "moe_validate_desc", "moe_plan_from_workspace", "moe_route",
     "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_layer_decode",
-    "moe_status_string", "moe_loaded_weight_bytes", "moe_stream_read",
+    "moe_status_string", "moe_loaded_weight_bytes", "moe_stream_read", "moe_layer_kernel_count",
 )
 
 _i32, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -127,6 +128,8 @@ def lib() -> ctypes.CDLL:
     L.moe_loaded_weight_bytes.restype = ctypes.c_uint64
     L.moe_stream_read.argtypes = [_vp, _sz, _vp, _vp]
     L.moe_stream_read.restype = _i32
+    L.moe_layer_kernel_count.argtypes = [P(LayerDesc), _i32]
+    L.moe_layer_kernel_count.restype = _i32
     _LIB = L
     return L
 
@@ -179,6 +182,12 @@ def moe_workspace_bytes(desc: LayerDesc) -> int:
 
 def moe_loaded_weight_bytes(desc: LayerDesc, n_active: int, n_active_depts: int = 0) -> int:
     return int(lib().moe_loaded_weight_bytes(ctypes.byref(desc), n_active, n_active_depts))
+
+
+def moe_layer_kernel_count(desc: LayerDesc, T: int) -> int:
+    """Kernels moe_layer_decode launches for T tokens (4: the down launch
+    writes y itself and the combine stage is empty)."""
+    return int(lib().moe_layer_kernel_count(ctypes.byref(desc), T))
 
 
 def moe_workspace_init(desc: LayerDesc, workspace: torch.Tensor):

@@ -838,6 +838,20 @@ moe_status moe_layer_decode(const moe_layer_desc* desc, const moe_weights* weigh
   return MOE_OK;
 }
 
+int32_t moe_layer_kernel_count(const moe_layer_desc* desc, int32_t T) {
+  if (check_desc(desc) != MOE_OK || check_tokens(desc, T) != MOE_OK) return -1;
+  if (T == 0) return 0;
+  if (factorised(*desc)) return 8;
+  // the eligibility test reads only the descriptor and T; the addresses it
+  // forms from a workspace base are never dereferenced here
+  void* base = reinterpret_cast<void*>(uintptr_t(1) << 20);
+  moe_weights w{};
+  moe_plan p;
+  fill_plan(*desc, base, T, &p);
+  moe::DownCombineArgs a;
+  return down_combine_args(*desc, w, p, base, T, &a) ? 4 : 5;
+}
+
 const char* moe_status_string(moe_status status) {
   switch (status) {
     case MOE_OK: return "ok";

@@ -14,8 +14,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared_functions():
     with open(os.path.join(ROOT, "include", "moe_decode.h")) as f:
         src = f.read()
-    return sorted(set(re.findall(r"^(?:const char\*|size_t|moe_status|uint64_t)\s+(moe_\w+)\(",
-                                 src, re.M)))
+    return sorted(set(re.findall(
+        r"^(?:const char\*|size_t|moe_status|uint64_t|int32_t)\s+(moe_\w+)\(", src, re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -259,3 +259,21 @@ def test_fp8_loaded_weight_bytes_match_the_oracle(lib):
                                          n_depts=d.n_depts, d_ff_dept=d.d_ff_dept,
                                          d_ff_shared=d.d_ff_shared)
         assert M.moe_loaded_weight_bytes(d, n_act, n_dep) == want
+
+
+def test_layer_kernel_count(lib):
+    """Four launches where the down projection writes y (bf16, T <= 4, rows
+    of h within the LDS budget), five otherwise, eight in the factorised
+    form; 0 at T = 0, -1 for an invalid descriptor or T."""
+    q = _desc(max_tokens=16)
+    assert [M.moe_layer_kernel_count(q, T) for T in (0, 1, 4, 5, 16)] == [0, 4, 4, 5, 5]
+    assert M.moe_layer_kernel_count(q, 17) == -1
+    assert M.moe_layer_kernel_count(_desc(d_model=7), 1) == -1
+    # rows of h over the LDS budget: 4 tokens x 8 experts x 2048 bf16 = 128 KiB
+    assert M.moe_layer_kernel_count(_desc(d_ff=2048, max_tokens=4), 4) == 5
+    assert M.moe_layer_kernel_count(_desc(d_ff=2048, max_tokens=4), 1) == 4
+    assert M.moe_layer_kernel_count(_desc(dtype="f32"), 1) == 5
+    assert M.moe_layer_kernel_count(_desc(expert_dtype="fp8"), 1) == 5
+    fac = _desc(n_experts=32, top_k=6, d_ff=256, n_depts=4, d_ff_dept=256,
+                dept_form="factorised")
+    assert M.moe_layer_kernel_count(fac, 3) == 8
