@@ -2501,7 +2501,8 @@ __device__ __forceinline__ u32x4_t fp8_ld(__amdgpu_buffer_rsrc_t rs, uint32_t of
 // range).  Rows past the matrix end store nothing.
 template <int RPW, int R>
 __device__ __forceinline__ void gu_fp8(const Family& F, const Slot& sl, const bf16_t* __restrict__ x,
-                                       int d, int i0, bf16_t* __restrict__ xl, int lane, int wid) {
+                                       int d, int i0, int nts, bf16_t* __restrict__ xl, int lane,
+                                       int wid) {
   constexpr int NT = kTokInline, STEP = 16 * kWave;
   const int rows = F.rows, n = sl.n;
   const size_t ms = (size_t)rows * d;
@@ -2522,8 +2523,8 @@ __device__ __forceinline__ void gu_fp8(const Family& F, const Slot& sl, const bf
   const bf16_t* xg = F.x_gate ? static_cast<const bf16_t*>(F.x_gate) : x;
   bf16_t* h = static_cast<bf16_t*>(F.h);
 #pragma unroll 1
-  for (int tc = 0; tc < n; tc += NT) {
-    const int nv = min(NT, n - tc);
+  for (int tc = 0; tc < n; tc += nts) {
+    const int nv = min(nts, n - tc);
     u32x4_t rg[R], ru[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -2537,7 +2538,9 @@ __device__ __forceinline__ void gu_fp8(const Family& F, const Slot& sl, const bf
       for (int q = wid; q < total; q += kWaves) {
         const int t = q / per_row, c0 = (q - t * per_row) * EPI;
         const int c = c0 + lane * 8;
-        const int tok = slot_token(sl, F.grp_token, tc, t, n, F.in_rows);
+        // row tc + t of the group (inline tokens are indexed from the
+        // group's first row, so the chunk offset goes into the row index)
+        const int tok = slot_token(sl, F.grp_token, 0, tc + t, n, F.in_rows);
         if (c < d)
           __builtin_amdgcn_global_load_lds(xg + (size_t)tok * d + c,
                                            (lds_void_t*)(xl + (size_t)t * d + c0), 16, 0, 0);
@@ -2604,7 +2607,7 @@ constexpr int kFp8Rows = kFp8RowsPerWave;
 template <int R>
 __global__ __launch_bounds__(kThreads) void gateup_fp8_kernel(FamilySet set,
                                                              const bf16_t* __restrict__ x, int T,
-                                                             int d) {
+                                                             int d, int nts) {
   extern __shared__ __align__(16) unsigned char fp8_lds[];
   int tile;
   const Family& F = block_part(set, tile);
@@ -2613,7 +2616,7 @@ __global__ __launch_bounds__(kThreads) void gateup_fp8_kernel(FamilySet set,
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   // the wave's first row, wave-uniform (the weight resources are scalar)
   const int i0 = __builtin_amdgcn_readfirstlane((tile * kWaves + wid) * kFp8Rows);
-  gu_fp8<kFp8Rows, R>(F, sl, x, d, i0, reinterpret_cast<bf16_t*>(fp8_lds), lane, wid);
+  gu_fp8<kFp8Rows, R>(F, sl, x, d, i0, nts, reinterpret_cast<bf16_t*>(fp8_lds), lane, wid);
 }
 
 // Down columns cb + q*G + g (lane group g of LPR lanes, column group q < CG,
@@ -2622,7 +2625,7 @@ __global__ __launch_bounds__(kThreads) void gateup_fp8_kernel(FamilySet set,
 // groups per wave give it as many bytes as a bf16 wave.  Loads are
 // unconditional (out-of-range offsets past a row's end), R steps ahead.
 template <int LPR, int CG, int R>
-__device__ __forceinline__ void dn_fp8(const Family& F, const Slot& sl, int d, int cb,
+__device__ __forceinline__ void dn_fp8(const Family& F, const Slot& sl, int d, int cb, int nts,
                                        bf16_t* __restrict__ hl, int lane, int wid) {
   constexpr int NT = kTokInline, STEP = 16 * LPR, G = 64 / LPR;
   const int rows = F.rows, n = sl.n;
@@ -2645,8 +2648,8 @@ __device__ __forceinline__ void dn_fp8(const Family& F, const Slot& sl, int d, i
   };
   const bf16_t* h = static_cast<const bf16_t*>(F.h);
 #pragma unroll 1
-  for (int tc = 0; tc < n; tc += NT) {
-    const int nv = min(NT, n - tc);
+  for (int tc = 0; tc < n; tc += nts) {
+    const int nv = min(nts, n - tc);
     u32x4_t rw[R][CG];
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -2717,7 +2720,7 @@ __device__ __forceinline__ void dn_fp8(const Family& F, const Slot& sl, int d, i
 constexpr int kFp8ColGroups = kFp8DownColGroups;
 
 template <int LPR>
-__global__ __launch_bounds__(kThreads) void down_fp8_kernel(FamilySet set, int T, int d) {
+__global__ __launch_bounds__(kThreads) void down_fp8_kernel(FamilySet set, int T, int d, int nts) {
   extern __shared__ __align__(16) unsigned char fp8_lds[];
   int tile;
   const Family& F = block_part(set, tile);
@@ -2726,8 +2729,8 @@ __global__ __launch_bounds__(kThreads) void down_fp8_kernel(FamilySet set, int T
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   constexpr int CPW = kFp8ColGroups * (64 / LPR);  // columns per wave
   const int cb = __builtin_amdgcn_readfirstlane(tile * (kWaves * CPW) + wid * CPW);
-  dn_fp8<LPR, kFp8ColGroups, kFp8DnAhead>(F, sl, d, cb, reinterpret_cast<bf16_t*>(fp8_lds), lane,
-                                          wid);
+  dn_fp8<LPR, kFp8ColGroups, kFp8DnAhead>(F, sl, d, cb, nts, reinterpret_cast<bf16_t*>(fp8_lds),
+                                          lane, wid);
 }
 
 __global__ void zero_kernel(unsigned int* p, size_t n) {
@@ -2895,18 +2898,30 @@ hipError_t launch_down_combine(const DownCombineArgs& a, void* y, hipStream_t st
   return hipGetLastError();
 }
 
+// Rows staged per token chunk of the FP8 kernels: at most kTokInline, at most
+// T (a group has at most T rows), and few enough that a block's staged rows
+// of `width` bf16 stay within kFp8StageBytes (long rows would otherwise leave
+// room for only two blocks per CU).
+constexpr int kFp8StageBytes = 32 * 1024;
+static int fp8_chunk_tokens(int T, int width) {
+  int n = T < kTokInline ? T : kTokInline;
+  while (n > 1 && (size_t)n * width * sizeof(bf16_t) > (size_t)kFp8StageBytes) --n;
+  return n;
+}
+
 hipError_t launch_gateup_fp8(const FamilySet& set, const void* x, int T, int d, hipStream_t st,
                              const KernelEvents* ev) {
   if (set.blk_start[set.n] <= 0) return hipSuccess;
   const dim3 grid(set.blk_start[set.n]), block(kThreads);
-  // a chunk stages at most min(T, kTokInline) activation rows
-  const size_t lds = (size_t)(T < kTokInline ? T : kTokInline) * d * sizeof(bf16_t);
+  const int nts = fp8_chunk_tokens(T, d);
+  const size_t lds = (size_t)nts * d * sizeof(bf16_t);
   const bf16_t* xb = static_cast<const bf16_t*>(x);
   auto go = [&](auto kernel) {
     if (ev)
-      hipExtLaunchKernelGGL(kernel, grid, block, lds, st, ev->start, ev->stop, 0, set, xb, T, d);
+      hipExtLaunchKernelGGL(kernel, grid, block, lds, st, ev->start, ev->stop, 0, set, xb, T, d,
+                            nts);
     else
-      hipLaunchKernelGGL(kernel, grid, block, lds, st, set, xb, T, d);
+      hipLaunchKernelGGL(kernel, grid, block, lds, st, set, xb, T, d, nts);
   };
   // measured: two steps ahead for rows of up to 2048 codes, four beyond
   if (d <= 2048)
@@ -2922,13 +2937,13 @@ hipError_t launch_down_fp8(const FamilySet& set, int T, int d, int lpr, hipStrea
   const dim3 grid(set.blk_start[set.n]), block(kThreads);
   int max_rows = 0;
   for (int i = 0; i < set.n; ++i) max_rows = set.f[i].rows > max_rows ? set.f[i].rows : max_rows;
-  // a group has at most T rows: a chunk stages at most min(T, kTokInline) rows of h
-  const size_t lds = (size_t)(T < kTokInline ? T : kTokInline) * max_rows * sizeof(bf16_t);
+  const int nts = fp8_chunk_tokens(T, max_rows);
+  const size_t lds = (size_t)nts * max_rows * sizeof(bf16_t);
   auto go = [&](auto kernel) {
     if (ev)
-      hipExtLaunchKernelGGL(kernel, grid, block, lds, st, ev->start, ev->stop, 0, set, T, d);
+      hipExtLaunchKernelGGL(kernel, grid, block, lds, st, ev->start, ev->stop, 0, set, T, d, nts);
     else
-      hipLaunchKernelGGL(kernel, grid, block, lds, st, set, T, d);
+      hipLaunchKernelGGL(kernel, grid, block, lds, st, set, T, d, nts);
   };
   if (lpr == 16)
     go(down_fp8_kernel<16>);

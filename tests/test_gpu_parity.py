@@ -58,6 +58,11 @@ FP8 = {
     "fp8_d512_e6_i1040_top3": moe_synth.LayerShape(
         name="fp8_d512_e6_i1040_top3", d=512, n_experts=6, top_k=3, d_ff=1040,
         expert_dtype="fp8", batches=(1, 3, 9)),
+    # rows long enough that the gate/up stages two tokens per chunk, so groups
+    # of three and four rows (tokens carried in the descriptor) span chunks
+    "fp8_d3088_e6_i96_top3": moe_synth.LayerShape(
+        name="fp8_d3088_e6_i96_top3", d=3088, n_experts=6, top_k=3, d_ff=96,
+        expert_dtype="fp8", batches=(1, 4, 9)),
 }
 SH = {**moe_synth.SHAPES, **FACT, **FP8}
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")
