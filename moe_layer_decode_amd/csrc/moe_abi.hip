@@ -576,7 +576,8 @@ moe_status run_experts(const moe_layer_desc& d, const moe_weights& w, const void
 }
 
 // The down projection with the combine as its epilogue (one launch writing y)
-// serves bf16 layers in the plain and slice forms at batches of at most
+// serves bf16-activation layers (bf16 or FP8 weights) in the plain and slice
+// forms at batches of at most
 // kTokInline tokens, where every group is small, when the rows of h it stages
 // fit kDcMaxLds (two blocks per CU) and no intermediate row is longer than
 // kDcMaxRows.  Returns false (and fills nothing) otherwise; the step then
@@ -584,7 +585,8 @@ moe_status run_experts(const moe_layer_desc& d, const moe_weights& w, const void
 constexpr size_t kDcMaxLds = 80 * 1024;
 bool down_combine_args(const moe_layer_desc& d, const moe_weights& w, const moe_plan& p,
                        void* ws, int32_t T, moe::DownCombineArgs* out) {
-  if (d.w_dtype != MOE_BF16 || d.act_dtype != MOE_BF16 || factorised(d)) return false;
+  if ((d.w_dtype != MOE_BF16 && !fp8(d)) || d.act_dtype != MOE_BF16 || factorised(d))
+    return false;
   if (T < 1 || T > moe::kTokInline) return false;
   const Layout L = layout_of(d);
   moe::DownCombineArgs a{};
@@ -602,6 +604,7 @@ bool down_combine_args(const moe_layer_desc& d, const moe_weights& w, const moe_
   {
     moe::DcFamily f{};
     f.down = w.w_down;
+    f.down_scale = w.w_down_scale;
     f.work = at<WorkDesc>(ws, L, R_WORK);  // the small list: every group at T <= kTokInline
     f.n_items = p.header + moe::kHdrSmall;
     f.wrow = p.row_weight;
@@ -616,6 +619,7 @@ bool down_combine_args(const moe_layer_desc& d, const moe_weights& w, const moe_
   if (d.n_depts > 0) {
     moe::DcFamily f{};
     f.down = w.wd_down;
+    f.down_scale = w.wd_down_scale;
     f.work = at<WorkDesc>(ws, L, R_DWORK);
     f.n_items = p.header + moe::kHdrDeptSmall;
     f.wrow = p.dept_row_scale;
@@ -630,6 +634,7 @@ bool down_combine_args(const moe_layer_desc& d, const moe_weights& w, const moe_
   if (d.d_ff_shared > 0) {
     moe::DcFamily f{};
     f.down = w.ws_down;
+    f.down_scale = w.ws_down_scale;
     f.h = at<void>(ws, L, R_HS);
     f.rows = d.d_ff_shared;
     f.max_items = 1;
@@ -639,6 +644,7 @@ bool down_combine_args(const moe_layer_desc& d, const moe_weights& w, const moe_
   }
   a.T = T;
   a.d = d.d_model;
+  a.fp8 = fp8(d) ? 1 : 0;
   a.h_elems = (int)off;
   a.max_items = (int)items;
   if (!fits || off > (int64_t)kDcMaxLds || moe::down_combine_lds_bytes(a) > kDcMaxLds)

@@ -115,7 +115,8 @@ constexpr int kDcWaves = 8;          // waves (output columns) per block
 constexpr int kDcFamilies = 3;       // routed experts, department slices, shared expert
 constexpr int kDcMaxRows = 2048;     // longest intermediate row it streams (4 steps of 512)
 struct DcFamily {
-  const void* down;        // [n_mats][d][rows]
+  const void* down;        // [n_mats][d][rows] (bf16, or FP8 codes)
+  const float* down_scale; // FP8: per-column scales [n_mats][d]; else nullptr
   const WorkDesc* work;    // small-group descriptors; nullptr: the shared expert (one group, all T tokens)
   const int* n_items;      // device count of descriptors (unused when work is nullptr)
   const float* wrow;       // weight of h row r (routing weight or c_{t,J}); nullptr: 1
@@ -133,6 +134,7 @@ struct DownCombineArgs {
   int T, d;
   int h_elems;             // staged elements of h over all families (multiple of 8)
   int max_items;           // sum of the families' max_items
+  int fp8;                 // 1: FP8 weights (E4M3 codes + per-column scales)
 };
 size_t down_combine_lds_bytes(const DownCombineArgs& a);
 
@@ -176,7 +178,8 @@ hipError_t launch_down(int w_dtype, const FamilySet& set, int T, int d, int lpr,
                        hipStream_t st, const KernelEvents* ev);
 hipError_t launch_combine(int act_dtype, const CombineArgs& a, void* y, hipStream_t st,
                           const KernelEvents* ev);
-// bf16 layers only; the caller checks T <= kTokInline and the LDS size.
+// bf16 activations (bf16 or FP8 weights); the caller checks T <= kTokInline,
+// the LDS size and kDcMaxRows.
 hipError_t launch_down_combine(const DownCombineArgs& a, void* y, hipStream_t st,
                                const KernelEvents* ev);
 // FP8 expert weights (E4M3 codes + per-row scales, bf16 activations): every

@@ -2218,6 +2218,36 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a, AT* __
   store_act(y + (size_t)t * a.d + c, acc);
 }
 
+// FP8 (OCP E4M3) weight codes, used by the fused down + combine and the FP8
+// expert kernels below.  Every E4M3 value is exactly a bf16 value, so
+// v_cvt_scalef32_pk_bf16_fp8 with scale 1 widens two codes to a bf16 pair.
+// Codes 4q .. 4q+3 of dword q as two bf16 pairs (byte 0 in the low half).
+__device__ __forceinline__ void fp8x16_to_bf16(const u32x4_t& w, uint32_t (&o)[8]) {
+  const uint32_t d4[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    o[2 * q] = __builtin_bit_cast(uint32_t,
+                                  __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d4[q], 1.0f, false));
+    o[2 * q + 1] = __builtin_bit_cast(uint32_t,
+                                      __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d4[q], 1.0f, true));
+  }
+}
+
+// sum over 16 consecutive k of weight (widened codes) * activation, where
+// the activations are 16 bf16 at p (16-byte aligned, LDS)
+__device__ __forceinline__ float dot16(const uint32_t (&wb)[8], const bf16_t* p, float acc) {
+  const u32x4_t a = *reinterpret_cast<const u32x4_t*>(p);
+  const u32x4_t b = *reinterpret_cast<const u32x4_t*>(p + 8);
+  acc = dot2_bf16(wb[0], a.x, acc);
+  acc = dot2_bf16(wb[1], a.y, acc);
+  acc = dot2_bf16(wb[2], a.z, acc);
+  acc = dot2_bf16(wb[3], a.w, acc);
+  acc = dot2_bf16(wb[4], b.x, acc);
+  acc = dot2_bf16(wb[5], b.y, acc);
+  acc = dot2_bf16(wb[6], b.z, acc);
+  return dot2_bf16(wb[7], b.w, acc);
+}
+
 // ---------------------------------------------------------------------------
 // Down projection with the combine as its epilogue, for batches of at most
 // kTokInline tokens.  DeaMoE Eq. (3) sums each token's routing-weighted expert
@@ -2235,7 +2265,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a, AT* __
 // order of the plan, so results do not depend on timing.
 // ---------------------------------------------------------------------------
 struct DcItem {
-  const bf16_t* w;          // the group's matrix [d][rows]
+  const void* w;            // the group's matrix [d][rows] (bf16, or FP8 codes)
+  const float* scale;       // FP8: the matrix's per-column scales [d]; else nullptr
   int rows;                 // row length (elements)
   int nsteps;               // steps of 64 lanes x 8 elements per weight row
   int n;                    // rows of the group (0: invalid descriptor, streamed and unused)
@@ -2255,12 +2286,16 @@ __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlan
 __device__ __forceinline__ float uni(float v) {
   return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
 }
-__device__ __forceinline__ const bf16_t* uni(const bf16_t* p) {
+template <typename P>
+__device__ __forceinline__ P* uni(P* p) {
   const uint64_t u = reinterpret_cast<uint64_t>(p);
   const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
   const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
-  return reinterpret_cast<const bf16_t*>(lo | (hi << 32));
+  return reinterpret_cast<P*>(lo | (hi << 32));
 }
+
+// Elements a lane takes per 16-byte step: 8 bf16 weights or 16 FP8 codes.
+template <bool FP8> constexpr int dc_epl() { return FP8 ? 16 : 8; }
 
 // Weight row of column c of group i < ie: NS steps of 64 lanes x 8 elements,
 // through a buffer resource that spans exactly that row, so lanes past the
@@ -2271,28 +2306,32 @@ __device__ __forceinline__ const bf16_t* uni(const bf16_t* p) {
 constexpr int kGfx9BufferDword3 = 0x00020000;  // raw (untyped) 32-bit buffer access
 constexpr int kCpolNt = 2;                     // non-temporal: weights are read once
 
-template <int NS>
+// FP8: also the column's scale (a scalar load, issued as far ahead).
+template <int NS, bool FP8>
 __device__ __forceinline__ void dc_load(const DcItem* items, int i, int ie, int c, int lane,
-                                        u32x4_t (&dst)[NS]) {
+                                        u32x4_t (&dst)[NS], float& scl) {
+  constexpr int EPL = dc_epl<FP8>(), ESZ = FP8 ? 1 : 2;
   const DcItem& it = items[min(i, ie - 1)];
   const int rows = uni(it.rows);
-  const bf16_t* w = uni(it.w) + (size_t)c * rows;
+  const char* w = static_cast<const char*>(uni(it.w)) + (size_t)c * rows * ESZ;
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16_t*>(w), (short)0, i < ie ? rows * 2 : 0, kGfx9BufferDword3);
+      const_cast<char*>(w), (short)0, i < ie ? rows * ESZ : 0, kGfx9BufferDword3);
 #pragma unroll
   for (int s = 0; s < NS; ++s)
     dst[s] = __builtin_bit_cast(
-        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (lane * 8 + s * 8 * kWave) * 2, 0,
-                                                       kCpolNt));
+        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                     rs, (lane * EPL + s * EPL * kWave) * ESZ, 0, kCpolNt));
+  if constexpr (FP8) scl = uni(it.scale)[c];
 }
 
 // Dot products of group i's weight row with its rows of h (LDS), folded into
 // the token accumulators with the rows' weights; nothing outside [ib, ie).
-template <int NS>
+template <int NS, bool FP8>
 __device__ __forceinline__ void dc_consume(const DcItem* items, int i, int ib, int ie,
                                            const bf16_t* hl,
-                                           int lane, const u32x4_t (&wv)[NS],
+                                           int lane, const u32x4_t (&wv)[NS], float scl,
                                            float (&acc)[kTokInline]) {
+  constexpr int EPL = dc_epl<FP8>();
   const DcItem& it = items[min(max(i, ib), ie - 1)];
   const int rows = uni(it.rows), n = (i >= ib && i < ie) ? uni(it.n) : 0;
 #pragma unroll
@@ -2303,16 +2342,22 @@ __device__ __forceinline__ void dc_consume(const DcItem* items, int i, int ib, i
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         // past the row's end the weights are zero and h is read at the row's
-        // last 16 bytes (finite values)
-        const int e = min(lane * 8 + s * 8 * kWave, rows - 8);
-        Raw8<bf16_t> w8;
-        w8.u = wv[s];
-        part = dot8(w8, *reinterpret_cast<const X8<bf16_t>*>(hl + ho + e), part);
+        // last EPL elements (finite values)
+        const int e = min(lane * EPL + s * EPL * kWave, rows - EPL);
+        if constexpr (FP8) {
+          uint32_t wb[8];
+          fp8x16_to_bf16(wv[s], wb);
+          part = dot16(wb, hl + ho + e, part);
+        } else {
+          Raw8<bf16_t> w8;
+          w8.u = wv[s];
+          part = dot8(w8, *reinterpret_cast<const X8<bf16_t>*>(hl + ho + e), part);
+        }
       }
       // a weight of 0 for the other tokens rather than a branch per token
-      // keeps acc in registers
+      // keeps acc in registers; FP8 rows carry their column's scale
       const int tk = uni(it.tok[j]);
-      const float wt = uni(it.wt[j]);
+      const float wt = FP8 ? uni(it.wt[j]) * scl : uni(it.wt[j]);
 #pragma unroll
       for (int t = 0; t < kTokInline; ++t) acc[t] = fmaf(tk == t ? wt : 0.f, part, acc[t]);
     }
@@ -2321,7 +2366,7 @@ __device__ __forceinline__ void dc_consume(const DcItem* items, int i, int ib, i
 
 // Groups [ib, ie) of one family (rows of at most NS steps), D groups of loads
 // ahead of the one being used.
-template <int NS>
+template <int NS, bool FP8>
 __device__ __forceinline__ void dc_family(const DcItem* items, int ib, int ie, int c,
                                           const bf16_t* hl, int lane, float (&acc)[kTokInline]) {
   constexpr int D = kDcLoads / NS > 0 ? kDcLoads / NS : 1;
@@ -2329,15 +2374,19 @@ __device__ __forceinline__ void dc_family(const DcItem* items, int ib, int ie, i
   // loads ahead of the loop, the buffers need no copies on entry, and each
   // use waits only for its own group's loads.
   u32x4_t buf[D][NS];
+  float scl[D];
+#pragma unroll
+  for (int q = 0; q < D; ++q) scl[q] = 1.f;
   for (int i0 = ib - D; i0 < ie; i0 += D) {
 #pragma unroll
     for (int q = 0; q < D; ++q) {
-      dc_consume<NS>(items, i0 + q, ib, ie, hl, lane, buf[q], acc);
-      dc_load<NS>(items, i0 + q + D, ie, c, lane, buf[q]);
+      dc_consume<NS, FP8>(items, i0 + q, ib, ie, hl, lane, buf[q], scl[q], acc);
+      dc_load<NS, FP8>(items, i0 + q + D, ie, c, lane, buf[q], scl[q]);
     }
   }
 }
 
+template <bool FP8>
 __global__ __launch_bounds__(kDcWaves * kWave) void down_combine_kernel(DownCombineArgs a,
                                                                      bf16_t* __restrict__ y) {
   extern __shared__ __align__(16) unsigned char dc_lds[];
@@ -2385,9 +2434,10 @@ __global__ __launch_bounds__(kDcWaves * kWave) void down_combine_kernel(DownComb
           n = min(min(T, kTokInline), nh);  // the shared expert: row t is token t
         }
         DcItem it;
-        it.w = static_cast<const bf16_t*>(F.down) + (size_t)mat * ms;
+        it.w = static_cast<const char*>(F.down) + (size_t)mat * ms * (FP8 ? 1 : 2);
+        it.scale = FP8 ? F.down_scale + (size_t)mat * d : nullptr;
         it.rows = F.rows;
-        it.nsteps = (F.rows + STEP - 1) / STEP;
+        it.nsteps = (F.rows + dc_epl<FP8>() * kWave - 1) / (dc_epl<FP8>() * kWave);
         it.n = n;
 #pragma unroll
         for (int j = 0; j < kTokInline; ++j) {
@@ -2419,15 +2469,16 @@ __global__ __launch_bounds__(kDcWaves * kWave) void down_combine_kernel(DownComb
 #pragma unroll
   for (int fi = 0; fi < kDcFamilies; ++fi) {
     if (fi < a.nf && fb[fi] < fb[fi + 1]) {
-      const int ns = (a.f[fi].rows + STEP - 1) / STEP;
+      constexpr int SE = dc_epl<FP8>() * kWave;  // elements per step
+      const int ns = (a.f[fi].rows + SE - 1) / SE;
       if (ns <= 1)
-        dc_family<1>(items, fb[fi], fb[fi + 1], c, hl, lane, acc);
-      else if (ns == 2)
-        dc_family<2>(items, fb[fi], fb[fi + 1], c, hl, lane, acc);
+        dc_family<1, FP8>(items, fb[fi], fb[fi + 1], c, hl, lane, acc);
+      else if (ns == 2 || FP8)
+        dc_family<2, FP8>(items, fb[fi], fb[fi + 1], c, hl, lane, acc);
       else if (ns == 3)
-        dc_family<3>(items, fb[fi], fb[fi + 1], c, hl, lane, acc);
+        dc_family<3, FP8>(items, fb[fi], fb[fi + 1], c, hl, lane, acc);
       else
-        dc_family<kDcMaxSteps>(items, fb[fi], fb[fi + 1], c, hl, lane, acc);
+        dc_family<kDcMaxSteps, FP8>(items, fb[fi], fb[fi + 1], c, hl, lane, acc);
     }
   }
   // lane 16 t holds token t's sum
@@ -2452,32 +2503,6 @@ __global__ __launch_bounds__(kDcWaves * kWave) void down_combine_kernel(DownComb
 // from the cache for each further chunk).
 // ---------------------------------------------------------------------------
 
-// Codes 4q .. 4q+3 of dword q as two bf16 pairs (byte 0 in the low half).
-__device__ __forceinline__ void fp8x16_to_bf16(const u32x4_t& w, uint32_t (&o)[8]) {
-  const uint32_t d4[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    o[2 * q] = __builtin_bit_cast(uint32_t,
-                                  __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d4[q], 1.0f, false));
-    o[2 * q + 1] = __builtin_bit_cast(uint32_t,
-                                      __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d4[q], 1.0f, true));
-  }
-}
-
-// sum over 16 consecutive k of weight (widened codes) * activation, where
-// the activations are 16 bf16 at p (16-byte aligned, LDS)
-__device__ __forceinline__ float dot16(const uint32_t (&wb)[8], const bf16_t* p, float acc) {
-  const u32x4_t a = *reinterpret_cast<const u32x4_t*>(p);
-  const u32x4_t b = *reinterpret_cast<const u32x4_t*>(p + 8);
-  acc = dot2_bf16(wb[0], a.x, acc);
-  acc = dot2_bf16(wb[1], a.y, acc);
-  acc = dot2_bf16(wb[2], a.z, acc);
-  acc = dot2_bf16(wb[3], a.w, acc);
-  acc = dot2_bf16(wb[4], b.x, acc);
-  acc = dot2_bf16(wb[5], b.y, acc);
-  acc = dot2_bf16(wb[6], b.z, acc);
-  return dot2_bf16(wb[7], b.w, acc);
-}
 
 // A buffer resource spanning one FP8 matrix: a load at a byte offset at or
 // past `bytes` returns zeros without a memory access, so a lane past its
@@ -2889,12 +2914,17 @@ hipError_t launch_down_combine(const DownCombineArgs& a, void* y, hipStream_t st
                                const KernelEvents* ev) {
   const dim3 grid((a.d + kDcWaves - 1) / kDcWaves), block(kDcWaves * kWave);
   const size_t lds = down_combine_lds_bytes(a);
-  auto k = down_combine_kernel;
   bf16_t* yo = static_cast<bf16_t*>(y);
-  if (ev)
-    hipExtLaunchKernelGGL(k, grid, block, lds, st, ev->start, ev->stop, 0, a, yo);
+  auto go = [&](auto k) {
+    if (ev)
+      hipExtLaunchKernelGGL(k, grid, block, lds, st, ev->start, ev->stop, 0, a, yo);
+    else
+      hipLaunchKernelGGL(k, grid, block, lds, st, a, yo);
+  };
+  if (a.fp8)
+    go(down_combine_kernel<true>);
   else
-    hipLaunchKernelGGL(k, grid, block, lds, st, a, yo);
+    go(down_combine_kernel<false>);
   return hipGetLastError();
 }
 

@@ -262,7 +262,7 @@ def test_fp8_loaded_weight_bytes_match_the_oracle(lib):
 
 
 def test_layer_kernel_count(lib):
-    """Four launches where the down projection writes y (bf16, T <= 4, rows
+    """Four launches where the down projection writes y (bf16 activations, T <= 4, rows
     of h within the LDS budget), five otherwise, eight in the factorised
     form; 0 at T = 0, -1 for an invalid descriptor or T."""
     q = _desc(max_tokens=16)
@@ -273,7 +273,8 @@ def test_layer_kernel_count(lib):
     assert M.moe_layer_kernel_count(_desc(d_ff=2048, max_tokens=4), 4) == 5
     assert M.moe_layer_kernel_count(_desc(d_ff=2048, max_tokens=4), 1) == 4
     assert M.moe_layer_kernel_count(_desc(dtype="f32"), 1) == 5
-    assert M.moe_layer_kernel_count(_desc(expert_dtype="fp8"), 1) == 5
+    assert M.moe_layer_kernel_count(_desc(expert_dtype="fp8"), 1) == 4
+    assert M.moe_layer_kernel_count(_desc(expert_dtype="fp8", max_tokens=8), 5) == 5
     fac = _desc(n_experts=32, top_k=6, d_ff=256, n_depts=4, d_ff_dept=256,
                 dept_form="factorised")
     assert M.moe_layer_kernel_count(fac, 3) == 8

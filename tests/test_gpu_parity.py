@@ -730,6 +730,61 @@ def test_layer_down_with_combine_epilogue(case, T):
     np.testing.assert_allclose(a, b, rtol=2 ** -7, atol=1e-6 * np.abs(b).max())
 
 
+def _to_fp8(w):
+    """The bf16 expert matrices of `w` as E4M3 codes with per-row scales
+    (torch's float8_e4m3fn rounding of row / (row max / 448))."""
+    out = {"w_router": w["w_router"]}
+    for k, v in w.items():
+        if k == "w_router":
+            continue
+        f = v.float()
+        sc = f.abs().amax(dim=-1).clamp_min(1e-30) / 448.0
+        out[k] = (f / sc[..., None]).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+        out[k + "_scale"] = sc.contiguous()
+    return out
+
+
+@pytest.mark.parametrize("case", [
+    # (d, E, k, I, m, S, Is): FP8 widths are multiples of 16
+    (1040, 6, 3, 48, 0, 0, 32),
+    (528, 12, 6, 64, 3, 208, 0),
+    (272, 5, 2, 2048, 0, 0, 0),
+])
+@pytest.mark.parametrize("T", [1, 3, 4])
+def test_layer_fp8_down_with_combine_epilogue(case, T):
+    """FP8 layers at batches of at most four tokens take the down launch
+    that writes y; against the oracle on the dequantized weights, and
+    against the separate down and combine launches."""
+    d, E, k, I, m, S, Is = case
+    w = _to_fp8(_rand_weights(sum(case) + 7 * T, d, E, I, m, S, Is, torch.bfloat16))
+    g = torch.Generator().manual_seed(T + 100)
+    x = torch.randn(T, d, generator=g).to(torch.bfloat16).to(DEV)
+    desc = M.layer_desc(d, E, k, I, n_depts=m, d_ff_dept=S, d_ff_shared=Is, dtype="bf16",
+                        expert_dtype="fp8", max_tokens=4)
+    assert M.moe_layer_kernel_count(desc, T) == 4
+    y, layer = run_layer(desc, w, x)
+    wc = {kk: v.cpu() for kk, v in w.items()}
+    o_ids, o_w, o_sel, _ = O.route(x.cpu(), wc["w_router"], k)
+    g_ids, _ = gpu_ids_from_plan(layer.plan(T), T, k)
+    ids, _ = reference_ids(o_ids, o_sel, g_ids, k)
+    ref = O.layer_bruteforce(x.cpu(), O.dequantize_layer(wc), ids, o_w, E, m)
+    assert_close(to_np(y), ref, "bf16", f"fp8 fused down+combine {case} T={T}")
+    ws = M.alloc_workspace(desc, DEV)
+    ti = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    tw = torch.empty(T, k, dtype=torch.float32, device=DEV)
+    M.moe_route(desc, x, w["w_router"], None, ti, tw, ws)
+    plan = M.moe_dispatch(desc, ti, tw, ws)
+    row_out = torch.empty(T * k, d, device=DEV)
+    dept_out = torch.empty(T * min(m, k), d, device=DEV) if m else None
+    shared_out = torch.empty(T, d, device=DEV) if Is else None
+    M.moe_expert_ffn(desc, w, x, plan, ws, row_out, dept_out, shared_out)
+    y2 = torch.empty_like(y)
+    M.moe_combine(desc, plan, row_out, dept_out, shared_out, y2)
+    torch.cuda.synchronize()
+    a, b = to_np(y), to_np(y2)
+    np.testing.assert_allclose(a, b, rtol=2 ** -7, atol=1e-6 * np.abs(b).max())
+
+
 def test_layer_zero_tokens_and_errors():
     shape = SH[TINY]
     w = gpu_layer(TINY, 0)
