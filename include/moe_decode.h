@@ -297,7 +297,8 @@ moe_status moe_combine(const moe_layer_desc* desc, const moe_plan* plan,
                        const float* shared_out, int32_t T, void* y, void* stream);
 
 /* The whole decode step: route -> top-k + dispatch -> grouped gate/up ->
- * grouped down -> combine, y[T][d] in act_dtype (five kernels on `stream`).
+ * grouped down -> combine, y[T][d] in act_dtype (the kernels on `stream` that
+ * moe_layer_kernel_count reports: the down launch writes y itself at T <= 4).
  * `stage_events`: see MOE_N_STAGES above (NULL = no timing). */
 moe_status moe_layer_decode(const moe_layer_desc* desc, const moe_weights* weights,
                             const void* x, int32_t T, void* y, void* workspace,
