@@ -53,23 +53,75 @@ __device__ __forceinline__ void load8_stream(const bf16_t* p, float (&v)[8]) {
   v[4] = bf16_lo(a.z); v[5] = bf16_hi(a.z); v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
 }
 
+// Cross-lane moves by DPP (a modifier of the VALU operand, no round trip
+// through the LDS crossbar as with ds_bpermute) inside 16-lane rows.
+// Controls: quad_perm [1,0,3,2] and [2,3,0,1] (lane xor 1, xor 2), the
+// half-row mirror (lane i <-> 7 - i in each 8 lanes), the row mirror (lane i
+// <-> 15 - i in each 16), and row shifts right by 1, 2, 4, 8 (lanes without a
+// source read 0).
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppRowMirror = 0x140;
+constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;
+// Across rows: lane 15 of each row to the next row, and lane 31 to rows 2
+// and 3; rows left out by the row mask keep their value.
+constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(dpp<CTRL>(__float_as_int(v)));
+}
+
+// Reduction of each 16-lane row, the result in every lane of the row:
+// pairs of lanes, then quads, then the two halves of each 8 (mirror), then
+// the two halves of the row (mirror).  OP(a, b) must be commutative.
+template <typename V, typename Op>
+__device__ __forceinline__ V row16_reduce(V v, Op op) {
+  v = op(v, dpp<kDppXor1>(v));
+  v = op(v, dpp<kDppXor2>(v));
+  v = op(v, dpp<kDppHalfMirror>(v));
+  return op(v, dpp<kDppRowMirror>(v));
+}
+
+// Whole-wave reductions (wave-uniform result): each row reduced by row16_reduce,
+// then row 1 takes row 0 and row 3 takes row 2 (lane 15 / 47 broadcast), and
+// row 3 takes row 1 (lane 31): lane 63 holds (r3 + r2) + (r1 + r0) in a fixed
+// order, read once into a scalar.  All on the vector unit but the final read.
+template <typename Op>
+__device__ __forceinline__ int wave_reduce_i(int v, Op op) {
+  v = row16_reduce(v, op);
+  v = op(v, __builtin_amdgcn_update_dpp(v, v, kDppBcast15, 0xA, 0xF, false));
+  v = op(v, __builtin_amdgcn_update_dpp(v, v, kDppBcast31, 0xC, 0xF, false));
+  return __builtin_amdgcn_readlane(v, 63);
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return __int_as_float(wave_reduce_i(__float_as_int(v), [](int a, int b) {
+    return __float_as_int(__int_as_float(a) + __int_as_float(b));
+  }));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  return __int_as_float(wave_reduce_i(__float_as_int(v), [](int a, int b) {
+    return __float_as_int(fmaxf(__int_as_float(a), __int_as_float(b)));
+  }));
 }
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const uint32_t u = (uint32_t)__shfl_xor((int)v, o, kWave);
-    v = u > v ? u : v;
-  }
-  return v;
+  return (uint32_t)wave_reduce_i((int)v, [](int a, int b) {
+    return (uint32_t)a > (uint32_t)b ? a : b;
+  });
+}
+
+// Inclusive prefix sum over the wave's lanes: a scan inside each 16-lane row
+// by DPP row shifts, then each row adds the totals of the rows before it.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+  v += dpp<kDppShr1>(v);
+  v += dpp<kDppShr2>(v);
+  v += dpp<kDppShr4>(v);
+  v += dpp<kDppShr8>(v);
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+            r2 = __builtin_amdgcn_readlane(v, 47);
+  const int q = lane >> 4;
+  return v + (q >= 1 ? r0 : 0) + (q >= 2 ? r1 : 0) + (q >= 3 ? r2 : 0);
 }
 
 template <int N> struct Log2 { static constexpr int value = 1 + Log2<N / 2>::value; };

@@ -114,14 +114,6 @@ __device__ __forceinline__ u32x4_t ld16_stream(const bf16_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
 }
 
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(v, o, kWave);
-    if (lane >= o) v += u;
-  }
-  return v;
-}
 
 // Reduce N per-lane values over the L lanes of an aligned lane group (lanes
 // differing only in bits below log2 L).  Upper lanes keep the upper half at
@@ -160,6 +152,11 @@ __device__ __forceinline__ void group_reduce_scatter(float (&v)[N], int lane) {
 constexpr int kTopkBuf = 10240;   // staged (token, expert) entries per chunk
 constexpr int kCand = 128;        // compacted candidates per token
 constexpr int kPlanWaves = kPlanThreads / kWave;
+constexpr int kRankMaskWords = 1024;
+__device__ __forceinline__ int rank_mask_words(int T, int E) {
+  const int nwt = (T + 63) >> 6;
+  return nwt * E <= kRankMaskWords ? nwt : 0;
+}
 struct TopkStage {
   float lg[kTopkBuf];
   uint32_t key[kTopkBuf];
@@ -181,6 +178,11 @@ struct PlanShared {
   float w[MOE_MAX_ASSIGNMENTS];           // their weights
   int cnt[MOE_MAX_EXPERTS];               // assignments per expert
   unsigned char flag[MOE_MAX_DEPT_PAIRS]; // (t, J): token t chose an expert of department J
+  // Tokens of each expert as bits (word e * ceil(T / 64) + t / 64, bit t % 64)
+  // when E * ceil(T / 64) words fit: an assignment's rank among its expert's
+  // rows is then a popcount of the lower tokens instead of a scan of the
+  // earlier assignments.
+  unsigned long long tmask[kRankMaskWords];
   union {
     TopkStage tk;
     PlanWork pw;
@@ -288,15 +290,12 @@ __device__ void stage_scores(const RouteArgs& p, int t0, int tc, PlanShared& s) 
     stage_scores_ks<1>(p, t0, tc, s);
 }
 
-// Radix select of the k largest of NP planes of keys (entry i of lane l has
-// key key[i] and expert eid(i, l); planes and lanes in ascending expert
-// order): 32 ballot rounds find the k-th largest key, and among entries tied
-// at it the lowest experts are taken.  The k chosen are compacted in expert
-// order into the wave's list (ck, ce); lane j < k then ranks entry j by
-// (key desc, expert asc) against the other k - 1 and sets slot_id[rank].
-template <int NP, typename EidOf>
-__device__ __forceinline__ void select_rank(const uint32_t (&key)[NP], EidOf eid, int k, int lane,
-                                            uint32_t* ck, int* ce, int* slot_id) {
+// The k-th largest key of the wave (NP keys per lane; key 0 lies below every
+// real key; k >= 1 and at most the number of keys): the largest value whose
+// count of keys at or above it is at least k, built one bit at a time from
+// the top.
+template <int NP>
+__device__ __forceinline__ uint32_t kth_largest_key(const uint32_t (&key)[NP], int k) {
   uint32_t thr = 0u;
   for (int b = 31; b >= 0; --b) {
     const uint32_t c = thr | (1u << b);
@@ -305,6 +304,19 @@ __device__ __forceinline__ void select_rank(const uint32_t (&key)[NP], EidOf eid
     for (int i = 0; i < NP; ++i) n += wave_count(key[i] >= c);
     if (n >= k) thr = c;
   }
+  return thr;
+}
+
+// Radix select of the k largest of NP planes of keys (entry i of lane l has
+// key key[i] and expert eid(i, l); planes and lanes in ascending expert
+// order): a radix select finds the k-th largest key, and among entries tied
+// at it the lowest experts are taken.  The k chosen are compacted in expert
+// order into the wave's list (ck, ce); lane j < k then ranks entry j by
+// (key desc, expert asc) against the other k - 1 and sets slot_id[rank].
+template <int NP, typename EidOf>
+__device__ __forceinline__ void select_rank(const uint32_t (&key)[NP], EidOf eid, int k, int lane,
+                                            uint32_t* ck, int* ce, int* slot_id) {
+  const uint32_t thr = kth_largest_key<NP>(key, k);
   int above = 0;
 #pragma unroll
   for (int i = 0; i < NP; ++i) above += wave_count(key[i] > thr);
@@ -335,6 +347,49 @@ __device__ __forceinline__ void select_rank(const uint32_t (&key)[NP], EidOf eid
     rank += (k2 > kj || (k2 == kj && e2 < ej)) ? 1 : 0;
   }
   if (lane < k) slot_id[rank] = ej;
+}
+
+// The k largest of NP planes of keys (entry i of lane l is expert l + 64 i),
+// taken one at a time in rank order: round r finds the wave's largest
+// remaining key (lowest expert among equal keys) and sets slot_id[r].  Every
+// round is a wave maximum by row moves plus one ballot per plane, so for
+// small k this is much shorter than a bitwise radix select followed by a
+// ranking pass.  Taken entries drop to key 0 and stay out of later ties
+// through the per-plane taken masks.
+constexpr int kExtractMaxK = 16;
+template <int NP>
+__device__ __forceinline__ void select_extract(uint32_t (&key)[NP], int k, int lane,
+                                               int* slot_id) {
+  uint64_t taken[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) taken[i] = 0ull;
+  int my_id = 0;
+  for (int r = 0; r < k; ++r) {
+    uint32_t lb = key[0];
+#pragma unroll
+    for (int i = 1; i < NP; ++i) lb = key[i] > lb ? key[i] : lb;
+    const uint32_t M = wave_max_u32(lb);
+    int pi = -1, pl = 0;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const uint64_t eq = __ballot(key[i] == M) & ~taken[i];
+      if (pi < 0 && eq != 0ull) {
+        pi = i;
+        pl = __builtin_ctzll(eq);
+      }
+    }
+    pi = __builtin_amdgcn_readfirstlane(pi);
+    pl = __builtin_amdgcn_readfirstlane(pl);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      if (i == pi) {
+        taken[i] |= 1ull << pl;
+        key[i] = lane == pl ? 0u : key[i];
+      }
+    }
+    my_id = lane == r ? pl + kWave * pi : my_id;
+  }
+  if (lane < k) slot_id[lane] = my_id;
 }
 
 // Top-k of token t by one wave from the staged row `row` (lane l holds experts
@@ -385,11 +440,8 @@ __device__ void topk_token(const RouteArgs& p, int t, int row, int lane, PlanSha
       dkey = (uint32_t)__shfl((int)v, min(lane, p.m - 1) * L, kWave);
       dkey = lane < p.m ? dkey : 0u;
     }
-    uint32_t dthr = 0u;
-    for (int b = 31; b >= 0; --b) {
-      const uint32_t c = dthr | (1u << b);
-      if (wave_count(dkey >= c) >= kd) dthr = c;
-    }
+    const uint32_t dkeys[1] = {dkey};
+    const uint32_t dthr = kth_largest_key<1>(dkeys, kd);
     const int dabove = wave_count(dkey > dthr);
     const uint64_t deq = __ballot(lane < p.m && dkey == dthr);
     const bool dtake = lane < p.m && (dkey > dthr ||
@@ -408,14 +460,10 @@ __device__ void topk_token(const RouteArgs& p, int t, int row, int lane, PlanSha
   int n_cand = 0;
   uint32_t cut = 1u;
   if constexpr (NPL >= 8) {
-    uint32_t lmax = 0u;
+    uint32_t lmax[1] = {0u};
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) lmax = key[i] > lmax ? key[i] : lmax;
-    uint32_t c0 = 0u;
-    for (int b = 31; b >= 0; --b) {
-      const uint32_t c = c0 | (1u << b);
-      if (wave_count(lmax >= c) >= k) c0 = c;
-    }
+    for (int i = 0; i < NPL; ++i) lmax[0] = key[i] > lmax[0] ? key[i] : lmax[0];
+    const uint32_t c0 = kth_largest_key<1>(lmax, k);
     cut = c0 > 1u ? c0 : 1u;
 #pragma unroll
     for (int i = 0; i < NPL; ++i) n_cand += wave_count(key[i] >= cut);
@@ -453,6 +501,8 @@ __device__ void topk_token(const RouteArgs& p, int t, int row, int lane, PlanSha
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
     select_rank<NC>(ckey, [&](int i, int) { return cexp[i]; }, k, lane, ck, ce, slot_id);
+  } else if (NPL <= 4 && k <= kExtractMaxK) {
+    select_extract<NPL>(key, k, lane, slot_id);
   } else {
     select_rank<NPL>(key, [](int i, int l) { return l + kWave * i; }, k, lane,
                      s.tk.cand_key[wid], s.tk.cand_e[wid], slot_id);
@@ -561,6 +611,8 @@ __device__ void topk_token(const RouteArgs& p, int t, int row, int lane, PlanSha
     s.w[a] = w;
     // the plan's tallies (the k experts of a token are distinct)
     atomicAdd(&s.cnt[my_id], 1);
+    const int nwt = rank_mask_words(p.T, E);
+    if (nwt > 0) atomicOr(&s.tmask[my_id * nwt + (t >> 6)], 1ull << (t & 63));
     if (p.m > 0) s.flag[t * p.m + my_id / (E / p.m)] = 1;
   }
 }
@@ -623,9 +675,10 @@ __device__ void dept_scan(PlanShared& s, const PlanArgs& pa, int lane) {
 // wave scans, wave totals through LDS) while the last wave scans the
 // departments; then every assignment and every pair writes its row.  Waves
 // with no entries stay out of the scan: cross-lane steps of idle waves would
-// only queue on the LDS crossbar.
+// only queue on the LDS crossbar.  `masks`: s.tmask holds the token bits of
+// every expert (the top-k filled it; its k experts per token are distinct).
 constexpr int kScanWaves = 4;
-__device__ void plan_phase(PlanShared& s, const PlanArgs& pa) {
+__device__ void plan_phase(PlanShared& s, const PlanArgs& pa, bool masks) {
   const int tid = threadIdx.x, nth = blockDim.x, lane = tid & 63, wid = tid >> 6;
   const int nw = nth >> 6;
   const int T = pa.T, k = pa.k, E = pa.E, A = T * k, m = pa.m;
@@ -702,13 +755,21 @@ __device__ void plan_phase(PlanShared& s, const PlanArgs& pa) {
   // in the factorised form a row's inputs are its (token, department) pair's
   // backbone outputs, so the pair index goes to row_pair and to the inline
   // entries of small groups
+  const int nwt = masks ? rank_mask_words(T, E) : 0;
   for (int a = tid; a < A; a += nth) {
     const int e = s.ids[a];
     if (e >= 0 && e < E) {
-      int rank = 0;
-      for (int b2 = 0; b2 < a; ++b2) rank += (s.ids[b2] == e) ? 1 : 0;
-      const int row = s.pw.off[e] + rank;
       const int t = a / k;
+      int rank = 0;
+      if (nwt > 0) {
+        // the earlier assignments to e are those of the lower tokens that chose it
+        const unsigned long long* mw = s.tmask + e * nwt;
+        for (int q = 0; q < (t >> 6); ++q) rank += __popcll(mw[q]);
+        rank += __popcll(mw[t >> 6] & ((1ull << (t & 63)) - 1ull));
+      } else {
+        for (int b2 = 0; b2 < a; ++b2) rank += (s.ids[b2] == e) ? 1 : 0;
+      }
+      const int row = s.pw.off[e] + rank;
       P.row_token[row] = t;
       P.row_slot[row] = a - t * k;
       P.row_expert[row] = e;
@@ -752,9 +813,92 @@ __device__ void plan_phase(PlanShared& s, const PlanArgs& pa) {
   }
 }
 
+// The plan by one wave, for layers with no departments, at most 4 * 64
+// experts and the token bits of every expert in s.tmask: lane l takes the
+// experts [l * per, (l + 1) * per), one wave scan of the counts gives their
+// first rows and list slots, and the same wave then writes every
+// assignment's row.  The lanes exchange offsets and slots through LDS inside
+// the wave: no block barrier anywhere.
+constexpr int kWavePlanPer = 4;  // experts per lane at most
+__device__ void plan_phase_wave(PlanShared& s, const PlanArgs& pa, int lane) {
+  const int T = pa.T, k = pa.k, E = pa.E, A = T * k;
+  const moe_plan& P = pa.plan;
+  const int per = (E + kWave - 1) / kWave;
+  const int b = min(E, lane * per), en = min(E, b + per);
+  int c[kWavePlanPer];
+  int sc = 0, sa = 0, ss = 0;
+#pragma unroll
+  for (int j = 0; j < kWavePlanPer; ++j) {
+    c[j] = b + j < en ? s.cnt[b + j] : 0;
+    sc += c[j];
+    sa += c[j] > 0 ? 1 : 0;
+    ss += (c[j] > 0 && c[j] <= kTokInline) ? 1 : 0;
+  }
+  const int ic = wave_incl_scan(sc, lane), ia = wave_incl_scan(sa, lane),
+            is = wave_incl_scan(ss, lane);
+  int rc = ic - sc, ra = ia - sa, rs = is - ss;
+  int rl = ra - rs;  // large groups before mine: active minus small
+#pragma unroll
+  for (int j = 0; j < kWavePlanPer; ++j) {
+    const int e = b + j;
+    if (e < en) {
+      s.pw.off[e] = rc;
+      P.offsets[e] = rc;
+      P.counts[e] = c[j];
+      if (c[j] > 0) {
+        P.active[ra++] = e;
+        const int sl = c[j] <= kTokInline ? rs++ : rl++;
+        s.pw.slot[e] = sl;
+        WorkDesc* wd = work_of(pa.work, E, c[j], sl);
+        wd->mat = e;
+        wd->r0 = rc;
+        wd->n = c[j];
+      }
+      rc += c[j];
+    }
+  }
+  if (lane == kWave - 1) {
+    P.offsets[E] = ic;
+    P.header[MOE_PLAN_N_ROWS] = ic;
+    P.header[MOE_PLAN_N_ACTIVE] = ia;
+    P.header[kHdrSmall] = is;
+    P.header[kHdrLarge] = ia - is;
+    P.header[MOE_PLAN_N_INVALID] = s.invalid;
+    P.header[MOE_PLAN_N_DEPT_ROWS] = 0;
+    P.header[MOE_PLAN_N_ACTIVE_DEPTS] = 0;
+    P.header[kHdrDeptSmall] = 0;
+    P.header[kHdrDeptLarge] = 0;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  const int nwt = rank_mask_words(T, E);
+  for (int a = lane; a < A; a += kWave) {
+    const int e = s.ids[a];
+    if (e >= 0 && e < E) {
+      const int t = a / k;
+      // the earlier assignments to e are those of the lower tokens that chose it
+      const unsigned long long* mw = s.tmask + e * nwt;
+      int rank = 0;
+      for (int q = 0; q < (t >> 6); ++q) rank += __popcll(mw[q]);
+      rank += __popcll(mw[t >> 6] & ((1ull << (t & 63)) - 1ull));
+      const int row = s.pw.off[e] + rank;
+      P.row_token[row] = t;
+      P.row_slot[row] = a - t * k;
+      P.row_expert[row] = e;
+      P.row_weight[row] = s.w[a];
+      P.inv_perm[a] = row;
+      if (s.cnt[e] <= kTokInline) pa.work[s.pw.slot[e]].tok[rank] = t;
+    } else {
+      P.inv_perm[a] = -1;
+    }
+  }
+}
+
 // Per-launch clearing of the plan's LDS tallies (before any top-k or count).
 __device__ __forceinline__ void plan_clear(PlanShared& s, int T, int E, int m) {
   for (int e = threadIdx.x; e < E; e += blockDim.x) s.cnt[e] = 0;
+  const int nm = rank_mask_words(T, E) * E;
+  for (int i = threadIdx.x; i < nm; i += blockDim.x) s.tmask[i] = 0ull;
   for (int p = threadIdx.x; p < T * (m > 0 ? m : 0); p += blockDim.x) s.flag[p] = 0;
   if (threadIdx.x == 0) s.invalid = 0;
 }
@@ -935,7 +1079,11 @@ __global__ __launch_bounds__(kPlanThreads) void topk_plan_kernel(RouteArgs ra, P
   }
   if (!do_plan) return;
   __syncthreads();
-  plan_phase(s, pa);
+  if (pa.m <= 0 && pa.E <= kWavePlanPer * kWave && rank_mask_words(pa.T, pa.E) > 0) {
+    if (wid == 0) plan_phase_wave(s, pa, lane);
+  } else {
+    plan_phase(s, pa, true);
+  }
 }
 
 __global__ __launch_bounds__(kPlanThreads) void dispatch_kernel(const int32_t* ids, const float* w,
@@ -956,7 +1104,7 @@ __global__ __launch_bounds__(kPlanThreads) void dispatch_kernel(const int32_t* i
     }
   }
   __syncthreads();
-  plan_phase(s, pa);
+  plan_phase(s, pa, false);  // given ids may repeat an expert within a token
 }
 
 // ---------------------------------------------------------------------------
