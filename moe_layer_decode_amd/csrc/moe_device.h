@@ -127,33 +127,82 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 template <int N> struct Log2 { static constexpr int value = 1 + Log2<N / 2>::value; };
 template <> struct Log2<1> { static constexpr int value = 0; };
 
-// Reduce N per-lane values (N a power of two, <= 64) over the 64 lanes of a
-// wave.  Each butterfly step halves the live values, so the whole reduction
-// costs N - 1 + (6 - log2 N) shuffles instead of 6 N.  On return lane l holds
-// the full sum of value index (l >> (6 - log2 N)) & (N - 1); the top index bit
-// always sits in lane bit 5.
+// The value of lane l ^ 32 (the other half of the wave), by the gfx950
+// half swap: swapping the upper half of a copy with the lower half of
+// another leaves each lane's partner value in one of the two.
+__device__ __forceinline__ float xor32(float v, int lane) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(lane < 32 ? r[1] : r[0]);
+}
+
+// a + (the same value of the partner lane) for one butterfly step across lane
+// bit 5 or 4, from one gfx950 half / row swap: swapping the upper halves of a
+// with the lower halves of b gives, in every lane, the sum of the pair it
+// keeps (lower lanes a + partner's a, upper lanes b + partner's b).
+template <int O>
+__device__ __forceinline__ float swap_pair_sum(float a, float b) {
+  const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+  if constexpr (O == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(ua, ub, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    static_assert(O == 16, "row swaps pair lanes 16 or 32 apart");
+    const auto r = __builtin_amdgcn_permlane16_swap(ua, ub, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+}
+
+// DPP control of a butterfly partner across lane bit log2(O), O <= 8: a
+// permutation inside the 16-lane row that flips that bit (and possibly lower
+// ones) and keeps every higher bit, which is all a reduce-scatter step needs.
+template <int O>
+constexpr int butterfly_dpp() {
+  return O == 8 ? kDppRowMirror : O == 4 ? kDppHalfMirror : O == 2 ? kDppXor2 : kDppXor1;
+}
+
+// Reduce N per-lane values over the L lanes of an aligned lane group (lanes
+// differing only in bits below log2 L; L a power of two, 2 .. 64).  Butterfly
+// steps from lane bit log2(L) - 1 down to bit 0; at each step a lane keeps the
+// half of its live values that its bit selects (upper lanes the upper half)
+// and adds its partner's copy of that half, so each step halves the live
+// values.  Afterwards lane j of the group holds, in v[0 .. max(N/L, 1)), the
+// sums of value indices (N/L) * j + i when N >= L, or of index j / (L/N) when
+// N < L.  Partners across bits 5 and 4 come from the gfx950 half / row swaps,
+// the others from DPP row permutations: no LDS traffic.
+template <int N, int L>
+__device__ __forceinline__ void group_reduce_scatter(float (&v)[N], int lane) {
+  static_assert(L >= 2 && L <= 64 && (L & (L - 1)) == 0, "L must be a power of two <= 64");
+  int n = N;
+#pragma unroll
+  for (int o = L / 2; o >= 1; o >>= 1) {
+    const int half = n > 1 ? n >> 1 : 1;
+#pragma unroll
+    for (int i = 0; i < (N > 1 ? N / 2 : 1); ++i) {
+      if (i < half) {
+        const float lo = v[i], hi = n > 1 ? v[i + half] : v[i];
+        if (o >= 16) {
+          v[i] = o == 32 ? swap_pair_sum<32>(lo, hi) : swap_pair_sum<16>(lo, hi);
+        } else {
+          const bool upper = (lane & o) != 0;
+          const float send = upper ? lo : hi, keep = upper ? hi : lo;
+          v[i] = keep + (o == 8 ? dpp<butterfly_dpp<8>()>(send)
+                         : o == 4 ? dpp<butterfly_dpp<4>()>(send)
+                         : o == 2 ? dpp<butterfly_dpp<2>()>(send)
+                                  : dpp<butterfly_dpp<1>()>(send));
+        }
+      }
+    }
+    n = half;
+  }
+}
+
+// group_reduce_scatter over the whole wave: lane l holds the full sum of value
+// index (l >> (6 - log2 N)) & (N - 1); the top index bit sits in lane bit 5.
 template <int N>
 __device__ __forceinline__ float wave_reduce_scatter(float (&v)[N], int lane) {
   static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "N must be a power of two <= 64");
-  int n = N;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    if (n > 1) {
-      const int half = n >> 1;
-      const bool upper = (lane & o) != 0;
-#pragma unroll
-      for (int i = 0; i < N / 2; ++i) {
-        if (i < half) {
-          const float send = upper ? v[i] : v[i + half];
-          const float keep = upper ? v[i + half] : v[i];
-          v[i] = keep + __shfl_xor(send, o, kWave);
-        }
-      }
-      n = half;
-    } else {
-      v[0] += __shfl_xor(v[0], o, kWave);
-    }
-  }
+  group_reduce_scatter<N, 64>(v, lane);
   return v[0];
 }
 

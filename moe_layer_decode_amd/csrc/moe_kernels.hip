@@ -115,34 +115,6 @@ __device__ __forceinline__ u32x4_t ld16_stream(const bf16_t* p) {
 }
 
 
-// Reduce N per-lane values over the L lanes of an aligned lane group (lanes
-// differing only in bits below log2 L).  Upper lanes keep the upper half at
-// each halving step, so afterwards lane j of the group holds, in
-// v[0 .. max(N/L, 1)), the sums of value indices (N/L) * j + i when N >= L,
-// or of index j / (L/N) when N < L.
-template <int N, int L>
-__device__ __forceinline__ void group_reduce_scatter(float (&v)[N], int lane) {
-  int n = N;
-#pragma unroll
-  for (int o = L / 2; o >= 1; o >>= 1) {
-    if (n > 1) {
-      const int half = n >> 1;
-      const bool upper = (lane & o) != 0;
-#pragma unroll
-      for (int i = 0; i < N / 2; ++i) {
-        if (i < half) {
-          const float send = upper ? v[i] : v[i + half];
-          const float keep = upper ? v[i + half] : v[i];
-          v[i] = keep + __shfl_xor(send, o, kWave);
-        }
-      }
-      n = half;
-    } else {
-      v[0] += __shfl_xor(v[0], o, kWave);
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Routing + plan
 // ---------------------------------------------------------------------------
@@ -1342,7 +1314,7 @@ __device__ __forceinline__ void gu_small(const T_* __restrict__ Wg, const T_* __
     }
   group_reduce_scatter<N, 64>(v, lane);
   // gate index idx and up index idx + N/2 sit in lanes l and l ^ 32
-  const float upv = __shfl_xor(v[0], 32, kWave);
+  const float upv = xor32(v[0], lane);
   constexpr int SH = 6 - Log2<N>::value;
   const int idx = lane >> SH;
   if (idx < N / 2 && (lane & ((1 << SH) - 1)) == 0) {
@@ -1567,7 +1539,7 @@ __device__ __forceinline__ void gu_small_lds(const T_* __restrict__ Wg, const T_
   }
   group_reduce_scatter<N, 64>(v, lane);
   // gate index t and up index t + NT sit in lanes l and l ^ 32
-  const float upv = __shfl_xor(v[0], 32, kWave);
+  const float upv = xor32(v[0], lane);
   constexpr int SH = 6 - Log2<N>::value;
   const int t = lane >> SH;
   if (t < NT && (lane & ((1 << SH) - 1)) == 0 && t < nv && i0 < rows)
@@ -2112,7 +2084,7 @@ __device__ void gu_plain(const float* __restrict__ Wg, const float* __restrict__
       v[RW * NT + r * NT + t] = au[r][t];
     }
   group_reduce_scatter<N, 64>(v, lane);
-  const float upv = __shfl_xor(v[0], 32, kWave);
+  const float upv = xor32(v[0], lane);
   constexpr int SH = 6 - Log2<N>::value;
   const int idx = lane >> SH;
   if (idx < N / 2 && (lane & ((1 << SH) - 1)) == 0) {
@@ -2758,7 +2730,7 @@ __device__ __forceinline__ void gu_fp8(const Family& F, const Slot& sl, const bf
       }
       group_reduce_scatter<N, 64>(v, lane);
       res[k] = v[0];
-      resu[k] = __shfl_xor(v[0], 32, kWave);  // gate index t and up index t + NT: lanes l, l ^ 32
+      resu[k] = xor32(v[0], lane);  // gate index t and up index t + NT: lanes l, l ^ 32
     }
     constexpr int SH = 6 - Log2<2 * NT>::value;
     const int t = lane >> SH;
