@@ -440,12 +440,19 @@ FamilySet make_families(const moe_layer_desc& d, const moe_weights& w, const moe
 // Tiles per slot and the block prefix for one launch: small parts tile by the
 // GEMV configuration; large parts of bf16 layers by one 64-row (gate/up) or
 // 64-column (down) matrix-core tile per block (each wave 16 of them over the
-// whole K), of fp32 layers by 16 rows or columns.
-void set_tiles(FamilySet& set, int d, bool gateup, int w_dtype, const moe::GemvConfig& c) {
+// whole K) -- gate/up at T <= kSplitKMaxT, where no group passes 16 rows, and
+// d <= kSplitKMaxD by one 16-row tile whose K the four waves split (four times
+// the blocks for the few large groups of a decode batch; measured faster there
+// for gate/up, slower for down and at d = 7168) --, of fp32 layers by 16 rows
+// or columns.
+void set_tiles(FamilySet& set, int d, bool gateup, int w_dtype, const moe::GemvConfig& c,
+               int T) {
   set.blk_start[0] = 0;
-  const int lt = w_dtype == MOE_BF16 ? moe::kWideRows : 16;
   for (int i = 0; i < set.n; ++i) {
     Family& f = set.f[i];
+    f.splitk = w_dtype == MOE_BF16 && f.large && gateup && T <= moe::kSplitKMaxT &&
+               d <= moe::kSplitKMaxD;
+    const int lt = w_dtype == MOE_BF16 && !f.splitk ? moe::kWideRows : 16;
     if (f.large)
       f.tiles = ceil_div(gateup ? f.rows : d, lt);
     else
@@ -516,12 +523,12 @@ moe_status run_experts(const moe_layer_desc& d, const moe_weights& w, const void
   }
   if (!factorised(d)) {
     FamilySet set = make_families(d, w, p, ws, T, row_out, dept_out, shared_out);
-    set_tiles(set, dm, true, d.w_dtype, cfg);
+    set_tiles(set, dm, true, d.w_dtype, cfg, T);
     if (moe::launch_gateup(d.w_dtype, set, x, T, dm, cfg.rows_per_wave, cfg.rows_per_pass, st,
                            ev_gu) != hipSuccess)
       return MOE_ERR_HIP;
     if (gateup_only) return MOE_OK;
-    set_tiles(set, dm, false, d.w_dtype, cfg);
+    set_tiles(set, dm, false, d.w_dtype, cfg, T);
     return hip_status(
         moe::launch_down(d.w_dtype, set, T, dm, cfg.lpr, cfg.col_groups, st, ev_dn));
   }
@@ -537,18 +544,18 @@ moe_status run_experts(const moe_layer_desc& d, const moe_weights& w, const void
     dn1.stop = ev_dn->stop;
   }
   FamilySet a = make_families(d, w, p, ws, T, row_out, dept_out, shared_out, Stage::kFactBackbone);
-  set_tiles(a, dm, true, d.w_dtype, cfg);
+  set_tiles(a, dm, true, d.w_dtype, cfg, T);
   if (moe::launch_gateup(d.w_dtype, a, x, T, dm, cfg.rows_per_wave, cfg.rows_per_pass, st,
                          ev_gu ? &gu0 : nullptr) != hipSuccess)
     return MOE_ERR_HIP;
   FamilySet b = make_families(d, w, p, ws, T, row_out, dept_out, shared_out, Stage::kFactPrivateUp);
-  set_tiles(b, S, true, d.w_dtype, cfg);
+  set_tiles(b, S, true, d.w_dtype, cfg, T);
   if (moe::launch_gateup(d.w_dtype, b, x, T, S, cfg.rows_per_wave, cfg.rows_per_pass, st,
                          ev_gu ? &gu1 : nullptr) != hipSuccess)
     return MOE_ERR_HIP;
   FamilySet c =
       make_families(d, w, p, ws, T, row_out, dept_out, shared_out, Stage::kFactPrivateDown);
-  set_tiles(c, S, false, d.w_dtype, cfg);
+  set_tiles(c, S, false, d.w_dtype, cfg, T);
   if (moe::launch_down(d.w_dtype, c, T, S, cfg.lpr, cfg.col_groups, st, ev_dn ? &dn0 : nullptr) !=
       hipSuccess)
     return MOE_ERR_HIP;
@@ -570,7 +577,7 @@ moe_status run_experts(const moe_layer_desc& d, const moe_weights& w, const void
       hipSuccess)
     return MOE_ERR_HIP;
   FamilySet e = make_families(d, w, p, ws, T, row_out, dept_out, shared_out, Stage::kFactDeptDown);
-  set_tiles(e, dm, false, d.w_dtype, cfg);
+  set_tiles(e, dm, false, d.w_dtype, cfg, T);
   return hip_status(moe::launch_down(d.w_dtype, e, T, dm, cfg.lpr, cfg.col_groups, st,
                                      ev_dn ? &dn1 : nullptr));
 }

@@ -13,7 +13,9 @@ constexpr int kWaves = 4;            // waves per block of every kernel
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRouteChunk = 512;     // d elements one router wave covers (64 lanes x 8)
 constexpr int kTokInline = 4;        // tokens carried inline in a work descriptor
-constexpr int kWideRows = 64;        // rows / columns of a bf16 large-group tile
+constexpr int kWideRows = 64;        // rows / columns of a bf16 large-group tile (unless split K)
+constexpr int kSplitKMaxT = 16;      // K-split gate/up tiles: T at most (every group <= 16 rows)
+constexpr int kSplitKMaxD = 2048;    //   and d at most
 constexpr int kPlanThreads = 1024;   // threads of the single-block top-k / plan kernel
 constexpr int kMaxRouteSplit = 8;   // partial-logit planes of the bf16 router at most
 constexpr int kMaxParts = 6;         // 3 matrix families x (small groups, large groups)
@@ -82,6 +84,8 @@ struct Family {
   int n_mats;              // matrices in the family (bounds check of work descriptors)
   int max_rows;            // rows h / out hold (bounds check of work descriptors)
   int large;               // 0: groups of <= kTokInline rows; 1: larger groups
+  int splitk;              // large gate/up part of bf16 weights: 16-row K-split tiles
+                           // (groups of at most 16 rows), else 64-row tiles
   const float* gate_scale; // FP8 weights: per-row scales [n_mats][rows] (gate, up)
   const float* up_scale;   //   and [n_mats][d] (down); unused otherwise
   const float* down_scale;

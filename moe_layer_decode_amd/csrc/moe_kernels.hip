@@ -1631,11 +1631,11 @@ __device__ __forceinline__ void dn_small_lds(const T_* __restrict__ Wd, int d, i
 // l%16.  A dot product is indifferent to the order of k, so each lane simply
 // takes the 16-byte chunk at 8g of every 32-element step.
 
-
-// K-split tiles: the four waves of a block share one 16-row (gate/up) or
-// 16-column (down) tile and each streams a quarter of K, two 32-wide steps
-// ahead of the matrix-core work; the four partial tiles are then added in
-// wave order through LDS, so results do not depend on timing.
+// K-split gate/up tiles (decode batches with d <= kSplitKMaxD): the four waves
+// of a block share one 16-row tile and each streams a quarter of K, two
+// 32-wide steps ahead of the matrix-core work, its token inputs read directly
+// (L2); the four partial tiles are then added in wave order through LDS, so
+// results do not depend on timing.
 
 constexpr int kMfmaAhead = 2;  // K-steps requested ahead of the one being used
 
@@ -1647,7 +1647,7 @@ __device__ __forceinline__ void k_quarter(int K, int wid, int& kb, int& ke) {
 }
 
 struct MfmaLds {
-  f32x4_t part[kWaves][2][2][kWave];  // [wave][token chunk][gate/up or down][lane]
+  f32x4_t part[kWaves][2][2][kWave];  // [wave][token chunk][gate / up][lane]
 };
 
 // 16 rows (i0..) of gate and up against 16*NC tokens (rows tc.. of the group).
@@ -1745,74 +1745,18 @@ __device__ void gu_mfma(const bf16_t* __restrict__ Wg, const bf16_t* __restrict_
   __syncthreads();
 }
 
-// 16 output columns (c0..) against 16*NC rows of h (rows tc.. of the group).
-template <int NC>
-__device__ void dn_mfma(const bf16_t* __restrict__ Wd, int d, int rows, int c0,
-                        const bf16_t* __restrict__ h, const Slot& sl, int tc,
-                        float* __restrict__ out, int epi, int lane, int wid, MfmaLds& lds) {
-  const int r16 = lane & 15, g = lane >> 4;
-  int kb, ke;
-  k_quarter(rows, wid, kb, ke);
-  const bf16_t* ap = Wd + (size_t)min(c0 + r16, d - 1) * rows + g * 8;
-  const bf16_t* hp[NC];
-  bool hv[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int t = tc + c * 16 + r16;
-    hv[c] = t < sl.n;
-    hp[c] = h + (size_t)(sl.r0 + (hv[c] ? t : 0)) * rows + g * 8;
-  }
-  f32x4_t acc[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const u32x4_t z = {0, 0, 0, 0};
-  u32x4_t ra[kMfmaAhead + 1], rh[kMfmaAhead + 1][NC];
-#pragma unroll
-  for (int s = 0; s < kMfmaAhead; ++s) {
-    const int k = kb + s * 32;
-    const bool in = k + g * 8 < ke;
-    ra[s] = in ? ld16_stream(ap + k) : z;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) rh[s][c] = (hv[c] && in) ? ld16(hp[c] + k) : z;
-  }
-  for (int k = kb; k < ke; k += 32 * (kMfmaAhead + 1)) {
-#pragma unroll
-    for (int s = 0; s <= kMfmaAhead; ++s) {
-      const int kn = k + (s + kMfmaAhead) * 32;
-      const int sn = (s + kMfmaAhead) % (kMfmaAhead + 1);
-      const bool nin = kn + g * 8 < ke;
-      ra[sn] = nin ? ld16_stream(ap + kn) : z;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) rh[sn][c] = (hv[c] && nin) ? ld16(hp[c] + kn) : z;
-      if (k + s * 32 < ke) {
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra[s]), as_bf16x8(rh[s][c]), acc[c], 0, 0, 0);
-      }
-    }
-  }
-#pragma unroll
-  for (int c = 0; c < NC; ++c) lds.part[wid][c][0][lane] = acc[c];
-  __syncthreads();
-  if (wid == 0) {
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      f32x4_t sum = lds.part[0][c][0][lane];
-#pragma unroll
-      for (int w = 1; w < kWaves; ++w) sum += lds.part[w][c][0][lane];
-      const int t = tc + c * 16 + r16;
-      if (t < sl.n) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int col = c0 + 4 * g + i;
-          if (col < d) dn_store(out, (size_t)(sl.r0 + t) * d + col, sum[i], epi);
-        }
-      }
-    }
-  }
-  __syncthreads();
+// Out-of-line entry of the K-split gate/up tile for one 16-token chunk
+// (groups of at most 16 rows), with plain-value arguments like gu_wide_call.
+template <bool DUAL>
+__device__ __attribute__((noinline)) void gu_mfma_call(
+    const bf16_t* __restrict__ Wg, const bf16_t* __restrict__ Wu, int d, int rows, int i0,
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ xu, int in_rows, int r0, int n,
+    const int* grp_token, GuOut<bf16_t> o, int lane, int wid, MfmaLds& lds) {
+  Slot sl{};
+  sl.r0 = r0;
+  sl.n = n;
+  gu_mfma<1, DUAL>(Wg, Wu, d, rows, i0, x, xu, in_rows, sl, grp_token, 0, o, lane, wid, lds);
 }
-
 // ---- large groups, bf16: 64-row tiles with LDS-shared inputs ---------------
 //
 // Four waves, each 16 rows (gate/up) or 16 output columns (down) over the whole
@@ -2154,7 +2098,8 @@ constexpr int down_min_waves() { return sizeof(T_) == 2 ? 7 : 1; }
 // group or the staged activations of a small one (a block is only ever one).
 template <typename T_, bool XL, bool DUAL = false, int NC = kDownNC>
 constexpr size_t expert_lds_bytes() {
-  const size_t a = sizeof(T_) == 2 ? sizeof(WideLds<NC, DUAL ? 2 : 1>) : 0;
+  const size_t w = sizeof(WideLds<NC, DUAL ? 2 : 1>);
+  const size_t a = sizeof(T_) == 2 ? (w > sizeof(MfmaLds) ? w : sizeof(MfmaLds)) : 0;
   const size_t b = XL ? sizeof(SmallLds<T_, DUAL ? 2 * kTokInline : kTokInline>) : 0;
   return a > b ? a : (b > 0 ? b : 16);
 }
@@ -2197,6 +2142,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     return;
   }
   if constexpr (sizeof(T_) == 2) {
+    if (F.splitk) {
+      // at most 16 rows per group: one 16-row K-split tile per block
+      const int i0 = tile * 16;
+      if (i0 < F.rows)
+        gu_mfma_call<DUAL>(Wg, Wu, d, F.rows, i0, xg, xu, F.in_rows, sl.r0, sl.n, F.grp_token, o,
+                           lane, wid, *reinterpret_cast<MfmaLds*>(lds_raw));
+      return;
+    }
     // large groups: the whole block on one 64-row tile, 16*NC tokens a pass
     const int i0 = tile * kWideRows;
     if (i0 >= F.rows) return;
