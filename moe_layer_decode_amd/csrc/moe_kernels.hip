@@ -2339,6 +2339,7 @@ __device__ __forceinline__ float dot16(const uint32_t (&wb)[8], const bf16_t* p,
 // ---------------------------------------------------------------------------
 struct DcItem {
   const void* w;            // the group's matrix [d][rows] (bf16, or FP8 codes)
+  uint32_t woff;            // byte offset of that matrix in the family's weights
   const float* scale;       // FP8: the matrix's per-column scales [d]; else nullptr
   int rows;                 // row length (elements)
   int nsteps;               // steps of 64 lanes x 8 elements per weight row
@@ -2346,6 +2347,8 @@ struct DcItem {
   int hoff[kTokInline];     // LDS element offset of the group's row j of h
   int tok[kTokInline];      // token of row j
   float wt[kTokInline];     // weight of row j (0 past n)
+  int thoff[kTokInline];    // per token t: LDS offset of the group's row of t (any row if none)
+  float twt[kTokInline];    //   and its weight (0 if the group has no row of t)
 };
 
 size_t down_combine_lds_bytes(const DownCombineArgs& a) {
@@ -2378,6 +2381,7 @@ template <bool FP8> constexpr int dc_epl() { return FP8 ? 16 : 8; }
 // before each use instead of only the oldest.
 constexpr int kGfx9BufferDword3 = 0x00020000;  // raw (untyped) 32-bit buffer access
 constexpr int kCpolNt = 2;                     // non-temporal: weights are read once
+constexpr uint32_t kDcOob = 0x80000000u;       // buffer offset past every resource: reads 0
 
 // FP8: also the column's scale (a scalar load, issued as far ahead).
 template <int NS, bool FP8>
@@ -2459,8 +2463,64 @@ __device__ __forceinline__ void dc_family(const DcItem* items, int ib, int ie, i
   }
 }
 
+// Groups [ib, ie) of a bf16 family whose rows are LPI * 8 elements (LPI = 16
+// or 32 lanes): one wave load takes column c's row of 64 / LPI groups at
+// once, lane l serving group i + l / LPI.  The loads go through a buffer
+// resource spanning the family's weights (`wbase`, `wbytes`), so a lane past
+// the last group reads zeros without a memory access; every lane folds its
+// own group's rows of h into the token accumulators (the weight of a lane
+// outside [ib, ie) is 0), and the wave reduction at the end adds the lanes.
+template <int LPI>
+__device__ __forceinline__ void dcp_load(const DcItem* items, int i, int ie, int c, int lane,
+                                         __amdgpu_buffer_rsrc_t rs, int rows, u32x4_t& dst) {
+  const int gi = i + lane / LPI;
+  const uint32_t off = gi < ie ? items[min(gi, ie - 1)].woff + (uint32_t)(c * rows * 2) +
+                                     (uint32_t)((lane % LPI) * 16)
+                               : kDcOob;
+  dst = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kCpolNt));
+}
+template <int LPI>
+__device__ __forceinline__ void dcp_consume(const DcItem* items, int i, int ib, int ie,
+                                            const bf16_t* hl, int lane, const u32x4_t& wv,
+                                            float (&acc)[kTokInline]) {
+  const int gi = i + lane / LPI;
+  const bool ok = gi >= ib && gi < ie;
+  const DcItem& it = items[min(max(gi, ib), ie - 1)];
+  const int e = (lane % LPI) * 8;
+  Raw8<bf16_t> w8;
+  w8.u = wv;
+#pragma unroll
+  for (int t = 0; t < kTokInline; ++t) {
+    // (a lane outside [ib, ie) may hold a not-yet-loaded buffer: its dot
+    // product is dropped by the select, never multiplied)
+    const float dp = dot8(w8, *reinterpret_cast<const X8<bf16_t>*>(hl + it.thoff[t] + e), 0.f);
+    acc[t] = fmaf(ok ? it.twt[t] : 0.f, ok ? dp : 0.f, acc[t]);
+  }
+}
+template <int LPI>
+__device__ __forceinline__ void dc_family_packed(const DcItem* items, int ib, int ie, int c,
+                                                 const bf16_t* hl, int lane, const DcFamily& F,
+                                                 int d, float (&acc)[kTokInline]) {
+  constexpr int G = kWave / LPI, D = kDcLoads;
+  const int rows = F.rows;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(F.down), (short)0, (int)((size_t)F.n_mats * F.rows * d * 2),
+      kGfx9BufferDword3);
+  u32x4_t buf[D];
+  for (int i0 = ib - D * G; i0 < ie; i0 += D * G) {
+#pragma unroll
+    for (int q = 0; q < D; ++q) {
+      dcp_consume<LPI>(items, i0 + q * G, ib, ie, hl, lane, buf[q], acc);
+      dcp_load<LPI>(items, i0 + (q + D) * G, ie, c, lane, rs, rows, buf[q]);
+    }
+  }
+}
+
+// (built for 8 waves per SIMD -- four 8-wave blocks per CU -- which the
+// register budget of 64 reaches without spills)
 template <bool FP8>
-__global__ __launch_bounds__(kDcWaves * kWave) void down_combine_kernel(DownCombineArgs a,
+__global__ __launch_bounds__(kDcWaves * kWave) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void down_combine_kernel(DownCombineArgs a,
                                                                      bf16_t* __restrict__ y) {
   extern __shared__ __align__(16) unsigned char dc_lds[];
   bf16_t* hl = reinterpret_cast<bf16_t*>(dc_lds);
@@ -2508,6 +2568,7 @@ __global__ __launch_bounds__(kDcWaves * kWave) void down_combine_kernel(DownComb
         }
         DcItem it;
         it.w = static_cast<const char*>(F.down) + (size_t)mat * ms * (FP8 ? 1 : 2);
+        it.woff = (uint32_t)((size_t)mat * ms * (FP8 ? 1 : 2));
         it.scale = FP8 ? F.down_scale + (size_t)mat * d : nullptr;
         it.rows = F.rows;
         it.nsteps = (F.rows + dc_epl<FP8>() * kWave - 1) / (dc_epl<FP8>() * kWave);
@@ -2517,6 +2578,18 @@ __global__ __launch_bounds__(kDcWaves * kWave) void down_combine_kernel(DownComb
           it.hoff[j] = F.lds_off + (r0 + min(j, max(n - 1, 0))) * F.rows;
           it.tok[j] = min(max(tk[j], 0), T - 1);
           it.wt[j] = j < n ? (F.wrow ? F.wrow[r0 + j] : 1.f) : 0.f;
+        }
+        // the same by token (a group's rows belong to distinct tokens)
+#pragma unroll
+        for (int t = 0; t < kTokInline; ++t) {
+          it.thoff[t] = it.hoff[0];
+          it.twt[t] = 0.f;
+#pragma unroll
+          for (int j = 0; j < kTokInline; ++j)
+            if (j < n && it.tok[j] == t) {
+              it.thoff[t] = it.hoff[j];
+              it.twt[t] = it.wt[j];
+            }
         }
         items[fb[fi] + i] = it;
       }
@@ -2544,7 +2617,14 @@ __global__ __launch_bounds__(kDcWaves * kWave) void down_combine_kernel(DownComb
     if (fi < a.nf && fb[fi] < fb[fi + 1]) {
       constexpr int SE = dc_epl<FP8>() * kWave;  // elements per step
       const int ns = (a.f[fi].rows + SE - 1) / SE;
-      if (ns <= 1)
+      const int rows = a.f[fi].rows;
+      // (packed loads address the family's weights by 32-bit byte offsets)
+      const bool packable = !FP8 && (size_t)a.f[fi].n_mats * rows * d * 2 < (size_t)kDcOob;
+      if (packable && rows == 16 * 8)
+        dc_family_packed<16>(items, fb[fi], fb[fi + 1], c, hl, lane, a.f[fi], d, acc);
+      else if (packable && rows == 32 * 8)
+        dc_family_packed<32>(items, fb[fi], fb[fi + 1], c, hl, lane, a.f[fi], d, acc);
+      else if (ns <= 1)
         dc_family<1, FP8>(items, fb[fi], fb[fi + 1], c, hl, lane, acc);
       else if (ns == 2 || FP8)
         dc_family<2, FP8>(items, fb[fi], fb[fi + 1], c, hl, lane, acc);

@@ -687,11 +687,16 @@ def test_layer_edge_shapes():
     # (d, E, k, I, m, S, Is): rows of one step with idle lanes (I = 40, Is = 24),
     # rows of several steps with a ragged last one (I = 1096: 137 chunks of 16
     # bytes over 64 lanes), department slices with and without the shared
-    # expert
+    # expert; rows of 128 and 256 elements, whose groups share a wave load
+    # four or two at a time (a ragged last load when the group count is not
+    # a multiple), in every family
     (776, 6, 3, 40, 0, 0, 24),
     (264, 8, 2, 1096, 0, 0, 0),
     (1024, 16, 4, 96, 4, 160, 64),
     (520, 12, 6, 56, 3, 200, 0),
+    (512, 16, 4, 128, 4, 256, 128),
+    (640, 10, 3, 256, 0, 0, 256),
+    (384, 24, 7, 128, 0, 0, 0),
 ])
 @pytest.mark.parametrize("T", [1, 2, 3, 4])
 def test_layer_down_with_combine_epilogue(case, T):
