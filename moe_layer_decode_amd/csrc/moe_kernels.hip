@@ -1022,11 +1022,20 @@ __global__ __launch_bounds__(kPlanThreads) void topk_plan_kernel(RouteArgs ra, P
   if constexpr (NPL <= 4) {
     // up to 256 experts: each wave stages its own token in its own row
     static_assert(kPlanWaves * 4 * kWave <= kTopkBuf, "a row per wave");
-    __syncthreads();  // the tallies are clear
-    for (int t = wid; t < ra.T; t += nw) {
+    if (ra.T <= nw) {
+      // one token per wave: its logits are requested before the barrier
+      // that completes the clearing (the staged row is not a tally)
       uint32_t key[NPL];
-      stage_token<NPL, GROUPED>(ra, t, wid * ra.E, lane, s, key);
-      topk_token<NPL, GROUPED>(ra, t, wid * ra.E, lane, s, key);
+      if (wid < ra.T) stage_token<NPL, GROUPED>(ra, wid, wid * ra.E, lane, s, key);
+      __syncthreads();  // the tallies are clear
+      if (wid < ra.T) topk_token<NPL, GROUPED>(ra, wid, wid * ra.E, lane, s, key);
+    } else {
+      __syncthreads();  // the tallies are clear
+      for (int t = wid; t < ra.T; t += nw) {
+        uint32_t key[NPL];
+        stage_token<NPL, GROUPED>(ra, t, wid * ra.E, lane, s, key);
+        topk_token<NPL, GROUPED>(ra, t, wid * ra.E, lane, s, key);
+      }
     }
   } else {
     // many experts: the whole block stages chunks of tokens (the first
