@@ -2275,25 +2275,55 @@ __global__ __launch_bounds__(kThreads) void pair_combine_kernel(PairCombineArgs 
 }
 
 // One block per (256 columns, token): every thread one output element.
+constexpr int kCombineBatch = 8;
 template <typename AT>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a, AT* __restrict__ y) {
   const int c = blockIdx.x * kThreads + threadIdx.x;
   const int t = blockIdx.y;
   if (c >= a.d) return;
+  // Slots (then departments) in order, kCombineBatch at a time: the batch's
+  // row indices are read together, then its weights and rows (a missing row
+  // reads row 0, and a select drops it), so a batch costs two round trips
+  // instead of two per slot.
+  constexpr int B = kCombineBatch;
   float acc = 0.f;
   if (a.row_out) {
-    for (int j = 0; j < a.k; ++j) {
-      const int r = a.inv_perm[t * a.k + j];
-      if (r >= 0 && r < a.max_rows)
-        acc = fmaf(a.row_weight[r], a.row_out[(size_t)r * a.d + c], acc);
+    const int* ip = a.inv_perm + (size_t)t * a.k;
+    for (int j0 = 0; j0 < a.k; j0 += B) {
+      int r[B];
+#pragma unroll
+      for (int q = 0; q < B; ++q) r[q] = ip[min(j0 + q, a.k - 1)];
+      float wv[B], ov[B];
+      bool ok[B];
+#pragma unroll
+      for (int q = 0; q < B; ++q) {
+        ok[q] = j0 + q < a.k && r[q] >= 0 && r[q] < a.max_rows;
+        const int rr = ok[q] ? r[q] : 0;
+        wv[q] = a.row_weight[rr];
+        ov[q] = a.row_out[(size_t)rr * a.d + c];
+      }
+#pragma unroll
+      for (int q = 0; q < B; ++q) acc = ok[q] ? fmaf(wv[q], ov[q], acc) : acc;
     }
   }
   if (a.dept_out) {
-    for (int J = 0; J < a.m; ++J) {
-      const int q = a.dept_inv[t * a.m + J];
-      if (q >= 0 && q < a.max_dept_rows)  // no scales: the weights are already inside (factorised)
-        acc = a.dept_scale ? fmaf(a.dept_scale[q], a.dept_out[(size_t)q * a.d + c], acc)
-                           : acc + a.dept_out[(size_t)q * a.d + c];
+    const int* dp = a.dept_inv + (size_t)t * a.m;
+    for (int J0 = 0; J0 < a.m; J0 += B) {
+      int r[B];
+#pragma unroll
+      for (int q = 0; q < B; ++q) r[q] = dp[min(J0 + q, a.m - 1)];
+      float wv[B], ov[B];
+      bool ok[B];
+#pragma unroll
+      for (int q = 0; q < B; ++q) {
+        ok[q] = J0 + q < a.m && r[q] >= 0 && r[q] < a.max_dept_rows;
+        const int rr = ok[q] ? r[q] : 0;
+        // no scales: the weights are already inside (factorised)
+        wv[q] = a.dept_scale ? a.dept_scale[rr] : 1.f;
+        ov[q] = a.dept_out[(size_t)rr * a.d + c];
+      }
+#pragma unroll
+      for (int q = 0; q < B; ++q) acc = ok[q] ? fmaf(wv[q], ov[q], acc) : acc;
     }
   }
   if (a.shared_out) acc += a.shared_out[(size_t)t * a.d + c];
