@@ -45,15 +45,17 @@ bool fp8(const moe_layer_desc& d) { return d.w_dtype == MOE_FP8_E4M3; }
 // Element type of the router: the activation dtype when the experts are FP8.
 int router_dtype(const moe_layer_desc& d) { return fp8(d) ? d.act_dtype : d.w_dtype; }
 
-// K pieces of the bf16 router: enough (16-expert tile, piece) blocks to reach
-// about 512 blocks, at most kMaxRouteSplit partial planes, and at least 64
-// elements of K per wave.  fp32 layers use one plane.
+// K pieces (partial-logit planes) of the bf16 router: enough (16-expert tile,
+// piece) blocks to reach about 512 blocks, at most kMaxRouteSplit planes, and
+// at least 128 elements of K per wave (measured: at d = 2048 four planes beat
+// eight -- the top-k then reads half the partials -- while at d = 7168 eight
+// beat four).  fp32 layers use one plane.
 int route_ksplit(const moe_layer_desc& d) {
   if (router_dtype(d) != MOE_BF16) return 1;
   const int tiles = ceil_div(d.n_experts, 16);
   int s = ceil_div(512, tiles);
   if (s > moe::kMaxRouteSplit) s = moe::kMaxRouteSplit;
-  const int kmax = d.d_model / (moe::kWaves * 64);
+  const int kmax = d.d_model / (moe::kWaves * 128);
   if (s > kmax) s = kmax;
   return s < 1 ? 1 : s;
 }
