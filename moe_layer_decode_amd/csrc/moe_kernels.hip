@@ -324,10 +324,11 @@ __device__ __forceinline__ void select_rank(const uint32_t (&key)[NP], EidOf eid
 // The k largest of NP planes of keys (entry i of lane l is expert l + 64 i),
 // taken one at a time in rank order: round r finds the wave's largest
 // remaining key (lowest expert among equal keys) and sets slot_id[r].  Every
-// round is a wave maximum by row moves plus one ballot per plane, so for
-// small k this is much shorter than a bitwise radix select followed by a
-// ranking pass.  Taken entries drop to key 0 and stay out of later ties
-// through the per-plane taken masks.
+// round is a wave maximum by row moves plus one ballot per plane: k rounds of
+// mostly vector work, against the 32 scalar-bound rounds of a bitwise radix
+// select plus a ranking pass (the scalar unit is the CU's, shared by the
+// block's waves when every wave selects a token at once).  Taken entries drop
+// to key 0 and stay out of later ties through the per-plane taken masks.
 constexpr int kExtractMaxK = 16;
 template <int NP>
 __device__ __forceinline__ void select_extract(uint32_t (&key)[NP], int k, int lane,
@@ -1477,15 +1478,17 @@ constexpr int kStageRing = 4;  // weight steps requested before the staging barr
 // Up to kStageRing steps of the row are requested before the staging, so they
 // are all in flight through the barrier; after it, each consumed step's slot
 // is refilled kStageRing steps ahead.  Same per-lane column order and
-// reduction as gu_small.
-template <typename T_, bool DUAL>
+// reduction as gu_small.  NT: rows a group can have in this launch (1 at a
+// batch of one token: a quarter of the accumulators and a shorter reduction).
+template <typename T_, bool DUAL, int NT = kTokInline>
 __device__ __forceinline__ void gu_small_lds(const T_* __restrict__ Wg, const T_* __restrict__ Wu,
                                              int d, int rows, int i0, const T_* __restrict__ x,
                                              const T_* __restrict__ xu, int in_rows,
                                              const Slot& sl, const int* grp_token,
                                              const GuOut<T_>& o, int lane, int wid,
                                              SmallLds<T_, DUAL ? 2 * kTokInline : kTokInline>& lds) {
-  constexpr int NT = kTokInline, R = kStageRing, STEP = 8 * kWave;
+  static_assert(NT >= 1 && NT <= kTokInline && (NT & (NT - 1)) == 0, "NT: 1, 2 or 4");
+  constexpr int R = kStageRing, STEP = 8 * kWave;
   constexpr int UROW = DUAL ? NT : 0;  // LDS row of the up input of row t: UROW + t
   const int nv = sl.n;
   const size_t i = (size_t)min(i0, rows - 1);
@@ -2118,7 +2121,8 @@ constexpr size_t expert_lds_bytes() {
 // XL: small groups read their activations from LDS (rows of at most kXLds).
 // DUAL: every part of the launch reads gate and up inputs from two different
 // matrices (the private transforms of the factorised form).
-template <typename T_, int RPW, int RW, int NCMAX, bool XL, bool DUAL>
+// NTI: rows a small group can have in the launch (kTokInline, or 1 at T = 1).
+template <typename T_, int RPW, int RW, int NCMAX, bool XL, bool DUAL, int NTI = kTokInline>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     gateup_min_waves<T_, NCMAX, DUAL>(), 8))) void gateup_kernel(FamilySet set,
                                                            const T_* __restrict__ x, int T,
@@ -2138,7 +2142,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   if (!F.large) {
     if constexpr (XL) {
       static_assert(RPW == 1 && RW == 1, "staged activations take one row per wave");
-      gu_small_lds<T_, DUAL>(
+      gu_small_lds<T_, DUAL, NTI>(
           Wg, Wu, d, F.rows, tile * kWaves + wid, xg, xu, F.in_rows, sl, F.grp_token, o, lane, wid,
           *reinterpret_cast<SmallLds<T_, DUAL ? 2 * kTokInline : kTokInline>*>(lds_raw));
       return;
@@ -3046,7 +3050,9 @@ static hipError_t launch_gateup_t(const FamilySet& set, const T_* x, int T, int 
     // the private transforms' groups seldom pass four rows: 16-token passes
     if (xl) MOE_GU(1, true, true); else MOE_GU(1, false, true);
   } else {
-    if (ncmax == 4) { if (xl) MOE_GU(4, true, false); else MOE_GU(4, false, false); }
+    if (T == 1 && xl)  // one token: one row per group
+      launch(gateup_kernel<T_, 1, 1, 1, true, false, 1>, grid, block, st, ev, set, x, T, d);
+    else if (ncmax == 4) { if (xl) MOE_GU(4, true, false); else MOE_GU(4, false, false); }
     else if (ncmax == 2) { if (xl) MOE_GU(2, true, false); else MOE_GU(2, false, false); }
     else if (xl) MOE_GU(1, true, false); else MOE_GU(1, false, false);
   }
