@@ -463,10 +463,10 @@ def run_layer(desc, w, x):
     return y, layer
 
 
-def check_layer(name, seed, T, sample_tokens=None):
+def check_layer(name, seed, T, sample_tokens=None, max_tokens=None):
     shape = SH[name]
     w = gpu_layer(name, seed)
-    desc = desc_of(shape)
+    desc = desc_of(shape, max_tokens)
     x = moe_synth.make_tokens(shape, seed, T, DEV)
     y, layer = run_layer(desc, w, x)
     g_plan = layer.plan(T)
@@ -510,6 +510,16 @@ def test_layer_qwen3_shape(seed, T):
 @pytest.mark.parametrize("seed", [0, 1])
 def test_layer_deamoe_7b(seed, T):
     check_layer(DEA7, seed, T)
+
+
+@pytest.mark.parametrize("name,T", [(QWEN, 128), (QWEN, 512), (DEA7, 100)])
+def test_layer_large_batch(name, T):
+    """Batches past 64 tokens: the plan ranks an assignment by popcounts over
+    its expert's token bits spread across several 64-bit words (eight at
+    T = 512, the assignment limit at top-8), one wave writes the plan when
+    there are no departments, and groups span several 16-token chunks.  The
+    whole plan is compared; outputs on a sample of tokens."""
+    check_layer(name, 0, T, sample_tokens=list(range(0, T, 7)) + [T - 1], max_tokens=T)
 
 
 @pytest.mark.parametrize("T", [1, 8, 32])
