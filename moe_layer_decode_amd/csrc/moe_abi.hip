@@ -500,28 +500,40 @@ moe_status run_experts(const moe_layer_desc& d, const moe_weights& w, const void
   const moe::GemvConfig cfg = choose_config(d, T);
   const int dm = d.d_model;
   if (fp8(d)) {
-    // FP8 experts: every part tiled like a small one (kFp8RowsPerWave
-    // gate/up rows per wave; down: kFp8DownColGroups * 64 / lpr columns per
-    // wave), any group size
+    // FP8 experts.  Register GEMVs, every part tiled like a small one
+    // (kFp8RowsPerWave gate/up rows per wave; down: kFp8DownColGroups *
+    // 64 / lpr columns per wave), kTokInline tokens a pass; or every part on
+    // 64-row (gate/up) or 64-column (down) matrix-core tiles, 16 or 32 tokens
+    // a pass.  Measured: the GEMVs are faster at T = 8 (d = 7168) and at
+    // T = 16 with d = 2048, the tiles from T = 16 at d = 7168 (624 against
+    // 656 us a step) and far ahead beyond (T = 128: 1293 against 3512 us).
     FamilySet set = make_families(d, w, p, ws, T, row_out, dept_out, shared_out);
+    const bool wide = T > 16 || (T > 8 && dm > 2048);
     // FP8 down: 16 lanes per weight row (8 columns per wave) for every row
     // length; measured faster than 32 or 64 lanes on 2048-code rows
     const int lpr = 16;
     set.blk_start[0] = 0;
     for (int i = 0; i < set.n; ++i) {
-      set.f[i].tiles = ceil_div(set.f[i].rows, moe::kWaves * moe::kFp8RowsPerWave);
-      set.blk_start[i + 1] = set.blk_start[i] + set.f[i].max_slots * set.f[i].tiles;
+      Family& f = set.f[i];
+      f.tiles = wide ? ceil_div(f.rows, moe::kWideRows)
+                     : ceil_div(f.rows, moe::kWaves * moe::kFp8RowsPerWave);
+      set.blk_start[i + 1] = set.blk_start[i] + f.max_slots * f.tiles;
     }
     for (int i = set.n + 1; i <= moe::kMaxParts; ++i) set.blk_start[i] = set.blk_start[set.n];
-    if (moe::launch_gateup_fp8(set, x, T, dm, st, ev_gu) != hipSuccess) return MOE_ERR_HIP;
+    if ((wide ? moe::launch_fp8_wide(true, set, x, T, dm, st, ev_gu)
+              : moe::launch_gateup_fp8(set, x, T, dm, st, ev_gu)) != hipSuccess)
+      return MOE_ERR_HIP;
     if (gateup_only) return MOE_OK;
     set.blk_start[0] = 0;
     for (int i = 0; i < set.n; ++i) {
-      set.f[i].tiles = ceil_div(dm, moe::kWaves * moe::kFp8DownColGroups * (64 / lpr));
-      set.blk_start[i + 1] = set.blk_start[i] + set.f[i].max_slots * set.f[i].tiles;
+      Family& f = set.f[i];
+      f.tiles = wide ? ceil_div(dm, moe::kWideRows)
+                     : ceil_div(dm, moe::kWaves * moe::kFp8DownColGroups * (64 / lpr));
+      set.blk_start[i + 1] = set.blk_start[i] + f.max_slots * f.tiles;
     }
     for (int i = set.n + 1; i <= moe::kMaxParts; ++i) set.blk_start[i] = set.blk_start[set.n];
-    return hip_status(moe::launch_down_fp8(set, T, dm, lpr, st, ev_dn));
+    return hip_status(wide ? moe::launch_fp8_wide(false, set, nullptr, T, dm, st, ev_dn)
+                           : moe::launch_down_fp8(set, T, dm, lpr, st, ev_dn));
   }
   if (!factorised(d)) {
     FamilySet set = make_families(d, w, p, ws, T, row_out, dept_out, shared_out);

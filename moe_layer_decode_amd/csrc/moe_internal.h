@@ -198,6 +198,11 @@ hipError_t launch_gateup_fp8(const FamilySet& set, const void* x, int T, int d, 
                              const KernelEvents* ev);
 hipError_t launch_down_fp8(const FamilySet& set, int T, int d, int lpr, hipStream_t st,
                            const KernelEvents* ev);
+// FP8 experts at larger batches: every group on matrix-core tiles (gate/up:
+// 64 rows per block, tiles = ceil(rows / kWideRows); down: 64 columns per
+// block, tiles = ceil(d / kWideRows)), the codes widened to bf16.
+hipError_t launch_fp8_wide(bool gateup, const FamilySet& set, const void* x, int T, int d,
+                           hipStream_t st, const KernelEvents* ev);
 hipError_t launch_zero(unsigned int* p, size_t n, hipStream_t st);
 hipError_t launch_stream_read(const void* src, size_t blocks, float* sink, hipStream_t st);
 hipError_t launch_pair_combine(int act_dtype, const PairCombineArgs& a, void* zc, int max_pairs,

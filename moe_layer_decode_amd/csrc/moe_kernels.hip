@@ -1788,53 +1788,59 @@ constexpr int kWideK = 64;     // K per step: two 32-wide matrix-core steps
 
 // Two buffers of one step's inputs: [buffer][input][token tile][half][lane],
 // lane l of (c, half) holding token 16c + l%16, k = 32 half + 8 (l/16) .. +7.
-template <int NC, int NX>
+// H: 8-element k pieces per lane group and step (2: the 64-element step of
+// bf16 weights; 4: the 128-element step of FP8 weights).
+template <int NC, int NX, int H = 2>
 struct WideLds {
-  u32x4_t x[2][NX * NC * 2 * kWave];
+  u32x4_t x[2][NX * NC * H * kWave];
 };
 
 // Per-thread share of one step's input chunks: chunk q = tid + kThreads * r
-// of Q = NX*NC*128, with l = q % 64, half = (q/64) % 2, c = (q/128) % NC,
-// input v = q / (128 NC).
-template <int NC, int NX>
+// of Q = NX*NC*64H, with l = q % 64, half = (q/64) % H, c = (q/(64H)) % NC,
+// input v = q / (64 H NC).
+template <int NC, int NX, int H = 2>
 struct WideIn {
-  static constexpr int Q = NX * NC * 2 * kWave;
+  static constexpr int Q = NX * NC * H * kWave;
   static constexpr int R = (Q + kThreads - 1) / kThreads;
   const bf16_t* p[R];  // input row + k offset of the chunk (nullptr: token past the group)
   int koff[R];
 };
 
-template <int NC, int NX, typename RowOf>
-__device__ __forceinline__ void wide_inputs(WideIn<NC, NX>& in, const bf16_t* const* src, int d,
-                                            int tc, int n, RowOf row_of) {
+// The k of a chunk within the step: H = 2 (bf16 weights) k = 32 half +
+// 8 (l/16); H = 4 (FP8 weights, whose lane group l/16 reads 32 consecutive
+// codes) k = 32 (l/16) + 8 half.
+template <int NC, int NX, int H = 2, typename RowOf>
+__device__ __forceinline__ void wide_inputs(WideIn<NC, NX, H>& in, const bf16_t* const* src,
+                                            int d, int tc, int n, RowOf row_of) {
 #pragma unroll
-  for (int r = 0; r < WideIn<NC, NX>::R; ++r) {
+  for (int r = 0; r < WideIn<NC, NX, H>::R; ++r) {
     const int q = threadIdx.x + kThreads * r;
-    const int l = q & 63, half = (q >> 6) & 1, rest = q >> 7;
+    const int l = q & 63, half = (q >> 6) % H, rest = (q >> 6) / H;
     const int c = rest % NC, v = rest / NC;
     const int t = tc + 16 * c + (l & 15);
-    in.koff[r] = 32 * half + 8 * (l >> 4);
-    in.p[r] = (q < WideIn<NC, NX>::Q && t < n) ? src[v < NX ? v : 0] + (size_t)row_of(t) * d : nullptr;
+    in.koff[r] = H == 2 ? 32 * half + 8 * (l >> 4) : 32 * (l >> 4) + 8 * half;
+    in.p[r] = (q < WideIn<NC, NX, H>::Q && t < n) ? src[v < NX ? v : 0] + (size_t)row_of(t) * d
+                                                  : nullptr;
   }
 }
 
-template <int NC, int NX>
-__device__ __forceinline__ void wide_load(u32x4_t* dst, const WideIn<NC, NX>& in, int k0,
+template <int NC, int NX, int H = 2>
+__device__ __forceinline__ void wide_load(u32x4_t* dst, const WideIn<NC, NX, H>& in, int k0,
                                           int K) {
   const u32x4_t z = {0, 0, 0, 0};
 #pragma unroll
-  for (int r = 0; r < WideIn<NC, NX>::R; ++r) {
+  for (int r = 0; r < WideIn<NC, NX, H>::R; ++r) {
     const int k = k0 + in.koff[r];
     dst[r] = (in.p[r] && k < K) ? ld16(in.p[r] + k) : z;
   }
 }
 
-template <int NC, int NX>
-__device__ __forceinline__ void wide_stage(WideLds<NC, NX>& lds, int buf, const u32x4_t* v) {
+template <int NC, int NX, int H = 2>
+__device__ __forceinline__ void wide_stage(WideLds<NC, NX, H>& lds, int buf, const u32x4_t* v) {
 #pragma unroll
-  for (int r = 0; r < WideIn<NC, NX>::R; ++r) {
+  for (int r = 0; r < WideIn<NC, NX, H>::R; ++r) {
     const int q = threadIdx.x + kThreads * r;
-    if (q < WideIn<NC, NX>::Q) lds.x[buf][q] = v[r];
+    if (q < WideIn<NC, NX, H>::Q) lds.x[buf][q] = v[r];
   }
 }
 
@@ -2694,9 +2700,9 @@ void down_combine_kernel(DownCombineArgs a,
 // instruction multiplies them with the bf16 activations, summing in fp32; the
 // row's scale multiplies the finished sum.  Groups of any size are taken
 // kTokInline tokens at a time, their activation rows (gate/up) or rows of h
-// (down) staged in LDS once per chunk; no matrix-core path (decode groups are
-// small, and the weights of a group of more than kTokInline rows are re-read
-// from the cache for each further chunk).
+// (down) staged in LDS once per chunk, so the weights of a group of more
+// than kTokInline rows are re-read from the cache for each further chunk;
+// larger batches take the matrix-core tiles further below instead.
 // ---------------------------------------------------------------------------
 
 
@@ -2820,6 +2826,162 @@ __device__ __forceinline__ void gu_fp8(const Family& F, const Slot& sl, const bf
     __syncthreads();  // every wave is done with the staged rows before the next chunk
   }
 }
+
+// ---- FP8 layers at batches past kTokInline: 64-row (gate/up) or 64-column
+// (down) matrix-core tiles, 16*NC tokens a pass, so each weight byte is read
+// once per pass rather than once per kTokInline tokens.  A step covers 128 codes
+// of K: lane group g = l/16 reads the 32 consecutive codes 32g .. 32g + 31 of
+// its row (two 16-byte loads through the matrix's buffer resource) and widens
+// them to four bf16 fragments; the activations are staged in the same k
+// order (H = 4).  The row (gate/up) or column (down) scale multiplies the
+// finished sum.
+constexpr int kWideK8 = 128;
+
+// Codes 8j .. 8j + 7 of a 16-byte load (j = 0, 1) as one bf16x8 fragment.
+__device__ __forceinline__ u32x4_t fp8x8_frag(const u32x4_t& w, int j) {
+  const uint32_t a = j == 0 ? w.x : w.z, b = j == 0 ? w.y : w.w;
+  u32x4_t o;
+  o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(a, 1.0f, false));
+  o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(a, 1.0f, true));
+  o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b, 1.0f, false));
+  o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b, 1.0f, true));
+  return o;
+}
+
+// Shared by both FP8 tiles: acc[m][c] += A_m (rows of codes, `rs[m]` at
+// offsets aoff(k)) x B (16*NC inputs staged from `in`), over K in 128-code
+// steps.
+template <int NC, int NM, typename AOff>
+__device__ __forceinline__ void fp8_wide_loop(const __amdgpu_buffer_rsrc_t (&rs)[NM], AOff aoff,
+                                              const WideIn<NC, 1, 4>& in, int K, int g,
+                                              int lane, WideLds<NC, 1, 4>& lds,
+                                              f32x4_t (&acc)[NM][NC]) {
+  constexpr int R = WideIn<NC, 1, 4>::R;
+  u32x4_t rx[2][R], ra[2][NM][2];
+  auto request = [&](auto S, int k0) {
+    constexpr int s = decltype(S)::value;
+    wide_load<NC, 1, 4>(rx[s], in, k0, K);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t o = aoff(k0 + 32 * g + 16 * j);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) ra[s][m][j] = fp8_ld(rs[m], o);
+    }
+  };
+  auto use = [&](auto S) {
+    constexpr int s = decltype(S)::value;
+    wide_stage<NC, 1, 4>(lds, s, rx[s]);
+    __syncthreads();
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      u32x4_t a[NM];
+#pragma unroll
+      for (int m = 0; m < NM; ++m) a[m] = fp8x8_frag(ra[s][m][hh >> 1], hh & 1);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const u32x4_t b = lds.x[s][(c * 4 + hh) * kWave + lane];
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+          acc[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[m]), as_bf16x8(b),
+                                                              acc[m][c], 0, 0, 0);
+      }
+    }
+  };
+  const int nk = (K + kWideK8 - 1) / kWideK8;
+  const Slot0 s0;
+  const Slot1 s1;
+  request(s0, 0);
+  for (int it = 0; it < nk; it += 2) {
+    if (it + 1 < nk) request(s1, (it + 1) * kWideK8);
+    use(s0);
+    if (it + 1 < nk) {
+      if (it + 2 < nk) request(s0, (it + 2) * kWideK8);
+      use(s1);
+    }
+  }
+}
+
+// 64 rows (i0..) of FP8 gate and up (matrix bases Wg, Wu; row scales gsc,
+// usc) against 16*NC tokens (rows tc.. of the group [r0, r0 + n)):
+// h[r0 + t][i] = SiLU(sg_i * g_t) * (su_i * u_t).
+template <int NC>
+__device__ __forceinline__ void gu_wide_fp8(
+    const uint8_t* __restrict__ Wg, const uint8_t* __restrict__ Wu,
+    const float* __restrict__ gsc, const float* __restrict__ usc, int d, int rows, int i0,
+    const bf16_t* __restrict__ x, int in_rows, int r0, int n, const int* grp_token, int tc,
+    bf16_t* __restrict__ h, int lane, int wid, WideLds<NC, 1, 4>& lds) {
+  const int r16 = lane & 15, g = lane >> 4;
+  const uint32_t ms = (uint32_t)((size_t)rows * d);
+  const __amdgpu_buffer_rsrc_t rs[2] = {fp8_rsrc(Wg, ms), fp8_rsrc(Wu, ms)};
+  const int wr = i0 + 16 * wid + r16;  // this lane's weight row
+  auto aoff = [&](int k) -> uint32_t {
+    return (wr < rows && k < d) ? (uint32_t)(wr * d + k) : kFp8Oob;
+  };
+  WideIn<NC, 1, 4> in;
+  const bf16_t* const src[1] = {x};
+  wide_inputs<NC, 1, 4>(in, src, d, tc, n, [&](int t) {
+    const int tok = grp_token ? grp_token[r0 + t] : t;
+    return min(max(tok, 0), in_rows - 1);
+  });
+  f32x4_t acc[2][NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) acc[0][c] = acc[1][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  fp8_wide_loop<NC, 2>(rs, aoff, in, d, g, lane, lds, acc);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int t = tc + c * 16 + r16;
+    if (t < n) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = i0 + 16 * wid + 4 * g + i;
+        if (rr < rows)
+          store_act(h + (size_t)(r0 + t) * rows + rr,
+                    silu(gsc[rr] * acc[0][c][i]) * (usc[rr] * acc[1][c][i]));
+      }
+    }
+  }
+  __syncthreads();  // the buffers are free for the next pass
+}
+
+// 64 output columns (c0..) of FP8 down (matrix base Wd, column scales dsc)
+// against 16*NC rows of h (rows tc.. of the group):
+// out[r0 + t][c] = sd_c * (W_down[c] . h[r0 + t]).
+template <int NC>
+__device__ __forceinline__ void dn_wide_fp8(const uint8_t* __restrict__ Wd,
+                                                      const float* __restrict__ dsc, int d,
+                                                      int rows, int c0,
+                                                      const bf16_t* __restrict__ h, int r0,
+                                                      int n, int tc, float* __restrict__ out,
+                                                      int lane, int wid,
+                                                      WideLds<NC, 1, 4>& lds) {
+  const int r16 = lane & 15, g = lane >> 4;
+  const __amdgpu_buffer_rsrc_t rs[1] = {fp8_rsrc(Wd, (uint32_t)((size_t)rows * d))};
+  const int wc = c0 + 16 * wid + r16;  // this lane's weight row (output column)
+  auto aoff = [&](int k) -> uint32_t {
+    return (wc < d && k < rows) ? (uint32_t)(wc * rows + k) : kFp8Oob;
+  };
+  WideIn<NC, 1, 4> in;
+  const bf16_t* const src[1] = {h};
+  wide_inputs<NC, 1, 4>(in, src, rows, tc, n, [&](int t) { return r0 + t; });
+  f32x4_t acc[1][NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) acc[0][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  fp8_wide_loop<NC, 1>(rs, aoff, in, rows, g, lane, lds, acc);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int t = tc + c * 16 + r16;
+    if (t < n) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int col = c0 + 16 * wid + 4 * g + i;
+        if (col < d) out[(size_t)(r0 + t) * d + col] = dsc[col] * acc[0][c][i];
+      }
+    }
+  }
+  __syncthreads();
+}
+
+constexpr size_t kFp8WideLds = sizeof(WideLds<2, 1, 4>);
 
 constexpr int kFp8Rows = kFp8RowsPerWave;
 
@@ -2952,6 +3114,61 @@ __global__ __launch_bounds__(kThreads) void down_fp8_kernel(FamilySet set, int T
   const int cb = __builtin_amdgcn_readfirstlane(tile * (kWaves * CPW) + wid * CPW);
   dn_fp8<LPR, kFp8ColGroups, kFp8DnAhead>(F, sl, d, cb, nts, reinterpret_cast<bf16_t*>(fp8_lds),
                                           lane, wid);
+}
+
+// FP8 layers at batches past kTokInline: every group (small or large) on
+// 64-row matrix-core tiles, the whole block on one tile.
+__global__ __launch_bounds__(kThreads) void gateup_fp8_wide_kernel(FamilySet set,
+                                                                  const bf16_t* __restrict__ x,
+                                                                  int T, int d) {
+  __shared__ __align__(16) unsigned char fp8_lds[kFp8WideLds];
+  int tile;
+  const Family& F = block_part(set, tile);
+  Slot sl;
+  if (!map_slot(F, T, sl, tile)) return;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int i0 = tile * kWideRows;
+  if (i0 >= F.rows) return;
+  const size_t ms = (size_t)F.rows * d;
+  const uint8_t* Wg = static_cast<const uint8_t*>(F.gate) + (size_t)sl.mat * ms;
+  const uint8_t* Wu = static_cast<const uint8_t*>(F.up) + (size_t)sl.mat * ms;
+  const float* gsc = F.gate_scale + (size_t)sl.mat * F.rows;
+  const float* usc = F.up_scale + (size_t)sl.mat * F.rows;
+  const bf16_t* xg = F.x_gate ? static_cast<const bf16_t*>(F.x_gate) : x;
+  bf16_t* h = static_cast<bf16_t*>(F.h);
+#pragma unroll 1
+  for (int tc = 0; tc < sl.n; tc += 32) {
+    if (sl.n - tc > 16)
+      gu_wide_fp8<2>(Wg, Wu, gsc, usc, d, F.rows, i0, xg, F.in_rows, sl.r0, sl.n, F.grp_token,
+                     tc, h, lane, wid, *reinterpret_cast<WideLds<2, 1, 4>*>(fp8_lds));
+    else
+      gu_wide_fp8<1>(Wg, Wu, gsc, usc, d, F.rows, i0, xg, F.in_rows, sl.r0, sl.n, F.grp_token,
+                     tc, h, lane, wid, *reinterpret_cast<WideLds<1, 1, 4>*>(fp8_lds));
+  }
+}
+
+// The same for the down projection, on 64-column tiles.
+__global__ __launch_bounds__(kThreads) void down_fp8_wide_kernel(FamilySet set, int T, int d) {
+  __shared__ __align__(16) unsigned char fp8_lds[kFp8WideLds];
+  int tile;
+  const Family& F = block_part(set, tile);
+  Slot sl;
+  if (!map_slot(F, T, sl, tile)) return;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int c0 = tile * kWideRows;
+  if (c0 >= d) return;
+  const uint8_t* Wd = static_cast<const uint8_t*>(F.down) + (size_t)sl.mat * F.rows * d;
+  const float* dsc = F.down_scale + (size_t)sl.mat * d;
+  const bf16_t* h = static_cast<const bf16_t*>(F.h);
+#pragma unroll 1
+  for (int tc = 0; tc < sl.n; tc += 32) {
+    if (sl.n - tc > 16)
+      dn_wide_fp8<2>(Wd, dsc, d, F.rows, c0, h, sl.r0, sl.n, tc, F.out, lane, wid,
+                     *reinterpret_cast<WideLds<2, 1, 4>*>(fp8_lds));
+    else
+      dn_wide_fp8<1>(Wd, dsc, d, F.rows, c0, h, sl.r0, sl.n, tc, F.out, lane, wid,
+                     *reinterpret_cast<WideLds<1, 1, 4>*>(fp8_lds));
+  }
 }
 
 __global__ void zero_kernel(unsigned int* p, size_t n) {
@@ -3179,6 +3396,27 @@ hipError_t launch_down_fp8(const FamilySet& set, int T, int d, int lpr, hipStrea
     go(down_fp8_kernel<32>);
   else
     go(down_fp8_kernel<64>);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_wide(bool gateup, const FamilySet& set, const void* x, int T, int d,
+                           hipStream_t st, const KernelEvents* ev) {
+  if (set.blk_start[set.n] <= 0) return hipSuccess;
+  const dim3 grid(set.blk_start[set.n]), block(kThreads);
+  const bf16_t* xb = static_cast<const bf16_t*>(x);
+  if (gateup) {
+    if (ev)
+      hipExtLaunchKernelGGL(gateup_fp8_wide_kernel, grid, block, 0, st, ev->start, ev->stop, 0,
+                            set, xb, T, d);
+    else
+      hipLaunchKernelGGL(gateup_fp8_wide_kernel, grid, block, 0, st, set, xb, T, d);
+  } else {
+    if (ev)
+      hipExtLaunchKernelGGL(down_fp8_wide_kernel, grid, block, 0, st, ev->start, ev->stop, 0,
+                            set, T, d);
+    else
+      hipLaunchKernelGGL(down_fp8_wide_kernel, grid, block, 0, st, set, T, d);
+  }
   return hipGetLastError();
 }
 

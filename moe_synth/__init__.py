@@ -97,7 +97,7 @@ SHAPES: Dict[str, LayerShape] = {
     "deepseek_v3_d7168_e256_i2048_s2048_top8": LayerShape(
         name="deepseek_v3_d7168_e256_i2048_s2048_top8", d=7168,
         n_experts=256, top_k=8, d_ff=2048, d_ff_shared=2048, score="sigmoid",
-        bias_range=0.1, batches=(1, 2, 4, 8, 16, 32)),
+        bias_range=0.1, batches=(1, 2, 4, 8, 16, 32, 64, 128)),
     # DeaMoE department layer at 7.3B scale: 64 experts in 8 departments,
     # intermediate [shared 1024 ; private 128], top-8 softmax.
     "deamoe_7b_d2048_e64_m8_s1024_p128_top8": LayerShape(
@@ -110,7 +110,7 @@ SHAPES: Dict[str, LayerShape] = {
         name="deamoe_dsv3_d7168_e256_m32_s1792_p256_top8", d=7168,
         n_experts=256, top_k=8, d_ff=256, n_depts=32, d_ff_dept=1792,
         d_ff_shared=2048, score="sigmoid", bias_range=0.1,
-        batches=(1, 2, 4, 8, 16),
+        batches=(1, 2, 4, 8, 16, 32, 64, 128),
         data_seed_of="deepseek_v3_d7168_e256_i2048_s2048_top8"),
     # DeaMoE's own factorised experts at the DeepSeek-V3-matched configuration
     # of its Table 1 (8 departments x 108 experts, h = 7168, hffn = 2048,
@@ -119,7 +119,7 @@ SHAPES: Dict[str, LayerShape] = {
     "deamoe_paper_dsv3_d7168_e864_m8_h2048_top10": LayerShape(
         name="deamoe_paper_dsv3_d7168_e864_m8_h2048_top10", d=7168,
         n_experts=864, top_k=10, d_ff=2048, n_depts=8, d_ff_dept=2048,
-        d_ff_shared=2048, dept_form="factorised", k_dept=5, batches=(1, 2, 4, 8, 16),
+        d_ff_shared=2048, dept_form="factorised", k_dept=5, batches=(1, 2, 4, 8, 16, 32, 64, 128),
         data_seed_of="deepseek_v3_d7168_e256_i2048_s2048_top8"),
     # The Qwen3-30B-A3B- and DeepSeek-V3-shaped layers with FP8 expert weights
     # (same draws, quantized per output row; router and activations bf16).
@@ -129,7 +129,7 @@ SHAPES: Dict[str, LayerShape] = {
     "deepseek_v3_d7168_e256_i2048_s2048_top8_fp8": LayerShape(
         name="deepseek_v3_d7168_e256_i2048_s2048_top8_fp8", d=7168,
         n_experts=256, top_k=8, d_ff=2048, d_ff_shared=2048, score="sigmoid",
-        bias_range=0.1, batches=(1, 2, 4, 8, 16, 32), expert_dtype="fp8"),
+        bias_range=0.1, batches=(1, 2, 4, 8, 16, 32, 64, 128), expert_dtype="fp8"),
 }
 
 # Tensor ids: part of the counter, so every tensor of a layer draws its own

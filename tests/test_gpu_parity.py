@@ -512,14 +512,17 @@ def test_layer_deamoe_7b(seed, T):
     check_layer(DEA7, seed, T)
 
 
-@pytest.mark.parametrize("name,T", [(QWEN, 128), (QWEN, 512), (DEA7, 100)])
+@pytest.mark.parametrize("name,T", [(QWEN, 128), (QWEN, 512), (DEA7, 100), (DSV3, 128),
+                                    (DEAV3, 128), (PAPER, 128),
+                                    ("deepseek_v3_d7168_e256_i2048_s2048_top8_fp8", 128)])
 def test_layer_large_batch(name, T):
     """Batches past 64 tokens: the plan ranks an assignment by popcounts over
     its expert's token bits spread across several 64-bit words (eight at
     T = 512, the assignment limit at top-8), one wave writes the plan when
     there are no departments, and groups span several 16-token chunks.  The
     whole plan is compared; outputs on a sample of tokens."""
-    check_layer(name, 0, T, sample_tokens=list(range(0, T, 7)) + [T - 1], max_tokens=T)
+    stride = 7 if SH[name].d <= 2048 else 31
+    check_layer(name, 0, T, sample_tokens=list(range(0, T, stride)) + [T - 1], max_tokens=T)
 
 
 @pytest.mark.parametrize("T", [1, 8, 32])
