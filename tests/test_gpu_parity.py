@@ -49,15 +49,17 @@ FACT = {
 }
 # Small FP8 layers (E4M3 expert codes, per-row scales) the oracle runs in
 # full: department slices with a shared expert, rows of one to several
-# 16-code steps, and batches whose groups exceed four rows (T = 9).
+# 16-code steps, batches whose groups exceed four rows (T = 9), and batches
+# past 16 tokens (T = 20), which take the matrix-core tiles with ragged last
+# tiles (48, 208 and 32 rows; 1040 columns) and ragged last K steps.
 FP8 = {
     "fp8_d1040_e12_m3_s208_i48_sh32_top4": moe_synth.LayerShape(
         name="fp8_d1040_e12_m3_s208_i48_sh32_top4", d=1040, n_experts=12, top_k=4, d_ff=48,
         n_depts=3, d_ff_dept=208, d_ff_shared=32, score="sigmoid", bias_range=0.1,
-        expert_dtype="fp8", batches=(1, 4, 9)),
+        expert_dtype="fp8", batches=(1, 4, 9, 20)),
     "fp8_d512_e6_i1040_top3": moe_synth.LayerShape(
         name="fp8_d512_e6_i1040_top3", d=512, n_experts=6, top_k=3, d_ff=1040,
-        expert_dtype="fp8", batches=(1, 3, 9)),
+        expert_dtype="fp8", batches=(1, 3, 9, 20)),
     # rows long enough that the gate/up stages two tokens per chunk, so groups
     # of three and four rows (tokens carried in the descriptor) span chunks
     "fp8_d3088_e6_i96_top3": moe_synth.LayerShape(
