@@ -3116,9 +3116,10 @@ __global__ __launch_bounds__(kThreads) void down_fp8_kernel(FamilySet set, int T
                                           lane, wid);
 }
 
-// FP8 layers at batches past kTokInline: every group (small or large) on
-// 64-row matrix-core tiles, the whole block on one tile.
-__global__ __launch_bounds__(kThreads) void gateup_fp8_wide_kernel(FamilySet set,
+// FP8 layers at larger batches: every group (small or large) on 64-row
+// matrix-core tiles, the whole block on one tile.  Held to four waves per
+// SIMD (128 registers, no spills; measured 0.2-1.7% faster than three).
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void gateup_fp8_wide_kernel(FamilySet set,
                                                                   const bf16_t* __restrict__ x,
                                                                   int T, int d) {
   __shared__ __align__(16) unsigned char fp8_lds[kFp8WideLds];
@@ -3148,7 +3149,7 @@ __global__ __launch_bounds__(kThreads) void gateup_fp8_wide_kernel(FamilySet set
 }
 
 // The same for the down projection, on 64-column tiles.
-__global__ __launch_bounds__(kThreads) void down_fp8_wide_kernel(FamilySet set, int T, int d) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void down_fp8_wide_kernel(FamilySet set, int T, int d) {
   __shared__ __align__(16) unsigned char fp8_lds[kFp8WideLds];
   int tile;
   const Family& F = block_part(set, tile);
