@@ -41,12 +41,18 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--batches", type=str, default="1,4,16")
+    p.add_argument("--batches", type=str, default="1,2,4,8,16,32")
     p.add_argument("--shape", type=str, default=HEADLINE)
     p.add_argument("--sweep", action="store_true", help="also time every other layer shape")
     p.add_argument("--sweep-out", type=str, default="gpurun_out/sweep.jsonl")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--cpu-steps", type=int, default=3,
+                   help="oracle steps per thread setting of the CPU baseline (median)")
+    p.add_argument("--no-dept", action="store_true",
+                   help="skip the department-layer comparisons (DeaMoE-7B-shaped against its "
+                        "expanded vanilla form; the department transform against the "
+                        "DeepSeek-V3-shaped layer)")
+    p.add_argument("--dept-steps", type=int, default=60)
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--profile-pass", action="store_true",
                    help="headline batch only, 20 eager steps + a 1 GiB calibration copy "
@@ -523,38 +529,162 @@ def measured_traffic():
         return None
 
 
-def cpu_baseline(shape, T, base, seconds):
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(shape, T, base, steps):
     """The oracle, as is, on the host: full decode steps of the same layer at
-    batch T on the same inputs, until `seconds` have elapsed."""
-    import numpy as np
-    import torch
+    batch T on the same inputs.  Timed single-threaded and with every host
+    core the process may use (numpy's BLAS thread pool), `steps` steps each;
+    the median step of each.  The reported value is the faster of the two,
+    with the thread count it used."""
+    import statistics
     import moe_synth
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = 1
+    from threadpoolctl import threadpool_limits
     host = {k: v.detach().cpu() for k, v in base.items()}
     if shape.expert_dtype == "fp8":  # the layer on its dequantized weights
         host = O.dequantize_layer(host)
     x = moe_synth.make_tokens(shape, 0, T, "cpu")
-    n, t0 = 0, time.perf_counter()
-    while True:
+    token_output = (O.deamoe_token_output if shape.dept_form == "factorised"
+                    else O.layer_token_output)
+
+    def one_step():
+        t0 = time.perf_counter()
         ids, w, _, _ = O.route(x, host["w_router"], shape.top_k, shape.score,
                                host.get("router_bias"), shape.renormalize, shape.route_scale,
                                shape.n_depts, shape.k_dept, shape.dept_strict)
-        token_output = (O.deamoe_token_output if shape.dept_form == "factorised"
-                        else O.layer_token_output)
         for t in range(T):
             token_output(x[t], ids[t], w[t], host, shape.n_experts, shape.n_depts)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or n >= 50:
-            break
-    return {"value": el / n * 1e6, "unit": "us", "cores": int(cores), "kind": "oracle",
-            "sample": f"{n} full decode steps of {shape.name} at batch {T} "
-                      f"(numpy fp64, {el:.1f} s)"}
+        return time.perf_counter() - t0
+
+    ncores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    res = {}
+    for nt in (1, ncores):
+        with threadpool_limits(nt):
+            one_step()  # warm-up: first-touch of the host weights
+            res[nt] = statistics.median(one_step() for _ in range(max(3, steps)))
+    best = min(res, key=res.get)
+    return {"value": round(res[best] * 1e6, 1), "unit": "us", "cores": int(best), "kind": "oracle",
+            "sample": f"median of {max(3, steps)} full decode steps of {shape.name} at batch {T} "
+                      f"(numpy fp64 oracle), single-threaded and with {ncores} BLAS threads",
+            "single_thread_us": round(res[1] * 1e6, 1),
+            "all_core_us": round(res[ncores] * 1e6, 1), "all_core_threads": int(ncores),
+            "nproc": int(os.cpu_count() or 0), "cpu_model": _cpu_model()}
+
+
+def measure(M, moe_synth, shape, T, dev, base, steps, warmup, graph=True, stage_steps=100):
+    """One (layer, batch) point: graph-replayed and eager step time, stage
+    kernel times, streamed bytes and rates."""
+    import torch
+    r = Runner(M, moe_synth, shape, T, dev, base=base)
+    eager_us = r.time_eager(steps, warmup)
+    graph_us, graph_same = None, None
+    if graph:
+        try:
+            graph_us, _, graph_same = r.time_graph(steps, warmup)
+        except Exception as ex:  # report, fall back to eager
+            log(f"graph capture failed: {ex!r}")
+    stages = r.stage_times(min(steps, stage_steps))
+    us = graph_us if (graph_us is not None and graph_same) else eager_us
+    gu = gateup_bytes(shape, T, r.n_active, r.n_active_depts, r.n_rows, r.n_dept_rows)
+    dn = down_bytes(shape, T, r.n_active, r.n_active_depts, r.n_rows, r.n_dept_rows)
+    rec = {"us": round(us, 2), "eager_us": round(eager_us, 2),
+           "graph_us": None if graph_us is None else round(graph_us, 2),
+           "graph_matches_eager": graph_same,
+           "graph_replay_us_p10_p50_p90": [r.spread[q] for q in (10, 50, 90)]
+           if graph_us is not None else None,
+           "weight_bytes": r.step_bytes, "active_experts": r.n_active,
+           "active_depts": r.n_active_depts,
+           "GBps": round(r.step_bytes / us * 1e-3, 1),
+           "frac_peak": round(r.step_bytes / us * 1e-3 / HBM_PEAK_GBS, 4),
+           "stage_us": {k: round(v, 2) for k, v in stages.items()},
+           "gateup_GBps": round(gu / stages["gateup"] * 1e-3, 1) if stages["gateup"] > 0 else None,
+           "down_GBps": round(dn / stages["down"] * 1e-3, 1) if stages["down"] > 0 else None,
+           "expert_stream_GBps": round((gu + dn) / (stages["gateup"] + stages["down"]) * 1e-3, 1),
+           "expert_stream_frac_peak": round((gu + dn) / (stages["gateup"] + stages["down"]) * 1e-3
+                                            / HBM_PEAK_GBS, 4),
+           "replicas": r.R}
+    del r
+    torch.cuda.empty_cache()
+    return rec, gu, stages
+
+
+def expanded_vanilla(shape, base):
+    """The department layer as a vanilla layer whose expert e carries the
+    concatenated [department slice ; private slice] matrices (the same
+    function; DeaMoE's loading comparison counts these bytes)."""
+    import dataclasses
+    import torch
+    G = shape.n_experts // shape.n_depts
+    dept = torch.arange(shape.n_experts, device=base["w_gate"].device) // G
+    w = {"w_router": base["w_router"],
+         "w_gate": torch.cat([base["wd_gate"][dept], base["w_gate"]], 1).contiguous(),
+         "w_up": torch.cat([base["wd_up"][dept], base["w_up"]], 1).contiguous(),
+         "w_down": torch.cat([base["wd_down"][dept], base["w_down"]], 2).contiguous()}
+    if base.get("router_bias") is not None:
+        w["router_bias"] = base["router_bias"]
+    for k in ("ws_gate", "ws_up", "ws_down"):
+        if base.get(k) is not None:
+            w[k] = base[k]
+    sh = dataclasses.replace(shape, name=shape.name + "_expanded_vanilla", n_depts=0,
+                             d_ff_dept=0, d_ff=shape.d_ff_dept + shape.d_ff)
+    return sh, w
+
+
+def department_comparisons(M, moe_synth, dev, steps, warmup):
+    """Timed department numbers: the DeaMoE-7B-shaped department
+    layer against its expanded vanilla form at batches 1/4/16, and the
+    department transform of the DeepSeek-V3-shaped layer against that layer
+    (same tokens, router and bias) at 1/4/16; each speedup beside the ratio
+    of streamed bytes (DeaMoE section 3.3, Figure 2; section 5.2)."""
+    import torch
+    out = {}
+    dept = moe_synth.SHAPES["deamoe_7b_d2048_e64_m8_s1024_p128_top8"]
+    base = moe_synth.make_layer(dept, 0, dev)
+    vsh, vw = expanded_vanilla(dept, base)
+    rows = {}
+    for T in (1, 4, 16):
+        a, _, _ = measure(M, moe_synth, dept, T, dev, base, steps, warmup, stage_steps=30)
+        b, _, _ = measure(M, moe_synth, vsh, T, dev, vw, steps, warmup, stage_steps=30)
+        rows[str(T)] = {"dept": a, "expanded_vanilla": b,
+                        "speedup": round(b["us"] / a["us"], 3),
+                        "byte_ratio": round(a["weight_bytes"] / b["weight_bytes"], 3)}
+        log(f"{dept.name} T={T}: dept {a['us']} us, expanded {b['us']} us, "
+            f"speedup {rows[str(T)]['speedup']} (byte ratio {rows[str(T)]['byte_ratio']})")
+    out[dept.name] = rows
+    del base, vw
+    torch.cuda.empty_cache()
+    van = moe_synth.SHAPES["deepseek_v3_d7168_e256_i2048_s2048_top8"]
+    tr = moe_synth.SHAPES["deamoe_dsv3_d7168_e256_m32_s1792_p256_top8"]
+    vrec = {}
+    base = moe_synth.make_layer(van, 0, dev)
+    for T in (1, 4, 16):
+        vrec[T], _, _ = measure(M, moe_synth, van, T, dev, base, steps, warmup, stage_steps=30)
+        log(f"{van.name} T={T}: {vrec[T]['us']} us")
+    del base
+    torch.cuda.empty_cache()
+    base = moe_synth.make_layer(tr, 0, dev)
+    rows = {}
+    for T in (1, 4, 16):
+        a, _, _ = measure(M, moe_synth, tr, T, dev, base, steps, warmup, stage_steps=30)
+        b = vrec[T]
+        rows[str(T)] = {"dept": a, "vanilla": b, "speedup": round(b["us"] / a["us"], 3),
+                        "byte_ratio": round(a["weight_bytes"] / b["weight_bytes"], 3)}
+        log(f"{tr.name} T={T}: {a['us']} us vs {b['us']} us, speedup {rows[str(T)]['speedup']} "
+            f"(byte ratio {rows[str(T)]['byte_ratio']})")
+    out[tr.name + "_vs_" + van.name] = rows
+    del base
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -617,42 +747,16 @@ def main():
 
     per_batch, head = {}, None
     for T in batches:
-        r = Runner(M, moe_synth, shape, T, dev, base=base)
-        eager_us = r.time_eager(args.steps, args.warmup)
-        graph_us, graph_same = None, None
-        if not args.no_graph:
-            try:
-                graph_us, _, graph_same = r.time_graph(args.steps, args.warmup)
-            except Exception as ex:  # report, fall back to eager
-                log(f"graph capture failed: {ex!r}")
-        stages = r.stage_times(min(args.steps, 100))
-        us = graph_us if (graph_us is not None and graph_same) else eager_us
-        gu = gateup_bytes(shape, T, r.n_active, r.n_active_depts, r.n_rows, r.n_dept_rows)
-        dn = down_bytes(shape, T, r.n_active, r.n_active_depts, r.n_rows, r.n_dept_rows)
-        rec = {"us": round(us, 2), "eager_us": round(eager_us, 2),
-               "graph_us": None if graph_us is None else round(graph_us, 2),
-               "graph_matches_eager": graph_same,
-               "graph_replay_us_p10_p50_p90": [r.spread[q] for q in (10, 50, 90)]
-               if graph_us is not None else None,
-               "weight_bytes": r.step_bytes, "active_experts": r.n_active,
-               "active_depts": r.n_active_depts,
-               "GBps": round(r.step_bytes / us * 1e-3, 1),
-               "frac_peak": round(r.step_bytes / us * 1e-3 / HBM_PEAK_GBS, 4),
-               "stage_us": {k: round(v, 2) for k, v in stages.items()},
-               "gateup_GBps": round(gu / stages["gateup"] * 1e-3, 1) if stages["gateup"] > 0 else None,
-               "down_GBps": round(dn / stages["down"] * 1e-3, 1) if stages["down"] > 0 else None,
-               "replicas": r.R}
+        rec, gu, stages = measure(M, moe_synth, shape, T, dev, base, args.steps, args.warmup,
+                                  graph=not args.no_graph)
         per_batch[str(T)] = rec
         log(f"T={T}: {json.dumps(rec)}")
         if T == head_T:
-            head = (r, us, gu, stages)
-        del r
+            head = (rec, rec["us"], gu, stages)
         torch.cuda.empty_cache()
 
-    r, us, gu, stages = head
-    head_R = r.R
-    del r, head
-    torch.cuda.empty_cache()
+    rec, us, gu, stages = head
+    head_R = rec["replicas"]
     achieved = gu / stages["gateup"] * 1e-3  # GB/s
     meas_peak = measured_peak_GBps(M, dev)
     out = {
@@ -678,7 +782,15 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("cpu baseline ...")
-        out["cpu_baseline"] = cpu_baseline(shape, head_T, base, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(shape, head_T, base, args.cpu_steps)
+        log(f"cpu baseline: {json.dumps(out['cpu_baseline'])}")
+    if not args.no_dept and shape.name == HEADLINE:
+        del base
+        torch.cuda.empty_cache()
+        base = None
+        out["department_layers"] = department_comparisons(M, moe_synth, dev, args.dept_steps,
+                                                          max(5, args.warmup // 2))
+        base = moe_synth.make_layer(shape, 0, dev) if args.sweep else None
     if args.sweep:
         os.makedirs(os.path.dirname(args.sweep_out) or ".", exist_ok=True)
         sweep_lines = []

@@ -212,7 +212,29 @@ typedef struct {
   int32_t n_tokens;         /* T the plan was built for (host copy) */
 } moe_plan;
 
-/* Kernel timing for moe_layer_decode: stage_events is NULL or an array of
+/* Per-step routing statistics, written on the device by moe_layer_decode
+ * (DeepSeekMoE Guide, "Sequence-Level and Batch-Level Expert Routing
+ * Balance Metrics": the expert load balance factor is the largest per-expert
+ * token count over the mean count of the N_r routed experts; MoE inference
+ * engineering, "Expert load imbalance and rank-level tail latency": record
+ * the assignment counts of every serving step).  The caller owns the struct
+ * in DEVICE memory (8-byte aligned); the top-k + plan kernel fills it in the
+ * same launch that builds the plan, so reading it needs no extra launch and
+ * the call stays legal in a HIP graph.  Nothing else reads it. */
+typedef struct {
+  int32_t n_tokens;             /* T of the step */
+  int32_t n_assignments;        /* dispatched (token, expert) rows: T*k */
+  int32_t n_active_experts;     /* experts with >= 1 row */
+  int32_t n_active_depts;       /* departments with >= 1 (token, department) pair; 0 if vanilla */
+  int32_t max_expert_rows;      /* max_e rows of expert e */
+  int32_t n_invalid;            /* dropped ids (always 0 here: the router picks valid experts) */
+  float mean_expert_rows;       /* n_assignments / E */
+  float imbalance_ratio;        /* max_expert_rows / mean_expert_rows (0 when T = 0) */
+  uint64_t loaded_weight_bytes; /* moe_loaded_weight_bytes(desc, n_active_experts, n_active_depts) */
+  int32_t expert_rows[MOE_MAX_EXPERTS]; /* rows of expert e, e < E (entries past E untouched) */
+} moe_step_stats;
+
+/* Kernel timing for moe_layer_decode_timed: stage_events is an array of
  * 2 * MOE_N_STAGES hipEvent_t created by the caller (with timing enabled);
  * stage i's kernel is launched with hipExtLaunchKernel so that the runtime
  * records stage_events[2i] when it starts and stage_events[2i+1] when it
@@ -286,23 +308,42 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_weights* weights
                           void* workspace, size_t ws_bytes, float* row_out,
                           float* dept_out, float* shared_out, void* stream);
 
-/* Combine: y[t] = sum_j topk weight(t,j) * row_out[inv_perm[t*k+j]]  (slot order)
- *               + sum_J c_{t,J} * dept_out[dept_inv[t*m+J]]           (J ascending)
- *               + shared_out[t]
+/* Combine ("How a batch becomes expert-specific matrices", the combine
+ * that restores token order, with DeaMoE section 2.1 Eq. (3)'s weighted
+ * sum of the selected experts' outputs; the department term is section
+ * 3.2's backbone output scaled by the token's weights in that department;
+ * the shared expert of "Shared Expert Isolation" is added with weight 1):
+ *   y[t] = sum_j topk weight(t,j) * row_out[inv_perm[t*k+j]]  (slot order)
+ *        + sum_J c_{t,J} * dept_out[dept_inv[t*m+J]]           (J ascending)
+ *        + shared_out[t]
  * written in act_dtype (bf16: round to nearest even).  Factorised form:
  * y[t] = sum_J dept_out[dept_inv[t*m+J]] + shared_out[t] (row_out unused, may
- * be NULL). */
+ * be NULL).  row_out / dept_out / shared_out are device float arrays laid
+ * out as moe_expert_ffn writes them; y is the caller's device [T][d]. */
 moe_status moe_combine(const moe_layer_desc* desc, const moe_plan* plan,
                        const float* row_out, const float* dept_out,
                        const float* shared_out, int32_t T, void* y, void* stream);
 
-/* The whole decode step: route -> top-k + dispatch -> grouped gate/up ->
- * grouped down -> combine, y[T][d] in act_dtype (the kernels on `stream` that
- * moe_layer_kernel_count reports: the down launch writes y itself at T <= 4).
- * `stage_events`: see MOE_N_STAGES above (NULL = no timing). */
+/* The whole decode step of DeaMoE section 2.1 (Eq. (1)-(3)) with the
+ * department form of section 3.2 and the shared expert of the DeepSeekMoE
+ * Guide, in the order of "Local MoE execution pipeline": route -> top-k +
+ * dispatch -> grouped gate/up -> grouped down -> combine, y[T][d] in
+ * act_dtype (the kernels on `stream` that moe_layer_kernel_count reports:
+ * the down launch writes y itself at T <= 4).  x and y are the caller's
+ * device arrays; intermediates live in `workspace`.  `stats`: NULL, or a
+ * DEVICE moe_step_stats the step fills (see above).  Errors: every argument
+ * is checked before the first launch (nothing written on failure). */
 moe_status moe_layer_decode(const moe_layer_desc* desc, const moe_weights* weights,
                             const void* x, int32_t T, void* y, void* workspace,
-                            size_t ws_bytes, void* const* stage_events, void* stream);
+                            size_t ws_bytes, moe_step_stats* stats, void* stream);
+
+/* moe_layer_decode with per-stage kernel timing (a measurement variant, not
+ * a step of the layer): stage_events as described at MOE_N_STAGES, or NULL
+ * (then it is exactly moe_layer_decode). */
+moe_status moe_layer_decode_timed(const moe_layer_desc* desc, const moe_weights* weights,
+                                  const void* x, int32_t T, void* y, void* workspace,
+                                  size_t ws_bytes, moe_step_stats* stats,
+                                  void* const* stage_events, void* stream);
 
 /* Static text for a status code. */
 const char* moe_status_string(moe_status status);

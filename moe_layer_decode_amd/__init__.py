@@ -20,7 +20,8 @@ import torch
 __all__ = [
     "MoeError", "LayerDesc", "Weights", "Plan", "layer_desc", "lib", "lib_path",
     "moe_workspace_bytes", "moe_workspace_init", "moe_validate_desc", "moe_route", "moe_dispatch",
-    "moe_expert_ffn", "moe_combine", "moe_layer_decode", "moe_status_string",
+    "moe_expert_ffn", "moe_combine", "moe_layer_decode", "moe_layer_decode_timed",
+    "moe_status_string", "StepStats", "STEP_STATS_BYTES", "alloc_step_stats", "step_stats_to_host",
     "moe_loaded_weight_bytes", "moe_stream_read", "moe_layer_kernel_count", "alloc_workspace",
     "plan_to_host", "MoeLayer",
     "MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE",
@@ -40,7 +41,7 @@ N_STAGES = 5
 STAGE_NAMES = ("route", "dispatch", "gateup", "down", "combine")
 EXPORTED_SYMBOLS = (
     "moe_workspace_bytes", "moe_workspace_init", "moe_validate_desc", "moe_plan_from_workspace", "moe_route",
-    "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_layer_decode",
+    "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_layer_decode", "moe_layer_decode_timed",
     "moe_status_string", "moe_loaded_weight_bytes", "moe_stream_read", "moe_layer_kernel_count",
 )
 
@@ -76,6 +77,21 @@ _PLAN_ARRAYS = ("header", "counts", "offsets", "row_token", "row_slot", "row_exp
 
 class Plan(ctypes.Structure):
     _fields_ = [(n, _vp) for n in _PLAN_ARRAYS] + [("n_tokens", _i32)]
+
+
+MAX_EXPERTS = 2048
+
+
+class StepStats(ctypes.Structure):
+    """moe_step_stats: the step's routing statistics, filled on the device."""
+    _fields_ = [("n_tokens", _i32), ("n_assignments", _i32), ("n_active_experts", _i32),
+                ("n_active_depts", _i32), ("max_expert_rows", _i32), ("n_invalid", _i32),
+                ("mean_expert_rows", _f32), ("imbalance_ratio", _f32),
+                ("loaded_weight_bytes", ctypes.c_uint64),
+                ("expert_rows", _i32 * MAX_EXPERTS)]
+
+
+STEP_STATS_BYTES = ctypes.sizeof(StepStats)
 
 
 class MoeError(RuntimeError):
@@ -122,6 +138,9 @@ def lib() -> ctypes.CDLL:
     L.moe_combine.restype = _i32
     L.moe_layer_decode.argtypes = [P(LayerDesc), P(Weights), _vp, _i32, _vp, _vp, _sz, _vp, _vp]
     L.moe_layer_decode.restype = _i32
+    L.moe_layer_decode_timed.argtypes = [P(LayerDesc), P(Weights), _vp, _i32, _vp, _vp, _sz, _vp,
+                                         _vp, _vp]
+    L.moe_layer_decode_timed.restype = _i32
     L.moe_status_string.argtypes = [_i32]
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_loaded_weight_bytes.argtypes = [P(LayerDesc), _i32, _i32]
@@ -332,10 +351,48 @@ def moe_combine(desc: LayerDesc, plan: Plan, row_out: torch.Tensor,
     _check(st, "moe_combine")
 
 
+def alloc_step_stats(device="cuda") -> torch.Tensor:
+    """Device storage for one moe_step_stats (8-byte aligned, torch-owned)."""
+    return torch.zeros(STEP_STATS_BYTES // 8, dtype=torch.int64, device=device)
+
+
+def step_stats_to_host(stats: torch.Tensor, n_experts: int) -> Dict[str, "object"]:
+    """Copy a moe_step_stats from the device (synchronising) into a dict;
+    expert_rows trimmed to the first n_experts entries."""
+    raw = stats.cpu().numpy().tobytes()
+    st = StepStats.from_buffer_copy(raw[:STEP_STATS_BYTES])
+    out = {name: getattr(st, name) for name, _ in StepStats._fields_ if name != "expert_rows"}
+    out["expert_rows"] = list(st.expert_rows[:n_experts])
+    return out
+
+
+def _stats_ptr(stats: Optional[torch.Tensor], device):
+    if stats is None:
+        return None
+    if stats.numel() * stats.element_size() < STEP_STATS_BYTES:
+        raise ValueError(f"stats needs {STEP_STATS_BYTES} bytes")
+    return _ptr(stats, "stats", device=device)
+
+
 def moe_layer_decode(desc: LayerDesc, weights: Dict[str, torch.Tensor], x: torch.Tensor,
-                     y: torch.Tensor, workspace: torch.Tensor, stage_events=None):
-    """y[T][d] = the layer on x[T][d].  stage_events: None or a sequence of
-    2 * N_STAGES torch.cuda.Event(enable_timing=True), each recorded once
+                     y: torch.Tensor, workspace: torch.Tensor, stats: Optional[torch.Tensor] = None):
+    """y[T][d] = the layer on x[T][d]; `stats` (alloc_step_stats()) receives
+    the step's routing statistics on the device when given."""
+    T, d = x.shape[0], desc.d_model
+    ws = _weights_struct(desc, weights)
+    wsp, wsn = _ws(desc, workspace)
+    st = lib().moe_layer_decode(
+        ctypes.byref(desc), ctypes.byref(ws), _ptr(x, "x", desc.torch_dtype, (T, d)), T,
+        _ptr(y, "y", desc.torch_dtype, (T, d)), wsp, wsn, _stats_ptr(stats, x.device),
+        _stream(x.device))
+    _check(st, "moe_layer_decode")
+
+
+def moe_layer_decode_timed(desc: LayerDesc, weights: Dict[str, torch.Tensor], x: torch.Tensor,
+                           y: torch.Tensor, workspace: torch.Tensor, stage_events=None,
+                           stats: Optional[torch.Tensor] = None):
+    """moe_layer_decode with kernel timing.  stage_events: None or a sequence
+    of 2 * N_STAGES torch.cuda.Event(enable_timing=True), each recorded once
     beforehand (so it exists); pairs (start, stop) bracket each stage's
     kernel exactly."""
     T, d = x.shape[0], desc.d_model
@@ -346,10 +403,11 @@ def moe_layer_decode(desc: LayerDesc, weights: Dict[str, torch.Tensor], x: torch
         if len(stage_events) != 2 * N_STAGES:
             raise ValueError(f"stage_events needs {2 * N_STAGES} events")
         ev = (_vp * (2 * N_STAGES))(*[e.cuda_event for e in stage_events])
-    st = lib().moe_layer_decode(
+    st = lib().moe_layer_decode_timed(
         ctypes.byref(desc), ctypes.byref(ws), _ptr(x, "x", desc.torch_dtype, (T, d)), T,
-        _ptr(y, "y", desc.torch_dtype, (T, d)), wsp, wsn, ev, _stream(x.device))
-    _check(st, "moe_layer_decode")
+        _ptr(y, "y", desc.torch_dtype, (T, d)), wsp, wsn, _stats_ptr(stats, x.device), ev,
+        _stream(x.device))
+    _check(st, "moe_layer_decode_timed")
 
 
 def plan_to_host(desc: LayerDesc, plan: Plan, workspace: torch.Tensor) -> Dict[str, "object"]:
@@ -396,10 +454,15 @@ class MoeLayer:
         self.device = torch.device(device)
         self.workspace = alloc_workspace(desc, self.device)
 
-    def __call__(self, x: torch.Tensor, y: Optional[torch.Tensor] = None, stage_events=None):
+    def __call__(self, x: torch.Tensor, y: Optional[torch.Tensor] = None, stage_events=None,
+                 stats: Optional[torch.Tensor] = None):
         if y is None:
             y = torch.empty_like(x)
-        moe_layer_decode(self.desc, self.weights, x, y, self.workspace, stage_events)
+        if stage_events is None:
+            moe_layer_decode(self.desc, self.weights, x, y, self.workspace, stats)
+        else:
+            moe_layer_decode_timed(self.desc, self.weights, x, y, self.workspace, stage_events,
+                                   stats)
         return y
 
     def plan(self, T: int) -> Dict[str, "object"]:

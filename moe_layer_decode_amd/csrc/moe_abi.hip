@@ -236,6 +236,8 @@ moe::PlanArgs plan_args(const moe_layer_desc& d, void* ws, int32_t T, const moe_
   pa.plan = p;
   pa.work = at<WorkDesc>(ws, L, R_WORK);
   pa.dwork = at<WorkDesc>(ws, L, R_DWORK);
+  pa.stats = nullptr;
+  pa.bytes_fixed = pa.bytes_expert = pa.bytes_dept = 0;
   return pa;
 }
 
@@ -303,11 +305,7 @@ moe::GemvConfig choose_config(const moe_layer_desc& d, int32_t T) {
     }
   }
   c.lpr = lpr;
-#ifdef MOE_FORCE_CG
-  c.col_groups = MOE_FORCE_CG;
-#else
   c.col_groups = 2;
-#endif
   return c;
 }
 
@@ -791,15 +789,17 @@ moe_status moe_combine(const moe_layer_desc* desc, const moe_plan* plan, const f
       moe::launch_combine(desc->act_dtype, a, y, static_cast<hipStream_t>(stream), nullptr));
 }
 
-moe_status moe_layer_decode(const moe_layer_desc* desc, const moe_weights* weights, const void* x,
-                            int32_t T, void* y, void* workspace, size_t ws_bytes,
-                            void* const* stage_events, void* stream) {
+moe_status moe_layer_decode_timed(const moe_layer_desc* desc, const moe_weights* weights,
+                                  const void* x, int32_t T, void* y, void* workspace,
+                                  size_t ws_bytes, moe_step_stats* stats,
+                                  void* const* stage_events, void* stream) {
   moe_status s = check_desc(desc);
   if (s != MOE_OK) return s;
   if ((s = check_tokens(desc, T)) != MOE_OK) return s;
   if (T == 0) return MOE_OK;
   if ((s = check_weights(desc, weights, true, true)) != MOE_OK) return s;
   if (!ok_ptr(x) || !ok_ptr(y)) return MOE_ERR_INVALID_ARG;
+  if (stats && ((uintptr_t)stats & 7u)) return MOE_ERR_INVALID_ARG;
   if ((s = check_ws(desc, workspace, ws_bytes)) != MOE_OK) return s;
   moe::KernelEvents ev[MOE_N_STAGES];
   if (stage_events) {
@@ -819,11 +819,18 @@ moe_status moe_layer_decode(const moe_layer_desc* desc, const moe_weights* weigh
   float* dept_out = desc->n_depts > 0 ? at<float>(workspace, L, R_DEPT_OUT) : nullptr;
   float* shared_out = desc->d_ff_shared > 0 ? at<float>(workspace, L, R_SHARED_OUT) : nullptr;
 
-  // router logits, then top-k + dispatch plan
+  // router logits, then top-k + dispatch plan (+ the step's statistics)
   const moe::RouteArgs ra =
       route_args(*desc, workspace, x, weights->w_router, weights->router_bias, T,
                  at<int32_t>(workspace, L, R_TOPK_IDS), at<float>(workspace, L, R_TOPK_W), nullptr);
-  const moe::PlanArgs pa = plan_args(*desc, workspace, T, plan);
+  moe::PlanArgs pa = plan_args(*desc, workspace, T, plan);
+  if (stats) {
+    const uint64_t b0 = moe_loaded_weight_bytes(desc, 0, 0);
+    pa.stats = stats;
+    pa.bytes_fixed = b0;
+    pa.bytes_expert = moe_loaded_weight_bytes(desc, 1, 0) - b0;
+    pa.bytes_dept = moe_loaded_weight_bytes(desc, 0, 1) - b0;
+  }
   if (moe::launch_route(router_dtype(*desc), ra, &pa, st, evp(MOE_STAGE_ROUTE)) != hipSuccess)
     return MOE_ERR_HIP;
 
@@ -850,6 +857,13 @@ moe_status moe_layer_decode(const moe_layer_desc* desc, const moe_weights* weigh
   if (moe::launch_combine(desc->act_dtype, ca, y, st, evp(MOE_STAGE_COMBINE)) != hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;
+}
+
+moe_status moe_layer_decode(const moe_layer_desc* desc, const moe_weights* weights, const void* x,
+                            int32_t T, void* y, void* workspace, size_t ws_bytes,
+                            moe_step_stats* stats, void* stream) {
+  return moe_layer_decode_timed(desc, weights, x, T, y, workspace, ws_bytes, stats, nullptr,
+                                stream);
 }
 
 int32_t moe_layer_kernel_count(const moe_layer_desc* desc, int32_t T) {

@@ -40,6 +40,10 @@ struct PlanArgs {
   moe_plan plan;
   WorkDesc* work;          // [2E] active experts: small groups from 0, large groups from E
   WorkDesc* dwork;         // [2m] the same for departments
+  moe_step_stats* stats;   // device stats of the step, or nullptr
+  // weight bytes one step streams: fixed (router, shared expert) plus per
+  // active expert and per active department (the host's byte count)
+  unsigned long long bytes_fixed, bytes_expert, bytes_dept;
 };
 
 struct RouteArgs {

@@ -867,6 +867,45 @@ __device__ void plan_phase_wave(PlanShared& s, const PlanArgs& pa, int lane) {
   }
 }
 
+// Routing statistics of the step (DeepSeekMoE Guide, "Sequence-Level and
+// Batch-Level Expert Routing Balance Metrics": the load balance factor is
+// the largest expert's token count over the mean count of the E routed
+// experts), by one wave from the plan's LDS tallies: rows per expert, and in
+// the department form the pair counts per department.  Both are final once
+// the plan phase has passed its barriers, and neither is written after them.
+__device__ void write_stats(const PlanShared& s, const PlanArgs& pa, int lane) {
+  moe_step_stats* st = pa.stats;
+  const int E = pa.E;
+  int rows = 0, act = 0, mx = 0, adep = 0;
+  for (int e = lane; e < E; e += kWave) {
+    const int c = s.cnt[e];
+    st->expert_rows[e] = c;
+    rows += c;
+    act += c > 0 ? 1 : 0;
+    mx = c > mx ? c : mx;
+  }
+  for (int J = lane; J < pa.m; J += kWave) adep += s.pw.dcnt[J] > 0 ? 1 : 0;
+  auto add = [](int a, int b) { return a + b; };
+  rows = wave_reduce_i(rows, add);
+  act = wave_reduce_i(act, add);
+  adep = wave_reduce_i(adep, add);
+  mx = wave_reduce_i(mx, [](int a, int b) { return a > b ? a : b; });
+  if (lane == 0) {
+    const float mean = (float)rows / (float)E;
+    st->n_tokens = pa.T;
+    st->n_assignments = rows;
+    st->n_active_experts = act;
+    st->n_active_depts = adep;
+    st->max_expert_rows = mx;
+    st->n_invalid = s.invalid;
+    st->mean_expert_rows = mean;
+    st->imbalance_ratio = rows > 0 ? (float)mx / mean : 0.f;
+    st->loaded_weight_bytes =
+        pa.bytes_fixed + (unsigned long long)act * pa.bytes_expert +
+        (unsigned long long)adep * pa.bytes_dept;
+  }
+}
+
 // Per-launch clearing of the plan's LDS tallies (before any top-k or count).
 __device__ __forceinline__ void plan_clear(PlanShared& s, int T, int E, int m) {
   for (int e = threadIdx.x; e < E; e += blockDim.x) s.cnt[e] = 0;
@@ -1066,6 +1105,9 @@ __global__ __launch_bounds__(kPlanThreads) void topk_plan_kernel(RouteArgs ra, P
   } else {
     plan_phase(s, pa, true);
   }
+  // the tallies the statistics read were final before the plan phase (rows
+  // per expert) or inside it, before its last barrier (pairs per department)
+  if (pa.stats && wid == 0) write_stats(s, pa, lane);
 }
 
 __global__ __launch_bounds__(kPlanThreads) void dispatch_kernel(const int32_t* ids, const float* w,
@@ -2122,6 +2164,25 @@ constexpr size_t expert_lds_bytes() {
   return a > b ? a : (b > 0 ? b : 16);
 }
 
+// One pass of a 64-row large-group tile over 16*NC tokens from tc, with the
+// LDS staging area of that width; out of line (CALL) or inlined.
+template <int NC, bool DUAL, bool CALL, typename T_>
+__device__ __forceinline__ void gu_wide_pass(const T_* __restrict__ Wg, const T_* __restrict__ Wu,
+                                             int d, int rows, int i0, const T_* xg, const T_* xu,
+                                             int in_rows, const Slot& sl, const int* grp_token,
+                                             int tc, const GuOut<T_>& o, int lane, int wid,
+                                             unsigned char* lds_raw) {
+  if constexpr (sizeof(T_) == 2) {
+    auto& lw = *reinterpret_cast<WideLds<NC, DUAL ? 2 : 1>*>(lds_raw);
+    if constexpr (CALL)
+      gu_wide_call<NC, DUAL>(Wg, Wu, d, rows, i0, xg, xu, in_rows, sl.r0, sl.n, grp_token, tc, o,
+                             lane, wid, lw);
+    else
+      gu_wide<NC, DUAL>(Wg, Wu, d, rows, i0, xg, xu, in_rows, sl.r0, sl.n, grp_token, tc, o, lane,
+                        wid, lw);
+  }
+}
+
 // NCMAX: 16-token chunks a large-group tile takes at once (2 only when a
 // group can exceed 16 rows, since the wider chunk costs registers).
 // XL: small groups read their activations from LDS (rows of at most kXLds).
@@ -2172,31 +2233,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     // large groups: the whole block on one 64-row tile, 16*NC tokens a pass
     const int i0 = tile * kWideRows;
     if (i0 >= F.rows) return;
-    constexpr int NX = DUAL ? 2 : 1;
     // out of line where large groups are rare (T <= 16, or the two-input
     // private transforms, whose groups seldom pass four rows)
     constexpr bool kCall = NCMAX == 1 || DUAL;
-#define MOE_GU_WIDE(NC_)                                                                      \
-  do {                                                                                       \
-    auto& lw = *reinterpret_cast<WideLds<NC_, NX>*>(lds_raw);                                \
-    if (kCall)                                                                               \
-      gu_wide_call<NC_, DUAL>(Wg, Wu, d, F.rows, i0, xg, xu, F.in_rows, sl.r0, sl.n,         \
-                              F.grp_token, tc, o, lane, wid, lw);                            \
-    else                                                                                     \
-      gu_wide<NC_, DUAL>(Wg, Wu, d, F.rows, i0, xg, xu, F.in_rows, sl.r0, sl.n, F.grp_token, \
-                         tc, o, lane, wid, lw);                                              \
-  } while (0)
 #pragma unroll 1
     for (int tc = 0; tc < sl.n; tc += 16 * NCMAX) {
       const int rem = sl.n - tc;
       if (NCMAX >= 4 && rem > 32)
-        MOE_GU_WIDE((NCMAX >= 4 ? 4 : 1));
+        gu_wide_pass<(NCMAX >= 4 ? 4 : 1), DUAL, kCall>(Wg, Wu, d, F.rows, i0, xg, xu, F.in_rows,
+                                                        sl, F.grp_token, tc, o, lane, wid, lds_raw);
       else if (NCMAX >= 2 && rem > 16)
-        MOE_GU_WIDE((NCMAX >= 2 ? 2 : 1));
+        gu_wide_pass<(NCMAX >= 2 ? 2 : 1), DUAL, kCall>(Wg, Wu, d, F.rows, i0, xg, xu, F.in_rows,
+                                                        sl, F.grp_token, tc, o, lane, wid, lds_raw);
       else
-        MOE_GU_WIDE(1);
+        gu_wide_pass<1, DUAL, kCall>(Wg, Wu, d, F.rows, i0, xg, xu, F.in_rows, sl, F.grp_token,
+                                     tc, o, lane, wid, lds_raw);
     }
-#undef MOE_GU_WIDE
   } else {
     // large groups, fp32 layers: the whole block on one 16-row tile
     const int i0 = tile * 16;

@@ -93,7 +93,7 @@ __all__ = [
     "deamoe_layer_two_stage", "deamoe_layer_precombined",
     "select_from_scores", "topk_select_grouped", "topk_select_strict", "silu", "cast_output", "SOFTMAX", "SIGMOID",
     "SOFTMAX_BIAS", "fp8_e4m3_decode", "fp8_dequantize", "dequantize_layer",
-    "loaded_weight_bytes_fp8",
+    "loaded_weight_bytes_fp8", "expert_load_stats",
 ]
 
 SOFTMAX, SIGMOID, SOFTMAX_BIAS = "softmax", "sigmoid", "softmax_bias"
@@ -637,6 +637,31 @@ def loaded_weight_bytes(ids, n_experts: int, d: int, d_ff: int, bytes_per_w: int
         g = n_experts // n_depts
         n += len({e // g for e in experts}) * 3 * d * d_ff_dept
     return n * bytes_per_w
+
+
+def expert_load_stats(ids, n_experts: int, n_depts: int = 0) -> Dict[str, object]:
+    """Routing load of one step ([DSMoE] "Sequence-Level and Batch-Level
+    Expert Routing Balance Metrics"; [MoEInf] "Expert load imbalance and
+    rank-level tail latency": count assignments per expert every step).
+    Tokens_j = assignments to routed expert j; the imbalance ratio is
+    max_j Tokens_j divided by the mean (1/N_r) sum_j Tokens_j over all N_r =
+    n_experts routed experts (0 when nothing is assigned).  Also the active
+    experts, and the departments holding at least one selected expert."""
+    ids = np.asarray(ids).reshape(-1)
+    counts = [0] * n_experts
+    for e in ids:
+        if 0 <= int(e) < n_experts:
+            counts[int(e)] += 1
+    total = sum(counts)
+    mean = total / n_experts
+    active = [e for e in range(n_experts) if counts[e] > 0]
+    depts = set()
+    if n_depts:
+        g = n_experts // n_depts
+        depts = {e // g for e in active}
+    return {"counts": counts, "n_assignments": total, "max": max(counts), "mean": mean,
+            "imbalance_ratio": (max(counts) / mean) if total else 0.0,
+            "n_active_experts": len(active), "n_active_depts": len(depts)}
 
 
 # ----------------------------------------------------------------------------

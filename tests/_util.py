@@ -77,12 +77,17 @@ def margins(sel: np.ndarray, k: int, n_depts: int = 0, k_dept: int = 0) -> np.nd
     return out
 
 
-def reference_ids(o_ids, o_sel, g_ids, k, n_depts: int = 0, k_dept: int = 0):
+def reference_ids(o_ids, o_sel, g_ids, k, n_depts: int = 0, k_dept: int = 0,
+                  allow_near: bool = False):
     """Oracle ids, except that on near-tie tokens (margin within 2 tau) the
     HIP path's choice stands.  Returns (ids, near_tie_mask); asserts that
-    every other token agrees exactly."""
+    every other token agrees exactly.  Unless allow_near, asserts that there
+    is no near-tie token at all, so the ids are the oracle's bit for bit (the
+    committed seeds of the listed layer shapes have none up to 32 tokens)."""
     tau = TAU * np.maximum(1.0, np.abs(o_sel).max(axis=1))
     near = margins(o_sel, k, n_depts, k_dept) <= 2 * tau
+    assert allow_near or not near.any(), \
+        f"near-tie tokens {np.nonzero(near)[0].tolist()} where none is expected"
     mism = np.any(o_ids != g_ids, axis=1)
     bad = mism & ~near
     assert not bad.any(), f"top-k ids differ on tokens {np.nonzero(bad)[0].tolist()} outside near-ties"
@@ -114,3 +119,11 @@ def assert_close(y_gpu: np.ndarray, y_ref: np.ndarray, dtype: str, what: str = "
         rms_err = np.sqrt(np.mean(err ** 2))
         assert rms_err <= rms_tol * rms_ref + 1e-30, f"{what}: rms err {rms_err:.3e} > {rms_tol} * rms ref {rms_ref:.3e}"
     return emax, ref_max
+
+
+def spread_tokens(T: int, n: int = 8):
+    """Every token when T <= 4, else n tokens spread evenly over [0, T)
+    with the first and the last among them."""
+    if T <= 4:
+        return list(range(T))
+    return sorted({int(round(v)) for v in np.linspace(0, T - 1, min(n, T))})

@@ -278,3 +278,37 @@ def test_layer_kernel_count(lib):
     fac = _desc(n_experts=32, top_k=6, d_ff=256, n_depts=4, d_ff_dept=256,
                 dept_form="factorised")
     assert M.moe_layer_kernel_count(fac, 3) == 8
+
+
+def test_step_stats_layout_matches_the_header(tmp_path):
+    """The binding's StepStats has the C struct's size and field offsets
+    (compiled from include/moe_decode.h with the host C compiler)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    fields = [f for f, _ in M.StepStats._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"moe_decode.h\"\n"
+                   "int main(void) {\n  printf(\"%zu\\n\", sizeof(moe_step_stats));\n"
+                   + "".join(f"  printf(\"%zu\\n\", offsetof(moe_step_stats, {f}));\n"
+                             for f in fields)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    out = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    assert out[0] == M.STEP_STATS_BYTES
+    assert out[1:] == [getattr(M.StepStats, f).offset for f in fields]
+
+
+def test_decode_rejects_a_misaligned_stats_pointer(lib):
+    d = _desc()
+    W = M.Weights(w_router=256, w_gate=256, w_up=256, w_down=256)
+    ws = M.moe_workspace_bytes(d)
+    assert lib.moe_layer_decode(ctypes.byref(d), ctypes.byref(W), 256, 1, 512, 4096, ws,
+                                4100, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_layer_decode_timed(ctypes.byref(d), ctypes.byref(W), 256, 1, 512, 4096, ws,
+                                      4100, None, None) == M.MOE_ERR_INVALID_ARG

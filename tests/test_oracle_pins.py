@@ -178,6 +178,57 @@ def test_sigmoid_bias_routing():
     assert not np.array_equal(np.sort(ids0, 1), np.sort(ids, 1))
 
 
+def test_router_logits_unit_tokens_read_router_columns():
+    """[DeaMoE] Eq. (2): l = W_r x.  A one-hot token x = e_c picks column c of
+    W_r exactly, so l[:, e] = W_r[e, c] for every expert: a transposed,
+    scaled, offset, row- or column-permuted router fails."""
+    rng = _rng(21)
+    E, d = 6, 10
+    wr = rng.normal(0, 1, (E, d)).astype(np.float32)
+    x = np.eye(d, dtype=np.float32)           # token c = e_c
+    l = O.router_logits(x, wr)
+    assert l.shape == (d, E) and l.dtype == np.float32
+    for c in range(d):
+        for e in range(E):
+            assert l[c, e] == wr[e, c], (c, e)
+    # a scaled one-hot token scales exactly (powers of two)
+    l2 = O.router_logits(4.0 * x[3:4], wr)
+    assert np.array_equal(l2[0], 4.0 * wr[:, 3])
+
+
+def test_router_logits_small_integers_hand_summed():
+    """Integer tokens and router rows give integer logits, every one summed
+    by hand here: x = [[1, 2, 3], [-1, 0, 4]], W_r = [[1, 0, 0], [0, 1, 1],
+    [2, -1, 3], [0, 0, -2]]."""
+    x = np.array([[1, 2, 3], [-1, 0, 4]], np.float32)
+    wr = np.array([[1, 0, 0], [0, 1, 1], [2, -1, 3], [0, 0, -2]], np.float32)
+    want = np.array([[1, 2 + 3, 2 - 2 + 9, -6],
+                     [-1, 0 + 4, -2 + 0 + 12, -8]], np.float32)
+    assert np.array_equal(O.router_logits(x, wr), want)
+    # and the logits are exactly the fp32 rounding of the exact sum: a sum
+    # that cancels to 1 from 2^24-scale terms loses nothing in fp64
+    xb = np.array([[16777216.0, 1.0, -16777216.0]], np.float32)
+    wb = np.ones((1, 3), np.float32)
+    assert O.router_logits(xb, wb)[0, 0] == 1.0
+
+
+def test_sigmoid_not_renormalised_is_expit():
+    """Sigmoid mode without renormalisation: each selected weight is the
+    expert's own sigmoid score (scipy's expit of the logit), times the
+    route scale; selection still ranks sigmoid + bias."""
+    rng = _rng(22)
+    x = rng.normal(0, 1, (3, 48)).astype(np.float32)
+    wr = rng.normal(0, 0.1, (12, 48)).astype(np.float32)
+    b = rng.uniform(-0.1, 0.1, 12).astype(np.float32)
+    ids, w, _, l32 = O.route(x, wr, 4, O.SIGMOID, b, renormalize=False, route_scale=1.5)
+    for t in range(3):
+        s = scipy.special.expit(l32[t].astype(np.float64))
+        np.testing.assert_allclose(w[t], 1.5 * s[ids[t]], rtol=1e-13)
+        assert w[t].sum() != pytest.approx(1.5)   # not renormalised
+        ranked = np.lexsort((np.arange(12), -(s.astype(np.float32) + b)))
+        assert ids[t].tolist() == ranked[:4].tolist()
+
+
 def test_zero_input_gives_zero_output_and_tied_logits():
     rng = _rng(5)
     w = _rand_layer(rng, 16, 6, 8, Is=8)
@@ -762,3 +813,42 @@ def test_fp8_loaded_bytes_of_a_deepseek_v3_expert():
                                     n_depts=2, d_ff_dept=8, d_ff_shared=8)
     mat3 = lambda r: 3 * 16 * r + 4 * (2 * r + 16)  # noqa: E731
     assert two == 12 * 16 * 2 + 2 * mat3(4) + mat3(8) + 2 * mat3(8)
+
+
+# ---------------------------------------------------------------------------
+# Per-step routing load ("Sequence-Level and Batch-Level Expert Routing
+# Balance Metrics": max expert count over the mean count of the routed
+# experts)
+# ---------------------------------------------------------------------------
+
+def test_load_stats_of_the_worked_example():
+    """The worked example's groups hold 3, 2, 2 and 1 rows: the mean over the
+    four routed experts is 2 and the largest is 3, so the ratio is 1.5."""
+    g = _golden()
+    st = O.expert_load_stats(np.array(g["topk_ids"]), g["n_experts"])
+    assert st["counts"] == g["expected"]["group_rows"] == [3, 2, 2, 1]
+    assert st["n_assignments"] == 8 and st["mean"] == 2.0 and st["max"] == 3
+    assert st["imbalance_ratio"] == 1.5
+    assert st["n_active_experts"] == 4
+
+
+def test_load_stats_closed_forms():
+    # perfectly balanced: every expert once -> ratio 1
+    E = 16
+    st = O.expert_load_stats(np.arange(E).reshape(4, 4), E)
+    assert st["imbalance_ratio"] == 1.0 and st["n_active_experts"] == E
+    # one hot expert taking every assignment -> ratio N_r (mean = total / N_r)
+    st = O.expert_load_stats(np.full((8, 1), 5), E)
+    assert st["imbalance_ratio"] == E and st["counts"][5] == 8
+    assert st["n_active_experts"] == 1
+    # the mean divides by every routed expert, active or not: 2 of 8 used
+    st = O.expert_load_stats(np.array([[0, 1], [0, 1], [0, 2]]), 8)
+    assert st["mean"] == 6 / 8 and st["imbalance_ratio"] == 3 / (6 / 8)
+    # departments of 4: experts 0..3 -> department 0, 4..7 -> 1
+    st = O.expert_load_stats(np.array([[0, 5], [1, 3]]), 8, n_depts=2)
+    assert st["n_active_depts"] == 2
+    st = O.expert_load_stats(np.array([[0, 2], [1, 3]]), 8, n_depts=2)
+    assert st["n_active_depts"] == 1
+    # nothing assigned (ids outside [0, E) are dropped)
+    st = O.expert_load_stats(np.array([[-1, 9]]), 8)
+    assert st["imbalance_ratio"] == 0.0 and st["n_assignments"] == 0
