@@ -348,6 +348,30 @@ moe_status moe_layer_decode_timed(const moe_layer_desc* desc, const moe_weights*
 /* Static text for a status code. */
 const char* moe_status_string(moe_status status);
 
+/* Allocation-free decode step, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): moe_layer_decode with no workspace argument.  Its
+ * intermediates live in a fixed per-GPU scratch array of
+ * MOE_NOALLOC_SCRATCH_BYTES that the library holds from its first use on a
+ * GPU until the process ends; the call allocates nothing (no hipMalloc, no
+ * hipFree, no allocating library routine).  The caller passes x, y and the
+ * optional device stats as for moe_layer_decode.
+ *   - The scratch is laid out for exactly T tokens (desc->max_tokens only
+ *     bounds T); MOE_ERR_UNSUPPORTED when that layout exceeds
+ *     MOE_NOALLOC_SCRATCH_BYTES (moe_workspace_bytes of the descriptor with
+ *     max_tokens = T tells the size), before anything is launched.
+ *   - The first call on each GPU looks up that GPU's copy of the array (its
+ *     device address) and clears its counter region with a small kernel on
+ *     `stream`; later calls launch only the layer's kernels.
+ *   - Every call on one GPU shares that GPU's array and leaves its contents
+ *     behind: calls that overlap on one GPU (different streams, or threads
+ *     without ordering) race and give undefined results; order them on one
+ *     stream. */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+moe_status moe_layer_decode_noalloc(const moe_layer_desc* desc, const moe_weights* weights,
+                                    const void* x, int32_t T, void* y, moe_step_stats* stats,
+                                    void* stream);
+
 /* Host-only: the number of kernels moe_layer_decode launches for T tokens
  * (0 for T = 0, -1 for an invalid descriptor or T): 5 (route, top-k + plan,
  * gate/up, down, combine); 4 where the down projection writes y itself (bf16

@@ -21,7 +21,7 @@ __all__ = [
     "MoeError", "LayerDesc", "Weights", "Plan", "layer_desc", "lib", "lib_path",
     "moe_workspace_bytes", "moe_workspace_init", "moe_validate_desc", "moe_route", "moe_dispatch",
     "moe_expert_ffn", "moe_combine", "moe_layer_decode", "moe_layer_decode_timed",
-    "moe_status_string", "StepStats", "STEP_STATS_BYTES", "alloc_step_stats", "step_stats_to_host",
+    "moe_layer_decode_noalloc", "NOALLOC_SCRATCH_BYTES", "moe_status_string", "StepStats", "STEP_STATS_BYTES", "alloc_step_stats", "step_stats_to_host",
     "moe_loaded_weight_bytes", "moe_stream_read", "moe_layer_kernel_count", "alloc_workspace",
     "plan_to_host", "MoeLayer",
     "MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE",
@@ -42,7 +42,7 @@ STAGE_NAMES = ("route", "dispatch", "gateup", "down", "combine")
 EXPORTED_SYMBOLS = (
     "moe_workspace_bytes", "moe_workspace_init", "moe_validate_desc", "moe_plan_from_workspace", "moe_route",
     "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_layer_decode", "moe_layer_decode_timed",
-    "moe_status_string", "moe_loaded_weight_bytes", "moe_stream_read", "moe_layer_kernel_count",
+    "moe_layer_decode_noalloc", "moe_status_string", "moe_loaded_weight_bytes", "moe_stream_read", "moe_layer_kernel_count",
 )
 
 _i32, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -92,6 +92,7 @@ class StepStats(ctypes.Structure):
 
 
 STEP_STATS_BYTES = ctypes.sizeof(StepStats)
+NOALLOC_SCRATCH_BYTES = 32 << 20   # MOE_NOALLOC_SCRATCH_BYTES
 
 
 class MoeError(RuntimeError):
@@ -141,6 +142,8 @@ def lib() -> ctypes.CDLL:
     L.moe_layer_decode_timed.argtypes = [P(LayerDesc), P(Weights), _vp, _i32, _vp, _vp, _sz, _vp,
                                          _vp, _vp]
     L.moe_layer_decode_timed.restype = _i32
+    L.moe_layer_decode_noalloc.argtypes = [P(LayerDesc), P(Weights), _vp, _i32, _vp, _vp, _vp]
+    L.moe_layer_decode_noalloc.restype = _i32
     L.moe_status_string.argtypes = [_i32]
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_loaded_weight_bytes.argtypes = [P(LayerDesc), _i32, _i32]
@@ -408,6 +411,19 @@ def moe_layer_decode_timed(desc: LayerDesc, weights: Dict[str, torch.Tensor], x:
         _ptr(y, "y", desc.torch_dtype, (T, d)), wsp, wsn, _stats_ptr(stats, x.device), ev,
         _stream(x.device))
     _check(st, "moe_layer_decode_timed")
+
+
+def moe_layer_decode_noalloc(desc: LayerDesc, weights: Dict[str, torch.Tensor], x: torch.Tensor,
+                             y: torch.Tensor, stats: Optional[torch.Tensor] = None):
+    """moe_layer_decode without a workspace: the library's fixed per-GPU
+    scratch holds the intermediates (no device allocation in the call).
+    Calls that overlap on one GPU race; order them on one stream."""
+    T, d = x.shape[0], desc.d_model
+    ws = _weights_struct(desc, weights)
+    st = lib().moe_layer_decode_noalloc(
+        ctypes.byref(desc), ctypes.byref(ws), _ptr(x, "x", desc.torch_dtype, (T, d)), T,
+        _ptr(y, "y", desc.torch_dtype, (T, d)), _stats_ptr(stats, x.device), _stream(x.device))
+    _check(st, "moe_layer_decode_noalloc")
 
 
 def plan_to_host(desc: LayerDesc, plan: Plan, workspace: torch.Tensor) -> Dict[str, "object"]:

@@ -6,7 +6,17 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "moe_internal.h"
+
+// Scratch of the allocation-free entry point: one fixed array per GPU, held
+// by the loaded module until the process ends.  In host code this name only
+// stands for the symbol; the device address of each GPU's copy comes from
+// hipGetSymbolAddress (see noalloc_scratch below) and is the only address
+// ever handed to a kernel or copy.
+constexpr size_t kNoAllocScratchBytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -672,6 +682,38 @@ bool down_combine_args(const moe_layer_desc& d, const moe_weights& w, const moe_
   return true;
 }
 
+// Per-device address of `scratch`, looked up once per device with that
+// device current (the first moe_layer_decode_noalloc call on it), together
+// with a one-time clearing of the workspace's counter region on the caller's
+// stream (a fill kernel, no hipMemset).
+constexpr int kMaxScratchDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxScratchDevices];
+
+moe_status noalloc_scratch(hipStream_t st, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxScratchDevices) return MOE_ERR_UNSUPPORTED;
+  ScratchSlot& sl = g_scratch[dev];
+  std::call_once(sl.once, [&] {
+    void* p = nullptr;
+    sl.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (sl.err == hipSuccess && p == nullptr) sl.err = hipErrorInvalidSymbol;
+    // counters region: at the start of every layout, never longer than
+    // (16 + d/8) words; d is not known yet, so clear the first 64 KiB
+    if (sl.err == hipSuccess)
+      sl.err = moe::launch_zero(static_cast<unsigned int*>(p), (64u << 10) / 4, st);
+    if (sl.err == hipSuccess) sl.ptr = p;
+  });
+  if (sl.err != hipSuccess || !sl.ptr) return MOE_ERR_HIP;
+  *out = sl.ptr;
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -863,6 +905,25 @@ moe_status moe_layer_decode(const moe_layer_desc* desc, const moe_weights* weigh
                             int32_t T, void* y, void* workspace, size_t ws_bytes,
                             moe_step_stats* stats, void* stream) {
   return moe_layer_decode_timed(desc, weights, x, T, y, workspace, ws_bytes, stats, nullptr,
+                                stream);
+}
+
+moe_status moe_layer_decode_noalloc(const moe_layer_desc* desc, const moe_weights* weights,
+                                    const void* x, int32_t T, void* y, moe_step_stats* stats,
+                                    void* stream) {
+  moe_status s = check_desc(desc);
+  if (s != MOE_OK) return s;
+  if ((s = check_tokens(desc, T)) != MOE_OK) return s;
+  if (T == 0) return MOE_OK;
+  // the workspace is laid out for exactly T tokens (same kernels and grids
+  // as any max_tokens >= T), so the scratch holds the largest step it can
+  moe_layer_desc dt = *desc;
+  dt.max_tokens = T;
+  if (layout_of(dt).total > kNoAllocScratchBytes) return MOE_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((s = noalloc_scratch(st, &ws)) != MOE_OK) return s;
+  return moe_layer_decode_timed(&dt, weights, x, T, y, ws, kNoAllocScratchBytes, stats, nullptr,
                                 stream);
 }
 

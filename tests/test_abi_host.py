@@ -312,3 +312,26 @@ def test_decode_rejects_a_misaligned_stats_pointer(lib):
                                 4100, None) == M.MOE_ERR_INVALID_ARG
     assert lib.moe_layer_decode_timed(ctypes.byref(d), ctypes.byref(W), 256, 1, 512, 4096, ws,
                                       4100, None, None) == M.MOE_ERR_INVALID_ARG
+
+
+def test_noalloc_refuses_steps_beyond_its_scratch(lib):
+    """The allocation-free entry point lays its scratch out for exactly T
+    tokens and refuses, on the host before any HIP call, a step that does
+    not fit MOE_NOALLOC_SCRATCH_BYTES (DeepSeek-V3 geometry at 128 tokens
+    needs about 42 MiB); invalid descriptors and T are refused first."""
+    big = _desc(d_model=7168, n_experts=256, d_ff=2048, d_ff_shared=2048, score="sigmoid",
+                max_tokens=128)
+    assert M.moe_workspace_bytes(big) > M.NOALLOC_SCRATCH_BYTES
+    fits = _desc(d_model=7168, n_experts=256, d_ff=2048, d_ff_shared=2048, score="sigmoid",
+                 max_tokens=32)
+    assert M.moe_workspace_bytes(fits) <= M.NOALLOC_SCRATCH_BYTES
+    W = M.Weights(w_router=256, w_gate=256, w_up=256, w_down=256, ws_gate=256, ws_up=256,
+                  ws_down=256)
+    assert lib.moe_layer_decode_noalloc(ctypes.byref(big), ctypes.byref(W), 256, 128, 512, None,
+                                        None) == M.MOE_ERR_UNSUPPORTED
+    assert lib.moe_layer_decode_noalloc(ctypes.byref(big), ctypes.byref(W), 256, 129, 512, None,
+                                        None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_layer_decode_noalloc(ctypes.byref(_desc(d_model=7)), ctypes.byref(W), 256, 1,
+                                        512, None, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_layer_decode_noalloc(ctypes.byref(big), ctypes.byref(W), 256, 0, 512, None,
+                                        None) == M.MOE_OK
