@@ -8,7 +8,10 @@
 //                     becomes expert-specific matrices": group by expert, keep
 //                     token ids and the inverse map), plus one work descriptor
 //                     per active expert and department
-//   dispatch_kernel   the plan alone, for caller-given ids
+//   topk_token_kernel the top-k of larger batches (or of more than 256
+//                     experts), one wave per token across many blocks
+//   dispatch_kernel   the plan alone, from caller-given ids or from the ids
+//                     topk_token_kernel wrote
 //   gateup_kernel     h = SiLU(W_gate x) * (W_up x) per dispatched row (Eq. (1))
 //   down_kernel       o = W_down h per dispatched row (Eq. (1))
 //   combine_kernel    y_t = sum_j p_j o_{t,j} + department + shared terms (Eq. (3))
@@ -178,42 +181,6 @@ __device__ __forceinline__ float route_aux(const RouteArgs& p, float l) {
   return p.score_fn == MOE_SCORE_SIGMOID ? 1.0f / (1.0f + expf(-l)) : l;
 }
 
-// Logits of tokens [t0, t0 + tc): the K-split partial planes added in plane
-// order (planes past ksplit add nothing), then the selection score and its
-// key, staged in LDS; the scores go to sel_out when asked for.  Each thread
-// requests NU entries' planes before the first add waits.
-template <int KS>
-__device__ void stage_scores_ks(const RouteArgs& p, int t0, int tc, PlanShared& s) {
-  constexpr int NU = KS >= 8 ? 4 : KS >= 4 ? 6 : 8;
-  const int n = tc * p.E, nth = blockDim.x, E = p.E;
-  const float* src = p.logits + (size_t)t0 * E;
-  const size_t plane = (size_t)p.T * E;
-#pragma unroll 1
-  for (int j0 = threadIdx.x; j0 < n; j0 += nth * NU) {
-    float v[NU][KS], b[NU];
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int j = min(j0 + u * nth, n - 1);
-#pragma unroll
-      for (int q = 0; q < KS; ++q) v[u][q] = src[(size_t)min(q, p.ksplit - 1) * plane + j];
-      b[u] = p.bias ? p.bias[j % E] : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int j = j0 + u * nth;
-      if (j < n) {
-        float l = 0.f;
-#pragma unroll
-        for (int q = 0; q < KS; ++q) l += q < p.ksplit ? v[u][q] : 0.f;
-        const float sc = p.score_fn == MOE_SCORE_SOFTMAX ? l : route_aux(p, l) + b[u];
-        if (p.sel_out) p.sel_out[(size_t)t0 * E + j] = sc;
-        s.tk.lg[j] = l;
-        s.tk.key[j] = score_key(sc);
-      }
-    }
-  }
-}
-
 // One token's row by its own wave (lane l: experts l, l+64, ...), for
 // layers with few experts per lane: the planes of all NPL entries are
 // requested before the first add waits, and no block barrier is needed.  The
@@ -223,43 +190,38 @@ template <int NPL, bool GROUPED>
 __device__ void stage_token(const RouteArgs& p, int t, int row, int lane, PlanShared& s,
                             uint32_t (&key)[NPL]) {
   const int E = p.E;
-  float v[kMaxRouteSplit][NPL], b[NPL];
+  // planes of experts in chunks of CH, each chunk's partial-logit loads all
+  // requested before its first add waits (a layer with few experts is one chunk)
+  constexpr int CH = NPL < 4 ? NPL : 4;
 #pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    const int e = min(lane + kWave * i, E - 1);
-    b[i] = p.bias ? p.bias[e] : 0.f;
+  for (int i0 = 0; i0 < NPL; i0 += CH) {
+    float v[kMaxRouteSplit][CH], b[CH];
 #pragma unroll
-    for (int q = 0; q < kMaxRouteSplit; ++q)
-      v[q][i] = p.logits[((size_t)min(q, p.ksplit - 1) * p.T + t) * E + e];
-  }
+    for (int i = 0; i < CH; ++i) {
+      const int e = min(lane + kWave * (i0 + i), E - 1);
+      b[i] = p.bias ? p.bias[e] : 0.f;
 #pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    const int e = lane + kWave * i;
-    key[i] = 0u;
-    if (e < E) {
-      float l = 0.f;
+      for (int q = 0; q < kMaxRouteSplit; ++q)
+        v[q][i] = q < p.ksplit ? p.logits[((size_t)q * p.T + t) * E + e] : 0.f;
+    }
 #pragma unroll
-      for (int q = 0; q < kMaxRouteSplit; ++q) l += q < p.ksplit ? v[q][i] : 0.f;
-      const float sc = p.score_fn == MOE_SCORE_SOFTMAX ? l : route_aux(p, l) + b[i];
-      if (p.sel_out) p.sel_out[(size_t)t * E + e] = sc;
-      s.tk.lg[row + e] = l;
-      key[i] = score_key(sc);
-      if (GROUPED) s.tk.key[row + e] = key[i];
+    for (int i = 0; i < CH; ++i) {
+      const int e = lane + kWave * (i0 + i);
+      key[i0 + i] = 0u;
+      if (e < E) {
+        float l = 0.f;
+#pragma unroll
+        for (int q = 0; q < kMaxRouteSplit; ++q) l += q < p.ksplit ? v[q][i] : 0.f;
+        const float sc = p.score_fn == MOE_SCORE_SOFTMAX ? l : route_aux(p, l) + b[i];
+        if (p.sel_out) p.sel_out[(size_t)t * E + e] = sc;
+        s.tk.lg[row + e] = l;
+        key[i0 + i] = score_key(sc);
+        if (GROUPED) s.tk.key[row + e] = key[i0 + i];
+      }
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
-}
-
-__device__ void stage_scores(const RouteArgs& p, int t0, int tc, PlanShared& s) {
-  if (p.ksplit > 4)
-    stage_scores_ks<kMaxRouteSplit>(p, t0, tc, s);
-  else if (p.ksplit > 2)
-    stage_scores_ks<4>(p, t0, tc, s);
-  else if (p.ksplit > 1)
-    stage_scores_ks<2>(p, t0, tc, s);
-  else
-    stage_scores_ks<1>(p, t0, tc, s);
 }
 
 // The k-th largest key of the wave (NP keys per lane; key 0 lies below every
@@ -374,7 +336,7 @@ __device__ __forceinline__ void select_extract(uint32_t (&key)[NP], int k, int l
 // weights.
 // `key` holds the row's keys on entry (lane l, plane i: expert l + 64 i; 0
 // past the last expert); the logits are read from the staged row.
-template <int NPL, bool GROUPED>
+template <int NPL, bool GROUPED, bool TALLY = true>
 __device__ void topk_token(const RouteArgs& p, int t, int row, int lane, PlanShared& s,
                            uint32_t (&key)[NPL]) {
   const int k = p.k, E = p.E, wid = threadIdx.x >> 6;
@@ -580,13 +542,15 @@ __device__ void topk_token(const RouteArgs& p, int t, int row, int lane, PlanSha
     const int a = t * p.k + lane;
     if (p.ids_out) p.ids_out[a] = my_id;
     if (p.w_out) p.w_out[a] = w;
-    s.ids[a] = my_id;
-    s.w[a] = w;
-    // the plan's tallies (the k experts of a token are distinct)
-    atomicAdd(&s.cnt[my_id], 1);
-    const int nwt = rank_mask_words(p.T, E);
-    if (nwt > 0) atomicOr(&s.tmask[my_id * nwt + (t >> 6)], 1ull << (t & 63));
-    if (p.m > 0) s.flag[t * p.m + my_id / (E / p.m)] = 1;
+    if constexpr (TALLY) {
+      s.ids[a] = my_id;
+      s.w[a] = w;
+      // the plan's tallies (the k experts of a token are distinct)
+      atomicAdd(&s.cnt[my_id], 1);
+      const int nwt = rank_mask_words(p.T, E);
+      if (nwt > 0) atomicOr(&s.tmask[my_id * nwt + (t >> 6)], 1ull << (t & 63));
+      if (p.m > 0) s.flag[t * p.m + my_id / (E / p.m)] = 1;
+    }
   }
 }
 
@@ -1051,53 +1015,23 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(RouteArgs ra) {
   }
 }
 
-// One block: per chunk of tokens, the whole block stages the logits and keys,
-// then one wave per token selects its top-k; then (do_plan) the dispatch plan.
+// One block for batches of at most one token per wave and at most 256
+// experts: each wave selects its token's top-k, then (do_plan) the block
+// builds the dispatch plan from the LDS tallies.
 template <int NPL, bool GROUPED>
 __global__ __launch_bounds__(kPlanThreads) void topk_plan_kernel(RouteArgs ra, PlanArgs pa,
                                                                  int do_plan) {
   __shared__ PlanShared s;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   plan_clear(s, ra.T, ra.E, ra.m);
-  if constexpr (NPL <= 4) {
-    // up to 256 experts: each wave stages its own token in its own row
-    static_assert(kPlanWaves * 4 * kWave <= kTopkBuf, "a row per wave");
-    if (ra.T <= nw) {
-      // one token per wave: its logits are requested before the barrier
-      // that completes the clearing (the staged row is not a tally)
-      uint32_t key[NPL];
-      if (wid < ra.T) stage_token<NPL, GROUPED>(ra, wid, wid * ra.E, lane, s, key);
-      __syncthreads();  // the tallies are clear
-      if (wid < ra.T) topk_token<NPL, GROUPED>(ra, wid, wid * ra.E, lane, s, key);
-    } else {
-      __syncthreads();  // the tallies are clear
-      for (int t = wid; t < ra.T; t += nw) {
-        uint32_t key[NPL];
-        stage_token<NPL, GROUPED>(ra, t, wid * ra.E, lane, s, key);
-        topk_token<NPL, GROUPED>(ra, t, wid * ra.E, lane, s, key);
-      }
-    }
-  } else {
-    // many experts: the whole block stages chunks of tokens (the first
-    // barrier also orders the clearing before the tallies)
-    const int tcap = kTopkBuf / ra.E;  // E <= MOE_MAX_EXPERTS < kTopkBuf
-    for (int t0 = 0; t0 < ra.T; t0 += tcap) {
-      const int tc = min(tcap, ra.T - t0);
-      if (t0 > 0) __syncthreads();  // the previous chunk's waves are done with the staging
-      stage_scores(ra, t0, tc, s);
-      __syncthreads();
-      for (int t = t0 + wid; t < t0 + tc; t += nw) {
-        const int row = (t - t0) * ra.E;
-        uint32_t key[NPL];
-#pragma unroll
-        for (int i = 0; i < NPL; ++i) {
-          const int e = lane + kWave * i;
-          key[i] = e < ra.E ? s.tk.key[row + e] : 0u;
-        }
-        topk_token<NPL, GROUPED>(ra, t, row, lane, s, key);
-      }
-    }
-  }
+  // up to 256 experts and one token per wave: each wave stages its own token
+  // in its own row, its logits requested before the barrier that completes
+  // the clearing (the staged row is not a tally)
+  static_assert(NPL <= 4 && kPlanWaves * 4 * kWave <= kTopkBuf, "a row per wave");
+  uint32_t key[NPL];
+  if (wid < ra.T) stage_token<NPL, GROUPED>(ra, wid, wid * ra.E, lane, s, key);
+  __syncthreads();  // the tallies are clear
+  if (wid < ra.T) topk_token<NPL, GROUPED>(ra, wid, wid * ra.E, lane, s, key);
   if (!do_plan) return;
   __syncthreads();
   if (pa.m <= 0 && pa.E <= kWavePlanPer * kWave && rank_mask_words(pa.T, pa.E) > 0) {
@@ -1110,25 +1044,94 @@ __global__ __launch_bounds__(kPlanThreads) void topk_plan_kernel(RouteArgs ra, P
   if (pa.stats && wid == 0) write_stats(s, pa, lane);
 }
 
+// Top-k of many tokens at once, the ids and weights written to ra.ids_out /
+// ra.w_out (and the ranked scores to ra.sel_out).  Serves batches past one
+// token per wave of the single plan block, and layers with more than 256
+// experts: the tokens then run side by side across the chip and a separate
+// plan launch follows.  Up to 256 experts: four tokens per block, each wave
+// stages and selects its own.  More experts: one token per block, whose four
+// waves stage its row together (each thread a few experts, every partial
+// plane requested at once), then one wave selects.
+template <int NPL, bool GROUPED>
+__global__ __launch_bounds__(kThreads) void topk_token_kernel(RouteArgs ra) {
+  __shared__ PlanShared s;  // only the staging rows and the per-wave lists are used
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  uint32_t key[NPL];
+  if constexpr (NPL <= 4) {
+    const int t = blockIdx.x * kWaves + wid;
+    if (t >= ra.T) return;
+    stage_token<NPL, GROUPED>(ra, t, wid * ra.E, lane, s, key);
+    topk_token<NPL, GROUPED, false>(ra, t, wid * ra.E, lane, s, key);
+  } else {
+    const int t = blockIdx.x, E = ra.E;
+    constexpr int PER = (NPL * kWave + kThreads - 1) / kThreads;  // experts per thread
+    float v[PER][kMaxRouteSplit], b[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = min((int)threadIdx.x + u * kThreads, E - 1);
+      b[u] = ra.bias ? ra.bias[e] : 0.f;
+#pragma unroll
+      for (int q = 0; q < kMaxRouteSplit; ++q)
+        v[u][q] = q < ra.ksplit ? ra.logits[((size_t)q * ra.T + t) * E + e] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = threadIdx.x + u * kThreads;
+      if (e < E) {
+        float l = 0.f;
+#pragma unroll
+        for (int q = 0; q < kMaxRouteSplit; ++q) l += q < ra.ksplit ? v[u][q] : 0.f;
+        const float sc = ra.score_fn == MOE_SCORE_SOFTMAX ? l : route_aux(ra, l) + b[u];
+        if (ra.sel_out) ra.sel_out[(size_t)t * E + e] = sc;
+        s.tk.lg[e] = l;
+        s.tk.key[e] = score_key(sc);
+      }
+    }
+    __syncthreads();
+    if (wid != 0) return;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int e = lane + kWave * i;
+      key[i] = e < E ? s.tk.key[e] : 0u;
+    }
+    topk_token<NPL, GROUPED, false>(ra, t, 0, lane, s, key);
+  }
+}
+
+// The dispatch plan from caller- or router-given ids and weights.  DISTINCT:
+// every id is a valid expert and a token's ids are distinct (the router's
+// top-k), so each expert's tokens are kept as bits and an assignment's row
+// is a popcount; otherwise ids may repeat within a token or fall outside
+// [0, E) (dropped and counted), and ranks come from a scan.
+template <bool DISTINCT>
 __global__ __launch_bounds__(kPlanThreads) void dispatch_kernel(const int32_t* ids, const float* w,
                                                                 PlanArgs pa) {
   __shared__ PlanShared s;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   plan_clear(s, pa.T, pa.E, pa.m);
   __syncthreads();
   const int G = pa.m > 0 ? pa.E / pa.m : 1;
+  const int nwt = DISTINCT ? rank_mask_words(pa.T, pa.E) : 0;
   for (int a = threadIdx.x; a < pa.T * pa.k; a += blockDim.x) {
     const int e = ids[a];
     s.ids[a] = e;
     s.w[a] = w[a];
     if (e >= 0 && e < pa.E) {
+      const int t = a / pa.k;
       atomicAdd(&s.cnt[e], 1);
-      if (pa.m > 0) s.flag[(a / pa.k) * pa.m + e / G] = 1;
+      if (nwt > 0) atomicOr(&s.tmask[e * nwt + (t >> 6)], 1ull << (t & 63));
+      if (pa.m > 0) s.flag[t * pa.m + e / G] = 1;
     } else {
       atomicAdd(&s.invalid, 1);
     }
   }
   __syncthreads();
-  plan_phase(s, pa, false);  // given ids may repeat an expert within a token
+  if (DISTINCT && pa.m <= 0 && pa.E <= kWavePlanPer * kWave && nwt > 0) {
+    if (wid == 0) plan_phase_wave(s, pa, lane);
+  } else {
+    plan_phase(s, pa, DISTINCT && nwt > 0);
+  }
+  if (pa.stats && wid == 0) write_stats(s, pa, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -3266,27 +3269,59 @@ static hipError_t launch_route_t(const RouteArgs& ra, const PlanArgs* pa, hipStr
   PlanArgs p{};
   if (pa) p = *pa;
   const int do_plan = pa != nullptr;
-  const dim3 grid(1), block(kPlanThreads);
   const KernelEvents* ev2 = ev ? ev + 1 : nullptr;
   // department-limited top-k only where the cap binds or coverage is
   // enforced (its own instances)
   const bool grouped = ra.k_dept > 0 && (ra.k_dept < ra.m || ra.strict);
-#define MOE_TOPK(N)                                                               \
-  (grouped ? launch(topk_plan_kernel<N, true>, grid, block, st, ev2, ra, p, do_plan) \
-           : launch(topk_plan_kernel<N, false>, grid, block, st, ev2, ra, p, do_plan))
-  if (ra.E <= 64)
-    MOE_TOPK(1);
-  else if (ra.E <= 128)
-    MOE_TOPK(2);
-  else if (ra.E <= 256)
-    MOE_TOPK(4);
-  else if (ra.E <= 512)
-    MOE_TOPK(8);
-  else if (ra.E <= 1024)
-    MOE_TOPK(16);
+  const int npl = (ra.E + kWave - 1) / kWave;
+  if (ra.T <= kPlanWaves && npl <= 4) {
+    // one block: a wave per token, then the plan from LDS
+    const dim3 grid(1), block(kPlanThreads);
+    auto go = [&](auto N) {
+      constexpr int NPL = decltype(N)::value;
+      if (grouped)
+        launch(topk_plan_kernel<NPL, true>, grid, block, st, ev2, ra, p, do_plan);
+      else
+        launch(topk_plan_kernel<NPL, false>, grid, block, st, ev2, ra, p, do_plan);
+    };
+    if (npl <= 1)
+      go(std::integral_constant<int, 1>{});
+    else if (npl <= 2)
+      go(std::integral_constant<int, 2>{});
+    else
+      go(std::integral_constant<int, 4>{});
+    return hipGetLastError();
+  }
+  // many tokens, or many experts per lane: the tokens' selections side by
+  // side in blocks of four waves, then (with a plan) the plan launch on the
+  // ids they wrote
+  const KernelEvents ea{ev2 ? ev2->start : nullptr, nullptr};
+  const KernelEvents eb{nullptr, ev2 ? ev2->stop : nullptr};
+  const dim3 grid(npl <= 4 ? (ra.T + kWaves - 1) / kWaves : ra.T), block(kThreads);
+  auto go = [&](auto N) {
+    constexpr int NPL = decltype(N)::value;
+    const KernelEvents* e1 = ev2 ? (do_plan ? &ea : ev2) : nullptr;
+    if (grouped)
+      launch(topk_token_kernel<NPL, true>, grid, block, st, e1, ra);
+    else
+      launch(topk_token_kernel<NPL, false>, grid, block, st, e1, ra);
+  };
+  if (npl <= 1)
+    go(std::integral_constant<int, 1>{});
+  else if (npl <= 2)
+    go(std::integral_constant<int, 2>{});
+  else if (npl <= 4)
+    go(std::integral_constant<int, 4>{});
+  else if (npl <= 8)
+    go(std::integral_constant<int, 8>{});
+  else if (npl <= 16)
+    go(std::integral_constant<int, 16>{});
   else
-    MOE_TOPK(32);
-#undef MOE_TOPK
+    go(std::integral_constant<int, 32>{});
+  if (!do_plan) return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  launch(dispatch_kernel<true>, dim3(1), dim3(kPlanThreads), st, ev2 ? &eb : nullptr,
+         (const int32_t*)ra.ids_out, (const float*)ra.w_out, p);
   return hipGetLastError();
 }
 
@@ -3298,7 +3333,7 @@ hipError_t launch_route(int w_dtype, const RouteArgs& ra, const PlanArgs* pa, hi
 
 hipError_t launch_dispatch(const int32_t* ids, const float* w, const PlanArgs& pa,
                            hipStream_t st) {
-  hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kPlanThreads), 0, st, ids, w, pa);
+  hipLaunchKernelGGL(dispatch_kernel<false>, dim3(1), dim3(kPlanThreads), 0, st, ids, w, pa);
   return hipGetLastError();
 }
 
