@@ -1,5 +1,5 @@
-// Device helpers for the gfx950 MoE decode kernels: bf16 <-> fp32, 8-wide
-// vector loads, and wave64 reductions.
+// Device helpers for the gfx950 MoE decode kernels: bf16 <-> fp32, global
+// loads, and wave64 reductions.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -25,33 +25,20 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 __device__ __forceinline__ void store_act(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_act(bf16_t* p, float v) { *p = f32_to_bf16(v); }
 
-// Eight consecutive elements widened to fp32.  p must be 16-byte aligned.
-__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
-__device__ __forceinline__ void load8(const bf16_t* p, float (&v)[8]) {
-  const uint4 a = *reinterpret_cast<const uint4*>(p);
-  v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x); v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
-  v[4] = bf16_lo(a.z); v[5] = bf16_hi(a.z); v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
+// Global-memory view of a generic pointer.  Loads through it compile to
+// global loads, counted by vmcnt alone.  A load through a generic pointer the
+// compiler cannot place (in an out-of-line function, say) becomes a flat
+// load, which also counts against lgkmcnt, so the compiler then waits for
+// every load in flight before the next LDS access or use -- a prefetch ring
+// of weight loads collapses to one step.
+template <typename V>
+__device__ __forceinline__ const __attribute__((address_space(1))) V* as_global(const void* p) {
+  return (const __attribute__((address_space(1))) V*)(p);
 }
 
-// Streaming (read-once) weight loads: same values, non-temporal cache hint.
+// 16-byte vectors of fp32 values and of raw 32-bit words.
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void load8_stream(const float* p, float (&v)[8]) {
-  const f32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
-  const f32x4_t b = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p + 4));
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
-__device__ __forceinline__ void load8_stream(const bf16_t* p, float (&v)[8]) {
-  const u32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-  v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x); v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
-  v[4] = bf16_lo(a.z); v[5] = bf16_hi(a.z); v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
-}
 
 // Cross-lane moves by DPP (a modifier of the VALU operand, no round trip
 // through the LDS crossbar as with ds_bpermute) inside 16-lane rows.

@@ -41,7 +41,7 @@ template <typename T_> struct Raw8;
 template <> struct Raw8<bf16_t> {
   u32x4_t u;
   __device__ __forceinline__ void load(const bf16_t* p) {
-    u = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    u = __builtin_nontemporal_load(as_global<u32x4_t>(p));
   }
   __device__ __forceinline__ void zero() { u = u32x4_t{0, 0, 0, 0}; }
   __device__ __forceinline__ void to_f32(float (&v)[8]) const {
@@ -52,8 +52,8 @@ template <> struct Raw8<bf16_t> {
 template <> struct Raw8<float> {
   f32x4_t a, b;
   __device__ __forceinline__ void load(const float* p) {
-    a = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
-    b = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p + 4));
+    a = __builtin_nontemporal_load(as_global<f32x4_t>(p));
+    b = __builtin_nontemporal_load(as_global<f32x4_t>(p + 4));
   }
   __device__ __forceinline__ void zero() { a = b = f32x4_t{0.f, 0.f, 0.f, 0.f}; }
   __device__ __forceinline__ void to_f32(float (&v)[8]) const {
@@ -69,15 +69,15 @@ template <typename T_> struct X8;
 template <> struct X8<bf16_t> {
   u32x4_t u;
   __device__ __forceinline__ void load(const bf16_t* p) {
-    u = *reinterpret_cast<const u32x4_t*>(p);
+    u = *as_global<u32x4_t>(p);
   }
   __device__ __forceinline__ void zero() { u = u32x4_t{0, 0, 0, 0}; }
 };
 template <> struct X8<float> {
   f32x4_t a, b;
   __device__ __forceinline__ void load(const float* p) {
-    a = *reinterpret_cast<const f32x4_t*>(p);
-    b = *reinterpret_cast<const f32x4_t*>(p + 4);
+    a = *as_global<f32x4_t>(p);
+    b = *as_global<f32x4_t>(p + 4);
   }
   __device__ __forceinline__ void zero() { a = b = f32x4_t{0.f, 0.f, 0.f, 0.f}; }
 };
@@ -110,13 +110,45 @@ __device__ __forceinline__ float dot8(const Raw8<float>& w, const X8<float>& x, 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& u) {
   return __builtin_bit_cast(bf16x8_t, u);
 }
-__device__ __forceinline__ u32x4_t ld16(const bf16_t* p) {
-  return *reinterpret_cast<const u32x4_t*>(p);
-}
+__device__ __forceinline__ u32x4_t ld16(const bf16_t* p) { return *as_global<u32x4_t>(p); }
 __device__ __forceinline__ u32x4_t ld16_stream(const bf16_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return __builtin_nontemporal_load(as_global<u32x4_t>(p));
 }
 
+
+// Wave-uniform copies (one lane's value in a scalar register), for values
+// that are uniform by construction but reach a function in vector registers.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ float uni(float v) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+template <typename P>
+__device__ __forceinline__ P* uni(P* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+  return reinterpret_cast<P*>(lo | (hi << 32));
+}
+
+// Raw buffer loads.  A resource spans 2 GiB from a wave-uniform base; a load
+// at an offset at or past its end returns zeros without touching memory, so a
+// bounds test becomes a select on the load's offset (kDcOob) and the load
+// itself stays unconditional.  (Loads under a branch make the compiler wait
+// for every load in flight at the branch's end, which empties any prefetch.)
+constexpr int kGfx9BufferDword3 = 0x00020000;  // raw (untyped) 32-bit buffer access
+constexpr int kCpolNt = 2;                     // non-temporal: weights are read once
+constexpr uint32_t kDcOob = 0x80000000u;       // buffer offset past every resource: reads 0
+constexpr int kSpanBytes = 0x7fffffff;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(uni(const_cast<void*>(base)), (short)0, kSpanBytes,
+                                           kGfx9BufferDword3);
+}
+__device__ __forceinline__ u32x4_t ld16_span(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+}
+__device__ __forceinline__ u32x4_t ld16_span_nt(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kCpolNt));
+}
 
 // ---------------------------------------------------------------------------
 // Routing + plan
@@ -1254,7 +1286,7 @@ __device__ __forceinline__ int slot_token(const Slot& sl, const int* grp_token, 
 // Input row of row t of a large group (per lane; t < n).
 __device__ __forceinline__ int lane_token(const Slot& sl, const int* grp_token, int t,
                                           int in_rows) {
-  const int tok = grp_token ? grp_token[sl.r0 + t] : t;
+  const int tok = grp_token ? *as_global<int>(grp_token + sl.r0 + t) : t;
   return min(max(tok, 0), in_rows - 1);
 }
 
@@ -1694,6 +1726,7 @@ __device__ __forceinline__ void dn_small_lds(const T_* __restrict__ Wd, int d, i
 // (L2); the four partial tiles are then added in wave order through LDS, so
 // results do not depend on timing.
 
+
 constexpr int kMfmaAhead = 2;  // K-steps requested ahead of the one being used
 
 // Per-wave K range [kb, ke) of a K-split tile: quarters rounded up to 32.
@@ -1720,56 +1753,51 @@ __device__ void gu_mfma(const bf16_t* __restrict__ Wg, const bf16_t* __restrict_
   const int r16 = lane & 15, g = lane >> 4;
   int kb, ke;
   k_quarter(d, wid, kb, ke);
-  const size_t row = (size_t)min(i0 + r16, rows - 1);
-  const bf16_t* ap = Wg + row * d + g * 8;
-  const bf16_t* bp = Wu + row * d + g * 8;
-  const bf16_t* xp[NX][NC];
+  // byte offsets into the spans of the two weight matrices and the inputs;
+  // a lane's load at step k is in range when k + 8g < ke, else it reads 0
+  const __amdgpu_buffer_rsrc_t rg = span_rsrc(Wg), ru = span_rsrc(Wu);
+  __amdgpu_buffer_rsrc_t rx[NX];
+  rx[0] = span_rsrc(x);
+  if constexpr (DUAL) rx[NX - 1] = span_rsrc(xu);
+  const uint32_t aoff = (uint32_t)(((size_t)min(i0 + r16, rows - 1) * d + g * 8) * 2);
+  uint32_t xoff[NC];
   bool xv[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int t = tc + c * 16 + r16;
     xv[c] = t < sl.n;
-    const size_t row = (size_t)(xv[c] ? lane_token(sl, grp_token, t, in_rows) : 0) * d + g * 8;
-    xp[0][c] = x + row;
-    if constexpr (DUAL) xp[NX - 1][c] = xu + row;
+    xoff[c] = (uint32_t)(((size_t)(xv[c] ? lane_token(sl, grp_token, t, in_rows) : 0) * d + g * 8) * 2);
   }
   f32x4_t accg[NC], accu[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) accg[c] = accu[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const u32x4_t z = {0, 0, 0, 0};
   // ring of kAhead + 1 steps in registers
-  u32x4_t ra[kAhead + 1], rb[kAhead + 1], rx[kAhead + 1][NX][NC];
-#pragma unroll
-  for (int s = 0; s <= kAhead; ++s) {
-    const int k = kb + s * 32;
+  u32x4_t ra[kAhead + 1], rb[kAhead + 1], rxv[kAhead + 1][NX][NC];
+  auto request = [&](int slot, int k) {
     const bool in = k + g * 8 < ke;
-    if (s < kAhead) {
-      ra[s] = in ? ld16_stream(ap + k) : z;
-      rb[s] = in ? ld16_stream(bp + k) : z;
+    const uint32_t kk = (uint32_t)k * 2;
+    ra[slot] = ld16_span_nt(rg, in ? aoff + kk : kDcOob);
+    rb[slot] = ld16_span_nt(ru, in ? aoff + kk : kDcOob);
 #pragma unroll
-      for (int v = 0; v < NX; ++v)
+    for (int v = 0; v < NX; ++v)
 #pragma unroll
-        for (int c = 0; c < NC; ++c) rx[s][v][c] = (xv[c] && in) ? ld16(xp[v][c] + k) : z;
-    }
-  }
+      for (int c = 0; c < NC; ++c) rxv[slot][v][c] = ld16_span(rx[v], (xv[c] && in) ? xoff[c] + kk : kDcOob);
+  };
+#pragma unroll
+  for (int s = 0; s < kAhead; ++s) request(s, kb + s * 32);
   for (int k = kb; k < ke; k += 32 * (kAhead + 1)) {
 #pragma unroll
     for (int s = 0; s <= kAhead; ++s) {
-      // request step s + kAhead into the slot freed last iteration
-      const int kn = k + (s + kAhead) * 32;
-      const int sn = (s + kAhead) % (kAhead + 1);
-      const bool nin = kn + g * 8 < ke;
-      ra[sn] = nin ? ld16_stream(ap + kn) : z;
-      rb[sn] = nin ? ld16_stream(bp + kn) : z;
-#pragma unroll
-      for (int v = 0; v < NX; ++v)
-#pragma unroll
-        for (int c = 0; c < NC; ++c) rx[sn][v][c] = (xv[c] && nin) ? ld16(xp[v][c] + kn) : z;
+      // request step s + kAhead into the slot freed last iteration, ahead of
+      // the matrix-core work on step s (kept in this order by the scheduling
+      // barrier, so the wait for step s leaves the newer loads in flight)
+      request((s + kAhead) % (kAhead + 1), k + (s + kAhead) * 32);
+      __builtin_amdgcn_sched_barrier(0);
       if (k + s * 32 < ke) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          accg[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra[s]), as_bf16x8(rx[s][0][c]), accg[c], 0, 0, 0);
-          accu[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rb[s]), as_bf16x8(rx[s][NX - 1][c]), accu[c], 0, 0, 0);
+          accg[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra[s]), as_bf16x8(rxv[s][0][c]), accg[c], 0, 0, 0);
+          accu[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rb[s]), as_bf16x8(rxv[s][NX - 1][c]), accu[c], 0, 0, 0);
         }
       }
     }
@@ -1910,7 +1938,7 @@ __device__ __forceinline__ void gu_wide(const bf16_t* __restrict__ Wg,
   src[0] = x;
   if constexpr (DUAL) src[NX - 1] = xu;
   wide_inputs<NC, NX>(in, src, d, tc, n, [&](int t) {
-    const int tok = grp_token ? grp_token[r0 + t] : t;
+    const int tok = grp_token ? *as_global<int>(grp_token + r0 + t) : t;
     return min(max(tok, 0), in_rows - 1);
   });
   f32x4_t accg[NC], accu[NC];
@@ -2462,18 +2490,6 @@ size_t down_combine_lds_bytes(const DownCombineArgs& a) {
 constexpr int kDcLoads = 4;   // 16-byte weight loads in flight per lane
 constexpr int kDcMaxSteps = kDcMaxRows / (8 * kWave);  // steps of the longest row
 
-__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
-__device__ __forceinline__ float uni(float v) {
-  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
-}
-template <typename P>
-__device__ __forceinline__ P* uni(P* p) {
-  const uint64_t u = reinterpret_cast<uint64_t>(p);
-  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
-  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
-  return reinterpret_cast<P*>(lo | (hi << 32));
-}
-
 // Elements a lane takes per 16-byte step: 8 bf16 weights or 16 FP8 codes.
 template <bool FP8> constexpr int dc_epl() { return FP8 ? 16 : 8; }
 
@@ -2483,9 +2499,6 @@ template <bool FP8> constexpr int dc_epl() { return FP8 ? 16 : 8; }
 // empty and every lane reads zeros.  The loads are thereby unconditional:
 // a branch around them would make the compiler wait for all loads in flight
 // before each use instead of only the oldest.
-constexpr int kGfx9BufferDword3 = 0x00020000;  // raw (untyped) 32-bit buffer access
-constexpr int kCpolNt = 2;                     // non-temporal: weights are read once
-constexpr uint32_t kDcOob = 0x80000000u;       // buffer offset past every resource: reads 0
 
 // FP8: also the column's scale (a scalar load, issued as far ahead).
 template <int NS, bool FP8>
@@ -2502,7 +2515,7 @@ __device__ __forceinline__ void dc_load(const DcItem* items, int i, int ie, int 
     dst[s] = __builtin_bit_cast(
         u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                      rs, (lane * EPL + s * EPL * kWave) * ESZ, 0, kCpolNt));
-  if constexpr (FP8) scl = uni(it.scale)[c];
+  if constexpr (FP8) scl = *as_global<float>(uni(it.scale) + c);
 }
 
 // Dot products of group i's weight row with its rows of h (LDS), folded into
@@ -2634,21 +2647,36 @@ void down_combine_kernel(DownCombineArgs a,
   const int T = a.T, d = a.d;
   constexpr int STEP = 8 * kWave;  // elements of a weight row per step
   // The group table (descriptors checked against the family's bounds and the
-  // rows of h in use), and the staging of those rows: family f's rows
-  // [0, nh) are contiguous in global memory and go to hl + lds_off.
-  int fb[kDcFamilies + 1];
-  fb[0] = 0;
+  // rows of h in use), and the staging of the rows of h.  Nothing here waits
+  // for anything else: the counts, every descriptor slot up to the host's
+  // bound and every row of h the step can use (family f's rows [0,
+  // max_hrows) are contiguous in global memory and go to hl + lds_off) are
+  // all requested at once, and slots past the count are simply not consumed.
+  // Family f's table entries start at fb[f] (the sum of the earlier
+  // families' bounds) and end at fe[f].
+  int fb[kDcFamilies], fe[kDcFamilies];
+  int ib = 0;
 #pragma unroll
   for (int fi = 0; fi < kDcFamilies; ++fi) {
-    fb[fi + 1] = fb[fi];
+    fb[fi] = fe[fi] = ib;
     if (fi < a.nf) {
       const DcFamily& F = a.f[fi];
-      // (counts read back as wave-uniform values: the group loop bounds and
-      // the weight-row resources built from them stay scalar)
+      const int nh = F.n_hrows ? F.max_hrows : min(T, F.max_hrows);  // rows staged
+      const int nmax = F.work ? F.max_items : 1;
+      // (the count read back as a wave-uniform value: the group loop bounds
+      // and the weight-row resources built from it stay scalar)
       const int nf = uni(F.work ? min(max(*F.n_items, 0), F.max_items) : 1);
-      const int nh = uni(F.n_hrows ? min(max(*F.n_hrows, 0), F.max_hrows) : min(T, F.max_hrows));
+      const int nu = uni(F.n_hrows ? min(max(*F.n_hrows, 0), F.max_hrows) : nh);  // rows in use
       const size_t ms = (size_t)d * F.rows;
-      for (int i = tid; i < nf; i += kDcWaves * kWave) {
+      const int nch = nh * (F.rows / 8);  // 16-byte chunks of the rows staged
+      const bf16_t* src = static_cast<const bf16_t*>(F.h);
+      for (int q = wid; q * kWave < nch; q += kDcWaves) {
+        const int ch = q * kWave + lane;
+        if (ch < nch)
+          __builtin_amdgcn_global_load_lds(src + (size_t)ch * 8,
+                                           (lds_void_t*)(hl + F.lds_off + q * STEP), 16, 0, 0);
+      }
+      for (int i = tid; i < nmax; i += kDcWaves * kWave) {
         int mat = 0, r0 = 0, n = 0;
         int tk[kTokInline] = {0, 1, 2, 3};
         if (F.work) {
@@ -2657,8 +2685,8 @@ void down_combine_kernel(DownCombineArgs a,
           const u32x4_t* wv = reinterpret_cast<const u32x4_t*>(F.work + i);
           const u32x4_t w0 = wv[0], w1 = wv[1];
           const int dm = (int)w0.x, dr = (int)w0.y, dn = (int)w0.z;
-          if (dm >= 0 && dm < F.n_mats && dr >= 0 && dn >= 1 && dn <= kTokInline &&
-              dn <= nh - dr) {
+          if (i < nf && dm >= 0 && dm < F.n_mats && dr >= 0 && dn >= 1 && dn <= kTokInline &&
+              dn <= nu - dr) {
             mat = dm;
             r0 = dr;
             n = dn;
@@ -2668,7 +2696,7 @@ void down_combine_kernel(DownCombineArgs a,
             tk[3] = (int)w1.z;
           }
         } else {
-          n = min(min(T, kTokInline), nh);  // the shared expert: row t is token t
+          n = min(min(T, kTokInline), nu);  // the shared expert: row t is token t
         }
         DcItem it;
         it.w = static_cast<const char*>(F.down) + (size_t)mat * ms * (FP8 ? 1 : 2);
@@ -2695,17 +2723,10 @@ void down_combine_kernel(DownCombineArgs a,
               it.twt[t] = it.wt[j];
             }
         }
-        items[fb[fi] + i] = it;
+        items[ib + i] = it;
       }
-      const int nch = nh * (F.rows / 8);  // 16-byte chunks of the rows in use
-      const bf16_t* src = static_cast<const bf16_t*>(F.h);
-      for (int q = wid; q * kWave < nch; q += kDcWaves) {
-        const int ch = q * kWave + lane;
-        if (ch < nch)
-          __builtin_amdgcn_global_load_lds(src + (size_t)ch * 8,
-                                           (lds_void_t*)(hl + F.lds_off + q * STEP), 16, 0, 0);
-      }
-      fb[fi + 1] += nf;
+      fe[fi] = ib + nf;
+      ib += nmax;
     }
   }
   // every wave's staged rows have landed, and the table is complete, for the block
@@ -2718,24 +2739,24 @@ void down_combine_kernel(DownCombineArgs a,
   for (int t = 0; t < kTokInline; ++t) acc[t] = 0.f;
 #pragma unroll
   for (int fi = 0; fi < kDcFamilies; ++fi) {
-    if (fi < a.nf && fb[fi] < fb[fi + 1]) {
+    if (fi < a.nf && fb[fi] < fe[fi]) {
       constexpr int SE = dc_epl<FP8>() * kWave;  // elements per step
       const int ns = (a.f[fi].rows + SE - 1) / SE;
       const int rows = a.f[fi].rows;
       // (packed loads address the family's weights by 32-bit byte offsets)
       const bool packable = !FP8 && (size_t)a.f[fi].n_mats * rows * d * 2 < (size_t)kDcOob;
       if (packable && rows == 16 * 8)
-        dc_family_packed<16>(items, fb[fi], fb[fi + 1], c, hl, lane, a.f[fi], d, acc);
+        dc_family_packed<16>(items, fb[fi], fe[fi], c, hl, lane, a.f[fi], d, acc);
       else if (packable && rows == 32 * 8)
-        dc_family_packed<32>(items, fb[fi], fb[fi + 1], c, hl, lane, a.f[fi], d, acc);
+        dc_family_packed<32>(items, fb[fi], fe[fi], c, hl, lane, a.f[fi], d, acc);
       else if (ns <= 1)
-        dc_family<1, FP8>(items, fb[fi], fb[fi + 1], c, hl, lane, acc);
+        dc_family<1, FP8>(items, fb[fi], fe[fi], c, hl, lane, acc);
       else if (ns == 2 || FP8)
-        dc_family<2, FP8>(items, fb[fi], fb[fi + 1], c, hl, lane, acc);
+        dc_family<2, FP8>(items, fb[fi], fe[fi], c, hl, lane, acc);
       else if (ns == 3)
-        dc_family<3, FP8>(items, fb[fi], fb[fi + 1], c, hl, lane, acc);
+        dc_family<3, FP8>(items, fb[fi], fe[fi], c, hl, lane, acc);
       else
-        dc_family<kDcMaxSteps, FP8>(items, fb[fi], fb[fi + 1], c, hl, lane, acc);
+        dc_family<kDcMaxSteps, FP8>(items, fb[fi], fe[fi], c, hl, lane, acc);
     }
   }
   // lane 16 t holds token t's sum
