@@ -1727,8 +1727,6 @@ __device__ __forceinline__ void dn_small_lds(const T_* __restrict__ Wd, int d, i
 // results do not depend on timing.
 
 
-constexpr int kMfmaAhead = 2;  // K-steps requested ahead of the one being used
-
 // Per-wave K range [kb, ke) of a K-split tile: quarters rounded up to 32.
 __device__ __forceinline__ void k_quarter(int K, int wid, int& kb, int& ke) {
   const int kq = ((K + 4 * 32 - 1) / (4 * 32)) * 32;
@@ -1736,94 +1734,158 @@ __device__ __forceinline__ void k_quarter(int K, int wid, int& kb, int& ke) {
   ke = min(K, kb + kq);
 }
 
+// Weight tiles of the K-split gate/up go HBM -> LDS with buffer loads that
+// write LDS directly (no registers): a tile is 16 rows x 64 elements of K,
+// two loads of 8 rows x 128 contiguous bytes.  The matrix-core operand layout
+// read straight from memory (lane l: row l % 16, 16 bytes at 8 (l / 16) of
+// each 32-element step) visits 16 rows per load in 64-byte pieces, which
+// measured 25% slower in HBM rate at the DeaMoE-7B-shaped batch 16; runs of
+// 128 bytes or longer stream at the full rate.  In LDS, lane s of row a of a
+// load holds chunk (s - rot) mod 8 of the row's 128 bytes, rot = a / 2 + 4 j
+// for load j, so that the operand reads (16 rows at one chunk) fall in 16
+// different 16-byte bank columns.
+constexpr int kTileK = 64;                 // K elements of a tile
+constexpr int kTileBytes = 16 * kTileK * 2;  // 2 KiB: 16 rows
+constexpr int kTileSlots = 3;              // per wave: gate and up tiles in turn
 struct MfmaLds {
-  f32x4_t part[kWaves][2][2][kWave];  // [wave][token chunk][gate / up][lane]
+  union {
+    f32x4_t part[kWaves][2][2][kWave];                   // [wave][token chunk][gate / up][lane]
+    unsigned char tile[kWaves][kTileSlots][kTileBytes];  // per wave: a ring of tiles
+  };
 };
+__device__ __forceinline__ int tile_rot(int j, int a) { return ((a >> 1) + 4 * j) & 7; }
+
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Request one tile (rows i0.., K elements k0 .. k0 + 63) of the matrix behind
+// `rs` into LDS tile `t` (wave-uniform): load j, lane l -> row 8 j + l / 8,
+// chunk ((l % 8) - rot) mod 8; elements at or past ke, and rows at or past
+// `rows`, read zeros.  Two vector-memory operations.
+__device__ __forceinline__ void tile_request(unsigned char* t, __amdgpu_buffer_rsrc_t rs, int i0,
+                                             int rows, int d, int k0, int ke, int lane) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int a = lane >> 3, r = 8 * j + a;
+    const int chunk = ((lane & 7) - tile_rot(j, a)) & 7;
+    const int k = k0 + 8 * chunk;
+    const uint32_t off =
+        (k < ke && i0 + r < rows) ? (uint32_t)(((size_t)(i0 + r) * d + k) * 2) : kDcOob;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(t + 1024 * j), 16, off, 0, 0,
+                                             kCpolNt);
+  }
+}
+// The operand of 32-element step m (0 or 1) of a tile in LDS.
+__device__ __forceinline__ u32x4_t tile_operand(const unsigned char* t, int m, int lane) {
+  const int r = lane & 15, j = r >> 3, a = r & 7;
+  const int chunk = 4 * m + (lane >> 4);
+  return *reinterpret_cast<const u32x4_t*>(t + 1024 * j +
+                                           16 * (8 * a + ((chunk + tile_rot(j, a)) & 7)));
+}
 
 // 16 rows (i0..) of gate and up against 16*NC tokens (rows tc.. of the group).
+// Each wave takes a quarter of K in tiles of 64: gate tile q and up tile q
+// take turns in a ring of three LDS slots, so while one is used the next two
+// are in flight; the inputs of tile q (two 32-element steps) come through
+// registers, two sets in turn.  Loads past ke read zeros, so every load is
+// unconditional.  The waits are counted by hand (the compiler does not see
+// the LDS data of these loads): per tile the vector-memory operations are,
+// in order, gate (2), inputs (2 NX NC), up (2).
 template <int NC, bool DUAL>
 __device__ void gu_mfma(const bf16_t* __restrict__ Wg, const bf16_t* __restrict__ Wu, int d,
                         int rows, int i0, const bf16_t* __restrict__ x,
                         const bf16_t* __restrict__ xu, int in_rows, const Slot& sl,
                         const int* grp_token, int tc, const GuOut<bf16_t>& o, int lane, int wid,
                         MfmaLds& lds) {
+  static_assert(NC == 1, "the LDS tile ring serves one 16-token chunk");
   constexpr int NX = DUAL ? 2 : 1;   // activation inputs: gate's, and up's when they differ
-  // two token chunks hold twice the activations: one step ahead keeps them in registers
-  constexpr int kAhead = NC > 1 ? 1 : kMfmaAhead;
+  constexpr int NXO = 2 * NX;        // input loads of one tile
   const int r16 = lane & 15, g = lane >> 4;
   int kb, ke;
   k_quarter(d, wid, kb, ke);
-  // byte offsets into the spans of the two weight matrices and the inputs;
-  // a lane's load at step k is in range when k + 8g < ke, else it reads 0
+  kb = uni(kb);
+  ke = uni(ke);
   const __amdgpu_buffer_rsrc_t rg = span_rsrc(Wg), ru = span_rsrc(Wu);
   __amdgpu_buffer_rsrc_t rx[NX];
   rx[0] = span_rsrc(x);
   if constexpr (DUAL) rx[NX - 1] = span_rsrc(xu);
-  const uint32_t aoff = (uint32_t)(((size_t)min(i0 + r16, rows - 1) * d + g * 8) * 2);
-  uint32_t xoff[NC];
-  bool xv[NC];
+  const int t = tc + r16;
+  const bool xv = t < sl.n;
+  const uint32_t xoff =
+      (uint32_t)(((size_t)(xv ? lane_token(sl, grp_token, t, in_rows) : 0) * d + g * 8) * 2);
+  f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+  unsigned char* slots = lds.tile[wid][0];
+  u32x4_t xa[2][NX], xb[2][NX];
+  auto request_x = [&](u32x4_t (&xr)[2][NX], int k0) {
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int t = tc + c * 16 + r16;
-    xv[c] = t < sl.n;
-    xoff[c] = (uint32_t)(((size_t)(xv[c] ? lane_token(sl, grp_token, t, in_rows) : 0) * d + g * 8) * 2);
-  }
-  f32x4_t accg[NC], accu[NC];
+    for (int m = 0; m < 2; ++m) {
+      const int k = k0 + 32 * m;
+      const bool in = xv && k + g * 8 < ke;
 #pragma unroll
-  for (int c = 0; c < NC; ++c) accg[c] = accu[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // ring of kAhead + 1 steps in registers
-  u32x4_t ra[kAhead + 1], rb[kAhead + 1], rxv[kAhead + 1][NX][NC];
-  auto request = [&](int slot, int k) {
-    const bool in = k + g * 8 < ke;
-    const uint32_t kk = (uint32_t)k * 2;
-    ra[slot] = ld16_span_nt(rg, in ? aoff + kk : kDcOob);
-    rb[slot] = ld16_span_nt(ru, in ? aoff + kk : kDcOob);
-#pragma unroll
-    for (int v = 0; v < NX; ++v)
-#pragma unroll
-      for (int c = 0; c < NC; ++c) rxv[slot][v][c] = ld16_span(rx[v], (xv[c] && in) ? xoff[c] + kk : kDcOob);
-  };
-#pragma unroll
-  for (int s = 0; s < kAhead; ++s) request(s, kb + s * 32);
-  for (int k = kb; k < ke; k += 32 * (kAhead + 1)) {
-#pragma unroll
-    for (int s = 0; s <= kAhead; ++s) {
-      // request step s + kAhead into the slot freed last iteration, ahead of
-      // the matrix-core work on step s (kept in this order by the scheduling
-      // barrier, so the wait for step s leaves the newer loads in flight)
-      request((s + kAhead) % (kAhead + 1), k + (s + kAhead) * 32);
-      __builtin_amdgcn_sched_barrier(0);
-      if (k + s * 32 < ke) {
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          accg[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra[s]), as_bf16x8(rxv[s][0][c]), accg[c], 0, 0, 0);
-          accu[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rb[s]), as_bf16x8(rxv[s][NX - 1][c]), accu[c], 0, 0, 0);
-        }
-      }
+      for (int v = 0; v < NX; ++v) xr[m][v] = ld16_span(rx[v], in ? xoff + (uint32_t)k * 2 : kDcOob);
     }
-  }
+  };
+  // unit u = 2q (gate tile q) or 2q + 1 (up tile q) lives in slot u % 3
+  auto slot = [&](int u) { return slots + (u % kTileSlots) * kTileBytes; };
+  auto mfma2 = [&](f32x4_t& acc, const unsigned char* tl, const u32x4_t (&xr)[2][NX], int v) {
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    lds.part[wid][c][0][lane] = accg[c];
-    lds.part[wid][c][1][lane] = accu[c];
+    for (int m = 0; m < 2; ++m)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(tile_operand(tl, m, lane)),
+                                                    as_bf16x8(xr[m][v]), acc, 0, 0, 0);
+  };
+  // one tile: its gate and up units were requested before; requests the next
+  // tile's units and inputs (into xn) as the slots free up
+  auto step = [&](int q, u32x4_t (&xc)[2][NX], u32x4_t (&xn)[2][NX]) {
+    const int k0 = kb + kTileK * q;
+    // gate q, then (after the request of gate q + 1 and its inputs) wait for
+    // gate q and inputs q: newer are up q, gate q + 1, inputs q + 1
+    __builtin_amdgcn_sched_barrier(0);
+    tile_request(slot(2 * q + 2), rg, i0, rows, d, k0 + kTileK, ke, lane);
+    request_x(xn, k0 + kTileK);
+    wait_vmcnt<2 + 2 + NXO>();
+    __builtin_amdgcn_sched_barrier(0);
+    mfma2(accg, slot(2 * q), xc, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // the slot of gate q takes up q + 1: its reads have returned, since the
+    // matrix-core steps issued above consumed them
+    tile_request(slot(2 * q + 3), ru, i0, rows, d, k0 + kTileK, ke, lane);
+    // up q: newer are gate q + 1, inputs q + 1, up q + 1
+    wait_vmcnt<2 + NXO + 2>();
+    __builtin_amdgcn_sched_barrier(0);
+    mfma2(accu, slot(2 * q + 1), xc, NX - 1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  tile_request(slot(0), rg, i0, rows, d, kb, ke, lane);
+  request_x(xa, kb);
+  tile_request(slot(1), ru, i0, rows, d, kb, ke, lane);
+  const int nq = (ke - kb + kTileK - 1) / kTileK;
+  for (int q = 0; q < nq; q += 2) {
+    step(q, xa, xb);
+    if (q + 1 < nq) step(q + 1, xb, xa);
   }
+  // no load may still write a slot when the area is reused below
+  wait_vmcnt<0>();
+  __syncthreads();
+  lds.part[wid][0][0][lane] = accg;
+  lds.part[wid][0][1][lane] = accu;
   __syncthreads();
   if (wid == 0) {
+    f32x4_t sg = lds.part[0][0][0][lane], su = lds.part[0][0][1][lane];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      f32x4_t sg = lds.part[0][c][0][lane], su = lds.part[0][c][1][lane];
+    for (int w = 1; w < kWaves; ++w) {
+      sg += lds.part[w][0][0][lane];
+      su += lds.part[w][0][1][lane];
+    }
+    if (t < sl.n) {
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) {
-        sg += lds.part[w][c][0][lane];
-        su += lds.part[w][c][1][lane];
-      }
-      const int t = tc + c * 16 + r16;
-      if (t < sl.n) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rr = i0 + 4 * g + i;
-          if (rr < rows) gu_store(o, (size_t)(sl.r0 + t) * rows + rr, sg[i], su[i]);
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int rr = i0 + 4 * g + i;
+        if (rr < rows) gu_store(o, (size_t)(sl.r0 + t) * rows + rr, sg[i], su[i]);
       }
     }
   }
