@@ -15,7 +15,9 @@ constexpr int kRouteChunk = 512;     // d elements one router wave covers (64 la
 constexpr int kTokInline = 4;        // tokens carried inline in a work descriptor
 constexpr int kWideRows = 64;        // rows / columns of a bf16 large-group tile (unless split K)
 constexpr int kSplitKMaxT = 16;      // K-split gate/up tiles: T at most (every group <= 16 rows)
-constexpr int kSplitKMaxD = 2048;    //   and d at most
+constexpr int kSplitKMaxD = 2048;    //   and d at most (K-split down tiles: d above it)
+constexpr int kSplitKCols = 32;      // K-split down tiles (T <= kSplitKMaxT): output columns per block
+constexpr int kSplitKMinK = 256;     //   and intermediate width at least (a full K tile per wave)
 constexpr int kPlanThreads = 1024;   // threads of the single-block top-k / plan kernel
 constexpr int kMaxRouteSplit = 8;   // partial-logit planes of the bf16 router at most
 constexpr int kMaxParts = 6;         // 3 matrix families x (small groups, large groups)
@@ -88,8 +90,9 @@ struct Family {
   int n_mats;              // matrices in the family (bounds check of work descriptors)
   int max_rows;            // rows h / out hold (bounds check of work descriptors)
   int large;               // 0: groups of <= kTokInline rows; 1: larger groups
-  int splitk;              // large gate/up part of bf16 weights: 16-row K-split tiles
-                           // (groups of at most 16 rows), else 64-row tiles
+  int splitk;              // large part of bf16 weights, groups of at most 16 rows: K-split
+                           // tiles (gate/up: 16 rows, down: kSplitKCols columns per block),
+                           // else 64-row / 64-column tiles
   const float* gate_scale; // FP8 weights: per-row scales [n_mats][rows] (gate, up)
   const float* up_scale;   //   and [n_mats][d] (down); unused otherwise
   const float* down_scale;

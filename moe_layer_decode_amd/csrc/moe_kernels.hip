@@ -1788,37 +1788,38 @@ __device__ __forceinline__ u32x4_t tile_operand(const unsigned char* t, int m, i
                                            16 * (8 * a + ((chunk + tile_rot(j, a)) & 7)));
 }
 
-// 16 rows (i0..) of gate and up against 16*NC tokens (rows tc.. of the group).
-// Each wave takes a quarter of K in tiles of 64: gate tile q and up tile q
-// take turns in a ring of three LDS slots, so while one is used the next two
-// are in flight; the inputs of tile q (two 32-element steps) come through
-// registers, two sets in turn.  Loads past ke read zeros, so every load is
-// unconditional.  The waits are counted by hand (the compiler does not see
-// the LDS data of these loads): per tile the vector-memory operations are,
-// in order, gate (2), inputs (2 NX NC), up (2).
-template <int NC, bool DUAL>
-__device__ void gu_mfma(const bf16_t* __restrict__ Wg, const bf16_t* __restrict__ Wu, int d,
-                        int rows, int i0, const bf16_t* __restrict__ x,
-                        const bf16_t* __restrict__ xu, int in_rows, const Slot& sl,
-                        const int* grp_token, int tc, const GuOut<bf16_t>& o, int lane, int wid,
-                        MfmaLds& lds) {
-  static_assert(NC == 1, "the LDS tile ring serves one 16-token chunk");
-  constexpr int NX = DUAL ? 2 : 1;   // activation inputs: gate's, and up's when they differ
+// K-split matrix-core tile: two 16-row tiles, A0 = rows a0.. of the matrix
+// behind rs0 and A1 = rows a1.. of the matrix behind rs1 (nrows rows of kdim
+// elements each), against up to 16 input rows (input row t at xrow(t) of x,
+// and of xu for A1 when DUAL; rows t >= n read zeros).  Each wave takes a
+// quarter of K in tiles of 64: tile q of A0 and tile q of A1 take turns in a
+// ring of three LDS slots, so while one is used the next two are in flight;
+// the inputs of tile q (two 32-element steps) come through registers, two
+// sets in turn.  Loads past the wave's K range, and rows at or past nrows,
+// read zeros, so every load is unconditional.  The waits are counted by hand
+// (the compiler does not see the LDS data of these loads): per tile the
+// vector-memory operations are, in order, A0 (2), inputs (2 NX), A1 (2).  The
+// four waves' partial tiles are added in wave order through LDS, and wave 0
+// calls epi(t, i, s0, s1) with the sums of rows 4 (l / 16) + i of both tiles
+// for input row t = l % 16 < n.
+template <bool DUAL, typename XRow, typename Epi>
+__device__ void ksplit_mfma(__amdgpu_buffer_rsrc_t rs0, int a0, __amdgpu_buffer_rsrc_t rs1,
+                            int a1, int nrows, int kdim, const bf16_t* __restrict__ x,
+                            const bf16_t* __restrict__ xu, XRow xrow, int n, Epi epi, int lane,
+                            int wid, MfmaLds& lds) {
+  constexpr int NX = DUAL ? 2 : 1;   // activation inputs: A0's, and A1's when they differ
   constexpr int NXO = 2 * NX;        // input loads of one tile
-  const int r16 = lane & 15, g = lane >> 4;
+  const int t = lane & 15, g = lane >> 4;
   int kb, ke;
-  k_quarter(d, wid, kb, ke);
+  k_quarter(kdim, wid, kb, ke);
   kb = uni(kb);
   ke = uni(ke);
-  const __amdgpu_buffer_rsrc_t rg = span_rsrc(Wg), ru = span_rsrc(Wu);
   __amdgpu_buffer_rsrc_t rx[NX];
   rx[0] = span_rsrc(x);
   if constexpr (DUAL) rx[NX - 1] = span_rsrc(xu);
-  const int t = tc + r16;
-  const bool xv = t < sl.n;
-  const uint32_t xoff =
-      (uint32_t)(((size_t)(xv ? lane_token(sl, grp_token, t, in_rows) : 0) * d + g * 8) * 2);
-  f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+  const bool xv = t < n;
+  const uint32_t xoff = (uint32_t)(((size_t)(xv ? xrow(t) : 0) * kdim + g * 8) * 2);
+  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   unsigned char* slots = lds.tile[wid][0];
   u32x4_t xa[2][NX], xb[2][NX];
   auto request_x = [&](u32x4_t (&xr)[2][NX], int k0) {
@@ -1830,7 +1831,7 @@ __device__ void gu_mfma(const bf16_t* __restrict__ Wg, const bf16_t* __restrict_
       for (int v = 0; v < NX; ++v) xr[m][v] = ld16_span(rx[v], in ? xoff + (uint32_t)k * 2 : kDcOob);
     }
   };
-  // unit u = 2q (gate tile q) or 2q + 1 (up tile q) lives in slot u % 3
+  // unit u = 2q (A0 tile q) or 2q + 1 (A1 tile q) lives in slot u % 3
   auto slot = [&](int u) { return slots + (u % kTileSlots) * kTileBytes; };
   auto mfma2 = [&](f32x4_t& acc, const unsigned char* tl, const u32x4_t (&xr)[2][NX], int v) {
 #pragma unroll
@@ -1838,31 +1839,30 @@ __device__ void gu_mfma(const bf16_t* __restrict__ Wg, const bf16_t* __restrict_
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(tile_operand(tl, m, lane)),
                                                     as_bf16x8(xr[m][v]), acc, 0, 0, 0);
   };
-  // one tile: its gate and up units were requested before; requests the next
+  // one tile, whose A0 and A1 units were requested before; requests the next
   // tile's units and inputs (into xn) as the slots free up
   auto step = [&](int q, u32x4_t (&xc)[2][NX], u32x4_t (&xn)[2][NX]) {
     const int k0 = kb + kTileK * q;
-    // gate q, then (after the request of gate q + 1 and its inputs) wait for
-    // gate q and inputs q: newer are up q, gate q + 1, inputs q + 1
     __builtin_amdgcn_sched_barrier(0);
-    tile_request(slot(2 * q + 2), rg, i0, rows, d, k0 + kTileK, ke, lane);
+    tile_request(slot(2 * q + 2), rs0, a0, nrows, kdim, k0 + kTileK, ke, lane);
     request_x(xn, k0 + kTileK);
+    // A0 tile q and inputs q: newer are A1 q, A0 q + 1, inputs q + 1
     wait_vmcnt<2 + 2 + NXO>();
     __builtin_amdgcn_sched_barrier(0);
-    mfma2(accg, slot(2 * q), xc, 0);
+    mfma2(acc0, slot(2 * q), xc, 0);
     __builtin_amdgcn_sched_barrier(0);
-    // the slot of gate q takes up q + 1: its reads have returned, since the
-    // matrix-core steps issued above consumed them
-    tile_request(slot(2 * q + 3), ru, i0, rows, d, k0 + kTileK, ke, lane);
-    // up q: newer are gate q + 1, inputs q + 1, up q + 1
+    // the slot of A0 tile q takes A1 tile q + 1: its reads have returned,
+    // since the matrix-core steps issued above consumed them
+    tile_request(slot(2 * q + 3), rs1, a1, nrows, kdim, k0 + kTileK, ke, lane);
+    // A1 tile q: newer are A0 q + 1, inputs q + 1, A1 q + 1
     wait_vmcnt<2 + NXO + 2>();
     __builtin_amdgcn_sched_barrier(0);
-    mfma2(accu, slot(2 * q + 1), xc, NX - 1);
+    mfma2(acc1, slot(2 * q + 1), xc, NX - 1);
     __builtin_amdgcn_sched_barrier(0);
   };
-  tile_request(slot(0), rg, i0, rows, d, kb, ke, lane);
+  tile_request(slot(0), rs0, a0, nrows, kdim, kb, ke, lane);
   request_x(xa, kb);
-  tile_request(slot(1), ru, i0, rows, d, kb, ke, lane);
+  tile_request(slot(1), rs1, a1, nrows, kdim, kb, ke, lane);
   const int nq = (ke - kb + kTileK - 1) / kTileK;
   for (int q = 0; q < nq; q += 2) {
     step(q, xa, xb);
@@ -1871,25 +1871,38 @@ __device__ void gu_mfma(const bf16_t* __restrict__ Wg, const bf16_t* __restrict_
   // no load may still write a slot when the area is reused below
   wait_vmcnt<0>();
   __syncthreads();
-  lds.part[wid][0][0][lane] = accg;
-  lds.part[wid][0][1][lane] = accu;
+  lds.part[wid][0][0][lane] = acc0;
+  lds.part[wid][0][1][lane] = acc1;
   __syncthreads();
   if (wid == 0) {
-    f32x4_t sg = lds.part[0][0][0][lane], su = lds.part[0][0][1][lane];
+    f32x4_t s0 = lds.part[0][0][0][lane], s1 = lds.part[0][0][1][lane];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) {
-      sg += lds.part[w][0][0][lane];
-      su += lds.part[w][0][1][lane];
+      s0 += lds.part[w][0][0][lane];
+      s1 += lds.part[w][0][1][lane];
     }
-    if (t < sl.n) {
+    if (t < n) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = i0 + 4 * g + i;
-        if (rr < rows) gu_store(o, (size_t)(sl.r0 + t) * rows + rr, sg[i], su[i]);
-      }
+      for (int i = 0; i < 4; ++i) epi(t, 4 * g + i, s0[i], s1[i]);
     }
   }
   __syncthreads();
+}
+
+// 16 rows (i0..) of gate and up against the group's (at most 16) rows.
+template <bool DUAL>
+__device__ void gu_mfma(const bf16_t* __restrict__ Wg, const bf16_t* __restrict__ Wu, int d,
+                        int rows, int i0, const bf16_t* __restrict__ x,
+                        const bf16_t* __restrict__ xu, int in_rows, const Slot& sl,
+                        const int* grp_token, const GuOut<bf16_t>& o, int lane, int wid,
+                        MfmaLds& lds) {
+  ksplit_mfma<DUAL>(
+      span_rsrc(Wg), i0, span_rsrc(Wu), i0, rows, d, x, xu,
+      [&](int t) { return lane_token(sl, grp_token, t, in_rows); }, sl.n,
+      [&](int t, int i, float g, float u) {
+        if (i0 + i < rows) gu_store(o, (size_t)(sl.r0 + t) * rows + i0 + i, g, u);
+      },
+      lane, wid, lds);
 }
 
 // Out-of-line entry of the K-split gate/up tile for one 16-token chunk
@@ -1902,7 +1915,28 @@ __device__ __attribute__((noinline)) void gu_mfma_call(
   Slot sl{};
   sl.r0 = r0;
   sl.n = n;
-  gu_mfma<1, DUAL>(Wg, Wu, d, rows, i0, x, xu, in_rows, sl, grp_token, 0, o, lane, wid, lds);
+  gu_mfma<DUAL>(Wg, Wu, d, rows, i0, x, xu, in_rows, sl, grp_token, o, lane, wid, lds);
+}
+
+// Down projection of a group of at most 16 rows of h as K-split tiles: 32
+// output columns (c0..) per block, two 16-column tiles sharing each input
+// step, K = the intermediate width split over the four waves.  out[r0 + t][c]
+// (SiLU of it when epi) for every row t < n of the group.  Out of line, like
+// gu_mfma_call.
+__device__ __attribute__((noinline)) void dn_mfma_call(const bf16_t* __restrict__ Wd, int d,
+                                                       int rows, int c0,
+                                                       const bf16_t* __restrict__ h, int r0,
+                                                       int n, float* __restrict__ out, int epi,
+                                                       int lane, int wid, MfmaLds& lds) {
+  const __amdgpu_buffer_rsrc_t rw = span_rsrc(Wd);
+  ksplit_mfma<false>(
+      rw, c0, rw, c0 + 16, d, rows, h + (size_t)r0 * rows, h, [](int t) { return t; }, n,
+      [&](int t, int i, float a, float b) {
+        float* o = out + (size_t)(r0 + t) * d;
+        if (c0 + i < d) dn_store(o, c0 + i, a, epi);
+        if (c0 + 16 + i < d) dn_store(o, c0 + 16 + i, b, epi);
+      },
+      lane, wid, lds);
 }
 // ---- large groups, bf16: 64-row tiles with LDS-shared inputs ---------------
 //
@@ -2377,6 +2411,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     return;
   }
   if constexpr (sizeof(T_) == 2) {
+    if (F.splitk) {
+      // at most 16 rows per group: 32 columns per block, K split over the waves
+      const int c0 = tile * kSplitKCols;
+      if (c0 < d)
+        dn_mfma_call(Wd, d, F.rows, c0, h, sl.r0, sl.n, F.out, F.epi, lane, wid,
+                     *reinterpret_cast<MfmaLds*>(lds_raw));
+      return;
+    }
     // large groups: the whole block on one 64-column tile, 16*NC rows of h a pass
     const int c0 = tile * kWideRows;
     if (c0 >= d) return;
