@@ -315,7 +315,16 @@ moe::GemvConfig choose_config(const moe_layer_desc& d, int32_t T) {
     }
   }
   c.lpr = lpr;
-  c.col_groups = 2;
+  // Down: two column groups per wave, or four where the routed rows are
+  // short (one 8 * lpr step) and d is wide: a small-group block then streams
+  // a few KB over hundreds of column tiles per group, and doubling its
+  // columns halves the blocks.  Measured on the DeaMoE transform of the
+  // DeepSeek-V3-shaped layer (d = 7168, private rows 256): down 168 -> 153 us
+  // at batch 8 and 224 -> 199 us at 16; on the DeepSeek-V3-shaped layer
+  // itself (rows 2048) four groups ran 9% slower at batch 4, and at d = 2048
+  // they gained nothing.
+  const int rr = family_rows(d, 0);
+  c.col_groups = d.d_model > 2048 && rr > 0 && rr <= 8 * lpr ? 4 : 2;
   return c;
 }
 

@@ -1642,7 +1642,8 @@ __device__ __forceinline__ void dn_small_lds(const T_* __restrict__ Wd, int d, i
                                              const T_* __restrict__ h, const Slot& sl,
                                              float* __restrict__ out, int epi, int lane, int wid,
                                              SmallLds<T_>& lds) {
-  constexpr int NT = kTokInline, R = kStageRing, STEP = 8 * LPR;
+  // (wider column groups take a shallower ring: the same loads in flight)
+  constexpr int NT = kTokInline, R = CG > 2 ? 2 * kStageRing / CG : kStageRing, STEP = 8 * LPR;
   constexpr int G = 64 / LPR;
   const int g = lane / LPR, j = lane - g * LPR;
   const int nv = sl.n;
@@ -3511,11 +3512,11 @@ static hipError_t launch_down_t(const FamilySet& set, int T, int d, int lpr, int
   (xl ? launch(down_kernel<T_, L, C, true>, grid, block, st, ev, set, T, d) \
       : launch(down_kernel<T_, L, C, false>, grid, block, st, ev, set, T, d))
   if (lpr == 16) {
-    if (cg >= 2) MOE_DOWN(16, 2); else MOE_DOWN(16, 1);
+    if (cg >= 4) MOE_DOWN(16, 4); else if (cg >= 2) MOE_DOWN(16, 2); else MOE_DOWN(16, 1);
   } else if (lpr == 32) {
-    if (cg >= 2) MOE_DOWN(32, 2); else MOE_DOWN(32, 1);
+    if (cg >= 4) MOE_DOWN(32, 4); else if (cg >= 2) MOE_DOWN(32, 2); else MOE_DOWN(32, 1);
   } else {
-    if (cg >= 2) MOE_DOWN(64, 2); else MOE_DOWN(64, 1);
+    if (cg >= 4) MOE_DOWN(64, 4); else if (cg >= 2) MOE_DOWN(64, 2); else MOE_DOWN(64, 1);
   }
 #undef MOE_DOWN
   return hipGetLastError();
