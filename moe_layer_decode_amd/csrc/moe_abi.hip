@@ -460,22 +460,21 @@ FamilySet make_families(const moe_layer_desc& d, const moe_weights& w, const moe
 // GEMV configuration; large parts of bf16 layers by one 64-row (gate/up) or
 // 64-column (down) matrix-core tile per block (each wave 16 of them over the
 // whole K), except at T <= kSplitKMaxT, where no group passes 16 rows: there
-// gate/up at d <= kSplitKMaxD takes one 16-row tile per block, and down at
-// d > kSplitKMaxD (intermediate width >= kSplitKMinK) kSplitKCols columns per
-// block, the four waves splitting K.  Measured at batch 16: K-split gate/up
-// is faster at d = 2048 and slower at d = 7168; K-split down is 2-3% faster
-// at d = 7168 (both DeepSeek-V3-shaped forms) but 5% slower for the
-// DeaMoE-7B-shaped department groups at d = 2048, and slower still over
-// 128-wide experts, where a wave's quarter of K is half a tile.  fp32 layers
-// tile by 16 rows or columns.
+// gate/up takes one 16-row tile per block, and down at d > kSplitKDownMinD
+// (intermediate width >= kSplitKMinK) kSplitKCols columns per block, the four
+// waves splitting K.  Measured at batch 16: K-split gate/up is faster at
+// d = 2048 and at d = 7168 (the DeaMoE transform of the DeepSeek-V3-shaped
+// layer: 382 -> 369 us); K-split down is 2-3% faster at d = 7168 but 5%
+// slower for the DeaMoE-7B-shaped department groups at d = 2048, and slower
+// still over 128-wide experts, where a wave's quarter of K is half a tile.
+// fp32 layers tile by 16 rows or columns.
 void set_tiles(FamilySet& set, int d, bool gateup, int w_dtype, const moe::GemvConfig& c,
                int T) {
   set.blk_start[0] = 0;
   for (int i = 0; i < set.n; ++i) {
     Family& f = set.f[i];
     f.splitk = w_dtype == MOE_BF16 && f.large && T <= moe::kSplitKMaxT &&
-               (gateup ? d <= moe::kSplitKMaxD
-                       : d > moe::kSplitKMaxD && f.rows >= moe::kSplitKMinK);
+               (gateup || (d > moe::kSplitKDownMinD && f.rows >= moe::kSplitKMinK));
     const int lt = w_dtype != MOE_BF16        ? 16
                    : !f.splitk                ? moe::kWideRows
                    : gateup                   ? 16

@@ -14,9 +14,9 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRouteChunk = 512;     // d elements one router wave covers (64 lanes x 8)
 constexpr int kTokInline = 4;        // tokens carried inline in a work descriptor
 constexpr int kWideRows = 64;        // rows / columns of a bf16 large-group tile (unless split K)
-constexpr int kSplitKMaxT = 16;      // K-split gate/up tiles: T at most (every group <= 16 rows)
-constexpr int kSplitKMaxD = 2048;    //   and d at most (K-split down tiles: d above it)
-constexpr int kSplitKCols = 32;      // K-split down tiles (T <= kSplitKMaxT): output columns per block
+constexpr int kSplitKMaxT = 16;      // K-split tiles: T at most (every group <= 16 rows)
+constexpr int kSplitKCols = 32;      // K-split down tiles: output columns per block,
+constexpr int kSplitKDownMinD = 2048;  //   d above it
 constexpr int kSplitKMinK = 256;     //   and intermediate width at least (a full K tile per wave)
 constexpr int kPlanThreads = 1024;   // threads of the single-block top-k / plan kernel
 constexpr int kMaxRouteSplit = 8;   // partial-logit planes of the bf16 router at most

@@ -1721,11 +1721,11 @@ __device__ __forceinline__ void dn_small_lds(const T_* __restrict__ Wd, int d, i
 // l%16.  A dot product is indifferent to the order of k, so each lane simply
 // takes the 16-byte chunk at 8g of every 32-element step.
 
-// K-split gate/up tiles (decode batches with d <= kSplitKMaxD): the four waves
-// of a block share one 16-row tile and each streams a quarter of K, two
-// 32-wide steps ahead of the matrix-core work, its token inputs read directly
-// (L2); the four partial tiles are then added in wave order through LDS, so
-// results do not depend on timing.
+// K-split tiles (decode batches, T <= kSplitKMaxT): the four waves of a
+// block share one 16-row tile (gate/up; two 16-column tiles for down) and
+// each streams a quarter of K through a ring of LDS weight tiles (below), its
+// token inputs read directly (L2); the four partial tiles are then added in
+// wave order through LDS, so results do not depend on timing.
 
 
 // Per-wave K range [kb, ke) of a K-split tile: quarters rounded up to 32.
