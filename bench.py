@@ -139,9 +139,11 @@ def trace_report(trace_csv, bench_json):
         print(f"| {T} | {r['us']} | {r['GBps']} | {st['route']} | {st['dispatch']} | {st['gateup']} "
               f"| {st['down']} | {st['combine']} |")
     rf = b["roofline"]
-    grids = sorted((gx, v) for (k, gx, gy), v in acc.items() if k == rf["kernel"])
-    gx, v = grids[-1] if grids else (0, [0.0])
-    mean = sum(v) / len(v)
+    # the roofline launch's own grid (other shapes timed in the same run give
+    # the kernel other grids)
+    gx = rf.get("grid_workitems", 0)
+    v = [d for (k, g, gy), vals in acc.items() if k == rf["kernel"] and g == gx for d in vals]
+    mean = sum(v) / len(v) if v else float("nan")
     print(f"\nRoofline ({rf['kernel']}, batch {head_T}): {rf['achieved']} GB/s of {rf['peak']} GB/s "
           f"= {rf['frac']} ({rf['algorithmic_bytes_per_launch']} algorithmic bytes per launch / "
           f"{rf['launch_us']} us event-timed launch); the trace gives the same kernel at the "
@@ -777,6 +779,9 @@ def main():
                      "traffic": measured_traffic() if shape.name == HEADLINE and head_T == 16 else None,
                      "algorithmic_bytes_per_launch": gu,
                      "launch_us": round(stages["gateup"], 2),
+                     # the launch's grid as a kernel trace reports it (work-items)
+                     "grid_workitems": M.moe_layer_launch_workitems(desc_of(M, shape, head_T),
+                                                                    head_T, M.STAGE_GATEUP),
                      "measured_peak": meas_peak,
                      "frac_measured_peak": round(achieved / meas_peak, 4)},
     }

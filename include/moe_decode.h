@@ -378,8 +378,17 @@ moe_status moe_layer_decode_noalloc(const moe_layer_desc* desc, const moe_weight
  * plain and slice forms at T <= 4 whose rows of h fit its LDS budget -- the
  * combine stage is then an empty interval); 8 in the factorised form
  * (backbone gate/up, private gate/up, private down, pair sums, department
- * down). */
+ * down).  One more where the selection runs per token ahead of a separate
+ * plan launch (T > 16, or more than 256 experts). */
 int32_t moe_layer_kernel_count(const moe_layer_desc* desc, int32_t T);
+
+/* Host-only: work-items of the grouped gate/up (stage MOE_STAGE_GATEUP) or
+ * down (MOE_STAGE_DOWN) launch of moe_layer_decode for T tokens -- the grid
+ * is sized on the host from T alone, so a profiler's kernel trace can be
+ * matched to a stage by its grid size.  Plain and slice forms with bf16 or
+ * fp32 weights; 0 for T = 0, FP8 weights or the factorised form; -1 for an
+ * invalid descriptor, T or stage. */
+int64_t moe_layer_launch_workitems(const moe_layer_desc* desc, int32_t T, int32_t stage);
 
 /* Bytes of weights one step streams for the given active counts: router,
  * n_active routed experts, n_active_depts department slices, the shared

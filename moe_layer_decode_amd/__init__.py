@@ -22,12 +22,14 @@ __all__ = [
     "moe_workspace_bytes", "moe_workspace_init", "moe_validate_desc", "moe_route", "moe_dispatch",
     "moe_expert_ffn", "moe_combine", "moe_layer_decode", "moe_layer_decode_timed",
     "moe_layer_decode_noalloc", "NOALLOC_SCRATCH_BYTES", "moe_status_string", "StepStats", "STEP_STATS_BYTES", "alloc_step_stats", "step_stats_to_host",
-    "moe_loaded_weight_bytes", "moe_stream_read", "moe_layer_kernel_count", "alloc_workspace",
+    "moe_loaded_weight_bytes", "moe_stream_read", "moe_layer_kernel_count",
+    "moe_layer_launch_workitems", "alloc_workspace",
     "plan_to_host", "MoeLayer",
     "MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE",
     "MOE_ERR_HIP", "SCORE_FNS", "DEPT_FORMS", "MOE_DEPT_SLICE", "MOE_DEPT_FACTORISED",
     "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3",
-    "N_STAGES", "STAGE_NAMES", "EXPORTED_SYMBOLS",
+    "N_STAGES", "STAGE_NAMES", "STAGE_ROUTE", "STAGE_DISPATCH", "STAGE_GATEUP", "STAGE_DOWN",
+    "STAGE_COMBINE", "EXPORTED_SYMBOLS",
 ]
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
@@ -39,10 +41,12 @@ PLAN_HEADER_LEN = 16
 PLAN_N_ROWS, PLAN_N_ACTIVE, PLAN_N_DEPT_ROWS, PLAN_N_ACTIVE_DEPTS, PLAN_N_INVALID = range(5)
 N_STAGES = 5
 STAGE_NAMES = ("route", "dispatch", "gateup", "down", "combine")
+STAGE_ROUTE, STAGE_DISPATCH, STAGE_GATEUP, STAGE_DOWN, STAGE_COMBINE = range(N_STAGES)
 EXPORTED_SYMBOLS = (
     "moe_workspace_bytes", "moe_workspace_init", "moe_validate_desc", "moe_plan_from_workspace", "moe_route",
     "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_layer_decode", "moe_layer_decode_timed",
     "moe_layer_decode_noalloc", "moe_status_string", "moe_loaded_weight_bytes", "moe_stream_read", "moe_layer_kernel_count",
+    "moe_layer_launch_workitems",
 )
 
 _i32, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -152,6 +156,8 @@ def lib() -> ctypes.CDLL:
     L.moe_stream_read.restype = _i32
     L.moe_layer_kernel_count.argtypes = [P(LayerDesc), _i32]
     L.moe_layer_kernel_count.restype = _i32
+    L.moe_layer_launch_workitems.argtypes = [P(LayerDesc), _i32, _i32]
+    L.moe_layer_launch_workitems.restype = ctypes.c_int64
     _LIB = L
     return L
 
@@ -210,6 +216,13 @@ def moe_layer_kernel_count(desc: LayerDesc, T: int) -> int:
     """Kernels moe_layer_decode launches for T tokens (4: the down launch
     writes y itself and the combine stage is empty)."""
     return int(lib().moe_layer_kernel_count(ctypes.byref(desc), T))
+
+
+def moe_layer_launch_workitems(desc: LayerDesc, T: int, stage: int) -> int:
+    """Work-items of the gate/up (STAGE_GATEUP) or down (STAGE_DOWN) launch of
+    a decode step of T tokens, as a profiler's kernel trace reports its grid
+    (0 where not reported: FP8 weights, the factorised form)."""
+    return int(lib().moe_layer_launch_workitems(ctypes.byref(desc), T, stage))
 
 
 def moe_workspace_init(desc: LayerDesc, workspace: torch.Tensor):

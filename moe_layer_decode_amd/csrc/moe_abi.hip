@@ -946,7 +946,8 @@ moe_status moe_layer_decode_noalloc(const moe_layer_desc* desc, const moe_weight
 int32_t moe_layer_kernel_count(const moe_layer_desc* desc, int32_t T) {
   if (check_desc(desc) != MOE_OK || check_tokens(desc, T) != MOE_OK) return -1;
   if (T == 0) return 0;
-  if (factorised(*desc)) return 8;
+  const int split = moe::topk_in_one_block(T, desc->n_experts) ? 0 : 1;
+  if (factorised(*desc)) return 8 + split;
   // the eligibility test reads only the descriptor and T; the addresses it
   // forms from a workspace base are never dereferenced here
   void* base = reinterpret_cast<void*>(uintptr_t(1) << 20);
@@ -954,7 +955,29 @@ int32_t moe_layer_kernel_count(const moe_layer_desc* desc, int32_t T) {
   moe_plan p;
   fill_plan(*desc, base, T, &p);
   moe::DownCombineArgs a;
-  return down_combine_args(*desc, w, p, base, T, &a) ? 4 : 5;
+  return (down_combine_args(*desc, w, p, base, T, &a) ? 4 : 5) + split;
+}
+
+int64_t moe_layer_launch_workitems(const moe_layer_desc* desc, int32_t T, int32_t stage) {
+  if (check_desc(desc) != MOE_OK || check_tokens(desc, T) != MOE_OK) return -1;
+  if (stage != MOE_STAGE_GATEUP && stage != MOE_STAGE_DOWN) return -1;
+  if (T == 0 || factorised(*desc) || fp8(*desc)) return 0;
+  // grids are sized on the host from T alone; the workspace addresses formed
+  // here are never dereferenced
+  void* base = reinterpret_cast<void*>(uintptr_t(1) << 20);
+  const Layout L = layout_of(*desc);
+  moe_weights w{};
+  moe_plan p;
+  fill_plan(*desc, base, T, &p);
+  moe::DownCombineArgs a;
+  if (stage == MOE_STAGE_DOWN && down_combine_args(*desc, w, p, base, T, &a))
+    return (int64_t)ceil_div(desc->d_model, moe::kDcWaves) * moe::kDcWaves * 64;
+  FamilySet set = make_families(*desc, w, p, base, T, at<float>(base, L, R_ROW_OUT),
+                                desc->n_depts > 0 ? at<float>(base, L, R_DEPT_OUT) : nullptr,
+                                desc->d_ff_shared > 0 ? at<float>(base, L, R_SHARED_OUT) : nullptr);
+  set_tiles(set, desc->d_model, stage == MOE_STAGE_GATEUP, desc->w_dtype,
+            choose_config(*desc, T), T);
+  return (int64_t)set.blk_start[set.n] * moe::kThreads;
 }
 
 const char* moe_status_string(moe_status status) {

@@ -19,6 +19,11 @@ constexpr int kSplitKCols = 32;      // K-split down tiles: output columns per b
 constexpr int kSplitKDownMinD = 2048;  //   d above it
 constexpr int kSplitKMinK = 256;     //   and intermediate width at least (a full K tile per wave)
 constexpr int kPlanThreads = 1024;   // threads of the single-block top-k / plan kernel
+// Top-k + plan in one block (a wave per token, at most 256 experts), or the
+// per-token selections across the chip followed by a one-block plan launch.
+inline bool topk_in_one_block(int T, int E) {
+  return T <= kPlanThreads / 64 && (E + 63) / 64 <= 4;
+}
 constexpr int kMaxRouteSplit = 8;   // partial-logit planes of the bf16 router at most
 constexpr int kMaxParts = 6;         // 3 matrix families x (small groups, large groups)
 // Plan header entries beyond the public ones: lengths of the compacted work

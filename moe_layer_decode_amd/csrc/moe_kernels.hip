@@ -3400,7 +3400,7 @@ static hipError_t launch_route_t(const RouteArgs& ra, const PlanArgs* pa, hipStr
   // enforced (its own instances)
   const bool grouped = ra.k_dept > 0 && (ra.k_dept < ra.m || ra.strict);
   const int npl = (ra.E + kWave - 1) / kWave;
-  if (ra.T <= kPlanWaves && npl <= 4) {
+  if (topk_in_one_block(ra.T, ra.E)) {
     // one block: a wave per token, then the plan from LDS
     const dim3 grid(1), block(kPlanThreads);
     auto go = [&](auto N) {

@@ -15,7 +15,7 @@ def _declared_functions():
     with open(os.path.join(ROOT, "include", "moe_decode.h")) as f:
         src = f.read()
     return sorted(set(re.findall(
-        r"^(?:const char\*|size_t|moe_status|uint64_t|int32_t)\s+(moe_\w+)\(", src, re.M)))
+        r"^(?:const char\*|size_t|moe_status|uint64_t|int64_t|int32_t)\s+(moe_\w+)\(", src, re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -278,6 +278,40 @@ def test_layer_kernel_count(lib):
     fac = _desc(n_experts=32, top_k=6, d_ff=256, n_depts=4, d_ff_dept=256,
                 dept_form="factorised")
     assert M.moe_layer_kernel_count(fac, 3) == 8
+    # the selection per token ahead of a separate plan launch: past 16 tokens,
+    # or past 256 experts
+    big = _desc(max_tokens=64)
+    assert [M.moe_layer_kernel_count(big, T) for T in (16, 17, 64)] == [5, 6, 6]
+    wide = _desc(n_experts=512, max_tokens=4)
+    assert [M.moe_layer_kernel_count(wide, T) for T in (1, 4)] == [5, 5]
+    assert M.moe_layer_kernel_count(_desc(n_experts=256, max_tokens=4), 1) == 4
+    fac_wide = _desc(n_experts=864, top_k=10, d_ff=2048, n_depts=8, d_ff_dept=2048,
+                     dept_form="factorised", k_dept=5, max_tokens=16)
+    assert M.moe_layer_kernel_count(fac_wide, 1) == 9
+
+
+def test_layer_launch_workitems(lib):
+    """Grids of the gate/up and down launches as a kernel trace reports them:
+    whole 256-thread blocks; the down launch that writes y
+    has one 512-thread block per 8 output columns; not reported for FP8 or
+    the factorised form; -1 for a stage that is no grouped launch."""
+    q = _desc(max_tokens=32)
+    G, D = M.STAGE_GATEUP, M.STAGE_DOWN
+    gu = [M.moe_layer_launch_workitems(q, T, G) for T in (1, 4, 16, 32)]
+    assert all(g > 0 and g % 256 == 0 for g in gu)
+    assert M.moe_layer_launch_workitems(q, 1, D) == 2048 // 8 * 512
+    assert M.moe_layer_launch_workitems(q, 16, D) % 256 == 0
+    assert M.moe_layer_launch_workitems(q, 16, D) != 2048 // 8 * 512
+    # gate/up at T = 1: each active-expert slot (at most 8) streams 768 rows, a
+    # row per wave of one 4-wave block
+    assert gu[0] == 8 * (768 // 4) * 256
+    assert M.moe_layer_launch_workitems(q, 0, G) == 0
+    assert M.moe_layer_launch_workitems(_desc(expert_dtype="fp8"), 1, G) == 0
+    fac = _desc(n_experts=32, top_k=6, d_ff=256, n_depts=4, d_ff_dept=256,
+                dept_form="factorised")
+    assert M.moe_layer_launch_workitems(fac, 1, G) == 0
+    assert M.moe_layer_launch_workitems(q, 1, M.STAGE_ROUTE) == -1
+    assert M.moe_layer_launch_workitems(q, 33, G) == -1
 
 
 def test_step_stats_layout_matches_the_header(tmp_path):
