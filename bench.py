@@ -17,6 +17,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import re
 import math
 import os
 import sys
@@ -111,6 +112,11 @@ def summarize_trace(path):
         print(f"| {k} | {gx} | {gy} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} |")
 
 
+def shape_tag(name):
+    """Short name of a layer shape for output paths: the part before its sizes."""
+    return re.split(r"_d[0-9]", name)[0]
+
+
 def trace_report(trace_csv, bench_json):
     """Markdown summary: the kernel trace of a profiled default run, the
     unprofiled run's per-batch stage times, and the roofline kernel's
@@ -118,12 +124,22 @@ def trace_report(trace_csv, bench_json):
     b = json.loads(open(bench_json).read().strip().splitlines()[-1])
     acc = trace_means(trace_csv)
     head_T = b["config"]["batch"]
-    print(f"# Kernel trace: bench.py default run ({b['config']['workload'].split(' MoE')[0]}, "
-          f"batches {'/'.join(b['batches'])})\n")
+    shape = b["config"]["workload"].split(" MoE")[0]
+    batches = "/".join(b["batches"])
+    # the commands as run: the default run, or one shape at its batches
+    if shape == HEADLINE:
+        what, args, tag = "bench.py default run", "", "bench"
+    else:
+        tag = shape_tag(shape)
+        what = "bench.py, one layer shape"
+        args = f" --shape {shape} --batches {batches.replace('/', ',')} --no-cpu-baseline --no-dept"
+    print(f"# Kernel trace: {what} ({shape}, batches {batches})\n")
     print("Command (repo root, one MI355X):\n\n```")
-    print("rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_bench -o run -- python -u bench.py")
-    print("python bench.py > gpurun_out/bench.json")
-    print("python bench.py --trace-report gpurun_out/prof_bench/run_kernel_trace.csv gpurun_out/bench.json")
+    print(f"rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_{tag} -o run -- "
+          f"python -u bench.py{args}")
+    print(f"python bench.py{args} > gpurun_out/{tag}.json")
+    print(f"python bench.py --trace-report gpurun_out/prof_{tag}/run_kernel_trace.csv "
+          f"gpurun_out/{tag}.json")
     print("```\n")
     print("Per-kernel durations, split by grid size (grid x = work-items; each decode batch gives "
           "its own grid per expert kernel). `__amd_rocclr_copyBuffer` rows are the weight-replica "
@@ -197,12 +213,23 @@ def pmc_report(fetch_csv, write_csv, meta_path):
     fetch, write = out["FETCH_SIZE"][1], out["WRITE_SIZE"][1]
     shape = meta.get("shape", HEADLINE)
     T = meta.get("batch", HEADLINE_T)
+    # the commands as run: the headline shape with the default paths, any
+    # other shape with its own name, output folders and pass record
+    if shape == HEADLINE:
+        extra, fdir, wdir, meta_arg = "", "pmc_fetch", "pmc_write", ""
+    else:
+        tag = shape_tag(shape)
+        extra = f" --shape {shape} --profile-meta gpurun_out/profile_pass_{tag}.json"
+        fdir, wdir = f"pmc_{tag}_fetch", f"pmc_{tag}_write"
+        meta_arg = f" --profile-meta gpurun_out/profile_pass_{tag}.json"
     print(f"# HBM traffic of the layer kernels, {shape}, batch {T}\n")
     print("Commands (repo root, one MI355X; one counter per pass):\n\n```")
-    print("rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o run -- python -u bench.py --profile-pass")
-    print("rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o run -- python -u bench.py --profile-pass")
-    print("python bench.py --pmc-report gpurun_out/pmc_fetch/run_counter_collection.csv "
-          "gpurun_out/pmc_write/run_counter_collection.csv")
+    print(f"rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/{fdir} -o run -- python -u bench.py "
+          f"--profile-pass{extra}")
+    print(f"rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/{wdir} -o run -- python -u bench.py "
+          f"--profile-pass{extra}")
+    print(f"python bench.py --pmc-report gpurun_out/{fdir}/run_counter_collection.csv "
+          f"gpurun_out/{wdir}/run_counter_collection.csv{meta_arg}")
     print("```\n")
     print(f"`--profile-pass` runs 20 eager batch-{T} steps, then a plain 1 GiB write (torch `fill_`) "
           "and a plain 1 GiB read (torch `sum`); the largest counter value after the last layer "
@@ -426,7 +453,7 @@ def sweep_report(path):
             rows.append(r)
     print("# Every layer shape at its batches: graph-replayed decode step\n")
     print("Command (repo root, one MI355X):\n\n```")
-    print("python bench.py --sweep --sweep-out gpurun_out/sweep.jsonl")
+    print("python bench.py --sweep --sweep-out gpurun_out/sweep.jsonl --no-cpu-baseline --no-dept")
     print("python bench.py --sweep-report gpurun_out/sweep.jsonl")
     print("```\n")
     print("Weights bytes are the distinct weights one step streams (router, active experts, "
