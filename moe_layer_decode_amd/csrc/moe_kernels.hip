@@ -213,6 +213,23 @@ __device__ __forceinline__ float route_aux(const RouteArgs& p, float l) {
   return p.score_fn == MOE_SCORE_SIGMOID ? 1.0f / (1.0f + expf(-l)) : l;
 }
 
+// The ksplit partial logits of expert e for token t (planes past ksplit read
+// 0), and its selection bias (0 without one).  Every load is unconditional --
+// a plane past ksplit re-reads plane 0, the bias of a layer without one reads
+// a logit -- and the values are selected afterwards: a load under a branch
+// would end in a wait for every load in flight at the branch's join.
+__device__ __forceinline__ void logit_parts(const RouteArgs& p, int t, int e,
+                                            float (&v)[kMaxRouteSplit], float& b) {
+  const float* bp = p.bias ? p.bias : p.logits;
+  const float bv = bp[e];
+#pragma unroll
+  for (int q = 0; q < kMaxRouteSplit; ++q)
+    v[q] = p.logits[((size_t)(q < p.ksplit ? q : 0) * p.T + t) * p.E + e];
+#pragma unroll
+  for (int q = 0; q < kMaxRouteSplit; ++q) v[q] = q < p.ksplit ? v[q] : 0.f;
+  b = p.bias ? bv : 0.f;
+}
+
 // One token's row by its own wave (lane l: experts l, l+64, ...), for
 // layers with few experts per lane: the planes of all NPL entries are
 // requested before the first add waits, and no block barrier is needed.  The
@@ -227,15 +244,9 @@ __device__ void stage_token(const RouteArgs& p, int t, int row, int lane, PlanSh
   constexpr int CH = NPL < 4 ? NPL : 4;
 #pragma unroll
   for (int i0 = 0; i0 < NPL; i0 += CH) {
-    float v[kMaxRouteSplit][CH], b[CH];
+    float v[CH][kMaxRouteSplit], b[CH];
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int e = min(lane + kWave * (i0 + i), E - 1);
-      b[i] = p.bias ? p.bias[e] : 0.f;
-#pragma unroll
-      for (int q = 0; q < kMaxRouteSplit; ++q)
-        v[q][i] = q < p.ksplit ? p.logits[((size_t)q * p.T + t) * E + e] : 0.f;
-    }
+    for (int i = 0; i < CH; ++i) logit_parts(p, t, min(lane + kWave * (i0 + i), E - 1), v[i], b[i]);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int e = lane + kWave * (i0 + i);
@@ -243,7 +254,7 @@ __device__ void stage_token(const RouteArgs& p, int t, int row, int lane, PlanSh
       if (e < E) {
         float l = 0.f;
 #pragma unroll
-        for (int q = 0; q < kMaxRouteSplit; ++q) l += q < p.ksplit ? v[q][i] : 0.f;
+        for (int q = 0; q < kMaxRouteSplit; ++q) l += v[i][q];
         const float sc = p.score_fn == MOE_SCORE_SOFTMAX ? l : route_aux(p, l) + b[i];
         if (p.sel_out) p.sel_out[(size_t)t * E + e] = sc;
         s.tk.lg[row + e] = l;
@@ -324,9 +335,9 @@ __device__ __forceinline__ void select_rank(const uint32_t (&key)[NP], EidOf eid
 // block's waves when every wave selects a token at once).  Taken entries drop
 // to key 0 and stay out of later ties through the per-plane taken masks.
 constexpr int kExtractMaxK = 16;
+constexpr int kDeptRankMax = 32;  // departments ranked by a per-lane count at most
 template <int NP>
-__device__ __forceinline__ void select_extract(uint32_t (&key)[NP], int k, int lane,
-                                               int* slot_id) {
+__device__ __forceinline__ int extract_positions(uint32_t (&key)[NP], int k, int lane) {
   uint64_t taken[NP];
 #pragma unroll
   for (int i = 0; i < NP; ++i) taken[i] = 0ull;
@@ -356,7 +367,25 @@ __device__ __forceinline__ void select_extract(uint32_t (&key)[NP], int k, int l
     }
     my_id = lane == r ? pl + kWave * pi : my_id;
   }
+  return my_id;
+}
+template <int NP>
+__device__ __forceinline__ void select_extract(uint32_t (&key)[NP], int k, int lane,
+                                               int* slot_id) {
+  const int my_id = extract_positions<NP>(key, k, lane);
   if (lane < k) slot_id[lane] = my_id;
+}
+
+// The k-th largest of the wave's 64 keys (one per lane; k <= 64), by k
+// rounds of a wave maximum that each retire one lane holding it.
+__device__ __forceinline__ uint32_t kth_largest_extract(uint32_t v, int k, int lane) {
+  uint32_t M = 0u;
+  for (int r = 0; r < k; ++r) {
+    M = wave_max_u32(v);
+    const int l0 = __builtin_ctzll(__ballot(v == M));
+    v = lane == l0 ? 0u : v;
+  }
+  return M;
 }
 
 // Top-k of token t by one wave from the staged row `row` (lane l holds experts
@@ -407,13 +436,26 @@ __device__ void topk_token(const RouteArgs& p, int t, int row, int lane, PlanSha
       dkey = (uint32_t)__shfl((int)v, min(lane, p.m - 1) * L, kWave);
       dkey = lane < p.m ? dkey : 0u;
     }
-    const uint32_t dkeys[1] = {dkey};
-    const uint32_t dthr = kth_largest_key<1>(dkeys, kd);
-    const int dabove = wave_count(dkey > dthr);
-    const uint64_t deq = __ballot(lane < p.m && dkey == dthr);
-    const bool dtake = lane < p.m && (dkey > dthr ||
-                                      (dkey == dthr && __popcll(deq & ((1ull << lane) - 1ull)) <
-                                                           kd - dabove));
+    bool dtake;
+    if (p.m <= kDeptRankMax) {
+      // few departments: each lane counts the departments ranked above its
+      // own (key desc, index asc) -- m vector steps instead of 32 rounds of
+      // a bitwise select
+      int above = 0;
+      for (int j = 0; j < p.m; ++j) {
+        const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)dkey, j);
+        above += (kj > dkey || (kj == dkey && j < lane)) ? 1 : 0;
+      }
+      dtake = lane < p.m && above < kd;
+    } else {
+      const uint32_t dkeys[1] = {dkey};
+      const uint32_t dthr = kth_largest_key<1>(dkeys, kd);
+      const int dabove = wave_count(dkey > dthr);
+      const uint64_t deq = __ballot(lane < p.m && dkey == dthr);
+      dtake = lane < p.m && (dkey > dthr ||
+                             (dkey == dthr && __popcll(deq & ((1ull << lane) - 1ull)) <
+                                                  kd - dabove));
+    }
     chosen_depts = __ballot(dtake);
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
@@ -423,14 +465,16 @@ __device__ void topk_token(const RouteArgs& p, int t, int row, int lane, PlanSha
   }
   // candidate cut (8 or more planes; with fewer a direct select is
   // cheaper): the k-th largest lane maximum, at least 1 so that key-0
-  // entries never qualify
+  // entries never qualify; k rounds of a wave maximum for k <= kExtractMaxK,
+  // else a bitwise select
   int n_cand = 0;
   uint32_t cut = 1u;
   if constexpr (NPL >= 8) {
     uint32_t lmax[1] = {0u};
 #pragma unroll
     for (int i = 0; i < NPL; ++i) lmax[0] = key[i] > lmax[0] ? key[i] : lmax[0];
-    const uint32_t c0 = kth_largest_key<1>(lmax, k);
+    const uint32_t c0 =
+        k <= kExtractMaxK ? kth_largest_extract(lmax[0], k, lane) : kth_largest_key<1>(lmax, k);
     cut = c0 > 1u ? c0 : 1u;
 #pragma unroll
     for (int i = 0; i < NPL; ++i) n_cand += wave_count(key[i] >= cut);
@@ -467,7 +511,14 @@ __device__ void topk_token(const RouteArgs& p, int t, int row, int lane, PlanSha
     // the list is rewritten with the chosen only after every lane has read it
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    select_rank<NC>(ckey, [&](int i, int) { return cexp[i]; }, k, lane, ck, ce, slot_id);
+    if (k <= kExtractMaxK) {
+      // candidates are in expert order, so the lowest position among equal
+      // keys is the lowest expert
+      const int pos = extract_positions<NC>(ckey, k, lane);
+      if (lane < k) slot_id[lane] = ce[pos];
+    } else {
+      select_rank<NC>(ckey, [&](int i, int) { return cexp[i]; }, k, lane, ck, ce, slot_id);
+    }
   } else if (NPL <= 4 && k <= kExtractMaxK) {
     select_extract<NPL>(key, k, lane, slot_id);
   } else {
@@ -1099,20 +1150,15 @@ __global__ __launch_bounds__(kThreads) void topk_token_kernel(RouteArgs ra) {
     constexpr int PER = (NPL * kWave + kThreads - 1) / kThreads;  // experts per thread
     float v[PER][kMaxRouteSplit], b[PER];
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int e = min((int)threadIdx.x + u * kThreads, E - 1);
-      b[u] = ra.bias ? ra.bias[e] : 0.f;
-#pragma unroll
-      for (int q = 0; q < kMaxRouteSplit; ++q)
-        v[u][q] = q < ra.ksplit ? ra.logits[((size_t)q * ra.T + t) * E + e] : 0.f;
-    }
+    for (int u = 0; u < PER; ++u)
+      logit_parts(ra, t, min((int)threadIdx.x + u * kThreads, E - 1), v[u], b[u]);
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int e = threadIdx.x + u * kThreads;
       if (e < E) {
         float l = 0.f;
 #pragma unroll
-        for (int q = 0; q < kMaxRouteSplit; ++q) l += q < ra.ksplit ? v[u][q] : 0.f;
+        for (int q = 0; q < kMaxRouteSplit; ++q) l += v[u][q];
         const float sc = ra.score_fn == MOE_SCORE_SOFTMAX ? l : route_aux(ra, l) + b[u];
         if (ra.sel_out) ra.sel_out[(size_t)t * E + e] = sc;
         s.tk.lg[e] = l;
