@@ -160,6 +160,10 @@ constexpr int kTopkBuf = 10240;   // staged (token, expert) entries per chunk
 constexpr int kCand = 128;        // compacted candidates per token
 constexpr int kPlanWaves = kPlanThreads / kWave;
 constexpr int kRankMaskWords = 1024;
+constexpr int kDeptMaskMax = 64;
+__device__ __forceinline__ bool dept_masks(int T, int m) {
+  return m > 0 && m <= kDeptMaskMax && T <= 64;
+}
 __device__ __forceinline__ int rank_mask_words(int T, int E) {
   const int nwt = (T + 63) >> 6;
   return nwt * E <= kRankMaskWords ? nwt : 0;
@@ -190,6 +194,10 @@ struct PlanShared {
   // rows is then a popcount of the lower tokens instead of a scan of the
   // earlier assignments.
   unsigned long long tmask[kRankMaskWords];
+  // Tokens of each department as bits (bit t of word J) when T <= 64 and
+  // m <= kDeptMaskMax: a pair's rank among its department's pairs is then a
+  // popcount of the lower tokens instead of a scan of the pair flags.
+  unsigned long long dtok[kDeptMaskMax];
   union {
     TopkStage tk;
     PlanWork pw;
@@ -632,7 +640,11 @@ __device__ void topk_token(const RouteArgs& p, int t, int row, int lane, PlanSha
       atomicAdd(&s.cnt[my_id], 1);
       const int nwt = rank_mask_words(p.T, E);
       if (nwt > 0) atomicOr(&s.tmask[my_id * nwt + (t >> 6)], 1ull << (t & 63));
-      if (p.m > 0) s.flag[t * p.m + my_id / (E / p.m)] = 1;
+      if (p.m > 0) {
+        const int J = my_id / (E / p.m);
+        s.flag[t * p.m + J] = 1;
+        if (dept_masks(p.T, p.m)) atomicOr(&s.dtok[J], 1ull << t);
+      }
     }
   }
 }
@@ -655,7 +667,10 @@ __device__ void dept_scan(PlanShared& s, const PlanArgs& pa, int lane) {
   int sc = 0, sa = 0, ss = 0;
   for (int J = b; J < en; ++J) {
     int c = 0;
-    for (int t = 0; t < T; ++t) c += s.flag[t * m + J];
+    if (dept_masks(T, m))
+      c = __popcll(s.dtok[J]);
+    else
+      for (int t = 0; t < T; ++t) c += s.flag[t * m + J];
     s.pw.dcnt[J] = c;
     sc += c;
     sa += c > 0 ? 1 : 0;
@@ -799,7 +814,10 @@ __device__ void plan_phase(PlanShared& s, const PlanArgs& pa, bool masks) {
       if (pa.factorised) {
         const int J = e / G;
         int rd = 0;
-        for (int u = 0; u < t; ++u) rd += s.flag[u * m + J];
+        if (dept_masks(T, m))
+          rd = __popcll(s.dtok[J] & ((1ull << t) - 1ull));
+        else
+          for (int u = 0; u < t; ++u) rd += s.flag[u * m + J];
         in = s.pw.doff[J] + rd;
         P.row_pair[row] = in;
       }
@@ -815,7 +833,10 @@ __device__ void plan_phase(PlanShared& s, const PlanArgs& pa, bool masks) {
     const int t = p / m, J = p - t * m;
     if (s.flag[p]) {
       int rank = 0;
-      for (int u = 0; u < t; ++u) rank += s.flag[u * m + J];
+      if (dept_masks(T, m))
+        rank = __popcll(s.dtok[J] & ((1ull << t) - 1ull));
+      else
+        for (int u = 0; u < t; ++u) rank += s.flag[u * m + J];
       const int q = s.pw.doff[J] + rank;
       float sc2 = 0.f;
       for (int j = 0; j < k; ++j) {
@@ -840,6 +861,7 @@ __device__ void plan_phase(PlanShared& s, const PlanArgs& pa, bool masks) {
 // assignment's row.  The lanes exchange offsets and slots through LDS inside
 // the wave: no block barrier anywhere.
 constexpr int kWavePlanPer = 4;  // experts per lane at most
+constexpr int kWavePlanMaxA = 512;  // assignments the one-wave plan writes at most
 __device__ void plan_phase_wave(PlanShared& s, const PlanArgs& pa, int lane) {
   const int T = pa.T, k = pa.k, E = pa.E, A = T * k;
   const moe_plan& P = pa.plan;
@@ -959,6 +981,8 @@ __device__ __forceinline__ void plan_clear(PlanShared& s, int T, int E, int m) {
   const int nm = rank_mask_words(T, E) * E;
   for (int i = threadIdx.x; i < nm; i += blockDim.x) s.tmask[i] = 0ull;
   for (int p = threadIdx.x; p < T * (m > 0 ? m : 0); p += blockDim.x) s.flag[p] = 0;
+  if (dept_masks(T, m))
+    for (int J = threadIdx.x; J < m; J += blockDim.x) s.dtok[J] = 0ull;
   if (threadIdx.x == 0) s.invalid = 0;
 }
 
@@ -1198,13 +1222,18 @@ __global__ __launch_bounds__(kPlanThreads) void dispatch_kernel(const int32_t* i
       const int t = a / pa.k;
       atomicAdd(&s.cnt[e], 1);
       if (nwt > 0) atomicOr(&s.tmask[e * nwt + (t >> 6)], 1ull << (t & 63));
-      if (pa.m > 0) s.flag[t * pa.m + e / G] = 1;
+      if (pa.m > 0) {
+        s.flag[t * pa.m + e / G] = 1;
+        if (dept_masks(pa.T, pa.m)) atomicOr(&s.dtok[e / G], 1ull << t);
+      }
     } else {
       atomicAdd(&s.invalid, 1);
     }
   }
   __syncthreads();
-  if (DISTINCT && pa.m <= 0 && pa.E <= kWavePlanPer * kWave && nwt > 0) {
+  // (one wave writes every row: past kWavePlanMaxA assignments the block does)
+  if (DISTINCT && pa.m <= 0 && pa.E <= kWavePlanPer * kWave && nwt > 0 &&
+      pa.T * pa.k <= kWavePlanMaxA) {
     if (wid == 0) plan_phase_wave(s, pa, lane);
   } else {
     plan_phase(s, pa, DISTINCT && nwt > 0);
