@@ -2668,6 +2668,7 @@ size_t down_combine_lds_bytes(const DownCombineArgs& a) {
 }
 
 constexpr int kDcLoads = 4;   // 16-byte weight loads in flight per lane
+constexpr int kDcPrefetchMinD = 2048;  // first groups requested ahead of the table above this d
 constexpr int kDcMaxSteps = kDcMaxRows / (8 * kWave);  // steps of the longest row
 
 // Elements a lane takes per 16-byte step: 8 bf16 weights or 16 FP8 codes.
@@ -2696,6 +2697,26 @@ __device__ __forceinline__ void dc_load(const DcItem* items, int i, int ie, int 
         u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                      rs, (lane * EPL + s * EPL * kWave) * ESZ, 0, kCpolNt));
   if constexpr (FP8) scl = *as_global<float>(uni(it.scale) + c);
+}
+
+// Group i's weight row of column c (matrix `mat` of the family, read from
+// its work descriptor before the group table exists and clamped into the
+// family, so a slot past the count -- whose data is never consumed -- still
+// reads inside the weights), bf16.  Slots below 4 of a work list are 128
+// bytes: inside its region, which is padded to 256 bytes like every
+// workspace region.
+template <int NS>
+__device__ __forceinline__ void dc_prefetch(const DcFamily& F, int i, int mat, int d, int c,
+                                            int lane, u32x4_t (&dst)[NS]) {
+  const int rows = F.rows;
+  const char* w = static_cast<const char*>(F.down) + ((size_t)mat * d + c) * rows * 2;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(w), (short)0, i < F.max_items ? rows * 2 : 0, kGfx9BufferDword3);
+#pragma unroll
+  for (int j = 0; j < NS; ++j)
+    dst[j] = __builtin_bit_cast(
+        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (lane * 8 + j * 8 * kWave) * 2, 0,
+                                                       kCpolNt));
 }
 
 // Dot products of group i's weight row with its rows of h (LDS), folded into
@@ -2740,18 +2761,27 @@ __device__ __forceinline__ void dc_consume(const DcItem* items, int i, int ib, i
 
 // Groups [ib, ie) of one family (rows of at most NS steps), D groups of loads
 // ahead of the one being used.
-template <int NS, bool FP8>
+template <int NS> constexpr int dc_ahead() { return kDcLoads / NS > 0 ? kDcLoads / NS : 1; }
+template <int NS, bool FP8, bool PRE = false>
 __device__ __forceinline__ void dc_family(const DcItem* items, int ib, int ie, int c,
-                                          const bf16_t* hl, int lane, float (&acc)[kTokInline]) {
-  constexpr int D = kDcLoads / NS > 0 ? kDcLoads / NS : 1;
+                                          const bf16_t* hl, int lane, float (&acc)[kTokInline],
+                                          const u32x4_t (*pre)[NS] = nullptr) {
+  constexpr int D = dc_ahead<NS>();
   // The first pass only loads (groups before ib are not consumed): with no
   // loads ahead of the loop, the buffers need no copies on entry, and each
-  // use waits only for its own group's loads.
+  // use waits only for its own group's loads.  PRE: groups ib .. ib + D - 1
+  // were requested before the loop (into pre), so that pass is skipped.
   u32x4_t buf[D][NS];
   float scl[D];
 #pragma unroll
   for (int q = 0; q < D; ++q) scl[q] = 1.f;
-  for (int i0 = ib - D; i0 < ie; i0 += D) {
+  if constexpr (PRE) {
+#pragma unroll
+    for (int q = 0; q < D; ++q)
+#pragma unroll
+      for (int j = 0; j < NS; ++j) buf[q][j] = pre[q][j];
+  }
+  for (int i0 = PRE ? ib : ib - D; i0 < ie; i0 += D) {
 #pragma unroll
     for (int q = 0; q < D; ++q) {
       dc_consume<NS, FP8>(items, i0 + q, ib, ie, hl, lane, buf[q], scl[q], acc);
@@ -2815,10 +2845,13 @@ __device__ __forceinline__ void dc_family_packed(const DcItem* items, int ib, in
 
 // (built for 8 waves per SIMD -- four 8-wave blocks per CU -- which the
 // register budget of 64 reaches without spills)
-template <bool FP8>
+// NS0 > 0 (bf16): the first family takes dc_family<NS0>, and each wave
+// requests its first groups' weight rows straight from the work descriptors
+// before the group table is built, so their HBM latency overlaps the table
+// and the staging of h instead of following them.
+template <bool FP8, int NS0>
 __global__ __launch_bounds__(kDcWaves * kWave) __attribute__((amdgpu_waves_per_eu(8, 8)))
-void down_combine_kernel(DownCombineArgs a,
-                                                                     bf16_t* __restrict__ y) {
+void down_combine_kernel(DownCombineArgs a, bf16_t* __restrict__ y) {
   extern __shared__ __align__(16) unsigned char dc_lds[];
   bf16_t* hl = reinterpret_cast<bf16_t*>(dc_lds);
   DcItem* items =
@@ -2826,6 +2859,30 @@ void down_combine_kernel(DownCombineArgs a,
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int T = a.T, d = a.d;
   constexpr int STEP = 8 * kWave;  // elements of a weight row per step
+  constexpr bool PRE = !FP8 && NS0 > 0;
+  constexpr int NSP = NS0 > 0 ? NS0 : 1;
+  const int c = uni((int)(blockIdx.x * kDcWaves) + wid);  // wave-uniform: scalar resource base
+  u32x4_t pre[dc_ahead<NSP>()][NSP];
+  if constexpr (PRE) {
+    // the descriptors first, then every row: one round trip for the
+    // descriptors in all
+    constexpr int DP = dc_ahead<NSP>();
+    int mat[DP];
+    if (a.f[0].work) {
+      const auto wv = as_global<u32x4_t>(a.f[0].work);
+      u32x4_t w[DP];
+#pragma unroll
+      for (int q = 0; q < DP; ++q) w[q] = wv[2 * q];
+#pragma unroll
+      for (int q = 0; q < DP; ++q) mat[q] = min(max(uni((int)w[q].x), 0), a.f[0].n_mats - 1);
+    } else {
+#pragma unroll
+      for (int q = 0; q < DP; ++q) mat[q] = 0;
+    }
+#pragma unroll
+    for (int q = 0; q < dc_ahead<NSP>(); ++q)
+      dc_prefetch<NSP>(a.f[0], q, mat[q], d, min(c, d - 1), lane, pre[q]);
+  }
   // The group table (descriptors checked against the family's bounds and the
   // rows of h in use), and the staging of the rows of h.  Nothing here waits
   // for anything else: the counts, every descriptor slot up to the host's
@@ -2912,7 +2969,6 @@ void down_combine_kernel(DownCombineArgs a,
   // every wave's staged rows have landed, and the table is complete, for the block
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  const int c = uni((int)(blockIdx.x * kDcWaves) + wid);  // wave-uniform: scalar resource base
   if (c >= d) return;
   float acc[kTokInline];
 #pragma unroll
@@ -2925,7 +2981,9 @@ void down_combine_kernel(DownCombineArgs a,
       const int rows = a.f[fi].rows;
       // (packed loads address the family's weights by 32-bit byte offsets)
       const bool packable = !FP8 && (size_t)a.f[fi].n_mats * rows * d * 2 < (size_t)kDcOob;
-      if (packable && rows == 16 * 8)
+      if (PRE && fi == 0)
+        dc_family<NSP, FP8, true>(items, fb[fi], fe[fi], c, hl, lane, acc, pre);
+      else if (packable && rows == 16 * 8)
         dc_family_packed<16>(items, fb[fi], fe[fi], c, hl, lane, a.f[fi], d, acc);
       else if (packable && rows == 32 * 8)
         dc_family_packed<32>(items, fb[fi], fe[fi], c, hl, lane, a.f[fi], d, acc);
@@ -3625,10 +3683,24 @@ hipError_t launch_down_combine(const DownCombineArgs& a, void* y, hipStream_t st
     else
       hipLaunchKernelGGL(k, grid, block, lds, st, a, yo);
   };
+  // the first family's path, as the kernel chooses it per family; its first
+  // groups are requested ahead of the table only for wide layers (measured:
+  // DeepSeek-V3-shaped batch 1 down 45.4 -> 43.6 us; at d = 2048 the early
+  // requests delayed the table's own loads, 7.9 -> 8.4 us at batch 1)
+  const int r0 = a.f[0].rows, ns0 = (r0 + 8 * kWave - 1) / (8 * kWave);
+  const bool packable0 = (size_t)a.f[0].n_mats * r0 * a.d * 2 < (size_t)kDcOob;
   if (a.fp8)
-    go(down_combine_kernel<true>);
+    go(down_combine_kernel<true, 0>);
+  else if ((packable0 && (r0 == 16 * 8 || r0 == 32 * 8)) || a.d <= kDcPrefetchMinD)
+    go(down_combine_kernel<false, 0>);
+  else if (ns0 <= 1)
+    go(down_combine_kernel<false, 1>);
+  else if (ns0 == 2)
+    go(down_combine_kernel<false, 2>);
+  else if (ns0 == 3)
+    go(down_combine_kernel<false, 3>);
   else
-    go(down_combine_kernel<false>);
+    go(down_combine_kernel<false, kDcMaxSteps>);
   return hipGetLastError();
 }
 
