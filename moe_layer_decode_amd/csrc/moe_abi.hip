@@ -459,9 +459,10 @@ FamilySet make_families(const moe_layer_desc& d, const moe_weights& w, const moe
 // Tiles per slot and the block prefix for one launch: small parts tile by the
 // GEMV configuration; large parts of bf16 layers by one 64-row (gate/up) or
 // 64-column (down) matrix-core tile per block (each wave 16 of them over the
-// whole K), except at T <= kSplitKMaxT, where no group passes 16 rows: there
-// gate/up takes one 16-row tile per block, and down at d > kSplitKDownMinD
-// (intermediate width >= kSplitKMinK) kSplitKCols columns per block, the four
+// whole K), except at decode batches: there gate/up (T <= kSplitKMaxT, 16
+// for two-input launches) takes one 16-row tile per block against up to
+// two 16-token tiles, and down at d > kSplitKDownMinD (T <= kSplitKDownMaxT,
+// intermediate width >= kSplitKMinK) kSplitKCols columns per block, the four
 // waves splitting K.  Measured at batch 16: K-split gate/up is faster at
 // d = 2048 and at d = 7168 (the DeaMoE transform of the DeepSeek-V3-shaped
 // layer: 382 -> 369 us); K-split down is 2-3% faster at d = 7168 but 5%
@@ -473,8 +474,11 @@ void set_tiles(FamilySet& set, int d, bool gateup, int w_dtype, const moe::GemvC
   set.blk_start[0] = 0;
   for (int i = 0; i < set.n; ++i) {
     Family& f = set.f[i];
-    f.splitk = w_dtype == MOE_BF16 && f.large && T <= moe::kSplitKMaxT &&
-               (gateup || (d > moe::kSplitKDownMinD && f.rows >= moe::kSplitKMinK));
+    // (a launch with two inputs per row passes 16 tokens at a time)
+    f.splitk = w_dtype == MOE_BF16 && f.large &&
+               (gateup ? T <= (f.x_up ? 16 : moe::kSplitKMaxT)
+                       : T <= moe::kSplitKDownMaxT && d > moe::kSplitKDownMinD &&
+                             f.rows >= moe::kSplitKMinK);
     const int lt = w_dtype != MOE_BF16        ? 16
                    : !f.splitk                ? moe::kWideRows
                    : gateup                   ? 16

@@ -1866,25 +1866,27 @@ __device__ __forceinline__ u32x4_t tile_operand(const unsigned char* t, int m, i
 
 // K-split matrix-core tile: two 16-row tiles, A0 = rows a0.. of the matrix
 // behind rs0 and A1 = rows a1.. of the matrix behind rs1 (nrows rows of kdim
-// elements each), against up to 16 input rows (input row t at xrow(t) of x,
-// and of xu for A1 when DUAL; rows t >= n read zeros).  Each wave takes a
-// quarter of K in tiles of 64: tile q of A0 and tile q of A1 take turns in a
-// ring of three LDS slots, so while one is used the next two are in flight;
-// the inputs of tile q (two 32-element steps) come through registers, two
-// sets in turn.  Loads past the wave's K range, and rows at or past nrows,
-// read zeros, so every load is unconditional.  The waits are counted by hand
-// (the compiler does not see the LDS data of these loads): per tile the
-// vector-memory operations are, in order, A0 (2), inputs (2 NX), A1 (2).  The
-// four waves' partial tiles are added in wave order through LDS, and wave 0
-// calls epi(t, i, s0, s1) with the sums of rows 4 (l / 16) + i of both tiles
-// for input row t = l % 16 < n.
-template <bool DUAL, typename XRow, typename Epi>
+// elements each), against up to 16 NT input rows (input row t at xrow(t) of
+// x, and of xu for A1 when DUAL; rows t >= n read zeros), as NT 16-row token
+// tiles.  Each wave takes a quarter of K in tiles of 64: tile q of A0 and
+// tile q of A1 take turns in a ring of three LDS slots, so while one is used
+// the next two are in flight; the inputs of tile q (two 32-element steps per
+// token tile) come through registers, two sets in turn.  Loads past the
+// wave's K range, and rows at or past nrows, read zeros, so every load is
+// unconditional.  The waits are counted by hand (the compiler does not see
+// the LDS data of these loads): per tile the vector-memory operations are,
+// in order, A0 (2), inputs (2 NX NT), A1 (2).  The four waves' partial tiles
+// are added in wave order through LDS, two token tiles at a time, and wave 0
+// calls epi(t, i, s0, s1) with the sums of rows 4 (l / 16) + i of both
+// tiles for input row t = 16 c + l % 16 < n of token tile c.
+template <bool DUAL, int NT, typename XRow, typename Epi>
 __device__ void ksplit_mfma(__amdgpu_buffer_rsrc_t rs0, int a0, __amdgpu_buffer_rsrc_t rs1,
                             int a1, int nrows, int kdim, const bf16_t* __restrict__ x,
                             const bf16_t* __restrict__ xu, XRow xrow, int n, Epi epi, int lane,
                             int wid, MfmaLds& lds) {
   constexpr int NX = DUAL ? 2 : 1;   // activation inputs: A0's, and A1's when they differ
-  constexpr int NXO = 2 * NX;        // input loads of one tile
+  constexpr int NXO = 2 * NX * NT;   // input loads of one tile
+  static_assert(NT == 1 || NT == 2 || NT == 4, "token tiles per pass");
   const int t = lane & 15, g = lane >> 4;
   int kb, ke;
   k_quarter(kdim, wid, kb, ke);
@@ -1893,31 +1895,51 @@ __device__ void ksplit_mfma(__amdgpu_buffer_rsrc_t rs0, int a0, __amdgpu_buffer_
   __amdgpu_buffer_rsrc_t rx[NX];
   rx[0] = span_rsrc(x);
   if constexpr (DUAL) rx[NX - 1] = span_rsrc(xu);
-  const bool xv = t < n;
-  const uint32_t xoff = (uint32_t)(((size_t)(xv ? xrow(t) : 0) * kdim + g * 8) * 2);
-  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  bool xv[NT];
+  uint32_t xoff[NT];
+#pragma unroll
+  for (int c = 0; c < NT; ++c) {
+    xv[c] = 16 * c + t < n;
+    xoff[c] = (uint32_t)(((size_t)(xv[c] ? xrow(16 * c + t) : 0) * kdim + g * 8) * 2);
+  }
+  // token tiles holding rows of the group (uniform): the matrix-core steps of
+  // the others are skipped, their input loads read zeros
+  const int ntl = min(NT, (n + 15) >> 4);
+  f32x4_t acc0[NT], acc1[NT];
+#pragma unroll
+  for (int c = 0; c < NT; ++c) acc0[c] = acc1[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   unsigned char* slots = lds.tile[wid][0];
-  u32x4_t xa[2][NX], xb[2][NX];
-  auto request_x = [&](u32x4_t (&xr)[2][NX], int k0) {
+  u32x4_t xa[2][NX][NT], xb[2][NX][NT];
+  auto request_x = [&](u32x4_t (&xr)[2][NX][NT], int k0) {
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const int k = k0 + 32 * m;
-      const bool in = xv && k + g * 8 < ke;
 #pragma unroll
-      for (int v = 0; v < NX; ++v) xr[m][v] = ld16_span(rx[v], in ? xoff + (uint32_t)k * 2 : kDcOob);
+      for (int c = 0; c < NT; ++c) {
+        const bool in = xv[c] && k + g * 8 < ke;
+#pragma unroll
+        for (int v = 0; v < NX; ++v)
+          xr[m][v][c] = ld16_span(rx[v], in ? xoff[c] + (uint32_t)k * 2 : kDcOob);
+      }
     }
   };
   // unit u = 2q (A0 tile q) or 2q + 1 (A1 tile q) lives in slot u % 3
   auto slot = [&](int u) { return slots + (u % kTileSlots) * kTileBytes; };
-  auto mfma2 = [&](f32x4_t& acc, const unsigned char* tl, const u32x4_t (&xr)[2][NX], int v) {
+  auto mfma2 = [&](f32x4_t (&acc)[NT], const unsigned char* tl, const u32x4_t (&xr)[2][NX][NT],
+                   int v) {
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(tile_operand(tl, m, lane)),
-                                                    as_bf16x8(xr[m][v]), acc, 0, 0, 0);
+    for (int m = 0; m < 2; ++m) {
+      const u32x4_t av = tile_operand(tl, m, lane);
+#pragma unroll
+      for (int c = 0; c < NT; ++c)
+        if (c < ntl)
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(xr[m][v][c]),
+                                                           acc[c], 0, 0, 0);
+    }
   };
   // one tile, whose A0 and A1 units were requested before; requests the next
   // tile's units and inputs (into xn) as the slots free up
-  auto step = [&](int q, u32x4_t (&xc)[2][NX], u32x4_t (&xn)[2][NX]) {
+  auto step = [&](int q, u32x4_t (&xc)[2][NX][NT], u32x4_t (&xn)[2][NX][NT]) {
     const int k0 = kb + kTileK * q;
     __builtin_amdgcn_sched_barrier(0);
     tile_request(slot(2 * q + 2), rs0, a0, nrows, kdim, k0 + kTileK, ke, lane);
@@ -1946,33 +1968,43 @@ __device__ void ksplit_mfma(__amdgpu_buffer_rsrc_t rs0, int a0, __amdgpu_buffer_
   }
   // no load may still write a slot when the area is reused below
   wait_vmcnt<0>();
-  __syncthreads();
-  lds.part[wid][0][0][lane] = acc0;
-  lds.part[wid][0][1][lane] = acc1;
-  __syncthreads();
-  if (wid == 0) {
-    f32x4_t s0 = lds.part[0][0][0][lane], s1 = lds.part[0][0][1][lane];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) {
-      s0 += lds.part[w][0][0][lane];
-      s1 += lds.part[w][0][1][lane];
+  for (int c0 = 0; c0 < NT; c0 += 2) {
+    if (c0 >= ntl) break;
+    __syncthreads();
+#pragma unroll
+    for (int c = c0; c < c0 + 2 && c < NT; ++c) {
+      lds.part[wid][c - c0][0][lane] = acc0[c];
+      lds.part[wid][c - c0][1][lane] = acc1[c];
     }
-    if (t < n) {
+    __syncthreads();
+    if (wid == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) epi(t, 4 * g + i, s0[i], s1[i]);
+      for (int c = c0; c < c0 + 2 && c < NT; ++c) {
+        f32x4_t s0 = lds.part[0][c - c0][0][lane], s1 = lds.part[0][c - c0][1][lane];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) {
+          s0 += lds.part[w][c - c0][0][lane];
+          s1 += lds.part[w][c - c0][1][lane];
+        }
+        if (16 * c + t < n) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) epi(16 * c + t, 4 * g + i, s0[i], s1[i]);
+        }
+      }
     }
   }
   __syncthreads();
 }
 
-// 16 rows (i0..) of gate and up against the group's (at most 16) rows.
-template <bool DUAL>
+// 16 rows (i0..) of gate and up against the group's (at most 16 NT) rows.
+template <bool DUAL, int NT>
 __device__ void gu_mfma(const bf16_t* __restrict__ Wg, const bf16_t* __restrict__ Wu, int d,
                         int rows, int i0, const bf16_t* __restrict__ x,
                         const bf16_t* __restrict__ xu, int in_rows, const Slot& sl,
                         const int* grp_token, const GuOut<bf16_t>& o, int lane, int wid,
                         MfmaLds& lds) {
-  ksplit_mfma<DUAL>(
+  ksplit_mfma<DUAL, NT>(
       span_rsrc(Wg), i0, span_rsrc(Wu), i0, rows, d, x, xu,
       [&](int t) { return lane_token(sl, grp_token, t, in_rows); }, sl.n,
       [&](int t, int i, float g, float u) {
@@ -1981,9 +2013,10 @@ __device__ void gu_mfma(const bf16_t* __restrict__ Wg, const bf16_t* __restrict_
       lane, wid, lds);
 }
 
-// Out-of-line entry of the K-split gate/up tile for one 16-token chunk
-// (groups of at most 16 rows), with plain-value arguments like gu_wide_call.
-template <bool DUAL>
+// Out-of-line entry of the K-split gate/up tile for NT 16-token tiles
+// (groups of at most 16 NT rows), with plain-value arguments like
+// gu_wide_call.
+template <bool DUAL, int NT>
 __device__ __attribute__((noinline)) void gu_mfma_call(
     const bf16_t* __restrict__ Wg, const bf16_t* __restrict__ Wu, int d, int rows, int i0,
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ xu, int in_rows, int r0, int n,
@@ -1991,21 +2024,22 @@ __device__ __attribute__((noinline)) void gu_mfma_call(
   Slot sl{};
   sl.r0 = r0;
   sl.n = n;
-  gu_mfma<DUAL>(Wg, Wu, d, rows, i0, x, xu, in_rows, sl, grp_token, o, lane, wid, lds);
+  gu_mfma<DUAL, NT>(Wg, Wu, d, rows, i0, x, xu, in_rows, sl, grp_token, o, lane, wid, lds);
 }
 
-// Down projection of a group of at most 16 rows of h as K-split tiles: 32
+// Down projection of a group of at most 16 NT rows of h as K-split tiles: 32
 // output columns (c0..) per block, two 16-column tiles sharing each input
 // step, K = the intermediate width split over the four waves.  out[r0 + t][c]
 // (SiLU of it when epi) for every row t < n of the group.  Out of line, like
 // gu_mfma_call.
+template <int NT>
 __device__ __attribute__((noinline)) void dn_mfma_call(const bf16_t* __restrict__ Wd, int d,
                                                        int rows, int c0,
                                                        const bf16_t* __restrict__ h, int r0,
                                                        int n, float* __restrict__ out, int epi,
                                                        int lane, int wid, MfmaLds& lds) {
   const __amdgpu_buffer_rsrc_t rw = span_rsrc(Wd);
-  ksplit_mfma<false>(
+  ksplit_mfma<false, NT>(
       rw, c0, rw, c0 + 16, d, rows, h + (size_t)r0 * rows, h, [](int t) { return t; }, n,
       [&](int t, int i, float a, float b) {
         float* o = out + (size_t)(r0 + t) * d;
@@ -2426,10 +2460,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   }
   if constexpr (sizeof(T_) == 2) {
     if (F.splitk) {
-      // at most 16 rows per group: one 16-row K-split tile per block
+      // at most 16 NCMAX rows per group: one 16-row K-split tile per block
       const int i0 = tile * 16;
       if (i0 < F.rows)
-        gu_mfma_call<DUAL>(Wg, Wu, d, F.rows, i0, xg, xu, F.in_rows, sl.r0, sl.n, F.grp_token, o,
+        gu_mfma_call<DUAL, (NCMAX < 2 ? NCMAX : 2)>(Wg, Wu, d, F.rows, i0, xg, xu, F.in_rows,
+                                                     sl.r0, sl.n, F.grp_token, o,
                            lane, wid, *reinterpret_cast<MfmaLds*>(lds_raw));
       return;
     }
@@ -2491,8 +2526,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       // at most 16 rows per group: 32 columns per block, K split over the waves
       const int c0 = tile * kSplitKCols;
       if (c0 < d)
-        dn_mfma_call(Wd, d, F.rows, c0, h, sl.r0, sl.n, F.out, F.epi, lane, wid,
-                     *reinterpret_cast<MfmaLds*>(lds_raw));
+        dn_mfma_call<1>(Wd, d, F.rows, c0, h, sl.r0, sl.n, F.out, F.epi, lane, wid,
+                        *reinterpret_cast<MfmaLds*>(lds_raw));
       return;
     }
     // large groups: the whole block on one 64-column tile, 16*NC rows of h a pass

@@ -518,6 +518,13 @@ def test_layer_deamoe_7b(seed, T):
     check_layer(DEA7, seed, T)
 
 
+@pytest.mark.parametrize("name", [QWEN, DEA7])
+def test_layer_two_token_tiles(name):
+    """Batches of 17-32 tokens at d = 2048: the K-split gate/up tiles pass two
+    16-token tiles (groups of up to 32 rows); 8 spread tokens checked."""
+    check_layer(name, 0, 32, sample_tokens=spread_tokens(32), max_tokens=32)
+
+
 @pytest.mark.parametrize("name,T", [(QWEN, 128), (QWEN, 512), (DEA7, 100), (DSV3, 128),
                                     (DEAV3, 128), (PAPER, 128),
                                     ("deepseek_v3_d7168_e256_i2048_s2048_top8_fp8", 128)])
