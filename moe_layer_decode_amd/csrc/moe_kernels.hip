@@ -1879,7 +1879,10 @@ __device__ __forceinline__ u32x4_t tile_operand(const unsigned char* t, int m, i
 // are added in wave order through LDS, two token tiles at a time, and wave 0
 // calls epi(t, i, s0, s1) with the sums of rows 4 (l / 16) + i of both
 // tiles for input row t = 16 c + l % 16 < n of token tile c.
-template <bool DUAL, int NT, typename XRow, typename Epi>
+// KSPLIT false: the same pipeline without the split -- wave w owns rows
+// 16 w.. of each matrix over the whole K and calls epi(t, 16 w + 4 (l / 16)
+// + i, ...) itself, so a block covers 64 rows.
+template <bool DUAL, int NT, bool KSPLIT = true, typename XRow, typename Epi>
 __device__ void ksplit_mfma(__amdgpu_buffer_rsrc_t rs0, int a0, __amdgpu_buffer_rsrc_t rs1,
                             int a1, int nrows, int kdim, const bf16_t* __restrict__ x,
                             const bf16_t* __restrict__ xu, XRow xrow, int n, Epi epi, int lane,
@@ -1888,8 +1891,13 @@ __device__ void ksplit_mfma(__amdgpu_buffer_rsrc_t rs0, int a0, __amdgpu_buffer_
   constexpr int NXO = 2 * NX * NT;   // input loads of one tile
   static_assert(NT == 1 || NT == 2 || NT == 4, "token tiles per pass");
   const int t = lane & 15, g = lane >> 4;
-  int kb, ke;
-  k_quarter(kdim, wid, kb, ke);
+  int kb = 0, ke = kdim;
+  if constexpr (KSPLIT) {
+    k_quarter(kdim, wid, kb, ke);
+  } else {
+    a0 += 16 * wid;
+    a1 += 16 * wid;
+  }
   kb = uni(kb);
   ke = uni(ke);
   __amdgpu_buffer_rsrc_t rx[NX];
@@ -1968,6 +1976,15 @@ __device__ void ksplit_mfma(__amdgpu_buffer_rsrc_t rs0, int a0, __amdgpu_buffer_
   }
   // no load may still write a slot when the area is reused below
   wait_vmcnt<0>();
+  if constexpr (!KSPLIT) {
+#pragma unroll
+    for (int c = 0; c < NT; ++c)
+      if (c < ntl && 16 * c + t < n) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) epi(16 * c + t, 16 * wid + 4 * g + i, acc0[c][i], acc1[c][i]);
+      }
+    return;
+  }
 #pragma unroll
   for (int c0 = 0; c0 < NT; c0 += 2) {
     if (c0 >= ntl) break;
@@ -2025,6 +2042,26 @@ __device__ __attribute__((noinline)) void gu_mfma_call(
   sl.r0 = r0;
   sl.n = n;
   gu_mfma<DUAL, NT>(Wg, Wu, d, rows, i0, x, xu, in_rows, sl, grp_token, o, lane, wid, lds);
+}
+
+// 64 rows (i0.., 16 per wave over the whole K) of gate and up against a
+// group of at most 16 NT rows, through the LDS weight tiles of ksplit_mfma
+// (one input set).  Out of line, like gu_mfma_call.
+template <int NT>
+__device__ __attribute__((noinline)) void gu_rows_call(
+    const bf16_t* __restrict__ Wg, const bf16_t* __restrict__ Wu, int d, int rows, int i0,
+    const bf16_t* __restrict__ x, int in_rows, int r0, int n, const int* grp_token,
+    GuOut<bf16_t> o, int lane, int wid, MfmaLds& lds) {
+  Slot sl{};
+  sl.r0 = r0;
+  sl.n = n;
+  ksplit_mfma<false, NT, false>(
+      span_rsrc(Wg), i0, span_rsrc(Wu), i0, rows, d, x, x,
+      [&](int t) { return lane_token(sl, grp_token, t, in_rows); }, n,
+      [&](int t, int i, float g, float u) {
+        if (i0 + i < rows) gu_store(o, (size_t)(r0 + t) * rows + i0 + i, g, u);
+      },
+      lane, wid, lds);
 }
 
 // Down projection of a group of at most 16 NT rows of h as K-split tiles: 32
@@ -2471,6 +2508,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     // large groups: the whole block on one 64-row tile, 16*NC tokens a pass
     const int i0 = tile * kWideRows;
     if (i0 >= F.rows) return;
+    if constexpr (!DUAL) {
+      // groups of at most 32 rows: each wave its 16 rows through the LDS
+      // weight tiles, in one pass
+      if (sl.n <= 32) {
+        gu_rows_call<2>(Wg, Wu, d, F.rows, i0, xg, F.in_rows, sl.r0, sl.n, F.grp_token, o, lane,
+                        wid, *reinterpret_cast<MfmaLds*>(lds_raw));
+        return;
+      }
+    }
     // out of line where large groups are rare (T <= 16, or the two-input
     // private transforms, whose groups seldom pass four rows)
     constexpr bool kCall = NCMAX == 1 || DUAL;
