@@ -16,6 +16,7 @@ constexpr int kTokInline = 4;        // tokens carried inline in a work descript
 constexpr int kWideRows = 64;        // rows / columns of a bf16 large-group tile (unless split K)
 constexpr int kSplitKMaxT = 32;      // K-split gate/up tiles: T at most (two 16-row token tiles)
 constexpr int kSplitKDownMaxT = 16;  // K-split down tiles: T at most (one token tile)
+constexpr int kDownRowCols = 128;    // down row tiles (T > kSplitKDownMaxT): output columns per block
 constexpr int kSplitKCols = 32;      // K-split down tiles: output columns per block,
 constexpr int kSplitKDownMinD = 2048;  //   d above it
 constexpr int kSplitKMinK = 256;     //   and intermediate width at least (a full K tile per wave)
@@ -96,9 +97,12 @@ struct Family {
   int n_mats;              // matrices in the family (bounds check of work descriptors)
   int max_rows;            // rows h / out hold (bounds check of work descriptors)
   int large;               // 0: groups of <= kTokInline rows; 1: larger groups
-  int splitk;              // large part of bf16 weights at decode batches: K-split tiles
-                           // (gate/up: 16 rows, down: kSplitKCols columns per block), else
-                           // 64-row / 64-column tiles
+  int routed;              // 1: the routed experts (many groups of a few rows each)
+  int splitk;              // large part of bf16 weights: 1 K-split tiles at decode batches
+                           // (gate/up: 16 rows, down: kSplitKCols columns per block); 2 (down
+                           // past kSplitKDownMaxT, routed experts) kDownRowCols columns per
+                           // block, row tiles for groups of at most 16 rows; 0 64-row /
+                           // 64-column tiles
   const float* gate_scale; // FP8 weights: per-row scales [n_mats][rows] (gate, up)
   const float* up_scale;   //   and [n_mats][d] (down); unused otherwise
   const float* down_scale;

@@ -2085,6 +2085,26 @@ __device__ __attribute__((noinline)) void dn_mfma_call(const bf16_t* __restrict_
       },
       lane, wid, lds);
 }
+// Down projection of a group of at most 16 NT rows of h over kDownRowCols
+// output columns (c0..): wave w takes columns c0 + 16 w.. and c0 + 64 +
+// 16 w.. over the whole K through the LDS weight tiles of ksplit_mfma.  Out
+// of line, like gu_mfma_call.
+template <int NT>
+__device__ __attribute__((noinline)) void dn_rows_call(const bf16_t* __restrict__ Wd, int d,
+                                                       int rows, int c0,
+                                                       const bf16_t* __restrict__ h, int r0,
+                                                       int n, float* __restrict__ out, int epi,
+                                                       int lane, int wid, MfmaLds& lds) {
+  const __amdgpu_buffer_rsrc_t rw = span_rsrc(Wd);
+  ksplit_mfma<false, NT, false>(
+      rw, c0, rw, c0 + kWideRows, d, rows, h + (size_t)r0 * rows, h, [](int t) { return t; }, n,
+      [&](int t, int i, float a, float b) {
+        float* o = out + (size_t)(r0 + t) * d;
+        if (c0 + i < d) dn_store(o, c0 + i, a, epi);
+        if (c0 + kWideRows + i < d) dn_store(o, c0 + kWideRows + i, b, epi);
+      },
+      lane, wid, lds);
+}
 // ---- large groups, bf16: 64-row tiles with LDS-shared inputs ---------------
 //
 // Four waves, each 16 rows (gate/up) or 16 output columns (down) over the whole
@@ -2568,7 +2588,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     return;
   }
   if constexpr (sizeof(T_) == 2) {
-    if (F.splitk) {
+    if (F.splitk == 1) {
       // at most 16 rows per group: 32 columns per block, K split over the waves
       const int c0 = tile * kSplitKCols;
       if (c0 < d)
@@ -2576,21 +2596,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
                         *reinterpret_cast<MfmaLds*>(lds_raw));
       return;
     }
-    // large groups: the whole block on one 64-column tile, 16*NC rows of h a pass
-    const int c0 = tile * kWideRows;
-    if (c0 >= d) return;
+    // large groups: 64-column tiles, 16*NC rows of h a pass -- one per block,
+    // or two (kDownRowCols columns) where groups of at most 16 rows take the
+    // LDS weight tiles instead, each wave 16 + 16 columns over the whole K
+    const int cols = F.splitk == 2 ? kDownRowCols : kWideRows;
+    const int cb = tile * cols;
+    if (cb >= d) return;
+    if (F.splitk == 2 && sl.n <= 16) {
+      dn_rows_call<1>(Wd, d, F.rows, cb, h, sl.r0, sl.n, F.out, F.epi, lane, wid,
+                      *reinterpret_cast<MfmaLds*>(lds_raw));
+      return;
+    }
 #pragma unroll 1
-    for (int tc = 0; tc < sl.n; tc += 16 * kDownNC) {
-      const int rem = sl.n - tc;
-      if (rem > 32)
-        dn_wide<kDownNC>(Wd, d, F.rows, c0, h, sl.r0, sl.n, tc, F.out, F.epi, lane, wid,
-                         *reinterpret_cast<WideLds<kDownNC, 1>*>(lds_raw));
-      else if (rem > 16)
-        dn_wide<2>(Wd, d, F.rows, c0, h, sl.r0, sl.n, tc, F.out, F.epi, lane, wid,
-                   *reinterpret_cast<WideLds<2, 1>*>(lds_raw));
-      else
-        dn_wide<1>(Wd, d, F.rows, c0, h, sl.r0, sl.n, tc, F.out, F.epi, lane, wid,
-                   *reinterpret_cast<WideLds<1, 1>*>(lds_raw));
+    for (int c0 = cb; c0 < cb + cols && c0 < d; c0 += kWideRows) {
+#pragma unroll 1
+      for (int tc = 0; tc < sl.n; tc += 16 * kDownNC) {
+        const int rem = sl.n - tc;
+        if (rem > 32)
+          dn_wide<kDownNC>(Wd, d, F.rows, c0, h, sl.r0, sl.n, tc, F.out, F.epi, lane, wid,
+                           *reinterpret_cast<WideLds<kDownNC, 1>*>(lds_raw));
+        else if (rem > 16)
+          dn_wide<2>(Wd, d, F.rows, c0, h, sl.r0, sl.n, tc, F.out, F.epi, lane, wid,
+                     *reinterpret_cast<WideLds<2, 1>*>(lds_raw));
+        else
+          dn_wide<1>(Wd, d, F.rows, c0, h, sl.r0, sl.n, tc, F.out, F.epi, lane, wid,
+                     *reinterpret_cast<WideLds<1, 1>*>(lds_raw));
+      }
     }
   } else {
     // large groups, fp32 layers: the whole block on one 16-column tile
