@@ -704,6 +704,42 @@ __device__ void dept_scan(PlanShared& s, const PlanArgs& pa, int lane) {
   }
 }
 
+// Rank of token t's pair among department J's pairs (its lower tokens that
+// chose one of J's experts).
+__device__ __forceinline__ int pair_rank(const PlanShared& s, int T, int m, int t, int J) {
+  if (dept_masks(T, m)) return __popcll(s.dtok[J] & ((1ull << t) - 1ull));
+  int r = 0;
+  for (int u = 0; u < t; ++u) r += s.flag[u * m + J];
+  return r;
+}
+
+// (token, department) pairs p = i0, i0 + stride, ...: department J is active
+// for token t when t selected at least one of its experts; c_{t,J} sums those
+// weights.  Needs the department offsets and slots of dept_scan.
+__device__ void write_pairs(const PlanShared& s, const PlanArgs& pa, int i0, int stride) {
+  const int T = pa.T, k = pa.k, E = pa.E, m = pa.m, G = E / m;
+  const moe_plan& P = pa.plan;
+  for (int p = i0; p < T * m; p += stride) {
+    const int t = p / m, J = p - t * m;
+    if (s.flag[p]) {
+      const int rank = pair_rank(s, T, m, t, J);
+      const int q = s.pw.doff[J] + rank;
+      float sc2 = 0.f;
+      for (int j = 0; j < k; ++j) {
+        const int e = s.ids[t * k + j];
+        if (e >= 0 && e < E && e / G == J) sc2 += s.w[t * k + j];
+      }
+      P.dept_row_token[q] = t;
+      P.dept_row_dept[q] = J;
+      P.dept_row_scale[q] = sc2;
+      P.dept_inv[p] = q;
+      if (s.pw.dcnt[J] <= kTokInline) pa.dwork[s.pw.dslot[J]].tok[rank] = t;
+    } else {
+      P.dept_inv[p] = -1;
+    }
+  }
+}
+
 // The dispatch plan from s.ids / s.w (T*k assignments), s.cnt (rows per
 // expert) and s.flag (pairs present).  Whole block, two barriers: a scan of
 // the expert counts by at most kScanWaves waves (contiguous entries per lane,
@@ -813,12 +849,7 @@ __device__ void plan_phase(PlanShared& s, const PlanArgs& pa, bool masks) {
       int in = t;
       if (pa.factorised) {
         const int J = e / G;
-        int rd = 0;
-        if (dept_masks(T, m))
-          rd = __popcll(s.dtok[J] & ((1ull << t) - 1ull));
-        else
-          for (int u = 0; u < t; ++u) rd += s.flag[u * m + J];
-        in = s.pw.doff[J] + rd;
+        in = s.pw.doff[J] + pair_rank(s, T, m, t, J);
         P.row_pair[row] = in;
       }
       if (s.cnt[e] <= kTokInline) pa.work[s.pw.slot[e]].tok[rank] = in;
@@ -826,44 +857,29 @@ __device__ void plan_phase(PlanShared& s, const PlanArgs& pa, bool masks) {
       P.inv_perm[a] = -1;
     }
   }
-  if (m <= 0) return;
-  // (token, department) pairs: department J is active for token t when t
-  // selected at least one of its experts; c_{t,J} sums those weights
-  for (int p = tid; p < T * m; p += nth) {
-    const int t = p / m, J = p - t * m;
-    if (s.flag[p]) {
-      int rank = 0;
-      if (dept_masks(T, m))
-        rank = __popcll(s.dtok[J] & ((1ull << t) - 1ull));
-      else
-        for (int u = 0; u < t; ++u) rank += s.flag[u * m + J];
-      const int q = s.pw.doff[J] + rank;
-      float sc2 = 0.f;
-      for (int j = 0; j < k; ++j) {
-        const int e = s.ids[t * k + j];
-        if (e >= 0 && e < E && e / G == J) sc2 += s.w[t * k + j];
-      }
-      P.dept_row_token[q] = t;
-      P.dept_row_dept[q] = J;
-      P.dept_row_scale[q] = sc2;
-      P.dept_inv[p] = q;
-      if (s.pw.dcnt[J] <= kTokInline) pa.dwork[s.pw.dslot[J]].tok[rank] = t;
-    } else {
-      P.dept_inv[p] = -1;
-    }
-  }
+  if (m > 0) write_pairs(s, pa, tid, nth);
 }
 
-// The plan by one wave, for layers with no departments, at most 4 * 64
-// experts and the token bits of every expert in s.tmask: lane l takes the
-// experts [l * per, (l + 1) * per), one wave scan of the counts gives their
-// first rows and list slots, and the same wave then writes every
-// assignment's row.  The lanes exchange offsets and slots through LDS inside
-// the wave: no block barrier anywhere.
+// The plan by one wave, for at most 4 * 64 experts with the token bits of
+// every expert in s.tmask and, in the department form, the token bits of
+// every department in s.dtok: lane l takes the experts [l * per, (l + 1) *
+// per), one wave scan of the counts gives their first rows and list slots
+// (dept_scan does the same for the departments), and the same wave then
+// writes every assignment's row and every pair's.  The lanes exchange
+// offsets and slots through LDS inside the wave: no block barrier anywhere.
 constexpr int kWavePlanPer = 4;  // experts per lane at most
 constexpr int kWavePlanMaxA = 512;  // assignments the one-wave plan writes at most
+// With departments only a lane's worth of assignments and of pairs: past it
+// the block-wide plan measured faster (DeaMoE-7B-shaped top-k + plan at one
+// token 7.9 -> 7.2 us with the wave, at 16 tokens 8.0 -> 9.4 us)
+constexpr int kWavePlanMaxDeptA = kWave;
+__device__ __forceinline__ bool wave_plan_fits(int T, int E, int k, int m) {
+  return E <= kWavePlanPer * kWave && rank_mask_words(T, E) > 0 &&
+         (m <= 0 ? T * k <= kWavePlanMaxA
+                 : dept_masks(T, m) && T * k <= kWavePlanMaxDeptA && T * m <= kWavePlanMaxDeptA);
+}
 __device__ void plan_phase_wave(PlanShared& s, const PlanArgs& pa, int lane) {
-  const int T = pa.T, k = pa.k, E = pa.E, A = T * k;
+  const int T = pa.T, k = pa.k, E = pa.E, A = T * k, m = pa.m;
   const moe_plan& P = pa.plan;
   const int per = (E + kWave - 1) / kWave;
   const int b = min(E, lane * per), en = min(E, b + per);
@@ -906,14 +922,17 @@ __device__ void plan_phase_wave(PlanShared& s, const PlanArgs& pa, int lane) {
     P.header[kHdrSmall] = is;
     P.header[kHdrLarge] = ia - is;
     P.header[MOE_PLAN_N_INVALID] = s.invalid;
-    P.header[MOE_PLAN_N_DEPT_ROWS] = 0;
-    P.header[MOE_PLAN_N_ACTIVE_DEPTS] = 0;
-    P.header[kHdrDeptSmall] = 0;
-    P.header[kHdrDeptLarge] = 0;
+    if (m <= 0) {
+      P.header[MOE_PLAN_N_DEPT_ROWS] = 0;
+      P.header[MOE_PLAN_N_ACTIVE_DEPTS] = 0;
+      P.header[kHdrDeptSmall] = 0;
+      P.header[kHdrDeptLarge] = 0;
+    }
   }
+  if (m > 0) dept_scan(s, pa, lane);
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  const int nwt = rank_mask_words(T, E);
+  const int nwt = rank_mask_words(T, E), G = m > 0 ? E / m : 1;
   for (int a = lane; a < A; a += kWave) {
     const int e = s.ids[a];
     if (e >= 0 && e < E) {
@@ -929,11 +948,18 @@ __device__ void plan_phase_wave(PlanShared& s, const PlanArgs& pa, int lane) {
       P.row_expert[row] = e;
       P.row_weight[row] = s.w[a];
       P.inv_perm[a] = row;
-      if (s.cnt[e] <= kTokInline) pa.work[s.pw.slot[e]].tok[rank] = t;
+      int in = t;
+      if (pa.factorised) {
+        const int J = e / G;
+        in = s.pw.doff[J] + pair_rank(s, T, m, t, J);
+        P.row_pair[row] = in;
+      }
+      if (s.cnt[e] <= kTokInline) pa.work[s.pw.slot[e]].tok[rank] = in;
     } else {
       P.inv_perm[a] = -1;
     }
   }
+  if (m > 0) write_pairs(s, pa, lane, kWave);
 }
 
 // Routing statistics of the step (DeepSeekMoE Guide, "Sequence-Level and
@@ -1141,7 +1167,7 @@ __global__ __launch_bounds__(kPlanThreads) void topk_plan_kernel(RouteArgs ra, P
   if (wid < ra.T) topk_token<NPL, GROUPED>(ra, wid, wid * ra.E, lane, s, key);
   if (!do_plan) return;
   __syncthreads();
-  if (pa.m <= 0 && pa.E <= kWavePlanPer * kWave && rank_mask_words(pa.T, pa.E) > 0) {
+  if (wave_plan_fits(pa.T, pa.E, pa.k, pa.m)) {
     if (wid == 0) plan_phase_wave(s, pa, lane);
   } else {
     plan_phase(s, pa, true);
@@ -1232,8 +1258,7 @@ __global__ __launch_bounds__(kPlanThreads) void dispatch_kernel(const int32_t* i
   }
   __syncthreads();
   // (one wave writes every row: past kWavePlanMaxA assignments the block does)
-  if (DISTINCT && pa.m <= 0 && pa.E <= kWavePlanPer * kWave && nwt > 0 &&
-      pa.T * pa.k <= kWavePlanMaxA) {
+  if (DISTINCT && wave_plan_fits(pa.T, pa.E, pa.k, pa.m)) {
     if (wid == 0) plan_phase_wave(s, pa, lane);
   } else {
     plan_phase(s, pa, DISTINCT && nwt > 0);
