@@ -161,12 +161,14 @@ constexpr int kCand = 128;        // compacted candidates per token
 constexpr int kPlanWaves = kPlanThreads / kWave;
 constexpr int kRankMaskWords = 1024;
 constexpr int kDeptMaskMax = 64;
+constexpr int kDeptMaskWords = 4;  // department token bits: up to 256 tokens
 __device__ __forceinline__ bool dept_masks(int T, int m) {
-  return m > 0 && m <= kDeptMaskMax && T <= 64;
+  return m > 0 && m <= kDeptMaskMax && T <= 64 * kDeptMaskWords;
 }
-__device__ __forceinline__ int rank_mask_words(int T, int E) {
+// Words of token bits per expert when E of them fit in `cap` words, else 0.
+__device__ __forceinline__ int rank_mask_words(int T, int E, int cap = kRankMaskWords) {
   const int nwt = (T + 63) >> 6;
-  return nwt * E <= kRankMaskWords ? nwt : 0;
+  return nwt * E <= cap ? nwt : 0;
 }
 struct TopkStage {
   float lg[kTopkBuf];
@@ -194,16 +196,32 @@ struct PlanShared {
   // rows is then a popcount of the lower tokens instead of a scan of the
   // earlier assignments.
   unsigned long long tmask[kRankMaskWords];
-  // Tokens of each department as bits (bit t of word J) when T <= 64 and
-  // m <= kDeptMaskMax: a pair's rank among its department's pairs is then a
-  // popcount of the lower tokens instead of a scan of the pair flags.
-  unsigned long long dtok[kDeptMaskMax];
+  // Tokens of each department as bits (word t / 64 of department J, bit
+  // t % 64) when T <= 64 kDeptMaskWords and m <= kDeptMaskMax: a pair's rank
+  // among its department's pairs is then a popcount of the lower tokens
+  // instead of a scan of the pair flags.
+  unsigned long long dtok[kDeptMaskMax][kDeptMaskWords];
   union {
     TopkStage tk;
-    PlanWork pw;
+    // the plan-only launch stages no top-k: its expert token bits take the
+    // staging area beside the plan's arrays (E * ceil(T / 64) up to
+    // kRankMaskWordsBig words)
+    struct {
+      PlanWork pw;
+      unsigned long long tbig[(sizeof(TopkStage) - sizeof(PlanWork)) / 8];
+    };
   };
   int invalid;
 };
+constexpr int kRankMaskWordsBig = (int)((sizeof(TopkStage) - sizeof(PlanWork)) / 8);
+static_assert(kRankMaskWordsBig >= 4096, "token bits of 864 experts at 256 tokens");
+
+// Rank of token t among the tokens whose bits `w` holds (its lower ones).
+__device__ __forceinline__ int bits_below(const unsigned long long* w, int t) {
+  int r = 0;
+  for (int q = 0; q < (t >> 6); ++q) r += __popcll(w[q]);
+  return r + __popcll(w[t >> 6] & ((1ull << (t & 63)) - 1ull));
+}
 
 // Order-preserving 32-bit key of a score: a larger float gives a larger key,
 // and +0 / -0 share one key (they compare equal as floats).  Key 0 lies below
@@ -643,7 +661,7 @@ __device__ void topk_token(const RouteArgs& p, int t, int row, int lane, PlanSha
       if (p.m > 0) {
         const int J = my_id / (E / p.m);
         s.flag[t * p.m + J] = 1;
-        if (dept_masks(p.T, p.m)) atomicOr(&s.dtok[J], 1ull << t);
+        if (dept_masks(p.T, p.m)) atomicOr(&s.dtok[J][t >> 6], 1ull << (t & 63));
       }
     }
   }
@@ -668,7 +686,7 @@ __device__ void dept_scan(PlanShared& s, const PlanArgs& pa, int lane) {
   for (int J = b; J < en; ++J) {
     int c = 0;
     if (dept_masks(T, m))
-      c = __popcll(s.dtok[J]);
+      for (int q = 0; q < ((T + 63) >> 6); ++q) c += __popcll(s.dtok[J][q]);
     else
       for (int t = 0; t < T; ++t) c += s.flag[t * m + J];
     s.pw.dcnt[J] = c;
@@ -707,7 +725,7 @@ __device__ void dept_scan(PlanShared& s, const PlanArgs& pa, int lane) {
 // Rank of token t's pair among department J's pairs (its lower tokens that
 // chose one of J's experts).
 __device__ __forceinline__ int pair_rank(const PlanShared& s, int T, int m, int t, int J) {
-  if (dept_masks(T, m)) return __popcll(s.dtok[J] & ((1ull << t) - 1ull));
+  if (dept_masks(T, m)) return bits_below(s.dtok[J], t);
   int r = 0;
   for (int u = 0; u < t; ++u) r += s.flag[u * m + J];
   return r;
@@ -746,10 +764,12 @@ __device__ void write_pairs(const PlanShared& s, const PlanArgs& pa, int i0, int
 // wave scans, wave totals through LDS) while the last wave scans the
 // departments; then every assignment and every pair writes its row.  Waves
 // with no entries stay out of the scan: cross-lane steps of idle waves would
-// only queue on the LDS crossbar.  `masks`: s.tmask holds the token bits of
-// every expert (the top-k filled it; its k experts per token are distinct).
+// only queue on the LDS crossbar.  nwt > 0: tm holds the token bits of every
+// expert, nwt words each (the tallies filled them; a token's k experts are
+// distinct).
 constexpr int kScanWaves = 4;
-__device__ void plan_phase(PlanShared& s, const PlanArgs& pa, bool masks) {
+__device__ void plan_phase(PlanShared& s, const PlanArgs& pa, const unsigned long long* tm,
+                           int nwt) {
   const int tid = threadIdx.x, nth = blockDim.x, lane = tid & 63, wid = tid >> 6;
   const int nw = nth >> 6;
   const int T = pa.T, k = pa.k, E = pa.E, A = T * k, m = pa.m;
@@ -826,7 +846,6 @@ __device__ void plan_phase(PlanShared& s, const PlanArgs& pa, bool masks) {
   // in the factorised form a row's inputs are its (token, department) pair's
   // backbone outputs, so the pair index goes to row_pair and to the inline
   // entries of small groups
-  const int nwt = masks ? rank_mask_words(T, E) : 0;
   for (int a = tid; a < A; a += nth) {
     const int e = s.ids[a];
     if (e >= 0 && e < E) {
@@ -834,9 +853,7 @@ __device__ void plan_phase(PlanShared& s, const PlanArgs& pa, bool masks) {
       int rank = 0;
       if (nwt > 0) {
         // the earlier assignments to e are those of the lower tokens that chose it
-        const unsigned long long* mw = s.tmask + e * nwt;
-        for (int q = 0; q < (t >> 6); ++q) rank += __popcll(mw[q]);
-        rank += __popcll(mw[t >> 6] & ((1ull << (t & 63)) - 1ull));
+        rank = bits_below(tm + e * nwt, t);
       } else {
         for (int b2 = 0; b2 < a; ++b2) rank += (s.ids[b2] == e) ? 1 : 0;
       }
@@ -861,7 +878,7 @@ __device__ void plan_phase(PlanShared& s, const PlanArgs& pa, bool masks) {
 }
 
 // The plan by one wave, for at most 4 * 64 experts with the token bits of
-// every expert in s.tmask and, in the department form, the token bits of
+// every expert in tm (nwt words each) and, in the department form, the token bits of
 // every department in s.dtok: lane l takes the experts [l * per, (l + 1) *
 // per), one wave scan of the counts gives their first rows and list slots
 // (dept_scan does the same for the departments), and the same wave then
@@ -873,12 +890,13 @@ constexpr int kWavePlanMaxA = 512;  // assignments the one-wave plan writes at m
 // the block-wide plan measured faster (DeaMoE-7B-shaped top-k + plan at one
 // token 7.9 -> 7.2 us with the wave, at 16 tokens 8.0 -> 9.4 us)
 constexpr int kWavePlanMaxDeptA = kWave;
-__device__ __forceinline__ bool wave_plan_fits(int T, int E, int k, int m) {
-  return E <= kWavePlanPer * kWave && rank_mask_words(T, E) > 0 &&
+__device__ __forceinline__ bool wave_plan_fits(int T, int E, int k, int m, int nwt) {
+  return E <= kWavePlanPer * kWave && nwt > 0 &&
          (m <= 0 ? T * k <= kWavePlanMaxA
                  : dept_masks(T, m) && T * k <= kWavePlanMaxDeptA && T * m <= kWavePlanMaxDeptA);
 }
-__device__ void plan_phase_wave(PlanShared& s, const PlanArgs& pa, int lane) {
+__device__ void plan_phase_wave(PlanShared& s, const PlanArgs& pa, int lane,
+                                const unsigned long long* tm, int nwt) {
   const int T = pa.T, k = pa.k, E = pa.E, A = T * k, m = pa.m;
   const moe_plan& P = pa.plan;
   const int per = (E + kWave - 1) / kWave;
@@ -932,16 +950,13 @@ __device__ void plan_phase_wave(PlanShared& s, const PlanArgs& pa, int lane) {
   if (m > 0) dept_scan(s, pa, lane);
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  const int nwt = rank_mask_words(T, E), G = m > 0 ? E / m : 1;
+  const int G = m > 0 ? E / m : 1;
   for (int a = lane; a < A; a += kWave) {
     const int e = s.ids[a];
     if (e >= 0 && e < E) {
       const int t = a / k;
       // the earlier assignments to e are those of the lower tokens that chose it
-      const unsigned long long* mw = s.tmask + e * nwt;
-      int rank = 0;
-      for (int q = 0; q < (t >> 6); ++q) rank += __popcll(mw[q]);
-      rank += __popcll(mw[t >> 6] & ((1ull << (t & 63)) - 1ull));
+      const int rank = bits_below(tm + e * nwt, t);
       const int row = s.pw.off[e] + rank;
       P.row_token[row] = t;
       P.row_slot[row] = a - t * k;
@@ -1002,13 +1017,14 @@ __device__ void write_stats(const PlanShared& s, const PlanArgs& pa, int lane) {
 }
 
 // Per-launch clearing of the plan's LDS tallies (before any top-k or count).
-__device__ __forceinline__ void plan_clear(PlanShared& s, int T, int E, int m) {
+__device__ __forceinline__ void plan_clear(PlanShared& s, int T, int E, int m,
+                                           unsigned long long* tm, int nwt) {
   for (int e = threadIdx.x; e < E; e += blockDim.x) s.cnt[e] = 0;
-  const int nm = rank_mask_words(T, E) * E;
-  for (int i = threadIdx.x; i < nm; i += blockDim.x) s.tmask[i] = 0ull;
+  for (int i = threadIdx.x; i < nwt * E; i += blockDim.x) tm[i] = 0ull;
   for (int p = threadIdx.x; p < T * (m > 0 ? m : 0); p += blockDim.x) s.flag[p] = 0;
   if (dept_masks(T, m))
-    for (int J = threadIdx.x; J < m; J += blockDim.x) s.dtok[J] = 0ull;
+    for (int i = threadIdx.x; i < m * kDeptMaskWords; i += blockDim.x)
+      s.dtok[i / kDeptMaskWords][i % kDeptMaskWords] = 0ull;
   if (threadIdx.x == 0) s.invalid = 0;
 }
 
@@ -1156,7 +1172,8 @@ __global__ __launch_bounds__(kPlanThreads) void topk_plan_kernel(RouteArgs ra, P
                                                                  int do_plan) {
   __shared__ PlanShared s;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  plan_clear(s, ra.T, ra.E, ra.m);
+  const int nwt = rank_mask_words(ra.T, ra.E);
+  plan_clear(s, ra.T, ra.E, ra.m, s.tmask, nwt);
   // up to 256 experts and one token per wave: each wave stages its own token
   // in its own row, its logits requested before the barrier that completes
   // the clearing (the staged row is not a tally)
@@ -1167,10 +1184,10 @@ __global__ __launch_bounds__(kPlanThreads) void topk_plan_kernel(RouteArgs ra, P
   if (wid < ra.T) topk_token<NPL, GROUPED>(ra, wid, wid * ra.E, lane, s, key);
   if (!do_plan) return;
   __syncthreads();
-  if (wave_plan_fits(pa.T, pa.E, pa.k, pa.m)) {
-    if (wid == 0) plan_phase_wave(s, pa, lane);
+  if (wave_plan_fits(pa.T, pa.E, pa.k, pa.m, nwt)) {
+    if (wid == 0) plan_phase_wave(s, pa, lane, s.tmask, nwt);
   } else {
-    plan_phase(s, pa, true);
+    plan_phase(s, pa, s.tmask, nwt);
   }
   // the tallies the statistics read were final before the plan phase (rows
   // per expert) or inside it, before its last barrier (pairs per department)
@@ -1236,10 +1253,11 @@ __global__ __launch_bounds__(kPlanThreads) void dispatch_kernel(const int32_t* i
                                                                 PlanArgs pa) {
   __shared__ PlanShared s;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  plan_clear(s, pa.T, pa.E, pa.m);
+  // no top-k staging here: the expert token bits take its area
+  const int nwt = DISTINCT ? rank_mask_words(pa.T, pa.E, kRankMaskWordsBig) : 0;
+  plan_clear(s, pa.T, pa.E, pa.m, s.tbig, nwt);
   __syncthreads();
   const int G = pa.m > 0 ? pa.E / pa.m : 1;
-  const int nwt = DISTINCT ? rank_mask_words(pa.T, pa.E) : 0;
   for (int a = threadIdx.x; a < pa.T * pa.k; a += blockDim.x) {
     const int e = ids[a];
     s.ids[a] = e;
@@ -1247,10 +1265,10 @@ __global__ __launch_bounds__(kPlanThreads) void dispatch_kernel(const int32_t* i
     if (e >= 0 && e < pa.E) {
       const int t = a / pa.k;
       atomicAdd(&s.cnt[e], 1);
-      if (nwt > 0) atomicOr(&s.tmask[e * nwt + (t >> 6)], 1ull << (t & 63));
+      if (nwt > 0) atomicOr(&s.tbig[e * nwt + (t >> 6)], 1ull << (t & 63));
       if (pa.m > 0) {
         s.flag[t * pa.m + e / G] = 1;
-        if (dept_masks(pa.T, pa.m)) atomicOr(&s.dtok[e / G], 1ull << t);
+        if (dept_masks(pa.T, pa.m)) atomicOr(&s.dtok[e / G][t >> 6], 1ull << (t & 63));
       }
     } else {
       atomicAdd(&s.invalid, 1);
@@ -1258,10 +1276,10 @@ __global__ __launch_bounds__(kPlanThreads) void dispatch_kernel(const int32_t* i
   }
   __syncthreads();
   // (one wave writes every row: past kWavePlanMaxA assignments the block does)
-  if (DISTINCT && wave_plan_fits(pa.T, pa.E, pa.k, pa.m)) {
-    if (wid == 0) plan_phase_wave(s, pa, lane);
+  if (DISTINCT && wave_plan_fits(pa.T, pa.E, pa.k, pa.m, nwt)) {
+    if (wid == 0) plan_phase_wave(s, pa, lane, s.tbig, nwt);
   } else {
-    plan_phase(s, pa, DISTINCT && nwt > 0);
+    plan_phase(s, pa, s.tbig, nwt);
   }
   if (pa.stats && wid == 0) write_stats(s, pa, lane);
 }
