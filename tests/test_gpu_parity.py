@@ -531,9 +531,13 @@ def test_layer_two_token_tiles(name):
 def test_layer_large_batch(name, T):
     """Batches past 64 tokens: the plan ranks an assignment by popcounts over
     its expert's token bits spread across several 64-bit words (eight at
-    T = 512, the assignment limit at top-8), one wave writes the plan when
-    there are no departments, and groups span several 16-token chunks.  The
-    whole plan is compared; outputs on a sample of tokens."""
+    T = 512, the assignment limit at top-8; the 864-expert layer's 1728 words
+    at T = 128 sit in the plan launch's staging area), a pair by its
+    department's token bits (two words at T = 100 and 128), one wave writes
+    the plan when there are no departments, the combine lists each token's
+    active departments (32 of them on the DeepSeek-V3 geometry), and groups
+    span several 16-token chunks.  The whole plan is compared; outputs on a
+    sample of tokens."""
     stride = 7 if SH[name].d <= 2048 else 31
     check_layer(name, 0, T, sample_tokens=list(range(0, T, stride)) + [T - 1], max_tokens=T,
                 allow_near=True)
