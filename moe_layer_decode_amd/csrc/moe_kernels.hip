@@ -105,15 +105,17 @@ __device__ __forceinline__ float dot8(const Raw8<float>& w, const X8<float>& x, 
   return fmaf(w.b.w, x.b.w, acc);
 }
 
-// 16-byte loads for the matrix-core paths: cached (activations) and
-// streaming (weights, read once).
+// 16-byte loads with the default cache policy.  Weights read in the
+// matrix-core operand layout (64-byte pieces of each row: the router's and the
+// 64-row tiles') take it too: the two halves of a 128-byte line arrive from
+// separate loads, and a non-temporal first half did not keep the line for the
+// second (DeaMoE on the DeepSeek-V3 geometry, batch 128: 1168 -> 1085 us;
+// the DeepSeek-V3-shaped router at batch 128: 18.7 -> 14.7 us).  Whole-line
+// streams (the GEMVs, the LDS weight tiles) stay non-temporal.
 __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& u) {
   return __builtin_bit_cast(bf16x8_t, u);
 }
 __device__ __forceinline__ u32x4_t ld16(const bf16_t* p) { return *as_global<u32x4_t>(p); }
-__device__ __forceinline__ u32x4_t ld16_stream(const bf16_t* p) {
-  return __builtin_nontemporal_load(as_global<u32x4_t>(p));
-}
 
 
 // Wave-uniform copies (one lane's value in a scalar register), for values
@@ -145,9 +147,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void* base) {
 }
 __device__ __forceinline__ u32x4_t ld16_span(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-}
-__device__ __forceinline__ u32x4_t ld16_span_nt(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
-  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kCpolNt));
 }
 
 // ---------------------------------------------------------------------------
@@ -1120,7 +1119,7 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(RouteArgs ra) {
     for (int q = 0; q < kAhead; ++q) {
       const int k = kb + q * 32;
       const bool in = k + g * 8 < ke;
-      ra_[q] = in ? ld16_stream(ap + k) : z;
+      ra_[q] = in ? ld16(ap + k) : z;
 #pragma unroll
       for (int c = 0; c < NCT; ++c) rb[q][c] = (bv[c] && in) ? ld16(bp[c] + k) : z;
     }
@@ -1130,7 +1129,7 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(RouteArgs ra) {
         const int kn = k + (q + kAhead) * 32;
         const int qn = (q + kAhead) % (kAhead + 1);
         const bool nin = kn + g * 8 < ke;
-        ra_[qn] = nin ? ld16_stream(ap + kn) : z;
+        ra_[qn] = nin ? ld16(ap + kn) : z;
 #pragma unroll
         for (int c = 0; c < NCT; ++c) rb[qn][c] = (bv[c] && nin) ? ld16(bp[c] + kn) : z;
         if (k + q * 32 < ke) {
@@ -2258,8 +2257,8 @@ __device__ __forceinline__ void gu_wide(const bf16_t* __restrict__ Wg,
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int k = k0 + 32 * h;
-      ra[s][h] = k + 8 * g < d ? ld16_stream(ap + k) : z;
-      rb[s][h] = k + 8 * g < d ? ld16_stream(bp + k) : z;
+      ra[s][h] = k + 8 * g < d ? ld16(ap + k) : z;
+      rb[s][h] = k + 8 * g < d ? ld16(bp + k) : z;
     }
   };
   auto use = [&](auto S) {
@@ -2339,7 +2338,7 @@ __device__ __attribute__((noinline)) void dn_wide(const bf16_t* __restrict__ Wd,
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int k = k0 + 32 * hh;
-      ra[s][hh] = k + 8 * g < rows ? ld16_stream(ap + k) : z;
+      ra[s][hh] = k + 8 * g < rows ? ld16(ap + k) : z;
     }
   };
   auto use = [&](auto S) {
@@ -3219,8 +3218,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t fp8_rsrc(const void* base, uin
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            kGfx9BufferDword3);
 }
+// POL: cache policy -- non-temporal where every code is read once (the
+// GEMVs: 7-9% faster steps at 1-16 tokens), the default where a 64-row tile
+// may read its codes once per token pass (non-temporal there: DeepSeek-V3-
+// shaped batch 128 1271 -> 1503 us).
+template <int POL = 0>
 __device__ __forceinline__ u32x4_t fp8_ld(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
-  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, POL));
 }
 
 // Gate and up rows i0 .. i0 + RPW - 1 (one wave) of matrix `mat` for every
@@ -3258,8 +3262,8 @@ __device__ __forceinline__ void gu_fp8(const Family& F, const Slot& sl, const bf
     u32x4_t rg[R], ru[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      rg[r] = fp8_ld(rsg, off(r));
-      ru[r] = fp8_ld(rsu, off(r));
+      rg[r] = fp8_ld<kCpolNt>(rsg, off(r));
+      ru[r] = fp8_ld<kCpolNt>(rsu, off(r));
     }
     // the chunk's activation rows, one 1 KB wave instruction at a time
     {
@@ -3302,8 +3306,8 @@ __device__ __forceinline__ void gu_fp8(const Family& F, const Slot& sl, const bf
             }
           }
           const int f = k * spr + sidx + R;
-          rg[r] = fp8_ld(rsg, off(f));
-          ru[r] = fp8_ld(rsu, off(f));
+          rg[r] = fp8_ld<kCpolNt>(rsg, off(f));
+          ru[r] = fp8_ld<kCpolNt>(rsu, off(f));
         }
       }
       constexpr int N = 2 * NT;
@@ -3540,7 +3544,7 @@ __device__ __forceinline__ void dn_fp8(const Family& F, const Slot& sl, int d, i
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int q = 0; q < CG; ++q) rw[r][q] = fp8_ld(rs, off(q, r));
+      for (int q = 0; q < CG; ++q) rw[r][q] = fp8_ld<kCpolNt>(rs, off(q, r));
     {
       constexpr int EPI = 8 * kWave;
       const int per_row = (rows + EPI - 1) / EPI, total = nv * per_row;
@@ -3570,7 +3574,7 @@ __device__ __forceinline__ void dn_fp8(const Family& F, const Slot& sl, int d, i
 #pragma unroll
           for (int t = 0; t < NT; ++t)
             if (t < nv) acc[q][t] = dot16(wb, hl + (size_t)t * rows + ho, acc[q][t]);
-          rw[r][q] = fp8_ld(rs, off(q, sidx + R));
+          rw[r][q] = fp8_ld<kCpolNt>(rs, off(q, sidx + R));
         }
       }
     }
