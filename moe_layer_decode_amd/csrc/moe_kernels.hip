@@ -741,10 +741,23 @@ __device__ void write_pairs(const PlanShared& s, const PlanArgs& pa, int i0, int
     if (s.flag[p]) {
       const int rank = pair_rank(s, T, m, t, J);
       const int q = s.pw.doff[J] + rank;
+      // the token's slots eight at a time: their ids and weights are read
+      // together, then added in slot order (department J holds experts
+      // [J G, J G + G))
+      const int e0 = J * G;
       float sc2 = 0.f;
-      for (int j = 0; j < k; ++j) {
-        const int e = s.ids[t * k + j];
-        if (e >= 0 && e < E && e / G == J) sc2 += s.w[t * k + j];
+      for (int j0 = 0; j0 < k; j0 += 8) {
+        int ev[8];
+        float wv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int a = t * k + min(j0 + j, k - 1);
+          ev[j] = s.ids[a];
+          wv[j] = s.w[a];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (j0 + j < k && ev[j] >= e0 && ev[j] < e0 + G && ev[j] < E) sc2 += wv[j];
       }
       P.dept_row_token[q] = t;
       P.dept_row_dept[q] = J;
