@@ -473,13 +473,24 @@ FamilySet make_families(const moe_layer_desc& d, const moe_weights& w, const moe
 void set_tiles(FamilySet& set, int d, bool gateup, int w_dtype, const moe::GemvConfig& c,
                int T) {
   set.blk_start[0] = 0;
+  // At d > 2048 past eight tokens the K-split tiles pay off only where few
+  // large groups can exist (each then needs the 4x blocks); with more, the
+  // whole-K tiles (gate/up row tiles, 64-column down tiles) stream better
+  // (DeaMoE on the DeepSeek-V3 geometry: batch 16 597 -> 586 us, batch 32
+  // 704 -> 688 us; its factorised 864-expert form, eight department groups,
+  // keeps the split: 772 us against 812).  The bound is the large parts'
+  // slot counts.
+  int large_groups = 0;
+  for (int i = 0; i < set.n; ++i)
+    if (set.f[i].large) large_groups += set.f[i].max_slots;
+  const bool few_large = d <= 2048 || T <= 8 || large_groups <= moe::kSplitKMaxGroups;
   for (int i = 0; i < set.n; ++i) {
     Family& f = set.f[i];
     // (a launch with two inputs per row passes 16 tokens at a time)
     f.splitk = w_dtype == MOE_BF16 && f.large &&
-               (gateup ? T <= (f.x_up ? 16 : moe::kSplitKMaxT)
+               (gateup ? T <= (f.x_up ? 16 : moe::kSplitKMaxT) && (f.x_up || few_large)
                        : T <= moe::kSplitKDownMaxT && d > moe::kSplitKDownMinD &&
-                             f.rows >= moe::kSplitKMinK);
+                             f.rows >= moe::kSplitKMinK && few_large);
     // past kSplitKDownMaxT the routed experts' groups, mostly of a few rows,
     // take row tiles of kDownRowCols columns (DeepSeek-V3-shaped down: 1011 ->
     // 878 us at batch 128); the department slices' and the shared expert's

@@ -20,6 +20,8 @@ constexpr int kDownRowCols = 128;    // down row tiles (T > kSplitKDownMaxT): ou
 constexpr int kSplitKCols = 32;      // K-split down tiles: output columns per block,
 constexpr int kSplitKDownMinD = 2048;  //   d above it
 constexpr int kSplitKMinK = 256;     //   and intermediate width at least (a full K tile per wave)
+constexpr int kSplitKMaxGroups = 16; // d > 2048, T > 8: K-split only if a launch holds at most this
+                                     //   many large groups
 constexpr int kPlanThreads = 1024;   // threads of the single-block top-k / plan kernel
 // Top-k + plan in one block (a wave per token, at most 256 experts), or the
 // per-token selections across the chip followed by a one-block plan launch.
